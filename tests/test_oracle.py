@@ -1,0 +1,352 @@
+"""Pins for the CPU oracle, independent of the oracle's own code.
+
+Each pin checks the oracle against something it does not compute itself:
+hand-worked values (tests/golden), a textbook reformulation (bag-count matrix
+times table; Z Z^T and its strict lower triangle), a closed form (the
+factorization-machine identity, F(F-1)/2 pair count, finite differences of a
+quadratic loss), brute force on tiny inputs, and invariants.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import dlrm_oracle as orc
+
+
+def _golden(golden_dir):
+    with open(os.path.join(golden_dir, "worked_example_t2_d2.json")) as f:
+        return json.load(f)
+
+
+def _tables_f32(g):
+    return [np.array(t, dtype=np.float32) for t in g["tables"]]
+
+
+# ---------------------------------------------------------------------------
+# Hand-worked example
+# ---------------------------------------------------------------------------
+def test_golden_forward(golden_dir):
+    g = _golden(golden_dir)
+    off = orc.lengths_to_offsets(g["lengths_table_major"])
+    assert off.tolist() == g["offsets"]
+    idx = np.array(g["indices"], dtype=np.int32)
+    r = orc.embbag_fwd(_tables_f32(g), "f32", g["B"], off, idx, np.array(g["e0"], np.float32))
+    np.testing.assert_array_equal(r["pooled"], np.array(g["pooled"], dtype=np.float64))
+    np.testing.assert_array_equal(r["out"], np.array(g["out"], dtype=np.float64))
+
+
+def test_golden_pair_order(golden_dir):
+    with open(os.path.join(golden_dir, "worked_example_pair_order_t3.json")) as f:
+        g = json.load(f)
+    tabs = [np.array(t, dtype=np.float32) for t in g["tables"]]
+    r = orc.embbag_fwd(tabs, "f32", g["B"], np.array(g["offsets"]), np.array(g["indices"], np.int32),
+                       np.array(g["e0"], np.float32))
+    np.testing.assert_array_equal(r["out"], np.array(g["out"], dtype=np.float64))
+
+
+def test_golden_backward(golden_dir):
+    g = _golden(golden_dir)
+    off = np.array(g["offsets"])
+    idx = np.array(g["indices"], dtype=np.int32)
+    tabs = _tables_f32(g)
+    e0 = np.array(g["e0"], np.float32)
+    pooled = np.array(g["pooled"], dtype=np.float64)
+    r = orc.embbag_bwd_update(tabs, "f32", g["B"], off, idx, e0, pooled,
+                              np.array(g["d_out"], np.float32), g["lr"])
+    np.testing.assert_array_equal(r["dZ"], np.array(g["dZ"], dtype=np.float64))
+    np.testing.assert_array_equal(r["d_e0"], np.array(g["d_e0"], dtype=np.float64))
+    key, _, _, _ = orc.occurrence_keys([t.shape[0] for t in tabs], g["B"], off, idx)
+    assert key.tolist() == g["keys"]
+    assert r["perm"].tolist() == g["perm"]
+    assert r["unique_keys"].tolist() == g["unique_keys"]
+    assert r["seg_offsets"].tolist() == g["seg_offsets"]
+    np.testing.assert_array_equal(r["grad"], np.array(g["grad"], dtype=np.float64))
+    np.testing.assert_array_equal(r["new_rows"], np.array(g["new_rows"], dtype=np.float64))
+
+
+# ---------------------------------------------------------------------------
+# Random tiny instances
+# ---------------------------------------------------------------------------
+def _random_instance(seed, T=3, B=5, D=4, max_len=4, rows=(5, 1, 7), dtype="f32", empty=True):
+    rng = np.random.default_rng(seed)
+    rows = list(rows)[:T]
+    lengths = rng.integers(0 if empty else 1, max_len + 1, size=T * B)
+    if empty:
+        lengths[1] = 0
+    idx = np.concatenate([rng.integers(0, rows[t], size=int(lengths[t * B:(t + 1) * B].sum()))
+                          for t in range(T)]).astype(np.int32)
+    if dtype == "f64":
+        tabs = [rng.standard_normal((n, D)) for n in rows]
+    else:
+        tabs = [rng.standard_normal((n, D)).astype(np.float32) for n in rows]
+    e0 = rng.standard_normal((B, D)).astype(np.float32)
+    return tabs, orc.lengths_to_offsets(lengths), idx, e0, lengths
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pool_equals_count_matrix_product(seed):
+    """EmbeddingBag-sum equals (bag-count matrix) @ table, a textbook identity."""
+    tabs, off, idx, _, _ = _random_instance(seed)
+    T, B = len(tabs), 5
+    pooled = orc.embbag_pool(tabs, "f32", B, off, idx)
+    for t in range(T):
+        A = np.zeros((B, tabs[t].shape[0]))
+        for b in range(B):
+            for p in range(off[t * B + b], off[t * B + b + 1]):
+                A[b, idx[p]] += 1.0
+        np.testing.assert_allclose(pooled[:, t], A @ tabs[t].astype(np.float64), rtol=1e-14, atol=1e-14)
+
+
+def test_pool_single_index_is_the_row_exactly():
+    rng = np.random.default_rng(7)
+    tab = rng.standard_normal((50, 8)).astype(np.float16)
+    idx = rng.integers(0, 50, size=10).astype(np.int32)
+    off = np.arange(11)
+    pooled = orc.embbag_pool([tab], "f16", 10, off, idx)
+    np.testing.assert_array_equal(pooled[:, 0], tab[idx].astype(np.float64))
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 7, 32])
+def test_pool_repeated_index_counts_k_times(k):
+    tab = np.random.default_rng(k).standard_normal((4, 16)).astype(np.float32)
+    idx = np.full(k, 2, dtype=np.int32)
+    pooled = orc.embbag_pool([tab], "f32", 1, np.array([0, k]), idx)
+    np.testing.assert_array_equal(pooled[0, 0], k * tab[2].astype(np.float64))
+
+
+def test_pool_empty_bag_is_positive_zero():
+    tab = np.ones((3, 4), np.float32)
+    pooled = orc.embbag_pool([tab], "f32", 2, np.array([0, 0, 2]), np.array([0, 1], np.int32))
+    assert np.all(pooled[0, 0] == 0.0) and not np.any(np.signbit(pooled[0, 0]))
+    np.testing.assert_array_equal(pooled[1, 0], [2, 2, 2, 2])
+
+
+def test_pool_permutation_invariant_exact_integers():
+    rng = np.random.default_rng(3)
+    tab = rng.integers(-4, 5, size=(20, 8)).astype(np.float32)
+    idx = rng.integers(0, 20, size=12).astype(np.int32)
+    a = orc.embbag_pool([tab], "f32", 1, np.array([0, 12]), idx)
+    b = orc.embbag_pool([tab], "f32", 1, np.array([0, 12]), idx[::-1].copy())
+    np.testing.assert_array_equal(a, b)
+
+
+def test_decode_bf16_and_f16_exact():
+    # bf16 bit patterns of 1.0, -2.0, 0.5, 3.140625 (0x4049), smallest normal
+    bits = np.array([[0x3F80, 0xC000, 0x3F00, 0x4049, 0x0080]], dtype=np.uint16)
+    v = orc.decode(bits, "bf16")
+    assert v.tolist() == [[1.0, -2.0, 0.5, 3.140625, 2.0 ** -126]]
+    h = np.array([[1.5, -0.25, 65504.0]], dtype=np.float16)
+    assert orc.decode(h, "f16").tolist() == [[1.5, -0.25, 65504.0]]
+
+
+# ---------------------------------------------------------------------------
+# Interaction
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("F", [2, 3, 5, 9, 27])
+def test_interaction_equals_gram_strict_lower(F):
+    """Dots equal the strict lower triangle of Z Z^T in numpy's row-major tril order."""
+    rng = np.random.default_rng(F)
+    B, D = 4, 6
+    e0 = rng.standard_normal((B, D))
+    pooled = rng.standard_normal((B, F - 1, D))
+    out = orc.interact(e0, pooled)
+    assert out.shape == (B, D + F * (F - 1) // 2)
+    np.testing.assert_array_equal(out[:, :D], e0)
+    ii, jj = np.tril_indices(F, -1)
+    for b in range(B):
+        Z = np.vstack([e0[b][None], pooled[b]])
+        G = Z @ Z.T
+        np.testing.assert_allclose(out[b, D:], G[ii, jj], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(G, G.T, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("F", range(1, 70))
+def test_pair_count_and_order(F):
+    pr = list(orc.pairs(F))
+    assert len(pr) == F * (F - 1) // 2 == orc.pair_count(F)
+    assert [k for k, _, _ in pr] == list(range(len(pr)))
+    assert all(k == i * (i - 1) // 2 + j and 0 <= j < i < F for k, i, j in pr)
+    assert len({(i, j) for _, i, j in pr}) == len(pr)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_interaction_fm_identity(seed):
+    """Sum of pairwise dots = 1/2 (|sum_i z_i|^2 - sum_i |z_i|^2) (FM second-order term)."""
+    rng = np.random.default_rng(100 + seed)
+    B, T, D = 3, 12, 16
+    e0 = rng.standard_normal((B, D))
+    pooled = rng.standard_normal((B, T, D))
+    out = orc.interact(e0, pooled)
+    Z = np.concatenate([e0[:, None], pooled], axis=1)
+    fm = 0.5 * ((Z.sum(axis=1) ** 2).sum(axis=1) - (Z ** 2).sum(axis=(1, 2)))
+    np.testing.assert_allclose(out[:, D:].sum(axis=1), fm, rtol=1e-12)
+
+
+def test_interaction_orthogonal_and_parallel_vectors():
+    F, D = 6, 8
+    e0 = np.zeros((2, D))
+    e0[0, 0] = 3.0
+    e0[1, 0] = 1.0
+    pooled = np.zeros((2, F - 1, D))
+    for i in range(F - 1):
+        pooled[0, i, i + 1] = i + 2.0   # mutually orthogonal rows -> every dot is 0
+        pooled[1, i, 0] = 1.0           # identical unit rows -> every dot is 1
+    out = orc.interact(e0, pooled)
+    assert np.all(out[0, D:] == 0.0)
+    assert np.all(out[1, D:] == 1.0)
+
+
+# ---------------------------------------------------------------------------
+# Backward: finite differences of a quadratic loss are exact up to rounding
+# ---------------------------------------------------------------------------
+def _loss(tabs, B, off, idx, e0, d_out):
+    r = orc.embbag_fwd(tabs, "f64", B, off, idx, e0)
+    return float((r["out"] * d_out).sum())
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_backward_matches_finite_differences(seed):
+    tabs, off, idx, e0, _ = _random_instance(seed, dtype="f64")
+    e0 = e0.astype(np.float64)
+    B = 5
+    rng = np.random.default_rng(50 + seed)
+    F = len(tabs) + 1
+    D = tabs[0].shape[1]
+    d_out = rng.standard_normal((B, D + F * (F - 1) // 2))
+    fwd = orc.embbag_fwd(tabs, "f64", B, off, idx, e0)
+    r = orc.embbag_bwd_update(tabs, "f64", B, off, idx, e0, fwd["pooled"], d_out, lr=0.0)
+    base = r["base"]
+    grad_of = {int(k): r["grad"][u] for u, k in enumerate(r["unique_keys"])}
+    h = 1e-3
+    for t, tab in enumerate(tabs):
+        for row in range(tab.shape[0]):
+            for d in range(D):
+                tp = [x.copy() for x in tabs]
+                tm = [x.copy() for x in tabs]
+                tp[t][row, d] += h
+                tm[t][row, d] -= h
+                fd = (_loss(tp, B, off, idx, e0, d_out) - _loss(tm, B, off, idx, e0, d_out)) / (2 * h)
+                want = grad_of.get(int(base[t]) + row, np.zeros(D))[d]
+                assert abs(fd - want) <= 1e-8 * (1 + abs(fd)), (t, row, d, fd, want)
+    for b in range(B):
+        for d in range(D):
+            ep = e0.copy()
+            em = e0.copy()
+            ep[b, d] += h
+            em[b, d] -= h
+            fd = (_loss(tabs, B, off, idx, ep, d_out) - _loss(tabs, B, off, idx, em, d_out)) / (2 * h)
+            assert abs(fd - r["d_e0"][b, d]) <= 1e-8 * (1 + abs(fd))
+
+
+def test_backward_gradient_conservation():
+    tabs, off, idx, e0, _ = _random_instance(11, B=5)
+    fwd = orc.embbag_fwd(tabs, "f32", 5, off, idx, e0)
+    d_out = np.random.default_rng(1).standard_normal((5, 4 + 6))
+    r = orc.embbag_bwd_update(tabs, "f32", 5, off, idx, e0, fwd["pooled"], d_out, lr=0.01)
+    _, tab, smp, _ = orc.occurrence_keys([t.shape[0] for t in tabs], 5, off, idx)
+    total = sum(r["dZ"][smp[p], 1 + tab[p]] for p in range(len(idx)))
+    np.testing.assert_allclose(r["grad"].sum(axis=0), total, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Sort and segments: brute force
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(5))
+def test_stable_order_and_segments_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    keys = rng.integers(0, 9, size=40)
+    perm = orc.stable_order(keys)
+    assert perm.tolist() == sorted(range(40), key=lambda p: (keys[p], p))
+    uniq, seg = orc.segments(keys[perm])
+    groups = [(k, len(list(g))) for k, g in itertools.groupby(sorted(keys.tolist()))]
+    assert uniq.tolist() == [k for k, _ in groups]
+    assert seg[0] == 0 and seg[-1] == 40
+    assert np.diff(seg).tolist() == [c for _, c in groups]
+    assert np.all(np.diff(uniq) > 0)
+
+
+def test_sgd_untouched_rows_and_closed_form():
+    tabs, off, idx, e0, _ = _random_instance(5, B=5)
+    fwd = orc.embbag_fwd(tabs, "f32", 5, off, idx, e0)
+    d_out = np.random.default_rng(2).standard_normal((5, 4 + 6))
+    lr = 0.01
+    r = orc.embbag_bwd_update(tabs, "f32", 5, off, idx, e0, fwd["pooled"], d_out, lr=lr)
+    base = r["base"]
+    touched = set(int(k) for k in r["unique_keys"])
+    used = set(int(base[t]) + int(i) for t in range(3)
+               for i in idx[off[t * 5]:off[(t + 1) * 5]])
+    assert touched == used
+    for u, k in enumerate(r["unique_keys"]):
+        t = int(np.searchsorted(base, k, side="right") - 1)
+        np.testing.assert_allclose(r["new_rows"][u], tabs[t][k - base[t]] - lr * r["grad"][u], rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Status bits
+# ---------------------------------------------------------------------------
+def test_status_bits():
+    rows = [4, 2]
+    good_off = np.array([0, 1, 2, 3, 4])
+    good_idx = np.array([0, 3, 1, 0], np.int32)
+    assert orc.bag_status(2, 2, rows, good_off, good_idx) == 0
+    assert orc.bag_status(2, 2, rows, good_off, np.array([0, 4, 1, 0], np.int32)) == oracle.STATUS_BAD_INDEX
+    assert orc.bag_status(2, 2, rows, good_off, np.array([0, 3, 2, 0], np.int32)) == oracle.STATUS_BAD_INDEX
+    assert orc.bag_status(2, 2, rows, good_off, np.array([-1, 3, 1, 0], np.int32)) == oracle.STATUS_BAD_INDEX
+    assert orc.bag_status(2, 2, rows, np.array([0, 2, 1, 3, 4]), good_idx) == oracle.STATUS_BAD_OFFSETS
+    assert orc.bag_status(2, 2, rows, np.array([0, 1, 2, 3, 3]), good_idx) == oracle.STATUS_BAD_OFFSETS
+    assert orc.bag_status(2, 2, rows, np.array([1, 1, 2, 3, 4]), good_idx) == oracle.STATUS_BAD_OFFSETS
+    with pytest.raises(oracle.BagError) as ei:
+        orc.embbag_pool([np.zeros((4, 4), np.float32), np.zeros((2, 4), np.float32)], "f32", 2,
+                        good_off, np.array([0, 4, 1, 0], np.int32))
+    assert ei.value.bits == oracle.STATUS_BAD_INDEX
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each pin above must catch a plausible oracle bug
+# ---------------------------------------------------------------------------
+def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
+    g = _golden(golden_dir)
+    idx = np.array(g["indices"], dtype=np.int32)
+    off = np.array(g["offsets"])
+    e0 = np.array(g["e0"], np.float32)
+    good = orc.embbag_fwd(_tables_f32(g), "f32", 2, off, idx, e0)["out"]
+
+    # (a) column-major pair order instead of row-major
+    def bad_pairs(F):
+        k = 0
+        for j in range(F):
+            for i in range(j + 1, F):
+                yield k, i, j
+                k += 1
+    with monkeypatch.context() as m:
+        m.setattr(orc, "pairs", bad_pairs)
+        with pytest.raises(AssertionError):
+            test_golden_pair_order(golden_dir)
+        with pytest.raises(AssertionError):
+            test_interaction_equals_gram_strict_lower(5)
+
+    # (b) backward dropping the dZ_j term
+    def bad_bwd(e0_, pooled, d_out):
+        B, T, D = pooled.shape
+        Z = orc.stack_z(np.asarray(e0_, np.float64), pooled)
+        dZ = np.zeros_like(Z)
+        for k, i, j in orc.pairs(T + 1):
+            dZ[:, i] += np.asarray(d_out, np.float64)[:, D + k][:, None] * Z[:, j]
+        return {"dZ": dZ, "d_e0": np.asarray(d_out, np.float64)[:, :D] + dZ[:, 0]}
+    with monkeypatch.context() as m:
+        m.setattr(orc, "interact_bwd", bad_bwd)
+        r = orc.embbag_bwd_update(_tables_f32(g), "f32", 2, off, idx, e0, np.array(g["pooled"], np.float64),
+                                  np.array(g["d_out"], np.float32), g["lr"])
+        assert not np.array_equal(r["grad"], np.array(g["grad"], dtype=np.float64))
+
+    # (c) an unstable sort changes the permutation on ties
+    with monkeypatch.context() as m:
+        m.setattr(orc, "stable_order", lambda k: np.argsort(-np.asarray(k), kind="stable")[::-1])
+        r = orc.embbag_bwd_update(_tables_f32(g), "f32", 2, off, idx, e0, np.array(g["pooled"], np.float64),
+                                  np.array(g["d_out"], np.float32), g["lr"])
+        assert r["perm"].tolist() != g["perm"]
+    assert np.array_equal(good, np.array(g["out"], dtype=np.float64))

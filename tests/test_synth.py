@@ -1,0 +1,67 @@
+"""Host-side checks of the seeded input generators (no GPU)."""
+import numpy as np
+import pytest
+import torch
+
+from sparse_embedding_lookup_dlrm_amd import synth
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(10000).astype(np.float32) * 0.01,
+                        np.array([1.0, -0.0, 0.0, 3.0e38, 1.00390625, 1.01171875], np.float32)])
+    bits = synth.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(bits, ref)
+
+
+def test_workloads_are_deterministic_and_shaped():
+    w = synth.WORKLOADS["tiny-4t1k-d16-b128"]
+    a = synth.make_batch(w)
+    b = synth.make_batch(w)
+    np.testing.assert_array_equal(a.indices, b.indices)
+    np.testing.assert_array_equal(a.tables[2], b.tables[2])
+    assert a.lengths.shape == (w.T * w.B,) and np.all(a.lengths == 1)
+    assert a.indices.dtype == np.int32 and a.indices.min() >= 0 and a.indices.max() < 1000
+    assert a.e0.shape == (128, 16) and a.e0.dtype == np.float32
+    assert w.P == 10 and w.out_width == 26
+
+
+def test_loguniform_rows_and_zipf_head():
+    w = synth.WORKLOADS["zipf-26t-d128-b2048"]
+    rows = synth.table_rows(w)
+    assert len(rows) == 26 and min(rows) >= 1000 and max(rows) <= 1_000_000
+    lengths = synth.gen_lengths(w)
+    idx = synth.gen_indices(w, rows, lengths)
+    assert len(idx) == 26 * 2048
+    # Row 0 is the hottest: its frequency is close to 1 / H(n, alpha).
+    t0 = idx[:2048]
+    n = rows[0]
+    h = (np.arange(1, n + 1, dtype=np.float64) ** -1.05).sum()
+    p0 = 1.0 / h
+    assert abs((t0 == 0).mean() - p0) < 5 * np.sqrt(p0 * (1 - p0) / 2048) + 1e-3
+    assert t0.max() < n
+
+
+def test_multihot_lengths_and_capacity_lengths():
+    w = synth.WORKLOADS["multihot-8t4m-d64-fp16-b4096"].replace(B=512)
+    L = synth.gen_lengths(w)
+    assert L.min() >= 0 and L.max() <= 100 and abs(L.mean() - 20) < 1.0
+    c = synth.WORKLOADS[synth.CAPACITY].replace(B=256)
+    L = synth.gen_lengths(c)
+    assert L.min() >= 1 and L.max() <= 32 and abs(L.mean() - 16.5) < 0.5
+
+
+def test_zipf_sampler_law_small_support():
+    rng = np.random.default_rng(9)
+    s = synth.sample_zipf(rng, 5, 1.1, 200000)
+    w = np.arange(1, 6, dtype=np.float64) ** -1.1
+    np.testing.assert_allclose(np.bincount(s, minlength=5) / 200000, w / w.sum(), atol=4e-3)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_host_table_dtypes(dtype):
+    w = synth.Workload("t", T=2, rows=10, D=8, dtype=dtype, B=4, bag=("fixed", 1), dist=("uniform",), seed=3)
+    tabs = synth.gen_tables_host(w)
+    want = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
+    assert all(t.dtype == want and t.shape == (10, 8) for t in tabs)
