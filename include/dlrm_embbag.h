@@ -1,0 +1,171 @@
+/*
+ * dlrm_embbag.h -- C ABI of libdlrm_embbag.so, the MI355X (gfx950) hot path of
+ * the DLRM recommendation model: multi-table embedding-bag pooling, the
+ * pairwise dot-product feature interaction, and the sparse embedding backward
+ * with an SGD update.
+ *
+ * Problem statement followed (web pages on DLRM):
+ *   - "DLRM" note (vault-aram.pages.dev/Notes/DLRM), section 2 "The
+ *     Architecture": one embedding table per categorical feature; each
+ *     categorical ID selects one row; dense features pass through a bottom MLP
+ *     whose output e_0 has the embedding dimension.
+ *   - same note, section 3 "The Pairwise Interaction Layer": dot products
+ *     e_i . e_j between the embeddings and e_0, concatenated with e_0. This
+ *     library computes the variant without self-pairs that the section
+ *     mentions: pairs i > j over Z = [e_0, e_1 .. e_T].
+ *   - same note, section 9 "Weaknesses": history (multi-valued) features are
+ *     aggregated before use; here a bag of IDs is sum-pooled.
+ *   - same note, section 5 "Training": the embedding tables are trained; the
+ *     update implemented here is plain SGD on the rows a batch touched.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   T       number of tables (1 <= T <= DLRM_MAX_TABLES)
+ *   B       batch size (samples), B >= 1
+ *   D       embedding dimension; the row of a table is D elements of the table
+ *           dtype, and D * sizeof(dtype) must be a power of two in [16, 1024]
+ *           bytes (fp32: D in {4,8,...,256}; fp16/bf16: D in {8,...,512})
+ *   F = T + 1 vectors per sample (e_0 then the T pooled embeddings)
+ *   P = F (F - 1) / 2 interaction values per sample
+ *   Bags are a single table-major CSR: bag (t, b) is
+ *       indices[offsets[t*B + b] .. offsets[t*B + b + 1])
+ *   i.e. the per-table CSRs laid end to end; offsets has T*B + 1 int32
+ *   entries, offsets[0] = 0 and offsets[T*B] = nnz; indices are int32 row
+ *   numbers in [0, rows[t]).
+ *   Interaction output, per sample b (row-major [B][D + P], fp32):
+ *       out[b][0 .. D)      = e0[b]  (bit copy)
+ *       out[b][D + k]       = Z[b][i] . Z[b][j],  k = i (i - 1) / 2 + j,
+ *                             0 <= j < i < F  (strict lower triangle, row-major)
+ *   Pooled layout: pooled[b][t][d], fp32, [B][T][D].
+ *
+ * Pointers: "device" pointers are HIP device memory (hipMalloc / torch CUDA
+ * tensors) aligned to 16 bytes; "host" pointers are ordinary CPU memory read
+ * during the call only. The caller owns every buffer; the library keeps no
+ * state between calls and allocates no device memory (the backward uses a
+ * caller-provided workspace).
+ *
+ * Ordering: every call only enqueues work on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns without synchronising. Inputs must stay
+ * unchanged, and outputs unread, until the stream has reached the work.
+ *
+ * Errors: argument errors are detected on the host before anything is
+ * enqueued; the call then returns a negative dlrm_status and touches no
+ * output. Data errors (an index outside its table, offsets that are not a
+ * valid CSR) are detected on the device: the kernels never read out of bounds,
+ * an out-of-range index contributes nothing, an invalid offset range counts as
+ * an empty bag, and the matching DLRM_STATUS_* bit is OR-ed into *status
+ * (device int32, may be NULL). The caller clears *status before the call.
+ */
+#ifndef DLRM_EMBBAG_H
+#define DLRM_EMBBAG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DLRM_MAX_TABLES 128
+
+typedef enum {
+  DLRM_OK = 0,
+  DLRM_E_INVAL = -1,       /* NULL where required, non-positive size, inconsistent sizes */
+  DLRM_E_UNSUPPORTED = -2, /* dtype, D or T outside what the kernels handle */
+  DLRM_E_WORKSPACE = -3,   /* workspace smaller than dlrm_embbag_bwd_workspace_bytes() */
+  DLRM_E_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  DLRM_E_ALIGN = -5        /* a device pointer is not 16-byte aligned */
+} dlrm_status;
+
+typedef enum { DLRM_F32 = 0, DLRM_F16 = 1, DLRM_BF16 = 2 } dlrm_dtype;
+
+/* bits OR-ed into the device status word */
+#define DLRM_STATUS_BAD_INDEX 1   /* an index outside [0, rows[t]) */
+#define DLRM_STATUS_BAD_OFFSETS 2 /* offsets[0] != 0, a decrease, an offset outside [0, nnz], offsets[T*B] != nnz,
+                                     or a negative bag length */
+
+/* Human-readable name of a dlrm_status value. Never NULL. */
+const char* dlrm_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int dlrm_version(void);
+
+/*
+ * Bag lengths -> CSR offsets (exclusive prefix sum).
+ *   lengths  device int32 [n]      length of each bag (table-major order)
+ *   offsets  device int32 [n + 1]  out: offsets[0] = 0, offsets[i+1] = offsets[i] + lengths[i]
+ *   n        number of bags (T*B), 0 <= n < 2^31
+ *   status   device int32 or NULL: DLRM_STATUS_BAD_OFFSETS if a length is negative (it then counts
+ *            as 0) or the total exceeds INT32_MAX (offsets are then unspecified)
+ * Uses no workspace: per-chunk totals are parked in `offsets` itself between its three kernels.
+ */
+int dlrm_lengths_to_offsets(int64_t n, const int32_t* lengths, int32_t* offsets, int32_t* status, void* stream);
+
+/*
+ * Embedding-bag forward, optionally fused with the interaction.
+ *   T, B, D, dtype      as above
+ *   tables   host array [T] of device pointers; table t is row-major [rows[t]][D] of dtype
+ *   rows     host int64 [T], 1 <= rows[t] < 2^31
+ *   offsets  device int32 [T*B + 1], indices device int32 [nnz], nnz (host) = offsets[T*B]
+ *   e0       device fp32 [B][D]; required when out_inter != NULL, ignored otherwise
+ *   out_pooled  device fp32 [B][T][D] or NULL: the pooled sums (fp32 accumulation)
+ *   out_inter   device fp32 [B][D + P] or NULL: [e0 | strict-lower dots]; pooled vectors are
+ *               kept on chip between the gather and the dots (nothing else is written)
+ *   At least one of out_pooled / out_inter must be non-NULL.
+ */
+int dlrm_embbag_fwd(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* const* tables,
+                    const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                    const float* e0, float* out_pooled, float* out_inter, int32_t* status, void* stream);
+
+/*
+ * Interaction alone, from pooled vectors in HBM.
+ *   e0 device fp32 [B][D], pooled device fp32 [B][T][D], out device fp32 [B][D + P].
+ */
+int dlrm_interact(int32_t T, int32_t B, int32_t D, const float* e0, const float* pooled, float* out,
+                  void* stream);
+
+/*
+ * Workspace needed by dlrm_embbag_bwd_update for these sizes (bytes, written to *bytes).
+ */
+int dlrm_embbag_bwd_workspace_bytes(int32_t T, int32_t B, int32_t D, int64_t nnz, const int64_t* rows,
+                                    size_t* bytes);
+
+/*
+ * Sparse backward of the forward above followed by an SGD step on the touched rows.
+ *   tables   host array [T] of device pointers, updated in place: for every row r of table t
+ *            that the batch references, W_t[r] <- W_t[r] - lr * G, G = sum over the occurrences
+ *            of (t, r) of dL/dpooled[b][t] (fp32 sum in a fixed order, result rounded to dtype).
+ *            Rows not referenced are not written.
+ *   rows, offsets, indices, nnz   as in the forward (same batch)
+ *   e0       device fp32 [B][D], pooled device fp32 [B][T][D] (the forward's out_pooled)
+ *   d_out    device fp32 [B][D + P]: dL/d(out_inter)
+ *   lr       learning rate
+ *   d_e0     device fp32 [B][D] or NULL: out, dL/de0 = d_out[:, :D] + sum_j g_{0j} Z_j
+ *   unique_keys  device int32 [nnz] or NULL: out, sorted distinct global rows
+ *                (key = rows[0] + ... + rows[t-1] + r) in the first U entries
+ *   seg_offsets  device int32 [nnz + 1] or NULL: out, occurrences of unique_keys[u] are
+ *                perm[seg_offsets[u] .. seg_offsets[u+1]); seg_offsets[U] = nnz
+ *   num_unique   device int32 [1] or NULL: out, U
+ *   perm     device int32 [nnz] or NULL: out, the stable order of occurrences by key
+ *            (ties keep CSR order); this permutation is unique
+ *   workspace, ws_bytes  device scratch of at least dlrm_embbag_bwd_workspace_bytes() bytes
+ * Requires sum(rows) < 2^31. Deterministic: identical inputs give bit-identical outputs.
+ * Occurrences with an out-of-range index are dropped (and flagged).
+ */
+int dlrm_embbag_bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables,
+                           const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                           const float* e0, const float* pooled, const float* d_out, float lr, float* d_e0,
+                           int32_t* unique_keys, int32_t* seg_offsets, int32_t* num_unique, int32_t* perm,
+                           void* workspace, size_t ws_bytes, int32_t* status, void* stream);
+
+/*
+ * Host-side check of a bag description (host arrays): returns the DLRM_STATUS_* bits the
+ * device would report (0 = valid), or a negative dlrm_status for bad arguments.
+ */
+int dlrm_validate_bags(int32_t T, int32_t B, const int64_t* rows, const int32_t* offsets,
+                       const int32_t* indices, int64_t nnz);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLRM_EMBBAG_H */

@@ -125,14 +125,13 @@ def embbag_pool(tables: List[np.ndarray], dtype: str, B: int, offsets: np.ndarra
     rows = [tb.shape[0] for tb in tables]
     check_bags(T, B, rows, offsets, indices)
     D = tables[0].shape[1]
-    W = [decode(tb, dtype) for tb in tables]
     pooled = np.zeros((B, T, D), dtype=np.float64)
     for t in range(T):
         for b in range(B):
             s, e = int(offsets[t * B + b]), int(offsets[t * B + b + 1])
             acc = np.zeros(D, dtype=np.float64)
             for p in range(s, e):
-                acc += W[t][int(indices[p])]
+                acc += decode(tables[t][int(indices[p])], dtype)
             pooled[b, t] = acc
     return pooled
 
@@ -260,10 +259,9 @@ def embbag_bwd_update(tables: List[np.ndarray], dtype: str, B: int, offsets, ind
         for q in range(int(seg[u]), int(seg[u + 1])):
             p = int(perm[q])
             grad[u] += dZ[smp[p], 1 + tab[p]]
-    W = [decode(tb, dtype) for tb in tables]
     new_rows = np.zeros((U, D), dtype=np.float64)
     for u in range(U):
         t = int(tab[perm[int(seg[u])]])
-        new_rows[u] = W[t][int(uniq[u]) - base[t]] - lr * grad[u]
+        new_rows[u] = decode(tables[t][int(uniq[u]) - base[t]], dtype) - lr * grad[u]
     return {"d_e0": bw["d_e0"], "dZ": dZ, "perm": perm, "unique_keys": uniq, "seg_offsets": seg,
             "grad": grad, "new_rows": new_rows, "base": np.array(base, dtype=np.int64)}

@@ -1,0 +1,490 @@
+// Sparse backward of the embedding-bag + interaction forward, then SGD on the
+// touched rows, for gfx950. All kernels are enqueued on one stream with no host
+// synchronisation; the number of distinct rows stays on the device.
+//
+// 1. interaction backward: the gradient of Z[i].Z[j] with respect to Z[i] is
+//    Z[j], so dZ[b] = S[b] Z[b] with S[b] the symmetric F x F matrix holding the
+//    upstream gradient of pair (i, j) at (i, j) and (j, i), zero diagonal;
+//    dL/dpooled[b][t] = dZ[b][1 + t], dL/de0[b] = d_out[b][:D] + dZ[b][0].
+// 2. keys: occurrence p of bag (t, b) gets key base_t + index (its global row)
+//    and value p; an out-of-range index gets the sentinel key sum(rows).
+// 3. stable LSD radix sort of (key, p), 8 bits per pass: per-tile digit counts,
+//    a device-wide scan of the digit-major count table, a stable scatter that
+//    ranks equal digits inside a wave with ballots.
+// 4. segments: head flags (key differs from its predecessor), scanned into the
+//    position of each distinct key.
+// 5. one wave per distinct row: sum the rows dL/dpooled of its occurrences in
+//    sorted order (fixed order, so the result is deterministic), then
+//    W <- W - lr * G in fp32, rounded once to the table's storage type.
+#include <algorithm>
+
+#include "scan_impl.h"
+
+namespace dlrm {
+
+constexpr int kBwdThreads = 256;
+constexpr int kRadixBits = 8;
+constexpr int kRadixBins = 1 << kRadixBits;
+constexpr int kRadixPerThread = 8;
+constexpr int kRadixTile = kBwdThreads * kRadixPerThread;  // 2048 keys per tile
+constexpr int kRadixWaves = kBwdThreads / kWave;
+constexpr int kRadixRounds = kRadixTile / kRadixWaves / kWave;  // rounds of 64 keys per wave
+
+// ---------------------------------------------------------------------------
+// 1. interaction backward
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B, int D,
+                                                                   const float* __restrict__ e0,
+                                                                   const float* __restrict__ pooled,
+                                                                   const float* __restrict__ d_out,
+                                                                   float* __restrict__ d_pooled,
+                                                                   float* __restrict__ d_e0) {
+  extern __shared__ __align__(16) float smem[];
+  const int F = T + 1;
+  const int LD = D + 4;
+  const int W = D + F * (F - 1) / 2;
+  float* Z = smem;                // [F][LD]
+  float* S = smem + F * LD;       // [F][F]
+  const int b = xcd_block(blockIdx.x, gridDim.x);
+  const int D4 = D / 4;
+  for (int i = threadIdx.x; i < F * D4; i += kBwdThreads) {
+    const int f = i / D4, d = (i - f * D4) * 4;
+    const float4 v = f == 0 ? *reinterpret_cast<const float4*>(e0 + static_cast<size_t>(b) * D + d)
+                            : *reinterpret_cast<const float4*>(pooled + (static_cast<size_t>(b) * T + f - 1) * D + d);
+    *reinterpret_cast<float4*>(Z + f * LD + d) = v;
+  }
+  const float* g = d_out + static_cast<size_t>(b) * W + D;
+  for (int i = threadIdx.x; i < F * F; i += kBwdThreads) {
+    const int r = i / F, c = i - r * F;
+    float v = 0.f;
+    if (r > c) v = g[r * (r - 1) / 2 + c];
+    else if (c > r) v = g[c * (c - 1) / 2 + r];
+    S[i] = v;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < F * D4; i += kBwdThreads) {
+    const int f = i / D4, d = (i - f * D4) * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* srow = S + f * F;
+    for (int j = 0; j < F; ++j) {
+      const float s = srow[j];
+      const float4 z = *reinterpret_cast<const float4*>(Z + j * LD + d);
+      acc.x = fmaf(s, z.x, acc.x);
+      acc.y = fmaf(s, z.y, acc.y);
+      acc.z = fmaf(s, z.z, acc.z);
+      acc.w = fmaf(s, z.w, acc.w);
+    }
+    if (f == 0) {
+      if (d_e0) {
+        const float4 go = make_float4(d_out[static_cast<size_t>(b) * W + d], d_out[static_cast<size_t>(b) * W + d + 1],
+                                      d_out[static_cast<size_t>(b) * W + d + 2], d_out[static_cast<size_t>(b) * W + d + 3]);
+        *reinterpret_cast<float4*>(d_e0 + static_cast<size_t>(b) * D + d) =
+            make_float4(go.x + acc.x, go.y + acc.y, go.z + acc.z, go.w + acc.w);
+      }
+    } else {
+      *reinterpret_cast<float4*>(d_pooled + (static_cast<size_t>(b) * T + f - 1) * D + d) = acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. keys (one thread per bag, table-major bag order = CSR order)
+// ---------------------------------------------------------------------------
+// Occurrences no bag covers (possible only with invalid offsets) keep the sentinel key.
+__global__ __launch_bounds__(kBwdThreads) void fill_sentinel(int32_t* __restrict__ keys, int32_t* __restrict__ vals,
+                                                             int32_t* __restrict__ bag_of, long long n,
+                                                             int32_t sentinel) {
+  const long long i = static_cast<long long>(blockIdx.x) * kBwdThreads + threadIdx.x;
+  if (i < n) {
+    keys[i] = sentinel;
+    vals[i] = static_cast<int32_t>(i);
+    bag_of[i] = 0;
+  }
+}
+
+__global__ __launch_bounds__(kBwdThreads) void build_keys(MutTableArgs tabs, int T, int B, const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ indices, long long nnz,
+                                                          int32_t sentinel, int32_t* __restrict__ keys,
+                                                          int32_t* __restrict__ vals, int32_t* __restrict__ bag_of,
+                                                          int32_t* status) {
+  const long long j = static_cast<long long>(blockIdx.x) * kBwdThreads + threadIdx.x;
+  if (j >= static_cast<long long>(T) * B) return;
+  const int t = static_cast<int>(j / B), b = static_cast<int>(j - static_cast<long long>(t) * B);
+  long long s0 = offsets[j], s1 = offsets[j + 1];
+  bool bad_off = false;
+  if (j == 0 && s0 != 0) bad_off = true;
+  if (j == static_cast<long long>(T) * B - 1 && s1 != nnz) bad_off = true;
+  if (s0 < 0) { s0 = 0; bad_off = true; }
+  if (s0 > nnz) { s0 = nnz; bad_off = true; }
+  if (s1 > nnz) { s1 = nnz; bad_off = true; }
+  if (s1 < s0) { s1 = s0; bad_off = true; }
+  if (bad_off) flag(status, DLRM_STATUS_BAD_OFFSETS);
+  const int rows = tabs.rows[t], base = tabs.base[t];
+  const int bag = b * T + t;
+  bool bad_idx = false;
+  for (long long p = s0; p < s1; ++p) {
+    const int r = indices[p];
+    int key = sentinel;
+    if (r >= 0 && r < rows) key = base + r;
+    else bad_idx = true;
+    keys[p] = key;
+    vals[p] = static_cast<int32_t>(p);
+    bag_of[p] = bag;
+  }
+  if (bad_idx) flag(status, DLRM_STATUS_BAD_INDEX);
+}
+
+// ---------------------------------------------------------------------------
+// 3. radix sort
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBwdThreads) void radix_count(const int32_t* __restrict__ keys, long long n, int shift,
+                                                           int ntiles, int32_t* __restrict__ counts) {
+  __shared__ int hist[kRadixBins];
+  hist[threadIdx.x] = 0;
+  __syncthreads();
+  const long long base = static_cast<long long>(blockIdx.x) * kRadixTile;
+#pragma unroll
+  for (int k = 0; k < kRadixPerThread; ++k) {
+    const long long i = base + k * kBwdThreads + threadIdx.x;
+    if (i < n) atomicAdd(&hist[(static_cast<uint32_t>(keys[i]) >> shift) & (kRadixBins - 1)], 1);
+  }
+  __syncthreads();
+  counts[static_cast<long long>(threadIdx.x) * ntiles + blockIdx.x] = hist[threadIdx.x];
+}
+
+// Stable scatter of one tile. Wave w owns keys [tile + w*512, +512) and walks
+// them in rounds of 64 in their original order; equal digits inside a round
+// are ranked by lane with ballots, and a per-wave running count per digit
+// carries the rank across rounds.
+__global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __restrict__ keys_in,
+                                                             const int32_t* __restrict__ vals_in, long long n,
+                                                             int shift, int ntiles,
+                                                             const int32_t* __restrict__ digit_off,
+                                                             int32_t* __restrict__ keys_out,
+                                                             int32_t* __restrict__ vals_out) {
+  __shared__ int wcount[kRadixWaves][kRadixBins];
+  __shared__ int gbase[kRadixBins];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  for (int w = 0; w < kRadixWaves; ++w) wcount[w][threadIdx.x] = 0;
+  gbase[threadIdx.x] = digit_off[static_cast<long long>(threadIdx.x) * ntiles + blockIdx.x];
+  __syncthreads();
+  const long long sub = static_cast<long long>(blockIdx.x) * kRadixTile + static_cast<long long>(wave) * kRadixRounds * kWave;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int key[kRadixRounds], val[kRadixRounds], dig[kRadixRounds], rank[kRadixRounds];
+#pragma unroll
+  for (int r = 0; r < kRadixRounds; ++r) {
+    const long long i = sub + r * kWave + lane;
+    const bool ok = i < n;
+    key[r] = ok ? keys_in[i] : 0;
+    val[r] = ok ? vals_in[i] : 0;
+    const int d = (static_cast<uint32_t>(key[r]) >> shift) & (kRadixBins - 1);
+    dig[r] = ok ? d : -1;
+    unsigned long long peers = __ballot(ok);
+#pragma unroll
+    for (int bit = 0; bit < kRadixBits; ++bit) {
+      const unsigned long long m = __ballot((d >> bit) & 1);
+      peers &= ((d >> bit) & 1) ? m : ~m;
+    }
+    const int before = __popcll(peers & lt);
+    const int cnt = __popcll(peers);
+    int running = 0;
+    if (ok) running = wcount[wave][d];
+    __builtin_amdgcn_wave_barrier();
+    if (ok && before == 0) wcount[wave][d] = running + cnt;
+    __builtin_amdgcn_wave_barrier();
+    rank[r] = running + before;
+  }
+  __syncthreads();
+  {
+    int acc = 0;
+    for (int w = 0; w < kRadixWaves; ++w) {
+      const int c = wcount[w][threadIdx.x];
+      wcount[w][threadIdx.x] = acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kRadixRounds; ++r) {
+    if (dig[r] < 0) continue;
+    const int dst = gbase[dig[r]] + wcount[wave][dig[r]] + rank[r];
+    keys_out[dst] = key[r];
+    vals_out[dst] = val[r];
+  }
+}
+
+struct CountsIn {
+  const int32_t* p;
+  __device__ __forceinline__ long long operator()(long long i) const { return p[i]; }
+};
+
+struct HeadIn {
+  const int32_t* keys;
+  int32_t sentinel;
+  __device__ __forceinline__ long long operator()(long long i) const {
+    const int32_t k = keys[i];
+    return (k != sentinel && (i == 0 || keys[i - 1] != k)) ? 1 : 0;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// 4. segments
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBwdThreads) void build_segments(const int32_t* __restrict__ keys, long long n,
+                                                              int32_t sentinel, const int32_t* __restrict__ pos,
+                                                              int32_t* __restrict__ unique_keys,
+                                                              int32_t* __restrict__ seg_offsets,
+                                                              int32_t* __restrict__ num_unique) {
+  const long long i = static_cast<long long>(blockIdx.x) * kBwdThreads + threadIdx.x;
+  if (i >= n) return;
+  const int32_t k = keys[i];
+  const bool valid = k != sentinel;
+  if (valid && (i == 0 || keys[i - 1] != k)) {
+    unique_keys[pos[i]] = k;
+    seg_offsets[pos[i]] = static_cast<int32_t>(i);
+  }
+  // the last valid key closes the segment list
+  const bool last_valid = valid && (i + 1 == n || keys[i + 1] == sentinel);
+  const bool none_valid = i == 0 && !valid;
+  if (last_valid || none_valid) {
+    const int32_t U = pos[n];
+    seg_offsets[U] = last_valid ? static_cast<int32_t>(i + 1) : 0;
+    *num_unique = U;
+  }
+}
+
+__global__ void zero_segments(int32_t* seg_offsets, int32_t* num_unique) {
+  if (threadIdx.x == 0) {
+    seg_offsets[0] = 0;
+    *num_unique = 0;
+  }
+}
+
+__global__ __launch_bounds__(kBwdThreads) void copy_i32(const int32_t* __restrict__ a, int32_t* __restrict__ b, long long n) {
+  const long long i = static_cast<long long>(blockIdx.x) * kBwdThreads + threadIdx.x;
+  if (i < n) b[i] = a[i];
+}
+
+// ---------------------------------------------------------------------------
+// 5. segmented reduce + SGD: one wave per distinct row
+// ---------------------------------------------------------------------------
+template <int DT, int D4>
+__global__ __launch_bounds__(kBwdThreads) void reduce_sgd(MutTableArgs tabs, int T, const int32_t* __restrict__ unique_keys,
+                                                          const int32_t* __restrict__ seg_offsets,
+                                                          const int32_t* __restrict__ num_unique,
+                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ bag_of,
+                                                          const float* __restrict__ d_pooled, float lr) {
+  constexpr int LPR = D4 < kWave ? D4 : kWave;  // lanes per row, one float4 each per step
+  constexpr int V = D4 / LPR;                   // float4 per lane
+  constexpr int R = kWave / LPR;                // occurrences summed in parallel
+  constexpr int D = D4 * 4;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int grp = lane / LPR, sub = lane % LPR;
+  const int U = *num_unique;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int u = blockIdx.x * (kBwdThreads / kWave) + wave; u < U; u += gridDim.x * (kBwdThreads / kWave)) {
+    const int q0 = seg_offsets[u], q1 = seg_offsets[u + 1];
+    float4 acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = q0 + grp; q < q1; q += R) {
+      const int bag = bag_of[perm[q]];
+      const float* row = d_pooled + static_cast<size_t>(bag) * D + sub * 4;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const float4 x = *reinterpret_cast<const float4*>(row + v * LPR * 4);
+        acc[v].x += x.x; acc[v].y += x.y; acc[v].z += x.z; acc[v].w += x.w;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+      for (int m = LPR; m < kWave; m <<= 1) {
+        acc[v].x += shfl_xor_f(acc[v].x, m);
+        acc[v].y += shfl_xor_f(acc[v].y, m);
+        acc[v].z += shfl_xor_f(acc[v].z, m);
+        acc[v].w += shfl_xor_f(acc[v].w, m);
+      }
+    if (lane >= LPR) continue;
+    const int key = unique_keys[u];
+    int t = 0;
+    for (int k = 1; k < T; ++k)
+      if (tabs.base[k] <= key) t = k;
+    const int r = key - tabs.base[t];
+    const float nlr = -lr;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int d = v * LPR * 4 + sub * 4;
+      if constexpr (DT == DLRM_F32) {
+        float4* w = reinterpret_cast<float4*>(static_cast<float*>(tabs.ptr[t]) + static_cast<size_t>(r) * D + d);
+        float4 x = *w;
+        x.x = fmaf(nlr, acc[v].x, x.x);
+        x.y = fmaf(nlr, acc[v].y, x.y);
+        x.z = fmaf(nlr, acc[v].z, x.z);
+        x.w = fmaf(nlr, acc[v].w, x.w);
+        *w = x;
+      } else {
+        uint2* w = reinterpret_cast<uint2*>(static_cast<uint16_t*>(tabs.ptr[t]) + static_cast<size_t>(r) * D + d);
+        uint2 x = *w;
+        float f0, f1, f2, f3;
+        if constexpr (DT == DLRM_BF16) {
+          f0 = bf16_lo(x.x); f1 = bf16_hi(x.x); f2 = bf16_lo(x.y); f3 = bf16_hi(x.y);
+        } else {
+          f0 = f16_lo(x.x); f1 = f16_hi(x.x); f2 = f16_lo(x.y); f3 = f16_hi(x.y);
+        }
+        f0 = fmaf(nlr, acc[v].x, f0);
+        f1 = fmaf(nlr, acc[v].y, f1);
+        f2 = fmaf(nlr, acc[v].z, f2);
+        f3 = fmaf(nlr, acc[v].w, f3);
+        x.x = static_cast<uint32_t>(to_half_bits<DT>(f0)) | (static_cast<uint32_t>(to_half_bits<DT>(f1)) << 16);
+        x.y = static_cast<uint32_t>(to_half_bits<DT>(f2)) | (static_cast<uint32_t>(to_half_bits<DT>(f3)) << 16);
+        *w = x;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+  size_t d_pooled, keys_a, keys_b, vals_a, vals_b, bag_of, counts, digit_off, partial, pos, uniq, seg, nuniq, total;
+};
+
+int radix_passes(int64_t total_rows) {
+  int bits = 0;
+  while ((1ll << bits) <= total_rows) ++bits;  // sentinel key = total_rows must fit
+  return (bits + kRadixBits - 1) / kRadixBits;
+}
+
+WsLayout layout(int T, int B, int D, int64_t nnz) {
+  WsLayout L{};
+  const size_t n = static_cast<size_t>(nnz);
+  const size_t ntiles = (n + kRadixTile - 1) / kRadixTile;
+  const size_t ncounts = ntiles * kRadixBins;
+  const size_t scan_max = std::max(n, ncounts) + 1;
+  size_t o = 0;
+  L.d_pooled = o; o = align_up(o + static_cast<size_t>(B) * T * D * 4);
+  L.keys_a = o; o = align_up(o + n * 4);
+  L.keys_b = o; o = align_up(o + n * 4);
+  L.vals_a = o; o = align_up(o + n * 4);
+  L.vals_b = o; o = align_up(o + n * 4);
+  L.bag_of = o; o = align_up(o + n * 4);
+  L.counts = o; o = align_up(o + ncounts * 4);
+  L.digit_off = o; o = align_up(o + (ncounts + 1) * 4);
+  L.partial = o; o = align_up(o + (scan_chunks(static_cast<long long>(scan_max)) + 1) * 8);
+  L.pos = o; o = align_up(o + (n + 1) * 4);
+  L.uniq = o; o = align_up(o + n * 4);
+  L.seg = o; o = align_up(o + (n + 1) * 4);
+  L.nuniq = o; o = align_up(o + 4);
+  L.total = o;
+  return L;
+}
+
+template <int DT>
+hipError_t launch_reduce_dt(const BwdArgs& a, const int32_t* uniq, const int32_t* seg, const int32_t* nuniq,
+                            const int32_t* perm, const int32_t* bag_of, const float* d_pooled, hipStream_t st) {
+  long long grid = (a.nnz + 3) / 4;
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+  const dim3 g(static_cast<unsigned>(grid)), blk(kBwdThreads);
+  switch (a.D / 4) {
+    case 1: hipLaunchKernelGGL((reduce_sgd<DT, 1>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
+    case 2: hipLaunchKernelGGL((reduce_sgd<DT, 2>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
+    case 4: hipLaunchKernelGGL((reduce_sgd<DT, 4>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
+    case 8: hipLaunchKernelGGL((reduce_sgd<DT, 8>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
+    case 16: hipLaunchKernelGGL((reduce_sgd<DT, 16>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
+    case 32: hipLaunchKernelGGL((reduce_sgd<DT, 32>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
+    case 64: hipLaunchKernelGGL((reduce_sgd<DT, 64>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
+    case 128: hipLaunchKernelGGL((reduce_sgd<DT, 128>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int T, int B, int D, int64_t nnz, int64_t /*total_rows*/) {
+  return layout(T, B, D, nnz).total;
+}
+
+hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
+  const WsLayout L = layout(a.T, a.B, a.D, a.nnz);
+  char* ws = static_cast<char*>(a.workspace);
+  float* d_pooled = reinterpret_cast<float*>(ws + L.d_pooled);
+  int32_t* keys[2] = {reinterpret_cast<int32_t*>(ws + L.keys_a), reinterpret_cast<int32_t*>(ws + L.keys_b)};
+  int32_t* vals[2] = {reinterpret_cast<int32_t*>(ws + L.vals_a), reinterpret_cast<int32_t*>(ws + L.vals_b)};
+  int32_t* bag_of = reinterpret_cast<int32_t*>(ws + L.bag_of);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* digit_off = reinterpret_cast<int32_t*>(ws + L.digit_off);
+  long long* partial = reinterpret_cast<long long*>(ws + L.partial);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  int32_t* uniq = a.unique_keys ? a.unique_keys : reinterpret_cast<int32_t*>(ws + L.uniq);
+  int32_t* seg = a.seg_offsets ? a.seg_offsets : reinterpret_cast<int32_t*>(ws + L.seg);
+  int32_t* nuniq = a.num_unique ? a.num_unique : reinterpret_cast<int32_t*>(ws + L.nuniq);
+
+  // 1. interaction backward
+  {
+    const int F = a.T + 1;
+    const size_t lds = (static_cast<size_t>(F) * (a.D + 4) + static_cast<size_t>(F) * F) * 4;
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(interact_bwd_kernel, dim3(a.B), dim3(kBwdThreads), lds, st, a.T, a.B, a.D, a.e0, a.pooled,
+                       a.d_out, d_pooled, a.d_e0);
+  }
+  const long long n = a.nnz;
+  if (n == 0) {
+    hipLaunchKernelGGL(zero_segments, dim3(1), dim3(64), 0, st, seg, nuniq);
+    return hipGetLastError();
+  }
+  const int32_t sentinel = static_cast<int32_t>(a.total_rows);
+  // 2. keys
+  hipLaunchKernelGGL(fill_sentinel, dim3(static_cast<unsigned>((n + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads), 0,
+                     st, keys[0], vals[0], bag_of, n, sentinel);
+  {
+    const long long nb = static_cast<long long>(a.T) * a.B;
+    hipLaunchKernelGGL(build_keys, dim3(static_cast<unsigned>((nb + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads), 0,
+                       st, a.tabs, a.T, a.B, a.offsets, a.indices, n, sentinel, keys[0], vals[0], bag_of, a.status);
+  }
+  // 3. radix sort, 8 bits per pass
+  const int ntiles = static_cast<int>((n + kRadixTile - 1) / kRadixTile);
+  const int passes = radix_passes(a.total_rows);
+  int cur = 0;
+  for (int p = 0; p < passes; ++p) {
+    const int shift = p * kRadixBits;
+    hipLaunchKernelGGL(radix_count, dim3(ntiles), dim3(kBwdThreads), 0, st, keys[cur], n, shift, ntiles, counts);
+    hipError_t e = device_exclusive_scan(CountsIn{counts}, static_cast<long long>(ntiles) * kRadixBins, digit_off,
+                                         partial, a.status, 0, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(radix_scatter, dim3(ntiles), dim3(kBwdThreads), 0, st, keys[cur], vals[cur], n, shift, ntiles,
+                       digit_off, keys[cur ^ 1], vals[cur ^ 1]);
+    cur ^= 1;
+  }
+  const int32_t* skeys = keys[cur];
+  const int32_t* perm = vals[cur];
+  if (a.perm) {
+    hipLaunchKernelGGL(copy_i32, dim3(static_cast<unsigned>((n + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads), 0, st,
+                       perm, a.perm, n);
+  }
+  // 4. segments
+  {
+    hipError_t e = device_exclusive_scan(HeadIn{skeys, sentinel}, n, pos, partial, a.status, 0, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(build_segments, dim3(static_cast<unsigned>((n + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads),
+                       0, st, skeys, n, sentinel, pos, uniq, seg, nuniq);
+  }
+  // 5. reduce + SGD
+  switch (a.dtype) {
+    case DLRM_F32: return launch_reduce_dt<DLRM_F32>(a, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
+    case DLRM_F16: return launch_reduce_dt<DLRM_F16>(a, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
+    case DLRM_BF16: return launch_reduce_dt<DLRM_BF16>(a, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dlrm

@@ -1,0 +1,70 @@
+// Host-side interface between the C ABI (api.cpp) and the kernel launchers.
+// Plain C++: no device code, so api.cpp builds as host code.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dlrm_embbag.h"
+
+namespace dlrm {
+
+// Table pointers and row counts travel in the kernel arguments (1.5 KB for 128 tables),
+// so a wave picks its table with a scalar load from the argument segment.
+struct TableArgs {
+  const void* ptr[DLRM_MAX_TABLES];
+  int32_t rows[DLRM_MAX_TABLES];
+};
+
+struct MutTableArgs {
+  void* ptr[DLRM_MAX_TABLES];
+  int32_t rows[DLRM_MAX_TABLES];
+  int32_t base[DLRM_MAX_TABLES];  // first global key of each table
+};
+
+struct FwdArgs {
+  int T, B, D, dtype;
+  TableArgs tabs;
+  const int32_t* offsets;
+  const int32_t* indices;
+  int64_t nnz;
+  const float* e0;
+  float* out_pooled;
+  float* out_inter;
+  int32_t* status;
+};
+
+hipError_t launch_embbag_fwd(const FwdArgs& a, hipStream_t s);
+hipError_t launch_interact(int T, int B, int D, const float* e0, const float* pooled, float* out, hipStream_t s);
+hipError_t launch_lengths_to_offsets(int64_t n, const int32_t* lengths, int32_t* offsets, int32_t* status,
+                                     hipStream_t s);
+
+struct BwdArgs {
+  int T, B, D, dtype;
+  MutTableArgs tabs;
+  int64_t total_rows;
+  const int32_t* offsets;
+  const int32_t* indices;
+  int64_t nnz;
+  const float* e0;
+  const float* pooled;
+  const float* d_out;
+  float lr;
+  float* d_e0;
+  int32_t* unique_keys;
+  int32_t* seg_offsets;
+  int32_t* num_unique;
+  int32_t* perm;
+  void* workspace;
+  size_t ws_bytes;
+  int32_t* status;
+};
+
+size_t bwd_workspace_bytes(int T, int B, int D, int64_t nnz, int64_t total_rows);
+hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t s);
+
+// shared by forward and backward: fused/standalone interaction tile sizes
+int fwd_supported_row_bytes(int D, int dtype);
+
+}  // namespace dlrm

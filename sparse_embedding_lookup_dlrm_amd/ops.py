@@ -1,0 +1,216 @@
+"""Thin ctypes binding over libdlrm_embbag.so (C ABI: include/dlrm_embbag.h).
+
+Only argument marshalling happens here: torch supplies device memory and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels. The names mirror the C entry points. If the library is missing or
+cannot be loaded, every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdlrm_embbag.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dlrm_embbag.h")
+
+DLRM_F32, DLRM_F16, DLRM_BF16 = 0, 1, 2
+STATUS_BAD_INDEX = 1
+STATUS_BAD_OFFSETS = 2
+MAX_TABLES = 128
+
+_TORCH_DT = {torch.float32: DLRM_F32, torch.float16: DLRM_F16, torch.bfloat16: DLRM_BF16}
+
+_c_void_p = ctypes.c_void_p
+_i32, _i64, _f32, _size_t = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_P = ctypes.POINTER
+
+_SIGNATURES = {
+    "dlrm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dlrm_version": (ctypes.c_int, []),
+    "dlrm_lengths_to_offsets": (ctypes.c_int, [_i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "dlrm_embbag_fwd": (ctypes.c_int, [_i32, _i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p, _c_void_p, _i64,
+                                       _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "dlrm_interact": (ctypes.c_int, [_i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "dlrm_embbag_bwd_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i64, _P(_i64), _P(_size_t)]),
+    "dlrm_embbag_bwd_update": (ctypes.c_int, [_i32, _i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p, _c_void_p,
+                                              _i64, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p, _c_void_p,
+                                              _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p,
+                                              _c_void_p]),
+    "dlrm_validate_bags": (ctypes.c_int, [_i32, _i32, _P(_i64), _P(_i32), _P(_i32), _i64]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class DlrmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {status_string(code)} ({code})")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdlrm_embbag.so (built in-tree). Raises if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m sparse_embedding_lookup_dlrm_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def header_functions() -> List[str]:
+    """Names of the functions declared in include/dlrm_embbag.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dlrm_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_string(code: int) -> str:
+    return lib().dlrm_status_string(code).decode()
+
+
+def version() -> int:
+    return lib().dlrm_version()
+
+
+def _check(code: int, where: str) -> None:
+    if code != 0:
+        raise DlrmError(code, where)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("device tensors must be contiguous CUDA (HIP) tensors")
+
+
+def _table_args(tables: Sequence[torch.Tensor]):
+    T = len(tables)
+    if T < 1:
+        raise ValueError("need at least one table")
+    dt = tables[0].dtype
+    if dt not in _TORCH_DT:
+        raise ValueError(f"unsupported table dtype {dt}")
+    D = tables[0].shape[1]
+    for t in tables:
+        if t.dtype != dt or t.dim() != 2 or t.shape[1] != D:
+            raise ValueError("all tables must be 2-D with the same dtype and width")
+    _require_cuda(*tables)
+    ptrs = (_c_void_p * T)(*[t.data_ptr() for t in tables])
+    rows = (_i64 * T)(*[t.shape[0] for t in tables])
+    return T, D, _TORCH_DT[dt], ptrs, rows
+
+
+def pair_count(T: int) -> int:
+    F = T + 1
+    return F * (F - 1) // 2
+
+
+def lengths_to_offsets(lengths: torch.Tensor, offsets: Optional[torch.Tensor] = None,
+                       status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """int32 bag lengths (device) -> int32 CSR offsets (device, n + 1 entries)."""
+    _require_cuda(lengths)
+    assert lengths.dtype == torch.int32
+    n = lengths.numel()
+    if offsets is None:
+        offsets = torch.empty(n + 1, dtype=torch.int32, device=lengths.device)
+    _check(lib().dlrm_lengths_to_offsets(n, _ptr(lengths), _ptr(offsets), _ptr(status), _stream(stream)),
+           "dlrm_lengths_to_offsets")
+    return offsets
+
+
+def embbag_fwd(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: torch.Tensor, B: int,
+               e0: Optional[torch.Tensor] = None, *, want_pooled: bool = False, want_inter: bool = True,
+               out_pooled: Optional[torch.Tensor] = None, out_inter: Optional[torch.Tensor] = None,
+               status: Optional[torch.Tensor] = None, stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Embedding-bag forward; returns (pooled [B,T,D] or None, [e0 | dots] [B, D+P] or None)."""
+    T, D, dt, ptrs, rows = _table_args(tables)
+    _require_cuda(offsets, indices, e0, out_pooled, out_inter, status)
+    assert offsets.dtype == torch.int32 and indices.dtype == torch.int32
+    if offsets.numel() != T * B + 1:
+        raise ValueError("offsets must have T*B + 1 entries")
+    dev = tables[0].device
+    if want_pooled and out_pooled is None:
+        out_pooled = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    if want_inter and out_inter is None:
+        out_inter = torch.empty((B, D + pair_count(T)), dtype=torch.float32, device=dev)
+    _check(lib().dlrm_embbag_fwd(T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(), _ptr(e0),
+                                 _ptr(out_pooled), _ptr(out_inter), _ptr(status), _stream(stream)),
+           "dlrm_embbag_fwd")
+    return out_pooled, out_inter
+
+
+def interact(e0: torch.Tensor, pooled: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """[e0 | strict-lower dots of Z = [e0; pooled]] from pooled [B, T, D] fp32."""
+    _require_cuda(e0, pooled, out)
+    B, T, D = pooled.shape
+    if out is None:
+        out = torch.empty((B, D + pair_count(T)), dtype=torch.float32, device=pooled.device)
+    _check(lib().dlrm_interact(T, B, D, _ptr(e0), _ptr(pooled), _ptr(out), _stream(stream)), "dlrm_interact")
+    return out
+
+
+def bwd_workspace_bytes(T: int, B: int, D: int, nnz: int, rows: Sequence[int]) -> int:
+    r = (_i64 * T)(*rows)
+    out = _size_t(0)
+    _check(lib().dlrm_embbag_bwd_workspace_bytes(T, B, D, nnz, r, ctypes.byref(out)),
+           "dlrm_embbag_bwd_workspace_bytes")
+    return out.value
+
+
+def embbag_bwd_update(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: torch.Tensor, B: int,
+                      e0: torch.Tensor, pooled: torch.Tensor, d_out: torch.Tensor, lr: float, *,
+                      want_d_e0: bool = True, want_segments: bool = True, workspace: Optional[torch.Tensor] = None,
+                      status: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Sparse backward + SGD on the touched rows (tables are updated in place)."""
+    T, D, dt, ptrs, rows = _table_args(tables)
+    _require_cuda(offsets, indices, e0, pooled, d_out, workspace, status)
+    nnz = indices.numel()
+    dev = tables[0].device
+    need = bwd_workspace_bytes(T, B, D, nnz, [t.shape[0] for t in tables])
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    res = {"d_e0": torch.empty((B, D), dtype=torch.float32, device=dev) if want_d_e0 else None}
+    if want_segments:
+        res["unique_keys"] = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+        res["seg_offsets"] = torch.empty(nnz + 1, dtype=torch.int32, device=dev)
+        res["num_unique"] = torch.empty(1, dtype=torch.int32, device=dev)
+        res["perm"] = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+    g = res.get
+    _check(lib().dlrm_embbag_bwd_update(T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), nnz, _ptr(e0),
+                                        _ptr(pooled), _ptr(d_out), float(lr), _ptr(g("d_e0")),
+                                        _ptr(g("unique_keys")), _ptr(g("seg_offsets")), _ptr(g("num_unique")),
+                                        _ptr(g("perm")), _ptr(workspace), workspace.numel(), _ptr(status),
+                                        _stream(stream)),
+           "dlrm_embbag_bwd_update")
+    return res
+
+
+def validate_bags(T: int, B: int, rows: Sequence[int], offsets, indices) -> int:
+    """Host check of a bag description (numpy/int sequences); returns the status bits."""
+    import numpy as np
+
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    r = (_i64 * T)(*rows)
+    return lib().dlrm_validate_bags(T, B, r, off.ctypes.data_as(_P(_i32)), idx.ctypes.data_as(_P(_i32)), len(idx))

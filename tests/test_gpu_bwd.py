@@ -1,0 +1,125 @@
+"""GPU parity of the sparse backward + SGD update against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dlrm_oracle as orc
+from sparse_embedding_lookup_dlrm_amd import ops, synth
+
+from gpu_util import DeviceBatch, RTOL, abs_tables, assert_mag_close, host_tables, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _round_storage(x64, dtype):
+    x32 = torch.from_numpy(np.asarray(x64, dtype=np.float32))
+    if dtype == "f32":
+        return x32.numpy()
+    if dtype == "f16":
+        return x64.astype(np.float32).astype(np.float16)
+    return x32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def run_bwd(w: synth.Workload, lr=0.01, exact=False, twice=False):
+    b = synth.make_batch(w, with_dout=True)
+    db = DeviceBatch(b)
+    pooled, _ = db.fwd(want_pooled=True)
+    d_out = torch.from_numpy(b.dout).cuda()
+    before = [t.clone() for t in db.tables]
+    res = ops.embbag_bwd_update(db.tables, db.offsets, db.indices, w.B, db.e0, pooled, d_out, lr, status=db.status)
+    torch.cuda.synchronize()
+    assert db.status.item() == 0
+    if twice:
+        tabs2 = [t.clone() for t in before]
+        res2 = ops.embbag_bwd_update(tabs2, db.offsets, db.indices, w.B, db.e0, pooled, d_out, lr)
+        torch.cuda.synchronize()
+        for k in ("d_e0", "perm", "unique_keys", "seg_offsets", "num_unique"):
+            assert torch.equal(res[k], res2[k]), k
+        for t1, t2 in zip(db.tables, tabs2):
+            assert torch.equal(t1.view(torch.int16) if t1.dtype != torch.float32 else t1,
+                               t2.view(torch.int16) if t2.dtype != torch.float32 else t2)
+
+    # oracle (own pooled, own offsets)
+    off = orc.lengths_to_offsets(b.lengths)
+    fwd = orc.embbag_fwd(b.tables, w.dtype, w.B, off, b.indices, b.e0)
+    r = orc.embbag_bwd_update(b.tables, w.dtype, w.B, off, b.indices, b.e0, fwd["pooled"], b.dout, lr)
+    # magnitudes: the same computation on absolute values
+    at = abs_tables(b.tables, w.dtype)
+    pm = orc.embbag_pool(at, w.dtype, w.B, off, b.indices)
+    rm = orc.embbag_bwd_update(at, w.dtype, w.B, off, b.indices, np.abs(b.e0), pm, np.abs(b.dout), lr)
+
+    U = int(res["num_unique"].item())
+    nnz = len(b.indices)
+    assert U == len(r["unique_keys"])
+    np.testing.assert_array_equal(res["perm"].cpu().numpy()[:nnz], r["perm"].astype(np.int32))
+    np.testing.assert_array_equal(res["unique_keys"].cpu().numpy()[:U], r["unique_keys"].astype(np.int32))
+    np.testing.assert_array_equal(res["seg_offsets"].cpu().numpy()[:U + 1], r["seg_offsets"].astype(np.int32))
+    rtol = 0.0 if exact else RTOL[w.dtype]
+    de0_mag = np.abs(b.dout[:, :w.D]) + rm["dZ"][:, 0]
+    assert_mag_close(res["d_e0"].cpu().numpy(), r["d_e0"], de0_mag, rtol, "d_e0")
+
+    # tables: touched rows updated, untouched rows bit-identical
+    after = host_tables(db.tables, w.dtype)
+    orig = host_tables(before, w.dtype)
+    base = r["base"]
+    touched = [np.zeros(t.shape[0], bool) for t in orig]
+    for k in r["unique_keys"]:
+        t = int(np.searchsorted(base, k, side="right") - 1)
+        touched[t][k - base[t]] = True
+    for t in range(w.T):
+        np.testing.assert_array_equal(after[t][~touched[t]], orig[t][~touched[t]])
+    keys = np.asarray(r["unique_keys"], dtype=np.int64)
+    tix = np.searchsorted(base, keys, side="right") - 1
+    rix = keys - base[tix]
+    got_rows = np.array([orc.decode(after[t][i][None], w.dtype)[0] for t, i in zip(tix, rix)]).reshape(U, w.D)
+    W_mag = np.abs(np.array([orc.decode(orig[t][i][None], w.dtype)[0] for t, i in zip(tix, rix)]).reshape(U, w.D))
+    if exact:
+        want = _round_storage(r["new_rows"], w.dtype)
+        np.testing.assert_array_equal(got_rows, orc.decode(want, w.dtype))
+    else:
+        # storage rounding of the result adds half an ulp of the stored format
+        store_ulp = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[w.dtype]
+        mag = W_mag + lr * rm["grad"]
+        lim_mag = mag + (store_ulp / rtol) * np.abs(r["new_rows"])
+        assert_mag_close(got_rows, r["new_rows"], lim_mag, rtol, "updated rows")
+    return res, r
+
+
+def test_backward_zipf_26_tables_full():
+    """Backward + SGD (lr = 0.01) on the 26-table Zipf(1.05) workload, full size."""
+    run_bwd(synth.WORKLOADS["bwd-zipf-26t-d128-b2048"], lr=0.01, twice=True)
+
+
+@pytest.mark.parametrize("name", ["tiny-4t1k-d16-b128", "bwd-zipf-26t-d128-b2048"])
+def test_backward_exact_arithmetic(name):
+    w = synth.WORKLOADS[name].replace(values="int")
+    run_bwd(w, lr=2.0 ** -7, exact=True)
+
+
+def test_backward_multihot_fp16():
+    w = synth.WORKLOADS["multihot-8t4m-d64-fp16-b4096"].replace(B=512, rows=200_000)
+    run_bwd(w, lr=0.01)
+
+
+def test_backward_capacity_shape_bf16():
+    w = synth.WORKLOADS[synth.CAPACITY].replace(B=48, rows=3000)
+    run_bwd(w, lr=0.01, twice=True)
+
+
+@pytest.mark.parametrize("T,D,B", [(1, 4, 1), (3, 16, 5), (7, 256, 9), (20, 32, 300)])
+def test_backward_shapes(T, D, B):
+    w = synth.Workload("bshape", T=T, rows=40, D=D, dtype="f32", B=B, bag=("uniform", 0, 12),
+                       dist=("zipf", 1.2), seed=T * 100 + D)
+    run_bwd(w, lr=0.05)
+
+
+def test_backward_many_keys_four_radix_passes():
+    """sum(rows) above 2^24 needs a fourth 8-bit pass of the sort."""
+    w = synth.Workload("bigkeys", T=3, rows=6_000_000, D=8, dtype="bf16", B=700, bag=("uniform", 0, 9),
+                       dist=("zipf", 1.05), seed=77)
+    run_bwd(w, lr=0.01)
