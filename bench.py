@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused embedding-bag + interaction forward on one MI355X.
+
+Default workload: the 164 GB capacity shard -- 64 bf16 tables x 10M rows x
+D=128, batch 16384, bag lengths uniform on [1, 32], uniform row indices, e0
+N(0,1) -- with every input resident in HBM before the timed region. One step
+is one call of dlrm_embbag_fwd that produces [e0 | strict-lower dots] (the
+gather, pooling, interaction and output write of the whole batch, one kernel).
+
+Printed (last line of stdout, one JSON object):
+  value        index lookups per second (rows gathered and pooled / time)
+  roofline     algorithmic bytes per launch / average launch time vs 8 TB/s
+  cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same batch
+  backward     the sparse backward + SGD on the 26-table Zipf workload (timed
+               the same way; reported next to the forward, not in `value`)
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1]
+  python bench.py --summarize-profile DIR --out profiles/NAME.txt   (rocprofv3 csv -> summary)
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "pooled lookups/sec + achieved HBM GB/s (% of peak) for fused embbag+interaction"
+FWD_KERNEL = "fused_kernel"
+KERNEL_SOURCES = ["sparse_embedding_lookup_dlrm_amd/csrc/embbag_fwd.hip",
+                  "sparse_embedding_lookup_dlrm_amd/csrc/common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_kernel_capacity-64t10m-d128-bf16-b16384_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def fwd_algorithmic_bytes(T, B, D, s, nnz) -> int:
+    """Bytes the fused forward must move: every lookup reads its row and its index once,
+    offsets and e0 are read once, [e0 | dots] is written once."""
+    P = (T + 1) * T // 2
+    return nnz * (D * s + 4) + 4 * (T * B + 1) + 4 * B * D + 4 * B * (D + P)
+
+
+def read_traffic(sha: str):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != sha:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 csv -> text summary
+# ---------------------------------------------------------------------------
+def summarize_profile(d: str, out: str, command: str, copy_bytes: float) -> None:
+    import csv
+
+    lines = [f"# rocprofv3 summary of: {command}", f"# source directory: {d}"]
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    for p in stats:
+        with open(p) as f:
+            rows = list(csv.DictReader(f))
+        lines.append(f"## kernel stats ({os.path.basename(p)})")
+        lines.append("name | calls | avg_us | min_us | max_us | pct")
+        for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+            nm = r["Name"].split("(")[0][:90]
+            lines.append(f"{nm} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                         f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}")
+    ctr = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    agg = {}
+    for p in ctr:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                nm = r["Kernel_Name"].split("(")[0]
+                key = (nm, r["Counter_Name"])
+                agg.setdefault(key, []).append(float(r["Counter_Value"]))
+    if agg:
+        lines.append("## counters (mean per dispatch)")
+        lines.append("kernel | counter | dispatches | mean")
+        for (nm, c), v in sorted(agg.items()):
+            lines.append(f"{nm[:90]} | {c} | {len(v)} | {sum(v) / len(v):.1f}")
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("\n".join(lines))
+
+
+# ---------------------------------------------------------------------------
+# benchmark
+# ---------------------------------------------------------------------------
+def build_capacity_inputs(w, dev):
+    import numpy as np
+    import torch
+
+    from sparse_embedding_lookup_dlrm_amd import ops, synth
+
+    rows = synth.table_rows(w)
+    t0 = time.time()
+    tables = synth.gen_tables_device(w, dev, rows)
+    lengths = synth.gen_lengths(w)
+    indices = synth.gen_indices(w, rows, lengths)
+    e0 = synth.gen_e0(w)
+    d_len = torch.from_numpy(lengths).to(dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    offsets = ops.lengths_to_offsets(d_len, status=status)
+    d_idx = torch.from_numpy(indices).to(dev)
+    d_e0 = torch.from_numpy(e0).to(dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s: nnz={len(indices)} tables={sum(rows) * w.D * 2 / 1e9:.1f} GB")
+    return dict(rows=rows, tables=tables, lengths=lengths, indices=indices, e0=e0, d_idx=d_idx, d_e0=d_e0,
+                offsets=offsets, status=status)
+
+
+def time_steps(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def cpu_baseline(w, inp, n_samples, seed=2024):
+    """The fp64 oracle on a seeded sample of whole samples of the same batch. Rows are
+    fetched from HBM first (not timed)."""
+    import numpy as np
+    import torch
+
+    from oracle import dlrm_oracle as orc
+
+    rng = np.random.default_rng(seed)
+    smp = np.sort(rng.choice(w.B, size=min(n_samples, w.B), replace=False))
+    off = np.zeros(w.T * w.B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(inp["lengths"])
+    sub_tables, sub_len, sub_idx = [], [], []
+    parts = []
+    for t in range(w.T):
+        segs = [inp["indices"][off[t * w.B + b]:off[t * w.B + b + 1]] for b in smp]
+        parts.append(segs)
+        uniq = np.unique(np.concatenate(segs)) if segs else np.zeros(0, np.int32)
+        rows = inp["tables"][t][torch.from_numpy(uniq.astype(np.int64)).to(inp["tables"][t].device)]
+        sub_tables.append(rows.view(torch.int16).cpu().numpy().view(np.uint16))
+        for s in segs:
+            sub_len.append(len(s))
+            sub_idx.append(np.searchsorted(uniq, s).astype(np.int32))
+    sub_off = orc.lengths_to_offsets(sub_len)
+    idx = np.concatenate(sub_idx).astype(np.int32)
+    e0 = inp["e0"][smp]
+    t0 = time.perf_counter()
+    orc.embbag_fwd(sub_tables, w.dtype, len(smp), sub_off, idx, e0)
+    dt = time.perf_counter() - t0
+    return {"value": len(idx) / dt, "unit": "lookups/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(smp)} of {w.B} samples ({len(idx)} lookups, all {w.T} tables), seed {seed}; "
+                      f"fp64 numpy oracle, single thread, {dt:.2f} s; host has {len(os.sched_getaffinity(0))} cores"}
+
+
+def bench_backward(steps, warmup):
+    import numpy as np
+    import torch
+
+    from sparse_embedding_lookup_dlrm_amd import ops, synth
+
+    w = synth.WORKLOADS["bwd-zipf-26t-d128-b2048"]
+    b = synth.make_batch(w, with_dout=True)
+    dev = torch.device("cuda:0")
+    tables = [torch.from_numpy(t).to(dev) for t in b.tables]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    offsets = ops.lengths_to_offsets(torch.from_numpy(b.lengths).to(dev), status=status)
+    idx = torch.from_numpy(b.indices).to(dev)
+    e0 = torch.from_numpy(b.e0).to(dev)
+    d_out = torch.from_numpy(b.dout).to(dev)
+    pooled, _ = ops.embbag_fwd(tables, offsets, idx, w.B, e0, want_pooled=True, want_inter=False)
+    nnz = len(b.indices)
+    ws = torch.empty(ops.bwd_workspace_bytes(w.T, w.B, w.D, nnz, b.rows), dtype=torch.uint8, device=dev)
+    d_e0 = torch.empty((w.B, w.D), dtype=torch.float32, device=dev)
+    plan = ops.BwdPlan(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, d_e0=d_e0, workspace=ws, status=status)
+    ms, _ = time_steps(plan.run, steps, warmup)
+    torch.cuda.synchronize()
+    U = int(plan.num_unique.item())
+    F = w.T + 1
+    P = F * w.T // 2
+    # method bytes: read d_out, Z (e0 + pooled), indices and offsets; write d_e0; gather one
+    # pooled-gradient row per occurrence; read and write each touched table row once.
+    alg = (4 * w.B * (w.D + P) + 4 * w.B * F * w.D + 4 * nnz + 4 * (w.T * w.B + 1) + 4 * w.B * w.D
+           + 4 * nnz * w.D + 2 * 4 * U * w.D)
+    return {"workload": w.name, "ms_per_step": ms, "lookups_per_s": nnz / (ms / 1e3), "nnz": nnz,
+            "unique_rows": U, "method_bytes": alg, "method_GBps": alg / (ms / 1e3) / 1e9,
+            "status": int(status.item()), "lr": 0.01}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-samples", type=int, default=1536)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="also run a plain copy of this size (for counter calibration)")
+    ap.add_argument("--summarize-profile", default=None)
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--command", default="")
+    args = ap.parse_args()
+
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.out, args.command, 0.0)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding of the tables is a "
+                                   "design note, not implemented", "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    from sparse_embedding_lookup_dlrm_amd import ops, synth
+
+    ops.lib()  # the HIP library must be present: no fallback
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[synth.CAPACITY]
+    inp = build_capacity_inputs(w, dev)
+    nnz = len(inp["indices"])
+    out = torch.empty((w.B, w.out_width), dtype=torch.float32, device=dev)
+    plan = ops.FwdPlan(inp["tables"], inp["offsets"], inp["d_idx"], w.B, inp["d_e0"], out_inter=out,
+                       status=inp["status"])
+
+    if args.copy_calibration_gib > 0:
+        n = int(args.copy_calibration_gib * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n * 4} bytes read, {n * 4} bytes written by one elementwise kernel")
+        del src, dst
+
+    ms, wall = time_steps(plan.run, args.steps, args.warmup)
+    st = int(inp["status"].item())
+    if st != 0:
+        raise RuntimeError(f"device status {st}: invalid bag description")
+    alg = fwd_algorithmic_bytes(w.T, w.B, w.D, 2, nnz)
+    gbs = alg / (ms / 1e3) / 1e9
+    sha = kernel_source_sha()
+    traffic = read_traffic(sha)
+    res = {
+        "metric": METRIC,
+        "value": nnz / (ms / 1e3),
+        "unit": "lookups/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tables": w.T, "rows_per_table": 10_000_000, "D": w.D,
+                   "storage": "bf16", "batch": w.B, "bag_len": "uniform[1,32]", "indices": "uniform",
+                   "nnz": nnz, "table_bytes": sum(inp["rows"]) * w.D * 2, "parallelism": "single GPU"},
+        "bags_per_s": w.T * w.B / (ms / 1e3),
+        "samples_per_s": w.B / (ms / 1e3),
+        "hbm_GBps_algorithmic": gbs,
+        "pct_of_peak_hbm": 100.0 * gbs / PEAK_HBM_GBS,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "kernel": FWD_KERNEL,
+                     "algorithmic_bytes_per_launch": alg, "kernel_source_sha": sha},
+        "wall_s_timed_region": wall,
+    }
+    log(f"fused forward: {ms * 1e3:.1f} us/step, {nnz / (ms / 1e3):.3e} lookups/s, {gbs:.0f} GB/s "
+        f"({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
+    del plan
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_samples)
+        log(f"cpu oracle: {res['cpu_baseline']['value']:.3e} lookups/s")
+    del inp
+    torch.cuda.empty_cache()
+    if not args.no_backward:
+        res["backward"] = bench_backward(max(args.steps, 20), args.warmup)
+        log(f"backward: {res['backward']['ms_per_step'] * 1e3:.1f} us/step")
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

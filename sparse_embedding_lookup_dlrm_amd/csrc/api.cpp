@@ -90,7 +90,7 @@ int dlrm_embbag_fwd(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* 
   if (out_inter && !e0) return DLRM_E_INVAL;
   if (out_pooled && !aligned(out_pooled, 16)) return DLRM_E_ALIGN;
   if (out_inter && (!aligned(out_inter, 4) || !aligned(e0, 16))) return DLRM_E_ALIGN;
-  if (out_inter && tile_bytes(T, D) > kLds) return DLRM_E_UNSUPPORTED;
+  if (out_inter && fwd_lds_bytes(T, D, dtype) > kLds) return DLRM_E_UNSUPPORTED;
   FwdArgs a;
   memset(&a, 0, sizeof(a));
   a.T = T; a.B = B; a.D = D; a.dtype = dtype;

@@ -160,6 +160,7 @@ __device__ __forceinline__ void block_pair(int w, int& bi, int& bj) {
 
 // Z: [Fpad][LD] fp32 in LDS (rows >= F may hold anything); dots of block (bi, bj)
 // for i in 4bi..4bi+3, j in 4bj..4bj+3 with j < i < F go to out[i(i-1)/2 + j].
+template <bool TO_LDS>
 __device__ __forceinline__ void dots_block(const float* Z, int F, int D, int LD, int bi, int bj,
                                            float* __restrict__ out) {
   float acc[4][4];
@@ -194,7 +195,10 @@ __device__ __forceinline__ void dots_block(const float* Z, int F, int D, int LD,
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int j = 4 * bj + q;
-      if (i < F && j < i) store_stream(out + (i * (i - 1) / 2 + j), acc[r][q]);
+      if (i < F && j < i) {
+        if constexpr (TO_LDS) out[i * (i - 1) / 2 + j] = acc[r][q];
+        else store_stream(out + (i * (i - 1) / 2 + j), acc[r][q]);
+      }
     }
   }
 }
@@ -229,7 +233,7 @@ __device__ __forceinline__ void interact_from_lds(const float* Zall, const Tile&
     if (b >= B) continue;
     int bi, bj;
     block_pair(blk, bi, bj);
-    dots_block(Zall + static_cast<size_t>(s) * tl.Fpad * tl.LD, tl.F, D, tl.LD, bi, bj,
+    dots_block<false>(Zall + static_cast<size_t>(s) * tl.Fpad * tl.LD, tl.F, D, tl.LD, bi, bj,
                out_inter + static_cast<size_t>(b) * W + D);
   }
 }
@@ -341,6 +345,392 @@ __global__ __launch_bounds__(kThreads) void interact_kernel(int T, int B, int D,
 }
 
 // ---------------------------------------------------------------------------
+// row-streaming fused forward: one sample per 512-thread workgroup
+// ---------------------------------------------------------------------------
+// For rows of 128..1024 bytes, one wave-wide load fetches exactly one table row
+// (LB = row bytes / 64 per lane), so a wave can stream the rows of consecutive
+// bags without any cross-lane reduction: every lane owns the same EL columns of
+// every row. The sample's bags are laid end to end into one row stream whose
+// indices are staged in LDS up front (one round trip for all of them); the 8
+// waves split the stream into equal contiguous ranges, keep WIN row loads in
+// flight, and sum rows in stream order. A bag cut by a range boundary is
+// finished by adding the later waves' partial sums in wave order after a
+// barrier, so the result does not depend on timing.
+//
+// Interaction: with 16-bit tables and T >= 24 the Gram matrix of the T pooled
+// rows is a real dense contraction and runs on MFMA (32x32x16 bf16) with each
+// fp32 operand split into hi + lo bf16 parts (hi*hi + hi*lo + lo*hi, fp32
+// accumulation); otherwise 4x4 register blocks of fp32 FMAs. The dots of e0
+// with each pooled row use fp32 FMAs. [e0 | dots] is assembled in LDS and
+// written with contiguous stores.
+constexpr int kRowThreads = 512;
+constexpr int kRowWaves = kRowThreads / kWave;
+constexpr int kStageCap = 2048;  // staged indices per sample; longer streams read indices from HBM
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+template <int LB>
+struct LaneChunk;
+template <>
+struct LaneChunk<2> {
+  using type = uint32_t;  // low 16 bits used
+  __device__ static type load(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+  }
+  __device__ static type zero() { return 0u; }
+};
+template <>
+struct LaneChunk<4> {
+  using type = uint32_t;
+  __device__ static type load(const char* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
+  __device__ static type zero() { return 0u; }
+};
+template <>
+struct LaneChunk<8> {
+  using type = uint2;
+  __device__ static type load(const char* p) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    return make_uint2(__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1));
+  }
+  __device__ static type zero() { return make_uint2(0u, 0u); }
+};
+template <>
+struct LaneChunk<16> {
+  using type = uint4;
+  __device__ static type load(const char* p) { return load16_stream(p); }
+  __device__ static type zero() { return make_uint4(0u, 0u, 0u, 0u); }
+};
+
+template <int DT>
+__device__ __forceinline__ float decode_lo(uint32_t w) {
+  if constexpr (DT == DLRM_BF16) return bf16_lo(w);
+  else if constexpr (DT == DLRM_F16) return f16_lo(w);
+  else return __uint_as_float(w);
+}
+template <int DT>
+__device__ __forceinline__ float decode_hi(uint32_t w) {
+  if constexpr (DT == DLRM_BF16) return bf16_hi(w);
+  else return f16_hi(w);
+}
+
+// acc[0..EL) += the lane's part of one row.
+template <int DT, int LB>
+__device__ __forceinline__ void acc_chunk(float* acc, const typename LaneChunk<LB>::type& v) {
+  if constexpr (LB == 2) {
+    acc[0] += decode_lo<DT>(v);
+  } else if constexpr (LB == 4) {
+    if constexpr (DT == DLRM_F32) acc[0] += __uint_as_float(v);
+    else { acc[0] += decode_lo<DT>(v); acc[1] += decode_hi<DT>(v); }
+  } else if constexpr (LB == 8) {
+    if constexpr (DT == DLRM_F32) { acc[0] += __uint_as_float(v.x); acc[1] += __uint_as_float(v.y); }
+    else {
+      acc[0] += decode_lo<DT>(v.x); acc[1] += decode_hi<DT>(v.x);
+      acc[2] += decode_lo<DT>(v.y); acc[3] += decode_hi<DT>(v.y);
+    }
+  } else {
+    accumulate16<DT>(acc, v);
+  }
+}
+
+template <int DT, int LB>
+struct RowShape {
+  static constexpr int EL = LB / Storage<DT>::bytes;  // fp32 columns per lane
+  static constexpr int WIN = LB >= 4 ? 128 / LB : 64;  // rows in flight per wave (32 VGPRs of data)
+};
+
+struct RowLayout {
+  int Tp;        // Z rows after e0 (T rounded up: 32 for MFMA, else to F multiple of 4)
+  int LD;        // Z row stride in floats
+  int off_pos;   // byte offsets inside the dynamic LDS block
+  int off_carry_t;
+  int off_stage;
+  int off_carry;
+  int off_out;
+  int off_z;
+  int bytes;
+};
+
+__host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
+
+__host__ __device__ inline RowLayout make_row_layout(int T, int D, bool mfma) {
+  RowLayout L;
+  L.Tp = mfma ? ((T + 31) / 32) * 32 : (((T + 1 + 3) & ~3) - 1);
+  L.LD = D + 4;
+  const int P = (T + 1) * T / 2;
+  int o = 0;
+  o += align16(T * 4);                 // bag begin (global index position)
+  L.off_pos = o; o += align16((T + 1) * 4);
+  L.off_carry_t = o; o += align16(kRowWaves * 4);
+  const int uni = o;                   // union { stage + carry ; output staging }
+  L.off_stage = uni;
+  L.off_carry = uni + kStageCap * 4;
+  const int gather_bytes = kStageCap * 4 + kRowWaves * D * 4;
+  L.off_out = uni;
+  const int out_bytes = (D + P) * 4;
+  o = uni + align16(gather_bytes > out_bytes ? gather_bytes : out_bytes);
+  L.off_z = o; o += (1 + L.Tp) * L.LD * 4;
+  L.bytes = o;
+  return L;
+}
+
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Split 8 fp32 into bf16 hi (round to nearest even) and the bf16 of the remainder.
+__device__ __forceinline__ void split_bf16x8(const float4& a, const float4& b, bf16x8_t& hi, bf16x8_t& lo) {
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint16_t h0 = to_half_bits<DLRM_BF16>(x[2 * k]), h1 = to_half_bits<DLRM_BF16>(x[2 * k + 1]);
+    const float r0 = x[2 * k] - __uint_as_float(static_cast<uint32_t>(h0) << 16);
+    const float r1 = x[2 * k + 1] - __uint_as_float(static_cast<uint32_t>(h1) << 16);
+    h[k] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+    l[k] = static_cast<uint32_t>(to_half_bits<DLRM_BF16>(r0)) | (static_cast<uint32_t>(to_half_bits<DLRM_BF16>(r1)) << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+// One 32x32 tile (I, J) of the Gram matrix of the pooled rows; results with
+// Z-row indices zi > zj go to out[D + zi(zi-1)/2 + zj].
+__device__ __forceinline__ void gram_tile_mfma(const float* Z, int LD, int D, int T, int I, int J, float* out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int m = lane & 31, kh = lane >> 5;
+  const float* za = Z + (1 + 32 * I + m) * LD + 8 * kh;
+  const float* zb = Z + (1 + 32 * J + m) * LD + 8 * kh;
+  floatx16_t acc = {};
+  for (int k0 = 0; k0 < D; k0 += 16) {
+    bf16x8_t ah, al, bh, bl;
+    split_bf16x8(*reinterpret_cast<const float4*>(za + k0), *reinterpret_cast<const float4*>(za + k0 + 4), ah, al);
+    if (I != J) {
+      split_bf16x8(*reinterpret_cast<const float4*>(zb + k0), *reinterpret_cast<const float4*>(zb + k0 + 4), bh, bl);
+    } else {
+      bh = ah;
+      bl = al;
+    }
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 8 * (i >> 2) + 4 * kh + (i & 3);
+    const int zi = 1 + 32 * I + row, zj = 1 + 32 * J + m;
+    if (zi > zj && zi <= T) out[D + zi * (zi - 1) / 2 + zj] = acc[i];
+  }
+}
+
+template <int DT, int LB, bool MFMA>
+__global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, RowLayout L) {
+  using C = LaneChunk<LB>;
+  using RS = RowShape<DT, LB>;
+  constexpr int EL = RS::EL;
+  constexpr int WIN = RS::WIN;
+  constexpr int RB = LB * kWave;  // row bytes
+  extern __shared__ __align__(16) char lds[];
+  int* sm_beg = reinterpret_cast<int*>(lds);
+  int* sm_pos = reinterpret_cast<int*>(lds + L.off_pos);
+  int* carry_t = reinterpret_cast<int*>(lds + L.off_carry_t);
+  int* stage = reinterpret_cast<int*>(lds + L.off_stage);
+  float* carry = reinterpret_cast<float*>(lds + L.off_carry);
+  float* outs = reinterpret_cast<float*>(lds + L.off_out);
+  float* Z = reinterpret_cast<float*>(lds + L.off_z);
+
+  const int T = a.T, B = a.B, D = a.D, LD = L.LD;
+  const int b = xcd_block(blockIdx.x, gridDim.x);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = rfl(tid >> 6);
+
+  // 1. bag ranges, Z cleared, e0 into Z row 0
+  if (tid < T) {
+    int s0 = a.offsets[tid * B + b], s1 = a.offsets[tid * B + b + 1];
+    bool bad = false;
+    if (tid == 0 && b == 0 && s0 != 0) bad = true;
+    if (tid == T - 1 && b == B - 1 && static_cast<int64_t>(s1) != a.nnz) bad = true;
+    if (s0 < 0) { s0 = 0; bad = true; }
+    if (static_cast<int64_t>(s0) > a.nnz) { s0 = static_cast<int>(a.nnz); bad = true; }
+    if (static_cast<int64_t>(s1) > a.nnz) { s1 = static_cast<int>(a.nnz); bad = true; }
+    if (s1 < s0) { s1 = s0; bad = true; }
+    if (bad) flag(a.status, DLRM_STATUS_BAD_OFFSETS);
+    sm_beg[tid] = s0;
+    sm_pos[tid + 1] = s1 - s0;  // lengths for now
+  }
+  if (tid < kRowWaves) carry_t[tid] = -1;
+  for (int i = tid; i < (1 + L.Tp) * LD; i += kRowThreads) Z[i] = 0.f;
+  __syncthreads();
+  for (int d = tid; d < D; d += kRowThreads) Z[d] = a.e0[static_cast<size_t>(b) * D + d];
+  if (wave == 0) {  // inclusive scan of the lengths -> stream positions
+    int carry_sum = 0;
+    for (int t0 = 0; t0 < T; t0 += kWave) {
+      const int t = t0 + lane;
+      int v = t < T ? sm_pos[t + 1] : 0;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(v, o, kWave);
+        if (lane >= o) v += y;
+      }
+      if (t < T) sm_pos[t + 1] = v + carry_sum;
+      carry_sum += __shfl(v, kWave - 1, kWave);
+    }
+    if (lane == 0) sm_pos[0] = 0;
+  }
+  __syncthreads();
+  const int N = rfl(sm_pos[T]);
+
+  // 2. stage the sample's indices (validated) in stream order
+  {
+    bool bad = false;
+    for (int t = wave; t < T; t += kRowWaves) {
+      const int beg = sm_beg[t], p = rfl(sm_pos[t]), len = rfl(sm_pos[t + 1]) - p;
+      const int rows = a.tabs.rows[t];
+      for (int i = lane; i < len && p + i < kStageCap; i += kWave) {
+        int r = a.indices[beg + i];
+        if (r < 0 || r >= rows) { bad = true; r = -1; }
+        stage[p + i] = r;
+      }
+    }
+    if (bad) flag(a.status, DLRM_STATUS_BAD_INDEX);
+  }
+  __syncthreads();
+
+  // 3. gather: wave w sums stream positions [p0, p1)
+  {
+    const int p0 = static_cast<int>((static_cast<long long>(N) * wave) / kRowWaves);
+    const int p1 = static_cast<int>((static_cast<long long>(N) * (wave + 1)) / kRowWaves);
+    if (p0 < p1) {
+      int t = 0;
+      while (rfl(sm_pos[t + 1]) <= p0) ++t;
+      int bag_end = rfl(sm_pos[t + 1]);
+      bool started_before = rfl(sm_pos[t]) < p0;
+      float acc[EL];
+#pragma unroll
+      for (int e = 0; e < EL; ++e) acc[e] = 0.f;
+      bool bad = false;
+      for (int q = p0; q < p1; q += WIN) {
+        const int nq = min(WIN, p1 - q);
+        int my = -1;
+        if (lane < nq) {
+          const int pos = q + lane;
+          if (pos < kStageCap) {
+            my = stage[pos];
+          } else {  // beyond the staging area: locate the bag and read the index from HBM
+            int tl = 0;
+            while (sm_pos[tl + 1] <= pos) ++tl;
+            const int r = a.indices[sm_beg[tl] + (pos - sm_pos[tl])];
+            if (r >= 0 && r < a.tabs.rows[tl]) my = r;
+            else bad = true;
+          }
+        }
+        typename C::type v[WIN];
+        {
+          int tt = t, be = bag_end;
+          const char* bs = static_cast<const char*>(a.tabs.ptr[tt]) + lane * LB;
+#pragma unroll
+          for (int j = 0; j < WIN; ++j) {
+            v[j] = C::zero();
+            if (j < nq) {
+              if (q + j >= be) {
+                do {
+                  ++tt;
+                  be = rfl(sm_pos[tt + 1]);
+                } while (q + j >= be);
+                bs = static_cast<const char*>(a.tabs.ptr[tt]) + lane * LB;
+              }
+              const int r = __builtin_amdgcn_readlane(my, j);
+              if (r >= 0) v[j] = C::load(bs + static_cast<size_t>(r) * RB);
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < WIN; ++j) {
+          if (j < nq) {
+            acc_chunk<DT, LB>(acc, v[j]);
+            if (q + j + 1 == bag_end) {
+              float* dst = started_before ? carry + wave * D : Z + (1 + t) * LD;
+              if (started_before && lane == 0) carry_t[wave] = t;
+#pragma unroll
+              for (int e = 0; e < EL; ++e) {
+                dst[lane * EL + e] = acc[e];
+                acc[e] = 0.f;
+              }
+              started_before = false;
+              if (q + j + 1 < p1) {
+                do {
+                  ++t;
+                  bag_end = rfl(sm_pos[t + 1]);
+                } while (bag_end <= q + j + 1);
+              }
+            }
+          }
+        }
+      }
+      if (bag_end > p1) {  // the last bag continues in the next wave's range
+        float* dst = started_before ? carry + wave * D : Z + (1 + t) * LD;
+        if (started_before && lane == 0) carry_t[wave] = t;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) dst[lane * EL + e] = acc[e];
+      }
+      if (bad) flag(a.status, DLRM_STATUS_BAD_INDEX);
+    }
+  }
+  __syncthreads();
+  // bags cut by a range boundary: add the later parts in wave order
+  for (int d = tid; d < D; d += kRowThreads) {
+    for (int w = 1; w < kRowWaves; ++w) {
+      const int t = carry_t[w];
+      if (t >= 0) Z[(1 + t) * LD + d] += carry[w * D + d];
+    }
+  }
+  __syncthreads();
+
+  // 4. interaction into the output staging area (which overlays the index stage)
+  for (int d = tid; d < D; d += kRowThreads) outs[d] = Z[d];
+  if constexpr (MFMA) {
+    const int nt = L.Tp / 32;
+    const int ntiles = nt * (nt + 1) / 2;
+    for (int tile = wave; tile < ntiles; tile += kRowWaves) {
+      int I, J;
+      block_pair(tile, I, J);
+      gram_tile_mfma(Z, LD, D, T, I, J, outs);
+    }
+  } else {
+    const Tile tl = make_tile(T, D, 1);
+    for (int w = tid; w < tl.nblk; w += kRowThreads) {
+      int bi, bj;
+      block_pair(w, bi, bj);
+      dots_block<true>(Z, tl.F, D, LD, bi, bj, outs + D);
+    }
+  }
+  if constexpr (MFMA) {  // dots of e0 with every pooled row: pair (zi, 0) sits at zi(zi-1)/2
+    for (int zi = 1 + (kRowThreads - 1 - tid); zi <= T; zi += kRowThreads) {
+      const float* zr = Z + zi * LD;
+      float s = 0.f;
+      for (int d = 0; d < D; d += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(zr + d);
+        const float4 y = *reinterpret_cast<const float4*>(Z + d);
+        s = fmaf(x.x, y.x, s);
+        s = fmaf(x.y, y.y, s);
+        s = fmaf(x.z, y.z, s);
+        s = fmaf(x.w, y.w, s);
+      }
+      outs[D + zi * (zi - 1) / 2] = s;
+    }
+  }
+  __syncthreads();
+  const int W = D + (T + 1) * T / 2;
+  float* o = a.out_inter + static_cast<size_t>(b) * W;
+  for (int i = tid; i < W; i += kRowThreads) store_stream(o + i, outs[i]);
+  if (a.out_pooled) {
+    float* op = a.out_pooled + static_cast<size_t>(b) * T * D;
+    for (int i = tid; i < T * D; i += kRowThreads) {
+      const int t = i / D, d = i - t * D;
+      op[i] = Z[(1 + t) * LD + d];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 int fwd_supported_row_bytes(int D, int dtype) {
@@ -363,8 +753,44 @@ static int pick_samples_per_block(int T, int B, int D) {
   }
 }
 
+// Row-streaming fused kernel: rows of 128..1024 bytes (16-bit storage) or
+// 256..1024 bytes (fp32); MFMA interaction for 16-bit storage with T >= 24.
+static bool use_row_kernel(int D, int dtype) {
+  const int rb = fwd_supported_row_bytes(D, dtype);
+  return dtype == DLRM_F32 ? (rb >= 256 && rb <= 1024) : (rb >= 128 && rb <= 1024);
+}
+static bool use_mfma(int T, int D, int dtype) { return dtype != DLRM_F32 && T >= 24 && D % 16 == 0; }
+
+size_t fwd_lds_bytes(int T, int D, int dtype) {
+  if (use_row_kernel(D, dtype)) return static_cast<size_t>(make_row_layout(T, D, use_mfma(T, D, dtype)).bytes);
+  const Tile tl = make_tile(T, D, 1);
+  return tl.z_floats() * 4 + static_cast<size_t>(T) * 2 * 4;
+}
+
+template <int DT, int LB>
+static hipError_t launch_rows(const FwdArgs& a, hipStream_t st) {
+  const bool mfma = use_mfma(a.T, a.D, DT);
+  const RowLayout L = make_row_layout(a.T, a.D, mfma);
+  if (static_cast<size_t>(L.bytes) > kMaxLds) return hipErrorInvalidValue;
+  if (mfma) {
+    if constexpr (DT != DLRM_F32)
+      hipLaunchKernelGGL((fused_rows_kernel<DT, LB, true>), dim3(a.B), dim3(kRowThreads), L.bytes, st, a, L);
+  } else {
+    hipLaunchKernelGGL((fused_rows_kernel<DT, LB, false>), dim3(a.B), dim3(kRowThreads), L.bytes, st, a, L);
+  }
+  return hipGetLastError();
+}
+
 template <int DT, int LPR>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  if (a.out_inter && use_row_kernel(a.D, DT)) {
+    constexpr int LB = LPR * 16 / kWave;  // bytes per lane when one wave reads one row
+    if constexpr (LB == 2 && DT != DLRM_F32) return launch_rows<DT, 2>(a, st);
+    else if constexpr (LB == 4) return launch_rows<DT, 4>(a, st);
+    else if constexpr (LB == 8) return launch_rows<DT, 8>(a, st);
+    else if constexpr (LB == 16) return launch_rows<DT, 16>(a, st);
+    else return hipErrorInvalidValue;
+  }
   if (a.out_inter) {
     const int S = pick_samples_per_block(a.T, a.B, a.D);
     const Tile tl = make_tile(a.T, a.D, S);

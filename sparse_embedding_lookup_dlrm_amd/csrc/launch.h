@@ -66,5 +66,7 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t s);
 
 // shared by forward and backward: fused/standalone interaction tile sizes
 int fwd_supported_row_bytes(int D, int dtype);
+// LDS bytes the fused forward needs for one workgroup (must be <= 160 KiB)
+size_t fwd_lds_bytes(int T, int D, int dtype);
 
 }  // namespace dlrm

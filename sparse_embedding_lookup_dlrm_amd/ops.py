@@ -214,3 +214,47 @@ def validate_bags(T: int, B: int, rows: Sequence[int], offsets, indices) -> int:
     idx = np.ascontiguousarray(indices, dtype=np.int32)
     r = (_i64 * T)(*rows)
     return lib().dlrm_validate_bags(T, B, r, off.ctypes.data_as(_P(_i32)), idx.ctypes.data_as(_P(_i32)), len(idx))
+
+
+class FwdPlan:
+    """dlrm_embbag_fwd with its arguments marshalled once, for repeated calls on
+    resident inputs (same tensors every call)."""
+
+    def __init__(self, tables, offsets, indices, B, e0=None, *, out_pooled=None, out_inter=None, status=None,
+                 stream=None):
+        T, D, dt, ptrs, rows = _table_args(tables)
+        _require_cuda(offsets, indices, e0, out_pooled, out_inter, status)
+        self._keep = (tables, offsets, indices, e0, out_pooled, out_inter, status, ptrs, rows)
+        self._args = (T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(), _ptr(e0),
+                      _ptr(out_pooled), _ptr(out_inter), _ptr(status), _stream(stream))
+        self._fn = lib().dlrm_embbag_fwd
+
+    def run(self):
+        _check(self._fn(*self._args), "dlrm_embbag_fwd")
+
+
+class BwdPlan:
+    """dlrm_embbag_bwd_update with its arguments marshalled once (tables updated in place each run)."""
+
+    def __init__(self, tables, offsets, indices, B, e0, pooled, d_out, lr, *, d_e0=None, workspace=None,
+                 status=None, stream=None):
+        T, D, dt, ptrs, rows = _table_args(tables)
+        nnz = indices.numel()
+        dev = tables[0].device
+        self.unique_keys = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+        self.seg_offsets = torch.empty(nnz + 1, dtype=torch.int32, device=dev)
+        self.num_unique = torch.empty(1, dtype=torch.int32, device=dev)
+        self.perm = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+        if workspace is None:
+            need = bwd_workspace_bytes(T, B, D, nnz, [t.shape[0] for t in tables])
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        _require_cuda(offsets, indices, e0, pooled, d_out, d_e0, workspace, status)
+        self._keep = (tables, offsets, indices, e0, pooled, d_out, d_e0, workspace, status, ptrs, rows)
+        self._args = (T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), nnz, _ptr(e0), _ptr(pooled),
+                      _ptr(d_out), float(lr), _ptr(d_e0), _ptr(self.unique_keys), _ptr(self.seg_offsets),
+                      _ptr(self.num_unique), _ptr(self.perm), _ptr(workspace), workspace.numel(), _ptr(status),
+                      _stream(stream))
+        self._fn = lib().dlrm_embbag_bwd_update
+
+    def run(self):
+        _check(self._fn(*self._args), "dlrm_embbag_bwd_update")
