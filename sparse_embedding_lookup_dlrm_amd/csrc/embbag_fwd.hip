@@ -370,27 +370,29 @@ constexpr int kStageCap = 2048;  // staged indices per sample; longer streams re
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
+// Loads of one lane's part of a table row, from a global (not generic) address.
+template <class T>
+using gptr = const __attribute__((address_space(1))) T*;
+
 template <int LB>
 struct LaneChunk;
 template <>
 struct LaneChunk<2> {
   using type = uint32_t;  // low 16 bits used
-  __device__ static type load(const char* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
-  }
+  __device__ static type load(uint64_t p) { return __builtin_nontemporal_load(reinterpret_cast<gptr<uint16_t>>(p)); }
   __device__ static type zero() { return 0u; }
 };
 template <>
 struct LaneChunk<4> {
   using type = uint32_t;
-  __device__ static type load(const char* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
+  __device__ static type load(uint64_t p) { return __builtin_nontemporal_load(reinterpret_cast<gptr<uint32_t>>(p)); }
   __device__ static type zero() { return 0u; }
 };
 template <>
 struct LaneChunk<8> {
   using type = uint2;
-  __device__ static type load(const char* p) {
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+  __device__ static type load(uint64_t p) {
+    const auto q = reinterpret_cast<gptr<uint32_t>>(p);
     return make_uint2(__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1));
   }
   __device__ static type zero() { return make_uint2(0u, 0u); }
@@ -398,9 +400,20 @@ struct LaneChunk<8> {
 template <>
 struct LaneChunk<16> {
   using type = uint4;
-  __device__ static type load(const char* p) { return load16_stream(p); }
+  __device__ static type load(uint64_t p) {
+    const auto q = reinterpret_cast<gptr<uint32_t>>(p);
+    return make_uint4(__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1),
+                      __builtin_nontemporal_load(q + 2), __builtin_nontemporal_load(q + 3));
+  }
   __device__ static type zero() { return make_uint4(0u, 0u, 0u, 0u); }
 };
+
+// Broadcast lane j's 64-bit value (two 32-bit halves) to a scalar.
+__device__ __forceinline__ uint64_t bcast64(uint32_t lo, uint32_t hi, int j) {
+  const uint32_t l = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), j));
+  const uint32_t h = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), j));
+  return (static_cast<uint64_t>(h) << 32) | l;
+}
 
 template <int DT>
 __device__ __forceinline__ float decode_lo(uint32_t w) {
@@ -436,7 +449,7 @@ __device__ __forceinline__ void acc_chunk(float* acc, const typename LaneChunk<L
 template <int DT, int LB>
 struct RowShape {
   static constexpr int EL = LB / Storage<DT>::bytes;  // fp32 columns per lane
-  static constexpr int WIN = LB >= 4 ? 128 / LB : 64;  // rows in flight per wave (32 VGPRs of data)
+  static constexpr int WIN = LB >= 4 ? 96 / LB : 24;  // rows per window (two windows in flight: <= 48 VGPRs)
 };
 
 struct RowLayout {
@@ -445,6 +458,8 @@ struct RowLayout {
   int off_pos;   // byte offsets inside the dynamic LDS block
   int off_carry_t;
   int off_stage;
+  int off_sbag;
+  int off_tbase;
   int off_carry;
   int off_out;
   int off_z;
@@ -464,8 +479,10 @@ __host__ __device__ inline RowLayout make_row_layout(int T, int D, bool mfma) {
   L.off_carry_t = o; o += align16(kRowWaves * 4);
   const int uni = o;                   // union { stage + carry ; output staging }
   L.off_stage = uni;
-  L.off_carry = uni + kStageCap * 4;
-  const int gather_bytes = kStageCap * 4 + kRowWaves * D * 4;
+  L.off_sbag = L.off_stage + kStageCap * 4;
+  L.off_tbase = L.off_sbag + align16(kStageCap);
+  L.off_carry = L.off_tbase + align16(T * 8);
+  const int gather_bytes = L.off_carry + kRowWaves * D * 4 - uni;
   L.off_out = uni;
   const int out_bytes = (D + P) * 4;
   o = uni + align16(gather_bytes > out_bytes ? gather_bytes : out_bytes);
@@ -476,20 +493,26 @@ __host__ __device__ inline RowLayout make_row_layout(int T, int D, bool mfma) {
 
 __device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Split 8 fp32 into bf16 hi (round to nearest even) and the bf16 of the remainder.
+// Split 8 fp32 into bf16 hi (round to nearest even) and the bf16 of the
+// remainder (x - hi, also rounded to nearest even): x = hi + lo + O(2^-17 |x|).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& h, uint32_t& l) {
+  const float2_t x = {x0, x1};
+  h = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+  const float2_t r = {x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u)};
+  l = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+}
+
 __device__ __forceinline__ void split_bf16x8(const float4& a, const float4& b, bf16x8_t& hi, bf16x8_t& lo) {
-  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint16_t h0 = to_half_bits<DLRM_BF16>(x[2 * k]), h1 = to_half_bits<DLRM_BF16>(x[2 * k + 1]);
-    const float r0 = x[2 * k] - __uint_as_float(static_cast<uint32_t>(h0) << 16);
-    const float r1 = x[2 * k + 1] - __uint_as_float(static_cast<uint32_t>(h1) << 16);
-    h[k] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-    l[k] = static_cast<uint32_t>(to_half_bits<DLRM_BF16>(r0)) | (static_cast<uint32_t>(to_half_bits<DLRM_BF16>(r1)) << 16);
-  }
-  hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
-  lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+  uint4 h, l;
+  split2(a.x, a.y, h.x, l.x);
+  split2(a.z, a.w, h.y, l.y);
+  split2(b.x, b.y, h.z, l.z);
+  split2(b.z, b.w, h.w, l.w);
+  hi = __builtin_bit_cast(bf16x8_t, h);
+  lo = __builtin_bit_cast(bf16x8_t, l);
 }
 
 // One 32x32 tile (I, J) of the Gram matrix of the pooled rows; results with
@@ -521,6 +544,98 @@ __device__ __forceinline__ void gram_tile_mfma(const float* Z, int LD, int D, in
   }
 }
 
+// Per-window state: each lane's row address (as two halves) and bag, and the
+// wave-wide masks of rows that end a partial sum and rows that must be skipped.
+struct Window {
+  uint32_t alo, ahi;
+  int tk;
+  unsigned long long fmask, smask;
+};
+
+struct RowCursor {
+  bool to_carry;  // the next flushed sum continues a bag begun by an earlier wave
+};
+
+__device__ __forceinline__ bool to_carry_init(const int* sm_pos, int t0, int p0) { return rfl(sm_pos[t0]) < p0; }
+
+template <int WIN, int RB>
+__device__ __forceinline__ void prepare_window(Window& w, const FwdArgs& a, const int* sm_beg, const int* sm_pos,
+                                               const int* stage, const uint8_t* sbag, const char* const* tbase,
+                                               int T, int q, int p1, uint64_t fallback) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t addr = fallback;
+  int tk = 0;
+  bool flush = false, skip = true;
+  const int pos = q + lane;
+  if (lane < WIN && pos < p1) {
+    int r;
+    if (pos < kStageCap) {
+      r = stage[pos];
+      tk = sbag[pos];
+    } else {  // beyond the staging area: locate the bag and read the index from HBM
+      int lo = 0, hi = T;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sm_pos[mid] <= pos) lo = mid;
+        else hi = mid;
+      }
+      tk = lo;
+      r = a.indices[sm_beg[lo] + (pos - sm_pos[lo])];
+      if (r < 0 || r >= a.tabs.rows[lo]) {
+        r = -1;
+        flag(a.status, DLRM_STATUS_BAD_INDEX);
+      }
+    }
+    if (r >= 0) {  // an index outside its table keeps the fallback row and is skipped
+      addr = reinterpret_cast<uint64_t>(tbase[tk]) + static_cast<uint64_t>(r) * RB;
+      skip = false;
+    }
+    flush = (pos + 1 == sm_pos[tk + 1]) || (pos + 1 == p1);
+  }
+  w.alo = static_cast<uint32_t>(addr);
+  w.ahi = static_cast<uint32_t>(addr >> 32);
+  w.tk = tk;
+  w.fmask = __ballot(flush);
+  w.smask = __ballot(skip);
+}
+
+template <class C, int WIN>
+__device__ __forceinline__ void issue_window(const Window& w, typename C::type (&v)[WIN], uint64_t lane_off) {
+#pragma unroll
+  for (int j = 0; j < WIN; ++j) v[j] = C::load(bcast64(w.alo, w.ahi, j) + lane_off);
+}
+
+template <int DT, int LB, int WIN>
+__device__ __forceinline__ void consume_window(const Window& w, typename LaneChunk<LB>::type (&v)[WIN],
+                                               float (&acc)[LB / Storage<DT>::bytes], RowCursor& cur, float* Z,
+                                               int LD, float* carry_w, int* carry_t_w) {
+  constexpr int EL = LB / Storage<DT>::bytes;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (w.smask) {
+#pragma unroll
+    for (int j = 0; j < WIN; ++j)
+      if ((w.smask >> j) & 1ull) v[j] = LaneChunk<LB>::zero();
+  }
+#pragma unroll
+  for (int j = 0; j < WIN; ++j) {
+    acc_chunk<DT, LB>(acc, v[j]);
+    if ((w.fmask >> j) & 1ull) {
+      const int tj = __builtin_amdgcn_readlane(w.tk, j);
+      float* dst = Z + (1 + tj) * LD;
+      if (cur.to_carry) {
+        dst = carry_w;
+        if (lane == 0) *carry_t_w = tj;
+        cur.to_carry = false;
+      }
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        dst[lane * EL + e] = acc[e];
+        acc[e] = 0.f;
+      }
+    }
+  }
+}
+
 template <int DT, int LB, bool MFMA>
 __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, RowLayout L) {
   using C = LaneChunk<LB>;
@@ -533,6 +648,8 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
   int* sm_pos = reinterpret_cast<int*>(lds + L.off_pos);
   int* carry_t = reinterpret_cast<int*>(lds + L.off_carry_t);
   int* stage = reinterpret_cast<int*>(lds + L.off_stage);
+  uint8_t* sbag = reinterpret_cast<uint8_t*>(lds + L.off_sbag);
+  const char** tbase = reinterpret_cast<const char**>(lds + L.off_tbase);
   float* carry = reinterpret_cast<float*>(lds + L.off_carry);
   float* outs = reinterpret_cast<float*>(lds + L.off_out);
   float* Z = reinterpret_cast<float*>(lds + L.off_z);
@@ -555,6 +672,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     if (bad) flag(a.status, DLRM_STATUS_BAD_OFFSETS);
     sm_beg[tid] = s0;
     sm_pos[tid + 1] = s1 - s0;  // lengths for now
+    tbase[tid] = static_cast<const char*>(a.tabs.ptr[tid]);
   }
   if (tid < kRowWaves) carry_t[tid] = -1;
   for (int i = tid; i < (1 + L.Tp) * LD; i += kRowThreads) Z[i] = 0.f;
@@ -578,100 +696,76 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
   __syncthreads();
   const int N = rfl(sm_pos[T]);
 
-  // 2. stage the sample's indices (validated) in stream order
+  // 2. stage the sample's indices (validated) in stream order: every thread
+  //    issues all of its index loads before writing any, so the whole sample
+  //    costs one round trip.
   {
+    constexpr int K = kStageCap / kRowThreads;
+    int r[K], tb[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int p = tid + k * kRowThreads;
+      r[k] = 0;
+      tb[k] = -1;
+      if (p < N) {
+        int lo = 0, hi = T;  // last t with sm_pos[t] <= p (skips empty bags)
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (sm_pos[mid] <= p) lo = mid;
+          else hi = mid;
+        }
+        tb[k] = lo;
+        r[k] = a.indices[sm_beg[lo] + (p - sm_pos[lo])];
+      }
+    }
     bool bad = false;
-    for (int t = wave; t < T; t += kRowWaves) {
-      const int beg = sm_beg[t], p = rfl(sm_pos[t]), len = rfl(sm_pos[t + 1]) - p;
-      const int rows = a.tabs.rows[t];
-      for (int i = lane; i < len && p + i < kStageCap; i += kWave) {
-        int r = a.indices[beg + i];
-        if (r < 0 || r >= rows) { bad = true; r = -1; }
-        stage[p + i] = r;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (tb[k] >= 0) {
+        int v = r[k];
+        if (v < 0 || v >= a.tabs.rows[tb[k]]) { bad = true; v = -1; }
+        stage[tid + k * kRowThreads] = v;
+        sbag[tid + k * kRowThreads] = static_cast<uint8_t>(tb[k]);
       }
     }
     if (bad) flag(a.status, DLRM_STATUS_BAD_INDEX);
   }
   __syncthreads();
 
-  // 3. gather: wave w sums stream positions [p0, p1)
+  // 3. gather: wave w sums stream positions [p0, p1) in windows of WIN rows.
+  //    For each window every lane first works out the address of "its" row and
+  //    whether a sum ends there; the loads of window k+1 are issued before
+  //    window k is summed, so a wave always has one window of rows in flight.
+  //    Slots past the range load a fixed in-bounds row (a cache hit) and are
+  //    zeroed, which keeps the number of loads per window constant.
   {
     const int p0 = static_cast<int>((static_cast<long long>(N) * wave) / kRowWaves);
     const int p1 = static_cast<int>((static_cast<long long>(N) * (wave + 1)) / kRowWaves);
     if (p0 < p1) {
-      int t = 0;
-      while (rfl(sm_pos[t + 1]) <= p0) ++t;
-      int bag_end = rfl(sm_pos[t + 1]);
-      bool started_before = rfl(sm_pos[t]) < p0;
+      int t0 = 0;
+      while (rfl(sm_pos[t0 + 1]) <= p0) ++t0;
+      RowCursor cur{to_carry_init(sm_pos, t0, p0)};
       float acc[EL];
 #pragma unroll
       for (int e = 0; e < EL; ++e) acc[e] = 0.f;
-      bool bad = false;
-      for (int q = p0; q < p1; q += WIN) {
-        const int nq = min(WIN, p1 - q);
-        int my = -1;
-        if (lane < nq) {
-          const int pos = q + lane;
-          if (pos < kStageCap) {
-            my = stage[pos];
-          } else {  // beyond the staging area: locate the bag and read the index from HBM
-            int tl = 0;
-            while (sm_pos[tl + 1] <= pos) ++tl;
-            const int r = a.indices[sm_beg[tl] + (pos - sm_pos[tl])];
-            if (r >= 0 && r < a.tabs.rows[tl]) my = r;
-            else bad = true;
-          }
-        }
-        typename C::type v[WIN];
-        {
-          int tt = t, be = bag_end;
-          const char* bs = static_cast<const char*>(a.tabs.ptr[tt]) + lane * LB;
-#pragma unroll
-          for (int j = 0; j < WIN; ++j) {
-            v[j] = C::zero();
-            if (j < nq) {
-              if (q + j >= be) {
-                do {
-                  ++tt;
-                  be = rfl(sm_pos[tt + 1]);
-                } while (q + j >= be);
-                bs = static_cast<const char*>(a.tabs.ptr[tt]) + lane * LB;
-              }
-              const int r = __builtin_amdgcn_readlane(my, j);
-              if (r >= 0) v[j] = C::load(bs + static_cast<size_t>(r) * RB);
-            }
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < WIN; ++j) {
-          if (j < nq) {
-            acc_chunk<DT, LB>(acc, v[j]);
-            if (q + j + 1 == bag_end) {
-              float* dst = started_before ? carry + wave * D : Z + (1 + t) * LD;
-              if (started_before && lane == 0) carry_t[wave] = t;
-#pragma unroll
-              for (int e = 0; e < EL; ++e) {
-                dst[lane * EL + e] = acc[e];
-                acc[e] = 0.f;
-              }
-              started_before = false;
-              if (q + j + 1 < p1) {
-                do {
-                  ++t;
-                  bag_end = rfl(sm_pos[t + 1]);
-                } while (bag_end <= q + j + 1);
-              }
-            }
-          }
-        }
+      const uint64_t fallback = reinterpret_cast<uint64_t>(tbase[0]);
+      const uint64_t lane_off = static_cast<uint64_t>(lane) * LB;
+      Window wa, wb;
+      typename C::type va[WIN], vb[WIN];
+      prepare_window<WIN, RB>(wa, a, sm_beg, sm_pos, stage, sbag, tbase, T, p0, p1, fallback);
+      issue_window<C, WIN>(wa, va, lane_off);
+      for (int q = p0;;) {
+        prepare_window<WIN, RB>(wb, a, sm_beg, sm_pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
+        issue_window<C, WIN>(wb, vb, lane_off);
+        consume_window<DT, LB, WIN>(wa, va, acc, cur, Z, LD, carry + wave * D, carry_t + wave);
+        q += WIN;
+        if (q >= p1) break;
+        prepare_window<WIN, RB>(wa, a, sm_beg, sm_pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
+        issue_window<C, WIN>(wa, va, lane_off);
+        consume_window<DT, LB, WIN>(wb, vb, acc, cur, Z, LD, carry + wave * D, carry_t + wave);
+        q += WIN;
+        if (q >= p1) break;
       }
-      if (bag_end > p1) {  // the last bag continues in the next wave's range
-        float* dst = started_before ? carry + wave * D : Z + (1 + t) * LD;
-        if (started_before && lane == 0) carry_t[wave] = t;
-#pragma unroll
-        for (int e = 0; e < EL; ++e) dst[lane * EL + e] = acc[e];
-      }
-      if (bad) flag(a.status, DLRM_STATUS_BAD_INDEX);
     }
   }
   __syncthreads();
