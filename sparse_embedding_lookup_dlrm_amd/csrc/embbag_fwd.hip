@@ -449,17 +449,19 @@ __device__ __forceinline__ void acc_chunk(float* acc, const typename LaneChunk<L
 template <int DT, int LB>
 struct RowShape {
   static constexpr int EL = LB / Storage<DT>::bytes;  // fp32 columns per lane
-  static constexpr int WIN = LB >= 4 ? 96 / LB : 24;  // rows per window (two windows in flight: <= 48 VGPRs)
+  static constexpr int WIN = LB >= 4 ? 64 / LB : 16;  // rows per window (two windows in flight: 32 VGPRs)
 };
 
 struct RowLayout {
   int Tp;        // Z rows after e0 (T rounded up: 32 for MFMA, else to F multiple of 4)
   int LD;        // Z row stride in floats
-  int off_pos;   // byte offsets inside the dynamic LDS block
+  int off_beg;   // byte offsets inside the dynamic LDS block; bag tables are double-buffered
+  int off_pos;
+  int pos_stride;  // bytes between the two bag-table buffers
   int off_carry_t;
+  int off_tbase;
   int off_stage;
   int off_sbag;
-  int off_tbase;
   int off_carry;
   int off_out;
   int off_z;
@@ -474,14 +476,16 @@ __host__ __device__ inline RowLayout make_row_layout(int T, int D, bool mfma) {
   L.LD = D + 4;
   const int P = (T + 1) * T / 2;
   int o = 0;
-  o += align16(T * 4);                 // bag begin (global index position)
-  L.off_pos = o; o += align16((T + 1) * 4);
+  L.pos_stride = align16(T * 4) + align16((T + 1) * 4);
+  L.off_beg = o;                       // [2] x { bag begin (index position) [T]; stream start [T+1] }
+  L.off_pos = o + align16(T * 4);
+  o += 2 * L.pos_stride;
   L.off_carry_t = o; o += align16(kRowWaves * 4);
-  const int uni = o;                   // union { stage + carry ; output staging }
+  L.off_tbase = o; o += align16(T * 8);
+  const int uni = o;                   // union { stage + bag ids + carries ; output staging }
   L.off_stage = uni;
   L.off_sbag = L.off_stage + kStageCap * 4;
-  L.off_tbase = L.off_sbag + align16(kStageCap);
-  L.off_carry = L.off_tbase + align16(T * 8);
+  L.off_carry = L.off_sbag + align16(kStageCap);
   const int gather_bytes = L.off_carry + kRowWaves * D * 4 - uni;
   L.off_out = uni;
   const int out_bytes = (D + P) * 4;
@@ -636,191 +640,286 @@ __device__ __forceinline__ void consume_window(const Window& w, typename LaneChu
   }
 }
 
+// Bag (t, b): clamp its CSR range into [0, nnz], report an invalid CSR, and
+// publish begin and length for the stream-position scan.
+__device__ __forceinline__ void publish_bag(const FwdArgs& a, int t, int b, int s0, int s1, int* beg, int* pos) {
+  bool bad = false;
+  if (t == 0 && b == 0 && s0 != 0) bad = true;
+  if (t == a.T - 1 && b == a.B - 1 && static_cast<int64_t>(s1) != a.nnz) bad = true;
+  if (s0 < 0) { s0 = 0; bad = true; }
+  if (static_cast<int64_t>(s0) > a.nnz) { s0 = static_cast<int>(a.nnz); bad = true; }
+  if (static_cast<int64_t>(s1) > a.nnz) { s1 = static_cast<int>(a.nnz); bad = true; }
+  if (s1 < s0) { s1 = s0; bad = true; }
+  if (bad) flag(a.status, DLRM_STATUS_BAD_OFFSETS);
+  beg[t] = s0;
+  pos[t + 1] = s1 - s0;  // a length until scan_positions runs
+}
+
+// Z row of an empty bag: no gather writes it, so it is cleared here.
+__device__ __forceinline__ void clear_if_empty(const int* pos, int t, float* Z, int LD, int D) {
+  if (pos[t + 1] == 0) {
+    float* z = Z + (1 + t) * LD;
+    for (int d = 0; d < D; d += 4) *reinterpret_cast<float4*>(z + d) = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// Inclusive scan of the bag lengths into stream start positions (one wave).
+__device__ __forceinline__ void scan_positions(int* pos, int T) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int carry_sum = 0;
+  for (int t0 = 0; t0 < T; t0 += kWave) {
+    const int t = t0 + lane;
+    int v = t < T ? pos[t + 1] : 0;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(v, o, kWave);
+      if (lane >= o) v += y;
+    }
+    if (t < T) pos[t + 1] = v + carry_sum;
+    carry_sum += __shfl(v, kWave - 1, kWave);
+  }
+  if (lane == 0) pos[0] = 0;
+}
+
+constexpr int kStagePerThread = kStageCap / kRowThreads;
+
+// Issue the loads of a sample's staged indices (stream positions tid + k*512);
+// the values are written to LDS later by write_stage.
+__device__ __forceinline__ void load_stage(const FwdArgs& a, const int* beg, const int* pos, int T, int N,
+                                           int (&r)[kStagePerThread], int (&tb)[kStagePerThread]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < kStagePerThread; ++k) {
+    const int p = tid + k * kRowThreads;
+    r[k] = 0;
+    tb[k] = -1;
+    if (p < N) {
+      int lo = 0, hi = T;  // last t with pos[t] <= p (skips empty bags)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pos[mid] <= p) lo = mid;
+        else hi = mid;
+      }
+      tb[k] = lo;
+      r[k] = a.indices[beg[lo] + (p - pos[lo])];
+    }
+  }
+}
+
+__device__ __forceinline__ void write_stage(const FwdArgs& a, const int (&r)[kStagePerThread],
+                                            const int (&tb)[kStagePerThread], int* stage, uint8_t* sbag) {
+  const int tid = threadIdx.x;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < kStagePerThread; ++k) {
+    if (tb[k] >= 0) {
+      int v = r[k];
+      if (v < 0 || v >= a.tabs.rows[tb[k]]) { bad = true; v = -1; }
+      stage[tid + k * kRowThreads] = v;
+      sbag[tid + k * kRowThreads] = static_cast<uint8_t>(tb[k]);
+    }
+  }
+  if (bad) flag(a.status, DLRM_STATUS_BAD_INDEX);
+}
+
+// Persistent workgroups: each takes a contiguous chunk of samples and runs,
+// per sample, [gather | prefetch next offsets and e0] -> [carries, scan of the
+// next sample] -> [interaction | next sample's index loads in flight] ->
+// [output] -> [stage next indices, reset Z]. The round trips of the next
+// sample's offsets, e0 and indices overlap this sample's gather and
+// interaction.
 template <int DT, int LB, bool MFMA>
-__global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, RowLayout L) {
+__global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, RowLayout L, int chunk) {
   using C = LaneChunk<LB>;
   using RS = RowShape<DT, LB>;
   constexpr int EL = RS::EL;
   constexpr int WIN = RS::WIN;
   constexpr int RB = LB * kWave;  // row bytes
   extern __shared__ __align__(16) char lds[];
-  int* sm_beg = reinterpret_cast<int*>(lds);
-  int* sm_pos = reinterpret_cast<int*>(lds + L.off_pos);
   int* carry_t = reinterpret_cast<int*>(lds + L.off_carry_t);
+  const char** tbase = reinterpret_cast<const char**>(lds + L.off_tbase);
   int* stage = reinterpret_cast<int*>(lds + L.off_stage);
   uint8_t* sbag = reinterpret_cast<uint8_t*>(lds + L.off_sbag);
-  const char** tbase = reinterpret_cast<const char**>(lds + L.off_tbase);
   float* carry = reinterpret_cast<float*>(lds + L.off_carry);
   float* outs = reinterpret_cast<float*>(lds + L.off_out);
   float* Z = reinterpret_cast<float*>(lds + L.off_z);
 
-  const int T = a.T, B = a.B, D = a.D, LD = L.LD;
-  const int b = xcd_block(blockIdx.x, gridDim.x);
+  const int T = a.T, D = a.D, LD = L.LD;
+  const int W = D + (T + 1) * T / 2;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = rfl(tid >> 6);
+  const int b_begin = xcd_block(blockIdx.x, gridDim.x) * chunk;
+  const int b_end = min(a.B, b_begin + chunk);
+  if (b_begin >= b_end) return;  // whole workgroup
 
-  // 1. bag ranges, Z cleared, e0 into Z row 0
-  if (tid < T) {
-    int s0 = a.offsets[tid * B + b], s1 = a.offsets[tid * B + b + 1];
-    bool bad = false;
-    if (tid == 0 && b == 0 && s0 != 0) bad = true;
-    if (tid == T - 1 && b == B - 1 && static_cast<int64_t>(s1) != a.nnz) bad = true;
-    if (s0 < 0) { s0 = 0; bad = true; }
-    if (static_cast<int64_t>(s0) > a.nnz) { s0 = static_cast<int>(a.nnz); bad = true; }
-    if (static_cast<int64_t>(s1) > a.nnz) { s1 = static_cast<int>(a.nnz); bad = true; }
-    if (s1 < s0) { s1 = s0; bad = true; }
-    if (bad) flag(a.status, DLRM_STATUS_BAD_OFFSETS);
-    sm_beg[tid] = s0;
-    sm_pos[tid + 1] = s1 - s0;  // lengths for now
-    tbase[tid] = static_cast<const char*>(a.tabs.ptr[tid]);
-  }
-  if (tid < kRowWaves) carry_t[tid] = -1;
-  for (int i = tid; i < (1 + L.Tp) * LD; i += kRowThreads) Z[i] = 0.f;
-  __syncthreads();
-  for (int d = tid; d < D; d += kRowThreads) Z[d] = a.e0[static_cast<size_t>(b) * D + d];
-  if (wave == 0) {  // inclusive scan of the lengths -> stream positions
-    int carry_sum = 0;
-    for (int t0 = 0; t0 < T; t0 += kWave) {
-      const int t = t0 + lane;
-      int v = t < T ? sm_pos[t + 1] : 0;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(v, o, kWave);
-        if (lane >= o) v += y;
-      }
-      if (t < T) sm_pos[t + 1] = v + carry_sum;
-      carry_sum += __shfl(v, kWave - 1, kWave);
-    }
-    if (lane == 0) sm_pos[0] = 0;
-  }
-  __syncthreads();
-  const int N = rfl(sm_pos[T]);
-
-  // 2. stage the sample's indices (validated) in stream order: every thread
-  //    issues all of its index loads before writing any, so the whole sample
-  //    costs one round trip.
+  // ---- prologue: first sample's bags, positions, indices, e0
+  int pb = 0;
   {
-    constexpr int K = kStageCap / kRowThreads;
-    int r[K], tb[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int p = tid + k * kRowThreads;
-      r[k] = 0;
-      tb[k] = -1;
-      if (p < N) {
-        int lo = 0, hi = T;  // last t with sm_pos[t] <= p (skips empty bags)
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (sm_pos[mid] <= p) lo = mid;
-          else hi = mid;
-        }
-        tb[k] = lo;
-        r[k] = a.indices[sm_beg[lo] + (p - sm_pos[lo])];
-      }
+    int* beg = reinterpret_cast<int*>(lds + L.off_beg);
+    int* pos = reinterpret_cast<int*>(lds + L.off_pos);
+    if (tid < T) {
+      publish_bag(a, tid, b_begin, a.offsets[tid * a.B + b_begin], a.offsets[tid * a.B + b_begin + 1], beg, pos);
+      tbase[tid] = static_cast<const char*>(a.tabs.ptr[tid]);
+      clear_if_empty(pos, tid, Z, LD, D);
     }
-    bool bad = false;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      if (tb[k] >= 0) {
-        int v = r[k];
-        if (v < 0 || v >= a.tabs.rows[tb[k]]) { bad = true; v = -1; }
-        stage[tid + k * kRowThreads] = v;
-        sbag[tid + k * kRowThreads] = static_cast<uint8_t>(tb[k]);
-      }
-    }
-    if (bad) flag(a.status, DLRM_STATUS_BAD_INDEX);
+    __syncthreads();
+    for (int d = tid; d < D; d += kRowThreads) Z[d] = a.e0[static_cast<size_t>(b_begin) * D + d];
+    if (wave == 0) scan_positions(pos, T);
+    __syncthreads();
+    int r[kStagePerThread], tb[kStagePerThread];
+    load_stage(a, beg, pos, T, rfl(pos[T]), r, tb);
+    write_stage(a, r, tb, stage, sbag);
+    if (tid < kRowWaves) carry_t[tid] = -1;
+    __syncthreads();
   }
-  __syncthreads();
 
-  // 3. gather: wave w sums stream positions [p0, p1) in windows of WIN rows.
-  //    For each window every lane first works out the address of "its" row and
-  //    whether a sum ends there; the loads of window k+1 are issued before
-  //    window k is summed, so a wave always has one window of rows in flight.
-  //    Slots past the range load a fixed in-bounds row (a cache hit) and are
-  //    zeroed, which keeps the number of loads per window constant.
-  {
-    const int p0 = static_cast<int>((static_cast<long long>(N) * wave) / kRowWaves);
-    const int p1 = static_cast<int>((static_cast<long long>(N) * (wave + 1)) / kRowWaves);
-    if (p0 < p1) {
-      int t0 = 0;
-      while (rfl(sm_pos[t0 + 1]) <= p0) ++t0;
-      RowCursor cur{to_carry_init(sm_pos, t0, p0)};
-      float acc[EL];
+  for (int b = b_begin; b < b_end; ++b) {
+    const bool has_next = b + 1 < b_end;
+    int* beg = reinterpret_cast<int*>(lds + L.off_beg + pb * L.pos_stride);
+    int* pos = reinterpret_cast<int*>(lds + L.off_pos + pb * L.pos_stride);
+    int* nbeg = reinterpret_cast<int*>(lds + L.off_beg + (pb ^ 1) * L.pos_stride);
+    int* npos = reinterpret_cast<int*>(lds + L.off_pos + (pb ^ 1) * L.pos_stride);
+    const int N = rfl(pos[T]);
+
+    // next sample's bag ranges and e0: loads in flight during the gather
+    int nx0 = 0, nx1 = 0;
+    float ne0 = 0.f;
+    if (has_next) {
+      if (tid < T) {
+        nx0 = a.offsets[tid * a.B + b + 1];
+        nx1 = a.offsets[tid * a.B + b + 2];
+      }
+      if (tid < D) ne0 = a.e0[static_cast<size_t>(b + 1) * D + tid];
+    }
+
+    // gather: wave w sums stream positions [p0, p1) in windows of WIN rows.
+    // Each lane first works out the address of "its" row of a window and
+    // whether a sum ends there; window k+1's loads are issued before window k
+    // is summed. Slots past the range load a fixed in-bounds row (a cache
+    // hit) and are zeroed, so every window issues the same number of loads.
+    {
+      const int p0 = static_cast<int>((static_cast<long long>(N) * wave) / kRowWaves);
+      const int p1 = static_cast<int>((static_cast<long long>(N) * (wave + 1)) / kRowWaves);
+      if (p0 < p1) {
+        int t0 = 0;
+        while (rfl(pos[t0 + 1]) <= p0) ++t0;
+        RowCursor cur{rfl(pos[t0]) < p0};
+        float acc[EL];
 #pragma unroll
-      for (int e = 0; e < EL; ++e) acc[e] = 0.f;
-      const uint64_t fallback = reinterpret_cast<uint64_t>(tbase[0]);
-      const uint64_t lane_off = static_cast<uint64_t>(lane) * LB;
-      Window wa, wb;
-      typename C::type va[WIN], vb[WIN];
-      prepare_window<WIN, RB>(wa, a, sm_beg, sm_pos, stage, sbag, tbase, T, p0, p1, fallback);
-      issue_window<C, WIN>(wa, va, lane_off);
-      for (int q = p0;;) {
-        prepare_window<WIN, RB>(wb, a, sm_beg, sm_pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
-        issue_window<C, WIN>(wb, vb, lane_off);
-        consume_window<DT, LB, WIN>(wa, va, acc, cur, Z, LD, carry + wave * D, carry_t + wave);
-        q += WIN;
-        if (q >= p1) break;
-        prepare_window<WIN, RB>(wa, a, sm_beg, sm_pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
+        for (int e = 0; e < EL; ++e) acc[e] = 0.f;
+        const uint64_t fallback = reinterpret_cast<uint64_t>(tbase[0]);
+        const uint64_t lane_off = static_cast<uint64_t>(lane) * LB;
+        Window wa, wb;
+        typename C::type va[WIN], vb[WIN];
+        prepare_window<WIN, RB>(wa, a, beg, pos, stage, sbag, tbase, T, p0, p1, fallback);
         issue_window<C, WIN>(wa, va, lane_off);
-        consume_window<DT, LB, WIN>(wb, vb, acc, cur, Z, LD, carry + wave * D, carry_t + wave);
-        q += WIN;
-        if (q >= p1) break;
+        for (int q = p0;;) {
+          prepare_window<WIN, RB>(wb, a, beg, pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
+          issue_window<C, WIN>(wb, vb, lane_off);
+          consume_window<DT, LB, WIN>(wa, va, acc, cur, Z, LD, carry + wave * D, carry_t + wave);
+          q += WIN;
+          if (q >= p1) break;
+          prepare_window<WIN, RB>(wa, a, beg, pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
+          issue_window<C, WIN>(wa, va, lane_off);
+          consume_window<DT, LB, WIN>(wb, vb, acc, cur, Z, LD, carry + wave * D, carry_t + wave);
+          q += WIN;
+          if (q >= p1) break;
+        }
       }
     }
-  }
-  __syncthreads();
-  // bags cut by a range boundary: add the later parts in wave order
-  for (int d = tid; d < D; d += kRowThreads) {
-    for (int w = 1; w < kRowWaves; ++w) {
-      const int t = carry_t[w];
-      if (t >= 0) Z[(1 + t) * LD + d] += carry[w * D + d];
+    bool next_empty = false;
+    if (has_next && tid < T) {
+      publish_bag(a, tid, b + 1, nx0, nx1, nbeg, npos);
+      next_empty = npos[tid + 1] == 0;
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // 4. interaction into the output staging area (which overlays the index stage)
-  for (int d = tid; d < D; d += kRowThreads) outs[d] = Z[d];
-  if constexpr (MFMA) {
-    const int nt = L.Tp / 32;
-    const int ntiles = nt * (nt + 1) / 2;
-    for (int tile = wave; tile < ntiles; tile += kRowWaves) {
-      int I, J;
-      block_pair(tile, I, J);
-      gram_tile_mfma(Z, LD, D, T, I, J, outs);
-    }
-  } else {
-    const Tile tl = make_tile(T, D, 1);
-    for (int w = tid; w < tl.nblk; w += kRowThreads) {
-      int bi, bj;
-      block_pair(w, bi, bj);
-      dots_block<true>(Z, tl.F, D, LD, bi, bj, outs + D);
-    }
-  }
-  if constexpr (MFMA) {  // dots of e0 with every pooled row: pair (zi, 0) sits at zi(zi-1)/2
-    for (int zi = 1 + (kRowThreads - 1 - tid); zi <= T; zi += kRowThreads) {
-      const float* zr = Z + zi * LD;
-      float s = 0.f;
-      for (int d = 0; d < D; d += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(zr + d);
-        const float4 y = *reinterpret_cast<const float4*>(Z + d);
-        s = fmaf(x.x, y.x, s);
-        s = fmaf(x.y, y.y, s);
-        s = fmaf(x.z, y.z, s);
-        s = fmaf(x.w, y.w, s);
+    // bags cut by a range boundary: add the later parts in wave order; scan the next positions
+    for (int d = tid; d < D; d += kRowThreads) {
+      for (int w = 1; w < kRowWaves; ++w) {
+        const int t = carry_t[w];
+        if (t >= 0) Z[(1 + t) * LD + d] += carry[w * D + d];
       }
-      outs[D + zi * (zi - 1) / 2] = s;
     }
-  }
-  __syncthreads();
-  const int W = D + (T + 1) * T / 2;
-  float* o = a.out_inter + static_cast<size_t>(b) * W;
-  for (int i = tid; i < W; i += kRowThreads) store_stream(o + i, outs[i]);
-  if (a.out_pooled) {
-    float* op = a.out_pooled + static_cast<size_t>(b) * T * D;
-    for (int i = tid; i < T * D; i += kRowThreads) {
-      const int t = i / D, d = i - t * D;
-      op[i] = Z[(1 + t) * LD + d];
+    if (has_next && wave == kRowWaves - 1) scan_positions(npos, T);
+    __syncthreads();
+
+    // next sample's index loads go out now; their values are staged after the output
+    int r[kStagePerThread], tb[kStagePerThread];
+    if (has_next) load_stage(a, nbeg, npos, T, rfl(npos[T]), r, tb);
+    else {
+#pragma unroll
+      for (int k = 0; k < kStagePerThread; ++k) { r[k] = 0; tb[k] = -1; }
     }
+
+    // interaction into the output staging area (which overlays the index stage)
+    for (int d = tid; d < D; d += kRowThreads) outs[d] = Z[d];
+    if constexpr (MFMA) {
+      const int nt = L.Tp / 32;
+      const int ntiles = nt * (nt + 1) / 2;
+      for (int tile = wave; tile < ntiles; tile += kRowWaves) {
+        int I, J;
+        block_pair(tile, I, J);
+        gram_tile_mfma(Z, LD, D, T, I, J, outs);
+      }
+      // dots of e0 with every pooled row (pair (zi, 0) sits at zi(zi-1)/2), on the
+      // waves that hold no Gram tile: 4 lanes per dot, each over a quarter of D,
+      // combined in a fixed order
+      const int spare = (ntiles < kRowWaves) ? kRowWaves - ntiles : kRowWaves;
+      const int first = kRowWaves - spare;
+      if (wave >= first) {
+        const int slot = tid - first * kWave;
+        const int quarter = slot & 3;
+        const int dq = D / 4;
+        for (int zi = 1 + (slot >> 2); zi <= T; zi += spare * kWave / 4) {
+          const float* zr = Z + zi * LD + quarter * dq;
+          const float* z0 = Z + quarter * dq;
+          float sum = 0.f;
+          for (int d = 0; d < dq; d += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(zr + d);
+            const float4 y = *reinterpret_cast<const float4*>(z0 + d);
+            sum = fmaf(x.x, y.x, sum);
+            sum = fmaf(x.y, y.y, sum);
+            sum = fmaf(x.z, y.z, sum);
+            sum = fmaf(x.w, y.w, sum);
+          }
+          sum += __shfl_xor(sum, 1, kWave);
+          sum += __shfl_xor(sum, 2, kWave);
+          if (quarter == 0) outs[D + zi * (zi - 1) / 2] = sum;
+        }
+      }
+    } else {
+      const Tile tl = make_tile(T, D, 1);
+      for (int w = tid; w < tl.nblk; w += kRowThreads) {
+        int bi, bj;
+        block_pair(w, bi, bj);
+        dots_block<true>(Z, tl.F, D, LD, bi, bj, outs + D);
+      }
+    }
+    __syncthreads();
+    float* o = a.out_inter + static_cast<size_t>(b) * W;
+    for (int i = tid; i < W; i += kRowThreads) store_stream(o + i, outs[i]);
+    if (a.out_pooled) {
+      float* op = a.out_pooled + static_cast<size_t>(b) * T * D;
+      for (int i = tid; i < T * D; i += kRowThreads) {
+        const int t = i / D, d = i - t * D;
+        op[i] = Z[(1 + t) * LD + d];
+      }
+    }
+    __syncthreads();
+
+    // stage the next sample: indices, cleared Z with its e0, no carries
+    if (has_next) {
+      write_stage(a, r, tb, stage, sbag);
+      if (next_empty) {
+        float* z = Z + (1 + tid) * LD;
+        for (int d = 0; d < D; d += 4) *reinterpret_cast<float4*>(z + d) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (tid < kRowWaves) carry_t[tid] = -1;
+      if (tid < D) Z[tid] = ne0;
+      __syncthreads();
+    }
+    pb ^= 1;
   }
 }
 
@@ -861,18 +960,38 @@ size_t fwd_lds_bytes(int T, int D, int dtype) {
   return tl.z_floats() * 4 + static_cast<size_t>(T) * 2 * 4;
 }
 
+// Persistent grid: as many 512-thread workgroups as the device keeps resident
+// at this LDS size, each with a contiguous chunk of samples.
+template <class K>
+static int resident_blocks(K kernel, size_t lds) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kRowThreads, lds) != hipSuccess) return 0;
+  return cus * (per_cu > 0 ? per_cu : 1);
+}
+
+template <int DT, int LB, bool MFMA>
+static hipError_t launch_rows_v(const FwdArgs& a, const RowLayout& L, hipStream_t st) {
+  auto kernel = fused_rows_kernel<DT, LB, MFMA>;
+  // Two samples per workgroup: the second sample's offsets, e0 and indices are
+  // fetched while the first is gathered, and the hardware dispatcher balances
+  // the many short-lived workgroups across CUs.
+  const int chunk = a.B >= 2 * resident_blocks(kernel, static_cast<size_t>(L.bytes)) ? 2 : 1;
+  const int grid = (a.B + chunk - 1) / chunk;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kRowThreads), L.bytes, st, a, L, chunk);
+  return hipGetLastError();
+}
+
 template <int DT, int LB>
 static hipError_t launch_rows(const FwdArgs& a, hipStream_t st) {
   const bool mfma = use_mfma(a.T, a.D, DT);
   const RowLayout L = make_row_layout(a.T, a.D, mfma);
   if (static_cast<size_t>(L.bytes) > kMaxLds) return hipErrorInvalidValue;
-  if (mfma) {
-    if constexpr (DT != DLRM_F32)
-      hipLaunchKernelGGL((fused_rows_kernel<DT, LB, true>), dim3(a.B), dim3(kRowThreads), L.bytes, st, a, L);
-  } else {
-    hipLaunchKernelGGL((fused_rows_kernel<DT, LB, false>), dim3(a.B), dim3(kRowThreads), L.bytes, st, a, L);
+  if constexpr (DT != DLRM_F32) {
+    if (mfma) return launch_rows_v<DT, LB, true>(a, L, st);
   }
-  return hipGetLastError();
+  return launch_rows_v<DT, LB, false>(a, L, st);
 }
 
 template <int DT, int LPR>
