@@ -924,6 +924,398 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
 }
 
 // ---------------------------------------------------------------------------
+// warp-specialised fused forward for large samples (MFMA interaction)
+// ---------------------------------------------------------------------------
+// One 1024-thread workgroup per CU walks a contiguous chunk of samples. Waves
+// 0..11 only gather: in step s they sum the rows of sample s into Z[s&1].
+// Waves 12..15 meanwhile finish sample s-1 (Gram tiles and e0 dots from
+// Z[(s-1)&1] into an output buffer), write sample s-2's output to HBM, and
+// prepare sample s+1 (bag ranges, positions, staged indices, e0). Two
+// workgroup barriers per step: C_s (after G has added sample s-1's carried
+// partial sums and W has cleared the empty rows of s-1 and written s-2's
+// output) and the end of the step. The row stream therefore never waits for
+// the interaction, the output or the next sample's index round trips.
+constexpr int kWsThreads = 1024;
+constexpr int kWsWaves = kWsThreads / kWave;   // 16
+constexpr int kGWaves = 12;                    // gathering waves
+constexpr int kWsWorkers = kWsWaves - kGWaves;  // 4 worker waves
+constexpr int kWsPosPerLane = kStageCap / (kWsWorkers * kWave);  // staged positions per worker lane
+
+struct WsLayout {
+  int Tp, LD;
+  int off_tbase;
+  int off_beg[2], off_pos[2];
+  int off_carry_t[2];
+  int off_e0[3];
+  int off_stage[2], off_sbag[2];
+  int off_carry[2];
+  int off_out[2];
+  int off_z[2];
+  int bytes;
+};
+
+__host__ __device__ inline WsLayout make_ws_layout(int T, int D) {
+  WsLayout L;
+  L.Tp = ((T + 31) / 32) * 32;
+  L.LD = D + 4;
+  const int P = (T + 1) * T / 2;
+  int o = 0;
+  L.off_tbase = o; o += align16(T * 8);
+  for (int i = 0; i < 2; ++i) {
+    L.off_beg[i] = o; o += align16(T * 4);
+    L.off_pos[i] = o; o += align16((T + 1) * 4);
+    L.off_carry_t[i] = o; o += align16(kGWaves * 4);
+  }
+  for (int i = 0; i < 3; ++i) { L.off_e0[i] = o; o += align16(D * 4); }
+  for (int i = 0; i < 2; ++i) {
+    L.off_stage[i] = o; o += kStageCap * 4;
+    L.off_sbag[i] = o; o += align16(kStageCap);
+    L.off_carry[i] = o; o += kGWaves * D * 4;
+    L.off_out[i] = o; o += align16((D + P) * 4);
+  }
+  for (int i = 0; i < 2; ++i) { L.off_z[i] = o; o += (1 + L.Tp) * L.LD * 4; }
+  L.bytes = o;
+  return L;
+}
+
+template <int LB>
+struct WsShape {
+  static constexpr int WIN = LB >= 4 ? 128 / LB : 32;  // rows per window (two in flight: 64 VGPRs)
+};
+
+// Value of entry t (0..127) of a per-lane pair (v[0] in lane t, v[1] in lane t-64); all lanes take part.
+__device__ __forceinline__ int sel64(const int (&v)[2], int t) {
+  const int a0 = __shfl(v[0], t & (kWave - 1), kWave);
+  const int a1 = __shfl(v[1], t & (kWave - 1), kWave);
+  return t < kWave ? a0 : a1;
+}
+
+// Worker-side preparation of a sample, split so that its round trips overlap
+// other work: ws_load_offsets (issued two steps ahead), ws_begin (bag ranges
+// clamped and scanned in-wave, tables published by the first worker, index
+// and e0 loads issued) and ws_commit (values written to LDS). Every worker
+// wave computes the ranges and the scan itself, so no worker waits for another.
+constexpr int kWsLoaders = kWsWorkers - 1;  // waves 12..14 load and compute; wave 15 only stores
+constexpr int kWsE0PerLane = 3;      // D <= 512 over 192 loader lanes
+constexpr int kWsBagsPerWorker = 43;  // T <= 128 over 3 loader waves
+
+struct WsRaw {
+  int s0[2], s1[2];  // offsets of bags t = lane and lane + 64
+};
+
+struct WsPending {
+  int bg[2], ln[2], ps[2];  // begin, length, inclusive end of bags t = lane and lane + 64
+  int r[kWsBagsPerWorker];  // index of this lane's row in each of this wave's bags
+  float e0v[kWsE0PerLane];
+};
+
+__device__ __forceinline__ WsRaw ws_load_offsets(const FwdArgs& a, int b) {
+  const int lane = threadIdx.x & (kWave - 1);
+  WsRaw w;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = lane + h * kWave;
+    w.s0[h] = 0;
+    w.s1[h] = 0;
+    if (t < a.T) {
+      w.s0[h] = a.offsets[t * a.B + b];
+      w.s1[h] = a.offsets[t * a.B + b + 1];
+    }
+  }
+  return w;
+}
+
+// Entry t (0..127) of a lane-distributed pair, as a wave-uniform value.
+__device__ __forceinline__ int lane_get(const int (&v)[2], int t) {
+  const int a0 = __builtin_amdgcn_readlane(v[0], t & (kWave - 1));
+  const int a1 = __builtin_amdgcn_readlane(v[1], t & (kWave - 1));
+  return t < kWave ? a0 : a1;
+}
+
+__device__ __forceinline__ void ws_begin(const FwdArgs& a, const WsLayout& L, char* lds, int b, int buf,
+                                         const WsRaw& raw, WsPending& pd) {
+  const int T = a.T, D = a.D;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wk = rfl(threadIdx.x >> 6) - kGWaves;  // 0..3
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = lane + h * kWave;
+    pd.bg[h] = 0;
+    pd.ln[h] = 0;
+    if (t < T) {
+      int s0 = raw.s0[h], s1 = raw.s1[h];
+      bool bad = false;
+      if (t == 0 && b == 0 && s0 != 0) bad = true;
+      if (t == T - 1 && b == a.B - 1 && static_cast<int64_t>(s1) != a.nnz) bad = true;
+      if (s0 < 0) { s0 = 0; bad = true; }
+      if (static_cast<int64_t>(s0) > a.nnz) { s0 = static_cast<int>(a.nnz); bad = true; }
+      if (static_cast<int64_t>(s1) > a.nnz) { s1 = static_cast<int>(a.nnz); bad = true; }
+      if (s1 < s0) { s1 = s0; bad = true; }
+      if (bad && wk == 0) flag(a.status, DLRM_STATUS_BAD_OFFSETS);
+      pd.bg[h] = s0;
+      pd.ln[h] = s1 - s0;
+    }
+  }
+  int carry_sum = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {  // inclusive scan: end of bag t
+    int v = pd.ln[h];
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(v, o, kWave);
+      if (lane >= o) v += y;
+    }
+    pd.ps[h] = v + carry_sum;
+    carry_sum += __shfl(v, kWave - 1, kWave);
+  }
+  if (wk == 0) {
+    int* beg = reinterpret_cast<int*>(lds + L.off_beg[buf]);
+    int* pos = reinterpret_cast<int*>(lds + L.off_pos[buf]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = lane + h * kWave;
+      if (t < T) {
+        beg[t] = pd.bg[h];
+        pos[t + 1] = pd.ps[h];
+      }
+    }
+    if (lane == 0) pos[0] = 0;
+  }
+  // this wave's bags t = wk + 3j: lane i loads the index of the bag's row i
+  // (rows past 64 and positions past the staging area are handled elsewhere)
+#pragma unroll
+  for (int j = 0; j < kWsBagsPerWorker; ++j) {
+    const int t = wk + kWsLoaders * j;
+    pd.r[j] = 0;
+    if (t < T) {
+      const int len = lane_get(pd.ln, t);
+      const int start = lane_get(pd.ps, t) - len;
+      const int bbeg = lane_get(pd.bg, t);
+      if (lane < len && start + lane < kStageCap) pd.r[j] = a.indices[bbeg + lane];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kWsE0PerLane; ++k) {
+    const int d = wk * kWave + lane + k * kWsLoaders * kWave;
+    pd.e0v[k] = d < D ? a.e0[static_cast<size_t>(b) * D + d] : 0.f;
+  }
+}
+
+__device__ __forceinline__ void ws_commit(const FwdArgs& a, const WsLayout& L, char* lds, int buf, int e0buf,
+                                          const WsPending& pd) {
+  const int T = a.T;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wk = rfl(threadIdx.x >> 6) - kGWaves;
+  int* stage = reinterpret_cast<int*>(lds + L.off_stage[buf]);
+  uint8_t* sbag = reinterpret_cast<uint8_t*>(lds + L.off_sbag[buf]);
+  float* e0s = reinterpret_cast<float*>(lds + L.off_e0[e0buf]);
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < kWsBagsPerWorker; ++j) {
+    const int t = wk + kWsLoaders * j;
+    if (t < T) {
+      const int len = lane_get(pd.ln, t);
+      const int start = lane_get(pd.ps, t) - len;
+      const int rows = a.tabs.rows[t];
+      if (lane < len && start + lane < kStageCap) {
+        int v = pd.r[j];
+        if (v < 0 || v >= rows) { bad = true; v = -1; }
+        stage[start + lane] = v;
+        sbag[start + lane] = static_cast<uint8_t>(t);
+      }
+      if (len > kWave) {  // long bag: the rest of its staged rows, one round trip each
+        const int bbeg = lane_get(pd.bg, t);
+        for (int i = kWave + lane; i < len && start + i < kStageCap; i += kWave) {
+          int v = a.indices[bbeg + i];
+          if (v < 0 || v >= rows) { bad = true; v = -1; }
+          stage[start + i] = v;
+          sbag[start + i] = static_cast<uint8_t>(t);
+        }
+      }
+    }
+  }
+  if (bad) flag(a.status, DLRM_STATUS_BAD_INDEX);
+#pragma unroll
+  for (int k = 0; k < kWsE0PerLane; ++k) {
+    const int d = wk * kWave + lane + k * kWsLoaders * kWave;
+    if (d < a.D) e0s[d] = pd.e0v[k];
+  }
+  if (wk == 0 && lane < kGWaves) reinterpret_cast<int*>(lds + L.off_carry_t[buf])[lane] = -1;
+}
+
+template <int DT, int LB>
+__global__ __launch_bounds__(kWsThreads, 4) void fused_ws_kernel(FwdArgs a, WsLayout L, int chunk) {
+  using C = LaneChunk<LB>;
+  constexpr int EL = LB / Storage<DT>::bytes;
+  constexpr int WIN = WsShape<LB>::WIN;
+  constexpr int RB = LB * kWave;
+  extern __shared__ __align__(16) char lds[];
+  const char** tbase = reinterpret_cast<const char**>(lds + L.off_tbase);
+  const int T = a.T, D = a.D, LD = L.LD;
+  const int W = D + (T + 1) * T / 2;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = rfl(tid >> 6);
+  const bool isG = wave < kGWaves;
+  const int b0 = xcd_block(blockIdx.x, gridDim.x) * chunk;
+  const int nS = min(a.B - b0, chunk);
+  if (nS <= 0) return;  // whole workgroup
+
+  if (tid < T) tbase[tid] = static_cast<const char*>(a.tabs.ptr[tid]);
+  if (tid < kGWaves) {
+    reinterpret_cast<int*>(lds + L.off_carry_t[0])[tid] = -1;
+    reinterpret_cast<int*>(lds + L.off_carry_t[1])[tid] = -1;
+  }
+  WsRaw raw_next{};
+  if (!isG && wave < kWsWaves - 1) {
+    WsPending pd;
+    ws_begin(a, L, lds, b0, 0, ws_load_offsets(a, b0), pd);
+    ws_commit(a, L, lds, 0, 0, pd);
+    if (nS > 1) raw_next = ws_load_offsets(a, b0 + 1);
+  }
+  __syncthreads();
+
+  // Each role runs its own loop with the same two barriers per step, so the
+  // register allocator sees the two roles' state as disjoint. (The role test is
+  // uniform per wave and a workgroup barrier counts waves, whichever barrier
+  // instruction they reach.)
+  if (isG) {
+    Window wa, wb;
+    typename C::type va[WIN], vb[WIN];
+    float acc[EL];
+    RowCursor cur{false};
+    int q = 0, p1 = 0;
+    const uint64_t lane_off = static_cast<uint64_t>(lane) * LB;
+    const uint64_t fallback = reinterpret_cast<uint64_t>(tbase[0]);
+    for (int s = 0; s <= nS + 1; ++s) {
+      const int cb = s & 1, pb = cb ^ 1;
+      const int* beg = reinterpret_cast<const int*>(lds + L.off_beg[cb]);
+      const int* pos = reinterpret_cast<const int*>(lds + L.off_pos[cb]);
+      const int* stage = reinterpret_cast<const int*>(lds + L.off_stage[cb]);
+      const uint8_t* sbag = reinterpret_cast<const uint8_t*>(lds + L.off_sbag[cb]);
+      float* Zc = reinterpret_cast<float*>(lds + L.off_z[cb]);
+      float* Zp = reinterpret_cast<float*>(lds + L.off_z[pb]);
+      if (s >= 1 && s <= nS) {  // carried partial sums of sample s-1, in wave order
+        const int* ct = reinterpret_cast<const int*>(lds + L.off_carry_t[pb]);
+        const float* cy = reinterpret_cast<const float*>(lds + L.off_carry[pb]);
+        for (int d = tid; d < D; d += kGWaves * kWave) {
+          for (int w = 1; w < kGWaves; ++w) {
+            const int t = ct[w];
+            if (t >= 0) Zp[(1 + t) * LD + d] += cy[w * D + d];
+          }
+        }
+      }
+      __syncthreads();  // C_s
+      q = 0;
+      p1 = 0;
+      if (s < nS) {  // first two windows of sample s
+        const int N = rfl(pos[T]);
+        const int p0 = static_cast<int>((static_cast<long long>(N) * wave) / kGWaves);
+        p1 = static_cast<int>((static_cast<long long>(N) * (wave + 1)) / kGWaves);
+        q = p0;
+        if (p0 < p1) {
+          int t0 = 0;
+          while (rfl(pos[t0 + 1]) <= p0) ++t0;
+          cur.to_carry = rfl(pos[t0]) < p0;
+#pragma unroll
+          for (int e = 0; e < EL; ++e) acc[e] = 0.f;
+          prepare_window<WIN, RB>(wa, a, beg, pos, stage, sbag, tbase, T, p0, p1, fallback);
+          issue_window<C, WIN>(wa, va, lane_off);
+          prepare_window<WIN, RB>(wb, a, beg, pos, stage, sbag, tbase, T, p0 + WIN, p1, fallback);
+          issue_window<C, WIN>(wb, vb, lane_off);
+        }
+      }
+      if (q < p1) {
+        float* carry_w = reinterpret_cast<float*>(lds + L.off_carry[cb]) + wave * D;
+        int* carry_t_w = reinterpret_cast<int*>(lds + L.off_carry_t[cb]) + wave;
+        for (;;) {
+          consume_window<DT, LB, WIN>(wa, va, acc, cur, Zc, LD, carry_w, carry_t_w);
+          q += WIN;
+          if (q >= p1) break;
+          prepare_window<WIN, RB>(wa, a, beg, pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
+          issue_window<C, WIN>(wa, va, lane_off);
+          consume_window<DT, LB, WIN>(wb, vb, acc, cur, Zc, LD, carry_w, carry_t_w);
+          q += WIN;
+          if (q >= p1) break;
+          prepare_window<WIN, RB>(wb, a, beg, pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
+          issue_window<C, WIN>(wb, vb, lane_off);
+        }
+      }
+      __syncthreads();  // end of step
+    }
+  } else {
+    const int wk = wave - kGWaves;
+    if (wk == kWsLoaders) {
+      // writer wave: outputs, cleared rows and e0 dots; it issues no global load,
+      // so its stores never hold up a wait on a load
+      for (int s = 0; s <= nS + 1; ++s) {
+        const int cb = s & 1, pb = cb ^ 1;
+        float* Zp = reinterpret_cast<float*>(lds + L.off_z[pb]);
+        if (s >= 2) {  // output of sample s-2
+          const float* o = reinterpret_cast<const float*>(lds + L.off_out[cb]);
+          float* dst = a.out_inter + static_cast<size_t>(b0 + s - 2) * W;
+          for (int i = lane; i < W; i += kWave) store_stream(dst + i, o[i]);
+        }
+        if (s >= 1 && s <= nS) {  // rows of empty bags of sample s-1
+          const int* pp = reinterpret_cast<const int*>(lds + L.off_pos[pb]);
+          for (int t = lane; t < T; t += kWave) {
+            if (pp[t + 1] == pp[t]) {
+              float* z = Zp + (1 + t) * LD;
+              for (int d = 0; d < D; d += 4) *reinterpret_cast<float4*>(z + d) = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+          }
+        }
+        __syncthreads();  // C_s
+        if (s >= 1 && s <= nS) {  // e0 block and dots of e0 with every pooled row of sample s-1
+          float* outs = reinterpret_cast<float*>(lds + L.off_out[pb]);
+          const float* e0s = reinterpret_cast<const float*>(lds + L.off_e0[(s - 1) % 3]);
+          for (int d = lane; d < D; d += kWave) outs[d] = e0s[d];
+          for (int zi = 1 + lane; zi <= T; zi += kWave) {  // pair (zi, 0) sits at zi(zi-1)/2
+            const float* zr = Zp + zi * LD;
+            float sum = 0.f;
+            for (int d = 0; d < D; d += 4) {
+              const float4 x = *reinterpret_cast<const float4*>(zr + d);
+              const float4 y = *reinterpret_cast<const float4*>(e0s + d);
+              sum = fmaf(x.x, y.x, sum);
+              sum = fmaf(x.y, y.y, sum);
+              sum = fmaf(x.z, y.z, sum);
+              sum = fmaf(x.w, y.w, sum);
+            }
+            outs[D + zi * (zi - 1) / 2] = sum;
+          }
+        }
+        __syncthreads();  // end of step
+      }
+    } else {
+      // loader waves: prepare sample s+1 (its index and e0 loads, and the
+      // offsets of s+2, fly while the Gram tiles of sample s-1 are computed)
+      for (int s = 0; s <= nS + 1; ++s) {
+        const int pb = (s & 1) ^ 1;
+        float* Zp = reinterpret_cast<float*>(lds + L.off_z[pb]);
+        __syncthreads();  // C_s
+        WsPending pd;
+        const bool prep = s + 1 < nS;
+        if (prep) {
+          ws_begin(a, L, lds, b0 + s + 1, pb, raw_next, pd);
+          if (s + 2 < nS) raw_next = ws_load_offsets(a, b0 + s + 2);
+        }
+        if (s >= 1 && s <= nS) {
+          float* outs = reinterpret_cast<float*>(lds + L.off_out[pb]);
+          const int nt = L.Tp / 32;
+          const int ntiles = nt * (nt + 1) / 2;
+          for (int tile = wk; tile < ntiles; tile += kWsLoaders) {
+            int I, J;
+            block_pair(tile, I, J);
+            gram_tile_mfma(Zp, LD, D, T, I, J, outs);
+          }
+        }
+        if (prep) ws_commit(a, L, lds, pb, (s + 1) % 3, pd);
+        __syncthreads();  // end of step
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 int fwd_supported_row_bytes(int D, int dtype) {
@@ -984,7 +1376,40 @@ static hipError_t launch_rows_v(const FwdArgs& a, const RowLayout& L, hipStream_
 }
 
 template <int DT, int LB>
+static hipError_t launch_ws(const FwdArgs& a, hipStream_t st) {
+  const WsLayout L = make_ws_layout(a.T, a.D);
+  auto kernel = fused_ws_kernel<DT, LB>;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidValue;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorInvalidValue;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWsThreads, L.bytes) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  int grid = cus * per_cu;
+  if (grid > a.B) grid = a.B;
+  const int chunk = (a.B + grid - 1) / grid;
+  grid = (a.B + chunk - 1) / chunk;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWsThreads), L.bytes, st, a, L, chunk);
+  return hipGetLastError();
+}
+
+// The warp-specialised kernel pays off when a sample carries hundreds of rows
+// and there are many samples per CU; it needs the MFMA interaction.
+static bool use_ws(const FwdArgs& a, int dtype) {
+#ifndef DLRM_ENABLE_WS
+  (void)a;
+  (void)dtype;
+  return false;  // measured slower than the 3-workgroups-per-CU kernel on the 164 GB workload
+#endif
+  if (!use_mfma(a.T, a.D, dtype) || a.T > 2 * kWave) return false;
+  if (static_cast<size_t>(make_ws_layout(a.T, a.D).bytes) > kMaxLds) return false;
+  return a.nnz >= static_cast<int64_t>(256) * a.B && a.B >= 4096;
+}
+
+template <int DT, int LB>
 static hipError_t launch_rows(const FwdArgs& a, hipStream_t st) {
+  if constexpr (DT != DLRM_F32) {
+    if (use_ws(a, DT)) return launch_ws<DT, LB>(a, st);
+  }
   const bool mfma = use_mfma(a.T, a.D, DT);
   const RowLayout L = make_row_layout(a.T, a.D, mfma);
   if (static_cast<size_t>(L.bytes) > kMaxLds) return hipErrorInvalidValue;

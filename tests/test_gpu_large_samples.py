@@ -1,0 +1,94 @@
+"""Parity of the forward path used for large samples (hundreds of rows per sample,
+thousands of samples, 16-bit tables, T >= 24): one workgroup per CU walks a chunk of
+samples. The oracle checks seeded samples, chunk edges included; integer inputs
+make every output exact so those cases compare bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dlrm_oracle as orc
+from sparse_embedding_lookup_dlrm_amd import ops, synth
+
+from gpu_util import RTOL, assert_mag_close, dev_tables, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _sub_batch(w, tables, lengths, indices, e0, samples):
+    off = orc.lengths_to_offsets(lengths)
+    st, sl, si = [], [], []
+    for t in range(w.T):
+        segs = [indices[off[t * w.B + b]:off[t * w.B + b + 1]] for b in samples]
+        cat = np.concatenate(segs) if segs else np.zeros(0, np.int32)
+        uniq = np.unique(cat) if len(cat) else np.zeros(1, np.int32)
+        st.append(tables[t][uniq])
+        for sg in segs:
+            sl.append(len(sg))
+            si.append(np.searchsorted(uniq, sg).astype(np.int32))
+    return st, orc.lengths_to_offsets(sl), np.concatenate(si).astype(np.int32), e0[samples]
+
+
+def _check(w, lengths_override=None, exact=False):
+    b = synth.make_batch(w)
+    if lengths_override is not None:
+        b.lengths = lengths_override(b.lengths).astype(np.int32)
+        b.indices = synth.gen_indices(w, b.rows, b.lengths)
+    dev = "cuda"
+    tables = dev_tables(b.tables, w.dtype, dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    offsets = ops.lengths_to_offsets(torch.from_numpy(b.lengths).to(dev), status=status)
+    idx = torch.from_numpy(b.indices).to(dev)
+    e0 = torch.from_numpy(b.e0).to(dev)
+    _, out = ops.embbag_fwd(tables, offsets, idx, w.B, e0, status=status)
+    _, out2 = ops.embbag_fwd(tables, offsets, idx, w.B, e0, status=status)
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    assert torch.equal(out, out2)
+    rng = np.random.default_rng(7)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    chunk = -(-w.B // cus)
+    edges = [0, 1, chunk - 1, chunk, chunk + 1, 2 * chunk - 1, w.B - chunk, w.B - 2, w.B - 1]
+    samples = np.unique(np.clip(np.concatenate([edges, rng.choice(w.B, 48, replace=False)]), 0, w.B - 1))
+    st, so, si, se0 = _sub_batch(w, b.tables, b.lengths, b.indices, b.e0, samples)
+    r = orc.embbag_fwd(st, w.dtype, len(samples), so, si, se0)
+    got = out.cpu().numpy()[samples]
+    np.testing.assert_array_equal(got[:, :w.D], se0)
+    if exact:
+        np.testing.assert_array_equal(got[:, w.D:], r["out"][:, w.D:].astype(np.float32))
+    else:
+        absq = [t & np.uint16(0x7FFF) for t in st] if w.dtype == "bf16" else [np.abs(t) for t in st]
+        mag = orc.interact(np.abs(se0), orc.embbag_pool(absq, w.dtype, len(samples), so, si))
+        assert_mag_close(got[:, w.D:], r["out"][:, w.D:], mag[:, w.D:], RTOL[w.dtype], "large-sample dots")
+
+
+BASE = synth.Workload("large-64t-d128-bf16-b4096", T=64, rows=3000, D=128, dtype="bf16", B=4096,
+                      bag=("uniform", 1, 32), dist=("uniform",), seed=31)
+
+
+def test_large_samples_bf16():
+    _check(BASE)
+
+
+def test_large_samples_exact_integers():
+    _check(BASE.replace(values="int", seed=32), exact=True)
+
+
+def test_large_samples_beyond_index_stage_and_empty_bags():
+    """Bags of 0..60 rows: some samples exceed 2048 rows (indices read from HBM past the
+    staged part) and some bags are empty."""
+    def lengths(L):
+        rng = np.random.default_rng(3)
+        L = rng.integers(0, 61, size=L.shape)
+        L[::7] = 0
+        return L
+    _check(BASE.replace(seed=33, B=4608), lengths_override=lengths)
+
+
+def test_large_samples_fp16_T26():
+    _check(synth.Workload("large-26t-d64-fp16-b8192", T=26, rows=4000, D=64, dtype="f16", B=8192,
+                          bag=("uniform", 8, 30), dist=("zipf", 1.1), seed=34))
