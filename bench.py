@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "pooled lookups/sec + achieved HBM GB/s (% of peak) for fused embbag+interaction"
-FWD_KERNEL = "fused_kernel"
+FWD_KERNEL = "fused_rows_kernel"
 KERNEL_SOURCES = ["sparse_embedding_lookup_dlrm_amd/csrc/embbag_fwd.hip",
                   "sparse_embedding_lookup_dlrm_amd/csrc/common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_kernel_capacity-64t10m-d128-bf16-b16384_traffic.txt")
@@ -107,6 +107,56 @@ def summarize_profile(d: str, out: str, command: str, copy_bytes: float) -> None
         for (nm, c), v in sorted(agg.items()):
             lines.append(f"{nm[:90]} | {c} | {len(v)} | {sum(v) / len(v):.1f}")
     os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("\n".join(lines))
+
+
+COPY_KERNEL = "AUnaryFunctor"  # torch.mul(src, 1.0, out=dst): reads and writes n*4 bytes once
+
+
+def _counter_means(d: str, counter: str):
+    import csv
+
+    agg = {}
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    agg.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def _pick(means, needle):
+    hits = [(k, v) for k, v in means.items() if needle in k]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {needle!r} in the counter csv, found {len(hits)}")
+    return hits[0][1]
+
+
+def write_traffic(fetch_dir: str, write_dir: str, copy_gib: float, out: str, command: str) -> None:
+    """HBM bytes per launch of the fused forward from a FETCH_SIZE run and a WRITE_SIZE run
+    (KiB per dispatch), each scaled by what the same counter reads for a plain elementwise
+    copy of known size launched in the same process."""
+    known = int(copy_gib * (1 << 30)) // 4 * 4
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    f_kib, w_kib = _pick(fetch, FWD_KERNEL), _pick(write, FWD_KERNEL)
+    f_copy, w_copy = _pick(fetch, COPY_KERNEL), _pick(write, COPY_KERNEL)
+    f_factor = known / (f_copy * 1024.0)
+    w_factor = known / (w_copy * 1024.0)
+    traffic = f_kib * 1024.0 * f_factor + w_kib * 1024.0 * w_factor
+    lines = [f"# HBM traffic of {FWD_KERNEL} on the capacity workload (64 bf16 tables x 10M rows, D=128, B=16384)",
+             f"# command: {command}",
+             f"kernel_source_sha: {kernel_source_sha()}",
+             f"fetch_kib_per_launch: {f_kib:.1f}",
+             f"write_kib_per_launch: {w_kib:.1f}",
+             f"copy_bytes_read_and_written: {known}",
+             f"copy_fetch_kib: {f_copy:.1f}",
+             f"copy_write_kib: {w_copy:.1f}",
+             f"fetch_factor: {f_factor:.4f}",
+             f"write_factor: {w_factor:.4f}",
+             f"traffic_bytes_per_launch: {traffic:.0f}"]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     log("\n".join(lines))
@@ -230,16 +280,23 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-samples", type=int, default=1536)
+    ap.add_argument("--cpu-samples", type=int, default=6144)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain copy of this size (for counter calibration)")
     ap.add_argument("--summarize-profile", default=None)
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="rocprofv3 FETCH_SIZE and WRITE_SIZE csv dirs (runs made with --copy-calibration-gib) "
+                         "-> traffic file")
     ap.add_argument("--out", default=None)
     ap.add_argument("--command", default="")
     args = ap.parse_args()
 
+    if args.traffic:
+        write_traffic(args.traffic[0], args.traffic[1], args.copy_calibration_gib, args.out or TRAFFIC_FILE,
+                      args.command)
+        return 0
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.out, args.command, 0.0)
         return 0

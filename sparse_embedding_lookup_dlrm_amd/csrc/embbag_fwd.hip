@@ -171,23 +171,23 @@ __device__ __forceinline__ void dots_block(const float* Z, int F, int D, int LD,
   const float* zi = Z + (4 * bi) * LD;
   const float* zj = Z + (4 * bj) * LD;
   for (int d = 0; d < D; d += 4) {
-    float4 x[4], y[4];
+    float4 x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = *reinterpret_cast<const float4*>(zi + r * LD + d);
-      y[r] = *reinterpret_cast<const float4*>(zj + r * LD + d);
-    }
+    for (int r = 0; r < 4; ++r) x[r] = *reinterpret_cast<const float4*>(zi + r * LD + d);
+    // one column operand at a time keeps the live set at 16 + 4 + 16 registers
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int q = 0; q < 4; ++q) {
+      const float4 y = *reinterpret_cast<const float4*>(zj + q * LD + d);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int r = 0; r < 4; ++r) {
         float s = acc[r][q];
-        s = fmaf(x[r].x, y[q].x, s);
-        s = fmaf(x[r].y, y[q].y, s);
-        s = fmaf(x[r].z, y[q].z, s);
-        s = fmaf(x[r].w, y[q].w, s);
+        s = fmaf(x[r].x, y.x, s);
+        s = fmaf(x[r].y, y.y, s);
+        s = fmaf(x[r].z, y.z, s);
+        s = fmaf(x[r].w, y.w, s);
         acc[r][q] = s;
       }
+    }
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -774,6 +774,11 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
   }
 
   for (int b = b_begin; b < b_end; ++b) {
+    // The thread index is re-derived opaquely each sample so that the compiler
+    // recomputes per-thread addresses instead of keeping them live (and
+    // spilled) across the whole loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const bool has_next = b + 1 < b_end;
     int* beg = reinterpret_cast<int*>(lds + L.off_beg + pb * L.pos_stride);
     int* pos = reinterpret_cast<int*>(lds + L.off_pos + pb * L.pos_stride);

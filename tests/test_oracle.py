@@ -350,3 +350,58 @@ def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
                                   np.array(g["d_out"], np.float32), g["lr"])
         assert r["perm"].tolist() != g["perm"]
     assert np.array_equal(good, np.array(g["out"], dtype=np.float64))
+
+
+def test_planted_pool_decode_sgd_segment_mistakes(monkeypatch, golden_dir):
+    """More plausible oracle bugs, each caught by a pin that does not use the oracle's code."""
+    real_pool = orc.embbag_pool
+    real_decode = orc.decode
+    real_segments = orc.segments
+
+    # (d) pooling that drops the last row of every bag (off-by-one on the CSR end)
+    def short_pool(tables, dtype, B, offsets, indices):
+        off = np.asarray(offsets).copy()
+        T = len(tables)
+        pooled = np.zeros((B, T, tables[0].shape[1]))
+        for t in range(T):
+            for b in range(B):
+                s, e = int(off[t * B + b]), int(off[t * B + b + 1])
+                for p in range(s, max(s, e - 1)):
+                    pooled[b, t] += real_decode(tables[t][int(indices[p])], dtype)
+        return pooled
+    with monkeypatch.context() as m:
+        m.setattr(orc, "embbag_pool", short_pool)
+        with pytest.raises(AssertionError):
+            test_pool_equals_count_matrix_product(0)
+        with pytest.raises(AssertionError):
+            test_golden_forward(golden_dir)
+
+    # (e) bf16 decode with the wrong shift (bits << 15)
+    def bad_decode(table, dtype):
+        if dtype == "bf16":
+            return (table.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+        return real_decode(table, dtype)
+    with monkeypatch.context() as m:
+        m.setattr(orc, "decode", bad_decode)
+        with pytest.raises(AssertionError):
+            test_decode_bf16_and_f16_exact()
+
+    # (f) SGD with the wrong sign: caught by the hand-worked updated rows
+    g = _golden(golden_dir)
+    r = orc.embbag_bwd_update(_tables_f32(g), "f32", 2, np.array(g["offsets"]), np.array(g["indices"], np.int32),
+                              np.array(g["e0"], np.float32), np.array(g["pooled"], np.float64),
+                              np.array(g["d_out"], np.float32), -g["lr"])
+    assert not np.array_equal(r["new_rows"], np.array(g["new_rows"], dtype=np.float64))
+
+    # (g) segments that start a new run one position late
+    def late_segments(sorted_keys):
+        u, s = real_segments(sorted_keys)
+        s = s.copy()
+        s[1:-1] += 1
+        return u, s
+    with monkeypatch.context() as m:
+        m.setattr(orc, "segments", late_segments)
+        with pytest.raises(AssertionError):
+            test_golden_backward(golden_dir)
+        with pytest.raises(AssertionError):
+            test_stable_order_and_segments_brute_force(0)
