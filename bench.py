@@ -14,6 +14,10 @@ Printed (last line of stdout, one JSON object):
   backward     the sparse backward + SGD on the 26-table Zipf workload (timed
                the same way; reported next to the forward, not in `value`)
 
+The launch time of a repeated batch settles only after ~30 launches (the
+first ones run up to 25% slower while the clocks settle), so the default
+warm-up is 50 launches: the figure is the steady state of a repeated batch.
+
   python bench.py [--steps K] [--warmup W] [--gpus 1]
   python bench.py --summarize-profile DIR --out profiles/NAME.txt   (rocprofv3 csv -> summary)
 """
@@ -35,7 +39,7 @@ METRIC = "pooled lookups/sec + achieved HBM GB/s (% of peak) for fused embbag+in
 FWD_KERNEL = "fused_rows_kernel"
 KERNEL_SOURCES = ["sparse_embedding_lookup_dlrm_amd/csrc/embbag_fwd.hip",
                   "sparse_embedding_lookup_dlrm_amd/csrc/common.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_kernel_capacity-64t10m-d128-bf16-b16384_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"{FWD_KERNEL}_capacity-64t10m-d128-bf16-b16384_traffic.txt")
 
 
 def log(*a):
@@ -79,7 +83,7 @@ def read_traffic(sha: str):
 # ---------------------------------------------------------------------------
 # rocprofv3 csv -> text summary
 # ---------------------------------------------------------------------------
-def summarize_profile(d: str, out: str, command: str, copy_bytes: float) -> None:
+def summarize_profile(d: str, out: str, command: str, timed: int = 0) -> None:
     import csv
 
     lines = [f"# rocprofv3 summary of: {command}", f"# source directory: {d}"]
@@ -93,6 +97,17 @@ def summarize_profile(d: str, out: str, command: str, copy_bytes: float) -> None
             nm = r["Name"].split("(")[0][:90]
             lines.append(f"{nm} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                          f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}")
+    traces = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    for p in traces:
+        with open(p) as f:
+            rows = [r for r in csv.DictReader(f) if FWD_KERNEL in r["Kernel_Name"]]
+        if rows:
+            rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+            us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+            lines.append(f"## {FWD_KERNEL}: per-launch durations (us), in launch order")
+            lines.append(" ".join(f"{x:.1f}" for x in us))
+            if timed > 0 and len(us) >= timed:
+                lines.append(f"mean of the last {timed} launches (the timed steps): {sum(us[-timed:]) / timed:.2f} us")
     ctr = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     agg = {}
     for p in ctr:
@@ -279,7 +294,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-samples", type=int, default=6144)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
@@ -298,7 +313,7 @@ def main():
                       args.command)
         return 0
     if args.summarize_profile:
-        summarize_profile(args.summarize_profile, args.out, args.command, 0.0)
+        summarize_profile(args.summarize_profile, args.out, args.command, args.steps)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

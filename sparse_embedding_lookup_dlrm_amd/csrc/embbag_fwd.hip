@@ -358,11 +358,11 @@ __global__ __launch_bounds__(kThreads) void interact_kernel(int T, int B, int D,
 // barrier, so the result does not depend on timing.
 //
 // Interaction: with 16-bit tables and T >= 24 the Gram matrix of the T pooled
-// rows is a real dense contraction and runs on MFMA (32x32x16 bf16) with each
-// fp32 operand split into hi + lo bf16 parts (hi*hi + hi*lo + lo*hi, fp32
-// accumulation); otherwise 4x4 register blocks of fp32 FMAs. The dots of e0
-// with each pooled row use fp32 FMAs. [e0 | dots] is assembled in LDS and
-// written with contiguous stores.
+// rows is a real dense contraction and runs on MFMA (32x32x16 bf16): once the
+// dots of e0 with each pooled row are taken in fp32, every pooled row is split
+// in place into bf16 hi + lo parts, and each Gram tile sums hi*hi + hi*lo +
+// lo*hi in fp32. Otherwise 4x4 register blocks of fp32 FMAs. [e0 | dots] is
+// assembled in LDS and written with contiguous stores.
 constexpr int kRowThreads = 512;
 constexpr int kRowWaves = kRowThreads / kWave;
 constexpr int kStageCap = 2048;  // staged indices per sample; longer streams read indices from HBM
@@ -460,6 +460,7 @@ struct RowLayout {
   int pos_stride;  // bytes between the two bag-table buffers
   int off_carry_t;
   int off_tbase;
+  int off_trows;
   int off_stage;
   int off_sbag;
   int off_carry;
@@ -482,6 +483,7 @@ __host__ __device__ inline RowLayout make_row_layout(int T, int D, bool mfma) {
   o += 2 * L.pos_stride;
   L.off_carry_t = o; o += align16(kRowWaves * 4);
   L.off_tbase = o; o += align16(T * 8);
+  L.off_trows = o; o += align16(T * 4);
   const int uni = o;                   // union { stage + bag ids + carries ; output staging }
   L.off_stage = uni;
   L.off_sbag = L.off_stage + kStageCap * 4;
@@ -519,23 +521,61 @@ __device__ __forceinline__ void split_bf16x8(const float4& a, const float4& b, b
   lo = __builtin_bit_cast(bf16x8_t, l);
 }
 
-// One 32x32 tile (I, J) of the Gram matrix of the pooled rows; results with
-// Z-row indices zi > zj go to out[D + zi(zi-1)/2 + zj].
-__device__ __forceinline__ void gram_tile_mfma(const float* Z, int LD, int D, int T, int I, int J, float* out) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int m = lane & 31, kh = lane >> 5;
-  const float* za = Z + (1 + 32 * I + m) * LD + 8 * kh;
-  const float* zb = Z + (1 + 32 * J + m) * LD + 8 * kh;
-  floatx16_t acc = {};
-  for (int k0 = 0; k0 < D; k0 += 16) {
-    bf16x8_t ah, al, bh, bl;
-    split_bf16x8(*reinterpret_cast<const float4*>(za + k0), *reinterpret_cast<const float4*>(za + k0 + 4), ah, al);
-    if (I != J) {
-      split_bf16x8(*reinterpret_cast<const float4*>(zb + k0), *reinterpret_cast<const float4*>(zb + k0 + 4), bh, bl);
-    } else {
-      bh = ah;
-      bl = al;
+// Split pooled rows 1..Tp of Z in place: the D fp32 values of a row become D
+// bf16 hi parts (bytes [0, 2D) of the row) followed by D bf16 lo parts (bytes
+// [2D, 4D)). Every thread reads its values before any thread writes (a
+// workgroup barrier between), in chunks of whole rows, so no row is
+// overwritten while still unread. Ends with a barrier.
+__device__ __forceinline__ void split_rows(float* Z, int LD, int D, int Tp, int tid) {
+  const int gpr = D / 8;  // 8-value groups per row
+  const int rows_per_chunk = (2 * kRowThreads) / gpr > 0 ? (2 * kRowThreads) / gpr : 1;
+  for (int r0 = 1; r0 <= Tp; r0 += rows_per_chunk) {
+    const int r1 = min(Tp + 1, r0 + rows_per_chunk);
+    float4 x[2][2];
+    int off[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int idx = tid + k * kRowThreads;
+      const int row = r0 + idx / gpr, g = idx % gpr;
+      off[k] = -1;
+      if (row < r1) {
+        const float* z = Z + row * LD + 8 * g;
+        x[k][0] = *reinterpret_cast<const float4*>(z);
+        x[k][1] = *reinterpret_cast<const float4*>(z + 4);
+        off[k] = row * LD * 4 + 16 * g;  // byte offset of the group's hi part
+      }
     }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (off[k] >= 0) {
+        bf16x8_t hi, lo;
+        split_bf16x8(x[k][0], x[k][1], hi, lo);
+        char* zc = reinterpret_cast<char*>(Z);
+        *reinterpret_cast<bf16x8_t*>(zc + off[k]) = hi;
+        *reinterpret_cast<bf16x8_t*>(zc + off[k] + 2 * D) = lo;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// One 32x32 tile (I, J) of the Gram matrix of the pooled rows, from rows split
+// by split_rows: hi*hi + hi*lo + lo*hi with fp32 accumulation. Results with
+// Z-row indices zi > zj go to out[D + zi(zi-1)/2 + zj].
+__device__ __forceinline__ void gram_tile_mfma(const float* Z, int LD, int D, int T, int I, int J, float* out,
+                                               int tid) {
+  const int lane = tid & (kWave - 1);
+  const int m = lane & 31, kh = lane >> 5;
+  const char* za = reinterpret_cast<const char*>(Z + (1 + 32 * I + m) * LD) + 16 * kh;
+  const char* zb = reinterpret_cast<const char*>(Z + (1 + 32 * J + m) * LD) + 16 * kh;
+  const int lo = 2 * D;
+  floatx16_t acc = {};
+  for (int k0 = 0; k0 < 2 * D; k0 += 32) {  // bytes: 16 bf16 per step
+    const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(za + k0);
+    const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(za + lo + k0);
+    const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(zb + k0);
+    const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(zb + lo + k0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
@@ -545,6 +585,29 @@ __device__ __forceinline__ void gram_tile_mfma(const float* Z, int LD, int D, in
     const int row = 8 * (i >> 2) + 4 * kh + (i & 3);
     const int zi = 1 + 32 * I + row, zj = 1 + 32 * J + m;
     if (zi > zj && zi <= T) out[D + zi * (zi - 1) / 2 + zj] = acc[i];
+  }
+}
+
+// Dots of e0 (Z row 0) with every pooled row, in fp32 from the unsplit rows:
+// 8 lanes per dot, lane j over the float4 chunks j, j+8, ... of D, combined
+// in a fixed order. Pair (zi, 0) sits at out[D + zi(zi-1)/2].
+__device__ __forceinline__ void e0_dots(const float* Z, int LD, int D, int T, float* out, int tid) {
+  const int j = tid & 7;
+  for (int zi = 1 + (tid >> 3); zi <= T; zi += kRowThreads / 8) {
+    const float* zr = Z + zi * LD;
+    float sum = 0.f;
+    for (int d = 4 * j; d < D; d += 32) {
+      const float4 x = *reinterpret_cast<const float4*>(zr + d);
+      const float4 y = *reinterpret_cast<const float4*>(Z + d);
+      sum = fmaf(x.x, y.x, sum);
+      sum = fmaf(x.y, y.y, sum);
+      sum = fmaf(x.z, y.z, sum);
+      sum = fmaf(x.w, y.w, sum);
+    }
+    sum += __shfl_xor(sum, 1, kWave);
+    sum += __shfl_xor(sum, 2, kWave);
+    sum += __shfl_xor(sum, 4, kWave);
+    if (j == 0) out[D + zi * (zi - 1) / 2] = sum;
   }
 }
 
@@ -562,30 +625,46 @@ struct RowCursor {
 
 __device__ __forceinline__ bool to_carry_init(const int* sm_pos, int t0, int p0) { return rfl(sm_pos[t0]) < p0; }
 
-template <int WIN, int RB>
+// Largest t in [0, T) with pos[t] <= x, for non-decreasing pos with pos[0] <=
+// x: the bag (skipping empty ones) that holds stream position x. A fixed
+// number of halving steps, each one LDS read, so that independent searches of
+// one thread overlap instead of running as data-dependent loops.
+__device__ __forceinline__ int last_le(const int* pos, int T, int x) {
+  static_assert(DLRM_MAX_TABLES <= 128, "steps below cover T <= 128");
+  int lo = 0;
+#pragma unroll
+  for (int step = 64; step > 0; step >>= 1) {
+    const int c = lo + step;
+    const int v = pos[c < T ? c : T - 1];
+    if (c < T && v <= x) lo = c;
+  }
+  return lo;
+}
+
+// BEYOND: the range may reach past the staged positions (a sample of more than
+// kStageCap rows); only then does this read indices from HBM. Keeping that
+// path out of the common loop keeps the loop free of loads other than the
+// table rows, so the compiler's wait counts stay exact.
+template <int WIN, int RB, bool BEYOND>
 __device__ __forceinline__ void prepare_window(Window& w, const FwdArgs& a, const int* sm_beg, const int* sm_pos,
                                                const int* stage, const uint8_t* sbag, const char* const* tbase,
-                                               int T, int q, int p1, uint64_t fallback) {
-  const int lane = threadIdx.x & (kWave - 1);
+                                               const int* trows, int T, int q, int p1, uint64_t fallback,
+                                               int tid) {
+  const int lane = tid & (kWave - 1);
   uint64_t addr = fallback;
   int tk = 0;
   bool flush = false, skip = true;
   const int pos = q + lane;
   if (lane < WIN && pos < p1) {
     int r;
-    if (pos < kStageCap) {
+    if (!BEYOND || pos < kStageCap) {
       r = stage[pos];
       tk = sbag[pos];
     } else {  // beyond the staging area: locate the bag and read the index from HBM
-      int lo = 0, hi = T;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (sm_pos[mid] <= pos) lo = mid;
-        else hi = mid;
-      }
+      const int lo = last_le(sm_pos, T, pos);
       tk = lo;
       r = a.indices[sm_beg[lo] + (pos - sm_pos[lo])];
-      if (r < 0 || r >= a.tabs.rows[lo]) {
+      if (r < 0 || r >= trows[lo]) {
         r = -1;
         flag(a.status, DLRM_STATUS_BAD_INDEX);
       }
@@ -599,8 +678,9 @@ __device__ __forceinline__ void prepare_window(Window& w, const FwdArgs& a, cons
   w.alo = static_cast<uint32_t>(addr);
   w.ahi = static_cast<uint32_t>(addr >> 32);
   w.tk = tk;
-  w.fmask = __ballot(flush);
-  w.smask = __ballot(skip);
+  constexpr unsigned long long kWinMask = WIN >= 64 ? ~0ull : ((1ull << WIN) - 1);
+  w.fmask = __ballot(flush) & kWinMask;
+  w.smask = __ballot(skip) & kWinMask;
 }
 
 template <class C, int WIN>
@@ -612,17 +692,15 @@ __device__ __forceinline__ void issue_window(const Window& w, typename C::type (
 template <int DT, int LB, int WIN>
 __device__ __forceinline__ void consume_window(const Window& w, typename LaneChunk<LB>::type (&v)[WIN],
                                                float (&acc)[LB / Storage<DT>::bytes], RowCursor& cur, float* Z,
-                                               int LD, float* carry_w, int* carry_t_w) {
+                                               int LD, float* carry_w, int* carry_t_w, int tid) {
   constexpr int EL = LB / Storage<DT>::bytes;
-  const int lane = threadIdx.x & (kWave - 1);
-  if (w.smask) {
-#pragma unroll
-    for (int j = 0; j < WIN; ++j)
-      if ((w.smask >> j) & 1ull) v[j] = LaneChunk<LB>::zero();
-  }
+  const int lane = tid & (kWave - 1);
 #pragma unroll
   for (int j = 0; j < WIN; ++j) {
-    acc_chunk<DT, LB>(acc, v[j]);
+    // a skipped slot loaded a valid fallback row; it adds zero instead (a
+    // select, so the load's register is only read, never overwritten early)
+    const typename LaneChunk<LB>::type x = ((w.smask >> j) & 1ull) ? LaneChunk<LB>::zero() : v[j];
+    acc_chunk<DT, LB>(acc, x);
     if ((w.fmask >> j) & 1ull) {
       const int tj = __builtin_amdgcn_readlane(w.tk, j);
       float* dst = Z + (1 + tj) * LD;
@@ -664,8 +742,8 @@ __device__ __forceinline__ void clear_if_empty(const int* pos, int t, float* Z, 
 }
 
 // Inclusive scan of the bag lengths into stream start positions (one wave).
-__device__ __forceinline__ void scan_positions(int* pos, int T) {
-  const int lane = threadIdx.x & (kWave - 1);
+__device__ __forceinline__ void scan_positions(int* pos, int T, int tid) {
+  const int lane = tid & (kWave - 1);
   int carry_sum = 0;
   for (int t0 = 0; t0 < T; t0 += kWave) {
     const int t = t0 + lane;
@@ -684,42 +762,102 @@ __device__ __forceinline__ void scan_positions(int* pos, int T) {
 constexpr int kStagePerThread = kStageCap / kRowThreads;
 
 // Issue the loads of a sample's staged indices (stream positions tid + k*512);
-// the values are written to LDS later by write_stage.
+// the values are written to LDS later by write_stage. The bag of each
+// position is found first (LDS only); then every load is issued without a
+// branch, a position past the stream reading the sample's last index
+// instead, so that the loads land straight in r[] and nothing waits for them
+// before write_stage.
 __device__ __forceinline__ void load_stage(const FwdArgs& a, const int* beg, const int* pos, int T, int N,
-                                           int (&r)[kStagePerThread], int (&tb)[kStagePerThread]) {
-  const int tid = threadIdx.x;
+                                           int (&r)[kStagePerThread], int (&tb)[kStagePerThread], int tid) {
+  int off[kStagePerThread];
+  // with no indices at all, the (always valid) offsets array stands in
+  const int* src = a.nnz > 0 ? a.indices : a.offsets;
+  const int last = a.nnz > 0 ? static_cast<int>(a.nnz) - 1 : 0;
 #pragma unroll
   for (int k = 0; k < kStagePerThread; ++k) {
     const int p = tid + k * kRowThreads;
-    r[k] = 0;
-    tb[k] = -1;
-    if (p < N) {
-      int lo = 0, hi = T;  // last t with pos[t] <= p (skips empty bags)
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pos[mid] <= p) lo = mid;
-        else hi = mid;
-      }
-      tb[k] = lo;
-      r[k] = a.indices[beg[lo] + (p - pos[lo])];
-    }
+    const int pc = p < N ? p : (N > 0 ? N - 1 : 0);
+    const int lo = last_le(pos, T, pc);
+    tb[k] = p < N ? lo : -1;
+    const int o = beg[lo] + (pc - pos[lo]);
+    off[k] = o < 0 ? 0 : (o > last ? last : o);
   }
+#pragma unroll
+  for (int k = 0; k < kStagePerThread; ++k) r[k] = src[off[k]];
 }
 
 __device__ __forceinline__ void write_stage(const FwdArgs& a, const int (&r)[kStagePerThread],
-                                            const int (&tb)[kStagePerThread], int* stage, uint8_t* sbag) {
-  const int tid = threadIdx.x;
+                                            const int (&tb)[kStagePerThread], int* stage, uint8_t* sbag,
+                                            const int* trows, int tid) {
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < kStagePerThread; ++k) {
     if (tb[k] >= 0) {
       int v = r[k];
-      if (v < 0 || v >= a.tabs.rows[tb[k]]) { bad = true; v = -1; }
+      if (v < 0 || v >= trows[tb[k]]) { bad = true; v = -1; }
       stage[tid + k * kRowThreads] = v;
       sbag[tid + k * kRowThreads] = static_cast<uint8_t>(tb[k]);
     }
   }
   if (bad) flag(a.status, DLRM_STATUS_BAD_INDEX);
+}
+
+// An empty use of a value in registers: the compiler must have it (and so
+// wait for the load that produced it) at this point.
+__device__ __forceinline__ void touch(uint32_t x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void touch(uint2 x) { asm volatile("" ::"v"(x.x), "v"(x.y)); }
+__device__ __forceinline__ void touch(uint4 x) { asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w)); }
+
+// Sum stream positions [p0, p1) of one wave into Z rows (or the wave's carry
+// slot for a bag begun by an earlier wave), in windows of WIN rows: each lane
+// first works out the address of "its" row of a window and whether a sum ends
+// there; window k+1's loads are issued before window k is summed. Slots past
+// the range load a fixed in-bounds row (a cache hit) and add zero, so every
+// window issues the same number of loads.
+template <int DT, int LB, bool BEYOND>
+__device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, const int* pos, const int* stage,
+                                             const uint8_t* sbag, const char* const* tbase, const int* trows, int T,
+                                             int p0, int p1, float* Z, int LD, float* carry_w, int* carry_t_w,
+                                             int tid) {
+  using C = LaneChunk<LB>;
+  using RS = RowShape<DT, LB>;
+  constexpr int EL = RS::EL;
+  constexpr int WIN = RS::WIN;
+  constexpr int RB = LB * kWave;  // row bytes
+  int t0 = 0;
+  while (rfl(pos[t0 + 1]) <= p0) ++t0;
+  RowCursor cur{rfl(pos[t0]) < p0};
+  float acc[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) acc[e] = 0.f;
+  const uint64_t fallback = reinterpret_cast<uint64_t>(tbase[0]);
+  const uint64_t lane_off = static_cast<uint64_t>(tid & (kWave - 1)) * LB;
+  Window wa, wb;
+  typename C::type va[WIN], vb[WIN];
+  prepare_window<WIN, RB, BEYOND>(wa, a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, fallback, tid);
+  issue_window<C, WIN>(wa, va, lane_off);
+  for (int q = p0;;) {
+    prepare_window<WIN, RB, BEYOND>(wb, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid);
+    issue_window<C, WIN>(wb, vb, lane_off);
+    consume_window<DT, LB, WIN>(wa, va, acc, cur, Z, LD, carry_w, carry_t_w, tid);
+    q += WIN;
+    if (q >= p1) break;
+    prepare_window<WIN, RB, BEYOND>(wa, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid);
+    issue_window<C, WIN>(wa, va, lane_off);
+    consume_window<DT, LB, WIN>(wb, vb, acc, cur, Z, LD, carry_w, carry_t_w, tid);
+    q += WIN;
+    if (q >= p1) break;
+  }
+  // The loop leaves one window of fallback-row loads (cache hits) in flight.
+  // Reading every window register here makes the compiler wait for them once
+  // per range; otherwise the next sample's loop sees those loads as possibly
+  // outstanding and guards each reuse of the registers with a full wait, in
+  // every iteration.
+#pragma unroll
+  for (int j = 0; j < WIN; ++j) {
+    touch(va[j]);
+    touch(vb[j]);
+  }
 }
 
 // Persistent workgroups: each takes a contiguous chunk of samples and runs,
@@ -738,6 +876,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
   extern __shared__ __align__(16) char lds[];
   int* carry_t = reinterpret_cast<int*>(lds + L.off_carry_t);
   const char** tbase = reinterpret_cast<const char**>(lds + L.off_tbase);
+  int* trows = reinterpret_cast<int*>(lds + L.off_trows);
   int* stage = reinterpret_cast<int*>(lds + L.off_stage);
   uint8_t* sbag = reinterpret_cast<uint8_t*>(lds + L.off_sbag);
   float* carry = reinterpret_cast<float*>(lds + L.off_carry);
@@ -746,7 +885,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
 
   const int T = a.T, D = a.D, LD = L.LD;
   const int W = D + (T + 1) * T / 2;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int tid = threadIdx.x;
   const int wave = rfl(tid >> 6);
   const int b_begin = xcd_block(blockIdx.x, gridDim.x) * chunk;
   const int b_end = min(a.B, b_begin + chunk);
@@ -760,15 +899,16 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     if (tid < T) {
       publish_bag(a, tid, b_begin, a.offsets[tid * a.B + b_begin], a.offsets[tid * a.B + b_begin + 1], beg, pos);
       tbase[tid] = static_cast<const char*>(a.tabs.ptr[tid]);
+      trows[tid] = a.tabs.rows[tid];
       clear_if_empty(pos, tid, Z, LD, D);
     }
     __syncthreads();
     for (int d = tid; d < D; d += kRowThreads) Z[d] = a.e0[static_cast<size_t>(b_begin) * D + d];
-    if (wave == 0) scan_positions(pos, T);
+    if (wave == 0) scan_positions(pos, T, tid);
     __syncthreads();
     int r[kStagePerThread], tb[kStagePerThread];
-    load_stage(a, beg, pos, T, rfl(pos[T]), r, tb);
-    write_stage(a, r, tb, stage, sbag);
+    load_stage(a, beg, pos, T, rfl(pos[T]), r, tb, tid);
+    write_stage(a, r, tb, stage, sbag, trows, tid);
     if (tid < kRowWaves) carry_t[tid] = -1;
     __syncthreads();
   }
@@ -779,6 +919,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     // spilled) across the whole loop.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
     const bool has_next = b + 1 < b_end;
     int* beg = reinterpret_cast<int*>(lds + L.off_beg + pb * L.pos_stride);
     int* pos = reinterpret_cast<int*>(lds + L.off_pos + pb * L.pos_stride);
@@ -786,15 +927,19 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     int* npos = reinterpret_cast<int*>(lds + L.off_pos + (pb ^ 1) * L.pos_stride);
     const int N = rfl(pos[T]);
 
-    // next sample's bag ranges and e0: loads in flight during the gather
-    int nx0 = 0, nx1 = 0;
-    float ne0 = 0.f;
-    if (has_next) {
-      if (tid < T) {
-        nx0 = a.offsets[tid * a.B + b + 1];
-        nx1 = a.offsets[tid * a.B + b + 2];
-      }
-      if (tid < D) ne0 = a.e0[static_cast<size_t>(b + 1) * D + tid];
+    // next sample's bag ranges and e0: loads in flight during the gather. Every
+    // thread issues them, clamped in bounds (the last sample re-reads its own),
+    // so that no branch merges their registers and nothing waits for them
+    // before the gather is done.
+    int nx0, nx1;
+    float ne0;
+    {
+      const int bn = has_next ? b + 1 : b;
+      const int tt = tid < T ? tid : T - 1;
+      const int td = tid < D ? tid : D - 1;
+      nx0 = a.offsets[tt * a.B + bn];
+      nx1 = a.offsets[tt * a.B + bn + 1];
+      ne0 = a.e0[static_cast<size_t>(bn) * D + td];
     }
 
     // gather: wave w sums stream positions [p0, p1) in windows of WIN rows.
@@ -806,32 +951,17 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
       const int p0 = static_cast<int>((static_cast<long long>(N) * wave) / kRowWaves);
       const int p1 = static_cast<int>((static_cast<long long>(N) * (wave + 1)) / kRowWaves);
       if (p0 < p1) {
-        int t0 = 0;
-        while (rfl(pos[t0 + 1]) <= p0) ++t0;
-        RowCursor cur{rfl(pos[t0]) < p0};
-        float acc[EL];
-#pragma unroll
-        for (int e = 0; e < EL; ++e) acc[e] = 0.f;
-        const uint64_t fallback = reinterpret_cast<uint64_t>(tbase[0]);
-        const uint64_t lane_off = static_cast<uint64_t>(lane) * LB;
-        Window wa, wb;
-        typename C::type va[WIN], vb[WIN];
-        prepare_window<WIN, RB>(wa, a, beg, pos, stage, sbag, tbase, T, p0, p1, fallback);
-        issue_window<C, WIN>(wa, va, lane_off);
-        for (int q = p0;;) {
-          prepare_window<WIN, RB>(wb, a, beg, pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
-          issue_window<C, WIN>(wb, vb, lane_off);
-          consume_window<DT, LB, WIN>(wa, va, acc, cur, Z, LD, carry + wave * D, carry_t + wave);
-          q += WIN;
-          if (q >= p1) break;
-          prepare_window<WIN, RB>(wa, a, beg, pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
-          issue_window<C, WIN>(wa, va, lane_off);
-          consume_window<DT, LB, WIN>(wb, vb, acc, cur, Z, LD, carry + wave * D, carry_t + wave);
-          q += WIN;
-          if (q >= p1) break;
-        }
+        float* cw = carry + wave * D;
+        int* ctw = carry_t + wave;
+        if (p1 <= kStageCap)
+          gather_range<DT, LB, false>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid);
+        else
+          gather_range<DT, LB, true>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid);
       }
     }
+    // the prefetched values are first used here (the barrier keeps every use,
+    // and the wait for them, after the gather)
+    asm volatile("" : "+v"(nx0), "+v"(nx1), "+v"(ne0));
     bool next_empty = false;
     if (has_next && tid < T) {
       publish_bag(a, tid, b + 1, nx0, nx1, nbeg, npos);
@@ -846,52 +976,35 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
         if (t >= 0) Z[(1 + t) * LD + d] += carry[w * D + d];
       }
     }
-    if (has_next && wave == kRowWaves - 1) scan_positions(npos, T);
+    if (has_next && wave == kRowWaves - 1) scan_positions(npos, T, tid);
     __syncthreads();
 
     // next sample's index loads go out now; their values are staged after the output
     int r[kStagePerThread], tb[kStagePerThread];
-    if (has_next) load_stage(a, nbeg, npos, T, rfl(npos[T]), r, tb);
-    else {
-#pragma unroll
-      for (int k = 0; k < kStagePerThread; ++k) { r[k] = 0; tb[k] = -1; }
-    }
+    // (issued unconditionally, with no positions when there is no next sample:
+    // every load stays in bounds and no branch merges the registers)
+    load_stage(a, nbeg, npos, T, has_next ? rfl(npos[T]) : 0, r, tb, tid);
 
+    // pooled output (if requested) from the final fp32 Z
+    if (a.out_pooled) {
+      float* op = a.out_pooled + static_cast<size_t>(b) * T * D;
+      for (int i = tid; i < T * D; i += kRowThreads) {
+        const int t = i / D, d = i - t * D;
+        op[i] = Z[(1 + t) * LD + d];
+      }
+    }
     // interaction into the output staging area (which overlays the index stage)
     for (int d = tid; d < D; d += kRowThreads) outs[d] = Z[d];
     if constexpr (MFMA) {
+      // e0 dots in fp32, then the pooled rows are split in place for the Gram
+      e0_dots(Z, LD, D, T, outs, tid);
+      split_rows(Z, LD, D, L.Tp, tid);
       const int nt = L.Tp / 32;
       const int ntiles = nt * (nt + 1) / 2;
       for (int tile = wave; tile < ntiles; tile += kRowWaves) {
         int I, J;
         block_pair(tile, I, J);
-        gram_tile_mfma(Z, LD, D, T, I, J, outs);
-      }
-      // dots of e0 with every pooled row (pair (zi, 0) sits at zi(zi-1)/2), on the
-      // waves that hold no Gram tile: 4 lanes per dot, each over a quarter of D,
-      // combined in a fixed order
-      const int spare = (ntiles < kRowWaves) ? kRowWaves - ntiles : kRowWaves;
-      const int first = kRowWaves - spare;
-      if (wave >= first) {
-        const int slot = tid - first * kWave;
-        const int quarter = slot & 3;
-        const int dq = D / 4;
-        for (int zi = 1 + (slot >> 2); zi <= T; zi += spare * kWave / 4) {
-          const float* zr = Z + zi * LD + quarter * dq;
-          const float* z0 = Z + quarter * dq;
-          float sum = 0.f;
-          for (int d = 0; d < dq; d += 4) {
-            const float4 x = *reinterpret_cast<const float4*>(zr + d);
-            const float4 y = *reinterpret_cast<const float4*>(z0 + d);
-            sum = fmaf(x.x, y.x, sum);
-            sum = fmaf(x.y, y.y, sum);
-            sum = fmaf(x.z, y.z, sum);
-            sum = fmaf(x.w, y.w, sum);
-          }
-          sum += __shfl_xor(sum, 1, kWave);
-          sum += __shfl_xor(sum, 2, kWave);
-          if (quarter == 0) outs[D + zi * (zi - 1) / 2] = sum;
-        }
+        gram_tile_mfma(Z, LD, D, T, I, J, outs, tid);
       }
     } else {
       const Tile tl = make_tile(T, D, 1);
@@ -902,20 +1015,17 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
       }
     }
     __syncthreads();
+    // the next sample's index loads have had the whole interaction to land:
+    // take them now, before the output stores are queued behind them
+#pragma unroll
+    for (int k = 0; k < kStagePerThread; ++k) asm volatile("" : "+v"(r[k]));
     float* o = a.out_inter + static_cast<size_t>(b) * W;
     for (int i = tid; i < W; i += kRowThreads) store_stream(o + i, outs[i]);
-    if (a.out_pooled) {
-      float* op = a.out_pooled + static_cast<size_t>(b) * T * D;
-      for (int i = tid; i < T * D; i += kRowThreads) {
-        const int t = i / D, d = i - t * D;
-        op[i] = Z[(1 + t) * LD + d];
-      }
-    }
     __syncthreads();
 
     // stage the next sample: indices, cleared Z with its e0, no carries
     if (has_next) {
-      write_stage(a, r, tb, stage, sbag);
+      write_stage(a, r, tb, stage, sbag, trows, tid);
       if (next_empty) {
         float* z = Z + (1 + tid) * LD;
         for (int d = 0; d < D; d += 4) *reinterpret_cast<float4*>(z + d) = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -925,398 +1035,6 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
       __syncthreads();
     }
     pb ^= 1;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// warp-specialised fused forward for large samples (MFMA interaction)
-// ---------------------------------------------------------------------------
-// One 1024-thread workgroup per CU walks a contiguous chunk of samples. Waves
-// 0..11 only gather: in step s they sum the rows of sample s into Z[s&1].
-// Waves 12..15 meanwhile finish sample s-1 (Gram tiles and e0 dots from
-// Z[(s-1)&1] into an output buffer), write sample s-2's output to HBM, and
-// prepare sample s+1 (bag ranges, positions, staged indices, e0). Two
-// workgroup barriers per step: C_s (after G has added sample s-1's carried
-// partial sums and W has cleared the empty rows of s-1 and written s-2's
-// output) and the end of the step. The row stream therefore never waits for
-// the interaction, the output or the next sample's index round trips.
-constexpr int kWsThreads = 1024;
-constexpr int kWsWaves = kWsThreads / kWave;   // 16
-constexpr int kGWaves = 12;                    // gathering waves
-constexpr int kWsWorkers = kWsWaves - kGWaves;  // 4 worker waves
-constexpr int kWsPosPerLane = kStageCap / (kWsWorkers * kWave);  // staged positions per worker lane
-
-struct WsLayout {
-  int Tp, LD;
-  int off_tbase;
-  int off_beg[2], off_pos[2];
-  int off_carry_t[2];
-  int off_e0[3];
-  int off_stage[2], off_sbag[2];
-  int off_carry[2];
-  int off_out[2];
-  int off_z[2];
-  int bytes;
-};
-
-__host__ __device__ inline WsLayout make_ws_layout(int T, int D) {
-  WsLayout L;
-  L.Tp = ((T + 31) / 32) * 32;
-  L.LD = D + 4;
-  const int P = (T + 1) * T / 2;
-  int o = 0;
-  L.off_tbase = o; o += align16(T * 8);
-  for (int i = 0; i < 2; ++i) {
-    L.off_beg[i] = o; o += align16(T * 4);
-    L.off_pos[i] = o; o += align16((T + 1) * 4);
-    L.off_carry_t[i] = o; o += align16(kGWaves * 4);
-  }
-  for (int i = 0; i < 3; ++i) { L.off_e0[i] = o; o += align16(D * 4); }
-  for (int i = 0; i < 2; ++i) {
-    L.off_stage[i] = o; o += kStageCap * 4;
-    L.off_sbag[i] = o; o += align16(kStageCap);
-    L.off_carry[i] = o; o += kGWaves * D * 4;
-    L.off_out[i] = o; o += align16((D + P) * 4);
-  }
-  for (int i = 0; i < 2; ++i) { L.off_z[i] = o; o += (1 + L.Tp) * L.LD * 4; }
-  L.bytes = o;
-  return L;
-}
-
-template <int LB>
-struct WsShape {
-  static constexpr int WIN = LB >= 4 ? 128 / LB : 32;  // rows per window (two in flight: 64 VGPRs)
-};
-
-// Value of entry t (0..127) of a per-lane pair (v[0] in lane t, v[1] in lane t-64); all lanes take part.
-__device__ __forceinline__ int sel64(const int (&v)[2], int t) {
-  const int a0 = __shfl(v[0], t & (kWave - 1), kWave);
-  const int a1 = __shfl(v[1], t & (kWave - 1), kWave);
-  return t < kWave ? a0 : a1;
-}
-
-// Worker-side preparation of a sample, split so that its round trips overlap
-// other work: ws_load_offsets (issued two steps ahead), ws_begin (bag ranges
-// clamped and scanned in-wave, tables published by the first worker, index
-// and e0 loads issued) and ws_commit (values written to LDS). Every worker
-// wave computes the ranges and the scan itself, so no worker waits for another.
-constexpr int kWsLoaders = kWsWorkers - 1;  // waves 12..14 load and compute; wave 15 only stores
-constexpr int kWsE0PerLane = 3;      // D <= 512 over 192 loader lanes
-constexpr int kWsBagsPerWorker = 43;  // T <= 128 over 3 loader waves
-
-struct WsRaw {
-  int s0[2], s1[2];  // offsets of bags t = lane and lane + 64
-};
-
-struct WsPending {
-  int bg[2], ln[2], ps[2];  // begin, length, inclusive end of bags t = lane and lane + 64
-  int r[kWsBagsPerWorker];  // index of this lane's row in each of this wave's bags
-  float e0v[kWsE0PerLane];
-};
-
-__device__ __forceinline__ WsRaw ws_load_offsets(const FwdArgs& a, int b) {
-  const int lane = threadIdx.x & (kWave - 1);
-  WsRaw w;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int t = lane + h * kWave;
-    w.s0[h] = 0;
-    w.s1[h] = 0;
-    if (t < a.T) {
-      w.s0[h] = a.offsets[t * a.B + b];
-      w.s1[h] = a.offsets[t * a.B + b + 1];
-    }
-  }
-  return w;
-}
-
-// Entry t (0..127) of a lane-distributed pair, as a wave-uniform value.
-__device__ __forceinline__ int lane_get(const int (&v)[2], int t) {
-  const int a0 = __builtin_amdgcn_readlane(v[0], t & (kWave - 1));
-  const int a1 = __builtin_amdgcn_readlane(v[1], t & (kWave - 1));
-  return t < kWave ? a0 : a1;
-}
-
-__device__ __forceinline__ void ws_begin(const FwdArgs& a, const WsLayout& L, char* lds, int b, int buf,
-                                         const WsRaw& raw, WsPending& pd) {
-  const int T = a.T, D = a.D;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wk = rfl(threadIdx.x >> 6) - kGWaves;  // 0..3
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int t = lane + h * kWave;
-    pd.bg[h] = 0;
-    pd.ln[h] = 0;
-    if (t < T) {
-      int s0 = raw.s0[h], s1 = raw.s1[h];
-      bool bad = false;
-      if (t == 0 && b == 0 && s0 != 0) bad = true;
-      if (t == T - 1 && b == a.B - 1 && static_cast<int64_t>(s1) != a.nnz) bad = true;
-      if (s0 < 0) { s0 = 0; bad = true; }
-      if (static_cast<int64_t>(s0) > a.nnz) { s0 = static_cast<int>(a.nnz); bad = true; }
-      if (static_cast<int64_t>(s1) > a.nnz) { s1 = static_cast<int>(a.nnz); bad = true; }
-      if (s1 < s0) { s1 = s0; bad = true; }
-      if (bad && wk == 0) flag(a.status, DLRM_STATUS_BAD_OFFSETS);
-      pd.bg[h] = s0;
-      pd.ln[h] = s1 - s0;
-    }
-  }
-  int carry_sum = 0;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {  // inclusive scan: end of bag t
-    int v = pd.ln[h];
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(v, o, kWave);
-      if (lane >= o) v += y;
-    }
-    pd.ps[h] = v + carry_sum;
-    carry_sum += __shfl(v, kWave - 1, kWave);
-  }
-  if (wk == 0) {
-    int* beg = reinterpret_cast<int*>(lds + L.off_beg[buf]);
-    int* pos = reinterpret_cast<int*>(lds + L.off_pos[buf]);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = lane + h * kWave;
-      if (t < T) {
-        beg[t] = pd.bg[h];
-        pos[t + 1] = pd.ps[h];
-      }
-    }
-    if (lane == 0) pos[0] = 0;
-  }
-  // this wave's bags t = wk + 3j: lane i loads the index of the bag's row i
-  // (rows past 64 and positions past the staging area are handled elsewhere)
-#pragma unroll
-  for (int j = 0; j < kWsBagsPerWorker; ++j) {
-    const int t = wk + kWsLoaders * j;
-    pd.r[j] = 0;
-    if (t < T) {
-      const int len = lane_get(pd.ln, t);
-      const int start = lane_get(pd.ps, t) - len;
-      const int bbeg = lane_get(pd.bg, t);
-      if (lane < len && start + lane < kStageCap) pd.r[j] = a.indices[bbeg + lane];
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kWsE0PerLane; ++k) {
-    const int d = wk * kWave + lane + k * kWsLoaders * kWave;
-    pd.e0v[k] = d < D ? a.e0[static_cast<size_t>(b) * D + d] : 0.f;
-  }
-}
-
-__device__ __forceinline__ void ws_commit(const FwdArgs& a, const WsLayout& L, char* lds, int buf, int e0buf,
-                                          const WsPending& pd) {
-  const int T = a.T;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wk = rfl(threadIdx.x >> 6) - kGWaves;
-  int* stage = reinterpret_cast<int*>(lds + L.off_stage[buf]);
-  uint8_t* sbag = reinterpret_cast<uint8_t*>(lds + L.off_sbag[buf]);
-  float* e0s = reinterpret_cast<float*>(lds + L.off_e0[e0buf]);
-  bool bad = false;
-#pragma unroll
-  for (int j = 0; j < kWsBagsPerWorker; ++j) {
-    const int t = wk + kWsLoaders * j;
-    if (t < T) {
-      const int len = lane_get(pd.ln, t);
-      const int start = lane_get(pd.ps, t) - len;
-      const int rows = a.tabs.rows[t];
-      if (lane < len && start + lane < kStageCap) {
-        int v = pd.r[j];
-        if (v < 0 || v >= rows) { bad = true; v = -1; }
-        stage[start + lane] = v;
-        sbag[start + lane] = static_cast<uint8_t>(t);
-      }
-      if (len > kWave) {  // long bag: the rest of its staged rows, one round trip each
-        const int bbeg = lane_get(pd.bg, t);
-        for (int i = kWave + lane; i < len && start + i < kStageCap; i += kWave) {
-          int v = a.indices[bbeg + i];
-          if (v < 0 || v >= rows) { bad = true; v = -1; }
-          stage[start + i] = v;
-          sbag[start + i] = static_cast<uint8_t>(t);
-        }
-      }
-    }
-  }
-  if (bad) flag(a.status, DLRM_STATUS_BAD_INDEX);
-#pragma unroll
-  for (int k = 0; k < kWsE0PerLane; ++k) {
-    const int d = wk * kWave + lane + k * kWsLoaders * kWave;
-    if (d < a.D) e0s[d] = pd.e0v[k];
-  }
-  if (wk == 0 && lane < kGWaves) reinterpret_cast<int*>(lds + L.off_carry_t[buf])[lane] = -1;
-}
-
-template <int DT, int LB>
-__global__ __launch_bounds__(kWsThreads, 4) void fused_ws_kernel(FwdArgs a, WsLayout L, int chunk) {
-  using C = LaneChunk<LB>;
-  constexpr int EL = LB / Storage<DT>::bytes;
-  constexpr int WIN = WsShape<LB>::WIN;
-  constexpr int RB = LB * kWave;
-  extern __shared__ __align__(16) char lds[];
-  const char** tbase = reinterpret_cast<const char**>(lds + L.off_tbase);
-  const int T = a.T, D = a.D, LD = L.LD;
-  const int W = D + (T + 1) * T / 2;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = rfl(tid >> 6);
-  const bool isG = wave < kGWaves;
-  const int b0 = xcd_block(blockIdx.x, gridDim.x) * chunk;
-  const int nS = min(a.B - b0, chunk);
-  if (nS <= 0) return;  // whole workgroup
-
-  if (tid < T) tbase[tid] = static_cast<const char*>(a.tabs.ptr[tid]);
-  if (tid < kGWaves) {
-    reinterpret_cast<int*>(lds + L.off_carry_t[0])[tid] = -1;
-    reinterpret_cast<int*>(lds + L.off_carry_t[1])[tid] = -1;
-  }
-  WsRaw raw_next{};
-  if (!isG && wave < kWsWaves - 1) {
-    WsPending pd;
-    ws_begin(a, L, lds, b0, 0, ws_load_offsets(a, b0), pd);
-    ws_commit(a, L, lds, 0, 0, pd);
-    if (nS > 1) raw_next = ws_load_offsets(a, b0 + 1);
-  }
-  __syncthreads();
-
-  // Each role runs its own loop with the same two barriers per step, so the
-  // register allocator sees the two roles' state as disjoint. (The role test is
-  // uniform per wave and a workgroup barrier counts waves, whichever barrier
-  // instruction they reach.)
-  if (isG) {
-    Window wa, wb;
-    typename C::type va[WIN], vb[WIN];
-    float acc[EL];
-    RowCursor cur{false};
-    int q = 0, p1 = 0;
-    const uint64_t lane_off = static_cast<uint64_t>(lane) * LB;
-    const uint64_t fallback = reinterpret_cast<uint64_t>(tbase[0]);
-    for (int s = 0; s <= nS + 1; ++s) {
-      const int cb = s & 1, pb = cb ^ 1;
-      const int* beg = reinterpret_cast<const int*>(lds + L.off_beg[cb]);
-      const int* pos = reinterpret_cast<const int*>(lds + L.off_pos[cb]);
-      const int* stage = reinterpret_cast<const int*>(lds + L.off_stage[cb]);
-      const uint8_t* sbag = reinterpret_cast<const uint8_t*>(lds + L.off_sbag[cb]);
-      float* Zc = reinterpret_cast<float*>(lds + L.off_z[cb]);
-      float* Zp = reinterpret_cast<float*>(lds + L.off_z[pb]);
-      if (s >= 1 && s <= nS) {  // carried partial sums of sample s-1, in wave order
-        const int* ct = reinterpret_cast<const int*>(lds + L.off_carry_t[pb]);
-        const float* cy = reinterpret_cast<const float*>(lds + L.off_carry[pb]);
-        for (int d = tid; d < D; d += kGWaves * kWave) {
-          for (int w = 1; w < kGWaves; ++w) {
-            const int t = ct[w];
-            if (t >= 0) Zp[(1 + t) * LD + d] += cy[w * D + d];
-          }
-        }
-      }
-      __syncthreads();  // C_s
-      q = 0;
-      p1 = 0;
-      if (s < nS) {  // first two windows of sample s
-        const int N = rfl(pos[T]);
-        const int p0 = static_cast<int>((static_cast<long long>(N) * wave) / kGWaves);
-        p1 = static_cast<int>((static_cast<long long>(N) * (wave + 1)) / kGWaves);
-        q = p0;
-        if (p0 < p1) {
-          int t0 = 0;
-          while (rfl(pos[t0 + 1]) <= p0) ++t0;
-          cur.to_carry = rfl(pos[t0]) < p0;
-#pragma unroll
-          for (int e = 0; e < EL; ++e) acc[e] = 0.f;
-          prepare_window<WIN, RB>(wa, a, beg, pos, stage, sbag, tbase, T, p0, p1, fallback);
-          issue_window<C, WIN>(wa, va, lane_off);
-          prepare_window<WIN, RB>(wb, a, beg, pos, stage, sbag, tbase, T, p0 + WIN, p1, fallback);
-          issue_window<C, WIN>(wb, vb, lane_off);
-        }
-      }
-      if (q < p1) {
-        float* carry_w = reinterpret_cast<float*>(lds + L.off_carry[cb]) + wave * D;
-        int* carry_t_w = reinterpret_cast<int*>(lds + L.off_carry_t[cb]) + wave;
-        for (;;) {
-          consume_window<DT, LB, WIN>(wa, va, acc, cur, Zc, LD, carry_w, carry_t_w);
-          q += WIN;
-          if (q >= p1) break;
-          prepare_window<WIN, RB>(wa, a, beg, pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
-          issue_window<C, WIN>(wa, va, lane_off);
-          consume_window<DT, LB, WIN>(wb, vb, acc, cur, Zc, LD, carry_w, carry_t_w);
-          q += WIN;
-          if (q >= p1) break;
-          prepare_window<WIN, RB>(wb, a, beg, pos, stage, sbag, tbase, T, q + WIN, p1, fallback);
-          issue_window<C, WIN>(wb, vb, lane_off);
-        }
-      }
-      __syncthreads();  // end of step
-    }
-  } else {
-    const int wk = wave - kGWaves;
-    if (wk == kWsLoaders) {
-      // writer wave: outputs, cleared rows and e0 dots; it issues no global load,
-      // so its stores never hold up a wait on a load
-      for (int s = 0; s <= nS + 1; ++s) {
-        const int cb = s & 1, pb = cb ^ 1;
-        float* Zp = reinterpret_cast<float*>(lds + L.off_z[pb]);
-        if (s >= 2) {  // output of sample s-2
-          const float* o = reinterpret_cast<const float*>(lds + L.off_out[cb]);
-          float* dst = a.out_inter + static_cast<size_t>(b0 + s - 2) * W;
-          for (int i = lane; i < W; i += kWave) store_stream(dst + i, o[i]);
-        }
-        if (s >= 1 && s <= nS) {  // rows of empty bags of sample s-1
-          const int* pp = reinterpret_cast<const int*>(lds + L.off_pos[pb]);
-          for (int t = lane; t < T; t += kWave) {
-            if (pp[t + 1] == pp[t]) {
-              float* z = Zp + (1 + t) * LD;
-              for (int d = 0; d < D; d += 4) *reinterpret_cast<float4*>(z + d) = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-          }
-        }
-        __syncthreads();  // C_s
-        if (s >= 1 && s <= nS) {  // e0 block and dots of e0 with every pooled row of sample s-1
-          float* outs = reinterpret_cast<float*>(lds + L.off_out[pb]);
-          const float* e0s = reinterpret_cast<const float*>(lds + L.off_e0[(s - 1) % 3]);
-          for (int d = lane; d < D; d += kWave) outs[d] = e0s[d];
-          for (int zi = 1 + lane; zi <= T; zi += kWave) {  // pair (zi, 0) sits at zi(zi-1)/2
-            const float* zr = Zp + zi * LD;
-            float sum = 0.f;
-            for (int d = 0; d < D; d += 4) {
-              const float4 x = *reinterpret_cast<const float4*>(zr + d);
-              const float4 y = *reinterpret_cast<const float4*>(e0s + d);
-              sum = fmaf(x.x, y.x, sum);
-              sum = fmaf(x.y, y.y, sum);
-              sum = fmaf(x.z, y.z, sum);
-              sum = fmaf(x.w, y.w, sum);
-            }
-            outs[D + zi * (zi - 1) / 2] = sum;
-          }
-        }
-        __syncthreads();  // end of step
-      }
-    } else {
-      // loader waves: prepare sample s+1 (its index and e0 loads, and the
-      // offsets of s+2, fly while the Gram tiles of sample s-1 are computed)
-      for (int s = 0; s <= nS + 1; ++s) {
-        const int pb = (s & 1) ^ 1;
-        float* Zp = reinterpret_cast<float*>(lds + L.off_z[pb]);
-        __syncthreads();  // C_s
-        WsPending pd;
-        const bool prep = s + 1 < nS;
-        if (prep) {
-          ws_begin(a, L, lds, b0 + s + 1, pb, raw_next, pd);
-          if (s + 2 < nS) raw_next = ws_load_offsets(a, b0 + s + 2);
-        }
-        if (s >= 1 && s <= nS) {
-          float* outs = reinterpret_cast<float*>(lds + L.off_out[pb]);
-          const int nt = L.Tp / 32;
-          const int ntiles = nt * (nt + 1) / 2;
-          for (int tile = wk; tile < ntiles; tile += kWsLoaders) {
-            int I, J;
-            block_pair(tile, I, J);
-            gram_tile_mfma(Zp, LD, D, T, I, J, outs);
-          }
-        }
-        if (prep) ws_commit(a, L, lds, pb, (s + 1) % 3, pd);
-        __syncthreads();  // end of step
-      }
-    }
   }
 }
 
@@ -1368,53 +1086,24 @@ static int resident_blocks(K kernel, size_t lds) {
   return cus * (per_cu > 0 ? per_cu : 1);
 }
 
+constexpr int kLongSampleRows = 512;  // average rows per sample from which a workgroup takes one sample
+
 template <int DT, int LB, bool MFMA>
 static hipError_t launch_rows_v(const FwdArgs& a, const RowLayout& L, hipStream_t st) {
   auto kernel = fused_rows_kernel<DT, LB, MFMA>;
-  // Two samples per workgroup: the second sample's offsets, e0 and indices are
-  // fetched while the first is gathered, and the hardware dispatcher balances
-  // the many short-lived workgroups across CUs.
-  const int chunk = a.B >= 2 * resident_blocks(kernel, static_cast<size_t>(L.bytes)) ? 2 : 1;
+  // Short samples: two per workgroup, the second sample's offsets, e0 and
+  // indices fetched while the first is gathered. Long samples (hundreds of
+  // rows): one per workgroup, which keeps the end of the launch short (the
+  // hardware dispatcher hands the many short-lived workgroups to free slots).
+  const bool long_samples = a.nnz >= static_cast<int64_t>(kLongSampleRows) * a.B;
+  const int chunk = (!long_samples && a.B >= 2 * resident_blocks(kernel, static_cast<size_t>(L.bytes))) ? 2 : 1;
   const int grid = (a.B + chunk - 1) / chunk;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kRowThreads), L.bytes, st, a, L, chunk);
   return hipGetLastError();
 }
 
 template <int DT, int LB>
-static hipError_t launch_ws(const FwdArgs& a, hipStream_t st) {
-  const WsLayout L = make_ws_layout(a.T, a.D);
-  auto kernel = fused_ws_kernel<DT, LB>;
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidValue;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorInvalidValue;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWsThreads, L.bytes) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  int grid = cus * per_cu;
-  if (grid > a.B) grid = a.B;
-  const int chunk = (a.B + grid - 1) / grid;
-  grid = (a.B + chunk - 1) / chunk;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWsThreads), L.bytes, st, a, L, chunk);
-  return hipGetLastError();
-}
-
-// The warp-specialised kernel pays off when a sample carries hundreds of rows
-// and there are many samples per CU; it needs the MFMA interaction.
-static bool use_ws(const FwdArgs& a, int dtype) {
-#ifndef DLRM_ENABLE_WS
-  (void)a;
-  (void)dtype;
-  return false;  // measured slower than the 3-workgroups-per-CU kernel on the 164 GB workload
-#endif
-  if (!use_mfma(a.T, a.D, dtype) || a.T > 2 * kWave) return false;
-  if (static_cast<size_t>(make_ws_layout(a.T, a.D).bytes) > kMaxLds) return false;
-  return a.nnz >= static_cast<int64_t>(256) * a.B && a.B >= 4096;
-}
-
-template <int DT, int LB>
 static hipError_t launch_rows(const FwdArgs& a, hipStream_t st) {
-  if constexpr (DT != DLRM_F32) {
-    if (use_ws(a, DT)) return launch_ws<DT, LB>(a, st);
-  }
   const bool mfma = use_mfma(a.T, a.D, DT);
   const RowLayout L = make_row_layout(a.T, a.D, mfma);
   if (static_cast<size_t>(L.bytes) > kMaxLds) return hipErrorInvalidValue;
