@@ -13,9 +13,10 @@
 //    ranks equal digits inside a wave with ballots.
 // 4. segments: head flags (key differs from its predecessor), scanned into the
 //    position of each distinct key.
-// 5. one wave per distinct row: sum the rows dL/dpooled of its occurrences in
-//    sorted order (fixed order, so the result is deterministic), then
-//    W <- W - lr * G in fp32, rounded once to the table's storage type.
+// 5. segmented sums of the rows dL/dpooled over the sorted occurrences, in
+//    fixed chunks of positions whatever the segment lengths (a fixed order, so
+//    the result is deterministic), then W <- W - lr * G in fp32, rounded once
+//    to the table's storage type.
 #include <algorithm>
 
 #include "scan_impl.h"
@@ -266,83 +267,257 @@ __global__ __launch_bounds__(kBwdThreads) void copy_i32(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// 5. segmented reduce + SGD: one wave per distinct row
+// 5. segmented reduce + SGD over fixed chunks of the sorted occurrences
 // ---------------------------------------------------------------------------
-template <int DT, int D4>
-__global__ __launch_bounds__(kBwdThreads) void reduce_sgd(MutTableArgs tabs, int T, const int32_t* __restrict__ unique_keys,
-                                                          const int32_t* __restrict__ seg_offsets,
-                                                          const int32_t* __restrict__ num_unique,
-                                                          const int32_t* __restrict__ perm,
-                                                          const int32_t* __restrict__ bag_of,
-                                                          const float* __restrict__ d_pooled, float lr) {
-  constexpr int LPR = D4 < kWave ? D4 : kWave;  // lanes per row, one float4 each per step
-  constexpr int V = D4 / LPR;                   // float4 per lane
-  constexpr int R = kWave / LPR;                // occurrences summed in parallel
-  constexpr int D = D4 * 4;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int grp = lane / LPR, sub = lane % LPR;
-  const int U = *num_unique;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  for (int u = blockIdx.x * (kBwdThreads / kWave) + wave; u < U; u += gridDim.x * (kBwdThreads / kWave)) {
-    const int q0 = seg_offsets[u], q1 = seg_offsets[u + 1];
-    float4 acc[V];
+// The sorted occurrences are cut into chunks of C consecutive positions, one
+// wave each, whatever the segment lengths (a Zipf-hot row can own thousands of
+// occurrences). A wave loads the C gradient rows of its chunk at once, then
+// sums them in position order, closing a sum at every segment end:
+//   - a segment that starts and ends in the chunk gets its SGD update here;
+//   - the part of a segment that began in an earlier chunk goes to carry[k];
+//   - the first part of a segment that goes on past the chunk goes to head[k].
+// seg_combine then adds head[k] + carry[k+1] + ... in chunk order for every
+// segment that crosses a chunk end and applies its update. The summation
+// order depends only on the positions, so results are deterministic.
+//
+// Row layout in registers: lane l holds EL fp32 columns [c, c + EL) of a
+// d_pooled row, c = (l % LPR) * EL, LPR = min(64, D) lanes per row (for D < 64
+// the lanes above D repeat lanes 0..D-1 and write the same values).
+constexpr int kChunkFirstCont = 1;  // the chunk's first segment began in an earlier chunk
+constexpr int kChunkLastCont = 2;   // the chunk's last segment goes on into the next chunk
+constexpr int kChunkSingle = 4;     // the chunk holds (part of) one segment only
+
+template <int EL>
+struct RowVec {
+  float v[EL];
+  __device__ __forceinline__ void load(const float* p) {
+    if constexpr (EL == 1) v[0] = *p;
+    else if constexpr (EL == 2) { const float2 x = *reinterpret_cast<const float2*>(p); v[0] = x.x; v[1] = x.y; }
+    else {
 #pragma unroll
-    for (int v = 0; v < V; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int q = q0 + grp; q < q1; q += R) {
-      const int bag = bag_of[perm[q]];
-      const float* row = d_pooled + static_cast<size_t>(bag) * D + sub * 4;
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const float4 x = *reinterpret_cast<const float4*>(row + v * LPR * 4);
-        acc[v].x += x.x; acc[v].y += x.y; acc[v].z += x.z; acc[v].w += x.w;
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-#pragma unroll
-      for (int m = LPR; m < kWave; m <<= 1) {
-        acc[v].x += shfl_xor_f(acc[v].x, m);
-        acc[v].y += shfl_xor_f(acc[v].y, m);
-        acc[v].z += shfl_xor_f(acc[v].z, m);
-        acc[v].w += shfl_xor_f(acc[v].w, m);
-      }
-    if (lane >= LPR) continue;
-    const int key = unique_keys[u];
-    int t = 0;
-    for (int k = 1; k < T; ++k)
-      if (tabs.base[k] <= key) t = k;
-    const int r = key - tabs.base[t];
-    const float nlr = -lr;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int d = v * LPR * 4 + sub * 4;
-      if constexpr (DT == DLRM_F32) {
-        float4* w = reinterpret_cast<float4*>(static_cast<float*>(tabs.ptr[t]) + static_cast<size_t>(r) * D + d);
-        float4 x = *w;
-        x.x = fmaf(nlr, acc[v].x, x.x);
-        x.y = fmaf(nlr, acc[v].y, x.y);
-        x.z = fmaf(nlr, acc[v].z, x.z);
-        x.w = fmaf(nlr, acc[v].w, x.w);
-        *w = x;
-      } else {
-        uint2* w = reinterpret_cast<uint2*>(static_cast<uint16_t*>(tabs.ptr[t]) + static_cast<size_t>(r) * D + d);
-        uint2 x = *w;
-        float f0, f1, f2, f3;
-        if constexpr (DT == DLRM_BF16) {
-          f0 = bf16_lo(x.x); f1 = bf16_hi(x.x); f2 = bf16_lo(x.y); f3 = bf16_hi(x.y);
-        } else {
-          f0 = f16_lo(x.x); f1 = f16_hi(x.x); f2 = f16_lo(x.y); f3 = f16_hi(x.y);
-        }
-        f0 = fmaf(nlr, acc[v].x, f0);
-        f1 = fmaf(nlr, acc[v].y, f1);
-        f2 = fmaf(nlr, acc[v].z, f2);
-        f3 = fmaf(nlr, acc[v].w, f3);
-        x.x = static_cast<uint32_t>(to_half_bits<DT>(f0)) | (static_cast<uint32_t>(to_half_bits<DT>(f1)) << 16);
-        x.y = static_cast<uint32_t>(to_half_bits<DT>(f2)) | (static_cast<uint32_t>(to_half_bits<DT>(f3)) << 16);
-        *w = x;
+      for (int i = 0; i < EL; i += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(p + i);
+        v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
       }
     }
   }
+  __device__ __forceinline__ void store(float* p) const {
+    if constexpr (EL == 1) *p = v[0];
+    else if constexpr (EL == 2) *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    else {
+#pragma unroll
+      for (int i = 0; i < EL; i += 4) *reinterpret_cast<float4*>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    }
+  }
+};
+
+// Table row of a global key: table t (the last whose base is <= key) and the
+// row's first element.
+struct RowRef {
+  int t;
+  size_t off;
+};
+
+__device__ __forceinline__ RowRef row_of_key(const MutTableArgs& tabs, int T, int D, int key) {
+  int t = 0;  // bases ascend
+#pragma unroll
+  for (int step = 64; step > 0; step >>= 1) {
+    const int c = t + step;
+    if (c < T && tabs.base[c] <= key) t = c;
+  }
+  return RowRef{t, static_cast<size_t>(key - tabs.base[t]) * D};
+}
+
+// This lane's EL columns of a table row, widened to fp32 (exactly), and the
+// SGD write-back W - lr * g, rounded once to the storage type.
+template <int DT, int EL>
+struct TabVec {
+  float v[EL];
+  __device__ __forceinline__ void load(const MutTableArgs& tabs, RowRef r, int col) {
+    if constexpr (DT == DLRM_F32) {
+      RowVec<EL> x;
+      x.load(static_cast<const float*>(tabs.ptr[r.t]) + r.off + col);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) v[e] = x.v[e];
+    } else {
+      const uint16_t* w = static_cast<const uint16_t*>(tabs.ptr[r.t]) + r.off + col;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        const uint32_t bits = w[e];
+        v[e] = DT == DLRM_BF16 ? bf16_lo(bits) : f16_lo(bits);
+      }
+    }
+  }
+  __device__ __forceinline__ void sgd_store(const MutTableArgs& tabs, RowRef r, int col, const RowVec<EL>& g,
+                                            float lr) const {
+    const float nlr = -lr;
+    if constexpr (DT == DLRM_F32) {
+      RowVec<EL> x;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) x.v[e] = fmaf(nlr, g.v[e], v[e]);
+      x.store(static_cast<float*>(tabs.ptr[r.t]) + r.off + col);
+    } else {
+      uint16_t* w = static_cast<uint16_t*>(tabs.ptr[r.t]) + r.off + col;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) w[e] = to_half_bits<DT>(fmaf(nlr, g.v[e], v[e]));
+    }
+  }
+};
+
+template <int DT, int EL, int C>
+__global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs tabs, int T, int D,
+                                                                 const int32_t* __restrict__ unique_keys,
+                                                                 const int32_t* __restrict__ seg_offsets,
+                                                                 const int32_t* __restrict__ num_unique,
+                                                                 const int32_t* __restrict__ head_pos,
+                                                                 const int32_t* __restrict__ perm,
+                                                                 const int32_t* __restrict__ bag_of,
+                                                                 const float* __restrict__ d_pooled, float lr,
+                                                                 float* __restrict__ carry, float* __restrict__ head,
+                                                                 int32_t* __restrict__ chunk_flags, long long nchunks) {
+  static_assert(C <= kWave, "one lane per chunk position");
+  __shared__ int sbase[DLRM_MAX_TABLES];  // first global key of each table
+  for (int t = threadIdx.x; t < T; t += kBwdThreads) sbase[t] = tabs.base[t];
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1);
+  const int lpr = D < kWave ? D : kWave;
+  const int col = (lane % lpr) * EL;
+  const int U = *num_unique;
+  const int nvalid = seg_offsets[U];  // occurrences with a valid key (the rest sort last)
+  const long long k = static_cast<long long>(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6);
+  if (k >= nchunks) return;
+  const int q0 = static_cast<int>(k * C);
+  if (q0 >= nvalid) {
+    if (lane == 0) chunk_flags[k] = 0;
+    return;
+  }
+  const int q1 = nvalid - q0 < C ? nvalid : q0 + C;
+  const int nq = q1 - q0;
+  // per position (lane j): gradient row, segment, and whether a segment starts
+  // there; head_pos is the exclusive scan of the segment-start flags, so position
+  // q belongs to segment head_pos[q + 1] - 1 and starts one if head_pos[q + 1] >
+  // head_pos[q]. Slots past the chunk repeat its first position.
+  const int qj = q0 + (lane < nq ? lane : 0);
+  const int src = bag_of[perm[qj]];
+  const int h1 = head_pos[qj + 1], h0 = head_pos[qj];
+  const int key = unique_keys[h1 - 1];
+  int tk = 0;  // table of this lane's key: the last one whose base is <= key
+#pragma unroll
+  for (int step = 64; step > 0; step >>= 1) {
+    const int c = tk + step;
+    const int b = sbase[c < T ? c : T - 1];
+    if (c < T && b <= key) tk = c;
+  }
+  const int rk = key - sbase[tk];
+  const bool starts = lane < nq && h1 > h0;
+  // does a segment start right after the chunk? (then the last one closes here)
+  const bool next_starts = q1 >= nvalid || head_pos[q1 + 1] > head_pos[q1];
+  const unsigned long long start_mask = __ballot(starts);
+  const unsigned long long lane_bit = 1ull << lane;
+  // position j closes a segment if a segment starts at j + 1 or j is the last one
+  const bool closes = lane < nq && (lane + 1 == nq || ((start_mask >> (lane + 1)) & 1ull));
+  const bool first_cont = !(start_mask & 1ull);
+  // a closing segment began before the chunk if no segment starts in (0, j]
+  const bool began_before = first_cont && (start_mask & (lane_bit | (lane_bit - 1)) & ~1ull) == 0;
+  const bool goes_on = lane + 1 == nq && !next_starts;
+  const unsigned long long complete_mask = __ballot(closes && !began_before && !goes_on);
+  const unsigned long long carry_mask = __ballot(closes && began_before);
+  int flags = first_cont ? kChunkFirstCont : 0;
+  if (!next_starts) flags |= kChunkLastCont;
+  if (__popcll(start_mask) + (first_cont ? 1 : 0) == 1) flags |= kChunkSingle;
+
+  // all gradient rows and the table rows of the segments completed here are
+  // loaded up front (slots without a completed segment re-read its first row)
+  RowVec<EL> rows[C];
+  TabVec<DT, EL> trow[C];
+  RowRef refs[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int r = __shfl(src, j, kWave);
+    rows[j].load(d_pooled + static_cast<size_t>(r) * D + col);
+    const int jj = ((complete_mask >> j) & 1ull) ? j : 0;
+    refs[j].t = __builtin_amdgcn_readfirstlane(__shfl(tk, jj, kWave));
+    refs[j].off = static_cast<size_t>(__builtin_amdgcn_readfirstlane(__shfl(rk, jj, kWave))) * D;
+    trow[j].load(tabs, refs[j], col);
+  }
+  RowVec<EL> acc;
+#pragma unroll
+  for (int e = 0; e < EL; ++e) acc.v[e] = 0.f;
+  const unsigned long long close_mask = __ballot(closes);
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    if (j < nq) {
+#pragma unroll
+      for (int e = 0; e < EL; ++e) acc.v[e] += rows[j].v[e];
+      if ((close_mask >> j) & 1ull) {
+        if ((complete_mask >> j) & 1ull) {
+          trow[j].sgd_store(tabs, refs[j], col, acc, lr);
+        } else if ((carry_mask >> j) & 1ull) {
+          // the chunk's first segment, begun in an earlier chunk, ends or runs through here
+          acc.store(carry + static_cast<size_t>(k) * D + col);
+        } else {
+          // a segment begun here that goes on into the next chunk
+          acc.store(head + static_cast<size_t>(k) * D + col);
+        }
+#pragma unroll
+        for (int e = 0; e < EL; ++e) acc.v[e] = 0.f;
+      }
+    }
+  }
+  if (lane == 0) chunk_flags[k] = flags;
+}
+
+// W[row of key] <- W - lr * g on this lane's EL columns (one segment).
+template <int DT, int EL>
+__device__ __forceinline__ void sgd_update(const MutTableArgs& tabs, int T, int D, int key, int col,
+                                           const RowVec<EL>& g, float lr) {
+  const RowRef r = row_of_key(tabs, T, D, key);
+  TabVec<DT, EL> x;
+  x.load(tabs, r, col);
+  x.sgd_store(tabs, r, col, g, lr);
+}
+
+// Segments that cross chunk ends: the chunk where such a segment begins (its
+// last segment goes on, and did not itself begin earlier) adds the later
+// chunks' carries in order and applies the update.
+template <int DT, int EL, int C>
+__global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, int T, int D,
+                                                           const int32_t* __restrict__ unique_keys,
+                                                           const int32_t* __restrict__ seg_offsets,
+                                                           const int32_t* __restrict__ num_unique,
+                                                           const int32_t* __restrict__ head_pos,
+                                                           const float* __restrict__ carry,
+                                                           const float* __restrict__ head,
+                                                           const int32_t* __restrict__ chunk_flags, long long nchunks,
+                                                           float lr) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int lpr = D < kWave ? D : kWave;
+  const int col = (lane % lpr) * EL;
+  const long long k = static_cast<long long>(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6);
+  if (k >= nchunks) return;
+  const int f = chunk_flags[k];
+  if (!(f & kChunkLastCont)) return;
+  // the chunk's last segment began inside it unless the chunk holds a single
+  // segment that began earlier (then an earlier chunk owns it)
+  if ((f & kChunkSingle) && (f & kChunkFirstCont)) return;
+  const int U = *num_unique;
+  const int nvalid = seg_offsets[U];
+  const int q0 = static_cast<int>(k * C);
+  const int q1 = nvalid - q0 < C ? nvalid : q0 + C;
+  const int sid = head_pos[q1] - 1;  // segment of the chunk's last position
+  RowVec<EL> acc;
+  acc.load(head + static_cast<size_t>(k) * D + col);
+  // chunk j's first part is this segment's; it goes on past chunk j only if
+  // chunk j holds nothing else and its last segment continues
+  for (long long j = k + 1; j < nchunks; ++j) {
+    RowVec<EL> x;
+    x.load(carry + static_cast<size_t>(j) * D + col);
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc.v[e] += x.v[e];
+    const int fj = chunk_flags[j];
+    if (!((fj & kChunkSingle) && (fj & kChunkLastCont))) break;
+  }
+  sgd_update<DT, EL>(tabs, T, D, unique_keys[sid], col, acc, lr);
 }
 
 // ---------------------------------------------------------------------------
@@ -354,8 +529,15 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t d_pooled, keys_a, keys_b, vals_a, vals_b, bag_of, counts, digit_off, partial, pos, uniq, seg, nuniq, total;
+  size_t d_pooled, keys_a, keys_b, vals_a, vals_b, bag_of, counts, digit_off, partial, pos, uniq, seg, nuniq;
+  size_t carry, head, chunk_flags, total;
 };
+
+// Gradient columns per lane for a row of D fp32 values, and the chunk of sorted
+// occurrences one wave reduces (its gradient rows and table rows stay in
+// registers: 2 * C * EL of them).
+constexpr int seg_el(int D) { return D >= kWave ? D / kWave : 1; }
+constexpr int seg_chunk(int el) { return el <= 1 ? 32 : 32 / el; }
 
 int radix_passes(int64_t total_rows) {
   int bits = 0;
@@ -383,29 +565,45 @@ WsLayout layout(int T, int B, int D, int64_t nnz) {
   L.uniq = o; o = align_up(o + n * 4);
   L.seg = o; o = align_up(o + (n + 1) * 4);
   L.nuniq = o; o = align_up(o + 4);
+  const size_t C = static_cast<size_t>(seg_chunk(seg_el(D)));
+  const size_t nchunks = (n + C - 1) / C;
+  L.carry = o; o = align_up(o + nchunks * D * 4);
+  L.head = o; o = align_up(o + nchunks * D * 4);
+  L.chunk_flags = o; o = align_up(o + nchunks * 4);
   L.total = o;
   return L;
 }
 
+template <int DT, int EL>
+hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, const int32_t* uniq, const int32_t* seg,
+                             const int32_t* nuniq, const int32_t* perm, const int32_t* bag_of, const float* d_pooled,
+                             hipStream_t st) {
+  constexpr int C = seg_chunk(EL);
+  const long long nchunks = (a.nnz + C - 1) / C;
+  const int32_t* head_pos = reinterpret_cast<const int32_t*>(ws + L.pos);
+  float* carry = reinterpret_cast<float*>(ws + L.carry);
+  float* head = reinterpret_cast<float*>(ws + L.head);
+  int32_t* flags = reinterpret_cast<int32_t*>(ws + L.chunk_flags);
+  constexpr int kWavesPerBlock = kBwdThreads / kWave;
+  const dim3 g(static_cast<unsigned>((nchunks + kWavesPerBlock - 1) / kWavesPerBlock)), blk(kBwdThreads);
+  hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C>), g, blk, 0, st, a.tabs, a.T, a.D, uniq, seg, nuniq, head_pos, perm,
+                     bag_of, d_pooled, a.lr, carry, head, flags, nchunks);
+  hipLaunchKernelGGL((seg_combine<DT, EL, C>), g, blk, 0, st, a.tabs, a.T, a.D, uniq, seg, nuniq, head_pos, carry, head,
+                     flags, nchunks, a.lr);
+  return hipGetLastError();
+}
+
 template <int DT>
-hipError_t launch_reduce_dt(const BwdArgs& a, const int32_t* uniq, const int32_t* seg, const int32_t* nuniq,
-                            const int32_t* perm, const int32_t* bag_of, const float* d_pooled, hipStream_t st) {
-  long long grid = (a.nnz + 3) / 4;
-  if (grid > 8192) grid = 8192;
-  if (grid < 1) grid = 1;
-  const dim3 g(static_cast<unsigned>(grid)), blk(kBwdThreads);
-  switch (a.D / 4) {
-    case 1: hipLaunchKernelGGL((reduce_sgd<DT, 1>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
-    case 2: hipLaunchKernelGGL((reduce_sgd<DT, 2>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
-    case 4: hipLaunchKernelGGL((reduce_sgd<DT, 4>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
-    case 8: hipLaunchKernelGGL((reduce_sgd<DT, 8>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
-    case 16: hipLaunchKernelGGL((reduce_sgd<DT, 16>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
-    case 32: hipLaunchKernelGGL((reduce_sgd<DT, 32>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
-    case 64: hipLaunchKernelGGL((reduce_sgd<DT, 64>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
-    case 128: hipLaunchKernelGGL((reduce_sgd<DT, 128>), g, blk, 0, st, a.tabs, a.T, uniq, seg, nuniq, perm, bag_of, d_pooled, a.lr); break;
+hipError_t launch_reduce_dt(const BwdArgs& a, const WsLayout& L, char* ws, const int32_t* uniq, const int32_t* seg,
+                            const int32_t* nuniq, const int32_t* perm, const int32_t* bag_of, const float* d_pooled,
+                            hipStream_t st) {
+  switch (seg_el(a.D)) {
+    case 1: return launch_seg_reduce<DT, 1>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
+    case 2: return launch_seg_reduce<DT, 2>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
+    case 4: return launch_seg_reduce<DT, 4>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
+    case 8: return launch_seg_reduce<DT, 8>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -480,9 +678,9 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   }
   // 5. reduce + SGD
   switch (a.dtype) {
-    case DLRM_F32: return launch_reduce_dt<DLRM_F32>(a, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
-    case DLRM_F16: return launch_reduce_dt<DLRM_F16>(a, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
-    case DLRM_BF16: return launch_reduce_dt<DLRM_BF16>(a, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
+    case DLRM_F32: return launch_reduce_dt<DLRM_F32>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
+    case DLRM_F16: return launch_reduce_dt<DLRM_F16>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
+    case DLRM_BF16: return launch_reduce_dt<DLRM_BF16>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
     default: return hipErrorInvalidValue;
   }
 }

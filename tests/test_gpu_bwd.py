@@ -127,3 +127,28 @@ def test_backward_many_keys_four_radix_passes():
     w = synth.Workload("bigkeys", T=3, rows=6_000_000, D=8, dtype="bf16", B=700, bag=("uniform", 0, 9),
                        dist=("zipf", 1.05), seed=77)
     run_bwd(w, lr=0.01)
+
+
+def test_backward_hot_rows_span_many_chunks():
+    """Multi-hot fp16 bags with a Zipf(1.1) hot row per table: its occurrences fill
+    dozens of consecutive reduction chunks, whose partial sums are chained in order
+    (and must give the same bits on a second run)."""
+    w = synth.Workload("hot-8t20k-d64-fp16-b1024", T=8, rows=20_000, D=64, dtype="f16", B=1024,
+                       bag=("poisson", 20, 100), dist=("zipf", 1.1), seed=41)
+    run_bwd(w, lr=0.01, twice=True)
+
+
+@pytest.mark.parametrize("B", [32, 64, 65, 96, 1000])
+def test_backward_single_row_whole_batch(B):
+    """Every occurrence hits the same row: one segment across every chunk, for batch
+    sizes that end on and off a chunk boundary."""
+    w = synth.Workload("onerow", T=1, rows=1, D=128, dtype="f32", B=B, bag=("fixed", 1),
+                       dist=("uniform",), seed=B)
+    run_bwd(w, lr=0.01, twice=True)
+
+
+def test_backward_wide_rows_bf16():
+    """D = 512 bf16 (eight fp32 gradient columns per lane)."""
+    w = synth.Workload("wide", T=2, rows=50, D=512, dtype="bf16", B=40, bag=("uniform", 0, 20),
+                       dist=("zipf", 1.2), seed=512)
+    run_bwd(w, lr=0.01, twice=True)
