@@ -290,6 +290,43 @@ def bench_backward(steps, warmup):
             "status": int(status.item()), "lr": 0.01}
 
 
+def bench_backward_multihot(steps, warmup):
+    """The backward + SGD on the multi-hot fp16 shapes (8 tables x 4M rows, D=64, batch
+    4096, bags min(Poisson(20), 100), Zipf(1.1)), tables filled on the device."""
+    import numpy as np
+    import torch
+
+    from sparse_embedding_lookup_dlrm_amd import ops, synth
+
+    w = synth.WORKLOADS["multihot-8t4m-d64-fp16-b4096"]
+    dev = torch.device("cuda:0")
+    rows = synth.table_rows(w)
+    tables = synth.gen_tables_device(w, dev, rows)
+    lengths = synth.gen_lengths(w)
+    indices = synth.gen_indices(w, rows, lengths)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    offsets = ops.lengths_to_offsets(torch.from_numpy(lengths).to(dev), status=status)
+    idx = torch.from_numpy(indices).to(dev)
+    e0 = torch.from_numpy(synth.gen_e0(w)).to(dev)
+    d_out = torch.from_numpy(synth.gen_dout(w)).to(dev)
+    pooled, _ = ops.embbag_fwd(tables, offsets, idx, w.B, e0, want_pooled=True, want_inter=False, status=status)
+    nnz = len(indices)
+    ws = torch.empty(ops.bwd_workspace_bytes(w.T, w.B, w.D, nnz, rows), dtype=torch.uint8, device=dev)
+    d_e0 = torch.empty((w.B, w.D), dtype=torch.float32, device=dev)
+    plan = ops.BwdPlan(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, d_e0=d_e0, workspace=ws, status=status)
+    ms, _ = time_steps(plan.run, steps, warmup)
+    torch.cuda.synchronize()
+    U = int(plan.num_unique.item())
+    off = np.concatenate([[0], np.cumsum(lengths.astype(np.int64))])
+    longest = max(int(np.unique(indices[off[t * w.B]:off[(t + 1) * w.B]], return_counts=True)[1].max())
+                  for t in range(w.T))
+    res = {"workload": w.name, "ms_per_step": ms, "lookups_per_s": nnz / (ms / 1e3), "nnz": nnz,
+           "unique_rows": U, "longest_row_segment": longest, "status": int(status.item()), "lr": 0.01}
+    del tables, plan
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,6 +425,8 @@ def main():
     if not args.no_backward:
         res["backward"] = bench_backward(max(args.steps, 20), args.warmup)
         log(f"backward: {res['backward']['ms_per_step'] * 1e3:.1f} us/step")
+        res["backward_multihot"] = bench_backward_multihot(max(args.steps, 20), min(args.warmup, 10))
+        log(f"backward multi-hot: {res['backward_multihot']['ms_per_step'] * 1e3:.1f} us/step")
     print(json.dumps(res), flush=True)
     return 0
 
