@@ -125,6 +125,34 @@ int dlrm_interact(int32_t T, int32_t B, int32_t D, const float* e0, const float*
                   void* stream);
 
 /*
+ * Interaction alone with a choice of pair set ("DLRM" note, section 3, The
+ * Pairwise Interaction Layer: its formula takes the dot products e_i . e_j for
+ * i <= j, self-pairs included, and the section mentions variants without them).
+ *   self_pairs  0: pairs i > j, P = F (F - 1) / 2, out[b][D + i(i-1)/2 + j]
+ *               1: pairs i >= j, P = F (F + 1) / 2, out[b][D + i(i+1)/2 + j]
+ *   e0 device fp32 [B][D], pooled device fp32 [B][T][D], out device fp32 [B][D + P];
+ *   out[b][0 .. D) = e0[b] (bit copy). D must be a multiple of 4, at most 1024.
+ */
+int dlrm_interact_ex(int32_t T, int32_t B, int32_t D, int32_t self_pairs, const float* e0, const float* pooled,
+                     float* out, void* stream);
+
+/*
+ * Backward of dlrm_interact_ex, for a caller that owns the layers above (a top
+ * MLP) and the optimizer of the pooled vectors. The gradient of Z_i . Z_j is
+ * Z_j for Z_i and Z_i for Z_j, so with g the upstream gradient of the pairs,
+ * S the symmetric F x F matrix holding g at (i, j) and (j, i) (2 g on the
+ * diagonal for self-pairs, 0 there otherwise): dZ[b] = S[b] Z[b].
+ *   e0 device fp32 [B][D], pooled device fp32 [B][T][D]   (the forward's inputs)
+ *   d_out     device fp32 [B][D + P]: dL/d(out) in the layout of dlrm_interact_ex
+ *   d_e0      device fp32 [B][D] or NULL: out, d_out[:, :D] + dZ[:, 0]
+ *   d_pooled  device fp32 [B][T][D]: out, dZ[:, 1 .. T]
+ * D must be a multiple of 4, at most 512; (T + 1)(D + 4 + T + 1) * 4 bytes of LDS
+ * must fit in 160 KB.
+ */
+int dlrm_interact_bwd(int32_t T, int32_t B, int32_t D, int32_t self_pairs, const float* e0, const float* pooled,
+                      const float* d_out, float* d_e0, float* d_pooled, void* stream);
+
+/*
  * Workspace needed by dlrm_embbag_bwd_update for these sizes (bytes, written to *bytes).
  */
 int dlrm_embbag_bwd_workspace_bytes(int32_t T, int32_t B, int32_t D, int64_t nnz, const int64_t* rows,

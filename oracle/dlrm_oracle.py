@@ -136,16 +136,19 @@ def embbag_pool(tables: List[np.ndarray], dtype: str, B: int, offsets: np.ndarra
     return pooled
 
 
-def pair_count(F: int) -> int:
-    """Number of unordered pairs without self-pairs among F vectors."""
-    return F * (F - 1) // 2
+def pair_count(F: int, self_pairs: bool = False) -> int:
+    """Number of unordered pairs among F vectors, without (F(F-1)/2) or with
+    (F(F+1)/2) the pairs of a vector with itself."""
+    return F * (F + 1) // 2 if self_pairs else F * (F - 1) // 2
 
 
-def pairs(F: int):
-    """(k, i, j) for the strict lower triangle, row-major: (1,0),(2,0),(2,1),(3,0),..."""
+def pairs(F: int, self_pairs: bool = False):
+    """(k, i, j) over the lower triangle, row-major. Strict (the default, i > j):
+    (1,0),(2,0),(2,1),(3,0),... With self-pairs (i >= j, the form of the dot
+    products in the "DLRM" note, section 3): (0,0),(1,0),(1,1),(2,0),..."""
     k = 0
-    for i in range(1, F):
-        for j in range(i):
+    for i in range(F):
+        for j in range(i + 1 if self_pairs else i):
             yield k, i, j
             k += 1
 
@@ -159,14 +162,14 @@ def stack_z(e0: np.ndarray, pooled: np.ndarray) -> np.ndarray:
     return Z
 
 
-def interact(e0: np.ndarray, pooled: np.ndarray) -> np.ndarray:
-    """out[b] = [e0[b] | Z[b,i] . Z[b,j] for i > j], float64."""
+def interact(e0: np.ndarray, pooled: np.ndarray, self_pairs: bool = False) -> np.ndarray:
+    """out[b] = [e0[b] | Z[b,i] . Z[b,j] for i > j (or i >= j with self_pairs)], float64."""
     B, T, D = pooled.shape
     F = T + 1
     Z = stack_z(np.asarray(e0, dtype=np.float64), pooled)
-    out = np.zeros((B, D + pair_count(F)), dtype=np.float64)
+    out = np.zeros((B, D + pair_count(F, self_pairs)), dtype=np.float64)
     out[:, :D] = e0
-    for k, i, j in pairs(F):
+    for k, i, j in pairs(F, self_pairs):
         out[:, D + k] = (Z[:, i, :] * Z[:, j, :]).sum(axis=1)
     return out
 
@@ -179,19 +182,21 @@ def embbag_fwd(tables, dtype, B, offsets, indices, e0) -> Dict[str, np.ndarray]:
 # ---------------------------------------------------------------------------
 # Backward + update
 # ---------------------------------------------------------------------------
-def interact_bwd(e0: np.ndarray, pooled: np.ndarray, d_out: np.ndarray) -> Dict[str, np.ndarray]:
+def interact_bwd(e0: np.ndarray, pooled: np.ndarray, d_out: np.ndarray,
+                 self_pairs: bool = False) -> Dict[str, np.ndarray]:
     """Gradient of out = [e0 | dots] with respect to Z and e0.
 
     d(Z_i . Z_j)/dZ_i = Z_j and d(Z_i . Z_j)/dZ_j = Z_i, so every pair (i, j) with
-    upstream gradient g adds g * Z_j to dZ_i and g * Z_i to dZ_j. e0 also reaches
-    the output directly (the first D columns), so d_e0 = d_out[:, :D] + dZ[:, 0].
+    upstream gradient g adds g * Z_j to dZ_i and g * Z_i to dZ_j (a self-pair
+    (i, i) thus adds 2 g Z_i). e0 also reaches the output directly (the first D
+    columns), so d_e0 = d_out[:, :D] + dZ[:, 0].
     """
     B, T, D = pooled.shape
     F = T + 1
     Z = stack_z(np.asarray(e0, dtype=np.float64), pooled)
     d_out = np.asarray(d_out, dtype=np.float64)
     dZ = np.zeros_like(Z)
-    for k, i, j in pairs(F):
+    for k, i, j in pairs(F, self_pairs):
         g = d_out[:, D + k][:, None]
         dZ[:, i] += g * Z[:, j]
         dZ[:, j] += g * Z[:, i]

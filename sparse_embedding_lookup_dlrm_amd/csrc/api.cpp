@@ -103,13 +103,34 @@ int dlrm_embbag_fwd(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* 
   return from_hip(launch_embbag_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
-int dlrm_interact(int32_t T, int32_t B, int32_t D, const float* e0, const float* pooled, float* out, void* stream) {
+int dlrm_interact_ex(int32_t T, int32_t B, int32_t D, int32_t self_pairs, const float* e0, const float* pooled,
+                     float* out, void* stream) {
   if (T < 1 || B < 1 || D < 1 || !e0 || !pooled || !out) return DLRM_E_INVAL;
+  if (self_pairs != 0 && self_pairs != 1) return DLRM_E_INVAL;
   if (T > DLRM_MAX_TABLES || D % 4 != 0 || D > 1024) return DLRM_E_UNSUPPORTED;
-  if (static_cast<int64_t>(B) * (D + static_cast<int64_t>(T + 1) * T / 2) >= (int64_t(1) << 40)) return DLRM_E_INVAL;
+  if (static_cast<int64_t>(B) * (D + static_cast<int64_t>(T + 1) * (T + 2) / 2) >= (int64_t(1) << 40))
+    return DLRM_E_INVAL;
   if (!aligned(e0, 16) || !aligned(pooled, 16) || !aligned(out, 4)) return DLRM_E_ALIGN;
   if (tile_bytes(T, D) > kLds) return DLRM_E_UNSUPPORTED;
-  return from_hip(launch_interact(T, B, D, e0, pooled, out, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_interact(T, B, D, self_pairs != 0, e0, pooled, out, static_cast<hipStream_t>(stream)));
+}
+
+int dlrm_interact(int32_t T, int32_t B, int32_t D, const float* e0, const float* pooled, float* out, void* stream) {
+  return dlrm_interact_ex(T, B, D, 0, e0, pooled, out, stream);
+}
+
+int dlrm_interact_bwd(int32_t T, int32_t B, int32_t D, int32_t self_pairs, const float* e0, const float* pooled,
+                      const float* d_out, float* d_e0, float* d_pooled, void* stream) {
+  if (T < 1 || B < 1 || D < 1 || !e0 || !pooled || !d_out || !d_pooled) return DLRM_E_INVAL;
+  if (self_pairs != 0 && self_pairs != 1) return DLRM_E_INVAL;
+  if (T > DLRM_MAX_TABLES || D % 4 != 0 || D > 512) return DLRM_E_UNSUPPORTED;
+  if (static_cast<int64_t>(B) * (D + static_cast<int64_t>(T + 1) * (T + 2) / 2) >= (int64_t(1) << 40))
+    return DLRM_E_INVAL;
+  if (!aligned(e0, 16) || !aligned(pooled, 16) || !aligned(d_out, 4) || !aligned(d_pooled, 16)) return DLRM_E_ALIGN;
+  if (d_e0 && !aligned(d_e0, 16)) return DLRM_E_ALIGN;
+  if (bwd_lds_bytes(T, D) > kLds) return DLRM_E_UNSUPPORTED;
+  return from_hip(launch_interact_bwd(T, B, D, self_pairs != 0, e0, pooled, d_out, d_e0, d_pooled,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int dlrm_embbag_bwd_workspace_bytes(int32_t T, int32_t B, int32_t D, int64_t nnz, const int64_t* rows, size_t* bytes) {

@@ -34,7 +34,9 @@ constexpr int kRadixRounds = kRadixTile / kRadixWaves / kWave;  // rounds of 64 
 // ---------------------------------------------------------------------------
 // 1. interaction backward
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B, int D,
+// With self-pairs the pair (i, i) sits at i(i+1)/2 + i and its gradient counts
+// twice on the diagonal of S (d(Z_i . Z_i)/dZ_i = 2 Z_i).
+__global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B, int D, bool self_pairs,
                                                                    const float* __restrict__ e0,
                                                                    const float* __restrict__ pooled,
                                                                    const float* __restrict__ d_out,
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
   extern __shared__ __align__(16) float smem[];
   const int F = T + 1;
   const int LD = D + 4;
-  const int W = D + F * (F - 1) / 2;
+  const int W = D + (self_pairs ? F * (F + 1) / 2 : F * (F - 1) / 2);
   float* Z = smem;                // [F][LD]
   float* S = smem + F * LD;       // [F][F]
   const int b = xcd_block(blockIdx.x, gridDim.x);
@@ -57,9 +59,10 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
   const float* g = d_out + static_cast<size_t>(b) * W + D;
   for (int i = threadIdx.x; i < F * F; i += kBwdThreads) {
     const int r = i / F, c = i - r * F;
+    const int hi = r > c ? r : c, lo = r > c ? c : r;
     float v = 0.f;
-    if (r > c) v = g[r * (r - 1) / 2 + c];
-    else if (c > r) v = g[c * (c - 1) / 2 + r];
+    if (self_pairs) v = hi == lo ? 2.f * g[hi * (hi + 1) / 2 + lo] : g[hi * (hi + 1) / 2 + lo];
+    else if (hi != lo) v = g[hi * (hi - 1) / 2 + lo];
     S[i] = v;
   }
   __syncthreads();
@@ -608,6 +611,16 @@ hipError_t launch_reduce_dt(const BwdArgs& a, const WsLayout& L, char* ws, const
 
 }  // namespace
 
+hipError_t launch_interact_bwd(int T, int B, int D, bool self_pairs, const float* e0, const float* pooled,
+                               const float* d_out, float* d_e0, float* d_pooled, hipStream_t st) {
+  const int F = T + 1;
+  const size_t lds = (static_cast<size_t>(F) * (D + 4) + static_cast<size_t>(F) * F) * 4;
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(interact_bwd_kernel, dim3(B), dim3(kBwdThreads), lds, st, T, B, D, self_pairs, e0, pooled, d_out,
+                     d_pooled, d_e0);
+  return hipGetLastError();
+}
+
 size_t bwd_workspace_bytes(int T, int B, int D, int64_t nnz, int64_t /*total_rows*/) {
   return layout(T, B, D, nnz).total;
 }
@@ -632,7 +645,7 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
     const int F = a.T + 1;
     const size_t lds = (static_cast<size_t>(F) * (a.D + 4) + static_cast<size_t>(F) * F) * 4;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(interact_bwd_kernel, dim3(a.B), dim3(kBwdThreads), lds, st, a.T, a.B, a.D, a.e0, a.pooled,
+    hipLaunchKernelGGL(interact_bwd_kernel, dim3(a.B), dim3(kBwdThreads), lds, st, a.T, a.B, a.D, false, a.e0, a.pooled,
                        a.d_out, d_pooled, a.d_e0);
   }
   const long long n = a.nnz;

@@ -159,10 +159,11 @@ __device__ __forceinline__ void block_pair(int w, int& bi, int& bj) {
 }
 
 // Z: [Fpad][LD] fp32 in LDS (rows >= F may hold anything); dots of block (bi, bj)
-// for i in 4bi..4bi+3, j in 4bj..4bj+3 with j < i < F go to out[i(i-1)/2 + j].
+// for i in 4bi..4bi+3, j in 4bj..4bj+3 with j < i < F go to out[i(i-1)/2 + j];
+// with self-pairs, j <= i < F go to out[i(i+1)/2 + j].
 template <bool TO_LDS>
 __device__ __forceinline__ void dots_block(const float* Z, int F, int D, int LD, int bi, int bj,
-                                           float* __restrict__ out) {
+                                           float* __restrict__ out, bool self_pairs = false) {
   float acc[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -195,9 +196,10 @@ __device__ __forceinline__ void dots_block(const float* Z, int F, int D, int LD,
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int j = 4 * bj + q;
-      if (i < F && j < i) {
-        if constexpr (TO_LDS) out[i * (i - 1) / 2 + j] = acc[r][q];
-        else store_stream(out + (i * (i - 1) / 2 + j), acc[r][q]);
+      if (i < F && (j < i || (self_pairs && j == i))) {
+        const int k = self_pairs ? i * (i + 1) / 2 + j : i * (i - 1) / 2 + j;
+        if constexpr (TO_LDS) out[k] = acc[r][q];
+        else store_stream(out + k, acc[r][q]);
       }
     }
   }
@@ -224,8 +226,8 @@ __host__ __device__ inline Tile make_tile(int T, int D, int S) {
 }
 
 __device__ __forceinline__ void interact_from_lds(const float* Zall, const Tile& tl, int D, int b0, int B,
-                                                  float* __restrict__ out_inter) {
-  const int W = D + tl.F * (tl.F - 1) / 2;
+                                                  float* __restrict__ out_inter, bool self_pairs = false) {
+  const int W = D + (self_pairs ? tl.F * (tl.F + 1) / 2 : tl.F * (tl.F - 1) / 2);
   const int items = tl.S * tl.nblk;
   for (int w = threadIdx.x; w < items; w += kThreads) {
     const int s = w / tl.nblk, blk = w - s * tl.nblk;
@@ -234,7 +236,7 @@ __device__ __forceinline__ void interact_from_lds(const float* Zall, const Tile&
     int bi, bj;
     block_pair(blk, bi, bj);
     dots_block<false>(Zall + static_cast<size_t>(s) * tl.Fpad * tl.LD, tl.F, D, tl.LD, bi, bj,
-               out_inter + static_cast<size_t>(b) * W + D);
+                      out_inter + static_cast<size_t>(b) * W + D, self_pairs);
   }
 }
 
@@ -318,11 +320,11 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FwdArgs a, int S) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void interact_kernel(int T, int B, int D, const float* __restrict__ e0,
                                                             const float* __restrict__ pooled,
-                                                            float* __restrict__ out, int S) {
+                                                            float* __restrict__ out, int S, bool self_pairs) {
   extern __shared__ __align__(16) float smem[];
   const Tile tl = make_tile(T, D, S);
   const int b0 = xcd_block(blockIdx.x, gridDim.x) * S;
-  const int W = D + tl.F * (tl.F - 1) / 2;
+  const int W = D + (self_pairs ? tl.F * (tl.F + 1) / 2 : tl.F * (tl.F - 1) / 2);
   const int D4 = D / 4;
   for (int i = threadIdx.x; i < S * tl.F * D4; i += kThreads) {
     const int s = i / (tl.F * D4);
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void interact_kernel(int T, int B, int D,
     *reinterpret_cast<float4*>(smem + (static_cast<size_t>(s) * tl.Fpad + f) * tl.LD + d) = v;
   }
   __syncthreads();
-  interact_from_lds(smem, tl, D, b0, B, out);
+  interact_from_lds(smem, tl, D, b0, B, out, self_pairs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1162,7 +1164,8 @@ hipError_t launch_embbag_fwd(const FwdArgs& a, hipStream_t st) {
   }
 }
 
-hipError_t launch_interact(int T, int B, int D, const float* e0, const float* pooled, float* out, hipStream_t st) {
+hipError_t launch_interact(int T, int B, int D, bool self_pairs, const float* e0, const float* pooled, float* out,
+                           hipStream_t st) {
   int S = 1;
   while (S * (T + 1) < 16 && S < B) S *= 2;
   for (;;) {
@@ -1174,7 +1177,7 @@ hipError_t launch_interact(int T, int B, int D, const float* e0, const float* po
   const size_t lds = tl.z_floats() * 4;
   if (lds > kMaxLds) return hipErrorInvalidValue;
   const int grid = (B + S - 1) / S;
-  hipLaunchKernelGGL(interact_kernel, dim3(grid), dim3(kThreads), lds, st, T, B, D, e0, pooled, out, S);
+  hipLaunchKernelGGL(interact_kernel, dim3(grid), dim3(kThreads), lds, st, T, B, D, e0, pooled, out, S, self_pairs);
   return hipGetLastError();
 }
 

@@ -36,7 +36,10 @@ struct FwdArgs {
 };
 
 hipError_t launch_embbag_fwd(const FwdArgs& a, hipStream_t s);
-hipError_t launch_interact(int T, int B, int D, const float* e0, const float* pooled, float* out, hipStream_t s);
+hipError_t launch_interact(int T, int B, int D, bool self_pairs, const float* e0, const float* pooled, float* out,
+                           hipStream_t s);
+hipError_t launch_interact_bwd(int T, int B, int D, bool self_pairs, const float* e0, const float* pooled,
+                               const float* d_out, float* d_e0, float* d_pooled, hipStream_t s);
 hipError_t launch_lengths_to_offsets(int64_t n, const int32_t* lengths, int32_t* offsets, int32_t* status,
                                      hipStream_t s);
 

@@ -35,6 +35,9 @@ _SIGNATURES = {
     "dlrm_embbag_fwd": (ctypes.c_int, [_i32, _i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p, _c_void_p, _i64,
                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "dlrm_interact": (ctypes.c_int, [_i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "dlrm_interact_ex": (ctypes.c_int, [_i32, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "dlrm_interact_bwd": (ctypes.c_int, [_i32, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_void_p, _c_void_p]),
     "dlrm_embbag_bwd_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i64, _P(_i64), _P(_size_t)]),
     "dlrm_embbag_bwd_update": (ctypes.c_int, [_i32, _i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p, _c_void_p,
                                               _i64, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p, _c_void_p,
@@ -160,14 +163,37 @@ def embbag_fwd(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: t
     return out_pooled, out_inter
 
 
-def interact(e0: torch.Tensor, pooled: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """[e0 | strict-lower dots of Z = [e0; pooled]] from pooled [B, T, D] fp32."""
+def interact(e0: torch.Tensor, pooled: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None,
+             self_pairs: bool = False) -> torch.Tensor:
+    """[e0 | lower-triangle dots of Z = [e0; pooled]] from pooled [B, T, D] fp32: pairs i > j
+    (dlrm_interact), or i >= j with self_pairs (dlrm_interact_ex)."""
     _require_cuda(e0, pooled, out)
     B, T, D = pooled.shape
+    F = T + 1
     if out is None:
-        out = torch.empty((B, D + pair_count(T)), dtype=torch.float32, device=pooled.device)
-    _check(lib().dlrm_interact(T, B, D, _ptr(e0), _ptr(pooled), _ptr(out), _stream(stream)), "dlrm_interact")
+        P = F * (F + 1) // 2 if self_pairs else F * (F - 1) // 2
+        out = torch.empty((B, D + P), dtype=torch.float32, device=pooled.device)
+    if self_pairs:
+        _check(lib().dlrm_interact_ex(T, B, D, 1, _ptr(e0), _ptr(pooled), _ptr(out), _stream(stream)),
+               "dlrm_interact_ex")
+    else:
+        _check(lib().dlrm_interact(T, B, D, _ptr(e0), _ptr(pooled), _ptr(out), _stream(stream)), "dlrm_interact")
     return out
+
+
+def interact_bwd(e0: torch.Tensor, pooled: torch.Tensor, d_out: torch.Tensor, self_pairs: bool = False,
+                 d_e0: Optional[torch.Tensor] = None, d_pooled: Optional[torch.Tensor] = None,
+                 want_d_e0: bool = True, stream=None) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
+    """(dL/de0, dL/dpooled) of the interaction from dL/dout (dlrm_interact_bwd)."""
+    _require_cuda(e0, pooled, d_out, d_e0, d_pooled)
+    B, T, D = pooled.shape
+    if d_pooled is None:
+        d_pooled = torch.empty((B, T, D), dtype=torch.float32, device=pooled.device)
+    if d_e0 is None and want_d_e0:
+        d_e0 = torch.empty((B, D), dtype=torch.float32, device=pooled.device)
+    _check(lib().dlrm_interact_bwd(T, B, D, 1 if self_pairs else 0, _ptr(e0), _ptr(pooled), _ptr(d_out), _ptr(d_e0),
+                                   _ptr(d_pooled), _stream(stream)), "dlrm_interact_bwd")
+    return d_e0, d_pooled
 
 
 def bwd_workspace_bytes(T: int, B: int, D: int, nnz: int, rows: Sequence[int]) -> int:

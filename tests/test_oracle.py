@@ -316,10 +316,10 @@ def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
     good = orc.embbag_fwd(_tables_f32(g), "f32", 2, off, idx, e0)["out"]
 
     # (a) column-major pair order instead of row-major
-    def bad_pairs(F):
+    def bad_pairs(F, self_pairs=False):
         k = 0
         for j in range(F):
-            for i in range(j + 1, F):
+            for i in range(j if self_pairs else j + 1, F):
                 yield k, i, j
                 k += 1
     with monkeypatch.context() as m:
@@ -405,3 +405,67 @@ def test_planted_pool_decode_sgd_segment_mistakes(monkeypatch, golden_dir):
             test_golden_backward(golden_dir)
         with pytest.raises(AssertionError):
             test_stable_order_and_segments_brute_force(0)
+
+
+# ---------------------------------------------------------------------------
+# Interaction with self-pairs (i >= j)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("F", [1, 2, 5, 27])
+def test_self_pair_interaction_equals_gram_lower_with_diagonal(F):
+    """With self-pairs the dots are numpy's lower triangle of Z Z^T, diagonal included,
+    in row-major order, F(F+1)/2 of them."""
+    rng = np.random.default_rng(F)
+    B, D = 3, 8
+    e0 = rng.standard_normal((B, D))
+    pooled = rng.standard_normal((B, F - 1, D))
+    out = orc.interact(e0, pooled, self_pairs=True)
+    assert out.shape == (B, D + F * (F + 1) // 2)
+    Z = np.concatenate([e0[:, None], pooled], axis=1)
+    il, jl = np.tril_indices(F)
+    for b in range(B):
+        np.testing.assert_allclose(out[b, D:], (Z[b] @ Z[b].T)[il, jl], rtol=1e-13, atol=1e-13)
+
+
+def test_self_pair_fm_identity_and_hand_example():
+    """Sum over i >= j of z_i . z_j = 1/2 (|sum z|^2 + sum |z|^2); and a hand-worked F=3 case:
+    z0=(1,0), z1=(2,1), z2=(0,3) -> (0,0)=1, (1,0)=2, (1,1)=5, (2,0)=0, (2,1)=3, (2,2)=9."""
+    rng = np.random.default_rng(9)
+    e0 = rng.standard_normal((4, 6))
+    pooled = rng.standard_normal((4, 5, 6))
+    out = orc.interact(e0, pooled, self_pairs=True)
+    Z = np.concatenate([e0[:, None], pooled], axis=1)
+    s = Z.sum(axis=1)
+    np.testing.assert_allclose(out[:, 6:].sum(axis=1), 0.5 * ((s * s).sum(1) + (Z * Z).sum((1, 2))), rtol=1e-12)
+    hand = orc.interact(np.array([[1.0, 0.0]]), np.array([[[2.0, 1.0], [0.0, 3.0]]]), self_pairs=True)
+    assert hand[0].tolist() == [1.0, 0.0, 1.0, 2.0, 5.0, 0.0, 3.0, 9.0]
+
+
+@pytest.mark.parametrize("self_pairs", [False, True])
+def test_interaction_backward_finite_differences(self_pairs):
+    """<d_out, out(Z)> is quadratic in Z: the central difference is exact up to rounding."""
+    rng = np.random.default_rng(5 + self_pairs)
+    B, T, D = 2, 3, 4
+    e0 = rng.standard_normal((B, D))
+    pooled = rng.standard_normal((B, T, D))
+    P = orc.pair_count(T + 1, self_pairs)
+    d_out = rng.standard_normal((B, D + P))
+    g = orc.interact_bwd(e0, pooled, d_out, self_pairs=self_pairs)
+
+    def loss(e, p):
+        return float((d_out * orc.interact(e, p, self_pairs=self_pairs)).sum())
+    h = 1e-3
+    for b in range(B):
+        for f in range(T + 1):
+            for d in range(D):
+                ep, pp = e0.copy(), pooled.copy()
+                em, pm = e0.copy(), pooled.copy()
+                if f == 0:
+                    ep[b, d] += h
+                    em[b, d] -= h
+                    want = g["d_e0"][b, d]
+                else:
+                    pp[b, f - 1, d] += h
+                    pm[b, f - 1, d] -= h
+                    want = g["dZ"][b, f, d]
+                num = (loss(ep, pp) - loss(em, pm)) / (2 * h)
+                assert abs(num - want) < 1e-8 * (1 + abs(want))
