@@ -256,7 +256,7 @@ def cpu_baseline(w, inp, n_samples, seed=2024):
                       f"fp64 numpy oracle, single thread, {dt:.2f} s; host has {len(os.sched_getaffinity(0))} cores"}
 
 
-def bench_backward(steps, warmup):
+def bench_backward(steps, warmup, adagrad=False):
     import numpy as np
     import torch
 
@@ -275,6 +275,14 @@ def bench_backward(steps, warmup):
     nnz = len(b.indices)
     ws = torch.empty(ops.bwd_workspace_bytes(w.T, w.B, w.D, nnz, b.rows), dtype=torch.uint8, device=dev)
     d_e0 = torch.empty((w.B, w.D), dtype=torch.float32, device=dev)
+    if adagrad:
+        state = [torch.zeros(n, dtype=torch.float32, device=dev) for n in b.rows]
+        run = lambda: ops.embbag_bwd_update(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, workspace=ws,
+                                            status=status, row_state=state)
+        ms, _ = time_steps(run, steps, warmup)
+        torch.cuda.synchronize()
+        return {"workload": w.name, "optimizer": "rowwise_adagrad", "ms_per_step": ms,
+                "lookups_per_s": len(b.indices) / (ms / 1e3), "status": int(status.item())}
     plan = ops.BwdPlan(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, d_e0=d_e0, workspace=ws, status=status)
     ms, _ = time_steps(plan.run, steps, warmup)
     torch.cuda.synchronize()
@@ -313,6 +321,14 @@ def bench_backward_multihot(steps, warmup):
     nnz = len(indices)
     ws = torch.empty(ops.bwd_workspace_bytes(w.T, w.B, w.D, nnz, rows), dtype=torch.uint8, device=dev)
     d_e0 = torch.empty((w.B, w.D), dtype=torch.float32, device=dev)
+    if adagrad:
+        state = [torch.zeros(n, dtype=torch.float32, device=dev) for n in b.rows]
+        run = lambda: ops.embbag_bwd_update(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, workspace=ws,
+                                            status=status, row_state=state)
+        ms, _ = time_steps(run, steps, warmup)
+        torch.cuda.synchronize()
+        return {"workload": w.name, "optimizer": "rowwise_adagrad", "ms_per_step": ms,
+                "lookups_per_s": len(b.indices) / (ms / 1e3), "status": int(status.item())}
     plan = ops.BwdPlan(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, d_e0=d_e0, workspace=ws, status=status)
     ms, _ = time_steps(plan.run, steps, warmup)
     torch.cuda.synchronize()
@@ -425,6 +441,8 @@ def main():
     if not args.no_backward:
         res["backward"] = bench_backward(max(args.steps, 20), args.warmup)
         log(f"backward: {res['backward']['ms_per_step'] * 1e3:.1f} us/step")
+        res["backward_adagrad"] = bench_backward(max(args.steps, 20), min(args.warmup, 10), adagrad=True)
+        log(f"backward row-wise AdaGrad: {res['backward_adagrad']['ms_per_step'] * 1e3:.1f} us/step")
         res["backward_multihot"] = bench_backward_multihot(max(args.steps, 20), min(args.warmup, 10))
         log(f"backward multi-hot: {res['backward_multihot']['ms_per_step'] * 1e3:.1f} us/step")
     print(json.dumps(res), flush=True)

@@ -187,6 +187,26 @@ int dlrm_embbag_bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void*
                            void* workspace, size_t ws_bytes, int32_t* status, void* stream);
 
 /*
+ * The same backward with a row-wise AdaGrad step instead of SGD ("DLRM" note,
+ * section 5, Training: the optimizer is typically adaptive, Adam or AdaGrad,
+ * and its state is sharded with the tables). The state is one fp32 value per
+ * table row, the running sum of the row's mean squared gradient:
+ *     s_r <- s_r + (1/D) sum_d G[r][d]^2,    W_r <- W_r - lr * G_r / (sqrt(s_r) + eps)
+ * for every row r the batch references (G as in dlrm_embbag_bwd_update; rows not
+ * referenced keep both W and s).
+ *   row_state  host array [T] of device fp32 pointers, table t's state is [rows[t]],
+ *              read and updated in place (start from zeros, or any non-negative values)
+ *   eps        > 0
+ * Every other argument as in dlrm_embbag_bwd_update. Deterministic.
+ */
+int dlrm_embbag_bwd_update_adagrad(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables,
+                                   const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                                   const float* e0, const float* pooled, const float* d_out, float lr, float eps,
+                                   float* const* row_state, float* d_e0, int32_t* unique_keys, int32_t* seg_offsets,
+                                   int32_t* num_unique, int32_t* perm, void* workspace, size_t ws_bytes,
+                                   int32_t* status, void* stream);
+
+/*
  * Host-side check of a bag description (host arrays): returns the DLRM_STATUS_* bits the
  * device would report (0 = valid), or a negative dlrm_status for bad arguments.
  */

@@ -241,13 +241,20 @@ def segments(sorted_keys: np.ndarray):
 
 
 def embbag_bwd_update(tables: List[np.ndarray], dtype: str, B: int, offsets, indices, e0,
-                      pooled, d_out, lr: float) -> Dict[str, object]:
-    """Interaction backward, per-row gradient, SGD on touched rows (all float64).
+                      pooled, d_out, lr: float, optimizer: str = "sgd", state=None,
+                      eps: float = 1e-8) -> Dict[str, object]:
+    """Interaction backward, per-row gradient, update of the touched rows (all float64).
+
+    optimizer "sgd": W <- W - lr * G. optimizer "rowwise_adagrad" (the "DLRM" note,
+    section 5, Training, names AdaGrad; the reading taken is the row-wise form, one
+    state value per row): s <- s + mean over the row of G^2, then
+    W <- W - lr * G / (sqrt(s) + eps). state is a list of per-table arrays [rows_t]
+    (None = zeros).
 
     Returns d_e0, dZ, perm (stable order of occurrences by key), unique_keys,
-    seg_offsets, grad (one row per unique key), and new_rows: the updated value
-    (float64) of every touched row, keyed like unique_keys. Untouched rows keep
-    their stored value.
+    seg_offsets, grad (one row per unique key), new_rows: the updated value
+    (float64) of every touched row, keyed like unique_keys, and for AdaGrad
+    new_state, keyed the same way. Untouched rows keep their stored value.
     """
     T = len(tables)
     rows = [tb.shape[0] for tb in tables]
@@ -265,8 +272,21 @@ def embbag_bwd_update(tables: List[np.ndarray], dtype: str, B: int, offsets, ind
             p = int(perm[q])
             grad[u] += dZ[smp[p], 1 + tab[p]]
     new_rows = np.zeros((U, D), dtype=np.float64)
+    new_state = np.zeros(U, dtype=np.float64)
     for u in range(U):
         t = int(tab[perm[int(seg[u])]])
-        new_rows[u] = decode(tables[t][int(uniq[u]) - base[t]], dtype) - lr * grad[u]
-    return {"d_e0": bw["d_e0"], "dZ": dZ, "perm": perm, "unique_keys": uniq, "seg_offsets": seg,
-            "grad": grad, "new_rows": new_rows, "base": np.array(base, dtype=np.int64)}
+        r = int(uniq[u]) - base[t]
+        w = decode(tables[t][r], dtype)
+        if optimizer == "sgd":
+            new_rows[u] = w - lr * grad[u]
+        elif optimizer == "rowwise_adagrad":
+            s = (0.0 if state is None else float(state[t][r])) + float(np.mean(grad[u] * grad[u]))
+            new_state[u] = s
+            new_rows[u] = w - lr * grad[u] / (np.sqrt(s) + eps)
+        else:
+            raise ValueError(optimizer)
+    out = {"d_e0": bw["d_e0"], "dZ": dZ, "perm": perm, "unique_keys": uniq, "seg_offsets": seg,
+           "grad": grad, "new_rows": new_rows, "base": np.array(base, dtype=np.int64)}
+    if optimizer == "rowwise_adagrad":
+        out["new_state"] = new_state
+    return out

@@ -59,6 +59,51 @@ constexpr size_t kLds = 160 * 1024;
 
 }  // namespace
 
+namespace {
+
+int bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables, const int64_t* rows,
+               const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0, const float* pooled,
+               const float* d_out, float lr, int opt, float eps, float* const* state, float* d_e0,
+               int32_t* unique_keys, int32_t* seg_offsets, int32_t* num_unique, int32_t* perm, void* workspace,
+               size_t ws_bytes, int32_t* status, void* stream) {
+  int rc = check_batch(T, B, D, dtype, const_cast<const void* const*>(tables), rows, offsets, indices, nnz);
+  if (rc != DLRM_OK) return rc;
+  if (!e0 || !pooled || !d_out || !workspace) return DLRM_E_INVAL;
+  if (!aligned(e0, 16) || !aligned(pooled, 16) || !aligned(d_out, 4) || !aligned(workspace, 256)) return DLRM_E_ALIGN;
+  if (d_e0 && !aligned(d_e0, 16)) return DLRM_E_ALIGN;
+  if (D % 4 != 0 || D > 512) return DLRM_E_UNSUPPORTED;
+  if (bwd_lds_bytes(T, D) > kLds) return DLRM_E_UNSUPPORTED;
+  if (opt == kRowwiseAdagrad) {
+    if (!state || !(eps > 0.f)) return DLRM_E_INVAL;
+    for (int t = 0; t < T; ++t)
+      if (!state[t]) return DLRM_E_INVAL;
+      else if (!aligned(state[t], 4)) return DLRM_E_ALIGN;
+  }
+  int64_t total = 0;
+  for (int t = 0; t < T; ++t) total += rows[t];
+  if (total >= kI32Max) return DLRM_E_UNSUPPORTED;  // keys and the sentinel are int32
+  if (ws_bytes < bwd_workspace_bytes(T, B, D, nnz, total)) return DLRM_E_WORKSPACE;
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.T = T; a.B = B; a.D = D; a.dtype = dtype;
+  int64_t base = 0;
+  for (int t = 0; t < T; ++t) {
+    a.tabs.ptr[t] = tables[t];
+    a.tabs.rows[t] = static_cast<int32_t>(rows[t]);
+    a.tabs.base[t] = static_cast<int32_t>(base);
+    base += rows[t];
+    if (opt == kRowwiseAdagrad) a.state.ptr[t] = state[t];
+  }
+  a.total_rows = total;
+  a.offsets = offsets; a.indices = indices; a.nnz = nnz;
+  a.e0 = e0; a.pooled = pooled; a.d_out = d_out; a.lr = lr; a.opt = opt; a.eps = eps; a.d_e0 = d_e0;
+  a.unique_keys = unique_keys; a.seg_offsets = seg_offsets; a.num_unique = num_unique; a.perm = perm;
+  a.workspace = workspace; a.ws_bytes = ws_bytes; a.status = status;
+  return from_hip(launch_embbag_bwd_update(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* dlrm_status_string(int status) {
@@ -143,38 +188,24 @@ int dlrm_embbag_bwd_workspace_bytes(int32_t T, int32_t B, int32_t D, int64_t nnz
   return DLRM_OK;
 }
 
+
 int dlrm_embbag_bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables, const int64_t* rows,
                            const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0,
                            const float* pooled, const float* d_out, float lr, float* d_e0, int32_t* unique_keys,
                            int32_t* seg_offsets, int32_t* num_unique, int32_t* perm, void* workspace, size_t ws_bytes,
                            int32_t* status, void* stream) {
-  int rc = check_batch(T, B, D, dtype, const_cast<const void* const*>(tables), rows, offsets, indices, nnz);
-  if (rc != DLRM_OK) return rc;
-  if (!e0 || !pooled || !d_out || !workspace) return DLRM_E_INVAL;
-  if (!aligned(e0, 16) || !aligned(pooled, 16) || !aligned(d_out, 4) || !aligned(workspace, 256)) return DLRM_E_ALIGN;
-  if (d_e0 && !aligned(d_e0, 16)) return DLRM_E_ALIGN;
-  if (D % 4 != 0 || D > 512) return DLRM_E_UNSUPPORTED;
-  if (bwd_lds_bytes(T, D) > kLds) return DLRM_E_UNSUPPORTED;
-  int64_t total = 0;
-  for (int t = 0; t < T; ++t) total += rows[t];
-  if (total >= kI32Max) return DLRM_E_UNSUPPORTED;  // keys and the sentinel are int32
-  if (ws_bytes < bwd_workspace_bytes(T, B, D, nnz, total)) return DLRM_E_WORKSPACE;
-  BwdArgs a;
-  memset(&a, 0, sizeof(a));
-  a.T = T; a.B = B; a.D = D; a.dtype = dtype;
-  int64_t base = 0;
-  for (int t = 0; t < T; ++t) {
-    a.tabs.ptr[t] = tables[t];
-    a.tabs.rows[t] = static_cast<int32_t>(rows[t]);
-    a.tabs.base[t] = static_cast<int32_t>(base);
-    base += rows[t];
-  }
-  a.total_rows = total;
-  a.offsets = offsets; a.indices = indices; a.nnz = nnz;
-  a.e0 = e0; a.pooled = pooled; a.d_out = d_out; a.lr = lr; a.d_e0 = d_e0;
-  a.unique_keys = unique_keys; a.seg_offsets = seg_offsets; a.num_unique = num_unique; a.perm = perm;
-  a.workspace = workspace; a.ws_bytes = ws_bytes; a.status = status;
-  return from_hip(launch_embbag_bwd_update(a, static_cast<hipStream_t>(stream)));
+  return bwd_update(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, pooled, d_out, lr, kSgd, 0.f, nullptr,
+                    d_e0, unique_keys, seg_offsets, num_unique, perm, workspace, ws_bytes, status, stream);
+}
+
+int dlrm_embbag_bwd_update_adagrad(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables,
+                                   const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                                   const float* e0, const float* pooled, const float* d_out, float lr, float eps,
+                                   float* const* row_state, float* d_e0, int32_t* unique_keys, int32_t* seg_offsets,
+                                   int32_t* num_unique, int32_t* perm, void* workspace, size_t ws_bytes,
+                                   int32_t* status, void* stream) {
+  return bwd_update(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, pooled, d_out, lr, kRowwiseAdagrad, eps,
+                    row_state, d_e0, unique_keys, seg_offsets, num_unique, perm, workspace, ws_bytes, status, stream);
 }
 
 int dlrm_validate_bags(int32_t T, int32_t B, const int64_t* rows, const int32_t* offsets, const int32_t* indices,

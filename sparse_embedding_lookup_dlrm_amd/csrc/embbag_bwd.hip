@@ -351,6 +351,7 @@ struct TabVec {
       }
     }
   }
+  // W - step * g with step = lr (SGD) or lr / (sqrt(state) + eps) (row-wise AdaGrad)
   __device__ __forceinline__ void sgd_store(const MutTableArgs& tabs, RowRef r, int col, const RowVec<EL>& g,
                                             float lr) const {
     const float nlr = -lr;
@@ -367,8 +368,28 @@ struct TabVec {
   }
 };
 
-template <int DT, int EL, int C>
-__global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs tabs, int T, int D,
+// Row-wise AdaGrad on a segment's summed gradient g (this lane's EL columns):
+// state <- state + mean over the row of g^2, then step = lr / (sqrt(state) + eps).
+// The sum of squares is a butterfly over the wave (fixed order); lanes that
+// repeat columns (D < 64) contribute nothing. Lane 0 writes the new state.
+template <int EL>
+__device__ __forceinline__ float adagrad_step(const RowVec<EL>& g, float s_old, float* s_ptr, int D, float lr,
+                                              float eps) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int lpr = D < kWave ? D : kWave;
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < EL; ++e) ss = fmaf(g.v[e], g.v[e], ss);
+  if (lane >= lpr) ss = 0.f;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) ss += shfl_xor_f(ss, m);
+  const float s_new = s_old + ss / static_cast<float>(D);
+  if (lane == 0) *s_ptr = s_new;
+  return lr / (sqrtf(s_new) + eps);
+}
+
+template <int DT, int EL, int C, int OPT>
+__global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs tabs, StateArgs state, float eps, int T, int D,
                                                                  const int32_t* __restrict__ unique_keys,
                                                                  const int32_t* __restrict__ seg_offsets,
                                                                  const int32_t* __restrict__ num_unique,
@@ -434,14 +455,17 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
   RowVec<EL> rows[C];
   TabVec<DT, EL> trow[C];
   RowRef refs[C];
+  float sold[OPT == kRowwiseAdagrad ? C : 1];
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int r = __shfl(src, j, kWave);
     rows[j].load(d_pooled + static_cast<size_t>(r) * D + col);
     const int jj = ((complete_mask >> j) & 1ull) ? j : 0;
     refs[j].t = __builtin_amdgcn_readfirstlane(__shfl(tk, jj, kWave));
-    refs[j].off = static_cast<size_t>(__builtin_amdgcn_readfirstlane(__shfl(rk, jj, kWave))) * D;
+    const int rj = __builtin_amdgcn_readfirstlane(__shfl(rk, jj, kWave));
+    refs[j].off = static_cast<size_t>(rj) * D;
     trow[j].load(tabs, refs[j], col);
+    if constexpr (OPT == kRowwiseAdagrad) sold[j] = state.ptr[refs[j].t][rj];
   }
   RowVec<EL> acc;
 #pragma unroll
@@ -454,7 +478,13 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
       for (int e = 0; e < EL; ++e) acc.v[e] += rows[j].v[e];
       if ((close_mask >> j) & 1ull) {
         if ((complete_mask >> j) & 1ull) {
-          trow[j].sgd_store(tabs, refs[j], col, acc, lr);
+          if constexpr (OPT == kRowwiseAdagrad) {
+            const int rj = static_cast<int>(refs[j].off / D);
+            trow[j].sgd_store(tabs, refs[j], col, acc,
+                              adagrad_step<EL>(acc, sold[j], state.ptr[refs[j].t] + rj, D, lr, eps));
+          } else {
+            trow[j].sgd_store(tabs, refs[j], col, acc, lr);
+          }
         } else if ((carry_mask >> j) & 1ull) {
           // the chunk's first segment, begun in an earlier chunk, ends or runs through here
           acc.store(carry + static_cast<size_t>(k) * D + col);
@@ -470,21 +500,26 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
   if (lane == 0) chunk_flags[k] = flags;
 }
 
-// W[row of key] <- W - lr * g on this lane's EL columns (one segment).
-template <int DT, int EL>
-__device__ __forceinline__ void sgd_update(const MutTableArgs& tabs, int T, int D, int key, int col,
-                                           const RowVec<EL>& g, float lr) {
+// The update of one segment's row (this lane's EL columns).
+template <int DT, int EL, int OPT>
+__device__ __forceinline__ void row_update(const MutTableArgs& tabs, const StateArgs& state, float eps, int T, int D,
+                                           int key, int col, const RowVec<EL>& g, float lr) {
   const RowRef r = row_of_key(tabs, T, D, key);
   TabVec<DT, EL> x;
   x.load(tabs, r, col);
-  x.sgd_store(tabs, r, col, g, lr);
+  if constexpr (OPT == kRowwiseAdagrad) {
+    const int row = key - tabs.base[r.t];
+    x.sgd_store(tabs, r, col, g, adagrad_step<EL>(g, state.ptr[r.t][row], state.ptr[r.t] + row, D, lr, eps));
+  } else {
+    x.sgd_store(tabs, r, col, g, lr);
+  }
 }
 
 // Segments that cross chunk ends: the chunk where such a segment begins (its
 // last segment goes on, and did not itself begin earlier) adds the later
 // chunks' carries in order and applies the update.
-template <int DT, int EL, int C>
-__global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, int T, int D,
+template <int DT, int EL, int C, int OPT>
+__global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, StateArgs state, float eps, int T, int D,
                                                            const int32_t* __restrict__ unique_keys,
                                                            const int32_t* __restrict__ seg_offsets,
                                                            const int32_t* __restrict__ num_unique,
@@ -520,7 +555,7 @@ __global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, in
     const int fj = chunk_flags[j];
     if (!((fj & kChunkSingle) && (fj & kChunkLastCont))) break;
   }
-  sgd_update<DT, EL>(tabs, T, D, unique_keys[sid], col, acc, lr);
+  row_update<DT, EL, OPT>(tabs, state, eps, T, D, unique_keys[sid], col, acc, lr);
 }
 
 // ---------------------------------------------------------------------------
@@ -589,10 +624,17 @@ hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, cons
   int32_t* flags = reinterpret_cast<int32_t*>(ws + L.chunk_flags);
   constexpr int kWavesPerBlock = kBwdThreads / kWave;
   const dim3 g(static_cast<unsigned>((nchunks + kWavesPerBlock - 1) / kWavesPerBlock)), blk(kBwdThreads);
-  hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C>), g, blk, 0, st, a.tabs, a.T, a.D, uniq, seg, nuniq, head_pos, perm,
-                     bag_of, d_pooled, a.lr, carry, head, flags, nchunks);
-  hipLaunchKernelGGL((seg_combine<DT, EL, C>), g, blk, 0, st, a.tabs, a.T, a.D, uniq, seg, nuniq, head_pos, carry, head,
-                     flags, nchunks, a.lr);
+  if (a.opt == kRowwiseAdagrad) {
+    hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D,
+                       uniq, seg, nuniq, head_pos, perm, bag_of, d_pooled, a.lr, carry, head, flags, nchunks);
+    hipLaunchKernelGGL((seg_combine<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, uniq,
+                       seg, nuniq, head_pos, carry, head, flags, nchunks, a.lr);
+  } else {
+    hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, uniq, seg,
+                       nuniq, head_pos, perm, bag_of, d_pooled, a.lr, carry, head, flags, nchunks);
+    hipLaunchKernelGGL((seg_combine<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, uniq, seg,
+                       nuniq, head_pos, carry, head, flags, nchunks, a.lr);
+  }
   return hipGetLastError();
 }
 

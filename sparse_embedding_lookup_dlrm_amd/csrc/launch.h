@@ -23,6 +23,13 @@ struct MutTableArgs {
   int32_t base[DLRM_MAX_TABLES];  // first global key of each table
 };
 
+// Per-row optimizer state (row-wise AdaGrad: one fp32 sum of squares per row).
+struct StateArgs {
+  float* ptr[DLRM_MAX_TABLES];
+};
+
+enum Optimizer { kSgd = 0, kRowwiseAdagrad = 1 };
+
 struct FwdArgs {
   int T, B, D, dtype;
   TableArgs tabs;
@@ -54,6 +61,9 @@ struct BwdArgs {
   const float* pooled;
   const float* d_out;
   float lr;
+  int opt;    // Optimizer
+  float eps;  // row-wise AdaGrad: added to sqrt(state)
+  StateArgs state;
   float* d_e0;
   int32_t* unique_keys;
   int32_t* seg_offsets;

@@ -43,6 +43,10 @@ _SIGNATURES = {
                                               _i64, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p, _c_void_p,
                                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p,
                                               _c_void_p]),
+    "dlrm_embbag_bwd_update_adagrad": (ctypes.c_int, [_i32, _i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p,
+                                                      _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _f32, _f32,
+                                                      _P(_c_void_p), _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                      _c_void_p, _c_void_p, _size_t, _c_void_p, _c_void_p]),
     "dlrm_validate_bags": (ctypes.c_int, [_i32, _i32, _P(_i64), _P(_i32), _P(_i32), _i64]),
 }
 
@@ -207,10 +211,20 @@ def bwd_workspace_bytes(T: int, B: int, D: int, nnz: int, rows: Sequence[int]) -
 def embbag_bwd_update(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: torch.Tensor, B: int,
                       e0: torch.Tensor, pooled: torch.Tensor, d_out: torch.Tensor, lr: float, *,
                       want_d_e0: bool = True, want_segments: bool = True, workspace: Optional[torch.Tensor] = None,
-                      status: Optional[torch.Tensor] = None, stream=None) -> dict:
-    """Sparse backward + SGD on the touched rows (tables are updated in place)."""
+                      status: Optional[torch.Tensor] = None, stream=None,
+                      row_state: Optional[Sequence[torch.Tensor]] = None, eps: float = 1e-8) -> dict:
+    """Sparse backward + update of the touched rows (tables are updated in place): SGD, or
+    row-wise AdaGrad when row_state (one fp32 [rows_t] tensor per table, updated in
+    place) is given (dlrm_embbag_bwd_update_adagrad)."""
     T, D, dt, ptrs, rows = _table_args(tables)
     _require_cuda(offsets, indices, e0, pooled, d_out, workspace, status)
+    if row_state is not None:
+        if len(row_state) != T:
+            raise ValueError("row_state needs one tensor per table")
+        for st_, t in zip(row_state, tables):
+            _require_cuda(st_)
+            if st_.dtype != torch.float32 or st_.numel() != t.shape[0] or not st_.is_contiguous():
+                raise ValueError("row_state[t] must be a contiguous fp32 tensor with one value per row")
     nnz = indices.numel()
     dev = tables[0].device
     need = bwd_workspace_bytes(T, B, D, nnz, [t.shape[0] for t in tables])
@@ -223,12 +237,21 @@ def embbag_bwd_update(tables: Sequence[torch.Tensor], offsets: torch.Tensor, ind
         res["num_unique"] = torch.empty(1, dtype=torch.int32, device=dev)
         res["perm"] = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
     g = res.get
-    _check(lib().dlrm_embbag_bwd_update(T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), nnz, _ptr(e0),
-                                        _ptr(pooled), _ptr(d_out), float(lr), _ptr(g("d_e0")),
-                                        _ptr(g("unique_keys")), _ptr(g("seg_offsets")), _ptr(g("num_unique")),
-                                        _ptr(g("perm")), _ptr(workspace), workspace.numel(), _ptr(status),
-                                        _stream(stream)),
-           "dlrm_embbag_bwd_update")
+    if row_state is None:
+        _check(lib().dlrm_embbag_bwd_update(T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), nnz, _ptr(e0),
+                                            _ptr(pooled), _ptr(d_out), float(lr), _ptr(g("d_e0")),
+                                            _ptr(g("unique_keys")), _ptr(g("seg_offsets")), _ptr(g("num_unique")),
+                                            _ptr(g("perm")), _ptr(workspace), workspace.numel(), _ptr(status),
+                                            _stream(stream)),
+               "dlrm_embbag_bwd_update")
+    else:
+        sptr = (_c_void_p * T)(*[s_.data_ptr() for s_ in row_state])
+        _check(lib().dlrm_embbag_bwd_update_adagrad(T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), nnz,
+                                                    _ptr(e0), _ptr(pooled), _ptr(d_out), float(lr), float(eps), sptr,
+                                                    _ptr(g("d_e0")), _ptr(g("unique_keys")), _ptr(g("seg_offsets")),
+                                                    _ptr(g("num_unique")), _ptr(g("perm")), _ptr(workspace),
+                                                    workspace.numel(), _ptr(status), _stream(stream)),
+               "dlrm_embbag_bwd_update_adagrad")
     return res
 
 

@@ -152,3 +152,80 @@ def test_backward_wide_rows_bf16():
     w = synth.Workload("wide", T=2, rows=50, D=512, dtype="bf16", B=40, bag=("uniform", 0, 20),
                        dist=("zipf", 1.2), seed=512)
     run_bwd(w, lr=0.01, twice=True)
+
+
+def run_bwd_adagrad(w: synth.Workload, lr=0.05, eps=1e-6, steps=2):
+    """Row-wise AdaGrad over `steps` identical backward calls (the state carries over),
+    checked after every step against the oracle run from the same tables and state."""
+    b = synth.make_batch(w, with_dout=True)
+    db = DeviceBatch(b)
+    pooled, _ = db.fwd(want_pooled=True)
+    d_out = torch.from_numpy(b.dout).cuda()
+    rng = np.random.default_rng(w.seed)
+    state_h = [rng.uniform(0.0, 1e-4, size=n).astype(np.float32) for n in (t.shape[0] for t in b.tables)]
+    state = [torch.from_numpy(s).cuda() for s in state_h]
+    off = orc.lengths_to_offsets(b.lengths)
+    fwd = orc.embbag_fwd(b.tables, w.dtype, w.B, off, b.indices, b.e0)
+    at = abs_tables(b.tables, w.dtype)
+    pm = orc.embbag_pool(at, w.dtype, w.B, off, b.indices)
+    rm = orc.embbag_bwd_update(at, w.dtype, w.B, off, b.indices, np.abs(b.e0), pm, np.abs(b.dout), lr)
+    tabs_now = [t.copy() for t in b.tables]
+    rtol = RTOL[w.dtype]
+    store_ulp = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[w.dtype]
+    for step in range(steps):
+        before_state = [s.clone() for s in state]
+        res = ops.embbag_bwd_update(db.tables, db.offsets, db.indices, w.B, db.e0, pooled, d_out, lr,
+                                    status=db.status, row_state=state, eps=eps)
+        torch.cuda.synchronize()
+        assert db.status.item() == 0
+        s_prev = [s.cpu().numpy().astype(np.float64) for s in before_state]
+        # the oracle keeps the pooled vectors of the original tables, as the GPU call does
+        r = orc.embbag_bwd_update(tabs_now, w.dtype, w.B, off, b.indices, b.e0, fwd["pooled"], b.dout, lr,
+                                  optimizer="rowwise_adagrad", state=s_prev, eps=eps)
+        U = int(res["num_unique"].item())
+        assert U == len(r["unique_keys"])
+        base = r["base"]
+        keys = np.asarray(r["unique_keys"], dtype=np.int64)
+        tix = np.searchsorted(base, keys, side="right") - 1
+        rix = keys - base[tix]
+        after = host_tables(db.tables, w.dtype)
+        got_rows = np.array([orc.decode(after[t][i][None], w.dtype)[0] for t, i in zip(tix, rix)]).reshape(U, w.D)
+        was = np.array([orc.decode(tabs_now[t][i][None], w.dtype)[0] for t, i in zip(tix, rix)]).reshape(U, w.D)
+        got_state = np.array([state[t][i].item() for t, i in zip(tix, rix)])
+        s_old = np.array([s_prev[t][i] for t, i in zip(tix, rix)])
+        # tolerances: G is within rtol * M_G; s = s_old + mean(G^2) then moves by at most
+        # 2 rtol mean(|G| M_G) (plus its own rounding); the step lr G / (sqrt(s) + eps)
+        # by at most rtol lr (M_G + |G| mean(|G| M_G) / s) / sqrt(s)
+        g, mg = r["grad"], rm["grad"]
+        sm = (s_old + 2 * np.mean(np.abs(g) * mg, axis=1)) + np.abs(r["new_state"])
+        assert_mag_close(got_state, r["new_state"], sm, rtol, "state")
+        root = np.sqrt(r["new_state"])[:, None] + eps
+        cross = (np.mean(np.abs(g) * mg, axis=1) / r["new_state"])[:, None]
+        step_mag = lr * (mg + np.abs(g) * cross) / root
+        lim = np.abs(was) + 3 * step_mag + (store_ulp / rtol) * np.abs(r["new_rows"])
+        assert_mag_close(got_rows, r["new_rows"], lim, rtol, f"updated rows, step {step}")
+        # untouched rows and states stay as they were
+        touched = [np.zeros(t.shape[0], bool) for t in tabs_now]
+        for t, i in zip(tix, rix):
+            touched[t][i] = True
+        for t in range(w.T):
+            np.testing.assert_array_equal(after[t][~touched[t]], tabs_now[t][~touched[t]])
+            np.testing.assert_array_equal(state[t].cpu().numpy()[~touched[t]], before_state[t].cpu().numpy()[~touched[t]])
+        tabs_now = [a.copy() for a in after]
+
+
+def test_backward_rowwise_adagrad_zipf_26_tables():
+    run_bwd_adagrad(synth.WORKLOADS["bwd-zipf-26t-d128-b2048"], lr=0.01)
+
+
+def test_backward_rowwise_adagrad_hot_rows_fp16():
+    w = synth.Workload("hot-ada-8t5k-d64-fp16-b512", T=8, rows=5_000, D=64, dtype="f16", B=512,
+                       bag=("poisson", 20, 100), dist=("zipf", 1.1), seed=43)
+    run_bwd_adagrad(w, lr=0.01)
+
+
+@pytest.mark.parametrize("T,D,B,dtype", [(3, 16, 40, "f32"), (2, 256, 30, "bf16"), (1, 512, 20, "bf16")])
+def test_backward_rowwise_adagrad_shapes(T, D, B, dtype):
+    w = synth.Workload("ada-shape", T=T, rows=60, D=D, dtype=dtype, B=B, bag=("uniform", 0, 10),
+                       dist=("zipf", 1.2), seed=T * 10 + D)
+    run_bwd_adagrad(w, lr=0.02, steps=3)

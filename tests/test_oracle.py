@@ -469,3 +469,59 @@ def test_interaction_backward_finite_differences(self_pairs):
                     want = g["dZ"][b, f, d]
                 num = (loss(ep, pp) - loss(em, pm)) / (2 * h)
                 assert abs(num - want) < 1e-8 * (1 + abs(want))
+
+
+# ---------------------------------------------------------------------------
+# Row-wise AdaGrad
+# ---------------------------------------------------------------------------
+def _adagrad_instance(seed, scale=1.0):
+    tabs, off, idx, e0, _ = _random_instance(seed, B=5)
+    fwd = orc.embbag_fwd(tabs, "f32", 5, off, idx, e0)
+    d_out = np.random.default_rng(seed + 1).standard_normal((5, 4 + 6)) * scale
+    return tabs, off, idx, e0, fwd, d_out
+
+
+def test_adagrad_first_step_moves_each_row_by_lr_rms():
+    """From a zero state, the first row-wise AdaGrad step divides G by its own RMS:
+    every touched row moves by exactly lr in RMS (eps -> 0), whatever the gradient."""
+    tabs, off, idx, e0, fwd, d_out = _adagrad_instance(3)
+    r = orc.embbag_bwd_update(tabs, "f32", 5, off, idx, e0, fwd["pooled"], d_out, 0.05,
+                              optimizer="rowwise_adagrad", eps=1e-30)
+    for u, k in enumerate(r["unique_keys"]):
+        t = int(np.searchsorted(r["base"], k, side="right") - 1)
+        w = tabs[t][k - r["base"][t]].astype(np.float64)
+        step = w - r["new_rows"][u]
+        assert abs(np.sqrt(np.mean(step * step)) - 0.05) < 1e-12
+        assert abs(r["new_state"][u] - np.mean(r["grad"][u] ** 2)) <= 1e-15 * (1 + r["new_state"][u])
+
+
+def test_adagrad_first_step_is_scale_invariant_and_sgd_is_not():
+    tabs, off, idx, e0, fwd, d1 = _adagrad_instance(4)
+    a = orc.embbag_bwd_update(tabs, "f32", 5, off, idx, e0, fwd["pooled"], d1, 0.1, optimizer="rowwise_adagrad",
+                              eps=1e-30)
+    b = orc.embbag_bwd_update(tabs, "f32", 5, off, idx, e0, fwd["pooled"], 37.0 * d1, 0.1,
+                              optimizer="rowwise_adagrad", eps=1e-30)
+    np.testing.assert_allclose(a["new_rows"], b["new_rows"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(b["new_state"], 37.0 ** 2 * a["new_state"], rtol=1e-12)
+    s1 = orc.embbag_bwd_update(tabs, "f32", 5, off, idx, e0, fwd["pooled"], d1, 0.1)
+    s2 = orc.embbag_bwd_update(tabs, "f32", 5, off, idx, e0, fwd["pooled"], 37.0 * d1, 0.1)
+    assert not np.allclose(s1["new_rows"], s2["new_rows"])
+
+
+def test_adagrad_state_accumulates_and_damps_the_step():
+    """With the state of a first step carried into a second identical gradient, the
+    second step is the first divided by sqrt(2) (state doubles, eps -> 0)."""
+    tabs, off, idx, e0, fwd, d_out = _adagrad_instance(6)
+    r1 = orc.embbag_bwd_update(tabs, "f32", 5, off, idx, e0, fwd["pooled"], d_out, 0.1,
+                               optimizer="rowwise_adagrad", eps=1e-30)
+    state = [np.zeros(t.shape[0]) for t in tabs]
+    for u, k in enumerate(r1["unique_keys"]):
+        t = int(np.searchsorted(r1["base"], k, side="right") - 1)
+        state[t][k - r1["base"][t]] = r1["new_state"][u]
+    r2 = orc.embbag_bwd_update(tabs, "f32", 5, off, idx, e0, fwd["pooled"], d_out, 0.1,
+                               optimizer="rowwise_adagrad", state=state, eps=1e-30)
+    np.testing.assert_allclose(r2["new_state"], 2 * r1["new_state"], rtol=1e-14)
+    for u, k in enumerate(r1["unique_keys"]):
+        t = int(np.searchsorted(r1["base"], k, side="right") - 1)
+        w = tabs[t][k - r1["base"][t]].astype(np.float64)
+        np.testing.assert_allclose(w - r2["new_rows"][u], (w - r1["new_rows"][u]) / np.sqrt(2.0), rtol=1e-12)
