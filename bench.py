@@ -298,6 +298,40 @@ def bench_backward(steps, warmup, adagrad=False):
             "status": int(status.item()), "lr": 0.01}
 
 
+def bench_forward_q8(inp, steps, warmup):
+    """The fused forward on row-wise 8-bit versions of the capacity tables (per row D
+    uint8 codes, then an fp32 scale and bias; random codes, the bandwidth does not
+    depend on them), same batch. Bytes per lookup: D + 8 + 4."""
+    import torch
+
+    from sparse_embedding_lookup_dlrm_amd import ops, synth
+
+    w = synth.WORKLOADS[synth.CAPACITY]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.stream_seed(w.seed, "values") + 8)
+    packed = []
+    for n in inp["rows"]:
+        t = torch.empty((n, w.D + 8), dtype=torch.uint8, device=dev)
+        t[:, :w.D] = torch.randint(0, 256, (n, w.D), dtype=torch.uint8, device=dev, generator=g)
+        sb = t[:, w.D:].view(torch.float32)  # [n, 2]: scale, bias
+        sb[:, 0].uniform_(1e-4, 2e-4, generator=g)
+        sb[:, 1].uniform_(-0.02, -0.01, generator=g)
+        packed.append(t)
+    out = torch.empty((w.B, w.out_width), dtype=torch.float32, device=dev)
+    run = lambda: ops.embbag_fwd_q8(packed, inp["offsets"], inp["d_idx"], w.B, inp["d_e0"], out_inter=out,
+                                    status=inp["status"])
+    ms, _ = time_steps(run, steps, warmup)
+    nnz = len(inp["indices"])
+    P = (w.T + 1) * w.T // 2
+    alg = nnz * (w.D + 8 + 4) + 4 * (w.T * w.B + 1) + 4 * w.B * w.D + 4 * w.B * (w.D + P)
+    del packed, out
+    torch.cuda.empty_cache()
+    return {"workload": w.name + "-q8", "ms_per_step": ms, "lookups_per_s": nnz / (ms / 1e3),
+            "algorithmic_bytes": alg, "hbm_GBps_algorithmic": alg / (ms / 1e3) / 1e9,
+            "frac_of_8TBps": alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, "status": int(inp["status"].item())}
+
+
 def bench_backward_multihot(steps, warmup):
     """The backward + SGD on the multi-hot fp16 shapes (8 tables x 4M rows, D=64, batch
     4096, bags min(Poisson(20), 100), Zipf(1.1)), tables filled on the device."""
@@ -343,6 +377,7 @@ def main():
     ap.add_argument("--cpu-samples", type=int, default=6144)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-q8", action="store_true", help="skip the 8-bit-row forward timing")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain copy of this size (for counter calibration)")
     ap.add_argument("--summarize-profile", default=None)
@@ -428,6 +463,13 @@ def main():
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_samples)
         log(f"cpu oracle: {res['cpu_baseline']['value']:.3e} lookups/s")
+    tables = inp.pop("tables")
+    del tables
+    torch.cuda.empty_cache()
+    if not args.no_q8:
+        res["forward_q8"] = bench_forward_q8(inp, args.steps, args.warmup)
+        log(f"fused forward, 8-bit rows: {res['forward_q8']['ms_per_step'] * 1e3:.1f} us/step, "
+            f"{res['forward_q8']['hbm_GBps_algorithmic']:.0f} GB/s")
     del inp
     torch.cuda.empty_cache()
     if not args.no_backward:

@@ -77,7 +77,9 @@ typedef enum {
   DLRM_E_ALIGN = -5        /* a device pointer is not 16-byte aligned */
 } dlrm_status;
 
-typedef enum { DLRM_F32 = 0, DLRM_F16 = 1, DLRM_BF16 = 2 } dlrm_dtype;
+/* DLRM_Q8: row-wise 8-bit tables (only through dlrm_embbag_fwd_q8): a row is D uint8 codes q
+ * followed by its fp32 scale and fp32 bias, value = scale * q + bias. */
+typedef enum { DLRM_F32 = 0, DLRM_F16 = 1, DLRM_BF16 = 2, DLRM_Q8 = 3 } dlrm_dtype;
 
 /* bits OR-ed into the device status word */
 #define DLRM_STATUS_BAD_INDEX 1   /* an index outside [0, rows[t]) */
@@ -116,6 +118,24 @@ int dlrm_lengths_to_offsets(int64_t n, const int32_t* lengths, int32_t* offsets,
 int dlrm_embbag_fwd(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* const* tables,
                     const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
                     const float* e0, float* out_pooled, float* out_inter, int32_t* status, void* stream);
+
+/*
+ * The fused forward on row-wise 8-bit tables: row r of table t is D uint8 codes
+ * q followed by the row's fp32 scale and fp32 bias (D + 8 bytes, one contiguous
+ * read per lookup), value[d] = scale * q[d] + bias; a lookup reads D + 8 bytes
+ * instead of 2 D (bf16). The "Terabyte Embedding Tables..." article (section
+ * "Scaling limits and the reality of production") reports 4-bit quantization of
+ * what is exchanged between devices; here the same idea is applied, at 8 bits,
+ * to the rows stored in HBM.
+ *   tables     host array [T] of device pointers (16-byte aligned), table t is
+ *              uint8 [rows[t]][D + 8] as above
+ *   D          128, 256 or 512
+ *   out_inter  required; out_pooled optional; everything else as in dlrm_embbag_fwd.
+ * Pooling sums scale * q per column in fp32 and adds the bag's summed biases.
+ */
+int dlrm_embbag_fwd_q8(int32_t T, int32_t B, int32_t D, const void* const* tables, const int64_t* rows,
+                       const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0,
+                       float* out_pooled, float* out_inter, int32_t* status, void* stream);
 
 /*
  * Interaction alone, from pooled vectors in HBM.

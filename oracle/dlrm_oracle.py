@@ -54,11 +54,31 @@ class BagError(ValueError):
 # ---------------------------------------------------------------------------
 # Storage decoding (exact: every fp32/fp16/bf16 value is an fp64 value)
 # ---------------------------------------------------------------------------
-def decode(table: np.ndarray, dtype: str) -> np.ndarray:
-    """Stored table -> float64. bf16 tables arrive as uint16 bit patterns.
+class Q8Table:
+    """Row-wise 8-bit table: codes uint8 [rows, D] and fp32 (scale, bias) [rows, 2];
+    row r stands for scale_r * codes[r] + bias_r. Indexing a row gives (codes, pair)."""
+
+    def __init__(self, codes: np.ndarray, scale_bias: np.ndarray):
+        assert codes.dtype == np.uint8 and scale_bias.dtype == np.float32
+        assert codes.ndim == 2 and scale_bias.shape == (codes.shape[0], 2)
+        self.codes, self.scale_bias = codes, scale_bias
+        self.shape = codes.shape
+
+    def __getitem__(self, r):
+        return self.codes[r], self.scale_bias[r]
+
+
+def decode(table, dtype: str) -> np.ndarray:
+    """Stored table (or row) -> float64. bf16 tables arrive as uint16 bit patterns;
+    "q8" rows arrive as (codes, (scale, bias)) from a Q8Table.
 
     "f64" (float64 tables) is accepted for the finite-difference pins only.
     """
+    if dtype == "q8":
+        codes, sb = table
+        sb = np.asarray(sb, dtype=np.float64)
+        return sb[..., 0:1] * codes.astype(np.float64) + sb[..., 1:2] if codes.ndim > 1 else \
+            sb[0] * codes.astype(np.float64) + sb[1]
     if dtype == "f64":
         assert table.dtype == np.float64
         return table.copy()

@@ -32,6 +32,11 @@ struct Storage<DLRM_BF16> {
   static constexpr int bytes = 2;
   static constexpr int per16 = 8;
 };
+template <>
+struct Storage<DLRM_Q8> {
+  static constexpr int bytes = 1;
+  static constexpr int per16 = 16;
+};
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

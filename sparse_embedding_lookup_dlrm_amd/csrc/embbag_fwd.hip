@@ -448,10 +448,34 @@ __device__ __forceinline__ void acc_chunk(float* acc, const typename LaneChunk<L
   }
 }
 
+// Row-wise 8-bit rows: acc[0..LB) += s * q for the lane's LB codes q (uint8).
+__device__ __forceinline__ float ubyte(uint32_t w, int k) { return static_cast<float>((w >> (8 * k)) & 0xffu); }
+
+template <int LB>
+__device__ __forceinline__ void acc_chunk_q8(float* acc, const typename LaneChunk<LB>::type& v, float s) {
+  if constexpr (LB == 2) {
+    acc[0] = fmaf(s, ubyte(v, 0), acc[0]);
+    acc[1] = fmaf(s, ubyte(v, 1), acc[1]);
+  } else if constexpr (LB == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] = fmaf(s, ubyte(v, k), acc[k]);
+  } else {
+    static_assert(LB == 8, "8-bit rows of 128, 256 or 512 bytes");
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[k] = fmaf(s, ubyte(v.x, k), acc[k]);
+      acc[4 + k] = fmaf(s, ubyte(v.y, k), acc[4 + k]);
+    }
+  }
+}
+
 template <int DT, int LB>
 struct RowShape {
   static constexpr int EL = LB / Storage<DT>::bytes;  // fp32 columns per lane
-  static constexpr int WIN = LB >= 4 ? 64 / LB : 16;  // rows per window (two windows in flight: 32 VGPRs)
+  // rows per window (two windows in flight: 32 VGPRs); 8-bit rows also carry a
+  // scale and a bias per row and keep more columns per lane, so their windows
+  // are smaller
+  static constexpr int WIN = DT == DLRM_Q8 ? (LB >= 8 ? 4 : 8) : (LB >= 4 ? 64 / LB : 16);
 };
 
 struct RowLayout {
@@ -619,6 +643,7 @@ struct Window {
   uint32_t alo, ahi;
   int tk;
   unsigned long long fmask, smask;
+  float sc, bi;  // 8-bit rows: this lane's row's scale and bias (in flight with the rows)
 };
 
 struct RowCursor {
@@ -647,11 +672,15 @@ __device__ __forceinline__ int last_le(const int* pos, int T, int x) {
 // kStageCap rows); only then does this read indices from HBM. Keeping that
 // path out of the common loop keeps the loop free of loads other than the
 // table rows, so the compiler's wait counts stay exact.
-template <int WIN, int RB, bool BEYOND>
+// 8-bit rows (Q8) are D codes followed by the row's fp32 scale and bias: a
+// row is RB + 8 bytes apart from the next, and each lane also loads the
+// (scale, bias) pair of "its" row of the window, from the same DRAM page.
+template <int WIN, int RB, bool BEYOND, bool Q8 = false>
 __device__ __forceinline__ void prepare_window(Window& w, const FwdArgs& a, const int* sm_beg, const int* sm_pos,
                                                const int* stage, const uint8_t* sbag, const char* const* tbase,
                                                const int* trows, int T, int q, int p1, uint64_t fallback,
                                                int tid) {
+  constexpr uint64_t kStride = Q8 ? RB + 8 : RB;
   const int lane = tid & (kWave - 1);
   uint64_t addr = fallback;
   int tk = 0;
@@ -672,10 +701,16 @@ __device__ __forceinline__ void prepare_window(Window& w, const FwdArgs& a, cons
       }
     }
     if (r >= 0) {  // an index outside its table keeps the fallback row and is skipped
-      addr = reinterpret_cast<uint64_t>(tbase[tk]) + static_cast<uint64_t>(r) * RB;
+      addr = reinterpret_cast<uint64_t>(tbase[tk]) + static_cast<uint64_t>(r) * kStride;
       skip = false;
     }
     flush = (pos + 1 == sm_pos[tk + 1]) || (pos + 1 == p1);
+  }
+  if constexpr (Q8) {
+    // every lane loads the (scale, bias) pair of its row (skipped slots: the fallback row's)
+    const auto p = reinterpret_cast<gptr<uint32_t>>(addr + RB);
+    w.sc = __uint_as_float(p[0]);
+    w.bi = __uint_as_float(p[1]);
   }
   w.alo = static_cast<uint32_t>(addr);
   w.ahi = static_cast<uint32_t>(addr >> 32);
@@ -694,15 +729,24 @@ __device__ __forceinline__ void issue_window(const Window& w, typename C::type (
 template <int DT, int LB, int WIN>
 __device__ __forceinline__ void consume_window(const Window& w, typename LaneChunk<LB>::type (&v)[WIN],
                                                float (&acc)[LB / Storage<DT>::bytes], RowCursor& cur, float* Z,
-                                               int LD, float* carry_w, int* carry_t_w, int tid) {
+                                               int LD, float* carry_w, int* carry_t_w, int tid, float& bacc) {
   constexpr int EL = LB / Storage<DT>::bytes;
   const int lane = tid & (kWave - 1);
 #pragma unroll
   for (int j = 0; j < WIN; ++j) {
     // a skipped slot loaded a valid fallback row; it adds zero instead (a
     // select, so the load's register is only read, never overwritten early)
-    const typename LaneChunk<LB>::type x = ((w.smask >> j) & 1ull) ? LaneChunk<LB>::zero() : v[j];
-    acc_chunk<DT, LB>(acc, x);
+    const bool skipped = (w.smask >> j) & 1ull;
+    const typename LaneChunk<LB>::type x = skipped ? LaneChunk<LB>::zero() : v[j];
+    if constexpr (DT == DLRM_Q8) {
+      // scale * q summed per column; the biases of the bag's rows summed once
+      const float sj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w.sc), j));
+      const float bj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w.bi), j));
+      acc_chunk_q8<LB>(acc, x, skipped ? 0.f : sj);
+      bacc += skipped ? 0.f : bj;
+    } else {
+      acc_chunk<DT, LB>(acc, x);
+    }
     if ((w.fmask >> j) & 1ull) {
       const int tj = __builtin_amdgcn_readlane(w.tk, j);
       float* dst = Z + (1 + tj) * LD;
@@ -713,9 +757,10 @@ __device__ __forceinline__ void consume_window(const Window& w, typename LaneChu
       }
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        dst[lane * EL + e] = acc[e];
+        dst[lane * EL + e] = DT == DLRM_Q8 ? acc[e] + bacc : acc[e];
         acc[e] = 0.f;
       }
+      bacc = 0.f;
     }
   }
 }
@@ -821,6 +866,7 @@ __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, c
                                              const uint8_t* sbag, const char* const* tbase, const int* trows, int T,
                                              int p0, int p1, float* Z, int LD, float* carry_w, int* carry_t_w,
                                              int tid) {
+  constexpr bool Q8 = DT == DLRM_Q8;
   using C = LaneChunk<LB>;
   using RS = RowShape<DT, LB>;
   constexpr int EL = RS::EL;
@@ -832,21 +878,22 @@ __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, c
   float acc[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) acc[e] = 0.f;
+  float bacc = 0.f;
   const uint64_t fallback = reinterpret_cast<uint64_t>(tbase[0]);
   const uint64_t lane_off = static_cast<uint64_t>(tid & (kWave - 1)) * LB;
   Window wa, wb;
   typename C::type va[WIN], vb[WIN];
-  prepare_window<WIN, RB, BEYOND>(wa, a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, fallback, tid);
+  prepare_window<WIN, RB, BEYOND, Q8>(wa, a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, fallback, tid);
   issue_window<C, WIN>(wa, va, lane_off);
   for (int q = p0;;) {
-    prepare_window<WIN, RB, BEYOND>(wb, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid);
+    prepare_window<WIN, RB, BEYOND, Q8>(wb, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid);
     issue_window<C, WIN>(wb, vb, lane_off);
-    consume_window<DT, LB, WIN>(wa, va, acc, cur, Z, LD, carry_w, carry_t_w, tid);
+    consume_window<DT, LB, WIN>(wa, va, acc, cur, Z, LD, carry_w, carry_t_w, tid, bacc);
     q += WIN;
     if (q >= p1) break;
-    prepare_window<WIN, RB, BEYOND>(wa, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid);
+    prepare_window<WIN, RB, BEYOND, Q8>(wa, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid);
     issue_window<C, WIN>(wa, va, lane_off);
-    consume_window<DT, LB, WIN>(wb, vb, acc, cur, Z, LD, carry_w, carry_t_w, tid);
+    consume_window<DT, LB, WIN>(wb, vb, acc, cur, Z, LD, carry_w, carry_t_w, tid, bacc);
     q += WIN;
     if (q >= p1) break;
   }
@@ -870,11 +917,6 @@ __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, c
 // interaction.
 template <int DT, int LB, bool MFMA>
 __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, RowLayout L, int chunk) {
-  using C = LaneChunk<LB>;
-  using RS = RowShape<DT, LB>;
-  constexpr int EL = RS::EL;
-  constexpr int WIN = RS::WIN;
-  constexpr int RB = LB * kWave;  // row bytes
   extern __shared__ __align__(16) char lds[];
   int* carry_t = reinterpret_cast<int*>(lds + L.off_carry_t);
   const char** tbase = reinterpret_cast<const char**>(lds + L.off_tbase);
@@ -921,7 +963,6 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     // spilled) across the whole loop.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    const int lane = tid & (kWave - 1);
     const bool has_next = b + 1 < b_end;
     int* beg = reinterpret_cast<int*>(lds + L.off_beg + pb * L.pos_stride);
     int* pos = reinterpret_cast<int*>(lds + L.off_pos + pb * L.pos_stride);
@@ -1044,7 +1085,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
 // host side
 // ---------------------------------------------------------------------------
 int fwd_supported_row_bytes(int D, int dtype) {
-  const int s = dtype == DLRM_F32 ? 4 : 2;
+  const int s = dtype == DLRM_F32 ? 4 : (dtype == DLRM_Q8 ? 1 : 2);
   const long rb = static_cast<long>(D) * s;
   if (rb < 16 || rb > 1024 || (rb & (rb - 1)) != 0) return 0;
   return static_cast<int>(rb);
@@ -1116,7 +1157,7 @@ static hipError_t launch_rows(const FwdArgs& a, hipStream_t st) {
 }
 
 template <int DT, int LPR>
-static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+static hipError_t launch_fwd_float(const FwdArgs& a, hipStream_t st) {
   if (a.out_inter && use_row_kernel(a.D, DT)) {
     constexpr int LB = LPR * 16 / kWave;  // bytes per lane when one wave reads one row
     if constexpr (LB == 2 && DT != DLRM_F32) return launch_rows<DT, 2>(a, st);
@@ -1141,6 +1182,18 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int DT, int LPR>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  if constexpr (DT == DLRM_Q8) {  // 8-bit rows: row-streaming fused kernel only, rows of 128..512 bytes
+    constexpr int LB = LPR * 16 / kWave;
+    if (!a.out_inter) return hipErrorInvalidValue;
+    if constexpr (LB == 2 || LB == 4 || LB == 8) return launch_rows<DT, LB>(a, st);
+    else return hipErrorInvalidValue;
+  } else {
+    return launch_fwd_float<DT, LPR>(a, st);
+  }
+}
+
 template <int DT>
 static hipError_t launch_fwd_dt(const FwdArgs& a, hipStream_t st) {
   switch (fwd_supported_row_bytes(a.D, a.dtype) / 16) {
@@ -1160,6 +1213,7 @@ hipError_t launch_embbag_fwd(const FwdArgs& a, hipStream_t st) {
     case DLRM_F32: return launch_fwd_dt<DLRM_F32>(a, st);
     case DLRM_F16: return launch_fwd_dt<DLRM_F16>(a, st);
     case DLRM_BF16: return launch_fwd_dt<DLRM_BF16>(a, st);
+    case DLRM_Q8: return launch_fwd_dt<DLRM_Q8>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,117 @@
+"""GPU parity of the fused forward on row-wise 8-bit tables (per row: uint8 codes, then
+an fp32 scale and bias) against the fp64 oracle.
+
+Tolerance: the values are fp32 products s*q + b, pooled in fp32 (error below
+gamma_n of the magnitude sum(|s q| + |b|)), and with T >= 24 the pooled-pooled dots
+run on the bf16x3 MFMA split, whose error is below 3 * 2^-18 of sum |a||b| per
+product plus fp32 accumulation: about 2e-5 in all. The tests use 1e-4 of the
+magnitude (the same computation on absolute values)."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dlrm_oracle as orc
+from sparse_embedding_lookup_dlrm_amd import ops, synth
+
+from gpu_util import assert_mag_close, need_gpu
+
+pytestmark = pytest.mark.gpu
+RTOL_Q8 = 1e-4
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _run(w, corrupt=None):
+    rows = synth.table_rows(w)
+    q8 = synth.gen_tables_q8_host(w, rows)
+    lengths = synth.gen_lengths(w)
+    indices = synth.gen_indices(w, rows, lengths)
+    if corrupt is not None:
+        indices = indices.copy()
+        indices[corrupt] = rows[0] + 5  # out of table 0's range (position in table 0's bags)
+    e0 = synth.gen_e0(w)
+    dev = "cuda"
+    packed = [torch.from_numpy(synth.pack_q8_rows(c, sb)).to(dev) for c, sb in q8]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    offsets = ops.lengths_to_offsets(torch.from_numpy(lengths).to(dev), status=status)
+    idx = torch.from_numpy(indices).to(dev)
+    pooled, out = ops.embbag_fwd_q8(packed, offsets, idx, w.B, torch.from_numpy(e0).to(dev), want_pooled=True,
+                                    status=status)
+    _, out2 = ops.embbag_fwd_q8(packed, offsets, idx, w.B, torch.from_numpy(e0).to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)  # run to run, bit for bit
+    return q8, lengths, indices, e0, pooled.cpu().numpy(), out.cpu().numpy(), int(status.item())
+
+
+def _oracle(w, q8, lengths, indices, e0):
+    off = orc.lengths_to_offsets(lengths)
+    tabs = [orc.Q8Table(c, sb) for c, sb in q8]
+    r = orc.embbag_fwd(tabs, "q8", w.B, off, indices, e0)
+    mags = [orc.Q8Table(c, np.abs(sb)) for c, sb in q8]
+    pm = orc.embbag_pool(mags, "q8", w.B, off, indices)
+    return r, pm, orc.interact(np.abs(e0), pm)
+
+
+@pytest.mark.parametrize("T,rows,D,B,seed", [(8, 5000, 128, 256, 61), (26, 3000, 256, 200, 62),
+                                             (64, 2000, 128, 96, 63), (4, 500, 512, 64, 64),
+                                             (30, 800, 512, 40, 65)])
+def test_q8_forward(T, rows, D, B, seed):
+    w = synth.Workload("q8", T=T, rows=rows, D=D, dtype="bf16", B=B, bag=("uniform", 0, 20), dist=("zipf", 1.05),
+                       seed=seed)
+    q8, lengths, indices, e0, pooled, out, st = _run(w)
+    assert st == 0
+    r, pm, mag = _oracle(w, q8, lengths, indices, e0)
+    np.testing.assert_array_equal(out[:, :D], e0)
+    assert_mag_close(pooled, r["pooled"], pm, RTOL_Q8, "q8 pooled")
+    assert_mag_close(out[:, D:], r["out"][:, D:], mag[:, D:], RTOL_Q8, "q8 dots")
+
+
+@pytest.mark.parametrize("T,D", [(6, 128), (40, 256)])
+def test_q8_forward_exact_dyadic_values(T, D):
+    """Codes 0..4 with scales in {0.5, 1, 2} and biases in {-1, 0, 1}: every sum and dot
+    is exact in fp32 (and in the MFMA split), so the output matches bit for bit."""
+    w = synth.Workload("q8int", T=T, rows=300, D=D, dtype="bf16", B=70, bag=("uniform", 0, 12),
+                       dist=("uniform",), seed=T, values="int")
+    q8, lengths, indices, e0, pooled, out, st = _run(w)
+    assert st == 0
+    r, _, _ = _oracle(w, q8, lengths, indices, e0)
+    np.testing.assert_array_equal(pooled, r["pooled"].astype(np.float32))
+    np.testing.assert_array_equal(out, r["out"].astype(np.float32))
+
+
+def test_q8_out_of_range_index_is_flagged_and_skipped():
+    w = synth.Workload("q8bad", T=3, rows=100, D=128, dtype="bf16", B=16, bag=("uniform", 1, 6),
+                       dist=("uniform",), seed=66)
+    q8, lengths, indices, e0, pooled, out, st = _run(w, corrupt=2)
+    assert st & 1  # DLRM_STATUS_BAD_INDEX
+    # the oracle of the same batch without that occurrence
+    off = orc.lengths_to_offsets(lengths)
+    bag = int(np.searchsorted(off, 2, side="right") - 1)
+    keep = np.ones(len(indices), bool)
+    keep[2] = False
+    lengths2 = lengths.copy()
+    lengths2[bag] -= 1
+    r, pm, _ = _oracle(w, q8, lengths2, indices[keep], e0)
+    assert_mag_close(pooled, r["pooled"], pm, RTOL_Q8, "pooled without the bad row")
+
+
+def test_q8_rejections():
+    L = ops.lib()
+    tab = torch.zeros((10, 64 + 8), dtype=torch.uint8, device="cuda")
+    off = torch.zeros(2, dtype=torch.int32, device="cuda")
+    e0 = torch.zeros((1, 64), device="cuda")
+    out = torch.zeros((1, 64 + 1), device="cuda")
+    P = ctypes.c_void_p
+    ptrs = (P * 1)(tab.data_ptr())
+    rows = (ctypes.c_int64 * 1)(10)
+    # D = 64 is not a supported 8-bit row width
+    assert L.dlrm_embbag_fwd_q8(1, 1, 64, ptrs, rows, P(off.data_ptr()), None, 0, P(e0.data_ptr()), None,
+                                P(out.data_ptr()), None, None) == -2
+    # the generic entry point does not take 8-bit tables
+    assert L.dlrm_embbag_fwd(1, 1, 64, 3, ptrs, rows, P(off.data_ptr()), None, 0, P(e0.data_ptr()), None,
+                             P(out.data_ptr()), None, None) == -2

@@ -525,3 +525,23 @@ def test_adagrad_state_accumulates_and_damps_the_step():
         t = int(np.searchsorted(r1["base"], k, side="right") - 1)
         w = tabs[t][k - r1["base"][t]].astype(np.float64)
         np.testing.assert_allclose(w - r2["new_rows"][u], (w - r1["new_rows"][u]) / np.sqrt(2.0), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Row-wise 8-bit tables
+# ---------------------------------------------------------------------------
+def test_q8_decode_hand_example_and_pool_equals_dequantized_f64():
+    codes = np.array([[0, 255, 128], [7, 0, 1]], dtype=np.uint8)
+    sb = np.array([[0.5, -1.0], [0.25, 2.0]], dtype=np.float32)
+    tab = orc.Q8Table(codes, sb)
+    assert orc.decode(tab[0], "q8").tolist() == [-1.0, 126.5, 63.0]
+    assert orc.decode(tab[1], "q8").tolist() == [3.75, 2.0, 2.25]
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 256, size=(30, 8)).astype(np.uint8)
+    sb = np.stack([rng.uniform(1e-4, 1e-2, 30), rng.uniform(-1, 1, 30)], axis=1).astype(np.float32)
+    deq = codes.astype(np.float64) * sb[:, 0:1].astype(np.float64) + sb[:, 1:2].astype(np.float64)
+    idx = rng.integers(0, 30, size=25).astype(np.int32)
+    off = np.array([0, 3, 3, 10, 25])
+    got = orc.embbag_pool([orc.Q8Table(codes, sb)], "q8", 4, off, idx)
+    want = orc.embbag_pool([deq], "f64", 4, off, idx)
+    np.testing.assert_array_equal(got, want)
