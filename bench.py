@@ -101,10 +101,12 @@ def summarize_profile(d: str, out: str, command: str, timed: int = 0) -> None:
     for p in traces:
         with open(p) as f:
             rows = [r for r in csv.DictReader(f) if FWD_KERNEL in r["Kernel_Name"]]
-        if rows:
-            rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-            us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
-            lines.append(f"## {FWD_KERNEL}: per-launch durations (us), in launch order")
+        by_name = {}
+        for r in sorted(rows, key=lambda r: int(r["Start_Timestamp"])):
+            by_name.setdefault(r["Kernel_Name"].split("(")[0], []).append(r)
+        for nm, rs in by_name.items():  # one list per instantiation (table storage type)
+            us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
+            lines.append(f"## {nm}: per-launch durations (us), in launch order")
             lines.append(" ".join(f"{x:.1f}" for x in us))
             if timed > 0 and len(us) >= timed:
                 lines.append(f"mean of the last {timed} launches (the timed steps): {sum(us[-timed:]) / timed:.2f} us")
@@ -332,6 +334,34 @@ def bench_forward_q8(inp, steps, warmup):
             "frac_of_8TBps": alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, "status": int(inp["status"].item())}
 
 
+def bench_forward_q8t(inp, steps, warmup):
+    """The fused forward on table-wise 8-bit versions of the capacity tables (D uint8
+    codes per row, one scale and bias per table; random codes), same batch. Bytes per
+    lookup: D + 4."""
+    import torch
+
+    from sparse_embedding_lookup_dlrm_amd import ops, synth
+
+    w = synth.WORKLOADS[synth.CAPACITY]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.stream_seed(w.seed, "values") + 9)
+    tabs = [torch.randint(0, 256, (n, w.D), dtype=torch.uint8, device=dev, generator=g) for n in inp["rows"]]
+    sb = [(1.5e-4, -0.02)] * w.T
+    out = torch.empty((w.B, w.out_width), dtype=torch.float32, device=dev)
+    run = lambda: ops.embbag_fwd_q8t(tabs, sb, inp["offsets"], inp["d_idx"], w.B, inp["d_e0"], out_inter=out,
+                                     status=inp["status"])
+    ms, _ = time_steps(run, steps, warmup)
+    nnz = len(inp["indices"])
+    P = (w.T + 1) * w.T // 2
+    alg = nnz * (w.D + 4) + 4 * (w.T * w.B + 1) + 4 * w.B * w.D + 4 * w.B * (w.D + P)
+    del tabs, out
+    torch.cuda.empty_cache()
+    return {"workload": w.name + "-q8t", "ms_per_step": ms, "lookups_per_s": nnz / (ms / 1e3),
+            "algorithmic_bytes": alg, "hbm_GBps_algorithmic": alg / (ms / 1e3) / 1e9,
+            "frac_of_8TBps": alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, "status": int(inp["status"].item())}
+
+
 def bench_backward_multihot(steps, warmup):
     """The backward + SGD on the multi-hot fp16 shapes (8 tables x 4M rows, D=64, batch
     4096, bags min(Poisson(20), 100), Zipf(1.1)), tables filled on the device."""
@@ -470,6 +500,9 @@ def main():
         res["forward_q8"] = bench_forward_q8(inp, args.steps, args.warmup)
         log(f"fused forward, 8-bit rows: {res['forward_q8']['ms_per_step'] * 1e3:.1f} us/step, "
             f"{res['forward_q8']['hbm_GBps_algorithmic']:.0f} GB/s")
+        res["forward_q8t"] = bench_forward_q8t(inp, args.steps, args.warmup)
+        log(f"fused forward, table-wise 8-bit rows: {res['forward_q8t']['ms_per_step'] * 1e3:.1f} us/step, "
+            f"{res['forward_q8t']['hbm_GBps_algorithmic']:.0f} GB/s")
     del inp
     torch.cuda.empty_cache()
     if not args.no_backward:

@@ -78,8 +78,10 @@ typedef enum {
 } dlrm_status;
 
 /* DLRM_Q8: row-wise 8-bit tables (only through dlrm_embbag_fwd_q8): a row is D uint8 codes q
- * followed by its fp32 scale and fp32 bias, value = scale * q + bias. */
-typedef enum { DLRM_F32 = 0, DLRM_F16 = 1, DLRM_BF16 = 2, DLRM_Q8 = 3 } dlrm_dtype;
+ * followed by its fp32 scale and fp32 bias, value = scale * q + bias.
+ * DLRM_Q8T: table-wise 8-bit tables (only through dlrm_embbag_fwd_q8t): a row is D uint8 codes,
+ * one (scale, bias) pair per table. */
+typedef enum { DLRM_F32 = 0, DLRM_F16 = 1, DLRM_BF16 = 2, DLRM_Q8 = 3, DLRM_Q8T = 4 } dlrm_dtype;
 
 /* bits OR-ed into the device status word */
 #define DLRM_STATUS_BAD_INDEX 1   /* an index outside [0, rows[t]) */
@@ -136,6 +138,20 @@ int dlrm_embbag_fwd(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* 
 int dlrm_embbag_fwd_q8(int32_t T, int32_t B, int32_t D, const void* const* tables, const int64_t* rows,
                        const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0,
                        float* out_pooled, float* out_inter, int32_t* status, void* stream);
+
+/*
+ * The fused forward on table-wise 8-bit tables: row r of table t is D uint8
+ * codes, value[d] = scale_t * q[d] + bias_t with one (scale, bias) pair per
+ * table, so a lookup reads exactly D bytes (one aligned 128-byte line for
+ * D = 128) and nothing else. Coarser than row-wise codes (the step is the
+ * table's range / 255), but no second read per lookup.
+ *   tables      host array [T] of device pointers (16-byte aligned), table t is uint8 [rows[t]][D]
+ *   scale_bias  host fp32 [T][2]: (scale_t, bias_t)
+ *   D           128, 256 or 512; out_inter required; everything else as in dlrm_embbag_fwd.
+ */
+int dlrm_embbag_fwd_q8t(int32_t T, int32_t B, int32_t D, const void* const* tables, const float* scale_bias,
+                        const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                        const float* e0, float* out_pooled, float* out_inter, int32_t* status, void* stream);
 
 /*
  * Interaction alone, from pooled vectors in HBM.

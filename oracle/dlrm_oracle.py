@@ -67,6 +67,13 @@ class Q8Table:
     def __getitem__(self, r):
         return self.codes[r], self.scale_bias[r]
 
+    @classmethod
+    def table_wise(cls, codes: np.ndarray, scale: float, bias: float) -> "Q8Table":
+        """Table-wise 8-bit table: one (scale, bias) pair for every row, i.e. the
+        row-wise form with that pair repeated."""
+        pair = np.array([scale, bias], dtype=np.float32)
+        return cls(codes, np.tile(pair, (codes.shape[0], 1)))
+
 
 def decode(table, dtype: str) -> np.ndarray:
     """Stored table (or row) -> float64. bf16 tables arrive as uint16 bit patterns;

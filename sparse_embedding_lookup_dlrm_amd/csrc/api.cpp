@@ -21,7 +21,8 @@ int dtype_bytes(int dtype) {
     case DLRM_F32: return 4;
     case DLRM_F16:
     case DLRM_BF16: return 2;
-    case DLRM_Q8: return 1;
+    case DLRM_Q8:
+    case DLRM_Q8T: return 1;
     default: return 0;
   }
 }
@@ -67,7 +68,7 @@ int bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tabl
                const float* d_out, float lr, int opt, float eps, float* const* state, float* d_e0,
                int32_t* unique_keys, int32_t* seg_offsets, int32_t* num_unique, int32_t* perm, void* workspace,
                size_t ws_bytes, int32_t* status, void* stream) {
-  if (dtype == DLRM_Q8) return DLRM_E_UNSUPPORTED;  // the update is defined for fp32 / fp16 / bf16 tables
+  if (dtype == DLRM_Q8 || dtype == DLRM_Q8T) return DLRM_E_UNSUPPORTED;  // defined for fp32 / fp16 / bf16
   int rc = check_batch(T, B, D, dtype, const_cast<const void* const*>(tables), rows, offsets, indices, nnz);
   if (rc != DLRM_OK) return rc;
   if (!e0 || !pooled || !d_out || !workspace) return DLRM_E_INVAL;
@@ -131,7 +132,7 @@ int dlrm_lengths_to_offsets(int64_t n, const int32_t* lengths, int32_t* offsets,
 int dlrm_embbag_fwd(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* const* tables, const int64_t* rows,
                     const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0, float* out_pooled,
                     float* out_inter, int32_t* status, void* stream) {
-  if (dtype == DLRM_Q8) return DLRM_E_UNSUPPORTED;  // 8-bit rows need their scales: dlrm_embbag_fwd_q8
+  if (dtype == DLRM_Q8 || dtype == DLRM_Q8T) return DLRM_E_UNSUPPORTED;  // 8-bit rows: dlrm_embbag_fwd_q8(t)
   int rc = check_batch(T, B, D, dtype, tables, rows, offsets, indices, nnz);
   if (rc != DLRM_OK) return rc;
   if (!out_pooled && !out_inter) return DLRM_E_INVAL;
@@ -151,26 +152,55 @@ int dlrm_embbag_fwd(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* 
   return from_hip(launch_embbag_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
-int dlrm_embbag_fwd_q8(int32_t T, int32_t B, int32_t D, const void* const* tables, const int64_t* rows,
-                       const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0,
-                       float* out_pooled, float* out_inter, int32_t* status, void* stream) {
-  int rc = check_batch(T, B, D, DLRM_Q8, tables, rows, offsets, indices, nnz);
+}  // extern "C"
+
+namespace {
+
+// Shared by the two 8-bit forwards: same checks, same launch; scale_bias is
+// the table-wise (scale, bias) array, or null for row-wise codes.
+int fwd_8bit(int32_t dtype, int32_t T, int32_t B, int32_t D, const void* const* tables, const float* scale_bias,
+             const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0,
+             float* out_pooled, float* out_inter, int32_t* status, void* stream) {
+  int rc = check_batch(T, B, D, dtype, tables, rows, offsets, indices, nnz);
   if (rc != DLRM_OK) return rc;
   if (D != 128 && D != 256 && D != 512) return DLRM_E_UNSUPPORTED;
   if (!out_inter || !e0) return DLRM_E_INVAL;
+  if (dtype == DLRM_Q8T && !scale_bias) return DLRM_E_INVAL;
   if (out_pooled && !aligned(out_pooled, 16)) return DLRM_E_ALIGN;
   if (!aligned(out_inter, 4) || !aligned(e0, 16)) return DLRM_E_ALIGN;
-  if (fwd_lds_bytes(T, D, DLRM_Q8) > kLds) return DLRM_E_UNSUPPORTED;
+  if (fwd_lds_bytes(T, D, dtype) > kLds) return DLRM_E_UNSUPPORTED;
   FwdArgs a;
   memset(&a, 0, sizeof(a));
-  a.T = T; a.B = B; a.D = D; a.dtype = DLRM_Q8;
+  a.T = T; a.B = B; a.D = D; a.dtype = dtype;
   for (int t = 0; t < T; ++t) {
     a.tabs.ptr[t] = tables[t];
     a.tabs.rows[t] = static_cast<int32_t>(rows[t]);
+    if (dtype == DLRM_Q8T) {
+      a.qscale[t] = scale_bias[2 * t];
+      a.qbias[t] = scale_bias[2 * t + 1];
+    }
   }
   a.offsets = offsets; a.indices = indices; a.nnz = nnz;
   a.e0 = e0; a.out_pooled = out_pooled; a.out_inter = out_inter; a.status = status;
   return from_hip(launch_embbag_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int dlrm_embbag_fwd_q8(int32_t T, int32_t B, int32_t D, const void* const* tables, const int64_t* rows,
+                       const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0,
+                       float* out_pooled, float* out_inter, int32_t* status, void* stream) {
+  return fwd_8bit(DLRM_Q8, T, B, D, tables, nullptr, rows, offsets, indices, nnz, e0, out_pooled, out_inter, status,
+                  stream);
+}
+
+int dlrm_embbag_fwd_q8t(int32_t T, int32_t B, int32_t D, const void* const* tables, const float* scale_bias,
+                        const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                        const float* e0, float* out_pooled, float* out_inter, int32_t* status, void* stream) {
+  return fwd_8bit(DLRM_Q8T, T, B, D, tables, scale_bias, rows, offsets, indices, nnz, e0, out_pooled, out_inter,
+                  status, stream);
 }
 
 int dlrm_interact_ex(int32_t T, int32_t B, int32_t D, int32_t self_pairs, const float* e0, const float* pooled,

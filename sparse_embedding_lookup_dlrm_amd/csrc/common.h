@@ -37,6 +37,11 @@ struct Storage<DLRM_Q8> {
   static constexpr int bytes = 1;
   static constexpr int per16 = 16;
 };
+template <>
+struct Storage<DLRM_Q8T> {
+  static constexpr int bytes = 1;
+  static constexpr int per16 = 16;
+};
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

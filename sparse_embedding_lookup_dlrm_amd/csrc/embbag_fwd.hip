@@ -475,7 +475,9 @@ struct RowShape {
   // rows per window (two windows in flight: 32 VGPRs); 8-bit rows also carry a
   // scale and a bias per row and keep more columns per lane, so their windows
   // are smaller
-  static constexpr int WIN = DT == DLRM_Q8 ? (LB >= 8 ? 4 : 8) : (LB >= 4 ? 64 / LB : 16);
+  static constexpr int WIN = DT == DLRM_Q8 ? (LB >= 8 ? 4 : 8)
+                             : DT == DLRM_Q8T ? (LB >= 8 ? 4 : 16)
+                                              : (LB >= 4 ? 64 / LB : 16);
 };
 
 struct RowLayout {
@@ -487,6 +489,7 @@ struct RowLayout {
   int off_carry_t;
   int off_tbase;
   int off_trows;
+  int off_qsb;  // table-wise 8-bit rows: (scale, bias) per table
   int off_stage;
   int off_sbag;
   int off_carry;
@@ -510,6 +513,7 @@ __host__ __device__ inline RowLayout make_row_layout(int T, int D, bool mfma) {
   L.off_carry_t = o; o += align16(kRowWaves * 4);
   L.off_tbase = o; o += align16(T * 8);
   L.off_trows = o; o += align16(T * 4);
+  L.off_qsb = o; o += align16(T * 8);
   const int uni = o;                   // union { stage + bag ids + carries ; output staging }
   L.off_stage = uni;
   L.off_sbag = L.off_stage + kStageCap * 4;
@@ -672,15 +676,16 @@ __device__ __forceinline__ int last_le(const int* pos, int T, int x) {
 // kStageCap rows); only then does this read indices from HBM. Keeping that
 // path out of the common loop keeps the loop free of loads other than the
 // table rows, so the compiler's wait counts stay exact.
-// 8-bit rows (Q8) are D codes followed by the row's fp32 scale and bias: a
-// row is RB + 8 bytes apart from the next, and each lane also loads the
-// (scale, bias) pair of "its" row of the window, from the same DRAM page.
-template <int WIN, int RB, bool BEYOND, bool Q8 = false>
+// 8-bit rows. QM = 1 (row-wise): D codes followed by the row's fp32 scale and
+// bias, rows RB + 8 bytes apart; each lane also loads the (scale, bias) pair of
+// "its" row of the window. QM = 2 (table-wise): D codes per row, the table's
+// (scale, bias) pair read from LDS (qsb).
+template <int WIN, int RB, bool BEYOND, int QM = 0>
 __device__ __forceinline__ void prepare_window(Window& w, const FwdArgs& a, const int* sm_beg, const int* sm_pos,
                                                const int* stage, const uint8_t* sbag, const char* const* tbase,
                                                const int* trows, int T, int q, int p1, uint64_t fallback,
-                                               int tid) {
-  constexpr uint64_t kStride = Q8 ? RB + 8 : RB;
+                                               int tid, const float* qsb = nullptr) {
+  constexpr uint64_t kStride = QM == 1 ? RB + 8 : RB;
   const int lane = tid & (kWave - 1);
   uint64_t addr = fallback;
   int tk = 0;
@@ -706,11 +711,14 @@ __device__ __forceinline__ void prepare_window(Window& w, const FwdArgs& a, cons
     }
     flush = (pos + 1 == sm_pos[tk + 1]) || (pos + 1 == p1);
   }
-  if constexpr (Q8) {
+  if constexpr (QM == 1) {
     // every lane loads the (scale, bias) pair of its row (skipped slots: the fallback row's)
     const auto p = reinterpret_cast<gptr<uint32_t>>(addr + RB);
     w.sc = __uint_as_float(p[0]);
     w.bi = __uint_as_float(p[1]);
+  } else if constexpr (QM == 2) {
+    w.sc = qsb[2 * tk];
+    w.bi = qsb[2 * tk + 1];
   }
   w.alo = static_cast<uint32_t>(addr);
   w.ahi = static_cast<uint32_t>(addr >> 32);
@@ -738,7 +746,7 @@ __device__ __forceinline__ void consume_window(const Window& w, typename LaneChu
     // select, so the load's register is only read, never overwritten early)
     const bool skipped = (w.smask >> j) & 1ull;
     const typename LaneChunk<LB>::type x = skipped ? LaneChunk<LB>::zero() : v[j];
-    if constexpr (DT == DLRM_Q8) {
+    if constexpr (DT == DLRM_Q8 || DT == DLRM_Q8T) {
       // scale * q summed per column; the biases of the bag's rows summed once
       const float sj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w.sc), j));
       const float bj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w.bi), j));
@@ -757,7 +765,7 @@ __device__ __forceinline__ void consume_window(const Window& w, typename LaneChu
       }
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        dst[lane * EL + e] = DT == DLRM_Q8 ? acc[e] + bacc : acc[e];
+        dst[lane * EL + e] = (DT == DLRM_Q8 || DT == DLRM_Q8T) ? acc[e] + bacc : acc[e];
         acc[e] = 0.f;
       }
       bacc = 0.f;
@@ -865,8 +873,8 @@ template <int DT, int LB, bool BEYOND>
 __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, const int* pos, const int* stage,
                                              const uint8_t* sbag, const char* const* tbase, const int* trows, int T,
                                              int p0, int p1, float* Z, int LD, float* carry_w, int* carry_t_w,
-                                             int tid) {
-  constexpr bool Q8 = DT == DLRM_Q8;
+                                             int tid, const float* qsb) {
+  constexpr int QM = DT == DLRM_Q8 ? 1 : (DT == DLRM_Q8T ? 2 : 0);
   using C = LaneChunk<LB>;
   using RS = RowShape<DT, LB>;
   constexpr int EL = RS::EL;
@@ -883,15 +891,17 @@ __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, c
   const uint64_t lane_off = static_cast<uint64_t>(tid & (kWave - 1)) * LB;
   Window wa, wb;
   typename C::type va[WIN], vb[WIN];
-  prepare_window<WIN, RB, BEYOND, Q8>(wa, a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, fallback, tid);
+  prepare_window<WIN, RB, BEYOND, QM>(wa, a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, fallback, tid, qsb);
   issue_window<C, WIN>(wa, va, lane_off);
   for (int q = p0;;) {
-    prepare_window<WIN, RB, BEYOND, Q8>(wb, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid);
+    prepare_window<WIN, RB, BEYOND, QM>(wb, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid,
+                                        qsb);
     issue_window<C, WIN>(wb, vb, lane_off);
     consume_window<DT, LB, WIN>(wa, va, acc, cur, Z, LD, carry_w, carry_t_w, tid, bacc);
     q += WIN;
     if (q >= p1) break;
-    prepare_window<WIN, RB, BEYOND, Q8>(wa, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid);
+    prepare_window<WIN, RB, BEYOND, QM>(wa, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid,
+                                        qsb);
     issue_window<C, WIN>(wa, va, lane_off);
     consume_window<DT, LB, WIN>(wb, vb, acc, cur, Z, LD, carry_w, carry_t_w, tid, bacc);
     q += WIN;
@@ -921,6 +931,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
   int* carry_t = reinterpret_cast<int*>(lds + L.off_carry_t);
   const char** tbase = reinterpret_cast<const char**>(lds + L.off_tbase);
   int* trows = reinterpret_cast<int*>(lds + L.off_trows);
+  float* qsb = reinterpret_cast<float*>(lds + L.off_qsb);
   int* stage = reinterpret_cast<int*>(lds + L.off_stage);
   uint8_t* sbag = reinterpret_cast<uint8_t*>(lds + L.off_sbag);
   float* carry = reinterpret_cast<float*>(lds + L.off_carry);
@@ -944,6 +955,10 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
       publish_bag(a, tid, b_begin, a.offsets[tid * a.B + b_begin], a.offsets[tid * a.B + b_begin + 1], beg, pos);
       tbase[tid] = static_cast<const char*>(a.tabs.ptr[tid]);
       trows[tid] = a.tabs.rows[tid];
+      if constexpr (DT == DLRM_Q8T) {
+        qsb[2 * tid] = a.qscale[tid];
+        qsb[2 * tid + 1] = a.qbias[tid];
+      }
       clear_if_empty(pos, tid, Z, LD, D);
     }
     __syncthreads();
@@ -997,9 +1012,9 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
         float* cw = carry + wave * D;
         int* ctw = carry_t + wave;
         if (p1 <= kStageCap)
-          gather_range<DT, LB, false>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid);
+          gather_range<DT, LB, false>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid, qsb);
         else
-          gather_range<DT, LB, true>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid);
+          gather_range<DT, LB, true>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid, qsb);
       }
     }
     // the prefetched values are first used here (the barrier keeps every use,
@@ -1085,7 +1100,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
 // host side
 // ---------------------------------------------------------------------------
 int fwd_supported_row_bytes(int D, int dtype) {
-  const int s = dtype == DLRM_F32 ? 4 : (dtype == DLRM_Q8 ? 1 : 2);
+  const int s = dtype == DLRM_F32 ? 4 : ((dtype == DLRM_Q8 || dtype == DLRM_Q8T) ? 1 : 2);
   const long rb = static_cast<long>(D) * s;
   if (rb < 16 || rb > 1024 || (rb & (rb - 1)) != 0) return 0;
   return static_cast<int>(rb);
@@ -1184,7 +1199,7 @@ static hipError_t launch_fwd_float(const FwdArgs& a, hipStream_t st) {
 
 template <int DT, int LPR>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  if constexpr (DT == DLRM_Q8) {  // 8-bit rows: row-streaming fused kernel only, rows of 128..512 bytes
+  if constexpr (DT == DLRM_Q8 || DT == DLRM_Q8T) {  // 8-bit rows: row-streaming fused kernel only, 128..512 B
     constexpr int LB = LPR * 16 / kWave;
     if (!a.out_inter) return hipErrorInvalidValue;
     if constexpr (LB == 2 || LB == 4 || LB == 8) return launch_rows<DT, LB>(a, st);
@@ -1214,6 +1229,7 @@ hipError_t launch_embbag_fwd(const FwdArgs& a, hipStream_t st) {
     case DLRM_F16: return launch_fwd_dt<DLRM_F16>(a, st);
     case DLRM_BF16: return launch_fwd_dt<DLRM_BF16>(a, st);
     case DLRM_Q8: return launch_fwd_dt<DLRM_Q8>(a, st);
+    case DLRM_Q8T: return launch_fwd_dt<DLRM_Q8T>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

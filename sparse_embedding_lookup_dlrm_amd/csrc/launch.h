@@ -33,6 +33,7 @@ enum Optimizer { kSgd = 0, kRowwiseAdagrad = 1 };
 struct FwdArgs {
   int T, B, D, dtype;
   TableArgs tabs;
+  float qscale[DLRM_MAX_TABLES], qbias[DLRM_MAX_TABLES];  // DLRM_Q8T: per-table scale and bias
   const int32_t* offsets;
   const int32_t* indices;
   int64_t nnz;

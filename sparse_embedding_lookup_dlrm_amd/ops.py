@@ -36,6 +36,9 @@ _SIGNATURES = {
                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "dlrm_embbag_fwd_q8": (ctypes.c_int, [_i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p, _c_void_p, _i64,
                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "dlrm_embbag_fwd_q8t": (ctypes.c_int, [_i32, _i32, _i32, _P(_c_void_p), _P(_f32), _P(_i64), _c_void_p,
+                                           _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                           _c_void_p]),
     "dlrm_interact": (ctypes.c_int, [_i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "dlrm_interact_ex": (ctypes.c_int, [_i32, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "dlrm_interact_bwd": (ctypes.c_int, [_i32, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -193,6 +196,37 @@ def embbag_fwd_q8(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices
     _check(lib().dlrm_embbag_fwd_q8(T, B, D, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(), _ptr(e0),
                                     _ptr(out_pooled), _ptr(out_inter), _ptr(status), _stream(stream)),
            "dlrm_embbag_fwd_q8")
+    return out_pooled, out_inter
+
+
+def embbag_fwd_q8t(tables: Sequence[torch.Tensor], scale_bias, offsets: torch.Tensor, indices: torch.Tensor,
+                   B: int, e0: torch.Tensor, *, want_pooled: bool = False,
+                   out_pooled: Optional[torch.Tensor] = None, out_inter: Optional[torch.Tensor] = None,
+                   status: Optional[torch.Tensor] = None, stream=None) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
+    """Fused forward on table-wise 8-bit tables: uint8 [rows, D] codes per table and one
+    (scale, bias) pair per table (host sequence of T pairs); returns (pooled or None, [e0 | dots])."""
+    T = len(tables)
+    if T < 1:
+        raise ValueError("need at least one table")
+    D = tables[0].shape[1]
+    for t in tables:
+        if t.dtype != torch.uint8 or t.dim() != 2 or t.shape[1] != D or not t.is_contiguous():
+            raise ValueError("8-bit tables must be contiguous uint8 [rows, D] with the same D")
+    sb = [float(v) for pair in scale_bias for v in pair]
+    if len(sb) != 2 * T:
+        raise ValueError("need one (scale, bias) pair per table")
+    _require_cuda(*tables, offsets, indices, e0, out_pooled, out_inter, status)
+    ptrs = (_c_void_p * T)(*[t.data_ptr() for t in tables])
+    rows = (_i64 * T)(*[t.shape[0] for t in tables])
+    dev = tables[0].device
+    if want_pooled and out_pooled is None:
+        out_pooled = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    if out_inter is None:
+        out_inter = torch.empty((B, D + pair_count(T)), dtype=torch.float32, device=dev)
+    _check(lib().dlrm_embbag_fwd_q8t(T, B, D, ptrs, (_f32 * (2 * T))(*sb), rows, _ptr(offsets), _ptr(indices),
+                                     indices.numel(), _ptr(e0), _ptr(out_pooled), _ptr(out_inter), _ptr(status),
+                                     _stream(stream)),
+           "dlrm_embbag_fwd_q8t")
     return out_pooled, out_inter
 
 

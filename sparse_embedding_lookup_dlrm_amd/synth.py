@@ -190,6 +190,38 @@ def gen_tables_q8_host(w: Workload, rows: Optional[Sequence[int]] = None):
     return out
 
 
+def quantize_table_q8(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Table-wise 8-bit codes of an fp32 table: one scale = (max - min) / 255 (1 for a
+    constant table) and bias = min for the whole table, codes = round((x - min) / scale)
+    clipped to [0, 255]. Returns (uint8 codes [rows, D], fp32 (scale, bias) [2])."""
+    x = np.asarray(x, dtype=np.float32)
+    lo, hi = x.min(), x.max()
+    scale = np.float32((hi - lo) / np.float32(255))
+    if scale == 0:
+        scale = np.float32(1)
+    codes = np.clip(np.rint((x - lo) / scale), 0, 255).astype(np.uint8)
+    return codes, np.array([scale, lo], dtype=np.float32)
+
+
+def gen_tables_q8t_host(w: Workload, rows: Optional[Sequence[int]] = None):
+    """Table-wise 8-bit tables: the fp32 N(0, sigma) tables (or, for values="int", codes
+    0..4 with scale in {0.5, 1, 2} and bias in {-1, 0, 1}, every sum exact) quantized per
+    table. Returns (list of codes, fp32 scale_bias [T, 2])."""
+    rows = table_rows(w) if rows is None else rows
+    rng = _streams(w.seed)["values"]
+    codes, sb = [], []
+    for n in rows:
+        if w.values == "int":
+            codes.append(rng.integers(0, 5, size=(n, w.D)).astype(np.uint8))
+            sb.append([rng.choice([0.5, 1.0, 2.0]), rng.choice([-1.0, 0.0, 1.0])])
+        else:
+            v = rng.standard_normal(size=(n, w.D), dtype=np.float32) * np.float32(w.sigma)
+            c, p = quantize_table_q8(v)
+            codes.append(c)
+            sb.append(p)
+    return codes, np.asarray(sb, dtype=np.float32).reshape(len(rows), 2)
+
+
 def gen_tables_device(w: Workload, device, rows: Optional[Sequence[int]] = None):
     """Device tables filled by torch's device RNG (for shards too large for host RAM).
 

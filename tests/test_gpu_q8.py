@@ -115,3 +115,78 @@ def test_q8_rejections():
     # the generic entry point does not take 8-bit tables
     assert L.dlrm_embbag_fwd(1, 1, 64, 3, ptrs, rows, P(off.data_ptr()), None, 0, P(e0.data_ptr()), None,
                              P(out.data_ptr()), None, None) == -2
+
+
+# ---------------------------------------------------------------------------
+# Table-wise 8-bit tables: uint8 [rows, D] codes, one (scale, bias) pair per table
+# ---------------------------------------------------------------------------
+def _run_t(w):
+    rows = synth.table_rows(w)
+    codes, sb = synth.gen_tables_q8t_host(w, rows)
+    lengths = synth.gen_lengths(w)
+    indices = synth.gen_indices(w, rows, lengths)
+    e0 = synth.gen_e0(w)
+    dev = "cuda"
+    tabs = [torch.from_numpy(c).to(dev) for c in codes]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    offsets = ops.lengths_to_offsets(torch.from_numpy(lengths).to(dev), status=status)
+    idx = torch.from_numpy(indices).to(dev)
+    d_e0 = torch.from_numpy(e0).to(dev)
+    pooled, out = ops.embbag_fwd_q8t(tabs, sb.tolist(), offsets, idx, w.B, d_e0, want_pooled=True, status=status)
+    _, out2 = ops.embbag_fwd_q8t(tabs, sb.tolist(), offsets, idx, w.B, d_e0)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    q8 = [(c, np.tile(p, (c.shape[0], 1))) for c, p in zip(codes, sb)]  # the row-wise form of each table
+    return q8, lengths, indices, e0, pooled.cpu().numpy(), out.cpu().numpy(), int(status.item())
+
+
+@pytest.mark.parametrize("T,rows,D,B,seed", [(8, 5000, 128, 256, 71), (26, 3000, 256, 200, 72),
+                                             (64, 2000, 128, 96, 73), (4, 500, 512, 64, 74),
+                                             (30, 800, 512, 40, 75)])
+def test_q8t_forward(T, rows, D, B, seed):
+    w = synth.Workload("q8t", T=T, rows=rows, D=D, dtype="bf16", B=B, bag=("uniform", 0, 20), dist=("zipf", 1.05),
+                       seed=seed)
+    q8, lengths, indices, e0, pooled, out, st = _run_t(w)
+    assert st == 0
+    r, pm, mag = _oracle(w, q8, lengths, indices, e0)
+    np.testing.assert_array_equal(out[:, :D], e0)
+    assert_mag_close(pooled, r["pooled"], pm, RTOL_Q8, "q8t pooled")
+    assert_mag_close(out[:, D:], r["out"][:, D:], mag[:, D:], RTOL_Q8, "q8t dots")
+
+
+@pytest.mark.parametrize("T,D", [(6, 128), (40, 256)])
+def test_q8t_forward_exact_dyadic_values(T, D):
+    w = synth.Workload("q8tint", T=T, rows=300, D=D, dtype="bf16", B=70, bag=("uniform", 0, 12),
+                       dist=("uniform",), seed=T + 1, values="int")
+    q8, lengths, indices, e0, pooled, out, st = _run_t(w)
+    assert st == 0
+    r, _, _ = _oracle(w, q8, lengths, indices, e0)
+    np.testing.assert_array_equal(pooled, r["pooled"].astype(np.float32))
+    np.testing.assert_array_equal(out, r["out"].astype(np.float32))
+
+
+def test_q8t_rejections():
+    L = ops.lib()
+    tab = torch.zeros((10, 128), dtype=torch.uint8, device="cuda")
+    off = torch.zeros(2, dtype=torch.int32, device="cuda")
+    e0 = torch.zeros((1, 128), device="cuda")
+    out = torch.zeros((1, 128 + 1), device="cuda")
+    P = ctypes.c_void_p
+    ptrs = (P * 1)(tab.data_ptr())
+    rows = (ctypes.c_int64 * 1)(10)
+    sb = (ctypes.c_float * 2)(1.0, 0.0)
+    # the (scale, bias) array is required
+    assert L.dlrm_embbag_fwd_q8t(1, 1, 128, ptrs, None, rows, P(off.data_ptr()), None, 0, P(e0.data_ptr()), None,
+                                 P(out.data_ptr()), None, None) == -1
+    # D = 64 is not a supported 8-bit row width
+    assert L.dlrm_embbag_fwd_q8t(1, 1, 64, ptrs, sb, rows, P(off.data_ptr()), None, 0, P(e0.data_ptr()), None,
+                                 P(out.data_ptr()), None, None) == -2
+    # the generic entry point does not take 8-bit tables
+    assert L.dlrm_embbag_fwd(1, 1, 128, 4, ptrs, rows, P(off.data_ptr()), None, 0, P(e0.data_ptr()), None,
+                             P(out.data_ptr()), None, None) == -2
+    # an empty batch (every bag empty) pools to the bias-free zero
+    pooled = torch.full((1, 1, 128), 7.0, device="cuda")
+    assert L.dlrm_embbag_fwd_q8t(1, 1, 128, ptrs, sb, rows, P(off.data_ptr()), None, 0, P(e0.data_ptr()),
+                                 P(pooled.data_ptr()), P(out.data_ptr()), None, None) == 0
+    torch.cuda.synchronize()
+    assert not pooled.any()

@@ -545,3 +545,20 @@ def test_q8_decode_hand_example_and_pool_equals_dequantized_f64():
     got = orc.embbag_pool([orc.Q8Table(codes, sb)], "q8", 4, off, idx)
     want = orc.embbag_pool([deq], "f64", 4, off, idx)
     np.testing.assert_array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# Table-wise 8-bit tables
+# ---------------------------------------------------------------------------
+def test_q8_table_wise_hand_example():
+    """One (scale, bias) pair for the table: rows decode with that pair, and a bag of n
+    rows pools to scale * (sum of its codes) + n * bias (worked by hand)."""
+    codes = np.array([[0, 255, 128], [7, 0, 1], [2, 2, 2]], dtype=np.uint8)
+    tab = orc.Q8Table.table_wise(codes, 0.5, -1.0)
+    assert orc.decode(tab[1], "q8").tolist() == [2.5, -1.0, -0.5]
+    off = np.array([0, 2, 5])
+    idx = np.array([0, 1, 1, 2, 2], dtype=np.int32)
+    got = orc.embbag_pool([tab], "q8", 2, off, idx)
+    assert got[0, 0].tolist() == [0.5 * 7 - 2, 0.5 * 255 - 2, 0.5 * 129 - 2]
+    assert got[1, 0].tolist() == [0.5 * 11 - 3, 0.5 * 4 - 3, 0.5 * 5 - 3]
+

@@ -65,3 +65,16 @@ def test_host_table_dtypes(dtype):
     tabs = synth.gen_tables_host(w)
     want = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
     assert all(t.dtype == want and t.shape == (10, 8) for t in tabs)
+
+
+def test_quantize_table_q8_round_trip_within_half_step():
+    """Table-wise codes reproduce every value within half a step (scale / 2), use the
+    full code range, and give a constant table scale 1 and exact values."""
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((200, 16)) * 0.05).astype(np.float32)
+    codes, sb = synth.quantize_table_q8(x)
+    back = codes.astype(np.float64) * float(sb[0]) + float(sb[1])
+    assert np.max(np.abs(back - x.astype(np.float64))) <= 0.5 * float(sb[0]) * (1 + 1e-5)
+    assert codes.min() == 0 and codes.max() == 255
+    c1, sb1 = synth.quantize_table_q8(np.full((3, 4), 0.75, np.float32))
+    assert sb1.tolist() == [1.0, 0.75] and not c1.any()
