@@ -362,6 +362,45 @@ def bench_forward_q8t(inp, steps, warmup):
             "frac_of_8TBps": alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, "status": int(inp["status"].item())}
 
 
+def bench_forward_configs(steps, warmup):
+    """The fused forward ([e0 | dots] only) on the three smaller workloads: 4 fp32 tables
+    of 1000 rows (D=16, B=128, one index per bag), 26 fp32 tables of log-uniform rows
+    (D=128, B=2048, one Zipf(1.05) index per bag) and 8 fp16 tables of 4M rows (D=64,
+    B=4096, min(Poisson(20), 100) Zipf(1.1) indices per bag). Tables filled on the device.
+    Short launches: many steps, and the times include launch gaps where the host is
+    slower than the kernel."""
+    import torch
+
+    from sparse_embedding_lookup_dlrm_amd import ops, synth
+
+    dev = torch.device("cuda:0")
+    out = {}
+    for name in ("tiny-4t1k-d16-b128", "zipf-26t-d128-b2048", "multihot-8t4m-d64-fp16-b4096"):
+        w = synth.WORKLOADS[name]
+        rows = synth.table_rows(w)
+        tables = synth.gen_tables_device(w, dev, rows)
+        lengths = synth.gen_lengths(w)
+        indices = synth.gen_indices(w, rows, lengths)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        offsets = ops.lengths_to_offsets(torch.from_numpy(lengths).to(dev), status=status)
+        idx = torch.from_numpy(indices).to(dev)
+        e0 = torch.from_numpy(synth.gen_e0(w)).to(dev)
+        res_out = torch.empty((w.B, w.out_width), dtype=torch.float32, device=dev)
+        plan = ops.FwdPlan(tables, offsets, idx, w.B, e0, out_inter=res_out, status=status)
+        ms, _ = time_steps(plan.run, 10 * steps, warmup)
+        nnz = len(indices)
+        s = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+        alg = fwd_algorithmic_bytes(w.T, w.B, w.D, s, nnz)
+        gbs = alg / (ms / 1e3) / 1e9
+        out[name] = {"us_per_step": ms * 1e3, "lookups_per_s": nnz / (ms / 1e3), "bags_per_s": w.T * w.B / (ms / 1e3),
+                     "nnz": nnz, "algorithmic_bytes": alg, "hbm_GBps_algorithmic": gbs,
+                     "frac_of_8TBps": gbs / PEAK_HBM_GBS, "status": int(status.item())}
+        log(f"fused forward {name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}%)")
+        del tables, plan
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_backward_multihot(steps, warmup):
     """The backward + SGD on the multi-hot fp16 shapes (8 tables x 4M rows, D=64, batch
     4096, bags min(Poisson(20), 100), Zipf(1.1)), tables filled on the device."""
@@ -408,6 +447,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-q8", action="store_true", help="skip the 8-bit-row forward timing")
+    ap.add_argument("--no-configs", action="store_true", help="skip the forward timing on the smaller workloads")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain copy of this size (for counter calibration)")
     ap.add_argument("--summarize-profile", default=None)
@@ -512,6 +552,8 @@ def main():
         log(f"backward row-wise AdaGrad: {res['backward_adagrad']['ms_per_step'] * 1e3:.1f} us/step")
         res["backward_multihot"] = bench_backward_multihot(max(args.steps, 20), min(args.warmup, 10))
         log(f"backward multi-hot: {res['backward_multihot']['ms_per_step'] * 1e3:.1f} us/step")
+    if not args.no_configs:
+        res["forward_configs"] = bench_forward_configs(args.steps, args.warmup)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -158,50 +158,57 @@ __device__ __forceinline__ void block_pair(int w, int& bi, int& bj) {
   bj = w - i * (i + 1) / 2;
 }
 
-// Z: [Fpad][LD] fp32 in LDS (rows >= F may hold anything); dots of block (bi, bj)
-// for i in 4bi..4bi+3, j in 4bj..4bj+3 with j < i < F go to out[i(i-1)/2 + j];
-// with self-pairs, j <= i < F go to out[i(i+1)/2 + j].
+// Z: [Fpad][LD] fp32 in LDS (rows >= F may hold anything). The 16 lanes of a
+// group (l = 0..15) compute the dots of block (bi, bj): rows i = 4bi..4bi+3
+// against rows j = 4bj..4bj+3. Lane l sums the float4 column chunks l, l+16,
+// l+32, ... of the block's eight rows; a 4-step exchange (lane distances 8, 4,
+// 2, 1, each step halving the values a lane keeps) then leaves lane l with the
+// complete dot of pair (4bi + l/4, 4bj + l%4). Pairs j < i < F go to
+// out[i(i-1)/2 + j]; with self-pairs, j <= i < F go to out[i(i+1)/2 + j]. Dots
+// of rows >= F stay in their own lanes and are dropped. The 16 lanes must run
+// this together (every exchange reads an active lane).
 template <bool TO_LDS>
-__device__ __forceinline__ void dots_block(const float* Z, int F, int D, int LD, int bi, int bj,
-                                           float* __restrict__ out, bool self_pairs = false) {
-  float acc[4][4];
+__device__ __forceinline__ void dots_block16(const float* Z, int F, int D, int LD, int bi, int bj, int l,
+                                             float* __restrict__ out, bool self_pairs = false) {
+  float acc[16];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[r][q] = 0.f;
-  const float* zi = Z + (4 * bi) * LD;
-  const float* zj = Z + (4 * bj) * LD;
-  for (int d = 0; d < D; d += 4) {
+  for (int m = 0; m < 16; ++m) acc[m] = 0.f;
+  const float* zi = Z + 4 * bi * LD;
+  const float* zj = Z + 4 * bj * LD;
+  for (int d = 4 * l; d < D; d += 64) {
     float4 x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = *reinterpret_cast<const float4*>(zi + r * LD + d);
-    // one column operand at a time keeps the live set at 16 + 4 + 16 registers
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 y = *reinterpret_cast<const float4*>(zj + q * LD + d);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float s = acc[r][q];
-        s = fmaf(x[r].x, y.x, s);
-        s = fmaf(x[r].y, y.y, s);
-        s = fmaf(x[r].z, y.z, s);
-        s = fmaf(x[r].w, y.w, s);
-        acc[r][q] = s;
+        float t = acc[4 * r + q];
+        t = fmaf(x[r].x, y.x, t);
+        t = fmaf(x[r].y, y.y, t);
+        t = fmaf(x[r].z, y.z, t);
+        t = fmaf(x[r].w, y.w, t);
+        acc[4 * r + q] = t;
       }
     }
   }
+  // keep the half of the values whose index has bit k equal to the lane's bit
+  // k, and add the partner's copy of that half
+  float v8[8], v4[4], v2[2];
+  const bool h3 = l & 8, h2 = l & 4, h1 = l & 2, h0 = l & 1;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 4 * bi + r;
+  for (int m = 0; m < 8; ++m) v8[m] = (h3 ? acc[m + 8] : acc[m]) + __shfl_xor(h3 ? acc[m] : acc[m + 8], 8, kWave);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = 4 * bj + q;
-      if (i < F && (j < i || (self_pairs && j == i))) {
-        const int k = self_pairs ? i * (i + 1) / 2 + j : i * (i - 1) / 2 + j;
-        if constexpr (TO_LDS) out[k] = acc[r][q];
-        else store_stream(out + k, acc[r][q]);
-      }
-    }
+  for (int m = 0; m < 4; ++m) v4[m] = (h2 ? v8[m + 4] : v8[m]) + __shfl_xor(h2 ? v8[m] : v8[m + 4], 4, kWave);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) v2[m] = (h1 ? v4[m + 2] : v4[m]) + __shfl_xor(h1 ? v4[m] : v4[m + 2], 2, kWave);
+  const float dot = (h0 ? v2[1] : v2[0]) + __shfl_xor(h0 ? v2[0] : v2[1], 1, kWave);
+  const int i = 4 * bi + (l >> 2), j = 4 * bj + (l & 3);
+  if (i < F && (j < i || (self_pairs && j == i))) {
+    const int k = self_pairs ? i * (i + 1) / 2 + j : i * (i - 1) / 2 + j;
+    if constexpr (TO_LDS) out[k] = dot;
+    else store_stream(out + k, dot);
   }
 }
 
@@ -229,14 +236,15 @@ __device__ __forceinline__ void interact_from_lds(const float* Zall, const Tile&
                                                   float* __restrict__ out_inter, bool self_pairs = false) {
   const int W = D + (self_pairs ? tl.F * (tl.F + 1) / 2 : tl.F * (tl.F - 1) / 2);
   const int items = tl.S * tl.nblk;
-  for (int w = threadIdx.x; w < items; w += kThreads) {
+  const int l = threadIdx.x & 15;
+  for (int w = threadIdx.x >> 4; w < items; w += kThreads / 16) {  // one 4x4 block per 16 lanes
     const int s = w / tl.nblk, blk = w - s * tl.nblk;
     const int b = b0 + s;
     if (b >= B) continue;
     int bi, bj;
     block_pair(blk, bi, bj);
-    dots_block<false>(Zall + static_cast<size_t>(s) * tl.Fpad * tl.LD, tl.F, D, tl.LD, bi, bj,
-                      out_inter + static_cast<size_t>(b) * W + D, self_pairs);
+    dots_block16<false>(Zall + static_cast<size_t>(s) * tl.Fpad * tl.LD, tl.F, D, tl.LD, bi, bj, l,
+                        out_inter + static_cast<size_t>(b) * W + D, self_pairs);
   }
 }
 
@@ -951,6 +959,8 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
   {
     int* beg = reinterpret_cast<int*>(lds + L.off_beg);
     int* pos = reinterpret_cast<int*>(lds + L.off_pos);
+    // e0 goes out with the offsets (D <= kRowThreads), not after them
+    const float e0v = tid < D ? a.e0[static_cast<size_t>(b_begin) * D + tid] : 0.f;
     if (tid < T) {
       publish_bag(a, tid, b_begin, a.offsets[tid * a.B + b_begin], a.offsets[tid * a.B + b_begin + 1], beg, pos);
       tbase[tid] = static_cast<const char*>(a.tabs.ptr[tid]);
@@ -962,7 +972,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
       clear_if_empty(pos, tid, Z, LD, D);
     }
     __syncthreads();
-    for (int d = tid; d < D; d += kRowThreads) Z[d] = a.e0[static_cast<size_t>(b_begin) * D + d];
+    if (tid < D) Z[tid] = e0v;
     if (wave == 0) scan_positions(pos, T, tid);
     __syncthreads();
     int r[kStagePerThread], tb[kStagePerThread];
@@ -1064,12 +1074,12 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
         block_pair(tile, I, J);
         gram_tile_mfma(Z, LD, D, T, I, J, outs, tid);
       }
-    } else {
-      const Tile tl = make_tile(T, D, 1);
-      for (int w = tid; w < tl.nblk; w += kRowThreads) {
+    } else {  // fp32 dots, one 4x4 block of pairs per 16 lanes
+      const int nb = (T + 1 + 3) >> 2;
+      for (int u = tid >> 4; u < nb * (nb + 1) / 2; u += kRowThreads / 16) {
         int bi, bj;
-        block_pair(w, bi, bj);
-        dots_block<true>(Z, tl.F, D, LD, bi, bj, outs + D);
+        block_pair(u, bi, bj);
+        dots_block16<true>(Z, T + 1, D, LD, bi, bj, tid & 15, outs + D);
       }
     }
     __syncthreads();
