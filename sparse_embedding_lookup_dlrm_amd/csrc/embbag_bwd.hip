@@ -545,15 +545,38 @@ __global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, St
   const int sid = head_pos[q1] - 1;  // segment of the chunk's last position
   RowVec<EL> acc;
   acc.load(head + static_cast<size_t>(k) * D + col);
-  // chunk j's first part is this segment's; it goes on past chunk j only if
-  // chunk j holds nothing else and its last segment continues
-  for (long long j = k + 1; j < nchunks; ++j) {
-    RowVec<EL> x;
-    x.load(carry + static_cast<size_t>(j) * D + col);
+  // Chunk j's first part is this segment's; the segment goes on past chunk j
+  // only if chunk j holds nothing else and its last segment continues. The
+  // last chunk it reaches is found 64 flags at a time (one per lane), so a
+  // segment spanning hundreds of chunks costs a few dependent loads, not one
+  // per chunk.
+  long long last = nchunks - 1;
+  for (long long j = k + 1; j < nchunks; j += kWave) {
+    const long long jj = j + lane;
+    const int fj = jj < nchunks ? chunk_flags[jj] : 0;
+    const unsigned long long ends = __ballot(!((fj & kChunkSingle) && (fj & kChunkLastCont)));
+    if (ends) {
+      const long long e = j + __ffsll(static_cast<long long>(ends)) - 1;
+      last = e < last ? e : last;
+      break;
+    }
+  }
+  // the carries of chunks k+1..last, added in chunk order; G loads in flight
+  constexpr int G = EL >= 8 ? 4 : (EL >= 4 ? 8 : 16);
+  for (long long j = k + 1; j <= last; j += G) {
+    RowVec<EL> x[G];
 #pragma unroll
-    for (int e = 0; e < EL; ++e) acc.v[e] += x.v[e];
-    const int fj = chunk_flags[j];
-    if (!((fj & kChunkSingle) && (fj & kChunkLastCont))) break;
+    for (int g = 0; g < G; ++g) {
+      const long long jj = j + g <= last ? j + g : last;
+      x[g].load(carry + static_cast<size_t>(jj) * D + col);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (j + g <= last) {
+#pragma unroll
+        for (int e = 0; e < EL; ++e) acc.v[e] += x[g].v[e];
+      }
+    }
   }
   row_update<DT, EL, OPT>(tabs, state, eps, T, D, unique_keys[sid], col, acc, lr);
 }
