@@ -50,20 +50,53 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
   float* S = smem + F * LD;       // [F][F]
   const int b = xcd_block(blockIdx.x, gridDim.x);
   const int D4 = D / 4;
-  for (int i = threadIdx.x; i < F * D4; i += kBwdThreads) {
-    const int f = i / D4, d = (i - f * D4) * 4;
-    const float4 v = f == 0 ? *reinterpret_cast<const float4*>(e0 + static_cast<size_t>(b) * D + d)
-                            : *reinterpret_cast<const float4*>(pooled + (static_cast<size_t>(b) * T + f - 1) * D + d);
-    *reinterpret_cast<float4*>(Z + f * LD + d) = v;
+  // Z and S are filled in batches whose loads are all issued before the first
+  // LDS store, so a batch costs one memory round trip, not one per element
+  constexpr int kBatch = 4;
+  for (int i0 = threadIdx.x; i0 < F * D4; i0 += kBatch * kBwdThreads) {
+    float4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kBwdThreads;
+      const int ic = i < F * D4 ? i : i0;  // past the end: reload the first element (in bounds)
+      const int f = ic / D4, d = (ic - f * D4) * 4;
+      v[u] = f == 0 ? *reinterpret_cast<const float4*>(e0 + static_cast<size_t>(b) * D + d)
+                    : *reinterpret_cast<const float4*>(pooled + (static_cast<size_t>(b) * T + f - 1) * D + d);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kBwdThreads;
+      if (i < F * D4) {
+        const int f = i / D4, d = (i - f * D4) * 4;
+        *reinterpret_cast<float4*>(Z + f * LD + d) = v[u];
+      }
+    }
   }
   const float* g = d_out + static_cast<size_t>(b) * W + D;
-  for (int i = threadIdx.x; i < F * F; i += kBwdThreads) {
-    const int r = i / F, c = i - r * F;
-    const int hi = r > c ? r : c, lo = r > c ? c : r;
-    float v = 0.f;
-    if (self_pairs) v = hi == lo ? 2.f * g[hi * (hi + 1) / 2 + lo] : g[hi * (hi + 1) / 2 + lo];
-    else if (hi != lo) v = g[hi * (hi - 1) / 2 + lo];
-    S[i] = v;
+  for (int i0 = threadIdx.x; i0 < F * F; i0 += kBatch * kBwdThreads) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kBwdThreads;
+      const int r = i / F, c = i - r * F;
+      const int hi = r > c ? r : c, lo = r > c ? c : r;
+      const bool use = i < F * F && (self_pairs || hi != lo);
+      const int k = self_pairs ? hi * (hi + 1) / 2 + lo : hi * (hi - 1) / 2 + lo;
+      v[u] = g[use ? k : 0];
+      if (!use) v[u] = 0.f;
+      else if (self_pairs && hi == lo) v[u] *= 2.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kBwdThreads;
+      if (i < F * F) S[i] = v[u];
+    }
+  }
+  // the upstream gradient of e0 (row 0 is item threadIdx.x < D/4 of the loop below)
+  float4 go = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (d_e0 && threadIdx.x < D4) {
+    const float* p = d_out + static_cast<size_t>(b) * W + 4 * threadIdx.x;
+    go = make_float4(p[0], p[1], p[2], p[3]);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < F * D4; i += kBwdThreads) {
@@ -80,8 +113,6 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
     }
     if (f == 0) {
       if (d_e0) {
-        const float4 go = make_float4(d_out[static_cast<size_t>(b) * W + d], d_out[static_cast<size_t>(b) * W + d + 1],
-                                      d_out[static_cast<size_t>(b) * W + d + 2], d_out[static_cast<size_t>(b) * W + d + 3]);
         *reinterpret_cast<float4*>(d_e0 + static_cast<size_t>(b) * D + d) =
             make_float4(go.x + acc.x, go.y + acc.y, go.z + acc.z, go.w + acc.w);
       }
@@ -156,21 +187,61 @@ __global__ __launch_bounds__(kBwdThreads) void radix_count(const int32_t* __rest
   counts[static_cast<long long>(threadIdx.x) * ntiles + blockIdx.x] = hist[threadIdx.x];
 }
 
+// Up to this many tiles, each scatter workgroup works out its own digit
+// offsets from the count table instead of a device-wide scan.
+constexpr int kInlineScanTiles = 128;
+
+// Where this tile's keys of digit d (= threadIdx.x) start in the output: all
+// keys of smaller digits, plus the keys of digit d in earlier tiles. The count
+// table is digit-major ([digit][tile]); the digit totals are scanned across
+// the workgroup.
+__device__ __forceinline__ int inline_digit_base(const int32_t* __restrict__ counts, int ntiles, int* lds4) {
+  const int d = threadIdx.x, lane = d & (kWave - 1), wave = d >> 6;
+  const int32_t* row = counts + static_cast<long long>(d) * ntiles;
+  int tot = 0, pre = 0;
+  for (int t0 = 0; t0 < ntiles; t0 += 8) {
+    int c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = t0 + u < ntiles ? row[t0 + u] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      tot += c[u];
+      if (t0 + u < static_cast<int>(blockIdx.x)) pre += c[u];
+    }
+  }
+  int x = tot;  // inclusive scan of the totals over the wave, then across the 4 waves
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) lds4[wave] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += lds4[w];
+  return before + x - tot + pre;
+}
+
 // Stable scatter of one tile. Wave w owns keys [tile + w*512, +512) and walks
 // them in rounds of 64 in their original order; equal digits inside a round
 // are ranked by lane with ballots, and a per-wave running count per digit
-// carries the rank across rounds.
+// carries the rank across rounds. The tile's digit offsets come from
+// digit_off (the scanned count table) or, with digit_off null, from the count
+// table itself (at most kInlineScanTiles tiles).
 __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __restrict__ keys_in,
                                                              const int32_t* __restrict__ vals_in, long long n,
                                                              int shift, int ntiles,
                                                              const int32_t* __restrict__ digit_off,
+                                                             const int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ keys_out,
                                                              int32_t* __restrict__ vals_out) {
   __shared__ int wcount[kRadixWaves][kRadixBins];
   __shared__ int gbase[kRadixBins];
+  __shared__ int lds4[kRadixWaves];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   for (int w = 0; w < kRadixWaves; ++w) wcount[w][threadIdx.x] = 0;
-  gbase[threadIdx.x] = digit_off[static_cast<long long>(threadIdx.x) * ntiles + blockIdx.x];
+  if (digit_off) gbase[threadIdx.x] = digit_off[static_cast<long long>(threadIdx.x) * ntiles + blockIdx.x];
+  else gbase[threadIdx.x] = inline_digit_base(counts, ntiles, lds4);
   __syncthreads();
   const long long sub = static_cast<long long>(blockIdx.x) * kRadixTile + static_cast<long long>(wave) * kRadixRounds * kWave;
   const unsigned long long lt = (1ull << lane) - 1ull;
@@ -257,6 +328,63 @@ __global__ __launch_bounds__(kBwdThreads) void build_segments(const int32_t* __r
   }
 }
 
+// The same for up to 256 scan chunks, in one pass after the chunk totals:
+// each workgroup adds up the totals of the chunks before its own, scans its
+// chunk's head flags, and writes pos (pos[i] = heads before position i, pos[n]
+// = all heads), the segment starts and keys, and the segment count.
+__global__ __launch_bounds__(kScanThreads) void build_segments_chunked(const int32_t* __restrict__ keys, long long n,
+                                                                      int32_t sentinel,
+                                                                      const long long* __restrict__ partial,
+                                                                      int32_t* __restrict__ pos,
+                                                                      int32_t* __restrict__ unique_keys,
+                                                                      int32_t* __restrict__ seg_offsets,
+                                                                      int32_t* __restrict__ num_unique) {
+  __shared__ long long lds[kScanThreads / kWave];
+  const long long c0 = static_cast<long long>(blockIdx.x) * kScanChunk + threadIdx.x * kScanPerThread;
+  // totals of the earlier chunks (at most 256, one per thread)
+  const long long pv = threadIdx.x < blockIdx.x ? partial[threadIdx.x] : 0;
+  int32_t k[kScanPerThread + 2];  // k[j] = key c0 - 1 + j, for c0 - 1 .. c0 + 16 (outside [0, n): the sentinel)
+#pragma unroll
+  for (int j = 0; j < kScanPerThread + 2; ++j) {
+    const long long i = c0 - 1 + j;
+    k[j] = (i >= 0 && i < n) ? keys[i] : sentinel;
+  }
+  long long tot_before;
+  block_exclusive_scan(pv, &tot_before, lds);
+  int h[kScanPerThread];
+  long long s = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPerThread; ++j) {
+    const int32_t kk = k[j + 1];
+    h[j] = (c0 + j < n && kk != sentinel && (c0 + j == 0 || k[j] != kk)) ? 1 : 0;
+    s += h[j];
+  }
+  long long chunk_tot;
+  long long ex = block_exclusive_scan(s, &chunk_tot, lds) + tot_before;
+#pragma unroll
+  for (int j = 0; j < kScanPerThread; ++j) {
+    const long long i = c0 + j;
+    if (i < n) {
+      pos[i] = static_cast<int32_t>(ex);
+      if (h[j]) {
+        unique_keys[ex] = k[j + 1];
+        seg_offsets[ex] = static_cast<int32_t>(i);
+      }
+      // the last valid key closes the segment list
+      const bool valid = k[j + 1] != sentinel;
+      const bool last_valid = valid && (i + 1 == n || k[j + 2] == sentinel);
+      const bool none_valid = i == 0 && !valid;
+      if (last_valid || none_valid) {
+        const long long U = ex + h[j];
+        seg_offsets[U] = last_valid ? static_cast<int32_t>(i + 1) : 0;
+        *num_unique = static_cast<int32_t>(U);
+      }
+    }
+    ex += h[j];
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) pos[n] = static_cast<int32_t>(tot_before + chunk_tot);
+}
+
 __global__ void zero_segments(int32_t* seg_offsets, int32_t* num_unique) {
   if (threadIdx.x == 0) {
     seg_offsets[0] = 0;
@@ -264,10 +392,6 @@ __global__ void zero_segments(int32_t* seg_offsets, int32_t* num_unique) {
   }
 }
 
-__global__ __launch_bounds__(kBwdThreads) void copy_i32(const int32_t* __restrict__ a, int32_t* __restrict__ b, long long n) {
-  const long long i = static_cast<long long>(blockIdx.x) * kBwdThreads + threadIdx.x;
-  if (i < n) b[i] = a[i];
-}
 
 // ---------------------------------------------------------------------------
 // 5. segmented reduce + SGD over fixed chunks of the sorted occurrences
@@ -734,25 +858,34 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   for (int p = 0; p < passes; ++p) {
     const int shift = p * kRadixBits;
     hipLaunchKernelGGL(radix_count, dim3(ntiles), dim3(kBwdThreads), 0, st, keys[cur], n, shift, ntiles, counts);
-    hipError_t e = device_exclusive_scan(CountsIn{counts}, static_cast<long long>(ntiles) * kRadixBins, digit_off,
-                                         partial, a.status, 0, st);
-    if (e != hipSuccess) return e;
+    const bool inline_scan = ntiles <= kInlineScanTiles;
+    if (!inline_scan) {
+      hipError_t e = device_exclusive_scan(CountsIn{counts}, static_cast<long long>(ntiles) * kRadixBins, digit_off,
+                                           partial, a.status, 0, st);
+      if (e != hipSuccess) return e;
+    }
+    // the last pass writes the permutation straight to the caller's array, if any
+    int32_t* vout = (p + 1 == passes && a.perm) ? a.perm : vals[cur ^ 1];
     hipLaunchKernelGGL(radix_scatter, dim3(ntiles), dim3(kBwdThreads), 0, st, keys[cur], vals[cur], n, shift, ntiles,
-                       digit_off, keys[cur ^ 1], vals[cur ^ 1]);
+                       inline_scan ? nullptr : digit_off, counts, keys[cur ^ 1], vout);
     cur ^= 1;
   }
   const int32_t* skeys = keys[cur];
-  const int32_t* perm = vals[cur];
-  if (a.perm) {
-    hipLaunchKernelGGL(copy_i32, dim3(static_cast<unsigned>((n + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads), 0, st,
-                       perm, a.perm, n);
-  }
+  const int32_t* perm = a.perm ? a.perm : vals[cur];  // radix_passes() >= 1, so the last pass wrote a.perm
   // 4. segments
   {
-    hipError_t e = device_exclusive_scan(HeadIn{skeys, sentinel}, n, pos, partial, a.status, 0, st);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(build_segments, dim3(static_cast<unsigned>((n + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads),
-                       0, st, skeys, n, sentinel, pos, uniq, seg, nuniq);
+    const long long m = scan_chunks(n);
+    if (m <= kScanThreads) {  // chunk totals, then one pass that scans and builds the segments
+      hipLaunchKernelGGL((scan_chunk_totals<HeadIn>), dim3(static_cast<unsigned>(m)), dim3(kScanThreads), 0, st,
+                         HeadIn{skeys, sentinel}, n, partial);
+      hipLaunchKernelGGL(build_segments_chunked, dim3(static_cast<unsigned>(m)), dim3(kScanThreads), 0, st, skeys, n,
+                         sentinel, partial, pos, uniq, seg, nuniq);
+    } else {
+      hipError_t e = device_exclusive_scan(HeadIn{skeys, sentinel}, n, pos, partial, a.status, 0, st);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(build_segments, dim3(static_cast<unsigned>((n + kBwdThreads - 1) / kBwdThreads)),
+                         dim3(kBwdThreads), 0, st, skeys, n, sentinel, pos, uniq, seg, nuniq);
+    }
   }
   // 5. reduce + SGD
   switch (a.dtype) {

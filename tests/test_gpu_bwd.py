@@ -129,6 +129,15 @@ def test_backward_many_keys_four_radix_passes():
     run_bwd(w, lr=0.01)
 
 
+@pytest.mark.parametrize("B,bag", [(2100, ("uniform", 60, 70)), (8200, ("uniform", 62, 68))])
+def test_backward_sort_and_segment_paths(B, bag):
+    """About 273K occurrences (134 sort tiles of 2048: the sort's offsets come from a
+    device-wide scan rather than inside each tile) and about 1.07M (more than 256 scan
+    chunks of 4096: the segment scan also takes the device-wide path)."""
+    w = synth.Workload("paths", T=2, rows=3000, D=8, dtype="f32", B=B, bag=bag, dist=("zipf", 1.05), seed=B)
+    run_bwd(w, lr=0.01)
+
+
 def test_backward_hot_rows_span_many_chunks():
     """Multi-hot fp16 bags with a Zipf(1.1) hot row per table: its occurrences fill
     dozens of consecutive reduction chunks, whose partial sums are chained in order
