@@ -54,7 +54,7 @@ size_t tile_bytes(int T, int D) {
 
 size_t bwd_lds_bytes(int T, int D) {
   const size_t F = static_cast<size_t>(T) + 1;
-  return (F * (static_cast<size_t>(D) + 4) + F * F) * 4;
+  return (F * (static_cast<size_t>(D) + 4) + ((F + 3) & ~static_cast<size_t>(3)) * F) * 4;  // S padded to 4-row blocks
 }
 
 constexpr size_t kLds = 160 * 1024;

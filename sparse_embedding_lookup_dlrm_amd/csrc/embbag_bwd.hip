@@ -46,8 +46,9 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
   const int F = T + 1;
   const int LD = D + 4;
   const int W = D + (self_pairs ? F * (F + 1) / 2 : F * (F - 1) / 2);
+  const int Fp = (F + 3) & ~3;    // S rows, padded with zeros to whole blocks of 4
   float* Z = smem;                // [F][LD]
-  float* S = smem + F * LD;       // [F][F]
+  float* S = smem + F * LD;       // [Fp][F]
   const int b = xcd_block(blockIdx.x, gridDim.x);
   const int D4 = D / 4;
   // Z and S are filled in batches whose loads are all issued before the first
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
     }
   }
   const float* g = d_out + static_cast<size_t>(b) * W + D;
-  for (int i0 = threadIdx.x; i0 < F * F; i0 += kBatch * kBwdThreads) {
+  for (int i0 = threadIdx.x; i0 < Fp * F; i0 += kBatch * kBwdThreads) {
     float v[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = i0 + u * kBwdThreads;
-      if (i < F * F) S[i] = v[u];
+      if (i < Fp * F) S[i] = v[u];
     }
   }
   // the upstream gradient of e0 (row 0 is item threadIdx.x < D/4 of the loop below)
@@ -99,25 +100,38 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
     go = make_float4(p[0], p[1], p[2], p[3]);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < F * D4; i += kBwdThreads) {
-    const int f = i / D4, d = (i - f * D4) * 4;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float* srow = S + f * F;
+  // dZ = S Z: a thread computes 4 rows (f0..f0+3) of one float4 column, so each
+  // Z read serves 4 rows; the lanes of a wave share f0 (the column varies
+  // fastest), so their S reads are broadcasts
+  for (int i = threadIdx.x; i < (Fp / 4) * D4; i += kBwdThreads) {
+    const int fb = i / D4, d = (i - fb * D4) * 4;
+    const int f0 = 4 * fb;
+    float4 acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* srow = S + f0 * F;
     for (int j = 0; j < F; ++j) {
-      const float s = srow[j];
       const float4 z = *reinterpret_cast<const float4*>(Z + j * LD + d);
-      acc.x = fmaf(s, z.x, acc.x);
-      acc.y = fmaf(s, z.y, acc.y);
-      acc.z = fmaf(s, z.z, acc.z);
-      acc.w = fmaf(s, z.w, acc.w);
-    }
-    if (f == 0) {
-      if (d_e0) {
-        *reinterpret_cast<float4*>(d_e0 + static_cast<size_t>(b) * D + d) =
-            make_float4(go.x + acc.x, go.y + acc.y, go.z + acc.z, go.w + acc.w);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float s = srow[r * F + j];
+        acc[r].x = fmaf(s, z.x, acc[r].x);
+        acc[r].y = fmaf(s, z.y, acc[r].y);
+        acc[r].z = fmaf(s, z.z, acc[r].z);
+        acc[r].w = fmaf(s, z.w, acc[r].w);
       }
-    } else {
-      *reinterpret_cast<float4*>(d_pooled + (static_cast<size_t>(b) * T + f - 1) * D + d) = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int f = f0 + r;
+      if (f == 0) {
+        if (d_e0) {
+          *reinterpret_cast<float4*>(d_e0 + static_cast<size_t>(b) * D + d) =
+              make_float4(go.x + acc[r].x, go.y + acc[r].y, go.z + acc[r].z, go.w + acc[r].w);
+        }
+      } else if (f < F) {
+        *reinterpret_cast<float4*>(d_pooled + (static_cast<size_t>(b) * T + f - 1) * D + d) = acc[r];
+      }
     }
   }
 }
@@ -157,14 +171,23 @@ __global__ __launch_bounds__(kBwdThreads) void build_keys(MutTableArgs tabs, int
   const int rows = tabs.rows[t], base = tabs.base[t];
   const int bag = b * T + t;
   bool bad_idx = false;
-  for (long long p = s0; p < s1; ++p) {
-    const int r = indices[p];
-    int key = sentinel;
-    if (r >= 0 && r < rows) key = base + r;
-    else bad_idx = true;
-    keys[p] = key;
-    vals[p] = static_cast<int32_t>(p);
-    bag_of[p] = bag;
+  // eight index loads in flight per step (past the bag: re-read its first index)
+  for (long long p0 = s0; p0 < s1; p0 += 8) {
+    int r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r[u] = indices[p0 + u < s1 ? p0 + u : p0];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const long long p = p0 + u;
+      if (p < s1) {
+        int key = sentinel;
+        if (r[u] >= 0 && r[u] < rows) key = base + r[u];
+        else bad_idx = true;
+        keys[p] = key;
+        vals[p] = static_cast<int32_t>(p);
+        bag_of[p] = bag;
+      }
+    }
   }
   if (bad_idx) flag(status, DLRM_STATUS_BAD_INDEX);
 }
@@ -246,12 +269,17 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
   const long long sub = static_cast<long long>(blockIdx.x) * kRadixTile + static_cast<long long>(wave) * kRadixRounds * kWave;
   const unsigned long long lt = (1ull << lane) - 1ull;
   int key[kRadixRounds], val[kRadixRounds], dig[kRadixRounds], rank[kRadixRounds];
+  // every round's key and value loads are issued before the first is ranked
+#pragma unroll
+  for (int r = 0; r < kRadixRounds; ++r) {
+    const long long i = sub + r * kWave + lane;
+    key[r] = i < n ? keys_in[i] : 0;
+    val[r] = i < n ? vals_in[i] : 0;
+  }
 #pragma unroll
   for (int r = 0; r < kRadixRounds; ++r) {
     const long long i = sub + r * kWave + lane;
     const bool ok = i < n;
-    key[r] = ok ? keys_in[i] : 0;
-    val[r] = ok ? vals_in[i] : 0;
     const int d = (static_cast<uint32_t>(key[r]) >> shift) & (kRadixBins - 1);
     dig[r] = ok ? d : -1;
     unsigned long long peers = __ballot(ok);
@@ -803,7 +831,7 @@ hipError_t launch_reduce_dt(const BwdArgs& a, const WsLayout& L, char* ws, const
 hipError_t launch_interact_bwd(int T, int B, int D, bool self_pairs, const float* e0, const float* pooled,
                                const float* d_out, float* d_e0, float* d_pooled, hipStream_t st) {
   const int F = T + 1;
-  const size_t lds = (static_cast<size_t>(F) * (D + 4) + static_cast<size_t>(F) * F) * 4;
+  const size_t lds = (static_cast<size_t>(F) * (D + 4) + static_cast<size_t>((F + 3) & ~3) * F) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(interact_bwd_kernel, dim3(B), dim3(kBwdThreads), lds, st, T, B, D, self_pairs, e0, pooled, d_out,
                      d_pooled, d_e0);
@@ -832,7 +860,7 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   // 1. interaction backward
   {
     const int F = a.T + 1;
-    const size_t lds = (static_cast<size_t>(F) * (a.D + 4) + static_cast<size_t>(F) * F) * 4;
+    const size_t lds = (static_cast<size_t>(F) * (a.D + 4) + static_cast<size_t>((F + 3) & ~3) * F) * 4;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     hipLaunchKernelGGL(interact_bwd_kernel, dim3(a.B), dim3(kBwdThreads), lds, st, a.T, a.B, a.D, false, a.e0, a.pooled,
                        a.d_out, d_pooled, a.d_e0);
