@@ -151,12 +151,18 @@ __global__ __launch_bounds__(kBwdThreads) void fill_sentinel(int32_t* __restrict
   }
 }
 
+// LG lanes per bag (a power of two, 1..64): lane k of a bag's group handles
+// its occurrences k, k + LG, ... so loads and stores are contiguous across the
+// group; LG follows the average bag length.
+template <int LG>
 __global__ __launch_bounds__(kBwdThreads) void build_keys(MutTableArgs tabs, int T, int B, const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ indices, long long nnz,
                                                           int32_t sentinel, int32_t* __restrict__ keys,
                                                           int32_t* __restrict__ vals, int32_t* __restrict__ bag_of,
                                                           int32_t* status) {
-  const long long j = static_cast<long long>(blockIdx.x) * kBwdThreads + threadIdx.x;
+  const long long g = static_cast<long long>(blockIdx.x) * kBwdThreads + threadIdx.x;
+  const long long j = g / LG;
+  const int sub = static_cast<int>(g % LG);
   if (j >= static_cast<long long>(T) * B) return;
   const int t = static_cast<int>(j / B), b = static_cast<int>(j - static_cast<long long>(t) * B);
   long long s0 = offsets[j], s1 = offsets[j + 1];
@@ -167,18 +173,19 @@ __global__ __launch_bounds__(kBwdThreads) void build_keys(MutTableArgs tabs, int
   if (s0 > nnz) { s0 = nnz; bad_off = true; }
   if (s1 > nnz) { s1 = nnz; bad_off = true; }
   if (s1 < s0) { s1 = s0; bad_off = true; }
-  if (bad_off) flag(status, DLRM_STATUS_BAD_OFFSETS);
+  if (bad_off && sub == 0) flag(status, DLRM_STATUS_BAD_OFFSETS);
   const int rows = tabs.rows[t], base = tabs.base[t];
   const int bag = b * T + t;
   bool bad_idx = false;
-  // eight index loads in flight per step (past the bag: re-read its first index)
-  for (long long p0 = s0; p0 < s1; p0 += 8) {
-    int r[8];
+  // four index loads in flight per step (past the bag: re-read its first index)
+  constexpr int U = 4;
+  for (long long p0 = s0 + sub; p0 < s1; p0 += U * LG) {
+    int r[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) r[u] = indices[p0 + u < s1 ? p0 + u : p0];
+    for (int u = 0; u < U; ++u) r[u] = indices[p0 + u * LG < s1 ? p0 + u * LG : s0];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const long long p = p0 + u;
+    for (int u = 0; u < U; ++u) {
+      const long long p = p0 + u * LG;
       if (p < s1) {
         int key = sentinel;
         if (r[u] >= 0 && r[u] < rows) key = base + r[u];
@@ -216,20 +223,29 @@ constexpr int kInlineScanTiles = 128;
 
 // Where this tile's keys of digit d (= threadIdx.x) start in the output: all
 // keys of smaller digits, plus the keys of digit d in earlier tiles. The count
-// table is digit-major ([digit][tile]); the digit totals are scanned across
-// the workgroup.
-__device__ __forceinline__ int inline_digit_base(const int32_t* __restrict__ counts, int ntiles, int* lds4) {
+// table is digit-major ([digit][tile]). With row_prefix null the digit's row
+// is summed here; otherwise row_prefix holds each row's exclusive scan and
+// row_total each row's sum (radix_row_scan). The digit totals are then
+// scanned across the workgroup.
+__device__ __forceinline__ int tile_digit_base(const int32_t* __restrict__ counts,
+                                               const int32_t* __restrict__ row_prefix,
+                                               const int32_t* __restrict__ row_total, int ntiles, int* lds4) {
   const int d = threadIdx.x, lane = d & (kWave - 1), wave = d >> 6;
-  const int32_t* row = counts + static_cast<long long>(d) * ntiles;
   int tot = 0, pre = 0;
-  for (int t0 = 0; t0 < ntiles; t0 += 8) {
-    int c[8];
+  if (row_prefix) {
+    pre = row_prefix[static_cast<long long>(d) * ntiles + blockIdx.x];
+    tot = row_total[d];
+  } else {
+    const int32_t* row = counts + static_cast<long long>(d) * ntiles;
+    for (int t0 = 0; t0 < ntiles; t0 += 8) {
+      int c[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) c[u] = t0 + u < ntiles ? row[t0 + u] : 0;
+      for (int u = 0; u < 8; ++u) c[u] = t0 + u < ntiles ? row[t0 + u] : 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      tot += c[u];
-      if (t0 + u < static_cast<int>(blockIdx.x)) pre += c[u];
+      for (int u = 0; u < 8; ++u) {
+        tot += c[u];
+        if (t0 + u < static_cast<int>(blockIdx.x)) pre += c[u];
+      }
     }
   }
   int x = tot;  // inclusive scan of the totals over the wave, then across the 4 waves
@@ -245,17 +261,47 @@ __device__ __forceinline__ int inline_digit_base(const int32_t* __restrict__ cou
   return before + x - tot + pre;
 }
 
+// Each digit's row of the count table (one workgroup per digit): exclusive
+// scan across the tiles into row_prefix, and the row's sum into row_total.
+__global__ __launch_bounds__(kScanThreads) void radix_row_scan(const int32_t* __restrict__ counts, int ntiles,
+                                                               int32_t* __restrict__ row_prefix,
+                                                               int32_t* __restrict__ row_total) {
+  __shared__ long long lds[kScanThreads / kWave];
+  const long long r0 = static_cast<long long>(blockIdx.x) * ntiles;
+  long long carry = 0;
+  for (int base = 0; base < ntiles; base += kScanChunk) {
+    const int c0 = base + threadIdx.x * kScanPerThread;
+    int v[kScanPerThread];
+    long long sum = 0;
+#pragma unroll
+    for (int k = 0; k < kScanPerThread; ++k) {
+      v[k] = c0 + k < ntiles ? counts[r0 + c0 + k] : 0;
+      sum += v[k];
+    }
+    long long tot;
+    long long ex = block_exclusive_scan(sum, &tot, lds) + carry;
+#pragma unroll
+    for (int k = 0; k < kScanPerThread; ++k) {
+      if (c0 + k < ntiles) row_prefix[r0 + c0 + k] = static_cast<int32_t>(ex);
+      ex += v[k];
+    }
+    carry += tot;
+  }
+  if (threadIdx.x == 0) row_total[blockIdx.x] = static_cast<int32_t>(carry);
+}
+
 // Stable scatter of one tile. Wave w owns keys [tile + w*512, +512) and walks
 // them in rounds of 64 in their original order; equal digits inside a round
 // are ranked by lane with ballots, and a per-wave running count per digit
-// carries the rank across rounds. The tile's digit offsets come from
-// digit_off (the scanned count table) or, with digit_off null, from the count
-// table itself (at most kInlineScanTiles tiles).
+// carries the rank across rounds. The tile's digit offsets come from the
+// row-scanned count table (row_prefix, row_total) or, with row_prefix null,
+// from the count table itself (at most kInlineScanTiles tiles).
 __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __restrict__ keys_in,
                                                              const int32_t* __restrict__ vals_in, long long n,
                                                              int shift, int ntiles,
-                                                             const int32_t* __restrict__ digit_off,
                                                              const int32_t* __restrict__ counts,
+                                                             const int32_t* __restrict__ row_prefix,
+                                                             const int32_t* __restrict__ row_total,
                                                              int32_t* __restrict__ keys_out,
                                                              int32_t* __restrict__ vals_out) {
   __shared__ int wcount[kRadixWaves][kRadixBins];
@@ -263,8 +309,7 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
   __shared__ int lds4[kRadixWaves];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   for (int w = 0; w < kRadixWaves; ++w) wcount[w][threadIdx.x] = 0;
-  if (digit_off) gbase[threadIdx.x] = digit_off[static_cast<long long>(threadIdx.x) * ntiles + blockIdx.x];
-  else gbase[threadIdx.x] = inline_digit_base(counts, ntiles, lds4);
+  gbase[threadIdx.x] = tile_digit_base(counts, row_prefix, row_total, ntiles, lds4);
   __syncthreads();
   const long long sub = static_cast<long long>(blockIdx.x) * kRadixTile + static_cast<long long>(wave) * kRadixRounds * kWave;
   const unsigned long long lt = (1ull << lane) - 1ull;
@@ -315,11 +360,6 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
     vals_out[dst] = val[r];
   }
 }
-
-struct CountsIn {
-  const int32_t* p;
-  __device__ __forceinline__ long long operator()(long long i) const { return p[i]; }
-};
 
 struct HeadIn {
   const int32_t* keys;
@@ -742,7 +782,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t d_pooled, keys_a, keys_b, vals_a, vals_b, bag_of, counts, digit_off, partial, pos, uniq, seg, nuniq;
+  size_t d_pooled, keys_a, keys_b, vals_a, vals_b, bag_of, counts, digit_off, row_total, partial, pos, uniq, seg, nuniq;
   size_t carry, head, chunk_flags, total;
 };
 
@@ -773,6 +813,7 @@ WsLayout layout(int T, int B, int D, int64_t nnz) {
   L.bag_of = o; o = align_up(o + n * 4);
   L.counts = o; o = align_up(o + ncounts * 4);
   L.digit_off = o; o = align_up(o + (ncounts + 1) * 4);
+  L.row_total = o; o = align_up(o + kRadixBins * 4);
   L.partial = o; o = align_up(o + (scan_chunks(static_cast<long long>(scan_max)) + 1) * 8);
   L.pos = o; o = align_up(o + (n + 1) * 4);
   L.uniq = o; o = align_up(o + n * 4);
@@ -851,6 +892,7 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   int32_t* bag_of = reinterpret_cast<int32_t*>(ws + L.bag_of);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* digit_off = reinterpret_cast<int32_t*>(ws + L.digit_off);
+  int32_t* row_total = reinterpret_cast<int32_t*>(ws + L.row_total);
   long long* partial = reinterpret_cast<long long*>(ws + L.partial);
   int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
   int32_t* uniq = a.unique_keys ? a.unique_keys : reinterpret_cast<int32_t*>(ws + L.uniq);
@@ -876,8 +918,22 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
                      st, keys[0], vals[0], bag_of, n, sentinel);
   {
     const long long nb = static_cast<long long>(a.T) * a.B;
-    hipLaunchKernelGGL(build_keys, dim3(static_cast<unsigned>((nb + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads), 0,
-                       st, a.tabs, a.T, a.B, a.offsets, a.indices, n, sentinel, keys[0], vals[0], bag_of, a.status);
+    const long long avg = n / nb;  // lanes per bag: the average bag length, rounded down to a power of two
+    const int lg = avg >= 64 ? 64 : avg >= 32 ? 32 : avg >= 16 ? 16 : avg >= 8 ? 8 : avg >= 4 ? 4 : avg >= 2 ? 2 : 1;
+    const dim3 g(static_cast<unsigned>((nb * lg + kBwdThreads - 1) / kBwdThreads)), blk(kBwdThreads);
+#define DLRM_BUILD_KEYS(L) \
+  hipLaunchKernelGGL(build_keys<L>, g, blk, 0, st, a.tabs, a.T, a.B, a.offsets, a.indices, n, sentinel, keys[0], vals[0], \
+                     bag_of, a.status)
+    switch (lg) {
+      case 64: DLRM_BUILD_KEYS(64); break;
+      case 32: DLRM_BUILD_KEYS(32); break;
+      case 16: DLRM_BUILD_KEYS(16); break;
+      case 8: DLRM_BUILD_KEYS(8); break;
+      case 4: DLRM_BUILD_KEYS(4); break;
+      case 2: DLRM_BUILD_KEYS(2); break;
+      default: DLRM_BUILD_KEYS(1); break;
+    }
+#undef DLRM_BUILD_KEYS
   }
   // 3. radix sort, 8 bits per pass
   const int ntiles = static_cast<int>((n + kRadixTile - 1) / kRadixTile);
@@ -888,14 +944,13 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(radix_count, dim3(ntiles), dim3(kBwdThreads), 0, st, keys[cur], n, shift, ntiles, counts);
     const bool inline_scan = ntiles <= kInlineScanTiles;
     if (!inline_scan) {
-      hipError_t e = device_exclusive_scan(CountsIn{counts}, static_cast<long long>(ntiles) * kRadixBins, digit_off,
-                                           partial, a.status, 0, st);
-      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(radix_row_scan, dim3(kRadixBins), dim3(kScanThreads), 0, st, counts, ntiles, digit_off,
+                         row_total);
     }
     // the last pass writes the permutation straight to the caller's array, if any
     int32_t* vout = (p + 1 == passes && a.perm) ? a.perm : vals[cur ^ 1];
     hipLaunchKernelGGL(radix_scatter, dim3(ntiles), dim3(kBwdThreads), 0, st, keys[cur], vals[cur], n, shift, ntiles,
-                       inline_scan ? nullptr : digit_off, counts, keys[cur ^ 1], vout);
+                       counts, inline_scan ? nullptr : digit_off, row_total, keys[cur ^ 1], vout);
     cur ^= 1;
   }
   const int32_t* skeys = keys[cur];
