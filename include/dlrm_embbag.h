@@ -210,6 +210,7 @@ int dlrm_embbag_bwd_workspace_bytes(int32_t T, int32_t B, int32_t D, int64_t nnz
  *   seg_offsets  device int32 [nnz + 1] or NULL: out, occurrences of unique_keys[u] are
  *                perm[seg_offsets[u] .. seg_offsets[u+1]); seg_offsets[U] = nnz
  *   num_unique   device int32 [1] or NULL: out, U
+ *                (the three segment outputs are built only when at least one is requested)
  *   perm     device int32 [nnz] or NULL: out, the stable order of occurrences by key
  *            (ties keep CSR order); this permutation is unique
  *   workspace, ws_bytes  device scratch of at least dlrm_embbag_bwd_workspace_bytes() bytes

@@ -303,7 +303,9 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
                                                              const int32_t* __restrict__ row_prefix,
                                                              const int32_t* __restrict__ row_total,
                                                              int32_t* __restrict__ keys_out,
-                                                             int32_t* __restrict__ vals_out) {
+                                                             int32_t* __restrict__ vals_out,
+                                                             const int32_t* __restrict__ bag_of,
+                                                             int32_t* __restrict__ src_out) {
   __shared__ int wcount[kRadixWaves][kRadixBins];
   __shared__ int gbase[kRadixBins];
   __shared__ int lds4[kRadixWaves];
@@ -320,6 +322,12 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
     const long long i = sub + r * kWave + lane;
     key[r] = i < n ? keys_in[i] : 0;
     val[r] = i < n ? vals_in[i] : 0;
+  }
+  // last pass: the bag of each occurrence travels with it (src_out[dst] = bag_of[val])
+  int src[kRadixRounds];
+  if (src_out) {
+#pragma unroll
+    for (int r = 0; r < kRadixRounds; ++r) src[r] = bag_of[val[r]];  // val = 0 past the end: in bounds
   }
 #pragma unroll
   for (int r = 0; r < kRadixRounds; ++r) {
@@ -358,6 +366,7 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
     const int dst = gbase[dig[r]] + wcount[wave][dig[r]] + rank[r];
     keys_out[dst] = key[r];
     vals_out[dst] = val[r];
+    if (src_out) src_out[dst] = src[r];
   }
 }
 
@@ -582,12 +591,9 @@ __device__ __forceinline__ float adagrad_step(const RowVec<EL>& g, float s_old, 
 
 template <int DT, int EL, int C, int OPT>
 __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs tabs, StateArgs state, float eps, int T, int D,
-                                                                 const int32_t* __restrict__ unique_keys,
-                                                                 const int32_t* __restrict__ seg_offsets,
-                                                                 const int32_t* __restrict__ num_unique,
-                                                                 const int32_t* __restrict__ head_pos,
-                                                                 const int32_t* __restrict__ perm,
-                                                                 const int32_t* __restrict__ bag_of,
+                                                                 const int32_t* __restrict__ skeys, long long n,
+                                                                 int32_t sentinel,
+                                                                 const int32_t* __restrict__ src_bag,
                                                                  const float* __restrict__ d_pooled, float lr,
                                                                  float* __restrict__ carry, float* __restrict__ head,
                                                                  int32_t* __restrict__ chunk_flags, long long nchunks) {
@@ -598,25 +604,33 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
   const int lane = threadIdx.x & (kWave - 1);
   const int lpr = D < kWave ? D : kWave;
   const int col = (lane % lpr) * EL;
-  const int U = *num_unique;
-  const int nvalid = seg_offsets[U];  // occurrences with a valid key (the rest sort last)
   const long long k = static_cast<long long>(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6);
   if (k >= nchunks) return;
-  const int q0 = static_cast<int>(k * C);
-  if (q0 >= nvalid) {
+  const long long q0 = k * C;
+  // per position (lane j < C): its key (sorted), the key before it, the key
+  // after it, and the bag whose gradient row it adds; all independent loads.
+  // Valid keys form a prefix (the sentinel sorts last). Slots past the chunk
+  // or past the valid keys repeat the chunk's first position.
+  const long long qa = q0 + lane;
+  const bool in_n = lane < C && qa < n;
+  const long long qc = in_n ? qa : q0;
+  const int key_raw = skeys[qc];
+  const int key_prev = qc > 0 ? skeys[qc - 1] : -1;
+  const int key_next = qc + 1 < n ? skeys[qc + 1] : sentinel;
+  const int src_raw = src_bag[qc];
+  const unsigned long long valid_mask = __ballot(in_n && key_raw != sentinel);
+  const int nq = __popcll(valid_mask);
+  if (nq == 0) {
     if (lane == 0) chunk_flags[k] = 0;
     return;
   }
-  const int q1 = nvalid - q0 < C ? nvalid : q0 + C;
-  const int nq = q1 - q0;
-  // per position (lane j): gradient row, segment, and whether a segment starts
-  // there; head_pos is the exclusive scan of the segment-start flags, so position
-  // q belongs to segment head_pos[q + 1] - 1 and starts one if head_pos[q + 1] >
-  // head_pos[q]. Slots past the chunk repeat its first position.
-  const int qj = q0 + (lane < nq ? lane : 0);
-  const int src = bag_of[perm[qj]];
-  const int h1 = head_pos[qj + 1], h0 = head_pos[qj];
-  const int key = unique_keys[h1 - 1];
+  const bool mine = lane < nq;
+  const int key = mine ? key_raw : __shfl(key_raw, 0, kWave);
+  const int src = mine ? src_raw : __shfl(src_raw, 0, kWave);
+  // the position after the chunk's last valid one starts a new segment, or is
+  // the end of the valid keys
+  const int last_next = __shfl(key_next, nq - 1, kWave);
+  const bool next_starts = nq < C || last_next == sentinel || last_next != __shfl(key_raw, nq - 1, kWave);
   int tk = 0;  // table of this lane's key: the last one whose base is <= key
 #pragma unroll
   for (int step = 64; step > 0; step >>= 1) {
@@ -625,9 +639,8 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
     if (c < T && b <= key) tk = c;
   }
   const int rk = key - sbase[tk];
-  const bool starts = lane < nq && h1 > h0;
+  const bool starts = mine && (qa == 0 || key_prev != key_raw);
   // does a segment start right after the chunk? (then the last one closes here)
-  const bool next_starts = q1 >= nvalid || head_pos[q1 + 1] > head_pos[q1];
   const unsigned long long start_mask = __ballot(starts);
   const unsigned long long lane_bit = 1ull << lane;
   // position j closes a segment if a segment starts at j + 1 or j is the last one
@@ -712,10 +725,7 @@ __device__ __forceinline__ void row_update(const MutTableArgs& tabs, const State
 // chunks' carries in order and applies the update.
 template <int DT, int EL, int C, int OPT>
 __global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, StateArgs state, float eps, int T, int D,
-                                                           const int32_t* __restrict__ unique_keys,
-                                                           const int32_t* __restrict__ seg_offsets,
-                                                           const int32_t* __restrict__ num_unique,
-                                                           const int32_t* __restrict__ head_pos,
+                                                           const int32_t* __restrict__ skeys,
                                                            const float* __restrict__ carry,
                                                            const float* __restrict__ head,
                                                            const int32_t* __restrict__ chunk_flags, long long nchunks,
@@ -730,11 +740,9 @@ __global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, St
   // the chunk's last segment began inside it unless the chunk holds a single
   // segment that began earlier (then an earlier chunk owns it)
   if ((f & kChunkSingle) && (f & kChunkFirstCont)) return;
-  const int U = *num_unique;
-  const int nvalid = seg_offsets[U];
-  const int q0 = static_cast<int>(k * C);
-  const int q1 = nvalid - q0 < C ? nvalid : q0 + C;
-  const int sid = head_pos[q1] - 1;  // segment of the chunk's last position
+  // a chunk whose last segment goes on is full of valid keys: that segment's
+  // key is the one at the chunk's last position
+  const int key = skeys[k * C + C - 1];
   RowVec<EL> acc;
   acc.load(head + static_cast<size_t>(k) * D + col);
   // Chunk j's first part is this segment's; the segment goes on past chunk j
@@ -770,7 +778,7 @@ __global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, St
       }
     }
   }
-  row_update<DT, EL, OPT>(tabs, state, eps, T, D, unique_keys[sid], col, acc, lr);
+  row_update<DT, EL, OPT>(tabs, state, eps, T, D, key, col, acc, lr);
 }
 
 // ---------------------------------------------------------------------------
@@ -782,7 +790,8 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t d_pooled, keys_a, keys_b, vals_a, vals_b, bag_of, counts, digit_off, row_total, partial, pos, uniq, seg, nuniq;
+  size_t d_pooled, keys_a, keys_b, vals_a, vals_b, bag_of, src_bag, counts, digit_off, row_total, partial, pos, uniq, seg,
+      nuniq;
   size_t carry, head, chunk_flags, total;
 };
 
@@ -811,6 +820,7 @@ WsLayout layout(int T, int B, int D, int64_t nnz) {
   L.vals_a = o; o = align_up(o + n * 4);
   L.vals_b = o; o = align_up(o + n * 4);
   L.bag_of = o; o = align_up(o + n * 4);
+  L.src_bag = o; o = align_up(o + n * 4);
   L.counts = o; o = align_up(o + ncounts * 4);
   L.digit_off = o; o = align_up(o + (ncounts + 1) * 4);
   L.row_total = o; o = align_up(o + kRadixBins * 4);
@@ -829,12 +839,10 @@ WsLayout layout(int T, int B, int D, int64_t nnz) {
 }
 
 template <int DT, int EL>
-hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, const int32_t* uniq, const int32_t* seg,
-                             const int32_t* nuniq, const int32_t* perm, const int32_t* bag_of, const float* d_pooled,
-                             hipStream_t st) {
+hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, const int32_t* skeys, int32_t sentinel,
+                             const int32_t* src_bag, const float* d_pooled, hipStream_t st) {
   constexpr int C = seg_chunk(EL);
   const long long nchunks = (a.nnz + C - 1) / C;
-  const int32_t* head_pos = reinterpret_cast<const int32_t*>(ws + L.pos);
   float* carry = reinterpret_cast<float*>(ws + L.carry);
   float* head = reinterpret_cast<float*>(ws + L.head);
   int32_t* flags = reinterpret_cast<int32_t*>(ws + L.chunk_flags);
@@ -842,27 +850,26 @@ hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, cons
   const dim3 g(static_cast<unsigned>((nchunks + kWavesPerBlock - 1) / kWavesPerBlock)), blk(kBwdThreads);
   if (a.opt == kRowwiseAdagrad) {
     hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D,
-                       uniq, seg, nuniq, head_pos, perm, bag_of, d_pooled, a.lr, carry, head, flags, nchunks);
-    hipLaunchKernelGGL((seg_combine<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, uniq,
-                       seg, nuniq, head_pos, carry, head, flags, nchunks, a.lr);
+                       skeys, a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks);
+    hipLaunchKernelGGL((seg_combine<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
+                       carry, head, flags, nchunks, a.lr);
   } else {
-    hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, uniq, seg,
-                       nuniq, head_pos, perm, bag_of, d_pooled, a.lr, carry, head, flags, nchunks);
-    hipLaunchKernelGGL((seg_combine<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, uniq, seg,
-                       nuniq, head_pos, carry, head, flags, nchunks, a.lr);
+    hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
+                       a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks);
+    hipLaunchKernelGGL((seg_combine<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys, carry, head,
+                       flags, nchunks, a.lr);
   }
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t launch_reduce_dt(const BwdArgs& a, const WsLayout& L, char* ws, const int32_t* uniq, const int32_t* seg,
-                            const int32_t* nuniq, const int32_t* perm, const int32_t* bag_of, const float* d_pooled,
-                            hipStream_t st) {
+hipError_t launch_reduce_dt(const BwdArgs& a, const WsLayout& L, char* ws, const int32_t* skeys, int32_t sentinel,
+                            const int32_t* src_bag, const float* d_pooled, hipStream_t st) {
   switch (seg_el(a.D)) {
-    case 1: return launch_seg_reduce<DT, 1>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
-    case 2: return launch_seg_reduce<DT, 2>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
-    case 4: return launch_seg_reduce<DT, 4>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
-    case 8: return launch_seg_reduce<DT, 8>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
+    case 1: return launch_seg_reduce<DT, 1>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
+    case 2: return launch_seg_reduce<DT, 2>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
+    case 4: return launch_seg_reduce<DT, 4>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
+    case 8: return launch_seg_reduce<DT, 8>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -890,6 +897,7 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   int32_t* keys[2] = {reinterpret_cast<int32_t*>(ws + L.keys_a), reinterpret_cast<int32_t*>(ws + L.keys_b)};
   int32_t* vals[2] = {reinterpret_cast<int32_t*>(ws + L.vals_a), reinterpret_cast<int32_t*>(ws + L.vals_b)};
   int32_t* bag_of = reinterpret_cast<int32_t*>(ws + L.bag_of);
+  int32_t* src_bag = reinterpret_cast<int32_t*>(ws + L.src_bag);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* digit_off = reinterpret_cast<int32_t*>(ws + L.digit_off);
   int32_t* row_total = reinterpret_cast<int32_t*>(ws + L.row_total);
@@ -949,14 +957,18 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
     }
     // the last pass writes the permutation straight to the caller's array, if any
     int32_t* vout = (p + 1 == passes && a.perm) ? a.perm : vals[cur ^ 1];
+    // ... and each sorted position's bag (for the reduce)
+    const bool last_pass = p + 1 == passes;
     hipLaunchKernelGGL(radix_scatter, dim3(ntiles), dim3(kBwdThreads), 0, st, keys[cur], vals[cur], n, shift, ntiles,
-                       counts, inline_scan ? nullptr : digit_off, row_total, keys[cur ^ 1], vout);
+                       counts, inline_scan ? nullptr : digit_off, row_total, keys[cur ^ 1], vout, bag_of,
+                       last_pass ? src_bag : nullptr);
     cur ^= 1;
   }
   const int32_t* skeys = keys[cur];
-  const int32_t* perm = a.perm ? a.perm : vals[cur];  // radix_passes() >= 1, so the last pass wrote a.perm
-  // 4. segments
-  {
+  // radix_passes() >= 1, so the last pass wrote a.perm (if given) and src_bag
+  // 4. segments: outputs only (the reduce reads the sorted keys), so built only
+  // when the caller asks for any of them
+  if (a.unique_keys || a.seg_offsets || a.num_unique) {
     const long long m = scan_chunks(n);
     if (m <= kScanThreads) {  // chunk totals, then one pass that scans and builds the segments
       hipLaunchKernelGGL((scan_chunk_totals<HeadIn>), dim3(static_cast<unsigned>(m)), dim3(kScanThreads), 0, st,
@@ -972,9 +984,9 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   }
   // 5. reduce + SGD
   switch (a.dtype) {
-    case DLRM_F32: return launch_reduce_dt<DLRM_F32>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
-    case DLRM_F16: return launch_reduce_dt<DLRM_F16>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
-    case DLRM_BF16: return launch_reduce_dt<DLRM_BF16>(a, L, ws, uniq, seg, nuniq, perm, bag_of, d_pooled, st);
+    case DLRM_F32: return launch_reduce_dt<DLRM_F32>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
+    case DLRM_F16: return launch_reduce_dt<DLRM_F16>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
+    case DLRM_BF16: return launch_reduce_dt<DLRM_BF16>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
     default: return hipErrorInvalidValue;
   }
 }

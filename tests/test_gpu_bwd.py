@@ -47,6 +47,15 @@ def run_bwd(w: synth.Workload, lr=0.01, exact=False, twice=False):
         for t1, t2 in zip(db.tables, tabs2):
             assert torch.equal(t1.view(torch.int16) if t1.dtype != torch.float32 else t1,
                                t2.view(torch.int16) if t2.dtype != torch.float32 else t2)
+        # without the segment outputs (not built then): the same update and d_e0, bit for bit
+        tabs3 = [t.clone() for t in before]
+        res3 = ops.embbag_bwd_update(tabs3, db.offsets, db.indices, w.B, db.e0, pooled, d_out, lr,
+                                     want_segments=False)
+        torch.cuda.synchronize()
+        assert torch.equal(res["d_e0"], res3["d_e0"])
+        for t1, t3 in zip(db.tables, tabs3):
+            assert torch.equal(t1.view(torch.int16) if t1.dtype != torch.float32 else t1,
+                               t3.view(torch.int16) if t3.dtype != torch.float32 else t3)
 
     # oracle (own pooled, own offsets)
     off = orc.lengths_to_offsets(b.lengths)
