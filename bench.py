@@ -129,6 +129,62 @@ def summarize_profile(d: str, out: str, command: str, timed: int = 0) -> None:
     log("\n".join(lines))
 
 
+def summarize_backward(d: str, out: str, command: str, warmup: int, steps: int) -> None:
+    """Per-kernel durations of one backward step, averaged over the timed steps, for the
+    three backward timings of a default run (26-table SGD, 26-table row-wise AdaGrad,
+    multi-hot SGD; each step starts with the interaction backward)."""
+    import csv
+
+    rows = []
+    for p in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(p) as f:
+            rows += list(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    starts = [i for i, r in enumerate(rows) if "interact_bwd_kernel" in r["Kernel_Name"]]
+    steps_bwd = max(steps, 20)
+    groups = [("bwd-zipf-26t-d128-b2048 (SGD)", warmup + steps_bwd),
+              ("bwd-zipf-26t-d128-b2048 (row-wise AdaGrad)", min(warmup, 10) + steps_bwd),
+              ("multihot-8t4m-d64-fp16-b4096 (SGD)", min(warmup, 10) + steps_bwd)]
+    lines = [f"# rocprofv3 summary of: {command}", f"# source directory: {d}",
+             "# mean kernel durations (us) over the timed steps of each backward timing"]
+    k = 0
+    for name, count in groups:
+        its = starts[k:k + count]
+        k += count
+        if len(its) < count:
+            break
+        per = {}
+        order = []
+        timed = its[-steps_bwd:]
+        for n, i0 in enumerate(timed):
+            i1 = starts[starts.index(i0) + 1] if starts.index(i0) + 1 < len(starts) else len(rows)
+            seen = {}
+            for r in rows[i0:i1]:
+                if "dlrm::" not in r["Kernel_Name"]:
+                    continue
+                nm = r["Kernel_Name"].split("(")[0]
+                seen[nm] = seen.get(nm, 0) + 1
+                key = (nm, seen[nm])
+                if key not in per:
+                    per[key] = []
+                    order.append(key)
+                per[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines.append(f"## {name}: {len(timed)} steps")
+        lines.append("kernel | launch | mean_us")
+        tot = 0.0
+        for key in order:
+            v = per[key]
+            if len(v) != len(timed):  # set-up work of the next timing, after the last step
+                continue
+            m = sum(v) / len(v)
+            tot += m
+            lines.append(f"{key[0][:70]} | {key[1]} | {m:.2f}")
+        lines.append(f"sum of kernel durations per step: {tot:.1f} us")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("\n".join(lines))
+
+
 COPY_KERNEL = "AUnaryFunctor"  # torch.mul(src, 1.0, out=dst): reads and writes n*4 bytes once
 
 
@@ -451,6 +507,7 @@ def main():
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain copy of this size (for counter calibration)")
     ap.add_argument("--summarize-profile", default=None)
+    ap.add_argument("--summarize-backward", default=None)
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="rocprofv3 FETCH_SIZE and WRITE_SIZE csv dirs (runs made with --copy-calibration-gib) "
                          "-> traffic file")
@@ -461,6 +518,9 @@ def main():
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.copy_calibration_gib, args.out or TRAFFIC_FILE,
                       args.command)
+        return 0
+    if args.summarize_backward:
+        summarize_backward(args.summarize_backward, args.out, args.command, args.warmup, args.steps)
         return 0
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.out, args.command, args.steps)
