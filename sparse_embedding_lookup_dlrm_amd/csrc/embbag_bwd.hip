@@ -52,8 +52,29 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
   const int b = xcd_block(blockIdx.x, gridDim.x);
   const int D4 = D / 4;
   // Z and S are filled in batches whose loads are all issued before the first
-  // LDS store, so a batch costs one memory round trip, not one per element
+  // LDS store, so a batch costs one memory round trip, not one per element; the
+  // first batch of S and the e0 gradient are loaded before Z's batches
   constexpr int kBatch = 4;
+  const float* g = d_out + static_cast<size_t>(b) * W + D;
+  auto s_value = [&](int i) -> float {  // S[r][c] from the upstream pair gradients (i = r * F + c)
+    const int r = i / F, c = i - r * F;
+    const int hi = r > c ? r : c, lo = r > c ? c : r;
+    const bool use = i < F * F && (self_pairs || hi != lo);
+    const int k = self_pairs ? hi * (hi + 1) / 2 + lo : hi * (hi - 1) / 2 + lo;
+    float v = g[use ? k : 0];
+    if (!use) v = 0.f;
+    else if (self_pairs && hi == lo) v *= 2.f;
+    return v;
+  };
+  float s_first[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) s_first[u] = s_value(threadIdx.x + u * kBwdThreads);
+  // the upstream gradient of e0 (row 0 is item threadIdx.x < D/4 of the dZ loop)
+  float4 go = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (d_e0 && threadIdx.x < D4) {
+    const float* p = d_out + static_cast<size_t>(b) * W + 4 * threadIdx.x;
+    go = make_float4(p[0], p[1], p[2], p[3]);
+  }
   for (int i0 = threadIdx.x; i0 < F * D4; i0 += kBatch * kBwdThreads) {
     float4 v[kBatch];
 #pragma unroll
@@ -73,31 +94,20 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
       }
     }
   }
-  const float* g = d_out + static_cast<size_t>(b) * W + D;
-  for (int i0 = threadIdx.x; i0 < Fp * F; i0 += kBatch * kBwdThreads) {
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int i = threadIdx.x + u * kBwdThreads;
+    if (i < Fp * F) S[i] = s_first[u];
+  }
+  for (int i0 = threadIdx.x + kBatch * kBwdThreads; i0 < Fp * F; i0 += kBatch * kBwdThreads) {
     float v[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u * kBwdThreads;
-      const int r = i / F, c = i - r * F;
-      const int hi = r > c ? r : c, lo = r > c ? c : r;
-      const bool use = i < F * F && (self_pairs || hi != lo);
-      const int k = self_pairs ? hi * (hi + 1) / 2 + lo : hi * (hi - 1) / 2 + lo;
-      v[u] = g[use ? k : 0];
-      if (!use) v[u] = 0.f;
-      else if (self_pairs && hi == lo) v[u] *= 2.f;
-    }
+    for (int u = 0; u < kBatch; ++u) v[u] = s_value(i0 + u * kBwdThreads);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = i0 + u * kBwdThreads;
       if (i < Fp * F) S[i] = v[u];
     }
-  }
-  // the upstream gradient of e0 (row 0 is item threadIdx.x < D/4 of the loop below)
-  float4 go = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (d_e0 && threadIdx.x < D4) {
-    const float* p = d_out + static_cast<size_t>(b) * W + 4 * threadIdx.x;
-    go = make_float4(p[0], p[1], p[2], p[3]);
   }
   __syncthreads();
   // dZ = S Z: a thread computes 4 rows (f0..f0+3) of one float4 column, so each
@@ -311,12 +321,11 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
   __shared__ int lds4[kRadixWaves];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   for (int w = 0; w < kRadixWaves; ++w) wcount[w][threadIdx.x] = 0;
-  gbase[threadIdx.x] = tile_digit_base(counts, row_prefix, row_total, ntiles, lds4);
-  __syncthreads();
   const long long sub = static_cast<long long>(blockIdx.x) * kRadixTile + static_cast<long long>(wave) * kRadixRounds * kWave;
   const unsigned long long lt = (1ull << lane) - 1ull;
   int key[kRadixRounds], val[kRadixRounds], dig[kRadixRounds], rank[kRadixRounds];
-  // every round's key and value loads are issued before the first is ranked
+  // every round's key and value loads are issued first, so that they are in
+  // flight while the tile's digit offsets are worked out
 #pragma unroll
   for (int r = 0; r < kRadixRounds; ++r) {
     const long long i = sub + r * kWave + lane;
@@ -329,6 +338,8 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
 #pragma unroll
     for (int r = 0; r < kRadixRounds; ++r) src[r] = bag_of[val[r]];  // val = 0 past the end: in bounds
   }
+  gbase[threadIdx.x] = tile_digit_base(counts, row_prefix, row_total, ntiles, lds4);
+  __syncthreads();
 #pragma unroll
   for (int r = 0; r < kRadixRounds; ++r) {
     const long long i = sub + r * kWave + lane;
