@@ -483,21 +483,33 @@ struct RowShape {
   // rows per window (two windows in flight: 32 VGPRs); 8-bit rows also carry a
   // scale and a bias per row and keep more columns per lane, so their windows
   // are smaller
-  static constexpr int WIN = DT == DLRM_Q8 ? (LB >= 8 ? 4 : 8)
-                             : DT == DLRM_Q8T ? (LB >= 8 ? 4 : 16)
-                                              : (LB >= 4 ? 64 / LB : 16);
+  // (16-bit rows of 512 and 1024 bytes and table-wise 8-bit rows keep a few
+  // rows fewer in flight, which keeps them within 80 VGPRs without spills)
+  static constexpr int WIN = DT == DLRM_Q8                   ? (LB >= 8 ? 4 : 8)
+                             : DT == DLRM_Q8T                ? (LB >= 8 ? 4 : 12)
+                             : (DT != DLRM_F32 && LB == 16) ? 3
+                             : (DT != DLRM_F32 && LB == 8)  ? 6
+                                                             : (LB >= 4 ? 64 / LB : 16);
 };
 
+// LDS of the row-streaming kernel: table bases, row counts and 8-bit scales
+// shared by the workgroup, then G identical per-group regions (a group of
+// 512/G threads works on its own sample). Offsets marked "in a group" are
+// relative to the group's region.
 struct RowLayout {
+  int G;         // sample groups per workgroup (1, 2, 4, 8)
   int Tp;        // Z rows after e0 (T rounded up: 32 for MFMA, else to F multiple of 4)
   int LD;        // Z row stride in floats
-  int off_beg;   // byte offsets inside the dynamic LDS block; bag tables are double-buffered
+  int off_tbase;
+  int off_trows;
+  int off_qsb;   // table-wise 8-bit rows: (scale, bias) per table
+  int off_groups;
+  int group_bytes;
+  // in a group:
+  int off_beg;   // bag tables, double-buffered
   int off_pos;
   int pos_stride;  // bytes between the two bag-table buffers
   int off_carry_t;
-  int off_tbase;
-  int off_trows;
-  int off_qsb;  // table-wise 8-bit rows: (scale, bias) per table
   int off_stage;
   int off_sbag;
   int off_carry;
@@ -508,30 +520,36 @@ struct RowLayout {
 
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
 
-__host__ __device__ inline RowLayout make_row_layout(int T, int D, bool mfma) {
+__host__ __device__ inline RowLayout make_row_layout(int T, int D, bool mfma, int G = 1) {
   RowLayout L;
+  L.G = G;
   L.Tp = mfma ? ((T + 31) / 32) * 32 : (((T + 1 + 3) & ~3) - 1);
   L.LD = D + 4;
   const int P = (T + 1) * T / 2;
   int o = 0;
-  L.pos_stride = align16(T * 4) + align16((T + 1) * 4);
-  L.off_beg = o;                       // [2] x { bag begin (index position) [T]; stream start [T+1] }
-  L.off_pos = o + align16(T * 4);
-  o += 2 * L.pos_stride;
-  L.off_carry_t = o; o += align16(kRowWaves * 4);
   L.off_tbase = o; o += align16(T * 8);
   L.off_trows = o; o += align16(T * 4);
   L.off_qsb = o; o += align16(T * 8);
-  const int uni = o;                   // union { stage + bag ids + carries ; output staging }
+  L.off_groups = o;
+  const int gw = kRowWaves / G;
+  const int cap = kStageCap / G;
+  int g = 0;
+  L.pos_stride = align16(T * 4) + align16((T + 1) * 4);
+  L.off_beg = g;                       // [2] x { bag begin (index position) [T]; stream start [T+1] }
+  L.off_pos = g + align16(T * 4);
+  g += 2 * L.pos_stride;
+  L.off_carry_t = g; g += align16(gw * 4);
+  const int uni = g;                   // union { stage + bag ids + carries ; output staging }
   L.off_stage = uni;
-  L.off_sbag = L.off_stage + kStageCap * 4;
-  L.off_carry = L.off_sbag + align16(kStageCap);
-  const int gather_bytes = L.off_carry + kRowWaves * D * 4 - uni;
+  L.off_sbag = L.off_stage + cap * 4;
+  L.off_carry = L.off_sbag + align16(cap);
+  const int gather_bytes = L.off_carry + gw * D * 4 - uni;
   L.off_out = uni;
   const int out_bytes = (D + P) * 4;
-  o = uni + align16(gather_bytes > out_bytes ? gather_bytes : out_bytes);
-  L.off_z = o; o += (1 + L.Tp) * L.LD * 4;
-  L.bytes = o;
+  g = uni + align16(gather_bytes > out_bytes ? gather_bytes : out_bytes);
+  L.off_z = g; g += (1 + L.Tp) * L.LD * 4;
+  L.group_bytes = align16(g);
+  L.bytes = L.off_groups + G * L.group_bytes;
   return L;
 }
 
@@ -564,16 +582,17 @@ __device__ __forceinline__ void split_bf16x8(const float4& a, const float4& b, b
 // [2D, 4D)). Every thread reads its values before any thread writes (a
 // workgroup barrier between), in chunks of whole rows, so no row is
 // overwritten while still unread. Ends with a barrier.
+template <int NT>
 __device__ __forceinline__ void split_rows(float* Z, int LD, int D, int Tp, int tid) {
   const int gpr = D / 8;  // 8-value groups per row
-  const int rows_per_chunk = (2 * kRowThreads) / gpr > 0 ? (2 * kRowThreads) / gpr : 1;
+  const int rows_per_chunk = (2 * NT) / gpr > 0 ? (2 * NT) / gpr : 1;
   for (int r0 = 1; r0 <= Tp; r0 += rows_per_chunk) {
     const int r1 = min(Tp + 1, r0 + rows_per_chunk);
     float4 x[2][2];
     int off[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int idx = tid + k * kRowThreads;
+      const int idx = tid + k * NT;
       const int row = r0 + idx / gpr, g = idx % gpr;
       off[k] = -1;
       if (row < r1) {
@@ -629,9 +648,10 @@ __device__ __forceinline__ void gram_tile_mfma(const float* Z, int LD, int D, in
 // Dots of e0 (Z row 0) with every pooled row, in fp32 from the unsplit rows:
 // 8 lanes per dot, lane j over the float4 chunks j, j+8, ... of D, combined
 // in a fixed order. Pair (zi, 0) sits at out[D + zi(zi-1)/2].
+template <int NT>
 __device__ __forceinline__ void e0_dots(const float* Z, int LD, int D, int T, float* out, int tid) {
   const int j = tid & 7;
-  for (int zi = 1 + (tid >> 3); zi <= T; zi += kRowThreads / 8) {
+  for (int zi = 1 + (tid >> 3); zi <= T; zi += NT / 8) {
     const float* zr = Z + zi * LD;
     float sum = 0.f;
     for (int d = 4 * j; d < D; d += 32) {
@@ -688,7 +708,7 @@ __device__ __forceinline__ int last_le(const int* pos, int T, int x) {
 // bias, rows RB + 8 bytes apart; each lane also loads the (scale, bias) pair of
 // "its" row of the window. QM = 2 (table-wise): D codes per row, the table's
 // (scale, bias) pair read from LDS (qsb).
-template <int WIN, int RB, bool BEYOND, int QM = 0>
+template <int WIN, int RB, bool BEYOND, int QM, int CAP>
 __device__ __forceinline__ void prepare_window(Window& w, const FwdArgs& a, const int* sm_beg, const int* sm_pos,
                                                const int* stage, const uint8_t* sbag, const char* const* tbase,
                                                const int* trows, int T, int q, int p1, uint64_t fallback,
@@ -701,7 +721,7 @@ __device__ __forceinline__ void prepare_window(Window& w, const FwdArgs& a, cons
   const int pos = q + lane;
   if (lane < WIN && pos < p1) {
     int r;
-    if (!BEYOND || pos < kStageCap) {
+    if (!BEYOND || pos < CAP) {
       r = stage[pos];
       tk = sbag[pos];
     } else {  // beyond the staging area: locate the bag and read the index from HBM
@@ -822,7 +842,7 @@ __device__ __forceinline__ void scan_positions(int* pos, int T, int tid) {
   if (lane == 0) pos[0] = 0;
 }
 
-constexpr int kStagePerThread = kStageCap / kRowThreads;
+constexpr int kStagePerThread = kStageCap / kRowThreads;  // the same for every group size
 
 // Issue the loads of a sample's staged indices (stream positions tid + k*512);
 // the values are written to LDS later by write_stage. The bag of each
@@ -830,6 +850,7 @@ constexpr int kStagePerThread = kStageCap / kRowThreads;
 // branch, a position past the stream reading the sample's last index
 // instead, so that the loads land straight in r[] and nothing waits for them
 // before write_stage.
+template <int NT>
 __device__ __forceinline__ void load_stage(const FwdArgs& a, const int* beg, const int* pos, int T, int N,
                                            int (&r)[kStagePerThread], int (&tb)[kStagePerThread], int tid) {
   int off[kStagePerThread];
@@ -838,7 +859,7 @@ __device__ __forceinline__ void load_stage(const FwdArgs& a, const int* beg, con
   const int last = a.nnz > 0 ? static_cast<int>(a.nnz) - 1 : 0;
 #pragma unroll
   for (int k = 0; k < kStagePerThread; ++k) {
-    const int p = tid + k * kRowThreads;
+    const int p = tid + k * NT;
     const int pc = p < N ? p : (N > 0 ? N - 1 : 0);
     const int lo = last_le(pos, T, pc);
     tb[k] = p < N ? lo : -1;
@@ -849,6 +870,7 @@ __device__ __forceinline__ void load_stage(const FwdArgs& a, const int* beg, con
   for (int k = 0; k < kStagePerThread; ++k) r[k] = src[off[k]];
 }
 
+template <int NT>
 __device__ __forceinline__ void write_stage(const FwdArgs& a, const int (&r)[kStagePerThread],
                                             const int (&tb)[kStagePerThread], int* stage, uint8_t* sbag,
                                             const int* trows, int tid) {
@@ -858,8 +880,8 @@ __device__ __forceinline__ void write_stage(const FwdArgs& a, const int (&r)[kSt
     if (tb[k] >= 0) {
       int v = r[k];
       if (v < 0 || v >= trows[tb[k]]) { bad = true; v = -1; }
-      stage[tid + k * kRowThreads] = v;
-      sbag[tid + k * kRowThreads] = static_cast<uint8_t>(tb[k]);
+      stage[tid + k * NT] = v;
+      sbag[tid + k * NT] = static_cast<uint8_t>(tb[k]);
     }
   }
   if (bad) flag(a.status, DLRM_STATUS_BAD_INDEX);
@@ -877,7 +899,7 @@ __device__ __forceinline__ void touch(uint4 x) { asm volatile("" ::"v"(x.x), "v"
 // there; window k+1's loads are issued before window k is summed. Slots past
 // the range load a fixed in-bounds row (a cache hit) and add zero, so every
 // window issues the same number of loads.
-template <int DT, int LB, bool BEYOND>
+template <int DT, int LB, bool BEYOND, int CAP>
 __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, const int* pos, const int* stage,
                                              const uint8_t* sbag, const char* const* tbase, const int* trows, int T,
                                              int p0, int p1, float* Z, int LD, float* carry_w, int* carry_t_w,
@@ -899,16 +921,16 @@ __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, c
   const uint64_t lane_off = static_cast<uint64_t>(tid & (kWave - 1)) * LB;
   Window wa, wb;
   typename C::type va[WIN], vb[WIN];
-  prepare_window<WIN, RB, BEYOND, QM>(wa, a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, fallback, tid, qsb);
+  prepare_window<WIN, RB, BEYOND, QM, CAP>(wa, a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, fallback, tid, qsb);
   issue_window<C, WIN>(wa, va, lane_off);
   for (int q = p0;;) {
-    prepare_window<WIN, RB, BEYOND, QM>(wb, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid,
+    prepare_window<WIN, RB, BEYOND, QM, CAP>(wb, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid,
                                         qsb);
     issue_window<C, WIN>(wb, vb, lane_off);
     consume_window<DT, LB, WIN>(wa, va, acc, cur, Z, LD, carry_w, carry_t_w, tid, bacc);
     q += WIN;
     if (q >= p1) break;
-    prepare_window<WIN, RB, BEYOND, QM>(wa, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid,
+    prepare_window<WIN, RB, BEYOND, QM, CAP>(wa, a, beg, pos, stage, sbag, tbase, trows, T, q + WIN, p1, fallback, tid,
                                         qsb);
     issue_window<C, WIN>(wa, va, lane_off);
     consume_window<DT, LB, WIN>(wb, vb, acc, cur, Z, LD, carry_w, carry_t_w, tid, bacc);
@@ -928,47 +950,65 @@ __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, c
 }
 
 // Persistent workgroups: each takes a contiguous chunk of samples and runs,
-// per sample, [gather | prefetch next offsets and e0] -> [carries, scan of the
+// per step, [gather | prefetch next offsets and e0] -> [carries, scan of the
 // next sample] -> [interaction | next sample's index loads in flight] ->
 // [output] -> [stage next indices, reset Z]. The round trips of the next
 // sample's offsets, e0 and indices overlap this sample's gather and
 // interaction.
-template <int DT, int LB, bool MFMA>
+//
+// With G > 1 (short samples) the workgroup is G groups of 512/G threads, each
+// with its own LDS region and its own sample in every step, so G samples'
+// latency chains overlap; every group runs the same steps and meets the same
+// barriers. In a step past the end of the chunk a group repeats the chunk's
+// last sample (all loads in bounds) and writes nothing.
+template <int DT, int LB, bool MFMA, int G>
 __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, RowLayout L, int chunk) {
+  constexpr int NT = kRowThreads / G;  // threads of a group
+  constexpr int GW = kRowWaves / G;    // waves of a group
+  constexpr int CAP = kStageCap / G;   // staged indices of a group's sample
   extern __shared__ __align__(16) char lds[];
-  int* carry_t = reinterpret_cast<int*>(lds + L.off_carry_t);
   const char** tbase = reinterpret_cast<const char**>(lds + L.off_tbase);
   int* trows = reinterpret_cast<int*>(lds + L.off_trows);
   float* qsb = reinterpret_cast<float*>(lds + L.off_qsb);
-  int* stage = reinterpret_cast<int*>(lds + L.off_stage);
-  uint8_t* sbag = reinterpret_cast<uint8_t*>(lds + L.off_sbag);
-  float* carry = reinterpret_cast<float*>(lds + L.off_carry);
-  float* outs = reinterpret_cast<float*>(lds + L.off_out);
-  float* Z = reinterpret_cast<float*>(lds + L.off_z);
 
   const int T = a.T, D = a.D, LD = L.LD;
   const int W = D + (T + 1) * T / 2;
-  const int tid = threadIdx.x;
-  const int wave = rfl(tid >> 6);
+  const int grp = G == 1 ? 0 : rfl(static_cast<int>(threadIdx.x) / NT);
+  const int wave = rfl((static_cast<int>(threadIdx.x) >> 6) % GW);  // wave within the group
+  char* gl = lds + L.off_groups + grp * L.group_bytes;
+  int* carry_t = reinterpret_cast<int*>(gl + L.off_carry_t);
+  int* stage = reinterpret_cast<int*>(gl + L.off_stage);
+  uint8_t* sbag = reinterpret_cast<uint8_t*>(gl + L.off_sbag);
+  float* carry = reinterpret_cast<float*>(gl + L.off_carry);
+  float* outs = reinterpret_cast<float*>(gl + L.off_out);
+  float* Z = reinterpret_cast<float*>(gl + L.off_z);
+
   const int b_begin = xcd_block(blockIdx.x, gridDim.x) * chunk;
   const int b_end = min(a.B, b_begin + chunk);
   if (b_begin >= b_end) return;  // whole workgroup
+  // this group's sample in the step that starts at sample bs (past the chunk:
+  // the chunk's last sample, not written)
+  auto sample_of = [&](int bs) { return G == 1 ? bs : min(bs + grp, b_end - 1); };
 
   // ---- prologue: first sample's bags, positions, indices, e0
   int pb = 0;
   {
-    int* beg = reinterpret_cast<int*>(lds + L.off_beg);
-    int* pos = reinterpret_cast<int*>(lds + L.off_pos);
-    // e0 goes out with the offsets (D <= kRowThreads), not after them
-    const float e0v = tid < D ? a.e0[static_cast<size_t>(b_begin) * D + tid] : 0.f;
-    if (tid < T) {
-      publish_bag(a, tid, b_begin, a.offsets[tid * a.B + b_begin], a.offsets[tid * a.B + b_begin + 1], beg, pos);
-      tbase[tid] = static_cast<const char*>(a.tabs.ptr[tid]);
-      trows[tid] = a.tabs.rows[tid];
+    const int tid = static_cast<int>(threadIdx.x) % NT;
+    const int b0 = sample_of(b_begin);
+    int* beg = reinterpret_cast<int*>(gl + L.off_beg);
+    int* pos = reinterpret_cast<int*>(gl + L.off_pos);
+    // e0 goes out with the offsets (D <= NT), not after them
+    const float e0v = tid < D ? a.e0[static_cast<size_t>(b0) * D + tid] : 0.f;
+    if (threadIdx.x < static_cast<unsigned>(T)) {
+      tbase[threadIdx.x] = static_cast<const char*>(a.tabs.ptr[threadIdx.x]);
+      trows[threadIdx.x] = a.tabs.rows[threadIdx.x];
       if constexpr (DT == DLRM_Q8T) {
-        qsb[2 * tid] = a.qscale[tid];
-        qsb[2 * tid + 1] = a.qbias[tid];
+        qsb[2 * threadIdx.x] = a.qscale[threadIdx.x];
+        qsb[2 * threadIdx.x + 1] = a.qbias[threadIdx.x];
       }
+    }
+    if (tid < T) {
+      publish_bag(a, tid, b0, a.offsets[tid * a.B + b0], a.offsets[tid * a.B + b0 + 1], beg, pos);
       clear_if_empty(pos, tid, Z, LD, D);
     }
     __syncthreads();
@@ -976,33 +1016,35 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     if (wave == 0) scan_positions(pos, T, tid);
     __syncthreads();
     int r[kStagePerThread], tb[kStagePerThread];
-    load_stage(a, beg, pos, T, rfl(pos[T]), r, tb, tid);
-    write_stage(a, r, tb, stage, sbag, trows, tid);
-    if (tid < kRowWaves) carry_t[tid] = -1;
+    load_stage<NT>(a, beg, pos, T, rfl(pos[T]), r, tb, tid);
+    write_stage<NT>(a, r, tb, stage, sbag, trows, tid);
+    if (tid < GW) carry_t[tid] = -1;
     __syncthreads();
   }
 
-  for (int b = b_begin; b < b_end; ++b) {
+  for (int bs = b_begin; bs < b_end; bs += G) {
     // The thread index is re-derived opaquely each sample so that the compiler
     // recomputes per-thread addresses instead of keeping them live (and
     // spilled) across the whole loop.
-    int tid = threadIdx.x;
+    int tid = static_cast<int>(threadIdx.x) % NT;
     asm volatile("" : "+v"(tid));
-    const bool has_next = b + 1 < b_end;
-    int* beg = reinterpret_cast<int*>(lds + L.off_beg + pb * L.pos_stride);
-    int* pos = reinterpret_cast<int*>(lds + L.off_pos + pb * L.pos_stride);
-    int* nbeg = reinterpret_cast<int*>(lds + L.off_beg + (pb ^ 1) * L.pos_stride);
-    int* npos = reinterpret_cast<int*>(lds + L.off_pos + (pb ^ 1) * L.pos_stride);
+    const int b = sample_of(bs);
+    const bool active = G == 1 || bs + grp < b_end;  // this group writes its sample
+    const bool has_next = bs + G < b_end;
+    int* beg = reinterpret_cast<int*>(gl + L.off_beg + pb * L.pos_stride);
+    int* pos = reinterpret_cast<int*>(gl + L.off_pos + pb * L.pos_stride);
+    int* nbeg = reinterpret_cast<int*>(gl + L.off_beg + (pb ^ 1) * L.pos_stride);
+    int* npos = reinterpret_cast<int*>(gl + L.off_pos + (pb ^ 1) * L.pos_stride);
     const int N = rfl(pos[T]);
 
     // next sample's bag ranges and e0: loads in flight during the gather. Every
-    // thread issues them, clamped in bounds (the last sample re-reads its own),
-    // so that no branch merges their registers and nothing waits for them
-    // before the gather is done.
+    // thread issues them, clamped in bounds (the last step re-reads its own
+    // sample), so that no branch merges their registers and nothing waits for
+    // them before the gather is done.
     int nx0, nx1;
     float ne0;
+    const int bn = has_next ? sample_of(bs + G) : b;
     {
-      const int bn = has_next ? b + 1 : b;
       const int tt = tid < T ? tid : T - 1;
       const int td = tid < D ? tid : D - 1;
       nx0 = a.offsets[tt * a.B + bn];
@@ -1010,21 +1052,23 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
       ne0 = a.e0[static_cast<size_t>(bn) * D + td];
     }
 
-    // gather: wave w sums stream positions [p0, p1) in windows of WIN rows.
-    // Each lane first works out the address of "its" row of a window and
-    // whether a sum ends there; window k+1's loads are issued before window k
-    // is summed. Slots past the range load a fixed in-bounds row (a cache
+    // gather: wave w of the group sums stream positions [p0, p1) in windows of
+    // WIN rows. Each lane first works out the address of "its" row of a window
+    // and whether a sum ends there; window k+1's loads are issued before window
+    // k is summed. Slots past the range load a fixed in-bounds row (a cache
     // hit) and are zeroed, so every window issues the same number of loads.
     {
-      const int p0 = static_cast<int>((static_cast<long long>(N) * wave) / kRowWaves);
-      const int p1 = static_cast<int>((static_cast<long long>(N) * (wave + 1)) / kRowWaves);
+      const int p0 = static_cast<int>((static_cast<long long>(N) * wave) / GW);
+      const int p1 = static_cast<int>((static_cast<long long>(N) * (wave + 1)) / GW);
       if (p0 < p1) {
         float* cw = carry + wave * D;
         int* ctw = carry_t + wave;
-        if (p1 <= kStageCap)
-          gather_range<DT, LB, false>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid, qsb);
+        if (p1 <= CAP)
+          gather_range<DT, LB, false, CAP>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid,
+                                           qsb);
         else
-          gather_range<DT, LB, true>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid, qsb);
+          gather_range<DT, LB, true, CAP>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid,
+                                          qsb);
       }
     }
     // the prefetched values are first used here (the barrier keeps every use,
@@ -1032,51 +1076,51 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     asm volatile("" : "+v"(nx0), "+v"(nx1), "+v"(ne0));
     bool next_empty = false;
     if (has_next && tid < T) {
-      publish_bag(a, tid, b + 1, nx0, nx1, nbeg, npos);
+      publish_bag(a, tid, bn, nx0, nx1, nbeg, npos);
       next_empty = npos[tid + 1] == 0;
     }
     __syncthreads();
 
     // bags cut by a range boundary: add the later parts in wave order; scan the next positions
-    for (int d = tid; d < D; d += kRowThreads) {
-      for (int w = 1; w < kRowWaves; ++w) {
+    for (int d = tid; d < D; d += NT) {
+      for (int w = 1; w < GW; ++w) {
         const int t = carry_t[w];
         if (t >= 0) Z[(1 + t) * LD + d] += carry[w * D + d];
       }
     }
-    if (has_next && wave == kRowWaves - 1) scan_positions(npos, T, tid);
+    if (has_next && wave == GW - 1) scan_positions(npos, T, tid);
     __syncthreads();
 
     // next sample's index loads go out now; their values are staged after the output
     int r[kStagePerThread], tb[kStagePerThread];
     // (issued unconditionally, with no positions when there is no next sample:
     // every load stays in bounds and no branch merges the registers)
-    load_stage(a, nbeg, npos, T, has_next ? rfl(npos[T]) : 0, r, tb, tid);
+    load_stage<NT>(a, nbeg, npos, T, has_next ? rfl(npos[T]) : 0, r, tb, tid);
 
     // pooled output (if requested) from the final fp32 Z
-    if (a.out_pooled) {
+    if (a.out_pooled && active) {
       float* op = a.out_pooled + static_cast<size_t>(b) * T * D;
-      for (int i = tid; i < T * D; i += kRowThreads) {
+      for (int i = tid; i < T * D; i += NT) {
         const int t = i / D, d = i - t * D;
         op[i] = Z[(1 + t) * LD + d];
       }
     }
     // interaction into the output staging area (which overlays the index stage)
-    for (int d = tid; d < D; d += kRowThreads) outs[d] = Z[d];
+    for (int d = tid; d < D; d += NT) outs[d] = Z[d];
     if constexpr (MFMA) {
       // e0 dots in fp32, then the pooled rows are split in place for the Gram
-      e0_dots(Z, LD, D, T, outs, tid);
-      split_rows(Z, LD, D, L.Tp, tid);
+      e0_dots<NT>(Z, LD, D, T, outs, tid);
+      split_rows<NT>(Z, LD, D, L.Tp, tid);
       const int nt = L.Tp / 32;
       const int ntiles = nt * (nt + 1) / 2;
-      for (int tile = wave; tile < ntiles; tile += kRowWaves) {
+      for (int tile = wave; tile < ntiles; tile += GW) {
         int I, J;
         block_pair(tile, I, J);
         gram_tile_mfma(Z, LD, D, T, I, J, outs, tid);
       }
     } else {  // fp32 dots, one 4x4 block of pairs per 16 lanes
       const int nb = (T + 1 + 3) >> 2;
-      for (int u = tid >> 4; u < nb * (nb + 1) / 2; u += kRowThreads / 16) {
+      for (int u = tid >> 4; u < nb * (nb + 1) / 2; u += NT / 16) {
         int bi, bj;
         block_pair(u, bi, bj);
         dots_block16<true>(Z, T + 1, D, LD, bi, bj, tid & 15, outs + D);
@@ -1087,18 +1131,20 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     // take them now, before the output stores are queued behind them
 #pragma unroll
     for (int k = 0; k < kStagePerThread; ++k) asm volatile("" : "+v"(r[k]));
-    float* o = a.out_inter + static_cast<size_t>(b) * W;
-    for (int i = tid; i < W; i += kRowThreads) store_stream(o + i, outs[i]);
+    if (active) {
+      float* o = a.out_inter + static_cast<size_t>(b) * W;
+      for (int i = tid; i < W; i += NT) store_stream(o + i, outs[i]);
+    }
     __syncthreads();
 
     // stage the next sample: indices, cleared Z with its e0, no carries
     if (has_next) {
-      write_stage(a, r, tb, stage, sbag, trows, tid);
+      write_stage<NT>(a, r, tb, stage, sbag, trows, tid);
       if (next_empty) {
         float* z = Z + (1 + tid) * LD;
         for (int d = 0; d < D; d += 4) *reinterpret_cast<float4*>(z + d) = make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      if (tid < kRowWaves) carry_t[tid] = -1;
+      if (tid < GW) carry_t[tid] = -1;
       if (tid < D) Z[tid] = ne0;
       __syncthreads();
     }
@@ -1156,29 +1202,58 @@ static int resident_blocks(K kernel, size_t lds) {
 
 constexpr int kLongSampleRows = 512;  // average rows per sample from which a workgroup takes one sample
 
-template <int DT, int LB, bool MFMA>
-static hipError_t launch_rows_v(const FwdArgs& a, const RowLayout& L, hipStream_t st) {
-  auto kernel = fused_rows_kernel<DT, LB, MFMA>;
-  // Short samples: two per workgroup, the second sample's offsets, e0 and
+// Sample groups per workgroup for short samples: as many as keep a group's
+// threads covering the bags and e0 (G * max(T, D) <= 512), the staged indices
+// covering a typical sample with room to spare, the LDS within one CU's, and
+// at least 64 workgroups of G samples.
+static int pick_groups(const FwdArgs& a, bool mfma) {
+  if (a.nnz >= static_cast<int64_t>(kLongSampleRows) * a.B) return 1;
+  const int64_t avg = a.nnz / a.B;  // rows per sample
+  const int wide = a.T > a.D ? a.T : a.D;
+  for (int G = 8; G > 1; G /= 2) {
+    if (G * wide > kRowThreads) continue;
+    if (avg * 3 / 2 > kStageCap / G) continue;
+    if (static_cast<size_t>(make_row_layout(a.T, a.D, mfma, G).bytes) > kMaxLds) continue;
+    if (a.B < G * 64) continue;
+    return G;
+  }
+  return 1;
+}
+
+template <int DT, int LB, bool MFMA, int G>
+static hipError_t launch_rows_g(const FwdArgs& a, hipStream_t st) {
+  const RowLayout L = make_row_layout(a.T, a.D, MFMA, G);
+  auto kernel = fused_rows_kernel<DT, LB, MFMA, G>;
+  // Short samples: two steps per workgroup, the second step's offsets, e0 and
   // indices fetched while the first is gathered. Long samples (hundreds of
   // rows): one per workgroup, which keeps the end of the launch short (the
   // hardware dispatcher hands the many short-lived workgroups to free slots).
   const bool long_samples = a.nnz >= static_cast<int64_t>(kLongSampleRows) * a.B;
-  const int chunk = (!long_samples && a.B >= 2 * resident_blocks(kernel, static_cast<size_t>(L.bytes))) ? 2 : 1;
+  const int steps = (!long_samples && a.B >= 2 * G * resident_blocks(kernel, static_cast<size_t>(L.bytes))) ? 2 : 1;
+  const int chunk = G * steps;
   const int grid = (a.B + chunk - 1) / chunk;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kRowThreads), L.bytes, st, a, L, chunk);
   return hipGetLastError();
 }
 
+template <int DT, int LB, bool MFMA>
+static hipError_t launch_rows_m(const FwdArgs& a, hipStream_t st) {
+  switch (pick_groups(a, MFMA)) {
+    case 8: return launch_rows_g<DT, LB, MFMA, 8>(a, st);
+    case 4: return launch_rows_g<DT, LB, MFMA, 4>(a, st);
+    case 2: return launch_rows_g<DT, LB, MFMA, 2>(a, st);
+    default: return launch_rows_g<DT, LB, MFMA, 1>(a, st);
+  }
+}
+
 template <int DT, int LB>
 static hipError_t launch_rows(const FwdArgs& a, hipStream_t st) {
   const bool mfma = use_mfma(a.T, a.D, DT);
-  const RowLayout L = make_row_layout(a.T, a.D, mfma);
-  if (static_cast<size_t>(L.bytes) > kMaxLds) return hipErrorInvalidValue;
+  if (static_cast<size_t>(make_row_layout(a.T, a.D, mfma).bytes) > kMaxLds) return hipErrorInvalidValue;
   if constexpr (DT != DLRM_F32) {
-    if (mfma) return launch_rows_v<DT, LB, true>(a, L, st);
+    if (mfma) return launch_rows_m<DT, LB, true>(a, st);
   }
-  return launch_rows_v<DT, LB, false>(a, L, st);
+  return launch_rows_m<DT, LB, false>(a, st);
 }
 
 template <int DT, int LPR>

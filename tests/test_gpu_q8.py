@@ -59,7 +59,7 @@ def _oracle(w, q8, lengths, indices, e0):
 
 @pytest.mark.parametrize("T,rows,D,B,seed", [(8, 5000, 128, 256, 61), (26, 3000, 256, 200, 62),
                                              (64, 2000, 128, 96, 63), (4, 500, 512, 64, 64),
-                                             (30, 800, 512, 40, 65)])
+                                             (30, 800, 512, 40, 65), (8, 3000, 128, 600, 66)])
 def test_q8_forward(T, rows, D, B, seed):
     w = synth.Workload("q8", T=T, rows=rows, D=D, dtype="bf16", B=B, bag=("uniform", 0, 20), dist=("zipf", 1.05),
                        seed=seed)
@@ -142,7 +142,7 @@ def _run_t(w):
 
 @pytest.mark.parametrize("T,rows,D,B,seed", [(8, 5000, 128, 256, 71), (26, 3000, 256, 200, 72),
                                              (64, 2000, 128, 96, 73), (4, 500, 512, 64, 74),
-                                             (30, 800, 512, 40, 75)])
+                                             (30, 800, 512, 40, 75), (8, 3000, 128, 600, 76)])
 def test_q8t_forward(T, rows, D, B, seed):
     w = synth.Workload("q8t", T=T, rows=rows, D=D, dtype="bf16", B=B, bag=("uniform", 0, 20), dist=("zipf", 1.05),
                        seed=seed)
