@@ -7,7 +7,8 @@
 //    upstream gradient of pair (i, j) at (i, j) and (j, i), zero diagonal;
 //    dL/dpooled[b][t] = dZ[b][1 + t], dL/de0[b] = d_out[b][:D] + dZ[b][0].
 // 2. keys: occurrence p of bag (t, b) gets key base_t + index (its global row)
-//    and value p; an out-of-range index gets the sentinel key sum(rows).
+//    and value p; an out-of-range index, or a position no bag covers (invalid
+//    offsets), gets the sentinel key sum(rows).
 // 3. stable LSD radix sort of (key, p), 8 bits per pass: per-tile digit counts,
 //    a device-wide scan of the digit-major count table, a stable scatter that
 //    ranks equal digits inside a wave with ballots.
@@ -147,20 +148,8 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
 }
 
 // ---------------------------------------------------------------------------
-// 2. keys (one thread per bag, table-major bag order = CSR order)
+// 2. keys (a group of lanes per bag, table-major bag order = CSR order)
 // ---------------------------------------------------------------------------
-// Occurrences no bag covers (possible only with invalid offsets) keep the sentinel key.
-__global__ __launch_bounds__(kBwdThreads) void fill_sentinel(int32_t* __restrict__ keys, int32_t* __restrict__ vals,
-                                                             int32_t* __restrict__ bag_of, long long n,
-                                                             int32_t sentinel) {
-  const long long i = static_cast<long long>(blockIdx.x) * kBwdThreads + threadIdx.x;
-  if (i < n) {
-    keys[i] = sentinel;
-    vals[i] = static_cast<int32_t>(i);
-    bag_of[i] = 0;
-  }
-}
-
 // LG lanes per bag (a power of two, 1..64): lane k of a bag's group handles
 // its occurrences k, k + LG, ... so loads and stores are contiguous across the
 // group; LG follows the average bag length.
@@ -181,7 +170,22 @@ __global__ __launch_bounds__(kBwdThreads) void build_keys(MutTableArgs tabs, int
   if (j == static_cast<long long>(T) * B - 1 && s1 != nnz) bad_off = true;
   if (s0 < 0) { s0 = 0; bad_off = true; }
   if (s0 > nnz) { s0 = nnz; bad_off = true; }
+  if (s1 < 0) { s1 = 0; bad_off = true; }
   if (s1 > nnz) { s1 = nnz; bad_off = true; }
+  // Every position in [first offset, last offset) lies in some bag (bag j holds
+  // [o_j, max(o_j, o_j+1)) once clamped into [0, nnz]: a position x is in bag j
+  // for the last j with o_j <= x). The positions before the first offset or
+  // from the last offset on belong to no bag: the first and the last bag give
+  // them the sentinel key (only with invalid offsets).
+  auto fill_gap = [&](long long g0, long long g1) {
+    for (long long p = g0 + sub; p < g1; p += LG) {
+      keys[p] = sentinel;
+      vals[p] = static_cast<int32_t>(p);
+      bag_of[p] = 0;
+    }
+  };
+  if (j == 0) fill_gap(0, s0);
+  if (j == static_cast<long long>(T) * B - 1) fill_gap(s1, nnz);
   if (s1 < s0) { s1 = s0; bad_off = true; }
   if (bad_off && sub == 0) flag(status, DLRM_STATUS_BAD_OFFSETS);
   const int rows = tabs.rows[t], base = tabs.base[t];
@@ -933,8 +937,6 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   }
   const int32_t sentinel = static_cast<int32_t>(a.total_rows);
   // 2. keys
-  hipLaunchKernelGGL(fill_sentinel, dim3(static_cast<unsigned>((n + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads), 0,
-                     st, keys[0], vals[0], bag_of, n, sentinel);
   {
     const long long nb = static_cast<long long>(a.T) * a.B;
     const long long avg = n / nb;  // lanes per bag: the average bag length, rounded down to a power of two

@@ -147,6 +147,38 @@ def test_backward_sort_and_segment_paths(B, bag):
     run_bwd(w, lr=0.01)
 
 
+def test_backward_positions_outside_every_bag_are_skipped():
+    """Offsets that start at 3 and end 5 short of nnz (invalid, flagged): the positions
+    before the first offset and from the last one on belong to no bag and add nothing."""
+    w = synth.Workload("gaps", T=3, rows=200, D=32, dtype="f32", B=50, bag=("uniform", 0, 8),
+                       dist=("zipf", 1.1), seed=91)
+    b = synth.make_batch(w, with_dout=True)
+    db = DeviceBatch(b)
+    pooled, _ = db.fwd(want_pooled=True)
+    d_out = torch.from_numpy(b.dout).cuda()
+    rng = np.random.default_rng(5)
+    off = orc.lengths_to_offsets(b.lengths)
+    nnz = len(b.indices)
+    # three extra occurrences in front, five behind: the offsets shift by 3 and nnz grows by 8
+    idx = np.concatenate([rng.integers(0, 200, 3), b.indices, rng.integers(0, 200, 5)]).astype(np.int32)
+    off_dev = torch.from_numpy((off + 3).astype(np.int32)).cuda()
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    before = [t.clone() for t in db.tables]
+    res = ops.embbag_bwd_update(db.tables, off_dev, torch.from_numpy(idx).cuda(), w.B, db.e0, pooled, d_out, 0.01,
+                                status=st)
+    torch.cuda.synchronize()
+    assert st.item() & ops.STATUS_BAD_OFFSETS
+    # the same update as the valid batch
+    tabs2 = [t.clone() for t in before]
+    ops.embbag_bwd_update(tabs2, db.offsets, db.indices, w.B, db.e0, pooled, d_out, 0.01)
+    torch.cuda.synchronize()
+    for t1, t2 in zip(db.tables, tabs2):
+        assert torch.equal(t1, t2)
+    assert int(res["num_unique"].item()) == len(np.unique(b.indices + np.repeat(
+        np.array([0, 200, 400]), [int(b.lengths[t * w.B:(t + 1) * w.B].sum()) for t in range(w.T)])))
+    assert nnz + 8 == len(idx)
+
+
 def test_backward_hot_rows_span_many_chunks():
     """Multi-hot fp16 bags with a Zipf(1.1) hot row per table: its occurrences fill
     dozens of consecutive reduction chunks, whose partial sums are chained in order
