@@ -10,14 +10,16 @@
 //    and value p; an out-of-range index, or a position no bag covers (invalid
 //    offsets), gets the sentinel key sum(rows).
 // 3. stable LSD radix sort of (key, p), 8 bits per pass: per-tile digit counts,
-//    a device-wide scan of the digit-major count table, a stable scatter that
-//    ranks equal digits inside a wave with ballots.
-// 4. segments: head flags (key differs from its predecessor), scanned into the
-//    position of each distinct key.
+//    each tile's digit offsets (from the digit-major count table, summed inside
+//    the scatter for up to 128 tiles, else scanned per digit by one kernel), a
+//    stable scatter that ranks equal digits inside a wave with ballots. The
+//    last pass also writes each sorted position's bag.
+// 4. segments (API outputs only): head flags (key differs from its
+//    predecessor), scanned into the position of each distinct key.
 // 5. segmented sums of the rows dL/dpooled over the sorted occurrences, in
 //    fixed chunks of positions whatever the segment lengths (a fixed order, so
 //    the result is deterministic), then W <- W - lr * G in fp32, rounded once
-//    to the table's storage type.
+//    to the table's storage type (or the row-wise AdaGrad step).
 #include <algorithm>
 
 #include "scan_impl.h"
