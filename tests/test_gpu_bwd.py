@@ -138,6 +138,21 @@ def test_backward_many_keys_four_radix_passes():
     run_bwd(w, lr=0.01)
 
 
+@pytest.mark.parametrize("T,rows,B,bag", [
+    (1, 200, 300, ("uniform", 0, 12)),  # 8-bit keys: one pass
+    (3, 500, 300, ("uniform", 0, 12)),  # 11 bits: two passes
+    (2, 50_000, 900, ("uniform", 0, 12)),  # 17 bits: three passes
+    (3, 1_000_000, 2000, ("uniform", 10, 14)),  # 22 bits, 36 tiles
+    (2, 5_000_000, 500, ("uniform", 0, 12)),  # 24 bits: three passes, the last digit full
+])
+def test_backward_sort_pass_counts(T, rows, B, bag):
+    """The sort takes as many 8-bit passes as the key width needs (the sentinel
+    sum(rows) included): one to three passes here, four in the test above."""
+    w = synth.Workload("passes", T=T, rows=rows, D=8, dtype="f32", B=B, bag=bag, dist=("zipf", 1.05),
+                       seed=rows % 997 + B)
+    run_bwd(w, lr=0.01)
+
+
 @pytest.mark.parametrize("B,bag", [(2100, ("uniform", 60, 70)), (8200, ("uniform", 62, 68))])
 def test_backward_sort_and_segment_paths(B, bag):
     """About 273K occurrences (134 sort tiles of 2048: the sort's offsets come from a
@@ -177,6 +192,45 @@ def test_backward_positions_outside_every_bag_are_skipped():
     assert int(res["num_unique"].item()) == len(np.unique(b.indices + np.repeat(
         np.array([0, 200, 400]), [int(b.lengths[t * w.B:(t + 1) * w.B].sum()) for t in range(w.T)])))
     assert nnz + 8 == len(idx)
+
+
+@pytest.mark.parametrize("T,rows,B", [(3, 200, 50), (26, 40_000, 300)])
+def test_backward_overlapping_bags_stay_in_bounds(T, rows, B):
+    """Offsets that decrease (invalid, flagged) make later bags cover positions that an
+    earlier bag already covers. The call still finishes in bounds: the status carries
+    the flag, rows that no index references stay bit-identical, the distinct rows are
+    strictly increasing keys of referenced rows, and d_e0 is the interaction gradient."""
+    w = synth.Workload("overlap", T=T, rows=rows, D=32, dtype="f32", B=B, bag=("uniform", 1, 8),
+                       dist=("zipf", 1.1), seed=T + B)
+    b = synth.make_batch(w, with_dout=True)
+    db = DeviceBatch(b)
+    pooled, _ = db.fwd(want_pooled=True)
+    d_out = torch.from_numpy(b.dout).cuda()
+    off = orc.lengths_to_offsets(b.lengths).astype(np.int64)
+    # bag 4 now runs to the end of bag 8; bag 5 (from there to its old end) is empty
+    # and bags 6..8 are covered twice
+    bad = off.copy()
+    bad[5] = off[9]
+    assert bad[5] > bad[6] > bad[4]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    before = [t.clone() for t in db.tables]
+    res = ops.embbag_bwd_update(db.tables, torch.from_numpy(bad.astype(np.int32)).cuda(), db.indices, w.B, db.e0,
+                                pooled, d_out, 0.01, status=st)
+    ref = ops.embbag_bwd_update([t.clone() for t in before], db.offsets, db.indices, w.B, db.e0, pooled, d_out, 0.01)
+    torch.cuda.synchronize()
+    assert st.item() & ops.STATUS_BAD_OFFSETS
+    assert torch.equal(res["d_e0"], ref["d_e0"])
+    base = np.arange(T + 1, dtype=np.int64) * rows
+    U = int(res["num_unique"].item())
+    uk = res["unique_keys"].cpu().numpy()[:U].astype(np.int64)
+    assert np.all(np.diff(uk) > 0)
+    for t in range(T):
+        referenced = np.zeros(rows, dtype=bool)
+        referenced[b.indices[off[t * B]:off[(t + 1) * B]]] = True
+        mine = uk[(uk >= base[t]) & (uk < base[t + 1])] - base[t]
+        assert referenced[mine].all()
+        untouched = torch.from_numpy(~referenced).cuda()
+        assert torch.equal(before[t][untouched], db.tables[t][untouched])
 
 
 def test_backward_hot_rows_span_many_chunks():
