@@ -6,6 +6,9 @@
 //    Z[j], so dZ[b] = S[b] Z[b] with S[b] the symmetric F x F matrix holding the
 //    upstream gradient of pair (i, j) at (i, j) and (j, i), zero diagonal;
 //    dL/dpooled[b][t] = dZ[b][1 + t], dL/de0[b] = d_out[b][:D] + dZ[b][0].
+//    One workgroup per sample; in the sparse backward these workgroups ride as
+//    extras on the sort's scatter launches and the segment build, since
+//    nothing before the reduce reads dZ.
 // 2. keys: occurrence p of bag (t, b) gets key base_t + index (its global row)
 //    and value p; an out-of-range index, or a position no bag covers (invalid
 //    offsets), gets the sentinel key sum(rows).
@@ -39,20 +42,39 @@ constexpr int kRadixRounds = kRadixTile / kRadixWaves / kWave;  // rounds of 64 
 // ---------------------------------------------------------------------------
 // With self-pairs the pair (i, i) sits at i(i+1)/2 + i and its gradient counts
 // twice on the diagonal of S (d(Z_i . Z_i)/dZ_i = 2 Z_i).
-__global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B, int D, bool self_pairs,
-                                                                   const float* __restrict__ e0,
-                                                                   const float* __restrict__ pooled,
-                                                                   const float* __restrict__ d_out,
-                                                                   float* __restrict__ d_pooled,
-                                                                   float* __restrict__ d_e0) {
-  extern __shared__ __align__(16) float smem[];
+//
+// Sample b's interaction backward by one workgroup, with smem holding
+// F*(D+4) + Fp*F floats. The standalone kernel runs one sample per workgroup;
+// inside the sparse backward the samples are shared out as extra workgroups
+// of the key build and sort launches (IbwdShare), whose own few workgroups
+// leave most of the chip idle, so this work overlaps the sort's chain of
+// launches instead of running before it.
+struct IbwdShare {
+  int T, D;
+  bool self_pairs;
+  const float* e0;
+  const float* pooled;
+  const float* d_out;
+  float* d_pooled;
+  float* d_e0;
+  int first;  // the sample of the first extra workgroup
+  int count;  // extra workgroups (samples) of this launch
+};
+
+__device__ __forceinline__ void interact_bwd_sample(const IbwdShare& ia, int b, float* smem) {
+  const int T = ia.T, D = ia.D;
+  const bool self_pairs = ia.self_pairs;
+  const float* __restrict__ e0 = ia.e0;
+  const float* __restrict__ pooled = ia.pooled;
+  const float* __restrict__ d_out = ia.d_out;
+  float* __restrict__ d_pooled = ia.d_pooled;
+  float* __restrict__ d_e0 = ia.d_e0;
   const int F = T + 1;
   const int LD = D + 4;
   const int W = D + (self_pairs ? F * (F + 1) / 2 : F * (F - 1) / 2);
   const int Fp = (F + 3) & ~3;    // S rows, padded with zeros to whole blocks of 4
   float* Z = smem;                // [F][LD]
   float* S = smem + F * LD;       // [Fp][F]
-  const int b = xcd_block(blockIdx.x, gridDim.x);
   const int D4 = D / 4;
   // Z and S are filled in batches whose loads are all issued before the first
   // LDS store, so a batch costs one memory round trip, not one per element; the
@@ -149,6 +171,20 @@ __global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(int T, int B,
   }
 }
 
+__global__ __launch_bounds__(kBwdThreads) void interact_bwd_kernel(IbwdShare ia) {
+  extern __shared__ __align__(16) float smem[];
+  interact_bwd_sample(ia, ia.first + xcd_block(blockIdx.x, gridDim.x), smem);
+}
+
+// In a launch with own_blocks workgroups of its own: the extra workgroups take
+// samples ia.first + (blockIdx.x - own_blocks). Returns true for those.
+__device__ __forceinline__ bool ibwd_extra(const IbwdShare& ia, int own_blocks) {
+  if (static_cast<int>(blockIdx.x) < own_blocks) return false;
+  extern __shared__ __align__(16) float smem[];
+  interact_bwd_sample(ia, ia.first + static_cast<int>(blockIdx.x) - own_blocks, smem);
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // 2. keys (a group of lanes per bag, table-major bag order = CSR order)
 // ---------------------------------------------------------------------------
@@ -160,7 +196,8 @@ __global__ __launch_bounds__(kBwdThreads) void build_keys(MutTableArgs tabs, int
                                                           const int32_t* __restrict__ indices, long long nnz,
                                                           int32_t sentinel, int32_t* __restrict__ keys,
                                                           int32_t* __restrict__ vals, int32_t* __restrict__ bag_of,
-                                                          int32_t* status) {
+                                                          int32_t* status, int own_blocks, IbwdShare ia) {
+  if (ibwd_extra(ia, own_blocks)) return;
   const long long g = static_cast<long long>(blockIdx.x) * kBwdThreads + threadIdx.x;
   const long long j = g / LG;
   const int sub = static_cast<int>(g % LG);
@@ -219,7 +256,8 @@ __global__ __launch_bounds__(kBwdThreads) void build_keys(MutTableArgs tabs, int
 // 3. radix sort
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBwdThreads) void radix_count(const int32_t* __restrict__ keys, long long n, int shift,
-                                                           int ntiles, int32_t* __restrict__ counts) {
+                                                           int ntiles, int32_t* __restrict__ counts, IbwdShare ia) {
+  if (ibwd_extra(ia, ntiles)) return;
   __shared__ int hist[kRadixBins];
   hist[threadIdx.x] = 0;
   __syncthreads();
@@ -321,7 +359,8 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
                                                              int32_t* __restrict__ keys_out,
                                                              int32_t* __restrict__ vals_out,
                                                              const int32_t* __restrict__ bag_of,
-                                                             int32_t* __restrict__ src_out) {
+                                                             int32_t* __restrict__ src_out, IbwdShare ia) {
+  if (ibwd_extra(ia, ntiles)) return;
   __shared__ int wcount[kRadixWaves][kRadixBins];
   __shared__ int gbase[kRadixBins];
   __shared__ int lds4[kRadixWaves];
@@ -432,7 +471,10 @@ __global__ __launch_bounds__(kScanThreads) void build_segments_chunked(const int
                                                                       int32_t* __restrict__ pos,
                                                                       int32_t* __restrict__ unique_keys,
                                                                       int32_t* __restrict__ seg_offsets,
-                                                                      int32_t* __restrict__ num_unique) {
+                                                                      int32_t* __restrict__ num_unique, int nchunks,
+                                                                      IbwdShare ia) {
+  static_assert(kScanThreads == kBwdThreads, "extra workgroups run the interaction backward");
+  if (ibwd_extra(ia, nchunks)) return;
   __shared__ long long lds[kScanThreads / kWave];
   const long long c0 = static_cast<long long>(blockIdx.x) * kScanChunk + threadIdx.x * kScanPerThread;
   // totals of the earlier chunks (at most 256, one per thread)
@@ -476,7 +518,7 @@ __global__ __launch_bounds__(kScanThreads) void build_segments_chunked(const int
     }
     ex += h[j];
   }
-  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) pos[n] = static_cast<int32_t>(tot_before + chunk_tot);
+  if (static_cast<int>(blockIdx.x) == nchunks - 1 && threadIdx.x == 0) pos[n] = static_cast<int32_t>(tot_before + chunk_tot);
 }
 
 __global__ void zero_segments(int32_t* seg_offsets, int32_t* num_unique) {
@@ -893,13 +935,18 @@ hipError_t launch_reduce_dt(const BwdArgs& a, const WsLayout& L, char* ws, const
 
 }  // namespace
 
+// LDS of one sample's interaction backward: Z [F][D+4] and S [Fp][F] fp32
+static size_t ibwd_lds(int T, int D) {
+  const int F = T + 1;
+  return (static_cast<size_t>(F) * (D + 4) + static_cast<size_t>((F + 3) & ~3) * F) * 4;
+}
+
 hipError_t launch_interact_bwd(int T, int B, int D, bool self_pairs, const float* e0, const float* pooled,
                                const float* d_out, float* d_e0, float* d_pooled, hipStream_t st) {
-  const int F = T + 1;
-  const size_t lds = (static_cast<size_t>(F) * (D + 4) + static_cast<size_t>((F + 3) & ~3) * F) * 4;
+  const size_t lds = ibwd_lds(T, D);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(interact_bwd_kernel, dim3(B), dim3(kBwdThreads), lds, st, T, B, D, self_pairs, e0, pooled, d_out,
-                     d_pooled, d_e0);
+  const IbwdShare ia{T, D, self_pairs, e0, pooled, d_out, d_pooled, d_e0, 0, B};
+  hipLaunchKernelGGL(interact_bwd_kernel, dim3(B), dim3(kBwdThreads), lds, st, ia);
   return hipGetLastError();
 }
 
@@ -924,29 +971,44 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   int32_t* seg = a.seg_offsets ? a.seg_offsets : reinterpret_cast<int32_t*>(ws + L.seg);
   int32_t* nuniq = a.num_unique ? a.num_unique : reinterpret_cast<int32_t*>(ws + L.nuniq);
 
-  // 1. interaction backward
-  {
-    const int F = a.T + 1;
-    const size_t lds = (static_cast<size_t>(F) * (a.D + 4) + static_cast<size_t>((F + 3) & ~3) * F) * 4;
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(interact_bwd_kernel, dim3(a.B), dim3(kBwdThreads), lds, st, a.T, a.B, a.D, false, a.e0, a.pooled,
-                       a.d_out, d_pooled, a.d_e0);
-  }
   const long long n = a.nnz;
-  if (n == 0) {
+  const size_t ilds = ibwd_lds(a.T, a.D);
+  if (ilds > 160 * 1024) return hipErrorInvalidValue;
+  if (n == 0) {  // 1. interaction backward on its own; no keys
+    const hipError_t e = launch_interact_bwd(a.T, a.B, a.D, false, a.e0, a.pooled, a.d_out, a.d_e0, d_pooled, st);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(zero_segments, dim3(1), dim3(64), 0, st, seg, nuniq);
     return hipGetLastError();
   }
+  // 1. interaction backward, its samples shared out as extra workgroups over
+  // the sort passes' scatter launches (the longest of the sort; a share takes
+  // about as long as a scatter, and much longer than a count) and the one-pass
+  // segment build; nothing before the reduce reads its outputs
+  const int passes = radix_passes(a.total_rows);
+  const bool want_segments = a.unique_keys || a.seg_offsets || a.num_unique;
+  const long long nscan = scan_chunks(n);
+  const bool seg_one_pass = want_segments && nscan <= kScanThreads;
+  const int nshare = passes + (seg_one_pass ? 1 : 0);
+  int ishare = 0;
+  const IbwdShare none{a.T, a.D, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
+  auto share = [&]() {
+    IbwdShare ia{a.T, a.D, false, a.e0, a.pooled, a.d_out, d_pooled, a.d_e0, 0, 0};
+    ia.first = static_cast<int>(static_cast<long long>(a.B) * ishare / nshare);
+    ia.count = static_cast<int>(static_cast<long long>(a.B) * (ishare + 1) / nshare) - ia.first;
+    ++ishare;
+    return ia;
+  };
   const int32_t sentinel = static_cast<int32_t>(a.total_rows);
   // 2. keys
   {
     const long long nb = static_cast<long long>(a.T) * a.B;
     const long long avg = n / nb;  // lanes per bag: the average bag length, rounded down to a power of two
     const int lg = avg >= 64 ? 64 : avg >= 32 ? 32 : avg >= 16 ? 16 : avg >= 8 ? 8 : avg >= 4 ? 4 : avg >= 2 ? 2 : 1;
-    const dim3 g(static_cast<unsigned>((nb * lg + kBwdThreads - 1) / kBwdThreads)), blk(kBwdThreads);
+    const int own = static_cast<int>((nb * lg + kBwdThreads - 1) / kBwdThreads);
+    const dim3 g(static_cast<unsigned>(own)), blk(kBwdThreads);
 #define DLRM_BUILD_KEYS(L) \
-  hipLaunchKernelGGL(build_keys<L>, g, blk, 0, st, a.tabs, a.T, a.B, a.offsets, a.indices, n, sentinel, keys[0], vals[0], \
-                     bag_of, a.status)
+  hipLaunchKernelGGL(build_keys<L>, g, blk, 0, st, a.tabs, a.T, a.B, a.offsets, a.indices, n, sentinel, keys[0], \
+                     vals[0], bag_of, a.status, own, none)
     switch (lg) {
       case 64: DLRM_BUILD_KEYS(64); break;
       case 32: DLRM_BUILD_KEYS(32); break;
@@ -960,11 +1022,10 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   }
   // 3. radix sort, 8 bits per pass
   const int ntiles = static_cast<int>((n + kRadixTile - 1) / kRadixTile);
-  const int passes = radix_passes(a.total_rows);
   int cur = 0;
   for (int p = 0; p < passes; ++p) {
     const int shift = p * kRadixBits;
-    hipLaunchKernelGGL(radix_count, dim3(ntiles), dim3(kBwdThreads), 0, st, keys[cur], n, shift, ntiles, counts);
+    hipLaunchKernelGGL(radix_count, dim3(ntiles), dim3(kBwdThreads), 0, st, keys[cur], n, shift, ntiles, counts, none);
     const bool inline_scan = ntiles <= kInlineScanTiles;
     if (!inline_scan) {
       hipLaunchKernelGGL(radix_row_scan, dim3(kRadixBins), dim3(kScanThreads), 0, st, counts, ntiles, digit_off,
@@ -974,22 +1035,24 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
     int32_t* vout = (p + 1 == passes && a.perm) ? a.perm : vals[cur ^ 1];
     // ... and each sorted position's bag (for the reduce)
     const bool last_pass = p + 1 == passes;
-    hipLaunchKernelGGL(radix_scatter, dim3(ntiles), dim3(kBwdThreads), 0, st, keys[cur], vals[cur], n, shift, ntiles,
-                       counts, inline_scan ? nullptr : digit_off, row_total, keys[cur ^ 1], vout, bag_of,
-                       last_pass ? src_bag : nullptr);
+    const IbwdShare ia_scatter = share();
+    hipLaunchKernelGGL(radix_scatter, dim3(ntiles + ia_scatter.count), dim3(kBwdThreads), ilds, st, keys[cur], vals[cur],
+                       n, shift, ntiles, counts, inline_scan ? nullptr : digit_off, row_total, keys[cur ^ 1], vout,
+                       bag_of, last_pass ? src_bag : nullptr, ia_scatter);
     cur ^= 1;
   }
   const int32_t* skeys = keys[cur];
   // radix_passes() >= 1, so the last pass wrote a.perm (if given) and src_bag
   // 4. segments: outputs only (the reduce reads the sorted keys), so built only
   // when the caller asks for any of them
-  if (a.unique_keys || a.seg_offsets || a.num_unique) {
-    const long long m = scan_chunks(n);
-    if (m <= kScanThreads) {  // chunk totals, then one pass that scans and builds the segments
+  if (want_segments) {
+    const long long m = nscan;
+    if (seg_one_pass) {  // chunk totals, then one pass that scans and builds the segments
       hipLaunchKernelGGL((scan_chunk_totals<HeadIn>), dim3(static_cast<unsigned>(m)), dim3(kScanThreads), 0, st,
                          HeadIn{skeys, sentinel}, n, partial);
-      hipLaunchKernelGGL(build_segments_chunked, dim3(static_cast<unsigned>(m)), dim3(kScanThreads), 0, st, skeys, n,
-                         sentinel, partial, pos, uniq, seg, nuniq);
+      const IbwdShare ia_seg = share();
+      hipLaunchKernelGGL(build_segments_chunked, dim3(static_cast<unsigned>(m) + ia_seg.count), dim3(kScanThreads), ilds,
+                         st, skeys, n, sentinel, partial, pos, uniq, seg, nuniq, static_cast<int>(m), ia_seg);
     } else {
       hipError_t e = device_exclusive_scan(HeadIn{skeys, sentinel}, n, pos, partial, a.status, 0, st);
       if (e != hipSuccess) return e;
