@@ -18,7 +18,9 @@
 //    stable scatter that ranks equal digits inside a wave with ballots. The
 //    last pass also writes each sorted position's bag.
 // 4. segments (API outputs only): head flags (key differs from its
-//    predecessor), scanned into the position of each distinct key.
+//    predecessor), scanned into the position of each distinct key. With few
+//    reduce chunks the reduce counts each chunk's heads and the combine step
+//    writes the outputs (no launches of their own).
 // 5. segmented sums of the rows dL/dpooled over the sorted occurrences, in
 //    fixed chunks of positions whatever the segment lengths (a fixed order, so
 //    the result is deterministic), then W <- W - lr * G in fp32, rounded once
@@ -655,7 +657,8 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
                                                                  const int32_t* __restrict__ src_bag,
                                                                  const float* __restrict__ d_pooled, float lr,
                                                                  float* __restrict__ carry, float* __restrict__ head,
-                                                                 int32_t* __restrict__ chunk_flags, long long nchunks) {
+                                                                 int32_t* __restrict__ chunk_flags, long long nchunks,
+                                                                 int32_t* __restrict__ hcount) {
   static_assert(C <= kWave, "one lane per chunk position");
   __shared__ int sbase[DLRM_MAX_TABLES];  // first global key of each table
   for (int t = threadIdx.x; t < T; t += kBwdThreads) sbase[t] = tabs.base[t];
@@ -680,7 +683,10 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
   const unsigned long long valid_mask = __ballot(in_n && key_raw != sentinel);
   const int nq = __popcll(valid_mask);
   if (nq == 0) {
-    if (lane == 0) chunk_flags[k] = 0;
+    if (lane == 0) {
+      chunk_flags[k] = 0;
+      if (hcount) hcount[k] = 0;
+    }
     return;
   }
   const bool mine = lane < nq;
@@ -761,7 +767,85 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
       }
     }
   }
-  if (lane == 0) chunk_flags[k] = flags;
+  if (lane == 0) {
+    chunk_flags[k] = flags;
+    if (hcount) hcount[k] = __popcll(start_mask);  // the chunk's segment starts (heads)
+  }
+}
+
+// Segment outputs written by seg_combine from the reduce's per-chunk head
+// counts (hcount null: not built there).
+struct SegOut {
+  const int32_t* hcount;
+  int32_t* unique_keys;
+  int32_t* seg_offsets;
+  int32_t* num_unique;
+  long long n;
+  int32_t sentinel;
+};
+
+// Up to this many reduce chunks, seg_combine writes the segment outputs: each
+// workgroup sums the head counts of all chunks before its own (a few int4
+// loads per thread), so the total reads grow with the square of the count.
+constexpr long long kFusedSegChunks = 4096;
+
+// The segment outputs of this workgroup's chunks (one per wave): a head is a
+// valid key that differs from its predecessor; its index among all heads is
+// the heads of the earlier chunks plus its rank in the chunk. The wave holding
+// the last valid key (or position 0 when there is none) closes the list.
+template <int C>
+__device__ __forceinline__ void write_segments(const SegOut& so, const int32_t* __restrict__ skeys, long long nchunks) {
+  constexpr int kW = kBwdThreads / kWave;  // chunks per workgroup
+  static_assert(kW == 4, "the chunks before a workgroup are whole int4s of head counts");
+  __shared__ int red[kW], own[kW];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const long long w0 = static_cast<long long>(blockIdx.x) * kW;
+  const int4* h4 = reinterpret_cast<const int4*>(so.hcount);
+  const long long n4 = w0 / 4;
+  int sum = 0;
+  for (long long i0 = threadIdx.x; i0 < n4; i0 += 4 * kBwdThreads) {
+    int4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long long i = i0 + u * kBwdThreads;
+      v[u] = i < n4 ? h4[i] : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sum += v[u].x + v[u].y + v[u].z + v[u].w;
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) sum += __shfl_xor(sum, m, kWave);
+  if (lane == 0) {
+    red[wave] = sum;
+    own[wave] = w0 + wave < nchunks ? so.hcount[w0 + wave] : 0;
+  }
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) before += red[w] + (w < wave ? own[w] : 0);
+  const long long k = w0 + wave;
+  if (k >= nchunks) return;
+  const long long q = k * C + lane;
+  const bool in = lane < C && q < so.n;
+  const long long qc = in ? q : k * C;  // k * C < n for every chunk
+  const int32_t key = skeys[qc];
+  const int32_t prev = qc > 0 ? skeys[qc - 1] : so.sentinel;
+  const int32_t next = qc + 1 < so.n ? skeys[qc + 1] : so.sentinel;
+  const bool valid = in && key != so.sentinel;
+  const bool is_head = valid && (q == 0 || prev != key);
+  const unsigned long long hm = __ballot(is_head);
+  const int idx = before + __popcll(hm & ((1ull << lane) - 1ull));
+  if (is_head) {
+    so.unique_keys[idx] = key;
+    so.seg_offsets[idx] = static_cast<int32_t>(q);
+  }
+  const bool last_valid = valid && (q + 1 == so.n || next == so.sentinel);
+  const bool none_valid = in && q == 0 && !valid;
+  if (last_valid || none_valid) {
+    const int U = before + __popcll(hm);  // no head lies past the last valid key
+    so.seg_offsets[U] = last_valid ? static_cast<int32_t>(q + 1) : 0;
+    *so.num_unique = U;
+  }
 }
 
 // The update of one segment's row (this lane's EL columns).
@@ -788,7 +872,8 @@ __global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, St
                                                            const float* __restrict__ carry,
                                                            const float* __restrict__ head,
                                                            const int32_t* __restrict__ chunk_flags, long long nchunks,
-                                                           float lr) {
+                                                           float lr, SegOut so) {
+  if (so.hcount) write_segments<C>(so, skeys, nchunks);  // uniform: every thread reaches its barrier
   const int lane = threadIdx.x & (kWave - 1);
   const int lpr = D < kWave ? D : kWave;
   const int col = (lane % lpr) * EL;
@@ -899,7 +984,8 @@ WsLayout layout(int T, int B, int D, int64_t nnz) {
 
 template <int DT, int EL>
 hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, const int32_t* skeys, int32_t sentinel,
-                             const int32_t* src_bag, const float* d_pooled, hipStream_t st) {
+                             const int32_t* src_bag, const float* d_pooled, const SegOut& so, hipStream_t st) {
+  int32_t* hcount = const_cast<int32_t*>(so.hcount);
   constexpr int C = seg_chunk(EL);
   const long long nchunks = (a.nnz + C - 1) / C;
   float* carry = reinterpret_cast<float*>(ws + L.carry);
@@ -909,26 +995,26 @@ hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, cons
   const dim3 g(static_cast<unsigned>((nchunks + kWavesPerBlock - 1) / kWavesPerBlock)), blk(kBwdThreads);
   if (a.opt == kRowwiseAdagrad) {
     hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D,
-                       skeys, a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks);
+                       skeys, a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, hcount);
     hipLaunchKernelGGL((seg_combine<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
-                       carry, head, flags, nchunks, a.lr);
+                       carry, head, flags, nchunks, a.lr, so);
   } else {
     hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
-                       a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks);
+                       a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, hcount);
     hipLaunchKernelGGL((seg_combine<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys, carry, head,
-                       flags, nchunks, a.lr);
+                       flags, nchunks, a.lr, so);
   }
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_reduce_dt(const BwdArgs& a, const WsLayout& L, char* ws, const int32_t* skeys, int32_t sentinel,
-                            const int32_t* src_bag, const float* d_pooled, hipStream_t st) {
+                            const int32_t* src_bag, const float* d_pooled, const SegOut& so, hipStream_t st) {
   switch (seg_el(a.D)) {
-    case 1: return launch_seg_reduce<DT, 1>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
-    case 2: return launch_seg_reduce<DT, 2>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
-    case 4: return launch_seg_reduce<DT, 4>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
-    case 8: return launch_seg_reduce<DT, 8>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
+    case 1: return launch_seg_reduce<DT, 1>(a, L, ws, skeys, sentinel, src_bag, d_pooled, so, st);
+    case 2: return launch_seg_reduce<DT, 2>(a, L, ws, skeys, sentinel, src_bag, d_pooled, so, st);
+    case 4: return launch_seg_reduce<DT, 4>(a, L, ws, skeys, sentinel, src_bag, d_pooled, so, st);
+    case 8: return launch_seg_reduce<DT, 8>(a, L, ws, skeys, sentinel, src_bag, d_pooled, so, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -983,11 +1069,15 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   // 1. interaction backward, its samples shared out as extra workgroups over
   // the sort passes' scatter launches (the longest of the sort; a share takes
   // about as long as a scatter, and much longer than a count) and the one-pass
-  // segment build; nothing before the reduce reads its outputs
+  // segment build when that runs; nothing before the reduce reads its outputs
   const int passes = radix_passes(a.total_rows);
   const bool want_segments = a.unique_keys || a.seg_offsets || a.num_unique;
+  // segment outputs from the reduce's head counts, written by seg_combine
+  // (no launches of their own), when the reduce has few enough chunks
+  const long long red_chunks = (n + seg_chunk(seg_el(a.D)) - 1) / seg_chunk(seg_el(a.D));
+  const bool fused_seg = want_segments && red_chunks <= kFusedSegChunks;
   const long long nscan = scan_chunks(n);
-  const bool seg_one_pass = want_segments && nscan <= kScanThreads;
+  const bool seg_one_pass = want_segments && !fused_seg && nscan <= kScanThreads;
   const int nshare = passes + (seg_one_pass ? 1 : 0);
   int ishare = 0;
   const IbwdShare none{a.T, a.D, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
@@ -1045,7 +1135,7 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   // radix_passes() >= 1, so the last pass wrote a.perm (if given) and src_bag
   // 4. segments: outputs only (the reduce reads the sorted keys), so built only
   // when the caller asks for any of them
-  if (want_segments) {
+  if (want_segments && !fused_seg) {
     const long long m = nscan;
     if (seg_one_pass) {  // chunk totals, then one pass that scans and builds the segments
       hipLaunchKernelGGL((scan_chunk_totals<HeadIn>), dim3(static_cast<unsigned>(m)), dim3(kScanThreads), 0, st,
@@ -1060,11 +1150,14 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
                          dim3(kBwdThreads), 0, st, skeys, n, sentinel, pos, uniq, seg, nuniq);
     }
   }
-  // 5. reduce + SGD
+  // 5. reduce + SGD (and the segment outputs with fused_seg: the head counts
+  // go to pos, which nothing else uses then)
+  const SegOut so = fused_seg ? SegOut{pos, uniq, seg, nuniq, n, sentinel}
+                              : SegOut{nullptr, nullptr, nullptr, nullptr, n, sentinel};
   switch (a.dtype) {
-    case DLRM_F32: return launch_reduce_dt<DLRM_F32>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
-    case DLRM_F16: return launch_reduce_dt<DLRM_F16>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
-    case DLRM_BF16: return launch_reduce_dt<DLRM_BF16>(a, L, ws, skeys, sentinel, src_bag, d_pooled, st);
+    case DLRM_F32: return launch_reduce_dt<DLRM_F32>(a, L, ws, skeys, sentinel, src_bag, d_pooled, so, st);
+    case DLRM_F16: return launch_reduce_dt<DLRM_F16>(a, L, ws, skeys, sentinel, src_bag, d_pooled, so, st);
+    case DLRM_BF16: return launch_reduce_dt<DLRM_BF16>(a, L, ws, skeys, sentinel, src_bag, d_pooled, so, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -162,6 +162,27 @@ def test_backward_sort_and_segment_paths(B, bag):
     run_bwd(w, lr=0.01)
 
 
+@pytest.mark.parametrize("B,twice", [(2048, True), (2040, False), (2064, False)])
+def test_backward_sort_tile_count_boundary(B, twice):
+    """Bags of exactly 64 over 2 tables: 128 full sort tiles (the most whose scatter sums its
+    digit offsets from the count table itself), 127.5 tiles (a ragged last tile) and 129 tiles
+    (the offsets come from a per-digit scan launch). The run twice matches bit for bit."""
+    w = synth.Workload("tiles", T=2, rows=3000, D=8, dtype="f32", B=B, bag=("fixed", 64),
+                       dist=("zipf", 1.05), seed=B + 5)
+    res, r = run_bwd(w, lr=0.01, twice=twice)
+    assert len(r["perm"]) == 2 * 64 * B
+
+
+@pytest.mark.parametrize("B", [1024, 1025])
+def test_backward_segment_outputs_chunk_boundary(B):
+    """D = 8 reduces 32 sorted positions per chunk. Bags of exactly 64 over 2 tables give
+    4096 chunks (the most for which the combine step writes the segment outputs from the
+    reduce's per-chunk head counts) and 4100 (a scan launch builds them)."""
+    w = synth.Workload("segs", T=2, rows=3000, D=8, dtype="f32", B=B, bag=("fixed", 64),
+                       dist=("zipf", 1.05), seed=B + 11)
+    run_bwd(w, lr=0.01, twice=True)
+
+
 def test_backward_positions_outside_every_bag_are_skipped():
     """Offsets that start at 3 and end 5 short of nnz (invalid, flagged): the positions
     before the first offset and from the last one on belong to no bag and add nothing."""
