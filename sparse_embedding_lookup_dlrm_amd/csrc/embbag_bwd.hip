@@ -12,11 +12,12 @@
 // 2. keys: occurrence p of bag (t, b) gets key base_t + index (its global row)
 //    and value p; an out-of-range index, or a position no bag covers (invalid
 //    offsets), gets the sentinel key sum(rows).
-// 3. stable LSD radix sort of (key, p), 8 bits per pass: per-tile digit counts,
-//    each tile's digit offsets (from the digit-major count table, summed inside
-//    the scatter for up to 128 tiles, else scanned per digit by one kernel), a
-//    stable scatter that ranks equal digits inside a wave with ballots. The
-//    last pass also writes each sorted position's bag.
+// 3. stable LSD radix sort of (key, p), 8 or 9 bits per pass (9 only where
+//    that saves a pass): per-tile digit counts, each tile's digit offsets (from
+//    the digit-major count table, summed inside the scatter for up to 128
+//    tiles, else scanned per digit by one kernel), a stable scatter that ranks
+//    equal digits inside a wave with ballots. The last pass also writes each
+//    sorted position's bag.
 // 4. segments (API outputs only): head flags (key differs from its
 //    predecessor), scanned into the position of each distinct key. With few
 //    reduce chunks the reduce counts each chunk's heads and the combine step
@@ -32,8 +33,10 @@
 namespace dlrm {
 
 constexpr int kBwdThreads = 256;
-constexpr int kRadixBits = 8;
-constexpr int kRadixBins = 1 << kRadixBits;
+// Digits of 8 bits, or 9 where that takes one pass fewer (keys of 9, 17-18 or
+// 25-27 bits): a 9-bit digit has 512 bins, two per thread.
+constexpr int kMaxRadixBits = 9;
+constexpr int kMaxRadixBins = 1 << kMaxRadixBits;
 constexpr int kRadixPerThread = 8;
 constexpr int kRadixTile = kBwdThreads * kRadixPerThread;  // 2048 keys per tile
 constexpr int kRadixWaves = kBwdThreads / kWave;
@@ -257,64 +260,84 @@ __global__ __launch_bounds__(kBwdThreads) void build_keys(MutTableArgs tabs, int
 // ---------------------------------------------------------------------------
 // 3. radix sort
 // ---------------------------------------------------------------------------
+template <int BITS>
 __global__ __launch_bounds__(kBwdThreads) void radix_count(const int32_t* __restrict__ keys, long long n, int shift,
                                                            int ntiles, int32_t* __restrict__ counts, IbwdShare ia) {
+  constexpr int kBins = 1 << BITS;
   if (ibwd_extra(ia, ntiles)) return;
-  __shared__ int hist[kRadixBins];
-  hist[threadIdx.x] = 0;
+  __shared__ int hist[kBins];
+  for (int d = threadIdx.x; d < kBins; d += kBwdThreads) hist[d] = 0;
   __syncthreads();
   const long long base = static_cast<long long>(blockIdx.x) * kRadixTile;
 #pragma unroll
   for (int k = 0; k < kRadixPerThread; ++k) {
     const long long i = base + k * kBwdThreads + threadIdx.x;
-    if (i < n) atomicAdd(&hist[(static_cast<uint32_t>(keys[i]) >> shift) & (kRadixBins - 1)], 1);
+    if (i < n) atomicAdd(&hist[(static_cast<uint32_t>(keys[i]) >> shift) & (kBins - 1)], 1);
   }
   __syncthreads();
-  counts[static_cast<long long>(threadIdx.x) * ntiles + blockIdx.x] = hist[threadIdx.x];
+  for (int d = threadIdx.x; d < kBins; d += kBwdThreads) counts[static_cast<long long>(d) * ntiles + blockIdx.x] = hist[d];
 }
 
 // Up to this many tiles, each scatter workgroup works out its own digit
 // offsets from the count table instead of a device-wide scan.
 constexpr int kInlineScanTiles = 128;
 
-// Where this tile's keys of digit d (= threadIdx.x) start in the output: all
-// keys of smaller digits, plus the keys of digit d in earlier tiles. The count
-// table is digit-major ([digit][tile]). With row_prefix null the digit's row
-// is summed here; otherwise row_prefix holds each row's exclusive scan and
-// row_total each row's sum (radix_row_scan). The digit totals are then
-// scanned across the workgroup.
-__device__ __forceinline__ int tile_digit_base(const int32_t* __restrict__ counts,
-                                               const int32_t* __restrict__ row_prefix,
-                                               const int32_t* __restrict__ row_total, int ntiles, int* lds4) {
-  const int d = threadIdx.x, lane = d & (kWave - 1), wave = d >> 6;
-  int tot = 0, pre = 0;
-  if (row_prefix) {
-    pre = row_prefix[static_cast<long long>(d) * ntiles + blockIdx.x];
-    tot = row_total[d];
-  } else {
-    const int32_t* row = counts + static_cast<long long>(d) * ntiles;
-    for (int t0 = 0; t0 < ntiles; t0 += 8) {
-      int c[8];
+// Where this tile's keys of each digit start in the output (gbase[d]): all
+// keys of smaller digits, plus the keys of digit d in earlier tiles. Thread
+// threadIdx.x handles digits threadIdx.x + j * 256. The count table is
+// digit-major ([digit][tile]). With row_prefix null the digit's row is summed
+// here; otherwise row_prefix holds each row's exclusive scan and row_total
+// each row's sum (radix_row_scan). The digit totals are then scanned across
+// the workgroup in digit order. lds holds kRadixWaves ints per digit per thread.
+template <int BITS>
+__device__ __forceinline__ void tile_digit_base(const int32_t* __restrict__ counts,
+                                                const int32_t* __restrict__ row_prefix,
+                                                const int32_t* __restrict__ row_total, int ntiles, int* lds,
+                                                int* gbase) {
+  constexpr int kDPT = (1 << BITS) / kBwdThreads;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  int tot[kDPT], pre[kDPT], x[kDPT];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = t0 + u < ntiles ? row[t0 + u] : 0;
+  for (int j = 0; j < kDPT; ++j) {
+    const int d = threadIdx.x + j * kBwdThreads;
+    tot[j] = 0;
+    pre[j] = 0;
+    if (row_prefix) {
+      pre[j] = row_prefix[static_cast<long long>(d) * ntiles + blockIdx.x];
+      tot[j] = row_total[d];
+    } else {
+      const int32_t* row = counts + static_cast<long long>(d) * ntiles;
+      for (int t0 = 0; t0 < ntiles; t0 += 8) {
+        int c[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        tot += c[u];
-        if (t0 + u < static_cast<int>(blockIdx.x)) pre += c[u];
+        for (int u = 0; u < 8; ++u) c[u] = t0 + u < ntiles ? row[t0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          tot[j] += c[u];
+          if (t0 + u < static_cast<int>(blockIdx.x)) pre[j] += c[u];
+        }
       }
     }
-  }
-  int x = tot;  // inclusive scan of the totals over the wave, then across the 4 waves
+    x[j] = tot[j];  // inclusive scan of the totals over the wave, then across the 4 waves
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(x[j], o, kWave);
+      if (lane >= o) x[j] += y;
+    }
+    if (lane == kWave - 1) lds[j * kRadixWaves + wave] = x[j];
   }
-  if (lane == kWave - 1) lds4[wave] = x;
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += lds4[w];
-  return before + x - tot + pre;
+  int carry = 0;  // keys of all digits below threadIdx.x + j * 256's block of 256
+#pragma unroll
+  for (int j = 0; j < kDPT; ++j) {
+    int before = carry;
+    for (int w = 0; w < kRadixWaves; ++w) {
+      const int v = lds[j * kRadixWaves + w];
+      if (w < wave) before += v;
+      carry += v;
+    }
+    gbase[threadIdx.x + j * kBwdThreads] = before + x[j] - tot[j] + pre[j];
+  }
 }
 
 // Each digit's row of the count table (one workgroup per digit): exclusive
@@ -352,6 +375,7 @@ __global__ __launch_bounds__(kScanThreads) void radix_row_scan(const int32_t* __
 // carries the rank across rounds. The tile's digit offsets come from the
 // row-scanned count table (row_prefix, row_total) or, with row_prefix null,
 // from the count table itself (at most kInlineScanTiles tiles).
+template <int BITS>
 __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __restrict__ keys_in,
                                                              const int32_t* __restrict__ vals_in, long long n,
                                                              int shift, int ntiles,
@@ -362,12 +386,14 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
                                                              int32_t* __restrict__ vals_out,
                                                              const int32_t* __restrict__ bag_of,
                                                              int32_t* __restrict__ src_out, IbwdShare ia) {
+  constexpr int kBins = 1 << BITS, kDPT = kBins / kBwdThreads;
   if (ibwd_extra(ia, ntiles)) return;
-  __shared__ int wcount[kRadixWaves][kRadixBins];
-  __shared__ int gbase[kRadixBins];
-  __shared__ int lds4[kRadixWaves];
+  __shared__ int wcount[kRadixWaves][kBins];
+  __shared__ int gbase[kBins];
+  __shared__ int lds[kRadixWaves * kDPT];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  for (int w = 0; w < kRadixWaves; ++w) wcount[w][threadIdx.x] = 0;
+  for (int w = 0; w < kRadixWaves; ++w)
+    for (int d = threadIdx.x; d < kBins; d += kBwdThreads) wcount[w][d] = 0;
   const long long sub = static_cast<long long>(blockIdx.x) * kRadixTile + static_cast<long long>(wave) * kRadixRounds * kWave;
   const unsigned long long lt = (1ull << lane) - 1ull;
   int key[kRadixRounds], val[kRadixRounds], dig[kRadixRounds], rank[kRadixRounds];
@@ -385,17 +411,17 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
 #pragma unroll
     for (int r = 0; r < kRadixRounds; ++r) src[r] = bag_of[val[r]];  // val = 0 past the end: in bounds
   }
-  gbase[threadIdx.x] = tile_digit_base(counts, row_prefix, row_total, ntiles, lds4);
+  tile_digit_base<BITS>(counts, row_prefix, row_total, ntiles, lds, gbase);
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < kRadixRounds; ++r) {
     const long long i = sub + r * kWave + lane;
     const bool ok = i < n;
-    const int d = (static_cast<uint32_t>(key[r]) >> shift) & (kRadixBins - 1);
+    const int d = (static_cast<uint32_t>(key[r]) >> shift) & (kBins - 1);
     dig[r] = ok ? d : -1;
     unsigned long long peers = __ballot(ok);
 #pragma unroll
-    for (int bit = 0; bit < kRadixBits; ++bit) {
+    for (int bit = 0; bit < BITS; ++bit) {
       const unsigned long long m = __ballot((d >> bit) & 1);
       peers &= ((d >> bit) & 1) ? m : ~m;
     }
@@ -409,11 +435,11 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
     rank[r] = running + before;
   }
   __syncthreads();
-  {
+  for (int d = threadIdx.x; d < kBins; d += kBwdThreads) {
     int acc = 0;
     for (int w = 0; w < kRadixWaves; ++w) {
-      const int c = wcount[w][threadIdx.x];
-      wcount[w][threadIdx.x] = acc;
+      const int c = wcount[w][d];
+      wcount[w][d] = acc;
       acc += c;
     }
   }
@@ -945,17 +971,24 @@ struct WsLayout {
 constexpr int seg_el(int D) { return D >= kWave ? D / kWave : 1; }
 constexpr int seg_chunk(int el) { return el <= 1 ? 32 : 32 / el; }
 
-int radix_passes(int64_t total_rows) {
+// Digit width and pass count of the sort: 8-bit digits, or 9-bit ones where
+// they need one pass fewer.
+struct RadixPlan {
+  int bits, passes;
+};
+
+RadixPlan radix_plan(int64_t total_rows) {
   int bits = 0;
   while ((1ll << bits) <= total_rows) ++bits;  // sentinel key = total_rows must fit
-  return (bits + kRadixBits - 1) / kRadixBits;
+  const int p8 = (bits + 7) / 8, p9 = (bits + 8) / 9;
+  return p9 < p8 ? RadixPlan{9, p9} : RadixPlan{8, p8};
 }
 
 WsLayout layout(int T, int B, int D, int64_t nnz) {
   WsLayout L{};
   const size_t n = static_cast<size_t>(nnz);
   const size_t ntiles = (n + kRadixTile - 1) / kRadixTile;
-  const size_t ncounts = ntiles * kRadixBins;
+  const size_t ncounts = ntiles * kMaxRadixBins;
   const size_t scan_max = std::max(n, ncounts) + 1;
   size_t o = 0;
   L.d_pooled = o; o = align_up(o + static_cast<size_t>(B) * T * D * 4);
@@ -967,7 +1000,7 @@ WsLayout layout(int T, int B, int D, int64_t nnz) {
   L.src_bag = o; o = align_up(o + n * 4);
   L.counts = o; o = align_up(o + ncounts * 4);
   L.digit_off = o; o = align_up(o + (ncounts + 1) * 4);
-  L.row_total = o; o = align_up(o + kRadixBins * 4);
+  L.row_total = o; o = align_up(o + kMaxRadixBins * 4);
   L.partial = o; o = align_up(o + (scan_chunks(static_cast<long long>(scan_max)) + 1) * 8);
   L.pos = o; o = align_up(o + (n + 1) * 4);
   L.uniq = o; o = align_up(o + n * 4);
@@ -1070,7 +1103,8 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   // the sort passes' scatter launches (the longest of the sort; a share takes
   // about as long as a scatter, and much longer than a count) and the one-pass
   // segment build when that runs; nothing before the reduce reads its outputs
-  const int passes = radix_passes(a.total_rows);
+  const RadixPlan plan = radix_plan(a.total_rows);
+  const int passes = plan.passes;
   const bool want_segments = a.unique_keys || a.seg_offsets || a.num_unique;
   // segment outputs from the reduce's head counts, written by seg_combine
   // (no launches of their own), when the reduce has few enough chunks
@@ -1110,29 +1144,36 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
     }
 #undef DLRM_BUILD_KEYS
   }
-  // 3. radix sort, 8 bits per pass
+  // 3. radix sort, plan.bits (8 or 9) bits per pass
   const int ntiles = static_cast<int>((n + kRadixTile - 1) / kRadixTile);
   int cur = 0;
   for (int p = 0; p < passes; ++p) {
-    const int shift = p * kRadixBits;
-    hipLaunchKernelGGL(radix_count, dim3(ntiles), dim3(kBwdThreads), 0, st, keys[cur], n, shift, ntiles, counts, none);
+    const int shift = p * plan.bits;
     const bool inline_scan = ntiles <= kInlineScanTiles;
-    if (!inline_scan) {
-      hipLaunchKernelGGL(radix_row_scan, dim3(kRadixBins), dim3(kScanThreads), 0, st, counts, ntiles, digit_off,
-                         row_total);
-    }
     // the last pass writes the permutation straight to the caller's array, if any
     int32_t* vout = (p + 1 == passes && a.perm) ? a.perm : vals[cur ^ 1];
     // ... and each sorted position's bag (for the reduce)
     const bool last_pass = p + 1 == passes;
     const IbwdShare ia_scatter = share();
-    hipLaunchKernelGGL(radix_scatter, dim3(ntiles + ia_scatter.count), dim3(kBwdThreads), ilds, st, keys[cur], vals[cur],
-                       n, shift, ntiles, counts, inline_scan ? nullptr : digit_off, row_total, keys[cur ^ 1], vout,
-                       bag_of, last_pass ? src_bag : nullptr, ia_scatter);
+    const dim3 gs(ntiles + ia_scatter.count), blk(kBwdThreads);
+#define DLRM_SORT_PASS(BITS)                                                                                          \
+  do {                                                                                                                \
+    hipLaunchKernelGGL(radix_count<BITS>, dim3(ntiles), blk, 0, st, keys[cur], n, shift, ntiles, counts, none);       \
+    if (!inline_scan) {                                                                                               \
+      hipLaunchKernelGGL(radix_row_scan, dim3(1 << (BITS)), dim3(kScanThreads), 0, st, counts, ntiles, digit_off,      \
+                         row_total);                                                                                  \
+    }                                                                                                                 \
+    hipLaunchKernelGGL(radix_scatter<BITS>, gs, blk, ilds, st, keys[cur], vals[cur], n, shift, ntiles, counts,         \
+                       inline_scan ? nullptr : digit_off, row_total, keys[cur ^ 1], vout, bag_of,                     \
+                       last_pass ? src_bag : nullptr, ia_scatter);                                                    \
+  } while (0)
+    if (plan.bits == 9) DLRM_SORT_PASS(9);
+    else DLRM_SORT_PASS(8);
+#undef DLRM_SORT_PASS
     cur ^= 1;
   }
   const int32_t* skeys = keys[cur];
-  // radix_passes() >= 1, so the last pass wrote a.perm (if given) and src_bag
+  // plan.passes >= 1, so the last pass wrote a.perm (if given) and src_bag
   // 4. segments: outputs only (the reduce reads the sorted keys), so built only
   // when the caller asks for any of them
   if (want_segments && !fused_seg) {

@@ -131,23 +131,26 @@ def test_backward_shapes(T, D, B):
     run_bwd(w, lr=0.05)
 
 
-def test_backward_many_keys_four_radix_passes():
-    """sum(rows) above 2^24 needs a fourth 8-bit pass of the sort."""
+def test_backward_many_keys_9bit_digits():
+    """sum(rows) = 18M: 25-bit keys, sorted in three 9-bit passes (8-bit digits would
+    need four)."""
     w = synth.Workload("bigkeys", T=3, rows=6_000_000, D=8, dtype="bf16", B=700, bag=("uniform", 0, 9),
                        dist=("zipf", 1.05), seed=77)
     run_bwd(w, lr=0.01)
 
 
 @pytest.mark.parametrize("T,rows,B,bag", [
-    (1, 200, 300, ("uniform", 0, 12)),  # 8-bit keys: one pass
-    (3, 500, 300, ("uniform", 0, 12)),  # 11 bits: two passes
-    (2, 50_000, 900, ("uniform", 0, 12)),  # 17 bits: three passes
-    (3, 1_000_000, 2000, ("uniform", 10, 14)),  # 22 bits, 36 tiles
-    (2, 5_000_000, 500, ("uniform", 0, 12)),  # 24 bits: three passes, the last digit full
+    (1, 200, 300, ("uniform", 0, 12)),  # 8-bit keys: one 8-bit pass
+    (1, 400, 300, ("uniform", 0, 12)),  # 9 bits: one 9-bit pass
+    (3, 500, 300, ("uniform", 0, 12)),  # 11 bits: two 8-bit passes
+    (2, 50_000, 900, ("uniform", 0, 12)),  # 17 bits: two 9-bit passes
+    (3, 1_000_000, 2000, ("uniform", 10, 14)),  # 22 bits: three 8-bit passes, 36 tiles
+    (2, 5_000_000, 500, ("uniform", 0, 12)),  # 24 bits: three 8-bit passes, the last digit full
 ])
 def test_backward_sort_pass_counts(T, rows, B, bag):
-    """The sort takes as many 8-bit passes as the key width needs (the sentinel
-    sum(rows) included): one to three passes here, four in the test above."""
+    """The sort takes as many passes as the key width needs (the sentinel sum(rows)
+    included), with 9-bit digits where they save a pass: one to three passes here, three
+    9-bit passes of 25-bit keys in the test above."""
     w = synth.Workload("passes", T=T, rows=rows, D=8, dtype="f32", B=B, bag=bag, dist=("zipf", 1.05),
                        seed=rows % 997 + B)
     run_bwd(w, lr=0.01)
