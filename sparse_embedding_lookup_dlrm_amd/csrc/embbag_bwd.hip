@@ -802,7 +802,7 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
 // Segment outputs written by seg_combine from the reduce's per-chunk head
 // counts (hcount null: not built there).
 struct SegOut {
-  const int32_t* hcount;
+  int32_t* hcount;  // written by the reduce, read by the combine step
   int32_t* unique_keys;
   int32_t* seg_offsets;
   int32_t* num_unique;
@@ -1018,7 +1018,6 @@ WsLayout layout(int T, int B, int D, int64_t nnz) {
 template <int DT, int EL>
 hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, const int32_t* skeys, int32_t sentinel,
                              const int32_t* src_bag, const float* d_pooled, const SegOut& so, hipStream_t st) {
-  int32_t* hcount = const_cast<int32_t*>(so.hcount);
   constexpr int C = seg_chunk(EL);
   const long long nchunks = (a.nnz + C - 1) / C;
   float* carry = reinterpret_cast<float*>(ws + L.carry);
@@ -1028,12 +1027,12 @@ hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, cons
   const dim3 g(static_cast<unsigned>((nchunks + kWavesPerBlock - 1) / kWavesPerBlock)), blk(kBwdThreads);
   if (a.opt == kRowwiseAdagrad) {
     hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D,
-                       skeys, a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, hcount);
+                       skeys, a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, so.hcount);
     hipLaunchKernelGGL((seg_combine<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
                        carry, head, flags, nchunks, a.lr, so);
   } else {
     hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
-                       a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, hcount);
+                       a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, so.hcount);
     hipLaunchKernelGGL((seg_combine<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys, carry, head,
                        flags, nchunks, a.lr, so);
   }
