@@ -687,7 +687,11 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
                                                                  int32_t* __restrict__ hcount) {
   static_assert(C <= kWave, "one lane per chunk position");
   __shared__ int sbase[DLRM_MAX_TABLES];  // first global key of each table
-  for (int t = threadIdx.x; t < T; t += kBwdThreads) sbase[t] = tabs.base[t];
+  __shared__ float* sstate[OPT == kRowwiseAdagrad ? DLRM_MAX_TABLES : 1];  // each table's row states
+  for (int t = threadIdx.x; t < T; t += kBwdThreads) {
+    sbase[t] = tabs.base[t];
+    if constexpr (OPT == kRowwiseAdagrad) sstate[t] = state.ptr[t];
+  }
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1);
   const int lpr = D < kWave ? D : kWave;
@@ -730,6 +734,10 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
     if (c < T && b <= key) tk = c;
   }
   const int rk = key - sbase[tk];
+  // row-wise AdaGrad: the state of this lane's row, one gather for the wave
+  // (lanes past the valid keys repeat lane 0's row: in bounds)
+  float s_lane = 0.f;
+  if constexpr (OPT == kRowwiseAdagrad) s_lane = sstate[tk][rk];
   const bool starts = mine && (qa == 0 || key_prev != key_raw);
   // does a segment start right after the chunk? (then the last one closes here)
   const unsigned long long start_mask = __ballot(starts);
@@ -751,7 +759,6 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
   RowVec<EL> rows[C];
   TabVec<DT, EL> trow[C];
   RowRef refs[C];
-  float sold[OPT == kRowwiseAdagrad ? C : 1];
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int r = __shfl(src, j, kWave);
@@ -761,7 +768,6 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
     const int rj = __builtin_amdgcn_readfirstlane(__shfl(rk, jj, kWave));
     refs[j].off = static_cast<size_t>(rj) * D;
     trow[j].load(tabs, refs[j], col);
-    if constexpr (OPT == kRowwiseAdagrad) sold[j] = state.ptr[refs[j].t][rj];
   }
   RowVec<EL> acc;
 #pragma unroll
@@ -775,9 +781,10 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
       if ((close_mask >> j) & 1ull) {
         if ((complete_mask >> j) & 1ull) {
           if constexpr (OPT == kRowwiseAdagrad) {
-            const int rj = static_cast<int>(refs[j].off / D);
-            trow[j].sgd_store(tabs, refs[j], col, acc,
-                              adagrad_step<EL>(acc, sold[j], state.ptr[refs[j].t] + rj, D, lr, eps));
+            // a complete segment closes at j, so lane j holds its row and that row's state
+            const int rj = __builtin_amdgcn_readlane(rk, j);
+            const float s_old = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane), j));
+            trow[j].sgd_store(tabs, refs[j], col, acc, adagrad_step<EL>(acc, s_old, sstate[refs[j].t] + rj, D, lr, eps));
           } else {
             trow[j].sgd_store(tabs, refs[j], col, acc, lr);
           }
