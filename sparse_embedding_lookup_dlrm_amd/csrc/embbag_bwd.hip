@@ -684,20 +684,42 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
                                                                  const float* __restrict__ d_pooled, float lr,
                                                                  float* __restrict__ carry, float* __restrict__ head,
                                                                  int32_t* __restrict__ chunk_flags, long long nchunks,
-                                                                 int32_t* __restrict__ hcount) {
+                                                                 int32_t* __restrict__ hcount, int32_t* __restrict__ hwg) {
   static_assert(C <= kWave, "one lane per chunk position");
   __shared__ int sbase[DLRM_MAX_TABLES];  // first global key of each table
   __shared__ float* sstate[OPT == kRowwiseAdagrad ? DLRM_MAX_TABLES : 1];  // each table's row states
+  __shared__ int wg_heads, wg_done;  // the workgroup's heads so far, and its waves done
   for (int t = threadIdx.x; t < T; t += kBwdThreads) {
     sbase[t] = tabs.base[t];
     if constexpr (OPT == kRowwiseAdagrad) sstate[t] = state.ptr[t];
   }
+  if (threadIdx.x == 0) {
+    wg_heads = 0;
+    wg_done = 0;
+  }
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1);
+  // Every wave ends here with its chunk's number of segment starts (heads):
+  // it adds them to the workgroup's sum, then counts itself done; the last of
+  // the four stores the sum for the combine step's prefix sums (no barrier, so
+  // waves may leave early).
+  auto finish = [&](int heads) {
+    if (hwg && lane == 0) {
+      atomicAdd(&wg_heads, heads);
+      __threadfence_block();
+      if (atomicAdd(&wg_done, 1) == kBwdThreads / kWave - 1) {
+        __threadfence_block();
+        hwg[blockIdx.x] = atomicAdd(&wg_heads, 0);
+      }
+    }
+  };
   const int lpr = D < kWave ? D : kWave;
   const int col = (lane % lpr) * EL;
   const long long k = static_cast<long long>(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6);
-  if (k >= nchunks) return;
+  if (k >= nchunks) {
+    finish(0);
+    return;
+  }
   const long long q0 = k * C;
   // per position (lane j < C): its key (sorted), the key before it, the key
   // after it, and the bag whose gradient row it adds; all independent loads.
@@ -717,6 +739,7 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
       chunk_flags[k] = 0;
       if (hcount) hcount[k] = 0;
     }
+    finish(0);
     return;
   }
   const bool mine = lane < nq;
@@ -804,12 +827,14 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
     chunk_flags[k] = flags;
     if (hcount) hcount[k] = __popcll(start_mask);  // the chunk's segment starts (heads)
   }
+  finish(__popcll(start_mask));
 }
 
 // Segment outputs written by seg_combine from the reduce's per-chunk head
 // counts (hcount null: not built there).
 struct SegOut {
-  int32_t* hcount;  // written by the reduce, read by the combine step
+  int32_t* hcount;  // per chunk: written by the reduce, read by the combine step
+  int32_t* hwg;     // per reduce workgroup of four chunks: the same, summed
   int32_t* unique_keys;
   int32_t* seg_offsets;
   int32_t* num_unique;
@@ -818,9 +843,10 @@ struct SegOut {
 };
 
 // Up to this many reduce chunks, seg_combine writes the segment outputs: each
-// workgroup sums the head counts of all chunks before its own (a few int4
-// loads per thread), so the total reads grow with the square of the count.
-constexpr long long kFusedSegChunks = 4096;
+// workgroup sums the head totals of all workgroups before its own (up to 32
+// loads per thread, from L2), so the total reads grow with the square of the
+// count (about 130 MB at the limit).
+constexpr long long kFusedSegChunks = 32768;
 
 // The segment outputs of this workgroup's chunks (one per wave): a head is a
 // valid key that differs from its predecessor; its index among all heads is
@@ -828,23 +854,22 @@ constexpr long long kFusedSegChunks = 4096;
 // the last valid key (or position 0 when there is none) closes the list.
 template <int C>
 __device__ __forceinline__ void write_segments(const SegOut& so, const int32_t* __restrict__ skeys, long long nchunks) {
-  constexpr int kW = kBwdThreads / kWave;  // chunks per workgroup
-  static_assert(kW == 4, "the chunks before a workgroup are whole int4s of head counts");
+  constexpr int kW = kBwdThreads / kWave;  // chunks per workgroup (the reduce's and this launch's)
   __shared__ int red[kW], own[kW];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const long long w0 = static_cast<long long>(blockIdx.x) * kW;
-  const int4* h4 = reinterpret_cast<const int4*>(so.hcount);
-  const long long n4 = w0 / 4;
+  // heads of the chunks before this workgroup's: the totals of the earlier workgroups
+  const int nbefore = static_cast<int>(blockIdx.x);
   int sum = 0;
-  for (long long i0 = threadIdx.x; i0 < n4; i0 += 4 * kBwdThreads) {
-    int4 v[4];
+  for (int i0 = threadIdx.x; i0 < nbefore; i0 += 8 * kBwdThreads) {
+    int v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const long long i = i0 + u * kBwdThreads;
-      v[u] = i < n4 ? h4[i] : make_int4(0, 0, 0, 0);
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kBwdThreads;
+      v[u] = i < nbefore ? so.hwg[i] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sum += v[u].x + v[u].y + v[u].z + v[u].w;
+    for (int u = 0; u < 8; ++u) sum += v[u];
   }
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) sum += __shfl_xor(sum, m, kWave);
@@ -969,7 +994,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct WsLayout {
   size_t d_pooled, keys_a, keys_b, vals_a, vals_b, bag_of, src_bag, counts, digit_off, row_total, partial, pos, uniq, seg,
       nuniq;
-  size_t carry, head, chunk_flags, total;
+  size_t carry, head, chunk_flags, hcount, hwg, total;
 };
 
 // Gradient columns per lane for a row of D fp32 values, and the chunk of sorted
@@ -1018,6 +1043,8 @@ WsLayout layout(int T, int B, int D, int64_t nnz) {
   L.carry = o; o = align_up(o + nchunks * D * 4);
   L.head = o; o = align_up(o + nchunks * D * 4);
   L.chunk_flags = o; o = align_up(o + nchunks * 4);
+  L.hcount = o; o = align_up(o + nchunks * 4);
+  L.hwg = o; o = align_up(o + (nchunks + 3) / 4 * 4);
   L.total = o;
   return L;
 }
@@ -1034,12 +1061,12 @@ hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, cons
   const dim3 g(static_cast<unsigned>((nchunks + kWavesPerBlock - 1) / kWavesPerBlock)), blk(kBwdThreads);
   if (a.opt == kRowwiseAdagrad) {
     hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D,
-                       skeys, a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, so.hcount);
+                       skeys, a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, so.hcount, so.hwg);
     hipLaunchKernelGGL((seg_combine<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
                        carry, head, flags, nchunks, a.lr, so);
   } else {
     hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
-                       a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, so.hcount);
+                       a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, so.hcount, so.hwg);
     hipLaunchKernelGGL((seg_combine<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys, carry, head,
                        flags, nchunks, a.lr, so);
   }
@@ -1197,10 +1224,10 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
                          dim3(kBwdThreads), 0, st, skeys, n, sentinel, pos, uniq, seg, nuniq);
     }
   }
-  // 5. reduce + SGD (and the segment outputs with fused_seg: the head counts
-  // go to pos, which nothing else uses then)
-  const SegOut so = fused_seg ? SegOut{pos, uniq, seg, nuniq, n, sentinel}
-                              : SegOut{nullptr, nullptr, nullptr, nullptr, n, sentinel};
+  // 5. reduce + SGD (and the segment outputs with fused_seg)
+  const SegOut so = fused_seg ? SegOut{reinterpret_cast<int32_t*>(ws + L.hcount), reinterpret_cast<int32_t*>(ws + L.hwg),
+                                       uniq, seg, nuniq, n, sentinel}
+                              : SegOut{nullptr, nullptr, nullptr, nullptr, nullptr, n, sentinel};
   switch (a.dtype) {
     case DLRM_F32: return launch_reduce_dt<DLRM_F32>(a, L, ws, skeys, sentinel, src_bag, d_pooled, so, st);
     case DLRM_F16: return launch_reduce_dt<DLRM_F16>(a, L, ws, skeys, sentinel, src_bag, d_pooled, so, st);

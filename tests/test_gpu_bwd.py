@@ -176,13 +176,22 @@ def test_backward_sort_tile_count_boundary(B, twice):
     assert len(r["perm"]) == 2 * 64 * B
 
 
-@pytest.mark.parametrize("B", [1024, 1025])
+@pytest.mark.parametrize("B", [8192, 8193])
 def test_backward_segment_outputs_chunk_boundary(B):
     """D = 8 reduces 32 sorted positions per chunk. Bags of exactly 64 over 2 tables give
-    4096 chunks (the most for which the combine step writes the segment outputs from the
-    reduce's per-chunk head counts) and 4100 (a scan launch builds them)."""
+    32768 chunks (the most for which the combine step writes the segment outputs from the
+    reduce's head counts) and 32772 (a device-wide scan builds them)."""
     w = synth.Workload("segs", T=2, rows=3000, D=8, dtype="f32", B=B, bag=("fixed", 64),
                        dist=("zipf", 1.05), seed=B + 11)
+    run_bwd(w, lr=0.01, twice=True)
+
+
+def test_backward_segment_outputs_one_pass_scan():
+    """D = 256 reduces 8 positions per chunk: 307,200 occurrences are 38,400 chunks (too
+    many for the combine step) but 75 scan chunks of 4096, so the segment outputs come from
+    the chunk totals and one scan-and-write pass."""
+    w = synth.Workload("segs1", T=2, rows=3000, D=256, dtype="f32", B=2400, bag=("fixed", 64),
+                       dist=("zipf", 1.05), seed=2411)
     run_bwd(w, lr=0.01, twice=True)
 
 
