@@ -843,9 +843,9 @@ struct SegOut {
 };
 
 // Up to this many reduce chunks, seg_combine writes the segment outputs: each
-// workgroup sums the head totals of all workgroups before its own (up to 32
-// loads per thread, from L2), so the total reads grow with the square of the
-// count (about 130 MB at the limit).
+// workgroup sums the head totals of all workgroups before its own (up to 8
+// 16-byte loads per thread, from L2), so the total reads grow with the square
+// of the count (about 130 MB at the limit).
 constexpr long long kFusedSegChunks = 32768;
 
 // The segment outputs of this workgroup's chunks (one per wave): a head is a
@@ -858,19 +858,24 @@ __device__ __forceinline__ void write_segments(const SegOut& so, const int32_t* 
   __shared__ int red[kW], own[kW];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const long long w0 = static_cast<long long>(blockIdx.x) * kW;
-  // heads of the chunks before this workgroup's: the totals of the earlier workgroups
+  // heads of the chunks before this workgroup's: the totals of the earlier
+  // workgroups, read 4 at a time (hwg is 16-byte aligned), so that up to 8192
+  // of them take one round of loads
   const int nbefore = static_cast<int>(blockIdx.x);
+  const int n4 = nbefore >> 2;
+  const int4* h4 = reinterpret_cast<const int4*>(so.hwg);
   int sum = 0;
-  for (int i0 = threadIdx.x; i0 < nbefore; i0 += 8 * kBwdThreads) {
-    int v[8];
+  for (int i0 = threadIdx.x; i0 < n4; i0 += 8 * kBwdThreads) {
+    int4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = i0 + u * kBwdThreads;
-      v[u] = i < nbefore ? so.hwg[i] : 0;
+      v[u] = i < n4 ? h4[i] : make_int4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sum += v[u];
+    for (int u = 0; u < 8; ++u) sum += v[u].x + v[u].y + v[u].z + v[u].w;
   }
+  if (4 * n4 + static_cast<int>(threadIdx.x) < nbefore) sum += so.hwg[4 * n4 + threadIdx.x];  // the last 0..3
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) sum += __shfl_xor(sum, m, kWave);
   if (lane == 0) {
