@@ -139,6 +139,14 @@ def test_backward_many_keys_9bit_digits():
     run_bwd(w, lr=0.01)
 
 
+def test_backward_9bit_digits_row_scan():
+    """25-bit keys (three 9-bit passes) over about 410K occurrences: about 200 sort tiles,
+    so each digit's offsets come from the row-scan launch, over 512 digit rows."""
+    w = synth.Workload("bigkeys-rs", T=3, rows=6_000_000, D=8, dtype="bf16", B=2100, bag=("uniform", 60, 70),
+                       dist=("zipf", 1.05), seed=78)
+    run_bwd(w, lr=0.01)
+
+
 @pytest.mark.parametrize("T,rows,B,bag", [
     (1, 200, 300, ("uniform", 0, 12)),  # 8-bit keys: one 8-bit pass
     (1, 400, 300, ("uniform", 0, 12)),  # 9 bits: one 9-bit pass
