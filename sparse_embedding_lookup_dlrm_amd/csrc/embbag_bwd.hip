@@ -858,6 +858,17 @@ __device__ __forceinline__ void write_segments(const SegOut& so, const int32_t* 
   __shared__ int red[kW], own[kW];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const long long w0 = static_cast<long long>(blockIdx.x) * kW;
+  // this wave's keys first (a wave past the last chunk reads the last chunk's
+  // and writes nothing), so that their loads and the prefix loads below share
+  // one round trip
+  const long long k = w0 + wave;
+  const long long kc = k < nchunks ? k : nchunks - 1;
+  const long long q = kc * C + lane;
+  const bool in = k < nchunks && lane < C && q < so.n;
+  const long long qc = lane < C && q < so.n ? q : kc * C;  // kc * C < n for every chunk
+  const int32_t key = skeys[qc];
+  const int32_t prev = qc > 0 ? skeys[qc - 1] : so.sentinel;
+  const int32_t next = qc + 1 < so.n ? skeys[qc + 1] : so.sentinel;
   // heads of the chunks before this workgroup's: the totals of the earlier
   // workgroups, read 4 at a time (hwg is 16-byte aligned), so that up to 8192
   // of them take one round of loads
@@ -886,14 +897,7 @@ __device__ __forceinline__ void write_segments(const SegOut& so, const int32_t* 
   int before = 0;
 #pragma unroll
   for (int w = 0; w < kW; ++w) before += red[w] + (w < wave ? own[w] : 0);
-  const long long k = w0 + wave;
   if (k >= nchunks) return;
-  const long long q = k * C + lane;
-  const bool in = lane < C && q < so.n;
-  const long long qc = in ? q : k * C;  // k * C < n for every chunk
-  const int32_t key = skeys[qc];
-  const int32_t prev = qc > 0 ? skeys[qc - 1] : so.sentinel;
-  const int32_t next = qc + 1 < so.n ? skeys[qc + 1] : so.sentinel;
   const bool valid = in && key != so.sentinel;
   const bool is_head = valid && (q == 0 || prev != key);
   const unsigned long long hm = __ballot(is_head);
@@ -936,22 +940,28 @@ __global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, St
                                                            const float* __restrict__ head,
                                                            const int32_t* __restrict__ chunk_flags, long long nchunks,
                                                            float lr, SegOut so) {
-  if (so.hcount) write_segments<C>(so, skeys, nchunks);  // uniform: every thread reaches its barrier
   const int lane = threadIdx.x & (kWave - 1);
   const int lpr = D < kWave ? D : kWave;
   const int col = (lane % lpr) * EL;
   const long long k = static_cast<long long>(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6);
+  // the chunk's flags, last key and head sum are loaded before the segment
+  // outputs are written, so that their round trip overlaps that step's (a wave
+  // past the last chunk, or whose chunk is not full, reads in-bounds stand-ins
+  // and uses none of them)
+  const long long kc = k < nchunks ? k : nchunks - 1;
+  const long long qlast = kc * C + C - 1 < so.n ? kc * C + C - 1 : so.n - 1;
+  const int f = chunk_flags[kc];
+  const int key = skeys[qlast];
+  RowVec<EL> acc;
+  acc.load(head + static_cast<size_t>(kc) * D + col);
+  if (so.hcount) write_segments<C>(so, skeys, nchunks);  // uniform: every thread reaches its barrier
   if (k >= nchunks) return;
-  const int f = chunk_flags[k];
   if (!(f & kChunkLastCont)) return;
   // the chunk's last segment began inside it unless the chunk holds a single
   // segment that began earlier (then an earlier chunk owns it)
   if ((f & kChunkSingle) && (f & kChunkFirstCont)) return;
-  // a chunk whose last segment goes on is full of valid keys: that segment's
-  // key is the one at the chunk's last position
-  const int key = skeys[k * C + C - 1];
-  RowVec<EL> acc;
-  acc.load(head + static_cast<size_t>(k) * D + col);
+  // a chunk whose last segment goes on is full of valid keys, so key (the one
+  // at the chunk's last position) is that segment's
   // Chunk j's first part is this segment's; the segment goes on past chunk j
   // only if chunk j holds nothing else and its last segment continues. The
   // last chunk it reaches is found 64 flags at a time (one per lane), so a
