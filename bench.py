@@ -336,9 +336,9 @@ def bench_backward(steps, warmup, adagrad=False):
     d_e0 = torch.empty((w.B, w.D), dtype=torch.float32, device=dev)
     if adagrad:
         state = [torch.zeros(n, dtype=torch.float32, device=dev) for n in b.rows]
-        run = lambda: ops.embbag_bwd_update(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, workspace=ws,
-                                            status=status, row_state=state)
-        ms, _ = time_steps(run, steps, warmup)
+        plan = ops.BwdPlan(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, d_e0=d_e0, workspace=ws,
+                           status=status, row_state=state)
+        ms, _ = time_steps(plan.run, steps, warmup)
         torch.cuda.synchronize()
         return {"workload": w.name, "optimizer": "rowwise_adagrad", "ms_per_step": ms,
                 "lookups_per_s": len(b.indices) / (ms / 1e3), "status": int(status.item())}

@@ -346,10 +346,11 @@ class FwdPlan:
 
 
 class BwdPlan:
-    """dlrm_embbag_bwd_update with its arguments marshalled once (tables updated in place each run)."""
+    """dlrm_embbag_bwd_update (or, with row_state, dlrm_embbag_bwd_update_adagrad) with its
+    arguments marshalled once (tables, and the row states, updated in place each run)."""
 
     def __init__(self, tables, offsets, indices, B, e0, pooled, d_out, lr, *, d_e0=None, workspace=None,
-                 status=None, stream=None):
+                 status=None, stream=None, row_state=None, eps: float = 1e-8):
         T, D, dt, ptrs, rows = _table_args(tables)
         nnz = indices.numel()
         dev = tables[0].device
@@ -361,12 +362,26 @@ class BwdPlan:
             need = bwd_workspace_bytes(T, B, D, nnz, [t.shape[0] for t in tables])
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         _require_cuda(offsets, indices, e0, pooled, d_out, d_e0, workspace, status)
-        self._keep = (tables, offsets, indices, e0, pooled, d_out, d_e0, workspace, status, ptrs, rows)
+        opt = ()
+        sptr = None
+        self._name = "dlrm_embbag_bwd_update"
+        if row_state is not None:
+            if len(row_state) != T:
+                raise ValueError("row_state needs one tensor per table")
+            for st_, t in zip(row_state, tables):
+                _require_cuda(st_)
+                if st_.dtype != torch.float32 or st_.numel() != t.shape[0] or not st_.is_contiguous():
+                    raise ValueError("row_state[t] must be a contiguous fp32 tensor with one value per row")
+            sptr = (_c_void_p * T)(*[s_.data_ptr() for s_ in row_state])
+            opt = (float(eps), sptr)
+            self._name = "dlrm_embbag_bwd_update_adagrad"
+        self._keep = (tables, offsets, indices, e0, pooled, d_out, d_e0, workspace, status, ptrs, rows, row_state,
+                      sptr)
         self._args = (T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), nnz, _ptr(e0), _ptr(pooled),
-                      _ptr(d_out), float(lr), _ptr(d_e0), _ptr(self.unique_keys), _ptr(self.seg_offsets),
+                      _ptr(d_out), float(lr), *opt, _ptr(d_e0), _ptr(self.unique_keys), _ptr(self.seg_offsets),
                       _ptr(self.num_unique), _ptr(self.perm), _ptr(workspace), workspace.numel(), _ptr(status),
                       _stream(stream))
-        self._fn = lib().dlrm_embbag_bwd_update
+        self._fn = getattr(lib(), self._name)
 
     def run(self):
-        _check(self._fn(*self._args), "dlrm_embbag_bwd_update")
+        _check(self._fn(*self._args), self._name)

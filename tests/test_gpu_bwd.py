@@ -374,3 +374,40 @@ def test_backward_rowwise_adagrad_shapes(T, D, B, dtype):
     w = synth.Workload("ada-shape", T=T, rows=60, D=D, dtype=dtype, B=B, bag=("uniform", 0, 10),
                        dist=("zipf", 1.2), seed=T * 10 + D)
     run_bwd_adagrad(w, lr=0.02, steps=3)
+
+
+def test_backward_plan_matches_call_sgd_and_adagrad():
+    """BwdPlan (arguments marshalled once, as the benchmark times it) gives the same bits as
+    embbag_bwd_update for SGD and for row-wise AdaGrad, over two steps (tables and row states
+    carried from the first step to the second)."""
+    w = synth.Workload("plan-6t-d64-f32", T=6, rows=300, D=64, dtype="f32", B=200, bag=("uniform", 0, 9),
+                       dist=("zipf", 1.1), seed=91)
+    b = synth.make_batch(w, with_dout=True)
+    db = DeviceBatch(b)
+    pooled, _ = db.fwd(want_pooled=True)
+    d_out = torch.from_numpy(b.dout).cuda()
+    for adagrad in (False, True):
+        tabs_a = [t.clone() for t in db.tables]
+        tabs_b = [t.clone() for t in db.tables]
+        st_a = [torch.zeros(t.shape[0], dtype=torch.float32, device="cuda") for t in db.tables] if adagrad else None
+        st_b = [s.clone() for s in st_a] if adagrad else None
+        d_e0 = torch.empty((w.B, w.D), dtype=torch.float32, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        plan = ops.BwdPlan(tabs_b, db.offsets, db.indices, w.B, db.e0, pooled, d_out, 0.01, d_e0=d_e0,
+                           status=status, row_state=st_b)
+        for _ in range(2):
+            res = ops.embbag_bwd_update(tabs_a, db.offsets, db.indices, w.B, db.e0, pooled, d_out, 0.01,
+                                        row_state=st_a)
+            plan.run()
+            torch.cuda.synchronize()
+            assert int(status.item()) == 0
+            assert torch.equal(res["d_e0"], d_e0)
+            U = int(res["num_unique"].item())
+            assert U == int(plan.num_unique.item())
+            assert torch.equal(res["unique_keys"][:U], plan.unique_keys[:U])
+            assert torch.equal(res["seg_offsets"][:U + 1], plan.seg_offsets[:U + 1])
+            for ta, tb in zip(tabs_a, tabs_b):
+                assert torch.equal(ta, tb)
+            if adagrad:
+                for sa, sb in zip(st_a, st_b):
+                    assert torch.equal(sa, sb)
