@@ -949,6 +949,24 @@ __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, c
   }
 }
 
+// Logical block of workgroup bid in the row-streaming kernel. The dispatcher
+// deals workgroups out round-robin over the 8 XCDs; here each XCD takes runs
+// of 16 consecutive logical blocks, interleaved with the other XCDs' runs. The
+// samples in flight at any time then form one compact window of the batch
+// (their offsets, indices and output lines likely share DRAM pages), while
+// neighbouring samples, which share offset and index cache lines, still meet
+// in one XCD's L2. On the 64-table capacity batch: 808 us with each XCD on one
+// contiguous eighth of the batch, 789-800 us in plain launch order (3.5% more
+// bytes fetched), 792-795 us with runs of 16. A ragged last group keeps the
+// plain order, so the map is a bijection on [0, n).
+__device__ __forceinline__ int run_block(int bid, int n) {
+  constexpr int kRun = 16, kSpan = 8 * kRun;
+  const int base = bid / kSpan * kSpan;
+  if (base + kSpan > n) return bid;
+  const int r = bid - base;
+  return base + (r % 8) * kRun + r / 8;
+}
+
 // Persistent workgroups: each takes a contiguous chunk of samples and runs,
 // per step, [gather | prefetch next offsets and e0] -> [carries, scan of the
 // next sample] -> [interaction | next sample's index loads in flight] ->
@@ -983,7 +1001,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
   float* outs = reinterpret_cast<float*>(gl + L.off_out);
   float* Z = reinterpret_cast<float*>(gl + L.off_z);
 
-  const int b_begin = xcd_block(blockIdx.x, gridDim.x) * chunk;
+  const int b_begin = run_block(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x)) * chunk;
   const int b_end = min(a.B, b_begin + chunk);
   if (b_begin >= b_end) return;  // whole workgroup
   // this group's sample in the step that starts at sample bs (past the chunk:
