@@ -57,6 +57,9 @@ def test_capacity_full_size_sampled_parity():
         torch.cuda.synchronize()
         assert status.item() == 0
         assert torch.equal(out, out2)  # run to run, bit for bit
+        # every sample was written: its e0 block is a bit copy of e0 (workgroups map to
+        # samples through a permutation of the launch order)
+        assert torch.equal(out[:, :w.D], d_e0)
         # offsets at full size: exact
         np.testing.assert_array_equal(offsets.cpu().numpy(), orc.lengths_to_offsets(lengths).astype(np.int32))
 

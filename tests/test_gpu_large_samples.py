@@ -50,6 +50,9 @@ def _check(w, lengths_override=None, exact=False):
     torch.cuda.synchronize()
     assert status.item() == 0
     assert torch.equal(out, out2)
+    # every sample was written: its e0 block is a bit copy of e0 (workgroups map to
+    # samples through a permutation of the launch order)
+    assert torch.equal(out[:, :w.D], e0)
     rng = np.random.default_rng(7)
     edges = [0, 1, 2, 3, w.B // 2 - 1, w.B // 2, w.B - 3, w.B - 2, w.B - 1]
     samples = np.unique(np.clip(np.concatenate([edges, rng.choice(w.B, 48, replace=False)]), 0, w.B - 1))
