@@ -107,6 +107,13 @@ int dlrm_lengths_to_offsets(int64_t n, const int32_t* lengths, int32_t* offsets,
 
 /*
  * Embedding-bag forward, optionally fused with the interaction.
+ * Defined by the "DLRM" note: section 2, The Architecture (one table per
+ * categorical feature, an ID selects one row, the bottom MLP yields e_0 in the
+ * embedding dimension); section 9, Weaknesses (a multi-valued feature is
+ * aggregated: here the bag's rows are summed, an empty bag gives zeros); and
+ * section 3, The Pairwise Interaction Layer (dot products of every pair of
+ * Z = [e_0, pooled_1 .. pooled_T], concatenated with e_0; the variant without
+ * self-pairs, i > j).
  *   T, B, D, dtype      as above
  *   tables   host array [T] of device pointers; table t is row-major [rows[t]][D] of dtype
  *   rows     host int64 [T], 1 <= rows[t] < 2^31
@@ -154,8 +161,11 @@ int dlrm_embbag_fwd_q8t(int32_t T, int32_t B, int32_t D, const void* const* tabl
                         const float* e0, float* out_pooled, float* out_inter, int32_t* status, void* stream);
 
 /*
- * Interaction alone, from pooled vectors in HBM.
- *   e0 device fp32 [B][D], pooled device fp32 [B][T][D], out device fp32 [B][D + P].
+ * Interaction alone, from pooled vectors in HBM ("DLRM" note, section 3, The
+ * Pairwise Interaction Layer: the dot products e_i . e_j of every pair i > j of
+ * Z = [e_0, e_1 .. e_T], concatenated with e_0).
+ *   e0 device fp32 [B][D], pooled device fp32 [B][T][D], out device fp32 [B][D + P]
+ *   in the layout given at the top of this file. D must be a multiple of 4, at most 1024.
  */
 int dlrm_interact(int32_t T, int32_t B, int32_t D, const float* e0, const float* pooled, float* out,
                   void* stream);
@@ -196,6 +206,12 @@ int dlrm_embbag_bwd_workspace_bytes(int32_t T, int32_t B, int32_t D, int64_t nnz
 
 /*
  * Sparse backward of the forward above followed by an SGD step on the touched rows.
+ * The "DLRM" note, section 5, Training, has the embedding tables trained with
+ * the rest of the model; the pages give no backward, so this is the exact
+ * gradient of dlrm_embbag_fwd's [e0 | dots]: dZ[b] = S[b] Z[b] with S[b] the
+ * symmetric matrix of the upstream pair gradients, then for each table row the
+ * sum of dZ over the bags that hold it (a bag holding the row k times counts it
+ * k times), then W <- W - lr * G (plain SGD, no momentum or decay).
  *   tables   host array [T] of device pointers, updated in place: for every row r of table t
  *            that the batch references, W_t[r] <- W_t[r] - lr * G, G = sum over the occurrences
  *            of (t, r) of dL/dpooled[b][t] (fp32 sum in a fixed order, result rounded to dtype).
@@ -208,14 +224,21 @@ int dlrm_embbag_bwd_workspace_bytes(int32_t T, int32_t B, int32_t D, int64_t nnz
  *   unique_keys  device int32 [nnz] or NULL: out, sorted distinct global rows
  *                (key = rows[0] + ... + rows[t-1] + r) in the first U entries
  *   seg_offsets  device int32 [nnz + 1] or NULL: out, occurrences of unique_keys[u] are
- *                perm[seg_offsets[u] .. seg_offsets[u+1]); seg_offsets[U] = nnz
+ *                perm[seg_offsets[u] .. seg_offsets[u+1]); seg_offsets[U] is the number of
+                occurrences with a valid index (= nnz for a valid batch; occurrences with an
+                out-of-range index are sorted after every valid one and belong to no segment)
  *   num_unique   device int32 [1] or NULL: out, U
  *                (the three segment outputs are built only when at least one is requested)
  *   perm     device int32 [nnz] or NULL: out, the stable order of occurrences by key
- *            (ties keep CSR order); this permutation is unique
+ *            (ties keep CSR order); this permutation is unique. Occurrences with an
+ *            out-of-range index come last, in CSR order
  *   workspace, ws_bytes  device scratch of at least dlrm_embbag_bwd_workspace_bytes() bytes
+ *            (no initial contents needed)
  * Requires sum(rows) < 2^31. Deterministic: identical inputs give bit-identical outputs.
- * Occurrences with an out-of-range index are dropped (and flagged).
+ * Occurrences with an out-of-range index are dropped (and DLRM_STATUS_BAD_INDEX set).
+ * With offsets that are not a valid CSR (DLRM_STATUS_BAD_OFFSETS set) every access still
+ * stays in bounds and rows that no index names are not written, but where bags overlap
+ * (decreasing offsets) the outputs and the update are unspecified.
  */
 int dlrm_embbag_bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables,
                            const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
@@ -242,6 +265,21 @@ int dlrm_embbag_bwd_update_adagrad(int32_t T, int32_t B, int32_t D, int32_t dtyp
                                    float* const* row_state, float* d_e0, int32_t* unique_keys, int32_t* seg_offsets,
                                    int32_t* num_unique, int32_t* perm, void* workspace, size_t ws_bytes,
                                    int32_t* status, void* stream);
+
+/*
+ * How dlrm_embbag_bwd_update / _adagrad will run for these sizes. Host only:
+ * no GPU call, nothing enqueued. plan is host int32 [4]:
+ *   plan[0]  digit width of the radix sort of the occurrences (8 or 9 bits)
+ *   plan[1]  sort passes (0 when nnz = 0)
+ *   plan[2]  1 when the interaction backward's samples run as extra workgroups
+ *            of the sort's launches, 0 when it is a launch of its own (one
+ *            sample's LDS does not fit beside the sort kernel's within 160 KiB)
+ *   plan[3]  largest LDS of any workgroup of the call, in bytes
+ *   want_segments  nonzero when the call will ask for unique_keys, seg_offsets or num_unique
+ * Returns DLRM_E_UNSUPPORTED when one sample's interaction backward alone exceeds 160 KiB.
+ */
+int dlrm_embbag_bwd_plan(int32_t T, int32_t B, int32_t D, int64_t nnz, const int64_t* rows, int32_t want_segments,
+                         int32_t* plan);
 
 /*
  * Host-side check of a bag description (host arrays): returns the DLRM_STATUS_* bits the

@@ -263,6 +263,24 @@ int dlrm_embbag_bwd_update_adagrad(int32_t T, int32_t B, int32_t D, int32_t dtyp
                     row_state, d_e0, unique_keys, seg_offsets, num_unique, perm, workspace, ws_bytes, status, stream);
 }
 
+int dlrm_embbag_bwd_plan(int32_t T, int32_t B, int32_t D, int64_t nnz, const int64_t* rows, int32_t want_segments,
+                         int32_t* plan) {
+  if (T < 1 || B < 1 || D < 1 || nnz < 0 || nnz >= kI32Max || !rows || !plan) return DLRM_E_INVAL;
+  if (T > DLRM_MAX_TABLES) return DLRM_E_UNSUPPORTED;
+  int64_t total = 0;
+  for (int t = 0; t < T; ++t) {
+    if (rows[t] < 1 || rows[t] >= kI32Max) return DLRM_E_INVAL;
+    total += rows[t];
+  }
+  if (total >= kI32Max) return DLRM_E_UNSUPPORTED;
+  const BwdPlanInfo p = bwd_plan(T, B, D, nnz, total, want_segments != 0);
+  plan[0] = p.radix_bits;
+  plan[1] = p.passes;
+  plan[2] = p.ibwd_shared ? 1 : 0;
+  plan[3] = static_cast<int32_t>(p.max_lds);
+  return p.ibwd_lds > kLds ? DLRM_E_UNSUPPORTED : DLRM_OK;
+}
+
 int dlrm_validate_bags(int32_t T, int32_t B, const int64_t* rows, const int32_t* offsets, const int32_t* indices,
                        int64_t nnz) {
   if (T < 1 || B < 1 || nnz < 0 || !rows || !offsets || (nnz > 0 && !indices)) return DLRM_E_INVAL;

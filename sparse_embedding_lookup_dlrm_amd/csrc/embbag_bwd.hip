@@ -216,11 +216,13 @@ __global__ __launch_bounds__(kBwdThreads) void build_keys(MutTableArgs tabs, int
   if (s0 > nnz) { s0 = nnz; bad_off = true; }
   if (s1 < 0) { s1 = 0; bad_off = true; }
   if (s1 > nnz) { s1 = nnz; bad_off = true; }
-  // Every position in [first offset, last offset) lies in some bag (bag j holds
-  // [o_j, max(o_j, o_j+1)) once clamped into [0, nnz]: a position x is in bag j
-  // for the last j with o_j <= x). The positions before the first offset or
-  // from the last offset on belong to no bag: the first and the last bag give
-  // them the sentinel key (only with invalid offsets).
+  // Bag j writes its range [o_j, max(o_j, o_j+1)) once clamped into [0, nnz].
+  // For a valid CSR the ranges tile [0, nnz). With invalid offsets (flagged)
+  // two things can happen. The positions before the first offset or from the
+  // last offset on belong to no bag: the first and the last bag give them the
+  // sentinel key. And where offsets decrease, the ranges of non-adjacent bags
+  // can overlap; a position covered twice then ends up with either bag's key
+  // (unspecified, as the header states), but every key written is in range.
   auto fill_gap = [&](long long g0, long long g1) {
     for (long long p = g0 + sub; p < g1; p += LG) {
       keys[p] = sentinel;
@@ -369,6 +371,16 @@ __global__ __launch_bounds__(kScanThreads) void radix_row_scan(const int32_t* __
   if (threadIdx.x == 0) row_total[blockIdx.x] = static_cast<int32_t>(carry);
 }
 
+// Static LDS of radix_scatter<BITS>. The host adds its size to the dynamic
+// LDS of the interaction-backward workgroups a scatter launch carries, so the
+// two must fit one workgroup's 160 KiB together.
+template <int BITS>
+struct ScatterLds {
+  int wcount[kRadixWaves][1 << BITS];                        // per-wave running digit counts
+  int gbase[1 << BITS];                                      // the tile's first output slot per digit
+  int lds[kRadixWaves * ((1 << BITS) / kBwdThreads)];        // digit-total scan across the waves
+};
+
 // Stable scatter of one tile. Wave w owns keys [tile + w*512, +512) and walks
 // them in rounds of 64 in their original order; equal digits inside a round
 // are ranked by lane with ballots, and a per-wave running count per digit
@@ -386,11 +398,12 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
                                                              int32_t* __restrict__ vals_out,
                                                              const int32_t* __restrict__ bag_of,
                                                              int32_t* __restrict__ src_out, IbwdShare ia) {
-  constexpr int kBins = 1 << BITS, kDPT = kBins / kBwdThreads;
+  constexpr int kBins = 1 << BITS;
   if (ibwd_extra(ia, ntiles)) return;
-  __shared__ int wcount[kRadixWaves][kBins];
-  __shared__ int gbase[kBins];
-  __shared__ int lds[kRadixWaves * kDPT];
+  __shared__ ScatterLds<BITS> sm;
+  auto& wcount = sm.wcount;
+  int* gbase = sm.gbase;
+  int* lds = sm.lds;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   for (int w = 0; w < kRadixWaves; ++w)
     for (int d = threadIdx.x; d < kBins; d += kBwdThreads) wcount[w][d] = 0;
@@ -489,6 +502,11 @@ __global__ __launch_bounds__(kBwdThreads) void build_segments(const int32_t* __r
   }
 }
 
+// Static LDS of build_segments_chunked (see ScatterLds).
+struct SegChunkedLds {
+  long long lds[kScanThreads / kWave];
+};
+
 // The same for up to 256 scan chunks, in one pass after the chunk totals:
 // each workgroup adds up the totals of the chunks before its own, scans its
 // chunk's head flags, and writes pos (pos[i] = heads before position i, pos[n]
@@ -503,7 +521,8 @@ __global__ __launch_bounds__(kScanThreads) void build_segments_chunked(const int
                                                                       IbwdShare ia) {
   static_assert(kScanThreads == kBwdThreads, "extra workgroups run the interaction backward");
   if (ibwd_extra(ia, nchunks)) return;
-  __shared__ long long lds[kScanThreads / kWave];
+  __shared__ SegChunkedLds sm;
+  long long* lds = sm.lds;
   const long long c0 = static_cast<long long>(blockIdx.x) * kScanChunk + threadIdx.x * kScanPerThread;
   // totals of the earlier chunks (at most 256, one per thread)
   const long long pv = threadIdx.x < blockIdx.x ? partial[threadIdx.x] : 0;
@@ -1108,10 +1127,14 @@ static size_t ibwd_lds(int T, int D) {
   return (static_cast<size_t>(F) * (D + 4) + static_cast<size_t>((F + 3) & ~3) * F) * 4;
 }
 
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;
+// room for the alignment of the dynamic LDS segment after a kernel's static one
+constexpr size_t kLdsSlack = 256;
+
 hipError_t launch_interact_bwd(int T, int B, int D, bool self_pairs, const float* e0, const float* pooled,
                                const float* d_out, float* d_e0, float* d_pooled, hipStream_t st) {
   const size_t lds = ibwd_lds(T, D);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  if (lds > kLdsPerWorkgroup) return hipErrorInvalidValue;
   const IbwdShare ia{T, D, self_pairs, e0, pooled, d_out, d_pooled, d_e0, 0, B};
   hipLaunchKernelGGL(interact_bwd_kernel, dim3(B), dim3(kBwdThreads), lds, st, ia);
   return hipGetLastError();
@@ -1119,6 +1142,27 @@ hipError_t launch_interact_bwd(int T, int B, int D, bool self_pairs, const float
 
 size_t bwd_workspace_bytes(int T, int B, int D, int64_t nnz, int64_t /*total_rows*/) {
   return layout(T, B, D, nnz).total;
+}
+
+// How a backward call runs, decided on the host from the sizes alone.
+BwdPlanInfo bwd_plan(int T, int B, int D, int64_t nnz, int64_t total_rows, bool want_segments) {
+  BwdPlanInfo p{};
+  const RadixPlan rp = radix_plan(total_rows);
+  p.radix_bits = rp.bits;
+  p.passes = nnz > 0 ? rp.passes : 0;
+  const long long red_chunks = (nnz + seg_chunk(seg_el(D)) - 1) / seg_chunk(seg_el(D));
+  p.fused_seg = nnz > 0 && want_segments && red_chunks <= kFusedSegChunks;
+  p.seg_one_pass = nnz > 0 && want_segments && !p.fused_seg && scan_chunks(nnz) <= kScanThreads;
+  const size_t ilds = ibwd_lds(T, D);
+  // the interaction backward's samples ride on the scatter launches (and the
+  // one-pass segment build) as extra workgroups when one sample's LDS fits
+  // beside those kernels' own static LDS; otherwise it is a launch of its own
+  size_t host_static = rp.bits == 9 ? sizeof(ScatterLds<9>) : sizeof(ScatterLds<8>);
+  if (p.seg_one_pass && sizeof(SegChunkedLds) > host_static) host_static = sizeof(SegChunkedLds);
+  p.ibwd_shared = nnz > 0 && host_static + kLdsSlack + ilds <= kLdsPerWorkgroup;
+  p.ibwd_lds = ilds;
+  p.max_lds = p.ibwd_shared ? host_static + kLdsSlack + ilds : (ilds > host_static ? ilds : host_static);
+  return p;
 }
 
 hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
@@ -1139,37 +1183,49 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   int32_t* nuniq = a.num_unique ? a.num_unique : reinterpret_cast<int32_t*>(ws + L.nuniq);
 
   const long long n = a.nnz;
-  const size_t ilds = ibwd_lds(a.T, a.D);
-  if (ilds > 160 * 1024) return hipErrorInvalidValue;
-  if (n == 0) {  // 1. interaction backward on its own; no keys
-    const hipError_t e = launch_interact_bwd(a.T, a.B, a.D, false, a.e0, a.pooled, a.d_out, a.d_e0, d_pooled, st);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(zero_segments, dim3(1), dim3(64), 0, st, seg, nuniq);
-    return hipGetLastError();
-  }
-  // 1. interaction backward, its samples shared out as extra workgroups over
-  // the sort passes' scatter launches (the longest of the sort; a share takes
-  // about as long as a scatter, and much longer than a count) and the one-pass
-  // segment build when that runs; nothing before the reduce reads its outputs
-  const RadixPlan plan = radix_plan(a.total_rows);
-  const int passes = plan.passes;
   const bool want_segments = a.unique_keys || a.seg_offsets || a.num_unique;
-  // segment outputs from the reduce's head counts, written by seg_combine
-  // (no launches of their own), when the reduce has few enough chunks
-  const long long red_chunks = (n + seg_chunk(seg_el(a.D)) - 1) / seg_chunk(seg_el(a.D));
-  const bool fused_seg = want_segments && red_chunks <= kFusedSegChunks;
+  const BwdPlanInfo plan = bwd_plan(a.T, a.B, a.D, n, a.total_rows, want_segments);
+  const size_t ilds = plan.ibwd_lds;
+  if (ilds > kLdsPerWorkgroup) return hipErrorInvalidValue;
+  hipError_t e = hipSuccess;
+  // every launch is checked before the next is queued: a later step must not
+  // run on the outputs of one that was never launched
+#define DLRM_CHECK_LAUNCH()                      \
+  do {                                           \
+    if ((e = hipGetLastError()) != hipSuccess) { \
+      return e;                                  \
+    }                                            \
+  } while (0)
+  if (n == 0 || !plan.ibwd_shared) {  // 1. interaction backward as a launch of its own
+    e = launch_interact_bwd(a.T, a.B, a.D, false, a.e0, a.pooled, a.d_out, a.d_e0, d_pooled, st);
+    if (e != hipSuccess) return e;
+    if (n == 0) {  // no keys
+      hipLaunchKernelGGL(zero_segments, dim3(1), dim3(64), 0, st, seg, nuniq);
+      return hipGetLastError();
+    }
+  }
+  // 1. otherwise the interaction backward's samples are shared out as extra
+  // workgroups over the sort passes' scatter launches (the longest of the
+  // sort; a share takes about as long as a scatter, and much longer than a
+  // count) and the one-pass segment build when that runs; nothing before the
+  // reduce reads its outputs
+  const int passes = plan.passes;
+  const bool fused_seg = plan.fused_seg;
   const long long nscan = scan_chunks(n);
-  const bool seg_one_pass = want_segments && !fused_seg && nscan <= kScanThreads;
-  const int nshare = passes + (seg_one_pass ? 1 : 0);
+  const bool seg_one_pass = plan.seg_one_pass;
+  const int nshare = plan.ibwd_shared ? passes + (seg_one_pass ? 1 : 0) : 0;
   int ishare = 0;
   const IbwdShare none{a.T, a.D, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
   auto share = [&]() {
+    if (nshare == 0) return none;
     IbwdShare ia{a.T, a.D, false, a.e0, a.pooled, a.d_out, d_pooled, a.d_e0, 0, 0};
     ia.first = static_cast<int>(static_cast<long long>(a.B) * ishare / nshare);
     ia.count = static_cast<int>(static_cast<long long>(a.B) * (ishare + 1) / nshare) - ia.first;
     ++ishare;
     return ia;
   };
+  // dynamic LDS only for a launch that carries interaction-backward workgroups
+  auto share_lds = [&](const IbwdShare& ia) -> size_t { return ia.count > 0 ? ilds : 0; };
   const int32_t sentinel = static_cast<int32_t>(a.total_rows);
   // 2. keys
   {
@@ -1191,12 +1247,13 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
       default: DLRM_BUILD_KEYS(1); break;
     }
 #undef DLRM_BUILD_KEYS
+    DLRM_CHECK_LAUNCH();
   }
-  // 3. radix sort, plan.bits (8 or 9) bits per pass
+  // 3. radix sort, plan.radix_bits (8 or 9) bits per pass
   const int ntiles = static_cast<int>((n + kRadixTile - 1) / kRadixTile);
   int cur = 0;
   for (int p = 0; p < passes; ++p) {
-    const int shift = p * plan.bits;
+    const int shift = p * plan.radix_bits;
     const bool inline_scan = ntiles <= kInlineScanTiles;
     // the last pass writes the permutation straight to the caller's array, if any
     int32_t* vout = (p + 1 == passes && a.perm) ? a.perm : vals[cur ^ 1];
@@ -1207,15 +1264,18 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
 #define DLRM_SORT_PASS(BITS)                                                                                          \
   do {                                                                                                                \
     hipLaunchKernelGGL(radix_count<BITS>, dim3(ntiles), blk, 0, st, keys[cur], n, shift, ntiles, counts, none);       \
+    DLRM_CHECK_LAUNCH();                                                                                              \
     if (!inline_scan) {                                                                                               \
       hipLaunchKernelGGL(radix_row_scan, dim3(1 << (BITS)), dim3(kScanThreads), 0, st, counts, ntiles, digit_off,      \
                          row_total);                                                                                  \
+      DLRM_CHECK_LAUNCH();                                                                                            \
     }                                                                                                                 \
-    hipLaunchKernelGGL(radix_scatter<BITS>, gs, blk, ilds, st, keys[cur], vals[cur], n, shift, ntiles, counts,         \
-                       inline_scan ? nullptr : digit_off, row_total, keys[cur ^ 1], vout, bag_of,                     \
+    hipLaunchKernelGGL(radix_scatter<BITS>, gs, blk, share_lds(ia_scatter), st, keys[cur], vals[cur], n, shift,       \
+                       ntiles, counts, inline_scan ? nullptr : digit_off, row_total, keys[cur ^ 1], vout, bag_of,     \
                        last_pass ? src_bag : nullptr, ia_scatter);                                                    \
+    DLRM_CHECK_LAUNCH();                                                                                              \
   } while (0)
-    if (plan.bits == 9) DLRM_SORT_PASS(9);
+    if (plan.radix_bits == 9) DLRM_SORT_PASS(9);
     else DLRM_SORT_PASS(8);
 #undef DLRM_SORT_PASS
     cur ^= 1;
@@ -1229,16 +1289,21 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
     if (seg_one_pass) {  // chunk totals, then one pass that scans and builds the segments
       hipLaunchKernelGGL((scan_chunk_totals<HeadIn>), dim3(static_cast<unsigned>(m)), dim3(kScanThreads), 0, st,
                          HeadIn{skeys, sentinel}, n, partial);
+      DLRM_CHECK_LAUNCH();
       const IbwdShare ia_seg = share();
-      hipLaunchKernelGGL(build_segments_chunked, dim3(static_cast<unsigned>(m) + ia_seg.count), dim3(kScanThreads), ilds,
-                         st, skeys, n, sentinel, partial, pos, uniq, seg, nuniq, static_cast<int>(m), ia_seg);
+      hipLaunchKernelGGL(build_segments_chunked, dim3(static_cast<unsigned>(m) + ia_seg.count), dim3(kScanThreads),
+                         share_lds(ia_seg), st, skeys, n, sentinel, partial, pos, uniq, seg, nuniq,
+                         static_cast<int>(m), ia_seg);
+      DLRM_CHECK_LAUNCH();
     } else {
-      hipError_t e = device_exclusive_scan(HeadIn{skeys, sentinel}, n, pos, partial, a.status, 0, st);
+      e = device_exclusive_scan(HeadIn{skeys, sentinel}, n, pos, partial, a.status, 0, st);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(build_segments, dim3(static_cast<unsigned>((n + kBwdThreads - 1) / kBwdThreads)),
                          dim3(kBwdThreads), 0, st, skeys, n, sentinel, pos, uniq, seg, nuniq);
+      DLRM_CHECK_LAUNCH();
     }
   }
+#undef DLRM_CHECK_LAUNCH
   // 5. reduce + SGD (and the segment outputs with fused_seg)
   const SegOut so = fused_seg ? SegOut{reinterpret_cast<int32_t*>(ws + L.hcount), reinterpret_cast<int32_t*>(ws + L.hwg),
                                        uniq, seg, nuniq, n, sentinel}

@@ -53,6 +53,7 @@ _SIGNATURES = {
                                                       _P(_c_void_p), _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                                       _c_void_p, _c_void_p, _size_t, _c_void_p, _c_void_p]),
     "dlrm_validate_bags": (ctypes.c_int, [_i32, _i32, _P(_i64), _P(_i32), _P(_i32), _i64]),
+    "dlrm_embbag_bwd_plan": (ctypes.c_int, [_i32, _i32, _i32, _i64, _P(_i64), _i32, _P(_i32)]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -116,6 +117,24 @@ def _require_cuda(*ts):
             raise ValueError("device tensors must be contiguous CUDA (HIP) tensors")
 
 
+def _expect(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, numel: int, at_least: bool = False) -> None:
+    """Size and dtype of a tensor handed to the C ABI, which takes raw pointers and cannot
+    see an undersized buffer: checked here, before any call."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    n = t.numel()
+    if (n < numel) if at_least else (n != numel):
+        raise ValueError(f"{name} has {n} elements, needs {'at least ' if at_least else ''}{numel}")
+
+
+def _check_bags(offsets: torch.Tensor, indices: torch.Tensor, T: int, B: int) -> None:
+    _expect(offsets, "offsets", torch.int32, T * B + 1)
+    if indices.dtype != torch.int32:
+        raise ValueError(f"indices must be torch.int32, got {indices.dtype}")
+
+
 def _table_args(tables: Sequence[torch.Tensor]):
     T = len(tables)
     if T < 1:
@@ -127,7 +146,6 @@ def _table_args(tables: Sequence[torch.Tensor]):
     for t in tables:
         if t.dtype != dt or t.dim() != 2 or t.shape[1] != D:
             raise ValueError("all tables must be 2-D with the same dtype and width")
-    _require_cuda(*tables)
     ptrs = (_c_void_p * T)(*[t.data_ptr() for t in tables])
     rows = (_i64 * T)(*[t.shape[0] for t in tables])
     return T, D, _TORCH_DT[dt], ptrs, rows
@@ -141,14 +159,24 @@ def pair_count(T: int) -> int:
 def lengths_to_offsets(lengths: torch.Tensor, offsets: Optional[torch.Tensor] = None,
                        status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """int32 bag lengths (device) -> int32 CSR offsets (device, n + 1 entries)."""
-    _require_cuda(lengths)
-    assert lengths.dtype == torch.int32
+    _expect(lengths, "lengths", torch.int32, lengths.numel())
     n = lengths.numel()
+    _expect(offsets, "offsets", torch.int32, n + 1)
+    _expect(status, "status", torch.int32, 1, at_least=True)
+    _require_cuda(lengths, offsets, status)
     if offsets is None:
         offsets = torch.empty(n + 1, dtype=torch.int32, device=lengths.device)
     _check(lib().dlrm_lengths_to_offsets(n, _ptr(lengths), _ptr(offsets), _ptr(status), _stream(stream)),
            "dlrm_lengths_to_offsets")
     return offsets
+
+
+def _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status, P=None):
+    _check_bags(offsets, indices, T, B)
+    _expect(e0, "e0", torch.float32, B * D)
+    _expect(out_pooled, "out_pooled", torch.float32, B * T * D)
+    _expect(out_inter, "out_inter", torch.float32, B * (D + (pair_count(T) if P is None else P)))
+    _expect(status, "status", torch.int32, 1, at_least=True)
 
 
 def embbag_fwd(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: torch.Tensor, B: int,
@@ -157,10 +185,8 @@ def embbag_fwd(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: t
                status: Optional[torch.Tensor] = None, stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Embedding-bag forward; returns (pooled [B,T,D] or None, [e0 | dots] [B, D+P] or None)."""
     T, D, dt, ptrs, rows = _table_args(tables)
-    _require_cuda(offsets, indices, e0, out_pooled, out_inter, status)
-    assert offsets.dtype == torch.int32 and indices.dtype == torch.int32
-    if offsets.numel() != T * B + 1:
-        raise ValueError("offsets must have T*B + 1 entries")
+    _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status)
+    _require_cuda(*tables, offsets, indices, e0, out_pooled, out_inter, status)
     dev = tables[0].device
     if want_pooled and out_pooled is None:
         out_pooled = torch.empty((B, T, D), dtype=torch.float32, device=dev)
@@ -185,6 +211,7 @@ def embbag_fwd_q8(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices
     for t in tables:
         if t.dtype != torch.uint8 or t.dim() != 2 or t.shape[1] != D + 8 or not t.is_contiguous():
             raise ValueError("8-bit tables must be contiguous uint8 [rows, D + 8] with the same D")
+    _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status)
     _require_cuda(*tables, offsets, indices, e0, out_pooled, out_inter, status)
     ptrs = (_c_void_p * T)(*[t.data_ptr() for t in tables])
     rows = (_i64 * T)(*[t.shape[0] for t in tables])
@@ -215,6 +242,7 @@ def embbag_fwd_q8t(tables: Sequence[torch.Tensor], scale_bias, offsets: torch.Te
     sb = [float(v) for pair in scale_bias for v in pair]
     if len(sb) != 2 * T:
         raise ValueError("need one (scale, bias) pair per table")
+    _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status)
     _require_cuda(*tables, offsets, indices, e0, out_pooled, out_inter, status)
     ptrs = (_c_void_p * T)(*[t.data_ptr() for t in tables])
     rows = (_i64 * T)(*[t.shape[0] for t in tables])
@@ -234,11 +262,14 @@ def interact(e0: torch.Tensor, pooled: torch.Tensor, out: Optional[torch.Tensor]
              self_pairs: bool = False) -> torch.Tensor:
     """[e0 | lower-triangle dots of Z = [e0; pooled]] from pooled [B, T, D] fp32: pairs i > j
     (dlrm_interact), or i >= j with self_pairs (dlrm_interact_ex)."""
-    _require_cuda(e0, pooled, out)
     B, T, D = pooled.shape
     F = T + 1
+    P = F * (F + 1) // 2 if self_pairs else F * (F - 1) // 2
+    _expect(pooled, "pooled", torch.float32, B * T * D)
+    _expect(e0, "e0", torch.float32, B * D)
+    _expect(out, "out", torch.float32, B * (D + P))
+    _require_cuda(e0, pooled, out)
     if out is None:
-        P = F * (F + 1) // 2 if self_pairs else F * (F - 1) // 2
         out = torch.empty((B, D + P), dtype=torch.float32, device=pooled.device)
     if self_pairs:
         _check(lib().dlrm_interact_ex(T, B, D, 1, _ptr(e0), _ptr(pooled), _ptr(out), _stream(stream)),
@@ -252,8 +283,15 @@ def interact_bwd(e0: torch.Tensor, pooled: torch.Tensor, d_out: torch.Tensor, se
                  d_e0: Optional[torch.Tensor] = None, d_pooled: Optional[torch.Tensor] = None,
                  want_d_e0: bool = True, stream=None) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
     """(dL/de0, dL/dpooled) of the interaction from dL/dout (dlrm_interact_bwd)."""
-    _require_cuda(e0, pooled, d_out, d_e0, d_pooled)
     B, T, D = pooled.shape
+    F = T + 1
+    P = F * (F + 1) // 2 if self_pairs else F * (F - 1) // 2
+    _expect(pooled, "pooled", torch.float32, B * T * D)
+    _expect(e0, "e0", torch.float32, B * D)
+    _expect(d_out, "d_out", torch.float32, B * (D + P))
+    _expect(d_e0, "d_e0", torch.float32, B * D)
+    _expect(d_pooled, "d_pooled", torch.float32, B * T * D)
+    _require_cuda(e0, pooled, d_out, d_e0, d_pooled)
     if d_pooled is None:
         d_pooled = torch.empty((B, T, D), dtype=torch.float32, device=pooled.device)
     if d_e0 is None and want_d_e0:
@@ -271,6 +309,23 @@ def bwd_workspace_bytes(T: int, B: int, D: int, nnz: int, rows: Sequence[int]) -
     return out.value
 
 
+def _check_bwd_buffers(T, B, D, offsets, indices, e0, pooled, d_out, d_e0, status):
+    _check_bags(offsets, indices, T, B)
+    _expect(e0, "e0", torch.float32, B * D)
+    _expect(pooled, "pooled", torch.float32, B * T * D)
+    _expect(d_out, "d_out", torch.float32, B * (D + pair_count(T)))
+    _expect(d_e0, "d_e0", torch.float32, B * D)
+    _expect(status, "status", torch.int32, 1, at_least=True)
+
+
+def bwd_plan(T: int, B: int, D: int, nnz: int, rows: Sequence[int], want_segments: bool = True) -> dict:
+    """How the sparse backward will run for these sizes (dlrm_embbag_bwd_plan; host only)."""
+    plan = (_i32 * 4)()
+    _check(lib().dlrm_embbag_bwd_plan(T, B, D, nnz, (_i64 * T)(*rows), 1 if want_segments else 0, plan),
+           "dlrm_embbag_bwd_plan")
+    return {"radix_bits": plan[0], "passes": plan[1], "interact_bwd_shared": bool(plan[2]), "max_lds": plan[3]}
+
+
 def embbag_bwd_update(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: torch.Tensor, B: int,
                       e0: torch.Tensor, pooled: torch.Tensor, d_out: torch.Tensor, lr: float, *,
                       want_d_e0: bool = True, want_segments: bool = True, workspace: Optional[torch.Tensor] = None,
@@ -280,7 +335,7 @@ def embbag_bwd_update(tables: Sequence[torch.Tensor], offsets: torch.Tensor, ind
     row-wise AdaGrad when row_state (one fp32 [rows_t] tensor per table, updated in
     place) is given (dlrm_embbag_bwd_update_adagrad)."""
     T, D, dt, ptrs, rows = _table_args(tables)
-    _require_cuda(offsets, indices, e0, pooled, d_out, workspace, status)
+    _check_bwd_buffers(T, B, D, offsets, indices, e0, pooled, d_out, None, status)
     if row_state is not None:
         if len(row_state) != T:
             raise ValueError("row_state needs one tensor per table")
@@ -291,6 +346,8 @@ def embbag_bwd_update(tables: Sequence[torch.Tensor], offsets: torch.Tensor, ind
     nnz = indices.numel()
     dev = tables[0].device
     need = bwd_workspace_bytes(T, B, D, nnz, [t.shape[0] for t in tables])
+    _expect(workspace, "workspace", torch.uint8, need, at_least=True)
+    _require_cuda(*tables, offsets, indices, e0, pooled, d_out, workspace, status)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     res = {"d_e0": torch.empty((B, D), dtype=torch.float32, device=dev) if want_d_e0 else None}
@@ -335,7 +392,8 @@ class FwdPlan:
     def __init__(self, tables, offsets, indices, B, e0=None, *, out_pooled=None, out_inter=None, status=None,
                  stream=None):
         T, D, dt, ptrs, rows = _table_args(tables)
-        _require_cuda(offsets, indices, e0, out_pooled, out_inter, status)
+        _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status)
+        _require_cuda(*tables, offsets, indices, e0, out_pooled, out_inter, status)
         self._keep = (tables, offsets, indices, e0, out_pooled, out_inter, status, ptrs, rows)
         self._args = (T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(), _ptr(e0),
                       _ptr(out_pooled), _ptr(out_inter), _ptr(status), _stream(stream))
@@ -358,10 +416,12 @@ class BwdPlan:
         self.seg_offsets = torch.empty(nnz + 1, dtype=torch.int32, device=dev)
         self.num_unique = torch.empty(1, dtype=torch.int32, device=dev)
         self.perm = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+        need = bwd_workspace_bytes(T, B, D, nnz, [t.shape[0] for t in tables])
+        _expect(workspace, "workspace", torch.uint8, need, at_least=True)
         if workspace is None:
-            need = bwd_workspace_bytes(T, B, D, nnz, [t.shape[0] for t in tables])
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-        _require_cuda(offsets, indices, e0, pooled, d_out, d_e0, workspace, status)
+        _check_bwd_buffers(T, B, D, offsets, indices, e0, pooled, d_out, d_e0, status)
+        _require_cuda(*tables, offsets, indices, e0, pooled, d_out, d_e0, workspace, status)
         opt = ()
         sptr = None
         self._name = "dlrm_embbag_bwd_update"

@@ -121,3 +121,97 @@ def test_host_validator_matches_oracle(seed):
         idx[-1] = -3
     want = orc.bag_status(T, B, rows, off, idx)
     assert ops.validate_bags(T, B, rows, off, idx) == want
+
+
+def _ibwd_lds(T, D):
+    F = T + 1
+    return (F * (D + 4) + ((F + 3) & ~3) * F) * 4
+
+
+def test_bwd_plan_interaction_backward_placement(lib):
+    """The interaction backward rides on the sort's launches only where one sample's LDS fits
+    beside the sort kernel's own within 160 KiB; otherwise it is a launch of its own."""
+    # 26 fp32 tables, D = 128, 22-bit keys: three 8-bit passes, shared
+    p = ops.bwd_plan(26, 2048, 128, 53248, [40_000] * 26)
+    assert (p["radix_bits"], p["passes"], p["interact_bwd_shared"]) == (8, 3, True)
+    assert p["max_lds"] <= 160 * 1024
+    # 68 tables, D = 512: one sample's tile (152 KiB) plus the scatter's static LDS exceeds 160 KiB
+    assert _ibwd_lds(68, 512) <= 160 * 1024
+    p = ops.bwd_plan(68, 16, 512, 1000, [2000] * 68)
+    assert p["interact_bwd_shared"] is False
+    assert p["max_lds"] <= 160 * 1024
+    # 65 tables, D = 512, 17-bit keys: two 9-bit passes (their scatter keeps 10 KiB of LDS): own launch
+    p = ops.bwd_plan(65, 24, 512, 800, [2000] * 65)
+    assert (p["radix_bits"], p["passes"], p["interact_bwd_shared"]) == (9, 2, False)
+    # the same with 24-bit keys (three 8-bit passes, a 5 KiB scatter): still too large together
+    p = ops.bwd_plan(65, 24, 512, 800, [200_000] * 65)
+    assert (p["radix_bits"], p["passes"]) == (8, 3)
+    assert p["interact_bwd_shared"] is (_ibwd_lds(65, 512) + 5136 + 256 <= 160 * 1024)
+    # no occurrences: no sort passes, the interaction backward runs alone
+    p = ops.bwd_plan(4, 8, 16, 0, [10] * 4)
+    assert p["passes"] == 0 and p["interact_bwd_shared"] is False
+    # one sample's tile alone beyond 160 KiB
+    plan = (ctypes.c_int32 * 4)()
+    rows = (ctypes.c_int64 * 128)(*([10] * 128))
+    assert lib.dlrm_embbag_bwd_plan(128, 4, 512, 8, rows, 1, plan) == E_UNSUPPORTED
+    assert lib.dlrm_embbag_bwd_plan(0, 4, 512, 8, rows, 1, plan) == E_INVAL
+
+
+def test_binding_rejects_wrong_sized_buffers_before_any_call():
+    """The C ABI takes raw pointers and cannot see an undersized caller buffer, so the
+    binding checks every buffer's element count and dtype first (host tensors here: the
+    size check fires before the device check)."""
+    import torch
+
+    T, B, D = 3, 4, 16
+    P = ops.pair_count(T)
+    tabs = [torch.zeros((10, D), dtype=torch.float32) for _ in range(T)]
+    off = torch.zeros(T * B + 1, dtype=torch.int32)
+    idx = torch.zeros(0, dtype=torch.int32)
+    e0 = torch.zeros((B, D), dtype=torch.float32)
+
+    def fwd(**kw):
+        args = dict(offsets=off, indices=idx, e0=e0)
+        args.update(kw)
+        return ops.embbag_fwd(tabs, args["offsets"], args["indices"], B, args["e0"],
+                              out_inter=kw.get("out_inter"), out_pooled=kw.get("out_pooled"),
+                              status=kw.get("status"))
+
+    with pytest.raises(ValueError, match="offsets has"):
+        fwd(offsets=torch.zeros(T * B, dtype=torch.int32))
+    with pytest.raises(ValueError, match="offsets must be"):
+        fwd(offsets=torch.zeros(T * B + 1, dtype=torch.int64))
+    with pytest.raises(ValueError, match="indices must be"):
+        fwd(indices=torch.zeros(3, dtype=torch.int64))
+    with pytest.raises(ValueError, match="e0 has"):
+        fwd(e0=torch.zeros((B - 1, D), dtype=torch.float32))
+    with pytest.raises(ValueError, match="out_inter has"):
+        fwd(out_inter=torch.zeros((B, D + P - 1), dtype=torch.float32))
+    with pytest.raises(ValueError, match="out_pooled has"):
+        fwd(out_pooled=torch.zeros((B, T, D - 4), dtype=torch.float32))
+    with pytest.raises(ValueError, match="out_pooled must be"):
+        fwd(out_pooled=torch.zeros((B, T, D), dtype=torch.float16))
+    with pytest.raises(ValueError, match="status has"):
+        fwd(status=torch.zeros(0, dtype=torch.int32))
+    # correctly sized host tensors pass the size checks and stop at the device check
+    with pytest.raises(ValueError, match="CUDA"):
+        fwd(out_inter=torch.zeros((B, D + P), dtype=torch.float32))
+
+    pooled = torch.zeros((B, T, D), dtype=torch.float32)
+    d_out = torch.zeros((B, D + P), dtype=torch.float32)
+    with pytest.raises(ValueError, match="pooled has"):
+        ops.embbag_bwd_update(tabs, off, idx, B, e0, pooled[:, :-1], d_out, 0.01)
+    with pytest.raises(ValueError, match="d_out has"):
+        ops.embbag_bwd_update(tabs, off, idx, B, e0, pooled, d_out[:, :-1], 0.01)
+    with pytest.raises(ValueError, match="workspace has"):
+        ops.embbag_bwd_update(tabs, off, idx, B, e0, pooled, d_out, 0.01, workspace=torch.zeros(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="d_e0 has"):
+        ops.BwdPlan(tabs, off, idx, B, e0, pooled, d_out, 0.01, d_e0=torch.zeros(B * D - 1))
+    with pytest.raises(ValueError, match="CUDA"):
+        ops.embbag_bwd_update(tabs, off, idx, B, e0, pooled, d_out, 0.01)
+    with pytest.raises(ValueError, match="out has"):
+        ops.interact(e0, pooled, out=torch.zeros((B, D + P + 1), dtype=torch.float32))
+    with pytest.raises(ValueError, match="d_pooled has"):
+        ops.interact_bwd(e0, pooled, d_out, d_pooled=torch.zeros((B, T, D + 4), dtype=torch.float32))
+    with pytest.raises(ValueError, match="lengths must be"):
+        ops.lengths_to_offsets(torch.zeros(4, dtype=torch.int64))

@@ -25,10 +25,10 @@ def _round_storage(x64, dtype):
     return x32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def run_bwd(w: synth.Workload, lr=0.01, exact=False, twice=False):
+def run_bwd(w: synth.Workload, lr=0.01, exact=False, twice=False, fused_fwd=True):
     b = synth.make_batch(w, with_dout=True)
     db = DeviceBatch(b)
-    pooled, _ = db.fwd(want_pooled=True)
+    pooled, _ = db.fwd(want_pooled=True, want_inter=fused_fwd)
     d_out = torch.from_numpy(b.dout).cuda()
     before = [t.clone() for t in db.tables]
     res = ops.embbag_bwd_update(db.tables, db.offsets, db.indices, w.B, db.e0, pooled, d_out, lr, status=db.status)
@@ -411,3 +411,87 @@ def test_backward_plan_matches_call_sgd_and_adagrad():
             if adagrad:
                 for sa, sb in zip(st_a, st_b):
                     assert torch.equal(sa, sb)
+
+
+def test_backward_interaction_backward_own_launch():
+    """65 bf16 tables with D = 512 and 17-bit keys (two 9-bit sort passes): one sample's
+    interaction-backward LDS does not fit beside the 9-bit scatter's own within 160 KiB, so
+    the interaction backward runs as a launch of its own instead of riding on the sort's."""
+    w = synth.Workload("ibwd-own-65t-d512-bf16", T=65, rows=2000, D=512, dtype="bf16", B=24, bag=("uniform", 0, 4),
+                       dist=("zipf", 1.1), seed=655)
+    nnz = int(synth.make_batch(w).indices.size)
+    p = ops.bwd_plan(w.T, w.B, w.D, nnz, [2000] * w.T)
+    assert (p["radix_bits"], p["passes"], p["interact_bwd_shared"]) == (9, 2, False)
+    run_bwd(w, lr=0.01, twice=True, fused_fwd=False)
+
+
+@pytest.mark.parametrize("dtype,T,D", [("f32", 5, 32), ("bf16", 26, 128)])
+def test_backward_out_of_range_indices_dropped(dtype, T, D):
+    """One out-of-range index per table (one of them negative): the status carries the
+    bad-index bit, and perm, the distinct rows, the segment bounds and U equal the oracle's
+    on the batch without those occurrences (positions mapped back; the dropped ones sort
+    last, in CSR order, and seg_offsets[U] counts the valid occurrences only); d_e0 and the
+    updated rows match within tolerance; rows nothing references stay bit-identical."""
+    w = synth.Workload("badidx", T=T, rows=300, D=D, dtype=dtype, B=64, bag=("uniform", 1, 6),
+                       dist=("zipf", 1.1), seed=T * 7 + D)
+    b = synth.make_batch(w, with_dout=True)
+    off = orc.lengths_to_offsets(b.lengths)
+    idx = b.indices.copy()
+    rng = np.random.default_rng(w.seed)
+    bad = []
+    for t in range(T):
+        p = int(rng.integers(off[t * w.B], off[(t + 1) * w.B]))
+        idx[p] = -1 - int(rng.integers(0, 5)) if t == 1 else 300 + int(rng.integers(0, 50))
+        bad.append(p)
+    bad = np.array(sorted(bad))
+    keep = np.ones(len(idx), bool)
+    keep[bad] = False
+    # the valid sub-batch the oracle sees
+    sub_len = np.array([int(keep[off[i]:off[i + 1]].sum()) for i in range(T * w.B)], dtype=np.int32)
+    sub_off = orc.lengths_to_offsets(sub_len)
+    sub_idx = idx[keep]
+    fwd = orc.embbag_fwd(b.tables, dtype, w.B, sub_off, sub_idx, b.e0)
+    r = orc.embbag_bwd_update(b.tables, dtype, w.B, sub_off, sub_idx, b.e0, fwd["pooled"], b.dout, 0.01)
+    at = abs_tables(b.tables, dtype)
+    pm = orc.embbag_pool(at, dtype, w.B, sub_off, sub_idx)
+    rm = orc.embbag_bwd_update(at, dtype, w.B, sub_off, sub_idx, np.abs(b.e0), pm, np.abs(b.dout), 0.01)
+
+    db = DeviceBatch(b)
+    db.indices = torch.from_numpy(idx).cuda()
+    db.status.zero_()
+    pooled, _ = db.fwd(want_pooled=True)
+    torch.cuda.synchronize()
+    assert db.status.item() == ops.STATUS_BAD_INDEX
+    d_out = torch.from_numpy(b.dout).cuda()
+    before = [t.clone() for t in db.tables]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = ops.embbag_bwd_update(db.tables, db.offsets, db.indices, w.B, db.e0, pooled, d_out, 0.01, status=st)
+    torch.cuda.synchronize()
+    assert st.item() == ops.STATUS_BAD_INDEX
+    nnz = len(idx)
+    kept_pos = np.flatnonzero(keep)
+    want_perm = np.concatenate([kept_pos[r["perm"]], bad]).astype(np.int32)
+    np.testing.assert_array_equal(res["perm"].cpu().numpy()[:nnz], want_perm)
+    U = int(res["num_unique"].item())
+    assert U == len(r["unique_keys"])
+    np.testing.assert_array_equal(res["unique_keys"].cpu().numpy()[:U], r["unique_keys"].astype(np.int32))
+    np.testing.assert_array_equal(res["seg_offsets"].cpu().numpy()[:U + 1], r["seg_offsets"].astype(np.int32))
+    assert int(res["seg_offsets"][U].item()) == nnz - len(bad)
+    rtol = RTOL[dtype]
+    assert_mag_close(res["d_e0"].cpu().numpy(), r["d_e0"], np.abs(b.dout[:, :D]) + rm["dZ"][:, 0], rtol, "d_e0")
+    after = host_tables(db.tables, dtype)
+    orig = host_tables(before, dtype)
+    base = r["base"]
+    keys = np.asarray(r["unique_keys"], dtype=np.int64)
+    tix = np.searchsorted(base, keys, side="right") - 1
+    rix = keys - base[tix]
+    touched = [np.zeros(t.shape[0], bool) for t in orig]
+    for t, i in zip(tix, rix):
+        touched[t][i] = True
+    for t in range(T):
+        np.testing.assert_array_equal(after[t][~touched[t]], orig[t][~touched[t]])
+    got_rows = np.array([orc.decode(after[t][i][None], dtype)[0] for t, i in zip(tix, rix)]).reshape(U, D)
+    W_mag = np.abs(np.array([orc.decode(orig[t][i][None], dtype)[0] for t, i in zip(tix, rix)]).reshape(U, D))
+    store_ulp = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[dtype]
+    lim_mag = W_mag + 0.01 * rm["grad"] + (store_ulp / rtol) * np.abs(r["new_rows"])
+    assert_mag_close(got_rows, r["new_rows"], lim_mag, rtol, "updated rows")

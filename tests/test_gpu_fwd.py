@@ -205,3 +205,32 @@ def test_scaling_tables_by_two_is_exact():
     torch.cuda.synchronize()
     assert torch.equal(p2, p1 * 2)
     assert torch.equal(i2[:, w.D:], i1[:, w.D:] * 4)
+
+
+@pytest.mark.parametrize("T,D,dtype,B", [(64, 128, "bf16", 40), (26, 128, "f32", 70), (4, 16, "f32", 128),
+                                         (8, 64, "f16", 300)])
+def test_all_bags_empty_nnz_zero(T, D, dtype, B):
+    """Every bag empty (nnz = 0, no index array at all): the row-streaming kernel (bf16
+    T = 64 and fp32 T = 26 at D = 128, fp16 D = 64 in sample groups) and the narrow-row
+    kernel (fp32 D = 16) write [e0 | 0 ...] exactly, the pooled output is all +0, and the
+    status stays 0."""
+    w = synth.Workload("empty", T=T, rows=50, D=D, dtype=dtype, B=B, bag=("fixed", 0), dist=("uniform",), seed=T + D)
+    b = synth.make_batch(w)
+    assert len(b.indices) == 0
+    db = DeviceBatch(b)
+    P = ops.pair_count(T)
+    out_inter = torch.full((B, D + P), float("nan"), dtype=torch.float32, device="cuda")
+    out_pooled = torch.full((B, T, D), float("nan"), dtype=torch.float32, device="cuda")
+    db.status.zero_()
+    ops.embbag_fwd(db.tables, db.offsets, db.indices, B, db.e0, out_pooled=out_pooled, out_inter=out_inter,
+                   status=db.status)
+    _, inter2 = db.fwd()
+    torch.cuda.synchronize()
+    assert db.status.item() == 0
+    got = out_inter.cpu().numpy()
+    np.testing.assert_array_equal(got[:, :D], b.e0)
+    assert np.all(got[:, D:] == 0.0) and not np.any(np.signbit(got[:, D:]))
+    p = out_pooled.cpu().numpy()
+    assert np.all(p == 0.0) and not np.any(np.signbit(p))
+    assert torch.equal(inter2, out_inter)
+    check_fwd(db, out_pooled, out_inter, exact=True)
