@@ -74,8 +74,12 @@ typedef enum {
   DLRM_E_UNSUPPORTED = -2, /* dtype, D or T outside what the kernels handle */
   DLRM_E_WORKSPACE = -3,   /* workspace smaller than dlrm_embbag_bwd_workspace_bytes() */
   DLRM_E_HIP = -4,         /* a HIP runtime call or kernel launch failed */
-  DLRM_E_ALIGN = -5        /* a device pointer is not 16-byte aligned */
+  DLRM_E_ALIGN = -5,       /* a device pointer is not 16-byte aligned */
+  DLRM_E_SCRATCH = -6      /* the batch needs more scratch than the allocation-free entry point holds */
 } dlrm_status;
+
+/* Bytes of the library-owned scratch array behind dlrm_embbag_bwd_update_noalloc (one per GPU). */
+#define DLRM_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* DLRM_Q8: row-wise 8-bit tables (only through dlrm_embbag_fwd_q8): a row is D uint8 codes q
  * followed by its fp32 scale and fp32 bias, value = scale * q + bias.
@@ -245,6 +249,27 @@ int dlrm_embbag_bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void*
                            const float* e0, const float* pooled, const float* d_out, float lr, float* d_e0,
                            int32_t* unique_keys, int32_t* seg_offsets, int32_t* num_unique, int32_t* perm,
                            void* workspace, size_t ws_bytes, int32_t* status, void* stream);
+
+/*
+ * dlrm_embbag_bwd_update for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid it): the
+ * same arguments minus the workspace, the same results bit for bit. The scratch
+ * the call needs lives in a static device array of DLRM_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that the library owns; each GPU the library runs on holds its own
+ * copy until the process ends. The call allocates nothing (no hipMalloc, no
+ * library routine that allocates).
+ *   Returns DLRM_E_SCRATCH, touching nothing, when dlrm_embbag_bwd_workspace_bytes()
+ *   for these sizes exceeds DLRM_NOALLOC_SCRATCH_BYTES (for D = 128 fp32 gradients
+ *   that is about 2,000 samples of 26 tables).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents
+ * (the call needs none of them): calls that overlap on one GPU (different streams,
+ * or threads) race and must be serialised by the caller.
+ */
+int dlrm_embbag_bwd_update_noalloc(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables,
+                                   const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                                   const float* e0, const float* pooled, const float* d_out, float lr, float* d_e0,
+                                   int32_t* unique_keys, int32_t* seg_offsets, int32_t* num_unique, int32_t* perm,
+                                   int32_t* status, void* stream);
 
 /*
  * The same backward with a row-wise AdaGrad step instead of SGD ("DLRM" note,

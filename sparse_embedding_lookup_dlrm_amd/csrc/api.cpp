@@ -117,6 +117,7 @@ const char* dlrm_status_string(int status) {
     case DLRM_E_WORKSPACE: return "workspace too small";
     case DLRM_E_HIP: return "HIP runtime error";
     case DLRM_E_ALIGN: return "device pointer not 16-byte aligned";
+    case DLRM_E_SCRATCH: return "batch needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }
@@ -251,6 +252,24 @@ int dlrm_embbag_bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void*
                            int32_t* status, void* stream) {
   return bwd_update(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, pooled, d_out, lr, kSgd, 0.f, nullptr,
                     d_e0, unique_keys, seg_offsets, num_unique, perm, workspace, ws_bytes, status, stream);
+}
+
+int dlrm_embbag_bwd_update_noalloc(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables,
+                                   const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                                   const float* e0, const float* pooled, const float* d_out, float lr, float* d_e0,
+                                   int32_t* unique_keys, int32_t* seg_offsets, int32_t* num_unique, int32_t* perm,
+                                   int32_t* status, void* stream) {
+  // size first (host only): a batch beyond the array is rejected before any HIP call
+  if (T < 1 || B < 1 || D < 1 || nnz < 0 || nnz >= kI32Max || !rows) return DLRM_E_INVAL;
+  if (T > DLRM_MAX_TABLES) return DLRM_E_UNSUPPORTED;
+  int64_t total = 0;
+  for (int t = 0; t < T; ++t) total += rows[t];
+  const size_t need = bwd_workspace_bytes(T, B, D, nnz, total);
+  if (need > kNoAllocScratchBytes) return DLRM_E_SCRATCH;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return DLRM_E_HIP;
+  return bwd_update(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, pooled, d_out, lr, kSgd, 0.f, nullptr,
+                    d_e0, unique_keys, seg_offsets, num_unique, perm, ws, kNoAllocScratchBytes, status, stream);
 }
 
 int dlrm_embbag_bwd_update_adagrad(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables,

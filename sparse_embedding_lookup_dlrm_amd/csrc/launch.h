@@ -77,6 +77,11 @@ struct BwdArgs {
 
 size_t bwd_workspace_bytes(int T, int B, int D, int64_t nnz, int64_t total_rows);
 
+// Library-owned scratch of the allocation-free backward (one array per GPU).
+constexpr size_t kNoAllocScratchBytes = size_t(DLRM_NOALLOC_SCRATCH_BYTES);
+// Device address of the current device's array (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
+
 // How the sparse backward runs for given sizes (host only).
 struct BwdPlanInfo {
   int radix_bits;    // digit width of the sort (8 or 9)

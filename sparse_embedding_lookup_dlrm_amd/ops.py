@@ -54,6 +54,10 @@ _SIGNATURES = {
                                                       _c_void_p, _c_void_p, _size_t, _c_void_p, _c_void_p]),
     "dlrm_validate_bags": (ctypes.c_int, [_i32, _i32, _P(_i64), _P(_i32), _P(_i32), _i64]),
     "dlrm_embbag_bwd_plan": (ctypes.c_int, [_i32, _i32, _i32, _i64, _P(_i64), _i32, _P(_i32)]),
+    "dlrm_embbag_bwd_update_noalloc": (ctypes.c_int, [_i32, _i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p,
+                                                      _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _f32,
+                                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                      _c_void_p, _c_void_p]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -373,6 +377,33 @@ def embbag_bwd_update(tables: Sequence[torch.Tensor], offsets: torch.Tensor, ind
                                                     workspace.numel(), _ptr(status), _stream(stream)),
                "dlrm_embbag_bwd_update_adagrad")
     return res
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def embbag_bwd_update_noalloc(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: torch.Tensor, B: int,
+                              e0: torch.Tensor, pooled: torch.Tensor, d_out: torch.Tensor, lr: float, *,
+                              d_e0: Optional[torch.Tensor] = None, unique_keys: Optional[torch.Tensor] = None,
+                              seg_offsets: Optional[torch.Tensor] = None, num_unique: Optional[torch.Tensor] = None,
+                              perm: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
+                              stream=None) -> None:
+    """dlrm_embbag_bwd_update_noalloc: the SGD backward with the library's own static scratch
+    (no workspace). Every output is a caller tensor (or None); this call allocates nothing."""
+    T, D, dt, ptrs, rows = _table_args(tables)
+    nnz = indices.numel()
+    _check_bwd_buffers(T, B, D, offsets, indices, e0, pooled, d_out, d_e0, status)
+    _expect(unique_keys, "unique_keys", torch.int32, nnz, at_least=True)
+    _expect(seg_offsets, "seg_offsets", torch.int32, nnz + 1, at_least=True)
+    _expect(num_unique, "num_unique", torch.int32, 1, at_least=True)
+    _expect(perm, "perm", torch.int32, nnz, at_least=True)
+    _require_cuda(*tables, offsets, indices, e0, pooled, d_out, d_e0, unique_keys, seg_offsets, num_unique, perm,
+                  status)
+    _check(lib().dlrm_embbag_bwd_update_noalloc(T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), nnz, _ptr(e0),
+                                                _ptr(pooled), _ptr(d_out), float(lr), _ptr(d_e0), _ptr(unique_keys),
+                                                _ptr(seg_offsets), _ptr(num_unique), _ptr(perm), _ptr(status),
+                                                _stream(stream)),
+           "dlrm_embbag_bwd_update_noalloc")
 
 
 def validate_bags(T: int, B: int, rows: Sequence[int], offsets, indices) -> int:
