@@ -14,9 +14,13 @@ Printed (last line of stdout, one JSON object):
   backward     the sparse backward + SGD on the 26-table Zipf workload (timed
                the same way; reported next to the forward, not in `value`)
 
-The launch time of a repeated batch settles only after ~30 launches (the
-first ones run up to 25% slower while the clocks settle), so the default
-warm-up is 50 launches: the figure is the steady state of a repeated batch.
+Inputs are prepared so that the device fill of the tables is the last GPU
+work before the warm-up: after the GPU has idled (even for a fraction of a
+second) its shader clock first drops (2.2 -> 1.6 GHz) and then takes ~35
+launches to climb back to 2.4 GHz, and the kernel time follows the clock
+(per-dispatch GRBM_GUI_ACTIVE counters; see --ramp). Every step is timed with
+its own pair of HIP events; the mean is the reported figure, median and min
+are printed beside it.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
   python bench.py --summarize-profile DIR --out profiles/NAME.txt   (rocprofv3 csv -> summary)
@@ -61,13 +65,17 @@ def fwd_algorithmic_bytes(T, B, D, s, nnz) -> int:
     return nnz * (D * s + 4) + 4 * (T * B + 1) + 4 * B * D + 4 * B * (D + P)
 
 
-def read_traffic(sha: str):
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{FWD_KERNEL}_{workload}_traffic.txt")
+
+
+def read_traffic(sha: str, path: str = TRAFFIC_FILE):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -208,19 +216,20 @@ def _pick(means, needle):
     return hits[0][1]
 
 
-def write_traffic(fetch_dir: str, write_dir: str, copy_gib: float, out: str, command: str) -> None:
+def write_traffic(fetch_dir: str, write_dir: str, copy_gib: float, out: str, command: str,
+                  kernel: str = FWD_KERNEL, label: str = "") -> None:
     """HBM bytes per launch of the fused forward from a FETCH_SIZE run and a WRITE_SIZE run
     (KiB per dispatch), each scaled by what the same counter reads for a plain elementwise
     copy of known size launched in the same process."""
     known = int(copy_gib * (1 << 30)) // 4 * 4
     fetch = _counter_means(fetch_dir, "FETCH_SIZE")
     write = _counter_means(write_dir, "WRITE_SIZE")
-    f_kib, w_kib = _pick(fetch, FWD_KERNEL), _pick(write, FWD_KERNEL)
+    f_kib, w_kib = _pick(fetch, kernel), _pick(write, kernel)
     f_copy, w_copy = _pick(fetch, COPY_KERNEL), _pick(write, COPY_KERNEL)
     f_factor = known / (f_copy * 1024.0)
     w_factor = known / (w_copy * 1024.0)
     traffic = f_kib * 1024.0 * f_factor + w_kib * 1024.0 * w_factor
-    lines = [f"# HBM traffic of {FWD_KERNEL} on the capacity workload (64 bf16 tables x 10M rows, D=128, B=16384)",
+    lines = [f"# HBM traffic of {kernel} on {label}",
              f"# command: {command}",
              f"kernel_source_sha: {kernel_source_sha()}",
              f"fetch_kib_per_launch: {f_kib:.1f}",
@@ -247,7 +256,9 @@ def build_capacity_inputs(w, dev):
 
     rows = synth.table_rows(w)
     t0 = time.time()
-    tables = synth.gen_tables_device(w, dev, rows)
+    # host arrays and their upload first, the device fill of the tables last: the
+    # warm-up then starts on a GPU that has just been busy, not on one whose clocks
+    # have dropped while the host was drawing indices
     lengths = synth.gen_lengths(w)
     indices = synth.gen_indices(w, rows, lengths)
     e0 = synth.gen_e0(w)
@@ -256,66 +267,143 @@ def build_capacity_inputs(w, dev):
     offsets = ops.lengths_to_offsets(d_len, status=status)
     d_idx = torch.from_numpy(indices).to(dev)
     d_e0 = torch.from_numpy(e0).to(dev)
+    tables = synth.gen_tables_device(w, dev, rows)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s: nnz={len(indices)} tables={sum(rows) * w.D * 2 / 1e9:.1f} GB")
     return dict(rows=rows, tables=tables, lengths=lengths, indices=indices, e0=e0, d_idx=d_idx, d_e0=d_e0,
                 offsets=offsets, status=status)
 
 
-def time_steps(fn, steps, warmup):
+def time_steps(fn, steps, warmup, detail=None, per_step_events=False):
+    """Mean ms per step over `steps` timed calls after `warmup` untimed ones, on the
+    current stream (the stream the library launches on). With per_step_events every
+    step is bracketed by its own HIP events (right for launches of hundreds of us);
+    otherwise one event pair brackets all steps, and if `detail` is given a second pass
+    of `steps` calls with an event pair per step gives the median and min (an event
+    record per step would add host time to launch-bound loops). `detail` receives
+    median, min and max per step and the per-step times."""
+    import statistics
+
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+
+    def each(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(stream)
+        for i in range(n):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return ev, [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
-        fn()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall
+    if per_step_events:
+        ev, per = each(steps)
+        wall = time.perf_counter() - t0
+        mean = ev[0].elapsed_time(ev[steps]) / steps
+    else:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        mean = e0.elapsed_time(e1) / steps
+        per = each(steps)[1] if detail is not None else None
+    if detail is not None:
+        detail.update({"ms_median": statistics.median(per), "ms_min": min(per), "ms_max": max(per),
+                       "ms_per_step_each": [round(x, 4) for x in per]})
+    return mean, wall
 
 
-def cpu_baseline(w, inp, n_samples, seed=2024):
-    """The fp64 oracle on a seeded sample of whole samples of the same batch. Rows are
-    fetched from HBM first (not timed)."""
+def _host_rows(dev_rows, dtype):
+    """Device rows -> host storage form (float32, float16, or uint16 bits for bf16)."""
+    import numpy as np
+    import torch
+
+    if dtype == "bf16":
+        return dev_rows.view(torch.int16).cpu().numpy().view(np.uint16)
+    return dev_rows.cpu().numpy()
+
+
+def _one_core():
+    """A context that holds numpy's thread pools (BLAS, OpenMP) to one thread."""
+    from threadpoolctl import threadpool_limits
+
+    return threadpool_limits(limits=1)
+
+
+def cpu_oracle_forward(w, tables, lengths, indices, e0, n_samples=None, seed=2024):
+    """The fp64 oracle's forward ([e0 | dots], the pooled sums on the way) on whole samples
+    of the batch: every sample, or a seeded subset of n_samples. The rows those samples
+    touch are fetched from HBM first and the indices renumbered into them (not timed);
+    the oracle then runs on one core."""
     import numpy as np
     import torch
 
     from oracle import dlrm_oracle as orc
 
-    rng = np.random.default_rng(seed)
-    smp = np.sort(rng.choice(w.B, size=min(n_samples, w.B), replace=False))
-    off = np.zeros(w.T * w.B + 1, dtype=np.int64)
-    off[1:] = np.cumsum(inp["lengths"])
+    B, T = w.B, w.T
+    if n_samples is None or n_samples >= B:
+        smp = np.arange(B)
+    else:
+        smp = np.sort(np.random.default_rng(seed).choice(B, size=n_samples, replace=False))
+    off = np.zeros(T * B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lengths)
     sub_tables, sub_len, sub_idx = [], [], []
-    parts = []
-    for t in range(w.T):
-        segs = [inp["indices"][off[t * w.B + b]:off[t * w.B + b + 1]] for b in smp]
-        parts.append(segs)
-        uniq = np.unique(np.concatenate(segs)) if segs else np.zeros(0, np.int32)
-        rows = inp["tables"][t][torch.from_numpy(uniq.astype(np.int64)).to(inp["tables"][t].device)]
-        sub_tables.append(rows.view(torch.int16).cpu().numpy().view(np.uint16))
-        for s in segs:
-            sub_len.append(len(s))
-            sub_idx.append(np.searchsorted(uniq, s).astype(np.int32))
+    for t in range(T):
+        segs = [indices[off[t * B + b]:off[t * B + b + 1]] for b in smp]
+        cat = np.concatenate(segs) if segs else np.zeros(0, np.int32)
+        uniq = np.unique(cat) if len(cat) else np.zeros(1, np.int64)
+        rows = tables[t][torch.from_numpy(uniq.astype(np.int64)).to(tables[t].device)]
+        sub_tables.append(_host_rows(rows, w.dtype))
+        for sg in segs:
+            sub_len.append(len(sg))
+            sub_idx.append(np.searchsorted(uniq, sg).astype(np.int32))
     sub_off = orc.lengths_to_offsets(sub_len)
-    idx = np.concatenate(sub_idx).astype(np.int32)
-    e0 = inp["e0"][smp]
-    t0 = time.perf_counter()
-    orc.embbag_fwd(sub_tables, w.dtype, len(smp), sub_off, idx, e0)
-    dt = time.perf_counter() - t0
+    idx = np.concatenate(sub_idx).astype(np.int32) if sub_idx else np.zeros(0, np.int32)
+    e0s = e0[smp]
+    with _one_core():
+        t0 = time.perf_counter()
+        orc.embbag_fwd(sub_tables, w.dtype, len(smp), sub_off, idx, e0s)
+        dt = time.perf_counter() - t0
+    what = "every sample" if len(smp) == B else f"{len(smp)} of {B} samples (seed {seed})"
     return {"value": len(idx) / dt, "unit": "lookups/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(smp)} of {w.B} samples ({len(idx)} lookups, all {w.T} tables), seed {seed}; "
-                      f"fp64 numpy oracle, single thread, {dt:.2f} s; host has {len(os.sched_getaffinity(0))} cores"}
+            "samples_per_s": len(smp) / dt,
+            "sample": f"{w.name}: {what}, {len(idx)} lookups over all {T} tables; fp64 numpy oracle forward "
+                      f"(pool + interaction), one thread, {dt:.2f} s; rows fetched from HBM beforehand, untimed; "
+                      f"host has {len(os.sched_getaffinity(0))} cores"}
 
 
-def bench_backward(steps, warmup, adagrad=False):
+def cpu_baseline(w, inp, n_samples, seed=2024):
+    """The fp64 oracle on a seeded sample of whole samples of the capacity batch."""
+    return cpu_oracle_forward(w, inp["tables"], inp["lengths"], inp["indices"], inp["e0"], n_samples, seed)
+
+
+def cpu_oracle_backward(w, b):
+    """The fp64 oracle's backward + SGD (interaction backward, occurrence keys, stable sort,
+    segments, per-row sums, update) on the whole host batch b, one core. Its forward pooled
+    sums are computed first, untimed."""
+    from oracle import dlrm_oracle as orc
+
+    off = orc.lengths_to_offsets(b.lengths)
+    pooled = orc.embbag_pool(b.tables, w.dtype, w.B, off, b.indices)
+    with _one_core():
+        t0 = time.perf_counter()
+        orc.embbag_bwd_update(b.tables, w.dtype, w.B, off, b.indices, b.e0, pooled, b.dout, 0.01)
+        dt = time.perf_counter() - t0
+    return {"value": len(b.indices) / dt, "unit": "lookups/s", "cores": 1, "kind": "oracle",
+            "sample": f"{w.name}: the whole batch ({len(b.indices)} lookups), fp64 numpy oracle backward + SGD, "
+                      f"one thread, {dt:.2f} s; host has {len(os.sched_getaffinity(0))} cores"}
+
+
+def bench_backward(steps, warmup, adagrad=False, cpu=False):
     import numpy as np
     import torch
 
@@ -343,7 +431,8 @@ def bench_backward(steps, warmup, adagrad=False):
         return {"workload": w.name, "optimizer": "rowwise_adagrad", "ms_per_step": ms,
                 "lookups_per_s": len(b.indices) / (ms / 1e3), "status": int(status.item())}
     plan = ops.BwdPlan(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, d_e0=d_e0, workspace=ws, status=status)
-    ms, _ = time_steps(plan.run, steps, warmup)
+    detail = {}
+    ms, _ = time_steps(plan.run, steps, warmup, detail)
     torch.cuda.synchronize()
     U = int(plan.num_unique.item())
     F = w.T + 1
@@ -352,9 +441,14 @@ def bench_backward(steps, warmup, adagrad=False):
     # pooled-gradient row per occurrence; read and write each touched table row once.
     alg = (4 * w.B * (w.D + P) + 4 * w.B * F * w.D + 4 * nnz + 4 * (w.T * w.B + 1) + 4 * w.B * w.D
            + 4 * nnz * w.D + 2 * 4 * U * w.D)
-    return {"workload": w.name, "ms_per_step": ms, "lookups_per_s": nnz / (ms / 1e3), "nnz": nnz,
-            "unique_rows": U, "method_bytes": alg, "method_GBps": alg / (ms / 1e3) / 1e9,
-            "status": int(status.item()), "lr": 0.01}
+    res = {"workload": w.name, "ms_per_step": ms, "ms_median": detail["ms_median"], "ms_min": detail["ms_min"],
+           "lookups_per_s": nnz / (ms / 1e3), "nnz": nnz,
+           "unique_rows": U, "method_bytes": alg, "method_GBps": alg / (ms / 1e3) / 1e9,
+           "status": int(status.item()), "lr": 0.01}
+    if cpu:
+        res["cpu_baseline"] = cpu_oracle_backward(w, b)
+        log(f"cpu oracle backward {w.name}: {res['cpu_baseline']['value']:.3e} lookups/s")
+    return res
 
 
 def bench_forward_q8(inp, steps, warmup):
@@ -419,7 +513,7 @@ def bench_forward_q8t(inp, steps, warmup):
             "frac_of_8TBps": alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, "status": int(inp["status"].item())}
 
 
-def bench_forward_configs(steps, warmup):
+def bench_forward_configs(steps, warmup, cpu=False):
     """The fused forward ([e0 | dots] only) on the three smaller workloads: 4 fp32 tables
     of 1000 rows (D=16, B=128, one index per bag), 26 fp32 tables of log-uniform rows
     (D=128, B=2048, one Zipf(1.05) index per bag) and 8 fp16 tables of 4M rows (D=64,
@@ -444,15 +538,22 @@ def bench_forward_configs(steps, warmup):
         e0 = torch.from_numpy(synth.gen_e0(w)).to(dev)
         res_out = torch.empty((w.B, w.out_width), dtype=torch.float32, device=dev)
         plan = ops.FwdPlan(tables, offsets, idx, w.B, e0, out_inter=res_out, status=status)
-        ms, _ = time_steps(plan.run, 10 * steps, warmup)
+        detail = {}
+        ms, _ = time_steps(plan.run, 10 * steps, warmup, detail)
         nnz = len(indices)
         s = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
         alg = fwd_algorithmic_bytes(w.T, w.B, w.D, s, nnz)
         gbs = alg / (ms / 1e3) / 1e9
-        out[name] = {"us_per_step": ms * 1e3, "lookups_per_s": nnz / (ms / 1e3), "bags_per_s": w.T * w.B / (ms / 1e3),
+        out[name] = {"us_per_step": ms * 1e3, "us_median": detail["ms_median"] * 1e3,
+                     "us_min": detail["ms_min"] * 1e3, "lookups_per_s": nnz / (ms / 1e3),
+                     "bags_per_s": w.T * w.B / (ms / 1e3),
                      "nnz": nnz, "algorithmic_bytes": alg, "hbm_GBps_algorithmic": gbs,
-                     "frac_of_8TBps": gbs / PEAK_HBM_GBS, "status": int(status.item())}
+                     "frac_of_8TBps": gbs / PEAK_HBM_GBS, "status": int(status.item()),
+                     "traffic": read_traffic(kernel_source_sha(), traffic_file(name))}
         log(f"fused forward {name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}%)")
+        if cpu:
+            out[name]["cpu_baseline"] = cpu_oracle_forward(w, tables, lengths, indices, synth.gen_e0(w))
+            log(f"cpu oracle {name}: {out[name]['cpu_baseline']['value']:.3e} lookups/s")
         del tables, plan
         torch.cuda.empty_cache()
     return out
@@ -482,24 +583,124 @@ def bench_backward_multihot(steps, warmup):
     ws = torch.empty(ops.bwd_workspace_bytes(w.T, w.B, w.D, nnz, rows), dtype=torch.uint8, device=dev)
     d_e0 = torch.empty((w.B, w.D), dtype=torch.float32, device=dev)
     plan = ops.BwdPlan(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, d_e0=d_e0, workspace=ws, status=status)
-    ms, _ = time_steps(plan.run, steps, warmup)
+    detail = {}
+    ms, _ = time_steps(plan.run, steps, warmup, detail)
     torch.cuda.synchronize()
     U = int(plan.num_unique.item())
     off = np.concatenate([[0], np.cumsum(lengths.astype(np.int64))])
     longest = max(int(np.unique(indices[off[t * w.B]:off[(t + 1) * w.B]], return_counts=True)[1].max())
                   for t in range(w.T))
-    res = {"workload": w.name, "ms_per_step": ms, "lookups_per_s": nnz / (ms / 1e3), "nnz": nnz,
+    res = {"workload": w.name, "ms_per_step": ms, "ms_median": detail["ms_median"], "ms_min": detail["ms_min"],
+           "lookups_per_s": nnz / (ms / 1e3), "nnz": nnz,
            "unique_rows": U, "longest_row_segment": longest, "status": int(status.item()), "lr": 0.01}
     del tables, plan
     torch.cuda.empty_cache()
     return res
 
 
+def copy_calibration(gib, dev):
+    """One plain elementwise copy of known size, for scaling the traffic counters."""
+    import torch
+
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {n * 4} bytes read, {n * 4} bytes written by one elementwise kernel")
+    del src, dst
+
+
+def bench_gather_ceiling(w, inp, steps, warmup, fused_gbs):
+    """The bare random-row gather of the same batch (dlrm_probe_row_gather: the same rows,
+    one wave-wide load per row, nothing else) timed like the forward. Its rate over the
+    lookup bytes nnz * (row + index) is the ceiling the forward's bandwidth is set against:
+    frac_of_ceiling = forward algorithmic GB/s / this GB/s."""
+    import numpy as np
+    import torch
+
+    from sparse_embedding_lookup_dlrm_amd import ops
+
+    nnz = len(inp["indices"])
+    per_table = inp["lengths"].reshape(w.T, w.B).sum(axis=1).astype(np.int64)
+    starts = np.concatenate([[0], np.cumsum(per_table)]).tolist()
+    sink = torch.empty(ops.PROBE_SINK_FLOATS, dtype=torch.float32, device=inp["d_idx"].device)
+    plan = ops.ProbeGatherPlan(inp["tables"], starts, inp["d_idx"], sink)
+    detail = {}
+    ms, _ = time_steps(plan.run, steps, warmup, detail, per_step_events=True)
+    nbytes = nnz * (w.D * 2 + 4)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    del sink
+    return {"kernel": "probe_gather_kernel", "us_per_step": ms * 1e3, "us_median": detail["ms_median"] * 1e3,
+            "us_min": detail["ms_min"] * 1e3, "lookup_bytes": nbytes, "gather_GBps": gbs,
+            "gather_frac_of_8TBps": gbs / PEAK_HBM_GBS, "frac_of_ceiling": fused_gbs / gbs,
+            "what": "bare gather of the batch's rows and indices (no bags, no interaction, no output); "
+                    "frac_of_ceiling = fused forward algorithmic GB/s / gather GB/s"}
+
+
+def ramp(plan, inp):
+    """Per-launch times of the capacity forward: 40 launches after a 3 s idle, then 40
+    after an in-place refill of the tables (GPU busy right before). Run under rocprofv3
+    --pmc GRBM_GUI_ACTIVE --kernel-trace for the per-dispatch shader clock."""
+    import torch
+
+    def timed(n):
+        st = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(st)
+        for i in range(n):
+            plan.run()
+            ev[i + 1].record(st)
+        torch.cuda.synchronize()
+        return [round(ev[i].elapsed_time(ev[i + 1]) * 1e3, 1) for i in range(n)]
+
+    out = {}
+    time.sleep(3.0)
+    out["after_3s_idle"] = timed(40)
+    g = torch.Generator(device=inp["tables"][0].device)
+    g.manual_seed(77)
+    for t in inp["tables"]:
+        t.normal_(0.0, 0.01, generator=g)
+    out["after_table_refill"] = timed(40)
+    for k, v in out.items():
+        log(f"{k}: " + " ".join(f"{x:.0f}" for x in v))
+    print(json.dumps({"ramp_us": out}), flush=True)
+    return 0
+
+
+def summarize_clock(d: str, out: str, command: str) -> None:
+    """Per-dispatch duration and effective shader clock (GRBM_GUI_ACTIVE summed over the 8
+    XCDs, / 8 / duration) of the forward kernel, in launch order."""
+    import csv
+
+    per = {}
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if FWD_KERNEL not in r["Kernel_Name"] or r["Counter_Name"] != "GRBM_GUI_ACTIVE":
+                    continue
+                t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+                per[int(r["Dispatch_Id"])] = (t0, (t1 - t0) / 1e3, float(r["Counter_Value"]))
+    lines = [f"# rocprofv3 summary of: {command}", f"# source directory: {d}",
+             "# per dispatch of the forward kernel, in launch order: duration (us), effective shader clock (GHz) "
+             "= GRBM_GUI_ACTIVE / 8 XCDs / duration, gap since the previous dispatch ended (us)",
+             "launch | us | GHz | gap_us"]
+    prev = None
+    for i, k in enumerate(sorted(per)):
+        t0, us, act = per[k]
+        gap = (t0 - prev) / 1e3 if prev is not None else 0.0
+        prev = t0 + us * 1e3
+        lines.append(f"{i} | {us:.1f} | {act / 8 / us / 1e3:.2f} | {gap:.0f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-samples", type=int, default=6144)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
@@ -512,13 +713,26 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="rocprofv3 FETCH_SIZE and WRITE_SIZE csv dirs (runs made with --copy-calibration-gib) "
                          "-> traffic file")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the bare row-gather ceiling leg")
+    ap.add_argument("--only-configs", action="store_true",
+                    help="time only the forward on the three smaller workloads (for counter runs)")
+    ap.add_argument("--ramp", action="store_true",
+                    help="per-launch times of the capacity forward after a 3 s idle and after a table refill")
+    ap.add_argument("--summarize-clock", default=None,
+                    help="rocprofv3 dir of a --ramp run with --pmc GRBM_GUI_ACTIVE -> per-dispatch clock summary")
+    ap.add_argument("--kernel", default=FWD_KERNEL, help="kernel name needle for --traffic")
+    ap.add_argument("--label", default="the capacity workload (64 bf16 tables x 10M rows, D=128, B=16384)",
+                    help="workload label for --traffic")
     ap.add_argument("--out", default=None)
     ap.add_argument("--command", default="")
     args = ap.parse_args()
 
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.copy_calibration_gib, args.out or TRAFFIC_FILE,
-                      args.command)
+                      args.command, args.kernel, args.label)
+        return 0
+    if args.summarize_clock:
+        summarize_clock(args.summarize_clock, args.out, args.command)
         return 0
     if args.summarize_backward:
         summarize_backward(args.summarize_backward, args.out, args.command, args.warmup, args.steps)
@@ -539,6 +753,11 @@ def main():
     ops.lib()  # the HIP library must be present: no fallback
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only_configs:
+        if args.copy_calibration_gib > 0:
+            copy_calibration(args.copy_calibration_gib, dev)
+        print(json.dumps({"forward_configs": bench_forward_configs(args.steps, args.warmup)}), flush=True)
+        return 0
     w = synth.WORKLOADS[synth.CAPACITY]
     inp = build_capacity_inputs(w, dev)
     nnz = len(inp["indices"])
@@ -546,16 +765,13 @@ def main():
     plan = ops.FwdPlan(inp["tables"], inp["offsets"], inp["d_idx"], w.B, inp["d_e0"], out_inter=out,
                        status=inp["status"])
 
+    if args.ramp:
+        return ramp(plan, inp)
     if args.copy_calibration_gib > 0:
-        n = int(args.copy_calibration_gib * (1 << 30)) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        log(f"copy calibration: {n * 4} bytes read, {n * 4} bytes written by one elementwise kernel")
-        del src, dst
+        copy_calibration(args.copy_calibration_gib, dev)
 
-    ms, wall = time_steps(plan.run, args.steps, args.warmup)
+    detail = {}
+    ms, wall = time_steps(plan.run, args.steps, args.warmup, detail, per_step_events=True)
     st = int(inp["status"].item())
     if st != 0:
         raise RuntimeError(f"device status {st}: invalid bag description")
@@ -571,6 +787,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_median": detail["ms_median"],
+        "ms_min": detail["ms_min"],
+        "ms_max": detail["ms_max"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -588,9 +807,15 @@ def main():
                      "algorithmic_bytes_per_launch": alg, "kernel_source_sha": sha},
         "wall_s_timed_region": wall,
     }
-    log(f"fused forward: {ms * 1e3:.1f} us/step, {nnz / (ms / 1e3):.3e} lookups/s, {gbs:.0f} GB/s "
-        f"({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s)")
+    log(f"fused forward: {ms * 1e3:.1f} us/step (median {detail['ms_median'] * 1e3:.1f}, min "
+        f"{detail['ms_min'] * 1e3:.1f}), {nnz / (ms / 1e3):.3e} lookups/s, {gbs:.0f} GB/s "
+        f"({100 * gbs / PEAK_HBM_GBS:.1f}% of 8 TB/s); per step: {detail['ms_per_step_each']}")
     del plan
+    if not args.no_ceiling:
+        res["gather_ceiling"] = bench_gather_ceiling(w, inp, args.steps, args.warmup, gbs)
+        log(f"bare row gather: {res['gather_ceiling']['us_per_step']:.1f} us/step, "
+            f"{res['gather_ceiling']['gather_GBps']:.0f} GB/s; fused forward at "
+            f"{100 * res['gather_ceiling']['frac_of_ceiling']:.1f}% of it")
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_samples)
         log(f"cpu oracle: {res['cpu_baseline']['value']:.3e} lookups/s")
@@ -607,14 +832,14 @@ def main():
     del inp
     torch.cuda.empty_cache()
     if not args.no_backward:
-        res["backward"] = bench_backward(max(args.steps, 20), args.warmup)
+        res["backward"] = bench_backward(max(args.steps, 20), args.warmup, cpu=not args.no_cpu)
         log(f"backward: {res['backward']['ms_per_step'] * 1e3:.1f} us/step")
         res["backward_adagrad"] = bench_backward(max(args.steps, 20), min(args.warmup, 10), adagrad=True)
         log(f"backward row-wise AdaGrad: {res['backward_adagrad']['ms_per_step'] * 1e3:.1f} us/step")
         res["backward_multihot"] = bench_backward_multihot(max(args.steps, 20), min(args.warmup, 10))
         log(f"backward multi-hot: {res['backward_multihot']['ms_per_step'] * 1e3:.1f} us/step")
     if not args.no_configs:
-        res["forward_configs"] = bench_forward_configs(args.steps, args.warmup)
+        res["forward_configs"] = bench_forward_configs(args.steps, args.warmup, cpu=not args.no_cpu)
     print(json.dumps(res), flush=True)
     return 0
 

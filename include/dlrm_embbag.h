@@ -87,6 +87,22 @@ typedef enum {
  * one (scale, bias) pair per table. */
 typedef enum { DLRM_F32 = 0, DLRM_F16 = 1, DLRM_BF16 = 2, DLRM_Q8 = 3, DLRM_Q8T = 4 } dlrm_dtype;
 
+/* Interaction output layouts ("DLRM" note, section 3, The Pairwise Interaction
+ * Layer): bits of the `layout` argument of dlrm_embbag_fwd_ex, dlrm_interact_ex
+ * and dlrm_interact_bwd. 0 is the layout given at the top of this file.
+ *   DLRM_PAIRS_SELF       the section's formula with the pairs of a vector with
+ *                         itself: pairs i >= j, P = F (F + 1) / 2, pair (i, j) at
+ *                         dot index i (i + 1) / 2 + j (row-major lower triangle
+ *                         with the diagonal). Without it: i > j, i (i - 1) / 2 + j.
+ *   DLRM_WITH_EMBEDDINGS  the variant the section mentions that concatenates the
+ *                         original embeddings alongside the interaction vector:
+ *                         out[b] = [Z[b][0] | Z[b][1] | .. | Z[b][T] | dots], i.e.
+ *                         e0 then the T pooled vectors (F * D floats), then the P
+ *                         dots. Without it: out[b] = [e0 | dots].
+ * A sample's output row has W = (with embeddings ? F * D : D) + P floats. */
+#define DLRM_PAIRS_SELF 1
+#define DLRM_WITH_EMBEDDINGS 2
+
 /* bits OR-ed into the device status word */
 #define DLRM_STATUS_BAD_INDEX 1   /* an index outside [0, rows[t]) */
 #define DLRM_STATUS_BAD_OFFSETS 2 /* offsets[0] != 0, a decrease, an offset outside [0, nnz], offsets[T*B] != nnz,
@@ -133,6 +149,22 @@ int dlrm_embbag_fwd(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* 
                     const float* e0, float* out_pooled, float* out_inter, int32_t* status, void* stream);
 
 /*
+ * dlrm_embbag_fwd with a choice of interaction layout (DLRM_PAIRS_SELF,
+ * DLRM_WITH_EMBEDDINGS or both; "DLRM" note, section 3, The Pairwise
+ * Interaction Layer: its formula includes the pairs of a vector with itself,
+ * and some variants concatenate the original embeddings alongside the
+ * interaction vector). The pooled vectors still stay on chip between the
+ * gather and the dots; with DLRM_WITH_EMBEDDINGS they are written to out_inter
+ * as part of the output row.
+ *   out_inter   device fp32 [B][W], W as given with the layout bits
+ *   layout      0 .. 3; every other argument as in dlrm_embbag_fwd (layout 0 is dlrm_embbag_fwd)
+ */
+int dlrm_embbag_fwd_ex(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* const* tables,
+                       const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                       const float* e0, float* out_pooled, float* out_inter, int32_t layout, int32_t* status,
+                       void* stream);
+
+/*
  * The fused forward on row-wise 8-bit tables: row r of table t is D uint8 codes
  * q followed by the row's fp32 scale and fp32 bias (D + 8 bytes, one contiguous
  * read per lookup), value[d] = scale * q[d] + bias; a lookup reads D + 8 bytes
@@ -175,15 +207,16 @@ int dlrm_interact(int32_t T, int32_t B, int32_t D, const float* e0, const float*
                   void* stream);
 
 /*
- * Interaction alone with a choice of pair set ("DLRM" note, section 3, The
+ * Interaction alone with a choice of layout ("DLRM" note, section 3, The
  * Pairwise Interaction Layer: its formula takes the dot products e_i . e_j for
- * i <= j, self-pairs included, and the section mentions variants without them).
- *   self_pairs  0: pairs i > j, P = F (F - 1) / 2, out[b][D + i(i-1)/2 + j]
- *               1: pairs i >= j, P = F (F + 1) / 2, out[b][D + i(i+1)/2 + j]
- *   e0 device fp32 [B][D], pooled device fp32 [B][T][D], out device fp32 [B][D + P];
- *   out[b][0 .. D) = e0[b] (bit copy). D must be a multiple of 4, at most 1024.
+ * i <= j, self-pairs included; the section mentions variants without them and
+ * variants that concatenate the original embeddings alongside the dots).
+ *   layout  bits DLRM_PAIRS_SELF, DLRM_WITH_EMBEDDINGS (0 .. 3; 0 is dlrm_interact)
+ *   e0 device fp32 [B][D], pooled device fp32 [B][T][D], out device fp32 [B][W]
+ *   (W as given with the layout bits); the e0 and pooled values in the output are
+ *   bit copies. D must be a multiple of 4, at most 1024.
  */
-int dlrm_interact_ex(int32_t T, int32_t B, int32_t D, int32_t self_pairs, const float* e0, const float* pooled,
+int dlrm_interact_ex(int32_t T, int32_t B, int32_t D, int32_t layout, const float* e0, const float* pooled,
                      float* out, void* stream);
 
 /*
@@ -191,15 +224,18 @@ int dlrm_interact_ex(int32_t T, int32_t B, int32_t D, int32_t self_pairs, const 
  * MLP) and the optimizer of the pooled vectors. The gradient of Z_i . Z_j is
  * Z_j for Z_i and Z_i for Z_j, so with g the upstream gradient of the pairs,
  * S the symmetric F x F matrix holding g at (i, j) and (j, i) (2 g on the
- * diagonal for self-pairs, 0 there otherwise): dZ[b] = S[b] Z[b].
+ * diagonal for self-pairs, 0 there otherwise): dZ[b] = S[b] Z[b] + the direct
+ * gradient of the Z rows that appear in the output themselves (e0 always; with
+ * DLRM_WITH_EMBEDDINGS every row).
+ *   layout    the forward's layout bits (0 .. 3)
  *   e0 device fp32 [B][D], pooled device fp32 [B][T][D]   (the forward's inputs)
- *   d_out     device fp32 [B][D + P]: dL/d(out) in the layout of dlrm_interact_ex
- *   d_e0      device fp32 [B][D] or NULL: out, d_out[:, :D] + dZ[:, 0]
+ *   d_out     device fp32 [B][W]: dL/d(out) in the layout of dlrm_interact_ex
+ *   d_e0      device fp32 [B][D] or NULL: out, dZ[:, 0]
  *   d_pooled  device fp32 [B][T][D]: out, dZ[:, 1 .. T]
  * D must be a multiple of 4, at most 512; (T + 1)(D + 4 + T + 1) * 4 bytes of LDS
  * must fit in 160 KB.
  */
-int dlrm_interact_bwd(int32_t T, int32_t B, int32_t D, int32_t self_pairs, const float* e0, const float* pooled,
+int dlrm_interact_bwd(int32_t T, int32_t B, int32_t D, int32_t layout, const float* e0, const float* pooled,
                       const float* d_out, float* d_e0, float* d_pooled, void* stream);
 
 /*

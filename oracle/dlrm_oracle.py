@@ -16,9 +16,10 @@ definitions, one bag / one pair / one occurrence at a time:
   * Interaction -- same note, section 3, The Pairwise Interaction Layer: dot
     products e_i . e_j over the embeddings and the bottom-MLP output e_0, then
     concatenation with e_0. The variant without self-pairs (mentioned in that
-    section) is the one computed: pairs i > j over Z = [e_0, e_1 .. e_T], in
+    section) is the default: pairs i > j over Z = [e_0, e_1 .. e_T], in
     row-major order of the strict lower triangle (k = i(i-1)/2 + j), output
-    [e_0 | dots].
+    [e_0 | dots]. The section's own formula (self-pairs i >= j) and the variant
+    that concatenates the original embeddings alongside the dots are options.
   * Backward -- the pages give no backward; it is the exact gradient of the
     forward above: dZ_i = sum_{j != i} g_{ij} Z_j with g the upstream gradient
     of pair (i, j), the gradient of an embedding row is the sum of dZ over
@@ -189,46 +190,67 @@ def stack_z(e0: np.ndarray, pooled: np.ndarray) -> np.ndarray:
     return Z
 
 
-def interact(e0: np.ndarray, pooled: np.ndarray, self_pairs: bool = False) -> np.ndarray:
-    """out[b] = [e0[b] | Z[b,i] . Z[b,j] for i > j (or i >= j with self_pairs)], float64."""
+def interact(e0: np.ndarray, pooled: np.ndarray, self_pairs: bool = False,
+             with_embeddings: bool = False) -> np.ndarray:
+    """out[b] = [e0[b] | Z[b,i] . Z[b,j] for i > j (or i >= j with self_pairs)], float64.
+
+    with_embeddings: the variant of the "DLRM" note, section 3, that concatenates the
+    original embeddings alongside the interaction vector; the reading taken is
+    out[b] = [Z[b,0] | Z[b,1] | ... | Z[b,T] | dots], every vector of Z in Z's order
+    (e0 first, as in the plain layout), then the dots.
+    """
     B, T, D = pooled.shape
     F = T + 1
     Z = stack_z(np.asarray(e0, dtype=np.float64), pooled)
-    out = np.zeros((B, D + pair_count(F, self_pairs)), dtype=np.float64)
-    out[:, :D] = e0
+    head = F * D if with_embeddings else D
+    out = np.zeros((B, head + pair_count(F, self_pairs)), dtype=np.float64)
+    if with_embeddings:
+        for f in range(F):
+            out[:, f * D:(f + 1) * D] = Z[:, f]
+    else:
+        out[:, :D] = e0
     for k, i, j in pairs(F, self_pairs):
-        out[:, D + k] = (Z[:, i, :] * Z[:, j, :]).sum(axis=1)
+        out[:, head + k] = (Z[:, i, :] * Z[:, j, :]).sum(axis=1)
     return out
 
 
-def embbag_fwd(tables, dtype, B, offsets, indices, e0) -> Dict[str, np.ndarray]:
+def embbag_fwd(tables, dtype, B, offsets, indices, e0, self_pairs: bool = False,
+               with_embeddings: bool = False) -> Dict[str, np.ndarray]:
     pooled = embbag_pool(tables, dtype, B, offsets, indices)
-    return {"pooled": pooled, "out": interact(e0, pooled)}
+    return {"pooled": pooled, "out": interact(e0, pooled, self_pairs, with_embeddings)}
 
 
 # ---------------------------------------------------------------------------
 # Backward + update
 # ---------------------------------------------------------------------------
 def interact_bwd(e0: np.ndarray, pooled: np.ndarray, d_out: np.ndarray,
-                 self_pairs: bool = False) -> Dict[str, np.ndarray]:
-    """Gradient of out = [e0 | dots] with respect to Z and e0.
+                 self_pairs: bool = False, with_embeddings: bool = False) -> Dict[str, np.ndarray]:
+    """Gradient of the interaction output with respect to e0 and the pooled vectors.
 
     d(Z_i . Z_j)/dZ_i = Z_j and d(Z_i . Z_j)/dZ_j = Z_i, so every pair (i, j) with
     upstream gradient g adds g * Z_j to dZ_i and g * Z_i to dZ_j (a self-pair
-    (i, i) thus adds 2 g Z_i). e0 also reaches the output directly (the first D
-    columns), so d_e0 = d_out[:, :D] + dZ[:, 0].
+    (i, i) thus adds 2 g Z_i); "dZ" holds this part. The vectors that appear in
+    the output themselves also get their own upstream gradient: e0 always (the
+    first D columns), and with with_embeddings every Z row. So
+    d_e0 = d_out[:, :D] + dZ[:, 0], and d_pooled[:, t] = dZ[:, 1 + t] plus, with
+    with_embeddings, the output gradient of pooled row t.
     """
     B, T, D = pooled.shape
     F = T + 1
     Z = stack_z(np.asarray(e0, dtype=np.float64), pooled)
     d_out = np.asarray(d_out, dtype=np.float64)
+    head = F * D if with_embeddings else D
     dZ = np.zeros_like(Z)
     for k, i, j in pairs(F, self_pairs):
-        g = d_out[:, D + k][:, None]
+        g = d_out[:, head + k][:, None]
         dZ[:, i] += g * Z[:, j]
         dZ[:, j] += g * Z[:, i]
     d_e0 = d_out[:, :D] + dZ[:, 0]
-    return {"dZ": dZ, "d_e0": d_e0}
+    d_pooled = dZ[:, 1:].copy()
+    if with_embeddings:
+        for t in range(T):
+            d_pooled[:, t] += d_out[:, (1 + t) * D:(2 + t) * D]
+    return {"dZ": dZ, "d_e0": d_e0, "d_pooled": d_pooled}
 
 
 def occurrence_keys(rows: Sequence[int], B: int, offsets: np.ndarray, indices: np.ndarray):

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdlrm_embbag.so")
 
-SOURCES = ["embbag_fwd.hip", "embbag_bwd.hip", "offsets.hip", "noalloc.hip", "api.cpp"]
+SOURCES = ["embbag_fwd.hip", "embbag_bwd.hip", "offsets.hip", "noalloc.hip", "probe.hip", "api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are switched off for all device code.

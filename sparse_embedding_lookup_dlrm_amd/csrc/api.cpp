@@ -59,6 +59,13 @@ size_t bwd_lds_bytes(int T, int D) {
 
 constexpr size_t kLds = 160 * 1024;
 
+// Floats per sample of the interaction output in a given layout.
+int64_t out_width(int T, int D, int layout) {
+  const int64_t F = T + 1;
+  const int64_t P = (layout & DLRM_PAIRS_SELF) ? F * (F + 1) / 2 : F * (F - 1) / 2;
+  return ((layout & DLRM_WITH_EMBEDDINGS) ? F * D : D) + P;
+}
+
 }  // namespace
 
 namespace {
@@ -133,9 +140,19 @@ int dlrm_lengths_to_offsets(int64_t n, const int32_t* lengths, int32_t* offsets,
 int dlrm_embbag_fwd(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* const* tables, const int64_t* rows,
                     const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0, float* out_pooled,
                     float* out_inter, int32_t* status, void* stream) {
+  return dlrm_embbag_fwd_ex(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, out_pooled, out_inter, 0, status,
+                            stream);
+}
+
+int dlrm_embbag_fwd_ex(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* const* tables,
+                       const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                       const float* e0, float* out_pooled, float* out_inter, int32_t layout, int32_t* status,
+                       void* stream) {
   if (dtype == DLRM_Q8 || dtype == DLRM_Q8T) return DLRM_E_UNSUPPORTED;  // 8-bit rows: dlrm_embbag_fwd_q8(t)
+  if (layout < 0 || layout > (DLRM_PAIRS_SELF | DLRM_WITH_EMBEDDINGS)) return DLRM_E_INVAL;
   int rc = check_batch(T, B, D, dtype, tables, rows, offsets, indices, nnz);
   if (rc != DLRM_OK) return rc;
+  if (static_cast<int64_t>(B) * out_width(T, D, layout) >= (int64_t(1) << 40)) return DLRM_E_INVAL;
   if (!out_pooled && !out_inter) return DLRM_E_INVAL;
   if (out_inter && !e0) return DLRM_E_INVAL;
   if (out_pooled && !aligned(out_pooled, 16)) return DLRM_E_ALIGN;
@@ -149,7 +166,7 @@ int dlrm_embbag_fwd(int32_t T, int32_t B, int32_t D, int32_t dtype, const void* 
     a.tabs.rows[t] = static_cast<int32_t>(rows[t]);
   }
   a.offsets = offsets; a.indices = indices; a.nnz = nnz;
-  a.e0 = e0; a.out_pooled = out_pooled; a.out_inter = out_inter; a.status = status;
+  a.e0 = e0; a.out_pooled = out_pooled; a.out_inter = out_inter; a.status = status; a.layout = layout;
   return from_hip(launch_embbag_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -204,33 +221,31 @@ int dlrm_embbag_fwd_q8t(int32_t T, int32_t B, int32_t D, const void* const* tabl
                   status, stream);
 }
 
-int dlrm_interact_ex(int32_t T, int32_t B, int32_t D, int32_t self_pairs, const float* e0, const float* pooled,
+int dlrm_interact_ex(int32_t T, int32_t B, int32_t D, int32_t layout, const float* e0, const float* pooled,
                      float* out, void* stream) {
   if (T < 1 || B < 1 || D < 1 || !e0 || !pooled || !out) return DLRM_E_INVAL;
-  if (self_pairs != 0 && self_pairs != 1) return DLRM_E_INVAL;
+  if (layout < 0 || layout > (DLRM_PAIRS_SELF | DLRM_WITH_EMBEDDINGS)) return DLRM_E_INVAL;
   if (T > DLRM_MAX_TABLES || D % 4 != 0 || D > 1024) return DLRM_E_UNSUPPORTED;
-  if (static_cast<int64_t>(B) * (D + static_cast<int64_t>(T + 1) * (T + 2) / 2) >= (int64_t(1) << 40))
-    return DLRM_E_INVAL;
+  if (static_cast<int64_t>(B) * out_width(T, D, layout) >= (int64_t(1) << 40)) return DLRM_E_INVAL;
   if (!aligned(e0, 16) || !aligned(pooled, 16) || !aligned(out, 4)) return DLRM_E_ALIGN;
   if (tile_bytes(T, D) > kLds) return DLRM_E_UNSUPPORTED;
-  return from_hip(launch_interact(T, B, D, self_pairs != 0, e0, pooled, out, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_interact(T, B, D, layout, e0, pooled, out, static_cast<hipStream_t>(stream)));
 }
 
 int dlrm_interact(int32_t T, int32_t B, int32_t D, const float* e0, const float* pooled, float* out, void* stream) {
   return dlrm_interact_ex(T, B, D, 0, e0, pooled, out, stream);
 }
 
-int dlrm_interact_bwd(int32_t T, int32_t B, int32_t D, int32_t self_pairs, const float* e0, const float* pooled,
+int dlrm_interact_bwd(int32_t T, int32_t B, int32_t D, int32_t layout, const float* e0, const float* pooled,
                       const float* d_out, float* d_e0, float* d_pooled, void* stream) {
   if (T < 1 || B < 1 || D < 1 || !e0 || !pooled || !d_out || !d_pooled) return DLRM_E_INVAL;
-  if (self_pairs != 0 && self_pairs != 1) return DLRM_E_INVAL;
+  if (layout < 0 || layout > (DLRM_PAIRS_SELF | DLRM_WITH_EMBEDDINGS)) return DLRM_E_INVAL;
   if (T > DLRM_MAX_TABLES || D % 4 != 0 || D > 512) return DLRM_E_UNSUPPORTED;
-  if (static_cast<int64_t>(B) * (D + static_cast<int64_t>(T + 1) * (T + 2) / 2) >= (int64_t(1) << 40))
-    return DLRM_E_INVAL;
+  if (static_cast<int64_t>(B) * out_width(T, D, layout) >= (int64_t(1) << 40)) return DLRM_E_INVAL;
   if (!aligned(e0, 16) || !aligned(pooled, 16) || !aligned(d_out, 4) || !aligned(d_pooled, 16)) return DLRM_E_ALIGN;
   if (d_e0 && !aligned(d_e0, 16)) return DLRM_E_ALIGN;
   if (bwd_lds_bytes(T, D) > kLds) return DLRM_E_UNSUPPORTED;
-  return from_hip(launch_interact_bwd(T, B, D, self_pairs != 0, e0, pooled, d_out, d_e0, d_pooled,
+  return from_hip(launch_interact_bwd(T, B, D, layout, e0, pooled, d_out, d_e0, d_pooled,
                                       static_cast<hipStream_t>(stream)));
 }
 

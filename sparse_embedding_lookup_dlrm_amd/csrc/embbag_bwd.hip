@@ -56,7 +56,8 @@ constexpr int kRadixRounds = kRadixTile / kRadixWaves / kWave;  // rounds of 64 
 // launches instead of running before it.
 struct IbwdShare {
   int T, D;
-  bool self_pairs;
+  bool self_pairs;  // pairs i >= j (else i > j)
+  bool with_emb;    // d_out holds the gradient of every Z row ahead of the pair gradients
   const float* e0;
   const float* pooled;
   const float* d_out;
@@ -69,6 +70,7 @@ struct IbwdShare {
 __device__ __forceinline__ void interact_bwd_sample(const IbwdShare& ia, int b, float* smem) {
   const int T = ia.T, D = ia.D;
   const bool self_pairs = ia.self_pairs;
+  const bool with_emb = ia.with_emb;
   const float* __restrict__ e0 = ia.e0;
   const float* __restrict__ pooled = ia.pooled;
   const float* __restrict__ d_out = ia.d_out;
@@ -76,7 +78,8 @@ __device__ __forceinline__ void interact_bwd_sample(const IbwdShare& ia, int b, 
   float* __restrict__ d_e0 = ia.d_e0;
   const int F = T + 1;
   const int LD = D + 4;
-  const int W = D + (self_pairs ? F * (F + 1) / 2 : F * (F - 1) / 2);
+  const int dot0 = with_emb ? F * D : D;  // first pair gradient of a sample's row of d_out
+  const int W = dot0 + (self_pairs ? F * (F + 1) / 2 : F * (F - 1) / 2);
   const int Fp = (F + 3) & ~3;    // S rows, padded with zeros to whole blocks of 4
   float* Z = smem;                // [F][LD]
   float* S = smem + F * LD;       // [Fp][F]
@@ -85,7 +88,7 @@ __device__ __forceinline__ void interact_bwd_sample(const IbwdShare& ia, int b, 
   // LDS store, so a batch costs one memory round trip, not one per element; the
   // first batch of S and the e0 gradient are loaded before Z's batches
   constexpr int kBatch = 4;
-  const float* g = d_out + static_cast<size_t>(b) * W + D;
+  const float* g = d_out + static_cast<size_t>(b) * W + dot0;
   auto s_value = [&](int i) -> float {  // S[r][c] from the upstream pair gradients (i = r * F + c)
     const int r = i / F, c = i - r * F;
     const int hi = r > c ? r : c, lo = r > c ? c : r;
@@ -170,7 +173,12 @@ __device__ __forceinline__ void interact_bwd_sample(const IbwdShare& ia, int b, 
               make_float4(go.x + acc[r].x, go.y + acc[r].y, go.z + acc[r].z, go.w + acc[r].w);
         }
       } else if (f < F) {
-        *reinterpret_cast<float4*>(d_pooled + (static_cast<size_t>(b) * T + f - 1) * D + d) = acc[r];
+        float4 v = acc[r];
+        if (with_emb) {  // the direct gradient of the pooled row, which is in the output too
+          const float4 dir = *reinterpret_cast<const float4*>(d_out + static_cast<size_t>(b) * W + f * D + d);
+          v = make_float4(v.x + dir.x, v.y + dir.y, v.z + dir.z, v.w + dir.w);
+        }
+        *reinterpret_cast<float4*>(d_pooled + (static_cast<size_t>(b) * T + f - 1) * D + d) = v;
       }
     }
   }
@@ -1131,11 +1139,12 @@ constexpr size_t kLdsPerWorkgroup = 160 * 1024;
 // room for the alignment of the dynamic LDS segment after a kernel's static one
 constexpr size_t kLdsSlack = 256;
 
-hipError_t launch_interact_bwd(int T, int B, int D, bool self_pairs, const float* e0, const float* pooled,
+hipError_t launch_interact_bwd(int T, int B, int D, int layout, const float* e0, const float* pooled,
                                const float* d_out, float* d_e0, float* d_pooled, hipStream_t st) {
   const size_t lds = ibwd_lds(T, D);
   if (lds > kLdsPerWorkgroup) return hipErrorInvalidValue;
-  const IbwdShare ia{T, D, self_pairs, e0, pooled, d_out, d_pooled, d_e0, 0, B};
+  const IbwdShare ia{T, D, (layout & DLRM_PAIRS_SELF) != 0, (layout & DLRM_WITH_EMBEDDINGS) != 0, e0, pooled,
+                     d_out, d_pooled, d_e0, 0, B};
   hipLaunchKernelGGL(interact_bwd_kernel, dim3(B), dim3(kBwdThreads), lds, st, ia);
   return hipGetLastError();
 }
@@ -1197,7 +1206,7 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
     }                                            \
   } while (0)
   if (n == 0 || !plan.ibwd_shared) {  // 1. interaction backward as a launch of its own
-    e = launch_interact_bwd(a.T, a.B, a.D, false, a.e0, a.pooled, a.d_out, a.d_e0, d_pooled, st);
+    e = launch_interact_bwd(a.T, a.B, a.D, 0, a.e0, a.pooled, a.d_out, a.d_e0, d_pooled, st);
     if (e != hipSuccess) return e;
     if (n == 0) {  // no keys
       hipLaunchKernelGGL(zero_segments, dim3(1), dim3(64), 0, st, seg, nuniq);
@@ -1215,10 +1224,10 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   const bool seg_one_pass = plan.seg_one_pass;
   const int nshare = plan.ibwd_shared ? passes + (seg_one_pass ? 1 : 0) : 0;
   int ishare = 0;
-  const IbwdShare none{a.T, a.D, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
+  const IbwdShare none{a.T, a.D, false, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
   auto share = [&]() {
     if (nshare == 0) return none;
-    IbwdShare ia{a.T, a.D, false, a.e0, a.pooled, a.d_out, d_pooled, a.d_e0, 0, 0};
+    IbwdShare ia{a.T, a.D, false, false, a.e0, a.pooled, a.d_out, d_pooled, a.d_e0, 0, 0};
     ia.first = static_cast<int>(static_cast<long long>(a.B) * ishare / nshare);
     ia.count = static_cast<int>(static_cast<long long>(a.B) * (ishare + 1) / nshare) - ia.first;
     ++ishare;

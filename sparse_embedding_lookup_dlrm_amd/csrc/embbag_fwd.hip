@@ -232,9 +232,12 @@ __host__ __device__ inline Tile make_tile(int T, int D, int S) {
   return tl;
 }
 
+// Dots of the workgroup's samples into out_inter; with with_emb the dots of a
+// sample start after its F Z rows (written by the caller), else after e0.
 __device__ __forceinline__ void interact_from_lds(const float* Zall, const Tile& tl, int D, int b0, int B,
-                                                  float* __restrict__ out_inter, bool self_pairs = false) {
-  const int W = D + (self_pairs ? tl.F * (tl.F + 1) / 2 : tl.F * (tl.F - 1) / 2);
+                                                  float* __restrict__ out_inter, bool self_pairs, bool with_emb) {
+  const int dot0 = with_emb ? tl.F * D : D;
+  const int W = dot0 + (self_pairs ? tl.F * (tl.F + 1) / 2 : tl.F * (tl.F - 1) / 2);
   const int items = tl.S * tl.nblk;
   const int l = threadIdx.x & 15;
   for (int w = threadIdx.x >> 4; w < items; w += kThreads / 16) {  // one 4x4 block per 16 lanes
@@ -244,7 +247,7 @@ __device__ __forceinline__ void interact_from_lds(const float* Zall, const Tile&
     int bi, bj;
     block_pair(blk, bi, bj);
     dots_block16<false>(Zall + static_cast<size_t>(s) * tl.Fpad * tl.LD, tl.F, D, tl.LD, bi, bj, l,
-                        out_inter + static_cast<size_t>(b) * W + D, self_pairs);
+                        out_inter + static_cast<size_t>(b) * W + dot0, self_pairs);
   }
 }
 
@@ -262,7 +265,9 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FwdArgs a, int S) {
   const int lb = xcd_block(blockIdx.x, gridDim.x);
   const int b0 = lb * S;
   const int T = a.T, B = a.B, D = a.D;
-  const int W = D + tl.F * (tl.F - 1) / 2;
+  const bool self_pairs = (a.layout & DLRM_PAIRS_SELF) != 0;
+  const bool with_emb = (a.layout & DLRM_WITH_EMBEDDINGS) != 0;
+  const int W = (with_emb ? tl.F * D : D) + (self_pairs ? tl.F * (tl.F + 1) / 2 : tl.F * (tl.F - 1) / 2);
 
   for (int i = threadIdx.x; i < T * (S + 1); i += kThreads) {
     const int t = i / (S + 1), j = i - t * (S + 1);
@@ -316,11 +321,20 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FwdArgs a, int S) {
     if (b < B) {
       const float v = a.e0[static_cast<size_t>(b) * D + d];
       Z[static_cast<size_t>(s) * tl.Fpad * tl.LD + d] = v;
-      store_stream(a.out_inter + static_cast<size_t>(b) * W + d, v);
+      if (!with_emb) store_stream(a.out_inter + static_cast<size_t>(b) * W + d, v);
     }
   }
   __syncthreads();
-  interact_from_lds(Z, tl, D, b0, B, a.out_inter);
+  if (with_emb) {  // the F Z rows of every sample ahead of its dots
+    for (int i = threadIdx.x; i < S * tl.F * D; i += kThreads) {
+      const int s = i / (tl.F * D), r = i - s * tl.F * D;
+      const int f = r / D, d = r - f * D;
+      const int b = b0 + s;
+      if (b < B) store_stream(a.out_inter + static_cast<size_t>(b) * W + r,
+                              Z[(static_cast<size_t>(s) * tl.Fpad + f) * tl.LD + d]);
+    }
+  }
+  interact_from_lds(Z, tl, D, b0, B, a.out_inter, self_pairs, with_emb);
 }
 
 // ---------------------------------------------------------------------------
@@ -328,11 +342,13 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FwdArgs a, int S) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void interact_kernel(int T, int B, int D, const float* __restrict__ e0,
                                                             const float* __restrict__ pooled,
-                                                            float* __restrict__ out, int S, bool self_pairs) {
+                                                            float* __restrict__ out, int S, int layout) {
   extern __shared__ __align__(16) float smem[];
   const Tile tl = make_tile(T, D, S);
   const int b0 = xcd_block(blockIdx.x, gridDim.x) * S;
-  const int W = D + (self_pairs ? tl.F * (tl.F + 1) / 2 : tl.F * (tl.F - 1) / 2);
+  const bool self_pairs = (layout & DLRM_PAIRS_SELF) != 0;
+  const bool with_emb = (layout & DLRM_WITH_EMBEDDINGS) != 0;
+  const int W = (with_emb ? tl.F * D : D) + (self_pairs ? tl.F * (tl.F + 1) / 2 : tl.F * (tl.F - 1) / 2);
   const int D4 = D / 4;
   for (int i = threadIdx.x; i < S * tl.F * D4; i += kThreads) {
     const int s = i / (tl.F * D4);
@@ -341,17 +357,16 @@ __global__ __launch_bounds__(kThreads) void interact_kernel(int T, int B, int D,
     const int b = b0 + s;
     if (b >= B) continue;
     float4 v;
-    if (f == 0) {
-      v = *reinterpret_cast<const float4*>(e0 + static_cast<size_t>(b) * D + d);
-      float* o = out + static_cast<size_t>(b) * W + d;
+    if (f == 0) v = *reinterpret_cast<const float4*>(e0 + static_cast<size_t>(b) * D + d);
+    else v = *reinterpret_cast<const float4*>(pooled + (static_cast<size_t>(b) * T + (f - 1)) * D + d);
+    if (f == 0 || with_emb) {  // e0 (and with with_emb every Z row) ahead of the dots
+      float* o = out + static_cast<size_t>(b) * W + f * D + d;
       store_stream(o + 0, v.x); store_stream(o + 1, v.y); store_stream(o + 2, v.z); store_stream(o + 3, v.w);
-    } else {
-      v = *reinterpret_cast<const float4*>(pooled + (static_cast<size_t>(b) * T + (f - 1)) * D + d);
     }
     *reinterpret_cast<float4*>(smem + (static_cast<size_t>(s) * tl.Fpad + f) * tl.LD + d) = v;
   }
   __syncthreads();
-  interact_from_lds(smem, tl, D, b0, B, out, self_pairs);
+  interact_from_lds(smem, tl, D, b0, B, out, self_pairs, with_emb);
 }
 
 // ---------------------------------------------------------------------------
@@ -484,11 +499,14 @@ struct RowShape {
   // scale and a bias per row and keep more columns per lane, so their windows
   // are smaller
   // (16-bit rows of 512 and 1024 bytes and table-wise 8-bit rows keep a few
-  // rows fewer in flight, which keeps them within 80 VGPRs without spills)
+  // rows fewer in flight, which keeps them within 80 VGPRs without spills;
+  // bf16 rows of 256 bytes keep 12: on the 64-table capacity batch 12, 16 and
+  // 20 rows per window measured 780.5, 784.8 and 793.3 us, bit-identical)
   static constexpr int WIN = DT == DLRM_Q8                   ? (LB >= 8 ? 4 : 8)
                              : DT == DLRM_Q8T                ? (LB >= 8 ? 4 : 12)
                              : (DT != DLRM_F32 && LB == 16) ? 3
                              : (DT != DLRM_F32 && LB == 8)  ? 6
+                             : (DT == DLRM_BF16 && LB == 4) ? 12
                                                              : (LB >= 4 ? 64 / LB : 16);
 };
 
@@ -525,7 +543,7 @@ __host__ __device__ inline RowLayout make_row_layout(int T, int D, bool mfma, in
   L.G = G;
   L.Tp = mfma ? ((T + 31) / 32) * 32 : (((T + 1 + 3) & ~3) - 1);
   L.LD = D + 4;
-  const int P = (T + 1) * T / 2;
+  const int P = (T + 1) * (T + 2) / 2;  // dots with self-pairs, the most any layout stages
   int o = 0;
   L.off_tbase = o; o += align16(T * 8);
   L.off_trows = o; o += align16(T * 4);
@@ -577,81 +595,54 @@ __device__ __forceinline__ void split_bf16x8(const float4& a, const float4& b, b
   lo = __builtin_bit_cast(bf16x8_t, l);
 }
 
-// Split pooled rows 1..Tp of Z in place: the D fp32 values of a row become D
-// bf16 hi parts (bytes [0, 2D) of the row) followed by D bf16 lo parts (bytes
-// [2D, 4D)). Every thread reads its values before any thread writes (a
-// workgroup barrier between), in chunks of whole rows, so no row is
-// overwritten while still unread. Ends with a barrier.
-template <int NT>
-__device__ __forceinline__ void split_rows(float* Z, int LD, int D, int Tp, int tid) {
-  const int gpr = D / 8;  // 8-value groups per row
-  const int rows_per_chunk = (2 * NT) / gpr > 0 ? (2 * NT) / gpr : 1;
-  for (int r0 = 1; r0 <= Tp; r0 += rows_per_chunk) {
-    const int r1 = min(Tp + 1, r0 + rows_per_chunk);
-    float4 x[2][2];
-    int off[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int idx = tid + k * NT;
-      const int row = r0 + idx / gpr, g = idx % gpr;
-      off[k] = -1;
-      if (row < r1) {
-        const float* z = Z + row * LD + 8 * g;
-        x[k][0] = *reinterpret_cast<const float4*>(z);
-        x[k][1] = *reinterpret_cast<const float4*>(z + 4);
-        off[k] = row * LD * 4 + 16 * g;  // byte offset of the group's hi part
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      if (off[k] >= 0) {
-        bf16x8_t hi, lo;
-        split_bf16x8(x[k][0], x[k][1], hi, lo);
-        char* zc = reinterpret_cast<char*>(Z);
-        *reinterpret_cast<bf16x8_t*>(zc + off[k]) = hi;
-        *reinterpret_cast<bf16x8_t*>(zc + off[k] + 2 * D) = lo;
-      }
-    }
-  }
-  __syncthreads();
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// 8 consecutive fp32 values of a Z row in LDS, split in registers into bf16
+// hi and lo parts.
+__device__ __forceinline__ void load_split8(const float* p, bf16x8_t& hi, bf16x8_t& lo) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  const float4 y = *reinterpret_cast<const float4*>(p + 4);
+  split_bf16x8(x, y, hi, lo);
 }
 
-// One 32x32 tile (I, J) of the Gram matrix of the pooled rows, from rows split
-// by split_rows: hi*hi + hi*lo + lo*hi with fp32 accumulation. Results with
-// Z-row indices zi > zj go to out[D + zi(zi-1)/2 + zj].
-__device__ __forceinline__ void gram_tile_mfma(const float* Z, int LD, int D, int T, int I, int J, float* out,
-                                               int tid) {
-  const int lane = tid & (kWave - 1);
-  const int m = lane & 31, kh = lane >> 5;
-  const char* za = reinterpret_cast<const char*>(Z + (1 + 32 * I + m) * LD) + 16 * kh;
-  const char* zb = reinterpret_cast<const char*>(Z + (1 + 32 * J + m) * LD) + 16 * kh;
-  const int lo = 2 * D;
-  floatx16_t acc = {};
-  for (int k0 = 0; k0 < 2 * D; k0 += 32) {  // bytes: 16 bf16 per step
-    const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(za + k0);
-    const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(za + lo + k0);
-    const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(zb + k0);
-    const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(zb + lo + k0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+// One 16x16 tile (I, J), I >= J, of the Gram matrix of the pooled rows (Z
+// rows 1..Tp, fp32 in LDS): hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16
+// with fp32 accumulation. Lane l supplies row l % 16 of each block at the 8
+// columns 8 (l / 16) .. +8 of every 32-column step (the same columns for both
+// operands), and receives the Gram entries of rows 4 (l / 16) .. +4 of block I
+// with row l % 16 of block J. Entries with Z-row indices zi > zj (zi >= zj for
+// self-pairs), zi <= T, go to dots[zi(zi-1)/2 + zj] (dots[zi(zi+1)/2 + zj]).
+__device__ __forceinline__ void gram_tile16(const float* Z, int LD, int D, int T, int I, int J,
+                                            float* __restrict__ dots, bool self_pairs, int lane) {
+  const int m = lane & 15, kq = lane >> 4;
+  const float* za = Z + (1 + 16 * I + m) * LD + 8 * kq;
+  const float* zb = Z + (1 + 16 * J + m) * LD + 8 * kq;
+  floatx4_t acc = {};
+  for (int k0 = 0; k0 < D; k0 += 32) {
+    bf16x8_t ah, al, bh, bl;
+    load_split8(za + k0, ah, al);
+    load_split8(zb + k0, bh, bl);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int row = 8 * (i >> 2) + 4 * kh + (i & 3);
-    const int zi = 1 + 32 * I + row, zj = 1 + 32 * J + m;
-    if (zi > zj && zi <= T) out[D + zi * (zi - 1) / 2 + zj] = acc[i];
+  for (int v = 0; v < 4; ++v) {
+    const int zi = 1 + 16 * I + 4 * kq + v, zj = 1 + 16 * J + m;
+    if (zi <= T && (zi > zj || (self_pairs && zi == zj)))
+      dots[self_pairs ? zi * (zi + 1) / 2 + zj : zi * (zi - 1) / 2 + zj] = acc[v];
   }
 }
 
-// Dots of e0 (Z row 0) with every pooled row, in fp32 from the unsplit rows:
-// 8 lanes per dot, lane j over the float4 chunks j, j+8, ... of D, combined
-// in a fixed order. Pair (zi, 0) sits at out[D + zi(zi-1)/2].
+// Dots of e0 (Z row 0) with every pooled row (and with itself for
+// self-pairs), in fp32: 8 lanes per dot, lane j over the float4 chunks j, j+8,
+// ... of D, combined in a fixed order. Pair (zi, 0) sits at out[zi(zi-1)/2]
+// (out[zi(zi+1)/2] with self-pairs), out being the start of the dots.
 template <int NT>
-__device__ __forceinline__ void e0_dots(const float* Z, int LD, int D, int T, float* out, int tid) {
+__device__ __forceinline__ void e0_dots(const float* Z, int LD, int D, int T, float* out, int tid,
+                                        bool self_pairs) {
   const int j = tid & 7;
-  for (int zi = 1 + (tid >> 3); zi <= T; zi += NT / 8) {
+  for (int zi = (self_pairs ? 0 : 1) + (tid >> 3); zi <= T; zi += NT / 8) {
     const float* zr = Z + zi * LD;
     float sum = 0.f;
     for (int d = 4 * j; d < D; d += 32) {
@@ -665,7 +656,7 @@ __device__ __forceinline__ void e0_dots(const float* Z, int LD, int D, int T, fl
     sum += __shfl_xor(sum, 1, kWave);
     sum += __shfl_xor(sum, 2, kWave);
     sum += __shfl_xor(sum, 4, kWave);
-    if (j == 0) out[D + zi * (zi - 1) / 2] = sum;
+    if (j == 0) out[self_pairs ? zi * (zi + 1) / 2 : zi * (zi - 1) / 2] = sum;
   }
 }
 
@@ -989,8 +980,14 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
   int* trows = reinterpret_cast<int*>(lds + L.off_trows);
   float* qsb = reinterpret_cast<float*>(lds + L.off_qsb);
 
+  // one step per workgroup (no next sample to fetch during this one) for G = 1
+  constexpr bool kMulti = G > 1;
   const int T = a.T, D = a.D, LD = L.LD;
-  const int W = D + (T + 1) * T / 2;
+  const int F = T + 1;
+  const bool self_pairs = (a.layout & DLRM_PAIRS_SELF) != 0;
+  const bool with_emb = (a.layout & DLRM_WITH_EMBEDDINGS) != 0;
+  const int P = self_pairs ? F * (F + 1) / 2 : F * (F - 1) / 2;
+  const int W = (with_emb ? F * D : D) + P;
   const int grp = G == 1 ? 0 : rfl(static_cast<int>(threadIdx.x) / NT);
   const int wave = rfl((static_cast<int>(threadIdx.x) >> 6) % GW);  // wave within the group
   char* gl = lds + L.off_groups + grp * L.group_bytes;
@@ -1048,7 +1045,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     asm volatile("" : "+v"(tid));
     const int b = sample_of(bs);
     const bool active = G == 1 || bs + grp < b_end;  // this group writes its sample
-    const bool has_next = bs + G < b_end;
+    const bool has_next = kMulti && bs + G < b_end;
     int* beg = reinterpret_cast<int*>(gl + L.off_beg + pb * L.pos_stride);
     int* pos = reinterpret_cast<int*>(gl + L.off_pos + pb * L.pos_stride);
     int* nbeg = reinterpret_cast<int*>(gl + L.off_beg + (pb ^ 1) * L.pos_stride);
@@ -1059,10 +1056,10 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     // thread issues them, clamped in bounds (the last step re-reads its own
     // sample), so that no branch merges their registers and nothing waits for
     // them before the gather is done.
-    int nx0, nx1;
-    float ne0;
+    int nx0 = 0, nx1 = 0;
+    float ne0 = 0.f;
     const int bn = has_next ? sample_of(bs + G) : b;
-    {
+    if constexpr (kMulti) {
       const int tt = tid < T ? tid : T - 1;
       const int td = tid < D ? tid : D - 1;
       nx0 = a.offsets[tt * a.B + bn];
@@ -1091,7 +1088,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     }
     // the prefetched values are first used here (the barrier keeps every use,
     // and the wait for them, after the gather)
-    asm volatile("" : "+v"(nx0), "+v"(nx1), "+v"(ne0));
+    if constexpr (kMulti) asm volatile("" : "+v"(nx0), "+v"(nx1), "+v"(ne0));
     bool next_empty = false;
     if (has_next && tid < T) {
       publish_bag(a, tid, bn, nx0, nx1, nbeg, npos);
@@ -1111,9 +1108,11 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
 
     // next sample's index loads go out now; their values are staged after the output
     int r[kStagePerThread], tb[kStagePerThread];
-    // (issued unconditionally, with no positions when there is no next sample:
-    // every load stays in bounds and no branch merges the registers)
-    load_stage<NT>(a, nbeg, npos, T, has_next ? rfl(npos[T]) : 0, r, tb, tid);
+    if constexpr (kMulti) {
+      // (issued unconditionally, with no positions when there is no next sample:
+      // every load stays in bounds and no branch merges the registers)
+      load_stage<NT>(a, nbeg, npos, T, has_next ? rfl(npos[T]) : 0, r, tb, tid);
+    }
 
     // pooled output (if requested) from the final fp32 Z
     if (a.out_pooled && active) {
@@ -1123,41 +1122,54 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
         op[i] = Z[(1 + t) * LD + d];
       }
     }
-    // interaction into the output staging area (which overlays the index stage)
-    for (int d = tid; d < D; d += NT) outs[d] = Z[d];
+    // interaction into the output staging area (which overlays the index
+    // stage): [e0 | dots], or only the dots when the Z rows go out as well
+    float* dots = with_emb ? outs : outs + D;
+    if (!with_emb)
+      for (int d = tid; d < D; d += NT) outs[d] = Z[d];
     if constexpr (MFMA) {
-      // e0 dots in fp32, then the pooled rows are split in place for the Gram
-      e0_dots<NT>(Z, LD, D, T, outs, tid);
-      split_rows<NT>(Z, LD, D, L.Tp, tid);
-      const int nt = L.Tp / 32;
+      // e0 dots in fp32; the Gram of the pooled rows on MFMA, every operand
+      // split into bf16 hi + lo in registers as it is read from LDS
+      e0_dots<NT>(Z, LD, D, T, dots, tid, self_pairs);
+      const int nt = L.Tp / 16;
       const int ntiles = nt * (nt + 1) / 2;
       for (int tile = wave; tile < ntiles; tile += GW) {
         int I, J;
         block_pair(tile, I, J);
-        gram_tile_mfma(Z, LD, D, T, I, J, outs, tid);
+        gram_tile16(Z, LD, D, T, I, J, dots, self_pairs, tid & (kWave - 1));
       }
     } else {  // fp32 dots, one 4x4 block of pairs per 16 lanes
       const int nb = (T + 1 + 3) >> 2;
       for (int u = tid >> 4; u < nb * (nb + 1) / 2; u += NT / 16) {
         int bi, bj;
         block_pair(u, bi, bj);
-        dots_block16<true>(Z, T + 1, D, LD, bi, bj, tid & 15, outs + D);
+        dots_block16<true>(Z, T + 1, D, LD, bi, bj, tid & 15, dots, self_pairs);
       }
     }
     __syncthreads();
     // the next sample's index loads have had the whole interaction to land:
     // take them now, before the output stores are queued behind them
+    if constexpr (kMulti) {
 #pragma unroll
-    for (int k = 0; k < kStagePerThread; ++k) asm volatile("" : "+v"(r[k]));
+      for (int k = 0; k < kStagePerThread; ++k) asm volatile("" : "+v"(r[k]));
+    }
     if (active) {
       float* o = a.out_inter + static_cast<size_t>(b) * W;
-      for (int i = tid; i < W; i += NT) store_stream(o + i, outs[i]);
+      if (with_emb) {  // [Z_0 | Z_1 .. Z_T | dots]
+        for (int i = tid; i < F * D; i += NT) {
+          const int f = i / D, d = i - f * D;
+          store_stream(o + i, Z[f * LD + d]);
+        }
+        for (int i = tid; i < P; i += NT) store_stream(o + F * D + i, outs[i]);
+      } else {
+        for (int i = tid; i < W; i += NT) store_stream(o + i, outs[i]);
+      }
     }
     __syncthreads();
 
     // stage the next sample: indices, cleared Z with its e0, no carries
     if (has_next) {
-      write_stage<NT>(a, r, tb, stage, sbag, trows, tid);
+      if constexpr (kMulti) write_stage<NT>(a, r, tb, stage, sbag, trows, tid);
       if (next_empty) {
         float* z = Z + (1 + tid) * LD;
         for (int d = 0; d < D; d += 4) *reinterpret_cast<float4*>(z + d) = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1247,7 +1259,8 @@ static hipError_t launch_rows_g(const FwdArgs& a, hipStream_t st) {
   // rows): one per workgroup, which keeps the end of the launch short (the
   // hardware dispatcher hands the many short-lived workgroups to free slots).
   const bool long_samples = a.nnz >= static_cast<int64_t>(kLongSampleRows) * a.B;
-  const int steps = (!long_samples && a.B >= 2 * G * resident_blocks(kernel, static_cast<size_t>(L.bytes))) ? 2 : 1;
+  const int steps =
+      (G > 1 && !long_samples && a.B >= 2 * G * resident_blocks(kernel, static_cast<size_t>(L.bytes))) ? 2 : 1;
   const int chunk = G * steps;
   const int grid = (a.B + chunk - 1) / chunk;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kRowThreads), L.bytes, st, a, L, chunk);
@@ -1337,7 +1350,7 @@ hipError_t launch_embbag_fwd(const FwdArgs& a, hipStream_t st) {
   }
 }
 
-hipError_t launch_interact(int T, int B, int D, bool self_pairs, const float* e0, const float* pooled, float* out,
+hipError_t launch_interact(int T, int B, int D, int layout, const float* e0, const float* pooled, float* out,
                            hipStream_t st) {
   int S = 1;
   while (S * (T + 1) < 16 && S < B) S *= 2;
@@ -1350,7 +1363,7 @@ hipError_t launch_interact(int T, int B, int D, bool self_pairs, const float* e0
   const size_t lds = tl.z_floats() * 4;
   if (lds > kMaxLds) return hipErrorInvalidValue;
   const int grid = (B + S - 1) / S;
-  hipLaunchKernelGGL(interact_kernel, dim3(grid), dim3(kThreads), lds, st, T, B, D, e0, pooled, out, S, self_pairs);
+  hipLaunchKernelGGL(interact_kernel, dim3(grid), dim3(kThreads), lds, st, T, B, D, e0, pooled, out, S, layout);
   return hipGetLastError();
 }
 

@@ -41,12 +41,13 @@ struct FwdArgs {
   float* out_pooled;
   float* out_inter;
   int32_t* status;
+  int layout;  // DLRM_PAIRS_SELF | DLRM_WITH_EMBEDDINGS bits of the interaction output
 };
 
 hipError_t launch_embbag_fwd(const FwdArgs& a, hipStream_t s);
-hipError_t launch_interact(int T, int B, int D, bool self_pairs, const float* e0, const float* pooled, float* out,
+hipError_t launch_interact(int T, int B, int D, int layout, const float* e0, const float* pooled, float* out,
                            hipStream_t s);
-hipError_t launch_interact_bwd(int T, int B, int D, bool self_pairs, const float* e0, const float* pooled,
+hipError_t launch_interact_bwd(int T, int B, int D, int layout, const float* e0, const float* pooled,
                                const float* d_out, float* d_e0, float* d_pooled, hipStream_t s);
 hipError_t launch_lengths_to_offsets(int64_t n, const int32_t* lengths, int32_t* offsets, int32_t* status,
                                      hipStream_t s);

@@ -15,9 +15,11 @@ from typing import List, Optional, Sequence, Tuple
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdlrm_embbag.so")
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dlrm_embbag.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = [os.path.join(INCLUDE, "dlrm_embbag.h"), os.path.join(INCLUDE, "dlrm_probe.h")]
 
 DLRM_F32, DLRM_F16, DLRM_BF16 = 0, 1, 2
+PAIRS_SELF, WITH_EMBEDDINGS = 1, 2  # interaction layout bits
 STATUS_BAD_INDEX = 1
 STATUS_BAD_OFFSETS = 2
 MAX_TABLES = 128
@@ -34,6 +36,8 @@ _SIGNATURES = {
     "dlrm_lengths_to_offsets": (ctypes.c_int, [_i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "dlrm_embbag_fwd": (ctypes.c_int, [_i32, _i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p, _c_void_p, _i64,
                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "dlrm_embbag_fwd_ex": (ctypes.c_int, [_i32, _i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p, _c_void_p,
+                                          _i64, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p]),
     "dlrm_embbag_fwd_q8": (ctypes.c_int, [_i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p, _c_void_p, _i64,
                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "dlrm_embbag_fwd_q8t": (ctypes.c_int, [_i32, _i32, _i32, _P(_c_void_p), _P(_f32), _P(_i64), _c_void_p,
@@ -54,6 +58,8 @@ _SIGNATURES = {
                                                       _c_void_p, _c_void_p, _size_t, _c_void_p, _c_void_p]),
     "dlrm_validate_bags": (ctypes.c_int, [_i32, _i32, _P(_i64), _P(_i32), _P(_i32), _i64]),
     "dlrm_embbag_bwd_plan": (ctypes.c_int, [_i32, _i32, _i32, _i64, _P(_i64), _i32, _P(_i32)]),
+    "dlrm_probe_row_gather": (ctypes.c_int, [_i32, _i32, _i32, _P(_c_void_p), _P(_i64), _P(_i64), _c_void_p, _i64,
+                                             _c_void_p, _c_void_p]),
     "dlrm_embbag_bwd_update_noalloc": (ctypes.c_int, [_i32, _i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p,
                                                       _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _f32,
                                                       _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -85,11 +91,14 @@ def lib() -> ctypes.CDLL:
 
 
 def header_functions() -> List[str]:
-    """Names of the functions declared in include/dlrm_embbag.h."""
-    with open(HEADER) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dlrm_[a-z0-9_]+)\s*\(", text)))
+    """Names of the functions declared in the library's headers (include/*.h)."""
+    names = set()
+    for h in HEADERS:
+        with open(h) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(dlrm_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def status_string(code: int) -> str:
@@ -155,9 +164,19 @@ def _table_args(tables: Sequence[torch.Tensor]):
     return T, D, _TORCH_DT[dt], ptrs, rows
 
 
-def pair_count(T: int) -> int:
+def pair_count(T: int, self_pairs: bool = False) -> int:
     F = T + 1
-    return F * (F - 1) // 2
+    return F * (F + 1) // 2 if self_pairs else F * (F - 1) // 2
+
+
+def layout_bits(self_pairs: bool = False, with_embeddings: bool = False) -> int:
+    return (PAIRS_SELF if self_pairs else 0) | (WITH_EMBEDDINGS if with_embeddings else 0)
+
+
+def out_width(T: int, D: int, layout: int = 0) -> int:
+    """Floats per sample of the interaction output in a layout."""
+    return (T + 1) * D * bool(layout & WITH_EMBEDDINGS) + D * (not layout & WITH_EMBEDDINGS) + \
+        pair_count(T, bool(layout & PAIRS_SELF))
 
 
 def lengths_to_offsets(lengths: torch.Tensor, offsets: Optional[torch.Tensor] = None,
@@ -175,30 +194,39 @@ def lengths_to_offsets(lengths: torch.Tensor, offsets: Optional[torch.Tensor] = 
     return offsets
 
 
-def _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status, P=None):
+def _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status, layout=0):
     _check_bags(offsets, indices, T, B)
     _expect(e0, "e0", torch.float32, B * D)
     _expect(out_pooled, "out_pooled", torch.float32, B * T * D)
-    _expect(out_inter, "out_inter", torch.float32, B * (D + (pair_count(T) if P is None else P)))
+    _expect(out_inter, "out_inter", torch.float32, B * out_width(T, D, layout))
     _expect(status, "status", torch.int32, 1, at_least=True)
 
 
 def embbag_fwd(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: torch.Tensor, B: int,
                e0: Optional[torch.Tensor] = None, *, want_pooled: bool = False, want_inter: bool = True,
                out_pooled: Optional[torch.Tensor] = None, out_inter: Optional[torch.Tensor] = None,
-               status: Optional[torch.Tensor] = None, stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
-    """Embedding-bag forward; returns (pooled [B,T,D] or None, [e0 | dots] [B, D+P] or None)."""
+               status: Optional[torch.Tensor] = None, stream=None,
+               layout: int = 0) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Embedding-bag forward; returns (pooled [B,T,D] or None, interaction output [B, W] or None):
+    [e0 | dots] with layout 0 (dlrm_embbag_fwd), else the layout bits PAIRS_SELF and
+    WITH_EMBEDDINGS (dlrm_embbag_fwd_ex)."""
     T, D, dt, ptrs, rows = _table_args(tables)
-    _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status)
+    _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status, layout)
     _require_cuda(*tables, offsets, indices, e0, out_pooled, out_inter, status)
     dev = tables[0].device
     if want_pooled and out_pooled is None:
         out_pooled = torch.empty((B, T, D), dtype=torch.float32, device=dev)
     if want_inter and out_inter is None:
-        out_inter = torch.empty((B, D + pair_count(T)), dtype=torch.float32, device=dev)
-    _check(lib().dlrm_embbag_fwd(T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(), _ptr(e0),
-                                 _ptr(out_pooled), _ptr(out_inter), _ptr(status), _stream(stream)),
-           "dlrm_embbag_fwd")
+        out_inter = torch.empty((B, out_width(T, D, layout)), dtype=torch.float32, device=dev)
+    if layout == 0:
+        _check(lib().dlrm_embbag_fwd(T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(),
+                                     _ptr(e0), _ptr(out_pooled), _ptr(out_inter), _ptr(status), _stream(stream)),
+               "dlrm_embbag_fwd")
+    else:
+        _check(lib().dlrm_embbag_fwd_ex(T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(),
+                                        _ptr(e0), _ptr(out_pooled), _ptr(out_inter), layout, _ptr(status),
+                                        _stream(stream)),
+               "dlrm_embbag_fwd_ex")
     return out_pooled, out_inter
 
 
@@ -263,20 +291,21 @@ def embbag_fwd_q8t(tables: Sequence[torch.Tensor], scale_bias, offsets: torch.Te
 
 
 def interact(e0: torch.Tensor, pooled: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None,
-             self_pairs: bool = False) -> torch.Tensor:
+             self_pairs: bool = False, with_embeddings: bool = False) -> torch.Tensor:
     """[e0 | lower-triangle dots of Z = [e0; pooled]] from pooled [B, T, D] fp32: pairs i > j
-    (dlrm_interact), or i >= j with self_pairs (dlrm_interact_ex)."""
+    (dlrm_interact); i >= j with self_pairs, and [Z rows | dots] with with_embeddings
+    (dlrm_interact_ex)."""
     B, T, D = pooled.shape
-    F = T + 1
-    P = F * (F + 1) // 2 if self_pairs else F * (F - 1) // 2
+    layout = layout_bits(self_pairs, with_embeddings)
+    W = out_width(T, D, layout)
     _expect(pooled, "pooled", torch.float32, B * T * D)
     _expect(e0, "e0", torch.float32, B * D)
-    _expect(out, "out", torch.float32, B * (D + P))
+    _expect(out, "out", torch.float32, B * W)
     _require_cuda(e0, pooled, out)
     if out is None:
-        out = torch.empty((B, D + P), dtype=torch.float32, device=pooled.device)
-    if self_pairs:
-        _check(lib().dlrm_interact_ex(T, B, D, 1, _ptr(e0), _ptr(pooled), _ptr(out), _stream(stream)),
+        out = torch.empty((B, W), dtype=torch.float32, device=pooled.device)
+    if layout:
+        _check(lib().dlrm_interact_ex(T, B, D, layout, _ptr(e0), _ptr(pooled), _ptr(out), _stream(stream)),
                "dlrm_interact_ex")
     else:
         _check(lib().dlrm_interact(T, B, D, _ptr(e0), _ptr(pooled), _ptr(out), _stream(stream)), "dlrm_interact")
@@ -285,14 +314,14 @@ def interact(e0: torch.Tensor, pooled: torch.Tensor, out: Optional[torch.Tensor]
 
 def interact_bwd(e0: torch.Tensor, pooled: torch.Tensor, d_out: torch.Tensor, self_pairs: bool = False,
                  d_e0: Optional[torch.Tensor] = None, d_pooled: Optional[torch.Tensor] = None,
-                 want_d_e0: bool = True, stream=None) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
+                 want_d_e0: bool = True, stream=None,
+                 with_embeddings: bool = False) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
     """(dL/de0, dL/dpooled) of the interaction from dL/dout (dlrm_interact_bwd)."""
     B, T, D = pooled.shape
-    F = T + 1
-    P = F * (F + 1) // 2 if self_pairs else F * (F - 1) // 2
+    layout = layout_bits(self_pairs, with_embeddings)
     _expect(pooled, "pooled", torch.float32, B * T * D)
     _expect(e0, "e0", torch.float32, B * D)
-    _expect(d_out, "d_out", torch.float32, B * (D + P))
+    _expect(d_out, "d_out", torch.float32, B * out_width(T, D, layout))
     _expect(d_e0, "d_e0", torch.float32, B * D)
     _expect(d_pooled, "d_pooled", torch.float32, B * T * D)
     _require_cuda(e0, pooled, d_out, d_e0, d_pooled)
@@ -300,7 +329,7 @@ def interact_bwd(e0: torch.Tensor, pooled: torch.Tensor, d_out: torch.Tensor, se
         d_pooled = torch.empty((B, T, D), dtype=torch.float32, device=pooled.device)
     if d_e0 is None and want_d_e0:
         d_e0 = torch.empty((B, D), dtype=torch.float32, device=pooled.device)
-    _check(lib().dlrm_interact_bwd(T, B, D, 1 if self_pairs else 0, _ptr(e0), _ptr(pooled), _ptr(d_out), _ptr(d_e0),
+    _check(lib().dlrm_interact_bwd(T, B, D, layout, _ptr(e0), _ptr(pooled), _ptr(d_out), _ptr(d_e0),
                                    _ptr(d_pooled), _stream(stream)), "dlrm_interact_bwd")
     return d_e0, d_pooled
 
@@ -379,6 +408,29 @@ def embbag_bwd_update(tables: Sequence[torch.Tensor], offsets: torch.Tensor, ind
     return res
 
 
+PROBE_SINK_FLOATS = 4096 * 256
+
+
+class ProbeGatherPlan:
+    """dlrm_probe_row_gather (measurement kernel: the bare random-row gather of a batch)
+    with its arguments marshalled once. table_start: host CSR position of each table's
+    first occurrence, T + 1 entries."""
+
+    def __init__(self, tables, table_start: Sequence[int], indices: torch.Tensor, sink: torch.Tensor, stream=None):
+        T, D, dt, ptrs, rows = _table_args(tables)
+        if len(table_start) != T + 1:
+            raise ValueError("table_start needs T + 1 entries")
+        _expect(sink, "sink", torch.float32, PROBE_SINK_FLOATS, at_least=True)
+        _require_cuda(*tables, indices, sink)
+        starts = (_i64 * (T + 1))(*[int(x) for x in table_start])
+        self._keep = (tables, indices, sink, ptrs, rows, starts)
+        self._args = (T, D, dt, ptrs, rows, starts, _ptr(indices), indices.numel(), _ptr(sink), _stream(stream))
+        self._fn = lib().dlrm_probe_row_gather
+
+    def run(self):
+        _check(self._fn(*self._args), "dlrm_probe_row_gather")
+
+
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -421,17 +473,23 @@ class FwdPlan:
     resident inputs (same tensors every call)."""
 
     def __init__(self, tables, offsets, indices, B, e0=None, *, out_pooled=None, out_inter=None, status=None,
-                 stream=None):
+                 stream=None, layout: int = 0):
         T, D, dt, ptrs, rows = _table_args(tables)
-        _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status)
+        _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status, layout)
         _require_cuda(*tables, offsets, indices, e0, out_pooled, out_inter, status)
         self._keep = (tables, offsets, indices, e0, out_pooled, out_inter, status, ptrs, rows)
-        self._args = (T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(), _ptr(e0),
-                      _ptr(out_pooled), _ptr(out_inter), _ptr(status), _stream(stream))
-        self._fn = lib().dlrm_embbag_fwd
+        if layout == 0:
+            self._args = (T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(), _ptr(e0),
+                          _ptr(out_pooled), _ptr(out_inter), _ptr(status), _stream(stream))
+            self._name = "dlrm_embbag_fwd"
+        else:
+            self._args = (T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(), _ptr(e0),
+                          _ptr(out_pooled), _ptr(out_inter), layout, _ptr(status), _stream(stream))
+            self._name = "dlrm_embbag_fwd_ex"
+        self._fn = getattr(lib(), self._name)
 
     def run(self):
-        _check(self._fn(*self._args), "dlrm_embbag_fwd")
+        _check(self._fn(*self._args), self._name)
 
 
 class BwdPlan:

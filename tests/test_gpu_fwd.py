@@ -234,3 +234,69 @@ def test_all_bags_empty_nnz_zero(T, D, dtype, B):
     assert np.all(p == 0.0) and not np.any(np.signbit(p))
     assert torch.equal(inter2, out_inter)
     check_fwd(db, out_pooled, out_inter, exact=True)
+
+
+# ---------------------------------------------------------------------------
+# interaction layouts in the fused forward (self-pairs, embeddings alongside)
+# ---------------------------------------------------------------------------
+_LAYOUT_SHAPES = [
+    # name, T, rows, D, dtype, B, bag: covers the row-streaming kernel with the MFMA Gram (16-bit, T >= 24),
+    # with fp32 dots in sample groups (fp32 T = 26; fp16 T = 8), and the narrow-row kernel (fp32 D = 16)
+    ("cap", 64, 3000, 128, "bf16", 40, ("uniform", 1, 32)),
+    ("mfma-odd", 27, 500, 64, "f16", 70, ("uniform", 0, 9)),
+    ("zipf26", 26, 4000, 128, "f32", 300, ("fixed", 1)),
+    ("multihot", 8, 5000, 64, "f16", 600, ("poisson", 20, 100)),
+    ("tiny", 4, 1000, 16, "f32", 128, ("fixed", 1)),
+]
+
+
+@pytest.mark.parametrize("layout", [1, 2, 3])
+@pytest.mark.parametrize("shape", _LAYOUT_SHAPES, ids=[s[0] for s in _LAYOUT_SHAPES])
+def test_fused_forward_layouts(layout, shape):
+    """dlrm_embbag_fwd_ex with self-pairs (layout 1), the embeddings concatenated alongside the
+    dots (2) or both (3), against the oracle on the same layout; the Z rows in the output are
+    the pooled sums, the e0 block is a bit copy."""
+    name, T, rows, D, dtype, B, bag = shape
+    w = synth.Workload("layout-" + name, T=T, rows=rows, D=D, dtype=dtype, B=B, bag=bag, dist=("zipf", 1.1),
+                       seed=T * 10 + layout)
+    b = synth.make_batch(w)
+    db = DeviceBatch(b)
+    sp, we = bool(layout & ops.PAIRS_SELF), bool(layout & ops.WITH_EMBEDDINGS)
+    pooled, inter = db.fwd(want_pooled=True, layout=layout)
+    torch.cuda.synchronize()
+    assert db.status.item() == 0
+    off = orc.lengths_to_offsets(b.lengths)
+    ref = orc.embbag_fwd(b.tables, dtype, B, off, b.indices, b.e0, self_pairs=sp, with_embeddings=we)
+    from gpu_util import abs_tables
+    pm = orc.embbag_pool(abs_tables(b.tables, dtype), dtype, B, off, b.indices)
+    mag = orc.interact(np.abs(b.e0), pm, self_pairs=sp, with_embeddings=we)
+    got = inter.cpu().numpy()
+    assert got.shape == ref["out"].shape
+    np.testing.assert_array_equal(got[:, :D], b.e0)
+    head = (T + 1) * D if we else D
+    if we:  # the pooled rows in the output are the pooled output, bit for bit
+        np.testing.assert_array_equal(got[:, D:head].reshape(B, T, D), pooled.cpu().numpy())
+    assert_mag_close(got[:, D:], ref["out"][:, D:], mag[:, D:], RTOL[dtype], f"{name} layout {layout}")
+    # the dots equal those of the plain layout, self-pairs aside
+    _, plain = db.fwd(layout=0 if not sp else ops.PAIRS_SELF)
+    torch.cuda.synchronize()
+    assert torch.equal(inter[:, head:], plain[:, D:])
+
+
+@pytest.mark.parametrize("layout", [1, 2, 3])
+@pytest.mark.parametrize("name", [synth.CAPACITY, "zipf-26t-d128-b2048", "tiny-4t1k-d16-b128"])
+def test_fused_forward_layouts_exact_integers(layout, name):
+    """Integer tables and e0: every layout bit for bit (the MFMA Gram included)."""
+    w = synth.WORKLOADS[name].replace(values="int")
+    if isinstance(w.rows, int) and w.rows > 100_000:
+        w = w.replace(B=96, rows=20_000)
+    elif w.B > 512:
+        w = w.replace(B=512)
+    b = synth.make_batch(w)
+    db = DeviceBatch(b)
+    sp, we = bool(layout & ops.PAIRS_SELF), bool(layout & ops.WITH_EMBEDDINGS)
+    _, inter = db.fwd(layout=layout)
+    torch.cuda.synchronize()
+    off = orc.lengths_to_offsets(b.lengths)
+    ref = orc.embbag_fwd(b.tables, w.dtype, w.B, off, b.indices, b.e0, self_pairs=sp, with_embeddings=we)
+    np.testing.assert_array_equal(inter.cpu().numpy(), ref["out"].astype(np.float32))

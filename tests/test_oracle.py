@@ -562,3 +562,98 @@ def test_q8_table_wise_hand_example():
     assert got[0, 0].tolist() == [0.5 * 7 - 2, 0.5 * 255 - 2, 0.5 * 129 - 2]
     assert got[1, 0].tolist() == [0.5 * 11 - 3, 0.5 * 4 - 3, 0.5 * 5 - 3]
 
+
+
+# ---------------------------------------------------------------------------
+# Interaction layouts: self-pairs and the embeddings concatenated alongside
+# ---------------------------------------------------------------------------
+_LAYOUTS = {"strict": (False, False), "self_pairs": (True, False), "with_embeddings": (False, True),
+            "self_pairs_with_embeddings": (True, True)}
+
+
+def test_golden_layouts(golden_dir):
+    """The four layouts and the with-embeddings backward against hand-worked values."""
+    with open(os.path.join(golden_dir, "worked_example_layouts_f3_d2.json")) as f:
+        g = json.load(f)
+    e0, pooled = np.array(g["e0"], float), np.array(g["pooled"], float)
+    for name, (sp, we) in _LAYOUTS.items():
+        assert orc.interact(e0, pooled, self_pairs=sp, with_embeddings=we).tolist() == g["out"][name], name
+    bw = g["backward_with_embeddings"]
+    r = orc.interact_bwd(e0, pooled, np.array(bw["d_out"], float), with_embeddings=True)
+    assert r["d_e0"].tolist() == bw["d_e0"]
+    assert r["d_pooled"].tolist() == bw["d_pooled"]
+
+
+@pytest.mark.parametrize("self_pairs", [False, True])
+def test_with_embeddings_output_is_z_then_the_dots_of_the_plain_layout(self_pairs):
+    """With the embeddings concatenated the row is Z's F vectors (a copy) followed by exactly
+    the dots of the layout without them."""
+    rng = np.random.default_rng(17 + self_pairs)
+    B, T, D = 3, 5, 6
+    e0, pooled = rng.standard_normal((B, D)), rng.standard_normal((B, T, D))
+    a = orc.interact(e0, pooled, self_pairs=self_pairs, with_embeddings=True)
+    b = orc.interact(e0, pooled, self_pairs=self_pairs)
+    F = T + 1
+    assert a.shape == (B, F * D + orc.pair_count(F, self_pairs))
+    np.testing.assert_array_equal(a[:, :D], e0)
+    np.testing.assert_array_equal(a[:, D:F * D].reshape(B, T, D), pooled)
+    np.testing.assert_array_equal(a[:, F * D:], b[:, D:])
+
+
+@pytest.mark.parametrize("self_pairs", [False, True])
+def test_with_embeddings_backward_finite_differences(self_pairs):
+    """<d_out, out(Z)> stays quadratic in Z with the embeddings concatenated (their part is
+    linear): the central difference is exact up to rounding."""
+    rng = np.random.default_rng(23 + self_pairs)
+    B, T, D = 2, 3, 4
+    e0 = rng.standard_normal((B, D))
+    pooled = rng.standard_normal((B, T, D))
+    d_out = rng.standard_normal((B, (T + 1) * D + orc.pair_count(T + 1, self_pairs)))
+    g = orc.interact_bwd(e0, pooled, d_out, self_pairs=self_pairs, with_embeddings=True)
+
+    def loss(e, p):
+        return float((d_out * orc.interact(e, p, self_pairs=self_pairs, with_embeddings=True)).sum())
+    h = 1e-3
+    for b in range(B):
+        for f in range(T + 1):
+            for d in range(D):
+                ep, pp, em, pm = e0.copy(), pooled.copy(), e0.copy(), pooled.copy()
+                if f == 0:
+                    ep[b, d] += h
+                    em[b, d] -= h
+                    want = g["d_e0"][b, d]
+                else:
+                    pp[b, f - 1, d] += h
+                    pm[b, f - 1, d] -= h
+                    want = g["d_pooled"][b, f - 1, d]
+                num = (loss(ep, pp) - loss(em, pm)) / (2 * h)
+                assert abs(num - want) <= 1e-8 * (1 + abs(want)), (b, f, d, num, want)
+
+
+def test_planted_layout_mistakes_are_caught(monkeypatch, golden_dir):
+    """A backward that forgets the direct gradient of the concatenated embeddings, and a
+    forward that puts the dots before the embeddings, both fail the pins above."""
+    real_bwd = orc.interact_bwd
+
+    def no_direct(e0, pooled, d_out, self_pairs=False, with_embeddings=False):
+        r = real_bwd(e0, pooled, d_out, self_pairs=self_pairs, with_embeddings=with_embeddings)
+        r["d_pooled"] = r["dZ"][:, 1:].copy()
+        return r
+    with monkeypatch.context() as m:
+        m.setattr(orc, "interact_bwd", no_direct)
+        with pytest.raises(AssertionError):
+            test_golden_layouts(golden_dir)
+        with pytest.raises(AssertionError):
+            test_with_embeddings_backward_finite_differences(False)
+    real_fwd = orc.interact
+
+    def dots_first(e0, pooled, self_pairs=False, with_embeddings=False):
+        out = real_fwd(e0, pooled, self_pairs=self_pairs, with_embeddings=with_embeddings)
+        if not with_embeddings:
+            return out
+        F, D = pooled.shape[1] + 1, pooled.shape[2]
+        return np.concatenate([out[:, F * D:], out[:, :F * D]], axis=1)
+    with monkeypatch.context() as m:
+        m.setattr(orc, "interact", dots_first)
+        with pytest.raises(AssertionError):
+            test_golden_layouts(golden_dir)
