@@ -451,10 +451,11 @@ def bench_backward(steps, warmup, adagrad=False, cpu=False):
     return res
 
 
-def bench_forward_q8(inp, steps, warmup):
-    """The fused forward on row-wise 8-bit versions of the capacity tables (per row D
-    uint8 codes, then an fp32 scale and bias; random codes, the bandwidth does not
-    depend on them), same batch. Bytes per lookup: D + 8 + 4."""
+def bench_forward_q4(inp, steps, warmup):
+    """The fused forward on row-wise 4-bit versions of the capacity tables (per row 64 bytes
+    of codes, an fp32 scale and bias, padding to one aligned 128-byte line; random codes, the
+    bandwidth does not depend on them), same batch. Bytes per lookup: D/2 + 8 + 4 (the line
+    holds 56 bytes of padding that a lookup does not need)."""
     import torch
 
     from sparse_embedding_lookup_dlrm_amd import ops, synth
@@ -463,24 +464,28 @@ def bench_forward_q8(inp, steps, warmup):
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(synth.stream_seed(w.seed, "values") + 8)
+    stride = synth.q4_row_stride(w.D)
     packed = []
     for n in inp["rows"]:
-        t = torch.empty((n, w.D + 8), dtype=torch.uint8, device=dev)
-        t[:, :w.D] = torch.randint(0, 256, (n, w.D), dtype=torch.uint8, device=dev, generator=g)
-        sb = t[:, w.D:].view(torch.float32)  # [n, 2]: scale, bias
-        sb[:, 0].uniform_(1e-4, 2e-4, generator=g)
+        t = torch.zeros((n, stride), dtype=torch.uint8, device=dev)
+        t[:, :w.D // 2] = torch.randint(0, 256, (n, w.D // 2), dtype=torch.uint8, device=dev, generator=g)
+        sb = t[:, w.D // 2:w.D // 2 + 8].view(torch.float32)  # [n, 2]: scale, bias
+        sb[:, 0].uniform_(1e-3, 2e-3, generator=g)
         sb[:, 1].uniform_(-0.02, -0.01, generator=g)
         packed.append(t)
     out = torch.empty((w.B, w.out_width), dtype=torch.float32, device=dev)
-    run = lambda: ops.embbag_fwd_q8(packed, inp["offsets"], inp["d_idx"], w.B, inp["d_e0"], out_inter=out,
+    run = lambda: ops.embbag_fwd_q4(packed, inp["offsets"], inp["d_idx"], w.B, inp["d_e0"], out_inter=out,
                                     status=inp["status"])
-    ms, _ = time_steps(run, steps, warmup)
+    detail = {}
+    ms, _ = time_steps(run, steps, warmup, detail, per_step_events=True)
     nnz = len(inp["indices"])
     P = (w.T + 1) * w.T // 2
-    alg = nnz * (w.D + 8 + 4) + 4 * (w.T * w.B + 1) + 4 * w.B * w.D + 4 * w.B * (w.D + P)
+    alg = nnz * (w.D // 2 + 8 + 4) + 4 * (w.T * w.B + 1) + 4 * w.B * w.D + 4 * w.B * (w.D + P)
     del packed, out
     torch.cuda.empty_cache()
-    return {"workload": w.name + "-q8", "ms_per_step": ms, "lookups_per_s": nnz / (ms / 1e3),
+    return {"workload": w.name + "-q4", "ms_per_step": ms, "ms_median": detail["ms_median"],
+            "ms_min": detail["ms_min"], "lookups_per_s": nnz / (ms / 1e3), "row_stride_bytes": stride,
+            "table_bytes": sum(inp["rows"]) * stride,
             "algorithmic_bytes": alg, "hbm_GBps_algorithmic": alg / (ms / 1e3) / 1e9,
             "frac_of_8TBps": alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, "status": int(inp["status"].item())}
 
@@ -502,13 +507,15 @@ def bench_forward_q8t(inp, steps, warmup):
     out = torch.empty((w.B, w.out_width), dtype=torch.float32, device=dev)
     run = lambda: ops.embbag_fwd_q8t(tabs, sb, inp["offsets"], inp["d_idx"], w.B, inp["d_e0"], out_inter=out,
                                      status=inp["status"])
-    ms, _ = time_steps(run, steps, warmup)
+    detail = {}
+    ms, _ = time_steps(run, steps, warmup, detail, per_step_events=True)
     nnz = len(inp["indices"])
     P = (w.T + 1) * w.T // 2
     alg = nnz * (w.D + 4) + 4 * (w.T * w.B + 1) + 4 * w.B * w.D + 4 * w.B * (w.D + P)
     del tabs, out
     torch.cuda.empty_cache()
-    return {"workload": w.name + "-q8t", "ms_per_step": ms, "lookups_per_s": nnz / (ms / 1e3),
+    return {"workload": w.name + "-q8t", "ms_per_step": ms, "ms_median": detail["ms_median"],
+            "ms_min": detail["ms_min"], "lookups_per_s": nnz / (ms / 1e3),
             "algorithmic_bytes": alg, "hbm_GBps_algorithmic": alg / (ms / 1e3) / 1e9,
             "frac_of_8TBps": alg / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, "status": int(inp["status"].item())}
 
@@ -704,7 +711,7 @@ def main():
     ap.add_argument("--cpu-samples", type=int, default=6144)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
-    ap.add_argument("--no-q8", action="store_true", help="skip the 8-bit-row forward timing")
+    ap.add_argument("--no-q8", action="store_true", help="skip the 4-bit and 8-bit row forward timings")
     ap.add_argument("--no-configs", action="store_true", help="skip the forward timing on the smaller workloads")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain copy of this size (for counter calibration)")
@@ -823,9 +830,9 @@ def main():
     del tables
     torch.cuda.empty_cache()
     if not args.no_q8:
-        res["forward_q8"] = bench_forward_q8(inp, args.steps, args.warmup)
-        log(f"fused forward, 8-bit rows: {res['forward_q8']['ms_per_step'] * 1e3:.1f} us/step, "
-            f"{res['forward_q8']['hbm_GBps_algorithmic']:.0f} GB/s")
+        res["forward_q4"] = bench_forward_q4(inp, args.steps, args.warmup)
+        log(f"fused forward, row-wise 4-bit rows: {res['forward_q4']['ms_per_step'] * 1e3:.1f} us/step, "
+            f"{res['forward_q4']['hbm_GBps_algorithmic']:.0f} GB/s")
         res["forward_q8t"] = bench_forward_q8t(inp, args.steps, args.warmup)
         log(f"fused forward, table-wise 8-bit rows: {res['forward_q8t']['ms_per_step'] * 1e3:.1f} us/step, "
             f"{res['forward_q8t']['hbm_GBps_algorithmic']:.0f} GB/s")

@@ -81,11 +81,13 @@ typedef enum {
 /* Bytes of the library-owned scratch array behind dlrm_embbag_bwd_update_noalloc (one per GPU). */
 #define DLRM_NOALLOC_SCRATCH_BYTES (64u << 20)
 
-/* DLRM_Q8: row-wise 8-bit tables (only through dlrm_embbag_fwd_q8): a row is D uint8 codes q
- * followed by its fp32 scale and fp32 bias, value = scale * q + bias.
- * DLRM_Q8T: table-wise 8-bit tables (only through dlrm_embbag_fwd_q8t): a row is D uint8 codes,
- * one (scale, bias) pair per table. */
-typedef enum { DLRM_F32 = 0, DLRM_F16 = 1, DLRM_BF16 = 2, DLRM_Q8 = 3, DLRM_Q8T = 4 } dlrm_dtype;
+/* DLRM_Q8T: table-wise 8-bit tables (only through dlrm_embbag_fwd_q8t): a row is D uint8 codes,
+ * one (scale, bias) pair per table.
+ * DLRM_Q4: row-wise 4-bit tables (only through dlrm_embbag_fwd_q4): a row is D 4-bit codes,
+ * its fp32 scale and fp32 bias, padded to a power of two (see dlrm_embbag_fwd_q4).
+ * (3 was a row-wise 8-bit format whose D + 8 byte rows straddle two 128-byte lines; it is
+ * not offered: it was slower than the bf16 rows it compresses.) */
+typedef enum { DLRM_F32 = 0, DLRM_F16 = 1, DLRM_BF16 = 2, DLRM_Q8T = 4, DLRM_Q4 = 5 } dlrm_dtype;
 
 /* Interaction output layouts ("DLRM" note, section 3, The Pairwise Interaction
  * Layer): bits of the `layout` argument of dlrm_embbag_fwd_ex, dlrm_interact_ex
@@ -165,20 +167,26 @@ int dlrm_embbag_fwd_ex(int32_t T, int32_t B, int32_t D, int32_t dtype, const voi
                        void* stream);
 
 /*
- * The fused forward on row-wise 8-bit tables: row r of table t is D uint8 codes
- * q followed by the row's fp32 scale and fp32 bias (D + 8 bytes, one contiguous
- * read per lookup), value[d] = scale * q[d] + bias; a lookup reads D + 8 bytes
- * instead of 2 D (bf16). The "Terabyte Embedding Tables..." article (section
- * "Scaling limits and the reality of production") reports 4-bit quantization of
- * what is exchanged between devices; here the same idea is applied, at 8 bits,
- * to the rows stored in HBM.
- *   tables     host array [T] of device pointers (16-byte aligned), table t is
- *              uint8 [rows[t]][D + 8] as above
+ * The fused forward on row-wise 4-bit tables. The "Terabyte Embedding Tables..."
+ * article (section "Scaling limits and the reality of production") reports
+ * 4-bit integer quantization of the embedding vectors exchanged between
+ * devices; here the same 4-bit codes, with a scale and a bias per row, are what
+ * the tables store in HBM, so a lookup reads a quarter of the bf16 row's bytes
+ * plus 8.
+ * Row r of table t starts at byte r * S, S = the smallest power of two >= D/2 + 8
+ * (128 for D = 128, 256 for D = 256, 512 for D = 512), so a row never straddles
+ * more 128-byte lines than its size needs (one line for D = 128):
+ *   bytes [0, D/2)        codes: byte k holds column 2k in its low 4 bits and
+ *                         column 2k + 1 in its high 4 bits (q in 0..15)
+ *   bytes [D/2, D/2 + 4)  fp32 scale s_r;  bytes [D/2 + 4, D/2 + 8)  fp32 bias c_r
+ *   the rest              padding, never read
+ *   value[d] = s_r * q[d] + c_r
+ *   tables     host array [T] of device pointers (16-byte aligned), table t is uint8 [rows[t]][S]
  *   D          128, 256 or 512
  *   out_inter  required; out_pooled optional; everything else as in dlrm_embbag_fwd.
- * Pooling sums scale * q per column in fp32 and adds the bag's summed biases.
+ * Pooling sums s_r * q per column in fp32 and adds the bag's summed biases.
  */
-int dlrm_embbag_fwd_q8(int32_t T, int32_t B, int32_t D, const void* const* tables, const int64_t* rows,
+int dlrm_embbag_fwd_q4(int32_t T, int32_t B, int32_t D, const void* const* tables, const int64_t* rows,
                        const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0,
                        float* out_pooled, float* out_inter, int32_t* status, void* stream);
 

@@ -56,8 +56,9 @@ class BagError(ValueError):
 # Storage decoding (exact: every fp32/fp16/bf16 value is an fp64 value)
 # ---------------------------------------------------------------------------
 class Q8Table:
-    """Row-wise 8-bit table: codes uint8 [rows, D] and fp32 (scale, bias) [rows, 2];
-    row r stands for scale_r * codes[r] + bias_r. Indexing a row gives (codes, pair)."""
+    """Affine 8-bit table: codes uint8 [rows, D] and fp32 (scale, bias) [rows, 2];
+    row r stands for scale_r * codes[r] + bias_r. Indexing a row gives (codes, pair).
+    The table-wise form (one pair for the whole table) is built by table_wise."""
 
     def __init__(self, codes: np.ndarray, scale_bias: np.ndarray):
         assert codes.dtype == np.uint8 and scale_bias.dtype == np.float32
@@ -76,12 +77,43 @@ class Q8Table:
         return cls(codes, np.tile(pair, (codes.shape[0], 1)))
 
 
+class Q4Table:
+    """Row-wise 4-bit table in its stored form: uint8 [rows, S] with S >= D/2 + 8. Row r
+    holds D/2 code bytes (column 2k in the low 4 bits of byte k, column 2k + 1 in the high
+    4 bits), then the row's fp32 scale and fp32 bias (little-endian), then padding; it
+    stands for scale_r * q + bias_r. Indexing a row gives (its bytes, D)."""
+
+    def __init__(self, packed: np.ndarray, D: int):
+        assert packed.dtype == np.uint8 and packed.ndim == 2 and packed.shape[1] >= D // 2 + 8 and D % 2 == 0
+        self.packed, self.D = packed, D
+        self.shape = (packed.shape[0], D)
+
+    def __getitem__(self, r):
+        return self.packed[r], self.D
+
+
+def decode_q4_row(row: np.ndarray, D: int) -> np.ndarray:
+    """One stored 4-bit row -> float64 [D], nibble by nibble."""
+    q = np.zeros(D, dtype=np.float64)
+    for k in range(D // 2):
+        byte = int(row[k])
+        q[2 * k] = byte & 0xF
+        q[2 * k + 1] = byte >> 4
+    scale = float(np.frombuffer(bytes(row[D // 2:D // 2 + 4]), dtype="<f4")[0])
+    bias = float(np.frombuffer(bytes(row[D // 2 + 4:D // 2 + 8]), dtype="<f4")[0])
+    return scale * q + bias
+
+
 def decode(table, dtype: str) -> np.ndarray:
     """Stored table (or row) -> float64. bf16 tables arrive as uint16 bit patterns;
-    "q8" rows arrive as (codes, (scale, bias)) from a Q8Table.
+    "q8" rows arrive as (codes, (scale, bias)) from a Q8Table, "q4" rows as
+    (stored bytes, D) from a Q4Table.
 
     "f64" (float64 tables) is accepted for the finite-difference pins only.
     """
+    if dtype == "q4":
+        row, D = table
+        return decode_q4_row(row, D)
     if dtype == "q8":
         codes, sb = table
         sb = np.asarray(sb, dtype=np.float64)

@@ -21,7 +21,7 @@ int dtype_bytes(int dtype) {
     case DLRM_F32: return 4;
     case DLRM_F16:
     case DLRM_BF16: return 2;
-    case DLRM_Q8:
+    case DLRM_Q4:
     case DLRM_Q8T: return 1;
     default: return 0;
   }
@@ -75,7 +75,7 @@ int bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tabl
                const float* d_out, float lr, int opt, float eps, float* const* state, float* d_e0,
                int32_t* unique_keys, int32_t* seg_offsets, int32_t* num_unique, int32_t* perm, void* workspace,
                size_t ws_bytes, int32_t* status, void* stream) {
-  if (dtype == DLRM_Q8 || dtype == DLRM_Q8T) return DLRM_E_UNSUPPORTED;  // defined for fp32 / fp16 / bf16
+  if (dtype == DLRM_Q4 || dtype == DLRM_Q8T) return DLRM_E_UNSUPPORTED;  // defined for fp32 / fp16 / bf16
   int rc = check_batch(T, B, D, dtype, const_cast<const void* const*>(tables), rows, offsets, indices, nnz);
   if (rc != DLRM_OK) return rc;
   if (!e0 || !pooled || !d_out || !workspace) return DLRM_E_INVAL;
@@ -148,7 +148,7 @@ int dlrm_embbag_fwd_ex(int32_t T, int32_t B, int32_t D, int32_t dtype, const voi
                        const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
                        const float* e0, float* out_pooled, float* out_inter, int32_t layout, int32_t* status,
                        void* stream) {
-  if (dtype == DLRM_Q8 || dtype == DLRM_Q8T) return DLRM_E_UNSUPPORTED;  // 8-bit rows: dlrm_embbag_fwd_q8(t)
+  if (dtype == DLRM_Q4 || dtype == DLRM_Q8T) return DLRM_E_UNSUPPORTED;  // quantized rows: dlrm_embbag_fwd_q4 / _q8t
   if (layout < 0 || layout > (DLRM_PAIRS_SELF | DLRM_WITH_EMBEDDINGS)) return DLRM_E_INVAL;
   int rc = check_batch(T, B, D, dtype, tables, rows, offsets, indices, nnz);
   if (rc != DLRM_OK) return rc;
@@ -174,9 +174,9 @@ int dlrm_embbag_fwd_ex(int32_t T, int32_t B, int32_t D, int32_t dtype, const voi
 
 namespace {
 
-// Shared by the two 8-bit forwards: same checks, same launch; scale_bias is
+// Shared by the two quantized forwards: same checks, same launch; scale_bias is
 // the table-wise (scale, bias) array, or null for row-wise codes.
-int fwd_8bit(int32_t dtype, int32_t T, int32_t B, int32_t D, const void* const* tables, const float* scale_bias,
+int fwd_quantized(int32_t dtype, int32_t T, int32_t B, int32_t D, const void* const* tables, const float* scale_bias,
              const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0,
              float* out_pooled, float* out_inter, int32_t* status, void* stream) {
   int rc = check_batch(T, B, D, dtype, tables, rows, offsets, indices, nnz);
@@ -207,17 +207,17 @@ int fwd_8bit(int32_t dtype, int32_t T, int32_t B, int32_t D, const void* const* 
 
 extern "C" {
 
-int dlrm_embbag_fwd_q8(int32_t T, int32_t B, int32_t D, const void* const* tables, const int64_t* rows,
+int dlrm_embbag_fwd_q4(int32_t T, int32_t B, int32_t D, const void* const* tables, const int64_t* rows,
                        const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0,
                        float* out_pooled, float* out_inter, int32_t* status, void* stream) {
-  return fwd_8bit(DLRM_Q8, T, B, D, tables, nullptr, rows, offsets, indices, nnz, e0, out_pooled, out_inter, status,
-                  stream);
+  return fwd_quantized(DLRM_Q4, T, B, D, tables, nullptr, rows, offsets, indices, nnz, e0, out_pooled, out_inter,
+                       status, stream);
 }
 
 int dlrm_embbag_fwd_q8t(int32_t T, int32_t B, int32_t D, const void* const* tables, const float* scale_bias,
                         const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
                         const float* e0, float* out_pooled, float* out_inter, int32_t* status, void* stream) {
-  return fwd_8bit(DLRM_Q8T, T, B, D, tables, scale_bias, rows, offsets, indices, nnz, e0, out_pooled, out_inter,
+  return fwd_quantized(DLRM_Q8T, T, B, D, tables, scale_bias, rows, offsets, indices, nnz, e0, out_pooled, out_inter,
                   status, stream);
 }
 

@@ -33,9 +33,9 @@ struct Storage<DLRM_BF16> {
   static constexpr int per16 = 8;
 };
 template <>
-struct Storage<DLRM_Q8> {
-  static constexpr int bytes = 1;
-  static constexpr int per16 = 16;
+struct Storage<DLRM_Q4> {
+  static constexpr int bytes = 1;   // a code byte (two columns)
+  static constexpr int per16 = 32;
 };
 template <>
 struct Storage<DLRM_Q8T> {

@@ -402,6 +402,12 @@ using gptr = const __attribute__((address_space(1))) T*;
 template <int LB>
 struct LaneChunk;
 template <>
+struct LaneChunk<1> {
+  using type = uint32_t;  // low 8 bits used
+  __device__ static type load(uint64_t p) { return __builtin_nontemporal_load(reinterpret_cast<gptr<uint8_t>>(p)); }
+  __device__ static type zero() { return 0u; }
+};
+template <>
 struct LaneChunk<2> {
   using type = uint32_t;  // low 16 bits used
   __device__ static type load(uint64_t p) { return __builtin_nontemporal_load(reinterpret_cast<gptr<uint16_t>>(p)); }
@@ -471,7 +477,7 @@ __device__ __forceinline__ void acc_chunk(float* acc, const typename LaneChunk<L
   }
 }
 
-// Row-wise 8-bit rows: acc[0..LB) += s * q for the lane's LB codes q (uint8).
+// Table-wise 8-bit rows: acc[0..LB) += s * q for the lane's LB codes q (uint8).
 __device__ __forceinline__ float ubyte(uint32_t w, int k) { return static_cast<float>((w >> (8 * k)) & 0xffu); }
 
 template <int LB>
@@ -492,9 +498,38 @@ __device__ __forceinline__ void acc_chunk_q8(float* acc, const typename LaneChun
   }
 }
 
+// Row-wise 4-bit rows: the lane's LB code bytes hold 2 LB columns, byte k the
+// column 2k in its low nibble and 2k + 1 in its high nibble;
+// acc[0..2 LB) += s * q.
+__device__ __forceinline__ float nibble(uint32_t w, int k) { return static_cast<float>((w >> (4 * k)) & 0xfu); }
+
+template <int LB>
+__device__ __forceinline__ void acc_chunk_q4(float* acc, const typename LaneChunk<LB>::type& v, float s) {
+  if constexpr (LB == 1) {
+    acc[0] = fmaf(s, nibble(v, 0), acc[0]);
+    acc[1] = fmaf(s, nibble(v, 1), acc[1]);
+  } else if constexpr (LB == 2) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] = fmaf(s, nibble(v, k), acc[k]);
+  } else {
+    static_assert(LB == 4, "4-bit codes of 64, 128 or 256 bytes per row");
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = fmaf(s, nibble(v, k), acc[k]);
+  }
+}
+
+// Bytes from one row-wise 4-bit row to the next: the code bytes and the fp32
+// (scale, bias) pair, rounded up to a power of two so that a row never
+// straddles more lines than its size needs (one 128-byte line for 128 columns).
+__host__ __device__ constexpr int q4_row_stride(int code_bytes) {
+  int s = 16;
+  while (s < code_bytes + 8) s *= 2;
+  return s;
+}
+
 template <int DT, int LB>
 struct RowShape {
-  static constexpr int EL = LB / Storage<DT>::bytes;  // fp32 columns per lane
+  static constexpr int EL = DT == DLRM_Q4 ? 2 * LB : LB / Storage<DT>::bytes;  // fp32 columns per lane
   // rows per window (two windows in flight: 32 VGPRs); 8-bit rows also carry a
   // scale and a bias per row and keep more columns per lane, so their windows
   // are smaller
@@ -502,7 +537,7 @@ struct RowShape {
   // rows fewer in flight, which keeps them within 80 VGPRs without spills;
   // bf16 rows of 256 bytes keep 12: on the 64-table capacity batch 12, 16 and
   // 20 rows per window measured 780.5, 784.8 and 793.3 us, bit-identical)
-  static constexpr int WIN = DT == DLRM_Q8                   ? (LB >= 8 ? 4 : 8)
+  static constexpr int WIN = DT == DLRM_Q4                   ? (LB >= 4 ? 6 : 12)
                              : DT == DLRM_Q8T                ? (LB >= 8 ? 4 : 12)
                              : (DT != DLRM_F32 && LB == 16) ? 3
                              : (DT != DLRM_F32 && LB == 8)  ? 6
@@ -704,7 +739,7 @@ __device__ __forceinline__ void prepare_window(Window& w, const FwdArgs& a, cons
                                                const int* stage, const uint8_t* sbag, const char* const* tbase,
                                                const int* trows, int T, int q, int p1, uint64_t fallback,
                                                int tid, const float* qsb = nullptr) {
-  constexpr uint64_t kStride = QM == 1 ? RB + 8 : RB;
+  constexpr uint64_t kStride = QM == 1 ? q4_row_stride(RB) : RB;
   const int lane = tid & (kWave - 1);
   uint64_t addr = fallback;
   int tk = 0;
@@ -755,9 +790,9 @@ __device__ __forceinline__ void issue_window(const Window& w, typename C::type (
 
 template <int DT, int LB, int WIN>
 __device__ __forceinline__ void consume_window(const Window& w, typename LaneChunk<LB>::type (&v)[WIN],
-                                               float (&acc)[LB / Storage<DT>::bytes], RowCursor& cur, float* Z,
+                                               float (&acc)[RowShape<DT, LB>::EL], RowCursor& cur, float* Z,
                                                int LD, float* carry_w, int* carry_t_w, int tid, float& bacc) {
-  constexpr int EL = LB / Storage<DT>::bytes;
+  constexpr int EL = RowShape<DT, LB>::EL;
   const int lane = tid & (kWave - 1);
 #pragma unroll
   for (int j = 0; j < WIN; ++j) {
@@ -765,11 +800,12 @@ __device__ __forceinline__ void consume_window(const Window& w, typename LaneChu
     // select, so the load's register is only read, never overwritten early)
     const bool skipped = (w.smask >> j) & 1ull;
     const typename LaneChunk<LB>::type x = skipped ? LaneChunk<LB>::zero() : v[j];
-    if constexpr (DT == DLRM_Q8 || DT == DLRM_Q8T) {
+    if constexpr (DT == DLRM_Q4 || DT == DLRM_Q8T) {
       // scale * q summed per column; the biases of the bag's rows summed once
       const float sj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w.sc), j));
       const float bj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w.bi), j));
-      acc_chunk_q8<LB>(acc, x, skipped ? 0.f : sj);
+      if constexpr (DT == DLRM_Q4) acc_chunk_q4<LB>(acc, x, skipped ? 0.f : sj);
+      else acc_chunk_q8<LB>(acc, x, skipped ? 0.f : sj);
       bacc += skipped ? 0.f : bj;
     } else {
       acc_chunk<DT, LB>(acc, x);
@@ -784,7 +820,7 @@ __device__ __forceinline__ void consume_window(const Window& w, typename LaneChu
       }
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        dst[lane * EL + e] = (DT == DLRM_Q8 || DT == DLRM_Q8T) ? acc[e] + bacc : acc[e];
+        dst[lane * EL + e] = (DT == DLRM_Q4 || DT == DLRM_Q8T) ? acc[e] + bacc : acc[e];
         acc[e] = 0.f;
       }
       bacc = 0.f;
@@ -895,7 +931,7 @@ __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, c
                                              const uint8_t* sbag, const char* const* tbase, const int* trows, int T,
                                              int p0, int p1, float* Z, int LD, float* carry_w, int* carry_t_w,
                                              int tid, const float* qsb) {
-  constexpr int QM = DT == DLRM_Q8 ? 1 : (DT == DLRM_Q8T ? 2 : 0);
+  constexpr int QM = DT == DLRM_Q4 ? 1 : (DT == DLRM_Q8T ? 2 : 0);
   using C = LaneChunk<LB>;
   using RS = RowShape<DT, LB>;
   constexpr int EL = RS::EL;
@@ -1186,8 +1222,9 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
 // host side
 // ---------------------------------------------------------------------------
 int fwd_supported_row_bytes(int D, int dtype) {
-  const int s = dtype == DLRM_F32 ? 4 : ((dtype == DLRM_Q8 || dtype == DLRM_Q8T) ? 1 : 2);
-  const long rb = static_cast<long>(D) * s;
+  // bytes of one row's values: D codes of one byte (table-wise 8-bit), D / 2 (4-bit)
+  const long rb = dtype == DLRM_Q4 ? D / 2
+                  : static_cast<long>(D) * (dtype == DLRM_F32 ? 4 : dtype == DLRM_Q8T ? 1 : 2);
   if (rb < 16 || rb > 1024 || (rb & (rb - 1)) != 0) return 0;
   return static_cast<int>(rb);
 }
@@ -1209,6 +1246,7 @@ static int pick_samples_per_block(int T, int B, int D) {
 // 256..1024 bytes (fp32); MFMA interaction for 16-bit storage with T >= 24.
 static bool use_row_kernel(int D, int dtype) {
   const int rb = fwd_supported_row_bytes(D, dtype);
+  if (dtype == DLRM_Q4 || dtype == DLRM_Q8T) return rb >= 64 && rb <= 512;  // the only kernel for quantized rows
   return dtype == DLRM_F32 ? (rb >= 256 && rb <= 1024) : (rb >= 128 && rb <= 1024);
 }
 static bool use_mfma(int T, int D, int dtype) { return dtype != DLRM_F32 && T >= 24 && D % 16 == 0; }
@@ -1315,10 +1353,11 @@ static hipError_t launch_fwd_float(const FwdArgs& a, hipStream_t st) {
 
 template <int DT, int LPR>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  if constexpr (DT == DLRM_Q8 || DT == DLRM_Q8T) {  // 8-bit rows: row-streaming fused kernel only, 128..512 B
-    constexpr int LB = LPR * 16 / kWave;
+  if constexpr (DT == DLRM_Q4 || DT == DLRM_Q8T) {  // quantized rows: row-streaming fused kernel only
+    constexpr int LB = LPR * 16 / kWave;  // code bytes per lane
     if (!a.out_inter) return hipErrorInvalidValue;
-    if constexpr (LB == 2 || LB == 4 || LB == 8) return launch_rows<DT, LB>(a, st);
+    if constexpr (DT == DLRM_Q4 && (LB == 1 || LB == 2 || LB == 4)) return launch_rows<DT, LB>(a, st);
+    else if constexpr (DT == DLRM_Q8T && (LB == 2 || LB == 4 || LB == 8)) return launch_rows<DT, LB>(a, st);
     else return hipErrorInvalidValue;
   } else {
     return launch_fwd_float<DT, LPR>(a, st);
@@ -1344,7 +1383,7 @@ hipError_t launch_embbag_fwd(const FwdArgs& a, hipStream_t st) {
     case DLRM_F32: return launch_fwd_dt<DLRM_F32>(a, st);
     case DLRM_F16: return launch_fwd_dt<DLRM_F16>(a, st);
     case DLRM_BF16: return launch_fwd_dt<DLRM_BF16>(a, st);
-    case DLRM_Q8: return launch_fwd_dt<DLRM_Q8>(a, st);
+    case DLRM_Q4: return launch_fwd_dt<DLRM_Q4>(a, st);
     case DLRM_Q8T: return launch_fwd_dt<DLRM_Q8T>(a, st);
     default: return hipErrorInvalidValue;
   }

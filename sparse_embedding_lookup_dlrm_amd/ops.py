@@ -38,7 +38,7 @@ _SIGNATURES = {
                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "dlrm_embbag_fwd_ex": (ctypes.c_int, [_i32, _i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p, _c_void_p,
                                           _i64, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p]),
-    "dlrm_embbag_fwd_q8": (ctypes.c_int, [_i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p, _c_void_p, _i64,
+    "dlrm_embbag_fwd_q4": (ctypes.c_int, [_i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p, _c_void_p, _i64,
                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "dlrm_embbag_fwd_q8t": (ctypes.c_int, [_i32, _i32, _i32, _P(_c_void_p), _P(_f32), _P(_i64), _c_void_p,
                                            _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -230,19 +230,20 @@ def embbag_fwd(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: t
     return out_pooled, out_inter
 
 
-def embbag_fwd_q8(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: torch.Tensor, B: int,
+def embbag_fwd_q4(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: torch.Tensor, B: int,
                   e0: torch.Tensor, *, want_pooled: bool = False, out_pooled: Optional[torch.Tensor] = None,
                   out_inter: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
                   stream=None) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
-    """Fused forward on row-wise 8-bit tables: uint8 [rows, D + 8], each row D codes then its
-    fp32 scale and bias (synth.pack_q8_rows builds them); returns (pooled or None, [e0 | dots])."""
+    """Fused forward on row-wise 4-bit tables: uint8 [rows, D] per table (D = 128, 256 or 512;
+    a row is D/2 code bytes, its fp32 scale and bias, then padding: synth.pack_q4_rows builds
+    them); returns (pooled or None, [e0 | dots])."""
     T = len(tables)
     if T < 1:
         raise ValueError("need at least one table")
-    D = tables[0].shape[1] - 8
+    D = tables[0].shape[1]
     for t in tables:
-        if t.dtype != torch.uint8 or t.dim() != 2 or t.shape[1] != D + 8 or not t.is_contiguous():
-            raise ValueError("8-bit tables must be contiguous uint8 [rows, D + 8] with the same D")
+        if t.dtype != torch.uint8 or t.dim() != 2 or t.shape[1] != D or not t.is_contiguous():
+            raise ValueError("4-bit tables must be contiguous uint8 [rows, D] with the same D")
     _check_fwd_buffers(T, B, D, offsets, indices, e0, out_pooled, out_inter, status)
     _require_cuda(*tables, offsets, indices, e0, out_pooled, out_inter, status)
     ptrs = (_c_void_p * T)(*[t.data_ptr() for t in tables])
@@ -252,9 +253,9 @@ def embbag_fwd_q8(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices
         out_pooled = torch.empty((B, T, D), dtype=torch.float32, device=dev)
     if out_inter is None:
         out_inter = torch.empty((B, D + pair_count(T)), dtype=torch.float32, device=dev)
-    _check(lib().dlrm_embbag_fwd_q8(T, B, D, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(), _ptr(e0),
+    _check(lib().dlrm_embbag_fwd_q4(T, B, D, ptrs, rows, _ptr(offsets), _ptr(indices), indices.numel(), _ptr(e0),
                                     _ptr(out_pooled), _ptr(out_inter), _ptr(status), _stream(stream)),
-           "dlrm_embbag_fwd_q8")
+           "dlrm_embbag_fwd_q4")
     return out_pooled, out_inter
 
 

@@ -151,42 +151,56 @@ def gen_tables_host(w: Workload, rows: Optional[Sequence[int]] = None) -> List[n
     return out
 
 
-def quantize_rows_q8(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Row-wise 8-bit codes of an fp32 table: per row, scale = (max - min) / 255 (1 for a
-    constant row), bias = min, codes = round((x - min) / scale) clipped to [0, 255].
-    Returns (uint8 codes [rows, D], fp32 (scale, bias) [rows, 2])."""
+def quantize_rows_q4(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Row-wise 4-bit codes of an fp32 table: per row, scale = (max - min) / 15 (1 for a
+    constant row), bias = min, codes = round((x - min) / scale) clipped to [0, 15].
+    Returns (uint8 codes 0..15 [rows, D], fp32 (scale, bias) [rows, 2])."""
     x = np.asarray(x, dtype=np.float32)
     lo = x.min(axis=1)
     hi = x.max(axis=1)
-    scale = ((hi - lo) / np.float32(255)).astype(np.float32)
+    scale = ((hi - lo) / np.float32(15)).astype(np.float32)
     scale[scale == 0] = 1.0
-    codes = np.clip(np.rint((x - lo[:, None]) / scale[:, None]), 0, 255).astype(np.uint8)
+    codes = np.clip(np.rint((x - lo[:, None]) / scale[:, None]), 0, 15).astype(np.uint8)
     return codes, np.stack([scale, lo], axis=1).astype(np.float32)
 
 
-def pack_q8_rows(codes: np.ndarray, scale_bias: np.ndarray) -> np.ndarray:
-    """The stored form of a row-wise 8-bit table: per row, the D codes then the fp32 scale
-    and bias as 8 bytes (uint8 [rows, D + 8])."""
-    sb = np.ascontiguousarray(scale_bias, dtype=np.float32).view(np.uint8).reshape(codes.shape[0], 8)
-    return np.ascontiguousarray(np.concatenate([codes, sb], axis=1))
+def q4_row_stride(D: int) -> int:
+    """Bytes from one stored row-wise 4-bit row to the next: D/2 code bytes and 8 bytes of
+    scale and bias, rounded up to a power of two (= D for D = 128, 256, 512)."""
+    s = 16
+    while s < D // 2 + 8:
+        s *= 2
+    return s
 
 
-def gen_tables_q8_host(w: Workload, rows: Optional[Sequence[int]] = None):
-    """Row-wise 8-bit tables: the fp32 N(0, sigma) rows (or, for values="int", small
-    dyadic ones: codes 0..4, scale in {0.5, 1, 2}, bias in {-1, 0, 1}, every sum exact)
+def pack_q4_rows(codes: np.ndarray, scale_bias: np.ndarray) -> np.ndarray:
+    """The stored form of a row-wise 4-bit table: per row, D/2 bytes of codes (column 2k in
+    the low 4 bits of byte k, 2k + 1 in the high 4 bits), the fp32 scale and bias, zero
+    padding to q4_row_stride(D) bytes (uint8 [rows, stride])."""
+    n, D = codes.shape
+    out = np.zeros((n, q4_row_stride(D)), dtype=np.uint8)
+    c = codes.astype(np.uint8)
+    out[:, :D // 2] = (c[:, 0::2] & 0xF) | ((c[:, 1::2] & 0xF) << 4)
+    out[:, D // 2:D // 2 + 8] = np.ascontiguousarray(scale_bias, dtype=np.float32).view(np.uint8).reshape(n, 8)
+    return out
+
+
+def gen_tables_q4_host(w: Workload, rows: Optional[Sequence[int]] = None):
+    """Row-wise 4-bit tables: the fp32 N(0, sigma) rows (or, for values="int", small
+    dyadic ones: codes 0..15, scale in {0.5, 1, 2}, bias in {-1, 0, 1}, every sum exact)
     quantized per row. Returns a list of (codes, scale_bias)."""
     rows = table_rows(w) if rows is None else rows
     rng = _streams(w.seed)["values"]
     out = []
     for n in rows:
         if w.values == "int":
-            codes = rng.integers(0, 5, size=(n, w.D)).astype(np.uint8)
+            codes = rng.integers(0, 16, size=(n, w.D)).astype(np.uint8)
             sb = np.stack([rng.choice([0.5, 1.0, 2.0], size=n), rng.choice([-1.0, 0.0, 1.0], size=n)],
                           axis=1).astype(np.float32)
             out.append((codes, sb))
         else:
             v = rng.standard_normal(size=(n, w.D), dtype=np.float32) * np.float32(w.sigma)
-            out.append(quantize_rows_q8(v))
+            out.append(quantize_rows_q4(v))
     return out
 
 

@@ -1,5 +1,6 @@
-"""GPU parity of the fused forward on row-wise 8-bit tables (per row: uint8 codes, then
-an fp32 scale and bias) against the fp64 oracle.
+"""GPU parity of the fused forward on quantized tables -- row-wise 4-bit (per row:
+4-bit codes, an fp32 scale and bias, in one aligned line) and table-wise 8-bit (codes,
+one scale and bias per table) -- against the fp64 oracle.
 
 Tolerance: the values are fp32 products s*q + b, pooled in fp32 (error below
 gamma_n of the magnitude sum(|s q| + |b|)), and with T >= 24 the pooled-pooled dots
@@ -28,7 +29,7 @@ def _gpu():
 
 def _run(w, corrupt=None):
     rows = synth.table_rows(w)
-    q8 = synth.gen_tables_q8_host(w, rows)
+    q4 = synth.gen_tables_q4_host(w, rows)
     lengths = synth.gen_lengths(w)
     indices = synth.gen_indices(w, rows, lengths)
     if corrupt is not None:
@@ -36,16 +37,26 @@ def _run(w, corrupt=None):
         indices[corrupt] = rows[0] + 5  # out of table 0's range (position in table 0's bags)
     e0 = synth.gen_e0(w)
     dev = "cuda"
-    packed = [torch.from_numpy(synth.pack_q8_rows(c, sb)).to(dev) for c, sb in q8]
+    stored = [synth.pack_q4_rows(c, sb) for c, sb in q4]
+    packed = [torch.from_numpy(x).to(dev) for x in stored]
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     offsets = ops.lengths_to_offsets(torch.from_numpy(lengths).to(dev), status=status)
     idx = torch.from_numpy(indices).to(dev)
-    pooled, out = ops.embbag_fwd_q8(packed, offsets, idx, w.B, torch.from_numpy(e0).to(dev), want_pooled=True,
+    pooled, out = ops.embbag_fwd_q4(packed, offsets, idx, w.B, torch.from_numpy(e0).to(dev), want_pooled=True,
                                     status=status)
-    _, out2 = ops.embbag_fwd_q8(packed, offsets, idx, w.B, torch.from_numpy(e0).to(dev))
+    _, out2 = ops.embbag_fwd_q4(packed, offsets, idx, w.B, torch.from_numpy(e0).to(dev))
     torch.cuda.synchronize()
     assert torch.equal(out, out2)  # run to run, bit for bit
-    return q8, lengths, indices, e0, pooled.cpu().numpy(), out.cpu().numpy(), int(status.item())
+    return stored, q4, lengths, indices, e0, pooled.cpu().numpy(), out.cpu().numpy(), int(status.item())
+
+
+def _oracle_q4(w, stored, q4, lengths, indices, e0):
+    """The oracle decodes the stored bytes; the magnitudes use the same rows with |scale| and |bias|."""
+    off = orc.lengths_to_offsets(lengths)
+    r = orc.embbag_fwd([orc.Q4Table(x, w.D) for x in stored], "q4", w.B, off, indices, e0)
+    mags = [orc.Q4Table(synth.pack_q4_rows(c, np.abs(sb)), w.D) for c, sb in q4]
+    pm = orc.embbag_pool(mags, "q4", w.B, off, indices)
+    return r, pm, orc.interact(np.abs(e0), pm)
 
 
 def _oracle(w, q8, lengths, indices, e0):
@@ -57,63 +68,64 @@ def _oracle(w, q8, lengths, indices, e0):
     return r, pm, orc.interact(np.abs(e0), pm)
 
 
-@pytest.mark.parametrize("T,rows,D,B,seed", [(8, 5000, 128, 256, 61), (26, 3000, 256, 200, 62),
-                                             (64, 2000, 128, 96, 63), (4, 500, 512, 64, 64),
-                                             (30, 800, 512, 40, 65), (8, 3000, 128, 600, 66)])
-def test_q8_forward(T, rows, D, B, seed):
-    w = synth.Workload("q8", T=T, rows=rows, D=D, dtype="bf16", B=B, bag=("uniform", 0, 20), dist=("zipf", 1.05),
+@pytest.mark.parametrize("T,rows,D,B,seed", [(8, 3000, 128, 256, 61), (26, 2000, 256, 200, 62),
+                                             (64, 1500, 128, 64, 63), (4, 500, 512, 64, 64),
+                                             (30, 600, 512, 40, 65), (1, 900, 128, 300, 66)])
+def test_q4_forward(T, rows, D, B, seed):
+    """Row-wise 4-bit tables at D = 128, 256 and 512 (one, two and four 128-byte lines a
+    row), with fp32 dots (T < 24) and the MFMA Gram (T >= 24)."""
+    w = synth.Workload("q4", T=T, rows=rows, D=D, dtype="bf16", B=B, bag=("uniform", 0, 20), dist=("zipf", 1.05),
                        seed=seed)
-    q8, lengths, indices, e0, pooled, out, st = _run(w)
+    stored, q4, lengths, indices, e0, pooled, out, st = _run(w)
     assert st == 0
-    r, pm, mag = _oracle(w, q8, lengths, indices, e0)
+    r, pm, mag = _oracle_q4(w, stored, q4, lengths, indices, e0)
     np.testing.assert_array_equal(out[:, :D], e0)
-    assert_mag_close(pooled, r["pooled"], pm, RTOL_Q8, "q8 pooled")
-    assert_mag_close(out[:, D:], r["out"][:, D:], mag[:, D:], RTOL_Q8, "q8 dots")
+    assert_mag_close(pooled, r["pooled"], pm, RTOL_Q8, "q4 pooled")
+    assert_mag_close(out[:, D:], r["out"][:, D:], mag[:, D:], RTOL_Q8, "q4 dots")
 
 
-@pytest.mark.parametrize("T,D", [(6, 128), (40, 256)])
-def test_q8_forward_exact_dyadic_values(T, D):
-    """Codes 0..4 with scales in {0.5, 1, 2} and biases in {-1, 0, 1}: every sum and dot
-    is exact in fp32 (and in the MFMA split), so the output matches bit for bit."""
-    w = synth.Workload("q8int", T=T, rows=300, D=D, dtype="bf16", B=70, bag=("uniform", 0, 12),
-                       dist=("uniform",), seed=T, values="int")
-    q8, lengths, indices, e0, pooled, out, st = _run(w)
+@pytest.mark.parametrize("T,D", [(6, 128), (40, 256), (3, 512)])
+def test_q4_forward_exact_dyadic_values(T, D):
+    """Codes 0..15, scale in {0.5, 1, 2}, bias in {-1, 0, 1}, bags of at most 4 rows: every
+    value is at most 31 in size, a pooled sum at most 124 (exact in a bf16 hi part), a dot
+    at most 512 * 124^2 < 2^24, so every sum and dot is exact in fp32 and the GPU equals the
+    oracle bit for bit (the nibble order included)."""
+    w = synth.Workload("q4int", T=T, rows=300, D=D, dtype="bf16", B=70, bag=("uniform", 0, 4),
+                       dist=("uniform",), seed=T + 1, values="int")
+    stored, q4, lengths, indices, e0, pooled, out, st = _run(w)
     assert st == 0
-    r, _, _ = _oracle(w, q8, lengths, indices, e0)
+    r, _, _ = _oracle_q4(w, stored, q4, lengths, indices, e0)
     np.testing.assert_array_equal(pooled, r["pooled"].astype(np.float32))
     np.testing.assert_array_equal(out, r["out"].astype(np.float32))
 
 
-def test_q8_out_of_range_index_is_flagged_and_skipped():
-    w = synth.Workload("q8bad", T=3, rows=100, D=128, dtype="bf16", B=16, bag=("uniform", 1, 6),
-                       dist=("uniform",), seed=66)
-    q8, lengths, indices, e0, pooled, out, st = _run(w, corrupt=2)
-    assert st & 1  # DLRM_STATUS_BAD_INDEX
-    # the oracle of the same batch without that occurrence
-    off = orc.lengths_to_offsets(lengths)
-    bag = int(np.searchsorted(off, 2, side="right") - 1)
+def test_q4_out_of_range_index_is_flagged_and_skipped():
+    w = synth.Workload("q4bad", T=3, rows=100, D=128, dtype="bf16", B=16, bag=("uniform", 1, 6),
+                       dist=("uniform",), seed=9)
+    stored, q4, lengths, indices, e0, pooled, out, st = _run(w, corrupt=2)
+    assert st == ops.STATUS_BAD_INDEX
     keep = np.ones(len(indices), bool)
     keep[2] = False
-    lengths2 = lengths.copy()
-    lengths2[bag] -= 1
-    r, pm, _ = _oracle(w, q8, lengths2, indices[keep], e0)
+    off = orc.lengths_to_offsets(lengths)
+    lengths2 = np.array([int(keep[off[i]:off[i + 1]].sum()) for i in range(w.T * w.B)], dtype=np.int32)
+    r, pm, _ = _oracle_q4(w, stored, q4, lengths2, indices[keep], e0)
     assert_mag_close(pooled, r["pooled"], pm, RTOL_Q8, "pooled without the bad row")
 
 
-def test_q8_rejections():
+def test_q4_rejections():
     L = ops.lib()
-    tab = torch.zeros((10, 64 + 8), dtype=torch.uint8, device="cuda")
+    tab = torch.zeros((10, 64), dtype=torch.uint8, device="cuda")
     off = torch.zeros(2, dtype=torch.int32, device="cuda")
     e0 = torch.zeros((1, 64), device="cuda")
     out = torch.zeros((1, 64 + 1), device="cuda")
     P = ctypes.c_void_p
     ptrs = (P * 1)(tab.data_ptr())
     rows = (ctypes.c_int64 * 1)(10)
-    # D = 64 is not a supported 8-bit row width
-    assert L.dlrm_embbag_fwd_q8(1, 1, 64, ptrs, rows, P(off.data_ptr()), None, 0, P(e0.data_ptr()), None,
+    # D = 64 is not a supported 4-bit row width
+    assert L.dlrm_embbag_fwd_q4(1, 1, 64, ptrs, rows, P(off.data_ptr()), None, 0, P(e0.data_ptr()), None,
                                 P(out.data_ptr()), None, None) == -2
-    # the generic entry point does not take 8-bit tables
-    assert L.dlrm_embbag_fwd(1, 1, 64, 3, ptrs, rows, P(off.data_ptr()), None, 0, P(e0.data_ptr()), None,
+    # the generic entry point does not take 4-bit tables
+    assert L.dlrm_embbag_fwd(1, 1, 128, 5, ptrs, rows, P(off.data_ptr()), None, 0, P(e0.data_ptr()), None,
                              P(out.data_ptr()), None, None) == -2
 
 

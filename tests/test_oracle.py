@@ -528,23 +528,56 @@ def test_adagrad_state_accumulates_and_damps_the_step():
 
 
 # ---------------------------------------------------------------------------
-# Row-wise 8-bit tables
+# Row-wise 4-bit tables
 # ---------------------------------------------------------------------------
-def test_q8_decode_hand_example_and_pool_equals_dequantized_f64():
-    codes = np.array([[0, 255, 128], [7, 0, 1]], dtype=np.uint8)
-    sb = np.array([[0.5, -1.0], [0.25, 2.0]], dtype=np.float32)
-    tab = orc.Q8Table(codes, sb)
-    assert orc.decode(tab[0], "q8").tolist() == [-1.0, 126.5, 63.0]
-    assert orc.decode(tab[1], "q8").tolist() == [3.75, 2.0, 2.25]
-    rng = np.random.default_rng(4)
-    codes = rng.integers(0, 256, size=(30, 8)).astype(np.uint8)
-    sb = np.stack([rng.uniform(1e-4, 1e-2, 30), rng.uniform(-1, 1, 30)], axis=1).astype(np.float32)
+def _q4_golden(golden_dir):
+    with open(os.path.join(golden_dir, "worked_example_q4_rows.json")) as f:
+        return json.load(f)
+
+
+def test_q4_decode_hand_worked_nibbles(golden_dir):
+    """Stored bytes decoded by hand: the low 4 bits of a code byte are the even column."""
+    g = _q4_golden(golden_dir)
+    tab = orc.Q4Table(np.array(g["stored"], dtype=np.uint8), g["D"])
+    for r, want in enumerate(g["rows"]):
+        assert orc.decode(tab[r], "q4").tolist() == want
+    off = np.array(g["bags"]["offsets"])
+    idx = np.array(g["bags"]["indices"], dtype=np.int32)
+    got = orc.embbag_pool([tab], "q4", len(off) - 1, off, idx)
+    assert got[:, 0].tolist() == g["bags"]["pooled"]
+
+
+def test_q4_pool_equals_dequantized_f64():
+    """Pooling 4-bit rows equals pooling the rows dequantized in fp64 from the unpacked
+    codes (the synthetic packer's codes and pairs, not the oracle's decoder)."""
+    rng = np.random.default_rng(44)
+    D = 16
+    codes = rng.integers(0, 16, size=(30, D)).astype(np.uint8)
+    sb = np.stack([rng.uniform(1e-3, 1e-1, 30), rng.uniform(-1, 1, 30)], axis=1).astype(np.float32)
+    from sparse_embedding_lookup_dlrm_amd import synth
+    stored = synth.pack_q4_rows(codes, sb)
+    assert stored.shape == (30, synth.q4_row_stride(D))
     deq = codes.astype(np.float64) * sb[:, 0:1].astype(np.float64) + sb[:, 1:2].astype(np.float64)
     idx = rng.integers(0, 30, size=25).astype(np.int32)
     off = np.array([0, 3, 3, 10, 25])
-    got = orc.embbag_pool([orc.Q8Table(codes, sb)], "q8", 4, off, idx)
+    got = orc.embbag_pool([orc.Q4Table(stored, D)], "q4", 4, off, idx)
     want = orc.embbag_pool([deq], "f64", 4, off, idx)
     np.testing.assert_array_equal(got, want)
+
+
+def test_q4_planted_nibble_swap_is_caught(monkeypatch, golden_dir):
+    """A decoder that reads the high 4 bits as the even column fails the hand-worked pin."""
+    def swapped(row, D):
+        q = np.zeros(D)
+        for k in range(D // 2):
+            q[2 * k], q[2 * k + 1] = int(row[k]) >> 4, int(row[k]) & 0xF
+        scale = float(np.frombuffer(bytes(row[D // 2:D // 2 + 4]), dtype="<f4")[0])
+        bias = float(np.frombuffer(bytes(row[D // 2 + 4:D // 2 + 8]), dtype="<f4")[0])
+        return scale * q + bias
+    with monkeypatch.context() as m:
+        m.setattr(orc, "decode_q4_row", swapped)
+        with pytest.raises(AssertionError):
+            test_q4_decode_hand_worked_nibbles(golden_dir)
 
 
 # ---------------------------------------------------------------------------

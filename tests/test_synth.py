@@ -78,3 +78,21 @@ def test_quantize_table_q8_round_trip_within_half_step():
     assert codes.min() == 0 and codes.max() == 255
     c1, sb1 = synth.quantize_table_q8(np.full((3, 4), 0.75, np.float32))
     assert sb1.tolist() == [1.0, 0.75] and not c1.any()
+
+
+def test_quantize_rows_q4_round_trip_and_packing():
+    """Row-wise 4-bit codes reconstruct each row within half a step, and the stored form
+    puts column 2k in the low 4 bits of byte k with the scale and bias right after."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((20, 128)) * 0.01).astype(np.float32)
+    codes, sb = synth.quantize_rows_q4(x)
+    assert codes.max() <= 15
+    rec = codes.astype(np.float64) * sb[:, :1] + sb[:, 1:]
+    assert np.all(np.abs(rec - x) <= 0.5 * sb[:, :1] * (1 + 1e-5) + 1e-9)
+    stored = synth.pack_q4_rows(codes, sb)
+    assert stored.shape == (20, 128) and synth.q4_row_stride(128) == 128
+    assert synth.q4_row_stride(256) == 256 and synth.q4_row_stride(512) == 512
+    np.testing.assert_array_equal(stored[:, :64] & 0xF, codes[:, 0::2])
+    np.testing.assert_array_equal(stored[:, :64] >> 4, codes[:, 1::2])
+    np.testing.assert_array_equal(stored[:, 64:72].copy().view(np.float32), sb)
+    assert not stored[:, 72:].any()
