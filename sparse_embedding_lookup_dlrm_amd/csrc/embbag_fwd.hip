@@ -542,6 +542,7 @@ struct RowShape {
                              : (DT != DLRM_F32 && LB == 16) ? 3
                              : (DT != DLRM_F32 && LB == 8)  ? 6
                              : (DT == DLRM_BF16 && LB == 4) ? 12
+                             : (DT == DLRM_F32 && LB == 8)  ? 6
                                                              : (LB >= 4 ? 64 / LB : 16);
 };
 
@@ -665,6 +666,65 @@ __device__ __forceinline__ void gram_tile16(const float* Z, int LD, int D, int T
   for (int v = 0; v < 4; ++v) {
     const int zi = 1 + 16 * I + 4 * kq + v, zj = 1 + 16 * J + m;
     if (zi <= T && (zi > zj || (self_pairs && zi == zj)))
+      dots[self_pairs ? zi * (zi + 1) / 2 + zj : zi * (zi - 1) / 2 + zj] = acc[v];
+  }
+}
+
+// Three-way split of 2 fp32 values into bf16 parts: x = h + m + l up to
+// 2^-27 |x| (h = bf16(x), m = bf16(x - h), l = bf16(x - h - m); both
+// differences are exact in fp32).
+__device__ __forceinline__ void split3(float x0, float x1, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const float2_t x = {x0, x1};
+  h = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+  const float2_t r1 = {x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u)};
+  m = __builtin_bit_cast(uint32_t, __builtin_convertvector(r1, bf16x2_t));
+  const float2_t r2 = {r1[0] - __uint_as_float(m << 16), r1[1] - __uint_as_float(m & 0xffff0000u)};
+  l = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2_t));
+}
+
+__device__ __forceinline__ void load_split3x8(const float* p, bf16x8_t& h, bf16x8_t& m, bf16x8_t& l) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  const float4 y = *reinterpret_cast<const float4*>(p + 4);
+  uint4 uh, um, ul;
+  split3(x.x, x.y, uh.x, um.x, ul.x);
+  split3(x.z, x.w, uh.y, um.y, ul.y);
+  split3(y.x, y.y, uh.z, um.z, ul.z);
+  split3(y.z, y.w, uh.w, um.w, ul.w);
+  h = __builtin_bit_cast(bf16x8_t, uh);
+  m = __builtin_bit_cast(bf16x8_t, um);
+  l = __builtin_bit_cast(bf16x8_t, ul);
+}
+
+// One 16x16 tile (I, J), I >= J, of the Gram matrix of every Z row (e0 and
+// the pooled rows, fp32 in LDS) for fp32 tables, on v_mfma_f32_16x16x32_bf16
+// with each operand split three ways (hi, mid, lo) in registers: the products
+// hh + hm + mh + hl + lh + mm leave out terms below 5 * 2^-27 |a||b|, so the
+// dots keep fp32 accuracy. The lane layout is gram_tile16's; rows past the last
+// Z row read that row instead (their entries are dropped), so Z needs no
+// padding rows. Entries with zi > zj (zi >= zj for self-pairs), zi < F, go to
+// dots[zi(zi-1)/2 + zj] (dots[zi(zi+1)/2 + zj]).
+__device__ __forceinline__ void gram_tile16_x6(const float* Z, int LD, int D, int F, int I, int J,
+                                               float* __restrict__ dots, bool self_pairs, int lane) {
+  const int m = lane & 15, kq = lane >> 4;
+  const int ra = min(16 * I + m, F - 1), rb = min(16 * J + m, F - 1);
+  const float* za = Z + ra * LD + 8 * kq;
+  const float* zb = Z + rb * LD + 8 * kq;
+  floatx4_t acc = {};
+  for (int k0 = 0; k0 < D; k0 += 32) {
+    bf16x8_t ah, am, al, bh, bm, bl;
+    load_split3x8(za + k0, ah, am, al);
+    load_split3x8(zb + k0, bh, bm, bl);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bm, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bm, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int zi = 16 * I + 4 * kq + v, zj = 16 * J + m;
+    if (zi < F && (zi > zj || (self_pairs && zi == zj)))
       dots[self_pairs ? zi * (zi + 1) / 2 + zj : zi * (zi - 1) / 2 + zj] = acc[v];
   }
 }
@@ -1016,8 +1076,10 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
   int* trows = reinterpret_cast<int*>(lds + L.off_trows);
   float* qsb = reinterpret_cast<float*>(lds + L.off_qsb);
 
-  // one step per workgroup (no next sample to fetch during this one) for G = 1
+  // one step per workgroup (no next sample to fetch during this one) for G = 1;
+  // for G > 1 the host may still launch one step per workgroup (multi false)
   constexpr bool kMulti = G > 1;
+  const bool multi = kMulti && chunk > G;
   const int T = a.T, D = a.D, LD = L.LD;
   const int F = T + 1;
   const bool self_pairs = (a.layout & DLRM_PAIRS_SELF) != 0;
@@ -1144,9 +1206,10 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
 
     // next sample's index loads go out now; their values are staged after the output
     int r[kStagePerThread], tb[kStagePerThread];
-    if constexpr (kMulti) {
-      // (issued unconditionally, with no positions when there is no next sample:
-      // every load stays in bounds and no branch merges the registers)
+    if (multi) {
+      // (issued unconditionally in a multi-step launch, with no positions when
+      // there is no next sample: every load stays in bounds and no branch
+      // inside the launch's steps merges the registers)
       load_stage<NT>(a, nbeg, npos, T, has_next ? rfl(npos[T]) : 0, r, tb, tid);
     }
 
@@ -1163,7 +1226,16 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     float* dots = with_emb ? outs : outs + D;
     if (!with_emb)
       for (int d = tid; d < D; d += NT) outs[d] = Z[d];
-    if constexpr (MFMA) {
+    if constexpr (MFMA && DT == DLRM_F32) {
+      // the Gram of every Z row on MFMA with three-way bf16 splits
+      const int nt = (F + 15) / 16;
+      const int ntiles = nt * (nt + 1) / 2;
+      for (int tile = wave; tile < ntiles; tile += GW) {
+        int I, J;
+        block_pair(tile, I, J);
+        gram_tile16_x6(Z, LD, D, F, I, J, dots, self_pairs, tid & (kWave - 1));
+      }
+    } else if constexpr (MFMA) {
       // e0 dots in fp32; the Gram of the pooled rows on MFMA, every operand
       // split into bf16 hi + lo in registers as it is read from LDS
       e0_dots<NT>(Z, LD, D, T, dots, tid, self_pairs);
@@ -1185,7 +1257,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
     __syncthreads();
     // the next sample's index loads have had the whole interaction to land:
     // take them now, before the output stores are queued behind them
-    if constexpr (kMulti) {
+    if (multi) {
 #pragma unroll
       for (int k = 0; k < kStagePerThread; ++k) asm volatile("" : "+v"(r[k]));
     }
@@ -1205,7 +1277,7 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
 
     // stage the next sample: indices, cleared Z with its e0, no carries
     if (has_next) {
-      if constexpr (kMulti) write_stage<NT>(a, r, tb, stage, sbag, trows, tid);
+      if (multi) write_stage<NT>(a, r, tb, stage, sbag, trows, tid);
       if (next_empty) {
         float* z = Z + (1 + tid) * LD;
         for (int d = 0; d < D; d += 4) *reinterpret_cast<float4*>(z + d) = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1249,10 +1321,16 @@ static bool use_row_kernel(int D, int dtype) {
   if (dtype == DLRM_Q4 || dtype == DLRM_Q8T) return rb >= 64 && rb <= 512;  // the only kernel for quantized rows
   return dtype == DLRM_F32 ? (rb >= 256 && rb <= 1024) : (rb >= 128 && rb <= 1024);
 }
-static bool use_mfma(int T, int D, int dtype) { return dtype != DLRM_F32 && T >= 24 && D % 16 == 0; }
+// MFMA only where the per-sample Gram is a real dense contraction (F >= 25):
+// a bf16 hi + lo split of the pooled rows for 16-bit and quantized tables, a
+// three-way split of every Z row for fp32 tables.
+static bool use_mfma(int T, int D, int /*dtype*/) { return T >= 24 && D % 16 == 0; }
+// Z needs whole 32-row tiles only for the two-way split (its tiles do not
+// clamp their rows).
+static bool padded_z(int T, int D, int dtype) { return dtype != DLRM_F32 && use_mfma(T, D, dtype); }
 
 size_t fwd_lds_bytes(int T, int D, int dtype) {
-  if (use_row_kernel(D, dtype)) return static_cast<size_t>(make_row_layout(T, D, use_mfma(T, D, dtype)).bytes);
+  if (use_row_kernel(D, dtype)) return static_cast<size_t>(make_row_layout(T, D, padded_z(T, D, dtype)).bytes);
   const Tile tl = make_tile(T, D, 1);
   return tl.z_floats() * 4 + static_cast<size_t>(T) * 2 * 4;
 }
@@ -1290,7 +1368,7 @@ static int pick_groups(const FwdArgs& a, bool mfma) {
 
 template <int DT, int LB, bool MFMA, int G>
 static hipError_t launch_rows_g(const FwdArgs& a, hipStream_t st) {
-  const RowLayout L = make_row_layout(a.T, a.D, MFMA, G);
+  const RowLayout L = make_row_layout(a.T, a.D, MFMA && DT != DLRM_F32, G);
   auto kernel = fused_rows_kernel<DT, LB, MFMA, G>;
   // Short samples: two steps per workgroup, the second step's offsets, e0 and
   // indices fetched while the first is gathered. Long samples (hundreds of
@@ -1307,7 +1385,7 @@ static hipError_t launch_rows_g(const FwdArgs& a, hipStream_t st) {
 
 template <int DT, int LB, bool MFMA>
 static hipError_t launch_rows_m(const FwdArgs& a, hipStream_t st) {
-  switch (pick_groups(a, MFMA)) {
+  switch (pick_groups(a, MFMA && DT != DLRM_F32)) {
     case 8: return launch_rows_g<DT, LB, MFMA, 8>(a, st);
     case 4: return launch_rows_g<DT, LB, MFMA, 4>(a, st);
     case 2: return launch_rows_g<DT, LB, MFMA, 2>(a, st);
@@ -1318,10 +1396,9 @@ static hipError_t launch_rows_m(const FwdArgs& a, hipStream_t st) {
 template <int DT, int LB>
 static hipError_t launch_rows(const FwdArgs& a, hipStream_t st) {
   const bool mfma = use_mfma(a.T, a.D, DT);
-  if (static_cast<size_t>(make_row_layout(a.T, a.D, mfma).bytes) > kMaxLds) return hipErrorInvalidValue;
-  if constexpr (DT != DLRM_F32) {
-    if (mfma) return launch_rows_m<DT, LB, true>(a, st);
-  }
+  if (static_cast<size_t>(make_row_layout(a.T, a.D, padded_z(a.T, a.D, DT)).bytes) > kMaxLds)
+    return hipErrorInvalidValue;
+  if (mfma) return launch_rows_m<DT, LB, true>(a, st);
   return launch_rows_m<DT, LB, false>(a, st);
 }
 
