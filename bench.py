@@ -151,20 +151,22 @@ def summarize_backward(d: str, out: str, command: str, warmup: int, steps: int) 
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     starts = [i for i, r in enumerate(rows) if "build_keys" in r["Kernel_Name"]]
     steps_bwd = max(steps, 20)
-    groups = [("bwd-zipf-26t-d128-b2048 (SGD)", warmup + steps_bwd),
-              ("bwd-zipf-26t-d128-b2048 (row-wise AdaGrad)", min(warmup, 10) + steps_bwd),
-              ("multihot-8t4m-d64-fp16-b4096 (SGD)", min(warmup, 10) + steps_bwd)]
+    # each timing: its warm-up steps, the timed steps (one event pair), then as many
+    # steps again with an event pair each (for the median and min)
+    groups = [("bwd-zipf-26t-d128-b2048 (SGD)", warmup, warmup + 2 * steps_bwd),
+              ("bwd-zipf-26t-d128-b2048 (row-wise AdaGrad)", min(warmup, 10), min(warmup, 10) + 2 * steps_bwd),
+              ("multihot-8t4m-d64-fp16-b4096 (SGD)", min(warmup, 10), min(warmup, 10) + 2 * steps_bwd)]
     lines = [f"# rocprofv3 summary of: {command}", f"# source directory: {d}",
              "# mean kernel durations (us) over the timed steps of each backward timing"]
     k = 0
-    for name, count in groups:
+    for name, wu, count in groups:
         its = starts[k:k + count]
         k += count
         if len(its) < count:
             break
         per = {}
         order = []
-        timed = its[-steps_bwd:]
+        timed = its[wu:wu + steps_bwd]
         for n, i0 in enumerate(timed):
             i1 = starts[starts.index(i0) + 1] if starts.index(i0) + 1 < len(starts) else len(rows)
             seen = {}
@@ -675,6 +677,41 @@ def ramp(plan, inp):
     return 0
 
 
+def summarize_mfma(d: str, out: str, command: str) -> None:
+    """MFMA use of the forward kernel from a counter run with SQ_INSTS_VALU_MFMA_MOPS_BF16,
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: utilisation = MFMA-busy SIMD cycles /
+    (active cycles per XCD x 1024 SIMDs), bf16 MFMA flops = MOPS x 512, per dispatch."""
+    import csv
+
+    per = {}
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if FWD_KERNEL not in r["Kernel_Name"]:
+                    continue
+                k = int(r["Dispatch_Id"])
+                e = per.setdefault(k, {"name": r["Kernel_Name"].split("(")[0],
+                                       "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = [f"# rocprofv3 summary of: {command}", f"# source directory: {d}",
+             "# per dispatch of the forward kernel: MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / "
+             "(GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); bf16 MFMA TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / "
+             "duration (counter runs serialise dispatches, so durations here are not the bench's)",
+             "kernel | launch | us | mfma_busy_cycles | gui_active | mfma_util_pct | bf16_mfma_GFLOP | "
+             "bf16_mfma_TFLOPs"]
+    for i, k in enumerate(sorted(per)):
+        e = per[k]
+        busy, gui = e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), e.get("GRBM_GUI_ACTIVE", 0.0)
+        mops = e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        util = 100.0 * busy / (gui / 8 * 1024) if gui else 0.0
+        gflop = mops * 512 / 1e9
+        lines.append(f"{e['name'][:60]} | {i} | {e['us']:.1f} | {busy:.0f} | {gui:.0f} | {util:.2f} | {gflop:.3f} | "
+                     f"{gflop / e['us'] * 1e3 if e['us'] else 0:.2f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("\n".join(lines))
+
+
 def summarize_clock(d: str, out: str, command: str) -> None:
     """Per-dispatch duration and effective shader clock (GRBM_GUI_ACTIVE summed over the 8
     XCDs, / 8 / duration) of the forward kernel, in launch order."""
@@ -727,6 +764,8 @@ def main():
                     help="per-launch times of the capacity forward after a 3 s idle and after a table refill")
     ap.add_argument("--summarize-clock", default=None,
                     help="rocprofv3 dir of a --ramp run with --pmc GRBM_GUI_ACTIVE -> per-dispatch clock summary")
+    ap.add_argument("--summarize-mfma", default=None,
+                    help="rocprofv3 dir of a run with the MFMA counters -> per-dispatch MFMA utilisation")
     ap.add_argument("--kernel", default=FWD_KERNEL, help="kernel name needle for --traffic")
     ap.add_argument("--label", default="the capacity workload (64 bf16 tables x 10M rows, D=128, B=16384)",
                     help="workload label for --traffic")
@@ -740,6 +779,9 @@ def main():
         return 0
     if args.summarize_clock:
         summarize_clock(args.summarize_clock, args.out, args.command)
+        return 0
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.out, args.command)
         return 0
     if args.summarize_backward:
         summarize_backward(args.summarize_backward, args.out, args.command, args.warmup, args.steps)
