@@ -428,9 +428,11 @@ def bench_backward(steps, warmup, adagrad=False, cpu=False):
         state = [torch.zeros(n, dtype=torch.float32, device=dev) for n in b.rows]
         plan = ops.BwdPlan(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, d_e0=d_e0, workspace=ws,
                            status=status, row_state=state)
-        ms, _ = time_steps(plan.run, steps, warmup)
+        detail = {}
+        ms, _ = time_steps(plan.run, steps, warmup, detail)
         torch.cuda.synchronize()
         return {"workload": w.name, "optimizer": "rowwise_adagrad", "ms_per_step": ms,
+                "ms_median": detail["ms_median"], "ms_min": detail["ms_min"],
                 "lookups_per_s": len(b.indices) / (ms / 1e3), "status": int(status.item())}
     plan = ops.BwdPlan(tables, offsets, idx, w.B, e0, pooled, d_out, 0.01, d_e0=d_e0, workspace=ws, status=status)
     detail = {}
