@@ -295,6 +295,23 @@ int dlrm_embbag_bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void*
                            void* workspace, size_t ws_bytes, int32_t* status, void* stream);
 
 /*
+ * The sparse backward for a forward run with an interaction layout (the
+ * general form of dlrm_embbag_bwd_update and dlrm_embbag_bwd_update_adagrad).
+ * d_out is the gradient of dlrm_embbag_fwd_ex's output in that layout ("DLRM"
+ * note, section 3: self-pairs, and the embeddings concatenated alongside the
+ * dots, whose own gradient then adds to the pooled vectors' and to e0's).
+ *   layout     0 .. 3 (DLRM_PAIRS_SELF | DLRM_WITH_EMBEDDINGS); d_out is device fp32 [B][W]
+ *   row_state  NULL: SGD (eps unused); else row-wise AdaGrad as in dlrm_embbag_bwd_update_adagrad
+ * Every other argument, the outputs and the determinism as in dlrm_embbag_bwd_update.
+ */
+int dlrm_embbag_bwd_update_ex(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables,
+                              const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                              const float* e0, const float* pooled, const float* d_out, int32_t layout, float lr,
+                              float eps, float* const* row_state, float* d_e0, int32_t* unique_keys,
+                              int32_t* seg_offsets, int32_t* num_unique, int32_t* perm, void* workspace,
+                              size_t ws_bytes, int32_t* status, void* stream);
+
+/*
  * dlrm_embbag_bwd_update for callers that cannot allocate device memory (code
  * under graph capture, tight serving loops, harnesses that forbid it): the
  * same arguments minus the workspace, the same results bit for bit. The scratch

@@ -323,7 +323,8 @@ def segments(sorted_keys: np.ndarray):
 
 def embbag_bwd_update(tables: List[np.ndarray], dtype: str, B: int, offsets, indices, e0,
                       pooled, d_out, lr: float, optimizer: str = "sgd", state=None,
-                      eps: float = 1e-8) -> Dict[str, object]:
+                      eps: float = 1e-8, self_pairs: bool = False,
+                      with_embeddings: bool = False) -> Dict[str, object]:
     """Interaction backward, per-row gradient, update of the touched rows (all float64).
 
     optimizer "sgd": W <- W - lr * G. optimizer "rowwise_adagrad" (the "DLRM" note,
@@ -341,8 +342,9 @@ def embbag_bwd_update(tables: List[np.ndarray], dtype: str, B: int, offsets, ind
     rows = [tb.shape[0] for tb in tables]
     check_bags(T, B, rows, offsets, indices)
     D = tables[0].shape[1]
-    bw = interact_bwd(e0, pooled, d_out)
+    bw = interact_bwd(e0, pooled, d_out, self_pairs, with_embeddings)
     dZ = bw["dZ"]
+    d_pooled = bw["d_pooled"]  # the gradient of pooled[b, t]: dZ[b, 1 + t] (+ its own, with embeddings)
     key, tab, smp, base = occurrence_keys(rows, B, offsets, indices)
     perm = stable_order(key)
     uniq, seg = segments(key[perm])
@@ -351,7 +353,7 @@ def embbag_bwd_update(tables: List[np.ndarray], dtype: str, B: int, offsets, ind
     for u in range(U):
         for q in range(int(seg[u]), int(seg[u + 1])):
             p = int(perm[q])
-            grad[u] += dZ[smp[p], 1 + tab[p]]
+            grad[u] += d_pooled[smp[p], tab[p]]
     new_rows = np.zeros((U, D), dtype=np.float64)
     new_state = np.zeros(U, dtype=np.float64)
     for u in range(U):

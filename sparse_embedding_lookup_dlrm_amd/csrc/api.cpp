@@ -72,13 +72,14 @@ namespace {
 
 int bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables, const int64_t* rows,
                const int32_t* offsets, const int32_t* indices, int64_t nnz, const float* e0, const float* pooled,
-               const float* d_out, float lr, int opt, float eps, float* const* state, float* d_e0,
+               const float* d_out, int layout, float lr, int opt, float eps, float* const* state, float* d_e0,
                int32_t* unique_keys, int32_t* seg_offsets, int32_t* num_unique, int32_t* perm, void* workspace,
                size_t ws_bytes, int32_t* status, void* stream) {
   if (dtype == DLRM_Q4 || dtype == DLRM_Q8T) return DLRM_E_UNSUPPORTED;  // defined for fp32 / fp16 / bf16
   int rc = check_batch(T, B, D, dtype, const_cast<const void* const*>(tables), rows, offsets, indices, nnz);
   if (rc != DLRM_OK) return rc;
   if (!e0 || !pooled || !d_out || !workspace) return DLRM_E_INVAL;
+  if (layout < 0 || layout > (DLRM_PAIRS_SELF | DLRM_WITH_EMBEDDINGS)) return DLRM_E_INVAL;
   if (!aligned(e0, 16) || !aligned(pooled, 16) || !aligned(d_out, 4) || !aligned(workspace, 256)) return DLRM_E_ALIGN;
   if (d_e0 && !aligned(d_e0, 16)) return DLRM_E_ALIGN;
   if (D % 4 != 0 || D > 512) return DLRM_E_UNSUPPORTED;
@@ -107,6 +108,7 @@ int bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tabl
   a.total_rows = total;
   a.offsets = offsets; a.indices = indices; a.nnz = nnz;
   a.e0 = e0; a.pooled = pooled; a.d_out = d_out; a.lr = lr; a.opt = opt; a.eps = eps; a.d_e0 = d_e0;
+  a.layout = layout;
   a.unique_keys = unique_keys; a.seg_offsets = seg_offsets; a.num_unique = num_unique; a.perm = perm;
   a.workspace = workspace; a.ws_bytes = ws_bytes; a.status = status;
   return from_hip(launch_embbag_bwd_update(a, static_cast<hipStream_t>(stream)));
@@ -265,7 +267,7 @@ int dlrm_embbag_bwd_update(int32_t T, int32_t B, int32_t D, int32_t dtype, void*
                            const float* pooled, const float* d_out, float lr, float* d_e0, int32_t* unique_keys,
                            int32_t* seg_offsets, int32_t* num_unique, int32_t* perm, void* workspace, size_t ws_bytes,
                            int32_t* status, void* stream) {
-  return bwd_update(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, pooled, d_out, lr, kSgd, 0.f, nullptr,
+  return bwd_update(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, pooled, d_out, 0, lr, kSgd, 0.f, nullptr,
                     d_e0, unique_keys, seg_offsets, num_unique, perm, workspace, ws_bytes, status, stream);
 }
 
@@ -283,7 +285,7 @@ int dlrm_embbag_bwd_update_noalloc(int32_t T, int32_t B, int32_t D, int32_t dtyp
   if (need > kNoAllocScratchBytes) return DLRM_E_SCRATCH;
   void* ws = nullptr;
   if (noalloc_scratch(&ws) != hipSuccess) return DLRM_E_HIP;
-  return bwd_update(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, pooled, d_out, lr, kSgd, 0.f, nullptr,
+  return bwd_update(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, pooled, d_out, 0, lr, kSgd, 0.f, nullptr,
                     d_e0, unique_keys, seg_offsets, num_unique, perm, ws, kNoAllocScratchBytes, status, stream);
 }
 
@@ -293,7 +295,7 @@ int dlrm_embbag_bwd_update_adagrad(int32_t T, int32_t B, int32_t D, int32_t dtyp
                                    float* const* row_state, float* d_e0, int32_t* unique_keys, int32_t* seg_offsets,
                                    int32_t* num_unique, int32_t* perm, void* workspace, size_t ws_bytes,
                                    int32_t* status, void* stream) {
-  return bwd_update(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, pooled, d_out, lr, kRowwiseAdagrad, eps,
+  return bwd_update(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, pooled, d_out, 0, lr, kRowwiseAdagrad, eps,
                     row_state, d_e0, unique_keys, seg_offsets, num_unique, perm, workspace, ws_bytes, status, stream);
 }
 
@@ -313,6 +315,17 @@ int dlrm_embbag_bwd_plan(int32_t T, int32_t B, int32_t D, int64_t nnz, const int
   plan[2] = p.ibwd_shared ? 1 : 0;
   plan[3] = static_cast<int32_t>(p.max_lds);
   return p.ibwd_lds > kLds ? DLRM_E_UNSUPPORTED : DLRM_OK;
+}
+
+int dlrm_embbag_bwd_update_ex(int32_t T, int32_t B, int32_t D, int32_t dtype, void* const* tables,
+                              const int64_t* rows, const int32_t* offsets, const int32_t* indices, int64_t nnz,
+                              const float* e0, const float* pooled, const float* d_out, int32_t layout, float lr,
+                              float eps, float* const* row_state, float* d_e0, int32_t* unique_keys,
+                              int32_t* seg_offsets, int32_t* num_unique, int32_t* perm, void* workspace,
+                              size_t ws_bytes, int32_t* status, void* stream) {
+  return bwd_update(T, B, D, dtype, tables, rows, offsets, indices, nnz, e0, pooled, d_out, layout, lr,
+                    row_state ? kRowwiseAdagrad : kSgd, eps, row_state, d_e0, unique_keys, seg_offsets, num_unique,
+                    perm, workspace, ws_bytes, status, stream);
 }
 
 int dlrm_validate_bags(int32_t T, int32_t B, const int64_t* rows, const int32_t* offsets, const int32_t* indices,

@@ -1206,7 +1206,7 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
     }                                            \
   } while (0)
   if (n == 0 || !plan.ibwd_shared) {  // 1. interaction backward as a launch of its own
-    e = launch_interact_bwd(a.T, a.B, a.D, 0, a.e0, a.pooled, a.d_out, a.d_e0, d_pooled, st);
+    e = launch_interact_bwd(a.T, a.B, a.D, a.layout, a.e0, a.pooled, a.d_out, a.d_e0, d_pooled, st);
     if (e != hipSuccess) return e;
     if (n == 0) {  // no keys
       hipLaunchKernelGGL(zero_segments, dim3(1), dim3(64), 0, st, seg, nuniq);
@@ -1227,7 +1227,8 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   const IbwdShare none{a.T, a.D, false, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
   auto share = [&]() {
     if (nshare == 0) return none;
-    IbwdShare ia{a.T, a.D, false, false, a.e0, a.pooled, a.d_out, d_pooled, a.d_e0, 0, 0};
+    IbwdShare ia{a.T, a.D, (a.layout & DLRM_PAIRS_SELF) != 0, (a.layout & DLRM_WITH_EMBEDDINGS) != 0, a.e0, a.pooled,
+                 a.d_out, d_pooled, a.d_e0, 0, 0};
     ia.first = static_cast<int>(static_cast<long long>(a.B) * ishare / nshare);
     ia.count = static_cast<int>(static_cast<long long>(a.B) * (ishare + 1) / nshare) - ia.first;
     ++ishare;

@@ -63,8 +63,9 @@ struct BwdArgs {
   const float* pooled;
   const float* d_out;
   float lr;
-  int opt;    // Optimizer
-  float eps;  // row-wise AdaGrad: added to sqrt(state)
+  int opt;     // Optimizer
+  int layout;  // interaction output layout bits of d_out (DLRM_PAIRS_SELF, DLRM_WITH_EMBEDDINGS)
+  float eps;   // row-wise AdaGrad: added to sqrt(state)
   StateArgs state;
   float* d_e0;
   int32_t* unique_keys;

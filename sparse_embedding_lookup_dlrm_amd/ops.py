@@ -57,6 +57,10 @@ _SIGNATURES = {
                                                       _P(_c_void_p), _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                                       _c_void_p, _c_void_p, _size_t, _c_void_p, _c_void_p]),
     "dlrm_validate_bags": (ctypes.c_int, [_i32, _i32, _P(_i64), _P(_i32), _P(_i32), _i64]),
+    "dlrm_embbag_bwd_update_ex": (ctypes.c_int, [_i32, _i32, _i32, _i32, _P(_c_void_p), _P(_i64), _c_void_p,
+                                                 _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
+                                                 _P(_c_void_p), _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                 _c_void_p, _c_void_p, _size_t, _c_void_p, _c_void_p]),
     "dlrm_embbag_bwd_plan": (ctypes.c_int, [_i32, _i32, _i32, _i64, _P(_i64), _i32, _P(_i32)]),
     "dlrm_probe_row_gather": (ctypes.c_int, [_i32, _i32, _i32, _P(_c_void_p), _P(_i64), _P(_i64), _c_void_p, _i64,
                                              _c_void_p, _c_void_p]),
@@ -343,11 +347,11 @@ def bwd_workspace_bytes(T: int, B: int, D: int, nnz: int, rows: Sequence[int]) -
     return out.value
 
 
-def _check_bwd_buffers(T, B, D, offsets, indices, e0, pooled, d_out, d_e0, status):
+def _check_bwd_buffers(T, B, D, offsets, indices, e0, pooled, d_out, d_e0, status, layout=0):
     _check_bags(offsets, indices, T, B)
     _expect(e0, "e0", torch.float32, B * D)
     _expect(pooled, "pooled", torch.float32, B * T * D)
-    _expect(d_out, "d_out", torch.float32, B * (D + pair_count(T)))
+    _expect(d_out, "d_out", torch.float32, B * out_width(T, D, layout))
     _expect(d_e0, "d_e0", torch.float32, B * D)
     _expect(status, "status", torch.int32, 1, at_least=True)
 
@@ -364,12 +368,14 @@ def embbag_bwd_update(tables: Sequence[torch.Tensor], offsets: torch.Tensor, ind
                       e0: torch.Tensor, pooled: torch.Tensor, d_out: torch.Tensor, lr: float, *,
                       want_d_e0: bool = True, want_segments: bool = True, workspace: Optional[torch.Tensor] = None,
                       status: Optional[torch.Tensor] = None, stream=None,
-                      row_state: Optional[Sequence[torch.Tensor]] = None, eps: float = 1e-8) -> dict:
+                      row_state: Optional[Sequence[torch.Tensor]] = None, eps: float = 1e-8,
+                      layout: int = 0) -> dict:
     """Sparse backward + update of the touched rows (tables are updated in place): SGD, or
     row-wise AdaGrad when row_state (one fp32 [rows_t] tensor per table, updated in
-    place) is given (dlrm_embbag_bwd_update_adagrad)."""
+    place) is given (dlrm_embbag_bwd_update_adagrad); d_out in the interaction layout
+    `layout` (dlrm_embbag_bwd_update_ex when it is not 0)."""
     T, D, dt, ptrs, rows = _table_args(tables)
-    _check_bwd_buffers(T, B, D, offsets, indices, e0, pooled, d_out, None, status)
+    _check_bwd_buffers(T, B, D, offsets, indices, e0, pooled, d_out, None, status, layout)
     if row_state is not None:
         if len(row_state) != T:
             raise ValueError("row_state needs one tensor per table")
@@ -391,7 +397,15 @@ def embbag_bwd_update(tables: Sequence[torch.Tensor], offsets: torch.Tensor, ind
         res["num_unique"] = torch.empty(1, dtype=torch.int32, device=dev)
         res["perm"] = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
     g = res.get
-    if row_state is None:
+    if layout != 0:
+        sptr = (_c_void_p * T)(*[s_.data_ptr() for s_ in row_state]) if row_state is not None else None
+        _check(lib().dlrm_embbag_bwd_update_ex(T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), nnz, _ptr(e0),
+                                               _ptr(pooled), _ptr(d_out), int(layout), float(lr), float(eps), sptr,
+                                               _ptr(g("d_e0")), _ptr(g("unique_keys")), _ptr(g("seg_offsets")),
+                                               _ptr(g("num_unique")), _ptr(g("perm")), _ptr(workspace),
+                                               workspace.numel(), _ptr(status), _stream(stream)),
+               "dlrm_embbag_bwd_update_ex")
+    elif row_state is None:
         _check(lib().dlrm_embbag_bwd_update(T, B, D, dt, ptrs, rows, _ptr(offsets), _ptr(indices), nnz, _ptr(e0),
                                             _ptr(pooled), _ptr(d_out), float(lr), _ptr(g("d_e0")),
                                             _ptr(g("unique_keys")), _ptr(g("seg_offsets")), _ptr(g("num_unique")),

@@ -321,12 +321,14 @@ def gen_e0(w: Workload) -> np.ndarray:
     return rng.standard_normal(size=(w.B, w.D), dtype=np.float32)
 
 
-def gen_dout(w: Workload) -> np.ndarray:
-    """Upstream gradient of the interaction output [B, D + F(F-1)/2]."""
+def gen_dout(w: Workload, width: Optional[int] = None) -> np.ndarray:
+    """Upstream gradient of the interaction output [B, width]; width defaults to the plain
+    layout's D + F(F-1)/2 (another layout passes its own output width)."""
     rng = _streams(w.seed)["dout"]
+    W = w.out_width if width is None else int(width)
     if w.values == "int":
-        return rng.integers(-2, 3, size=(w.B, w.out_width)).astype(np.float32)
-    return rng.standard_normal(size=(w.B, w.out_width), dtype=np.float32)
+        return rng.integers(-2, 3, size=(w.B, W)).astype(np.float32)
+    return rng.standard_normal(size=(w.B, W), dtype=np.float32)
 
 
 @dataclasses.dataclass

@@ -25,18 +25,23 @@ def _round_storage(x64, dtype):
     return x32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def run_bwd(w: synth.Workload, lr=0.01, exact=False, twice=False, fused_fwd=True):
+def run_bwd(w: synth.Workload, lr=0.01, exact=False, twice=False, fused_fwd=True, layout=0):
     b = synth.make_batch(w, with_dout=True)
+    self_pairs = bool(layout & ops.PAIRS_SELF)
+    with_emb = bool(layout & ops.WITH_EMBEDDINGS)
+    if layout:
+        b.dout = synth.gen_dout(w, ops.out_width(w.T, w.D, layout))
     db = DeviceBatch(b)
-    pooled, _ = db.fwd(want_pooled=True, want_inter=fused_fwd)
+    pooled, _ = db.fwd(want_pooled=True, want_inter=fused_fwd, layout=layout)
     d_out = torch.from_numpy(b.dout).cuda()
     before = [t.clone() for t in db.tables]
-    res = ops.embbag_bwd_update(db.tables, db.offsets, db.indices, w.B, db.e0, pooled, d_out, lr, status=db.status)
+    res = ops.embbag_bwd_update(db.tables, db.offsets, db.indices, w.B, db.e0, pooled, d_out, lr, status=db.status,
+                                layout=layout)
     torch.cuda.synchronize()
     assert db.status.item() == 0
     if twice:
         tabs2 = [t.clone() for t in before]
-        res2 = ops.embbag_bwd_update(tabs2, db.offsets, db.indices, w.B, db.e0, pooled, d_out, lr)
+        res2 = ops.embbag_bwd_update(tabs2, db.offsets, db.indices, w.B, db.e0, pooled, d_out, lr, layout=layout)
         torch.cuda.synchronize()
         U1 = int(res["num_unique"].item())
         assert U1 == int(res2["num_unique"].item())
@@ -50,7 +55,7 @@ def run_bwd(w: synth.Workload, lr=0.01, exact=False, twice=False, fused_fwd=True
         # without the segment outputs (not built then): the same update and d_e0, bit for bit
         tabs3 = [t.clone() for t in before]
         res3 = ops.embbag_bwd_update(tabs3, db.offsets, db.indices, w.B, db.e0, pooled, d_out, lr,
-                                     want_segments=False)
+                                     want_segments=False, layout=layout)
         torch.cuda.synchronize()
         assert torch.equal(res["d_e0"], res3["d_e0"])
         for t1, t3 in zip(db.tables, tabs3):
@@ -60,11 +65,13 @@ def run_bwd(w: synth.Workload, lr=0.01, exact=False, twice=False, fused_fwd=True
     # oracle (own pooled, own offsets)
     off = orc.lengths_to_offsets(b.lengths)
     fwd = orc.embbag_fwd(b.tables, w.dtype, w.B, off, b.indices, b.e0)
-    r = orc.embbag_bwd_update(b.tables, w.dtype, w.B, off, b.indices, b.e0, fwd["pooled"], b.dout, lr)
+    r = orc.embbag_bwd_update(b.tables, w.dtype, w.B, off, b.indices, b.e0, fwd["pooled"], b.dout, lr,
+                              self_pairs=self_pairs, with_embeddings=with_emb)
     # magnitudes: the same computation on absolute values
     at = abs_tables(b.tables, w.dtype)
     pm = orc.embbag_pool(at, w.dtype, w.B, off, b.indices)
-    rm = orc.embbag_bwd_update(at, w.dtype, w.B, off, b.indices, np.abs(b.e0), pm, np.abs(b.dout), lr)
+    rm = orc.embbag_bwd_update(at, w.dtype, w.B, off, b.indices, np.abs(b.e0), pm, np.abs(b.dout), lr,
+                               self_pairs=self_pairs, with_embeddings=with_emb)
 
     U = int(res["num_unique"].item())
     nnz = len(b.indices)
@@ -112,6 +119,33 @@ def test_backward_zipf_26_tables_full():
 def test_backward_exact_arithmetic(name):
     w = synth.WORKLOADS[name].replace(values="int")
     run_bwd(w, lr=2.0 ** -7, exact=True)
+
+
+@pytest.mark.parametrize("layout", [1, 2, 3])
+@pytest.mark.parametrize("T,D,dtype,B", [(26, 128, "bf16", 300), (3, 16, "f32", 50), (30, 64, "f32", 70)])
+def test_backward_interaction_layouts(layout, T, D, dtype, B):
+    """The sparse backward for a forward in each interaction layout (self-pairs, the
+    embeddings concatenated, both): the interaction-backward share inside the sort and,
+    at T = 3, the small case."""
+    w = synth.Workload(f"blayout-{T}t-d{D}", T=T, rows=500, D=D, dtype=dtype, B=B, bag=("uniform", 0, 6),
+                       dist=("zipf", 1.1), seed=T * 7 + layout)
+    run_bwd(w, lr=0.01, twice=(T == 26), layout=layout)
+
+
+@pytest.mark.parametrize("layout", [1, 2, 3])
+def test_backward_interaction_layouts_exact(layout):
+    w = synth.WORKLOADS["tiny-4t1k-d16-b128"].replace(values="int")
+    run_bwd(w, lr=2.0 ** -7, exact=True, layout=layout)
+
+
+def test_backward_interaction_layout_own_launch():
+    """Self-pairs and the embeddings at T = 65, D = 512 bf16: the interaction backward in
+    its own launch, in the layout."""
+    w = synth.Workload("ibwd-own-layout", T=65, rows=2000, D=512, dtype="bf16", B=24, bag=("uniform", 0, 4),
+                       dist=("zipf", 1.1), seed=653)
+    nnz = int(synth.make_batch(w).indices.size)
+    assert not ops.bwd_plan(w.T, w.B, w.D, nnz, [2000] * w.T)["interact_bwd_shared"]
+    run_bwd(w, lr=0.01, fused_fwd=False, layout=3)
 
 
 def test_backward_multihot_fp16():

@@ -330,13 +330,13 @@ def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
             test_interaction_equals_gram_strict_lower(5)
 
     # (b) backward dropping the dZ_j term
-    def bad_bwd(e0_, pooled, d_out):
+    def bad_bwd(e0_, pooled, d_out, self_pairs=False, with_embeddings=False):
         B, T, D = pooled.shape
         Z = orc.stack_z(np.asarray(e0_, np.float64), pooled)
         dZ = np.zeros_like(Z)
         for k, i, j in orc.pairs(T + 1):
             dZ[:, i] += np.asarray(d_out, np.float64)[:, D + k][:, None] * Z[:, j]
-        return {"dZ": dZ, "d_e0": np.asarray(d_out, np.float64)[:, :D] + dZ[:, 0]}
+        return {"dZ": dZ, "d_e0": np.asarray(d_out, np.float64)[:, :D] + dZ[:, 0], "d_pooled": dZ[:, 1:]}
     with monkeypatch.context() as m:
         m.setattr(orc, "interact_bwd", bad_bwd)
         r = orc.embbag_bwd_update(_tables_f32(g), "f32", 2, off, idx, e0, np.array(g["pooled"], np.float64),
@@ -663,6 +663,38 @@ def test_with_embeddings_backward_finite_differences(self_pairs):
                 assert abs(num - want) <= 1e-8 * (1 + abs(want)), (b, f, d, num, want)
 
 
+@pytest.mark.parametrize("self_pairs,with_emb", [(True, False), (False, True), (True, True)])
+def test_sparse_backward_layouts_match_finite_differences(self_pairs, with_emb):
+    """The row gradients of the sparse backward in every interaction layout equal central
+    differences of <d_out, forward(tables)> taken through the whole forward (pooling,
+    then the layout's output)."""
+    tabs, off, idx, e0, _ = _random_instance(7, dtype="f64")
+    e0 = e0.astype(np.float64)
+    B = 5
+    T, D = len(tabs), tabs[0].shape[1]
+    W = ((T + 1) * D if with_emb else D) + orc.pair_count(T + 1, self_pairs)
+    d_out = np.random.default_rng(71).standard_normal((B, W))
+
+    def loss(tb):
+        r = orc.embbag_fwd(tb, "f64", B, off, idx, e0, self_pairs=self_pairs, with_embeddings=with_emb)
+        return float((r["out"] * d_out).sum())
+    fwd = orc.embbag_fwd(tabs, "f64", B, off, idx, e0, self_pairs=self_pairs, with_embeddings=with_emb)
+    r = orc.embbag_bwd_update(tabs, "f64", B, off, idx, e0, fwd["pooled"], d_out, lr=0.0,
+                              self_pairs=self_pairs, with_embeddings=with_emb)
+    grad_of = {int(k): r["grad"][u] for u, k in enumerate(r["unique_keys"])}
+    h = 1e-3
+    for t, tab in enumerate(tabs):
+        for row in range(tab.shape[0]):
+            for d in range(D):
+                tp = [x.copy() for x in tabs]
+                tm = [x.copy() for x in tabs]
+                tp[t][row, d] += h
+                tm[t][row, d] -= h
+                fd = (loss(tp) - loss(tm)) / (2 * h)
+                want = grad_of.get(int(r["base"][t]) + row, np.zeros(D))[d]
+                assert abs(fd - want) <= 1e-8 * (1 + abs(fd)), (t, row, d, fd, want)
+
+
 def test_planted_layout_mistakes_are_caught(monkeypatch, golden_dir):
     """A backward that forgets the direct gradient of the concatenated embeddings, and a
     forward that puts the dots before the embeddings, both fail the pins above."""
@@ -678,6 +710,8 @@ def test_planted_layout_mistakes_are_caught(monkeypatch, golden_dir):
             test_golden_layouts(golden_dir)
         with pytest.raises(AssertionError):
             test_with_embeddings_backward_finite_differences(False)
+        with pytest.raises(AssertionError):
+            test_sparse_backward_layouts_match_finite_differences(False, True)
     real_fwd = orc.interact
 
     def dots_first(e0, pooled, self_pairs=False, with_embeddings=False):
