@@ -797,8 +797,6 @@ struct RowCursor {
   bool to_carry;  // the next flushed sum continues a bag begun by an earlier wave
 };
 
-__device__ __forceinline__ bool to_carry_init(const int* sm_pos, int t0, int p0) { return rfl(sm_pos[t0]) < p0; }
-
 // Largest t in [0, T) with pos[t] <= x, for non-decreasing pos with pos[0] <=
 // x: the bag (skipping empty ones) that holds stream position x. A fixed
 // number of halving steps, each one LDS read, so that independent searches of
@@ -1028,8 +1026,9 @@ __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, c
   constexpr int EL = RS::EL;
   constexpr int WIN = RS::WIN;
   constexpr int RB = LB * kWave;  // row bytes
-  int t0 = 0;
-  while (rfl(pos[t0 + 1]) <= p0) ++t0;
+  // the bag holding p0 (a search of fixed length: a wave late in the sample
+  // would otherwise walk past dozens of bags before its first load)
+  const int t0 = rfl(last_le(pos, T, p0));
   RowCursor cur{rfl(pos[t0]) < p0};
   float acc[EL];
 #pragma unroll
