@@ -716,27 +716,41 @@ def summarize_mfma(d: str, out: str, command: str) -> None:
 
 def summarize_clock(d: str, out: str, command: str) -> None:
     """Per-dispatch duration and effective shader clock (GRBM_GUI_ACTIVE summed over the 8
-    XCDs, / 8 / duration) of the forward kernel, in launch order."""
+    XCDs, / 8 / duration) of the forward kernel, in launch order, with every other counter
+    of the run beside them (FETCH_SIZE as HBM GB/s at the copy calibration's x2.0, and the
+    translation counters as they are)."""
     import csv
 
     per = {}
+    names = []
     for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         with open(p) as f:
             for r in csv.DictReader(f):
-                if FWD_KERNEL not in r["Kernel_Name"] or r["Counter_Name"] != "GRBM_GUI_ACTIVE":
+                if FWD_KERNEL not in r["Kernel_Name"]:
                     continue
                 t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
-                per[int(r["Dispatch_Id"])] = (t0, (t1 - t0) / 1e3, float(r["Counter_Value"]))
+                e = per.setdefault(int(r["Dispatch_Id"]), {"t0": t0, "us": (t1 - t0) / 1e3})
+                c = r["Counter_Name"]
+                e[c] = e.get(c, 0.0) + float(r["Counter_Value"])
+                if c != "GRBM_GUI_ACTIVE" and c not in names:
+                    names.append(c)
+    cols = ["launch", "us", "GHz", "gap_us"] + ["FETCH_GBps" if c == "FETCH_SIZE" else c for c in names]
     lines = [f"# rocprofv3 summary of: {command}", f"# source directory: {d}",
              "# per dispatch of the forward kernel, in launch order: duration (us), effective shader clock (GHz) "
-             "= GRBM_GUI_ACTIVE / 8 XCDs / duration, gap since the previous dispatch ended (us)",
-             "launch | us | GHz | gap_us"]
+             "= GRBM_GUI_ACTIVE / 8 XCDs / duration, gap since the previous dispatch ended (us), then the run's "
+             "other counters per dispatch (FETCH_SIZE as GB/s: KiB x 1024 x 2.0 / duration)",
+             " | ".join(cols)]
     prev = None
     for i, k in enumerate(sorted(per)):
-        t0, us, act = per[k]
-        gap = (t0 - prev) / 1e3 if prev is not None else 0.0
-        prev = t0 + us * 1e3
-        lines.append(f"{i} | {us:.1f} | {act / 8 / us / 1e3:.2f} | {gap:.0f}")
+        e = per[k]
+        us = e["us"]
+        gap = (e["t0"] - prev) / 1e3 if prev is not None else 0.0
+        prev = e["t0"] + us * 1e3
+        row = [str(i), f"{us:.1f}", f"{e.get('GRBM_GUI_ACTIVE', 0.0) / 8 / us / 1e3:.2f}", f"{gap:.0f}"]
+        for c in names:
+            v = e.get(c, 0.0)
+            row.append(f"{v * 1024 * 2.0 / (us * 1e3):.0f}" if c == "FETCH_SIZE" else f"{v:.0f}")
+        lines.append(" | ".join(row))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     log("\n".join(lines))
