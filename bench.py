@@ -679,6 +679,70 @@ def ramp(plan, inp):
     return 0
 
 
+def stream(plan, seconds: float) -> int:
+    """Back-to-back launches of the capacity forward for `seconds` after a 3 s idle, with the
+    wall-clock time and mean launch time of every block of 25 launches (to line up with
+    power and clock samples that a separate process takes meanwhile)."""
+    import torch
+
+    st = torch.cuda.current_stream()
+    time.sleep(3.0)
+    rows = []
+    t_end = time.time() + seconds
+    while time.time() < t_end:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(25):
+            plan.run()
+        e1.record(st)
+        e1.synchronize()
+        rows.append((round(time.time(), 3), round(e0.elapsed_time(e1) * 1e3 / 25, 1)))
+    for t, us in rows:
+        log(f"{t:.3f} {us:.1f}")
+    print(json.dumps({"stream_blocks_of_25": rows}), flush=True)
+    return 0
+
+
+def summarize_power(smi_file: str, stream_json: str, out: str, command: str) -> None:
+    """Line up amd-smi samples (blocks of: a `date +%s.%N` line, then SOCKET_POWER, the GFX_0
+    clock, the MEM_0 clock, HOTSPOT and MEM temperature lines) with the block means of a
+    --stream run: each sample gets the block of 25 launches that was running at its time."""
+    import re
+
+    samples, cur = [], None
+    with open(smi_file) as f:
+        for line in f:
+            line = line.strip()
+            if re.fullmatch(r"\d+\.\d+", line):
+                cur = {"t": float(line), "vals": []}
+                samples.append(cur)
+            elif cur is not None:
+                m = re.search(r"(-?\d+(?:\.\d+)?)", line.split(":", 1)[1] if ":" in line else line)
+                if m:
+                    cur["vals"].append(float(m.group(1)))
+    with open(stream_json) as f:
+        blocks = [json.loads(x)["stream_blocks_of_25"] for x in f if x.startswith("{")][-1]
+    ends = [b[0] for b in blocks]
+    t0 = ends[0] if ends else 0.0
+    lines = [f"# power and clocks from a separate process beside: {command}",
+             "# t = wall time relative to the end of the first block of 25 launches (s); block_us = mean launch time "
+             "of the block running at that time (blank: the GPU idle or the host preparing)",
+             "t_s | socket_W | gfx0_MHz | mem_MHz | hotspot_C | mem_C | block_us"]
+    for smp in samples:
+        v = smp["vals"] + [float("nan")] * 5
+        blk = ""
+        for i, e in enumerate(ends):
+            start = ends[i - 1] if i else e - 0.025
+            if start <= smp["t"] <= e:
+                blk = f"{blocks[i][1]:.1f}"
+                break
+        lines.append(f"{smp['t'] - t0:+.3f} | {v[0]:.0f} | {v[1]:.0f} | {v[2]:.0f} | {v[3]:.0f} | {v[4]:.0f} | {blk}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("\n".join(lines))
+
+
 def summarize_mfma(d: str, out: str, command: str) -> None:
     """MFMA use of the forward kernel from a counter run with SQ_INSTS_VALU_MFMA_MOPS_BF16,
     SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: utilisation = MFMA-busy SIMD cycles /
@@ -778,6 +842,10 @@ def main():
                     help="time only the forward on the three smaller workloads (for counter runs)")
     ap.add_argument("--ramp", action="store_true",
                     help="per-launch times of the capacity forward after a 3 s idle and after a table refill")
+    ap.add_argument("--stream", type=float, default=0.0,
+                    help="seconds of back-to-back capacity forwards after a 3 s idle (block means with wall times)")
+    ap.add_argument("--summarize-power", nargs=2, metavar=("SMI_FILE", "STREAM_JSON"), default=None,
+                    help="amd-smi samples + a --stream run's output -> aligned power/clock table")
     ap.add_argument("--summarize-clock", default=None,
                     help="rocprofv3 dir of a --ramp run with --pmc GRBM_GUI_ACTIVE -> per-dispatch clock summary")
     ap.add_argument("--summarize-mfma", default=None,
@@ -792,6 +860,9 @@ def main():
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.copy_calibration_gib, args.out or TRAFFIC_FILE,
                       args.command, args.kernel, args.label)
+        return 0
+    if args.summarize_power:
+        summarize_power(args.summarize_power[0], args.summarize_power[1], args.out, args.command)
         return 0
     if args.summarize_clock:
         summarize_clock(args.summarize_clock, args.out, args.command)
@@ -832,6 +903,8 @@ def main():
 
     if args.ramp:
         return ramp(plan, inp)
+    if args.stream > 0:
+        return stream(plan, args.stream)
     if args.copy_calibration_gib > 0:
         copy_calibration(args.copy_calibration_gib, dev)
 
