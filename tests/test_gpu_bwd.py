@@ -333,10 +333,14 @@ def test_backward_wide_rows_bf16():
     run_bwd(w, lr=0.01, twice=True)
 
 
-def run_bwd_adagrad(w: synth.Workload, lr=0.05, eps=1e-6, steps=2):
+def run_bwd_adagrad(w: synth.Workload, lr=0.05, eps=1e-6, steps=2, layout=0):
     """Row-wise AdaGrad over `steps` identical backward calls (the state carries over),
     checked after every step against the oracle run from the same tables and state."""
     b = synth.make_batch(w, with_dout=True)
+    self_pairs = bool(layout & ops.PAIRS_SELF)
+    with_emb = bool(layout & ops.WITH_EMBEDDINGS)
+    if layout:
+        b.dout = synth.gen_dout(w, ops.out_width(w.T, w.D, layout))
     db = DeviceBatch(b)
     pooled, _ = db.fwd(want_pooled=True)
     d_out = torch.from_numpy(b.dout).cuda()
@@ -347,20 +351,22 @@ def run_bwd_adagrad(w: synth.Workload, lr=0.05, eps=1e-6, steps=2):
     fwd = orc.embbag_fwd(b.tables, w.dtype, w.B, off, b.indices, b.e0)
     at = abs_tables(b.tables, w.dtype)
     pm = orc.embbag_pool(at, w.dtype, w.B, off, b.indices)
-    rm = orc.embbag_bwd_update(at, w.dtype, w.B, off, b.indices, np.abs(b.e0), pm, np.abs(b.dout), lr)
+    rm = orc.embbag_bwd_update(at, w.dtype, w.B, off, b.indices, np.abs(b.e0), pm, np.abs(b.dout), lr,
+                               self_pairs=self_pairs, with_embeddings=with_emb)
     tabs_now = [t.copy() for t in b.tables]
     rtol = RTOL[w.dtype]
     store_ulp = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[w.dtype]
     for step in range(steps):
         before_state = [s.clone() for s in state]
         res = ops.embbag_bwd_update(db.tables, db.offsets, db.indices, w.B, db.e0, pooled, d_out, lr,
-                                    status=db.status, row_state=state, eps=eps)
+                                    status=db.status, row_state=state, eps=eps, layout=layout)
         torch.cuda.synchronize()
         assert db.status.item() == 0
         s_prev = [s.cpu().numpy().astype(np.float64) for s in before_state]
         # the oracle keeps the pooled vectors of the original tables, as the GPU call does
         r = orc.embbag_bwd_update(tabs_now, w.dtype, w.B, off, b.indices, b.e0, fwd["pooled"], b.dout, lr,
-                                  optimizer="rowwise_adagrad", state=s_prev, eps=eps)
+                                  optimizer="rowwise_adagrad", state=s_prev, eps=eps, self_pairs=self_pairs,
+                                  with_embeddings=with_emb)
         U = int(res["num_unique"].item())
         assert U == len(r["unique_keys"])
         base = r["base"]
@@ -408,6 +414,14 @@ def test_backward_rowwise_adagrad_shapes(T, D, B, dtype):
     w = synth.Workload("ada-shape", T=T, rows=60, D=D, dtype=dtype, B=B, bag=("uniform", 0, 10),
                        dist=("zipf", 1.2), seed=T * 10 + D)
     run_bwd_adagrad(w, lr=0.02, steps=3)
+
+
+@pytest.mark.parametrize("layout", [1, 2, 3])
+def test_backward_rowwise_adagrad_layouts(layout):
+    """Row-wise AdaGrad through dlrm_embbag_bwd_update_ex for a forward in each layout."""
+    w = synth.Workload("ada-layout", T=26, rows=400, D=64, dtype="bf16", B=80, bag=("uniform", 0, 6),
+                       dist=("zipf", 1.1), seed=300 + layout)
+    run_bwd_adagrad(w, lr=0.02, steps=2, layout=layout)
 
 
 def test_backward_plan_matches_call_sgd_and_adagrad():
