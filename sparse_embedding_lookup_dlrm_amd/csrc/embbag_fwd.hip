@@ -382,12 +382,14 @@ __global__ __launch_bounds__(kThreads) void interact_kernel(int T, int B, int D,
 // finished by adding the later waves' partial sums in wave order after a
 // barrier, so the result does not depend on timing.
 //
-// Interaction: with 16-bit tables and T >= 24 the Gram matrix of the T pooled
-// rows is a real dense contraction and runs on MFMA (32x32x16 bf16): once the
-// dots of e0 with each pooled row are taken in fp32, every pooled row is split
-// in place into bf16 hi + lo parts, and each Gram tile sums hi*hi + hi*lo +
-// lo*hi in fp32. Otherwise 4x4 register blocks of fp32 FMAs. [e0 | dots] is
-// assembled in LDS and written with contiguous stores.
+// Interaction: with T >= 24 the Gram matrix of Z is a real dense contraction
+// and runs on MFMA. For 16-bit and quantized tables the dots of e0 with each
+// pooled row are taken in fp32 and the Gram of the pooled rows in 16x16 tiles
+// (16x16x32 bf16), each operand split into bf16 hi + lo in registers as it is
+// read from LDS (hi*hi + hi*lo + lo*hi in fp32); for fp32 tables the whole
+// Gram in 32x32 tiles (32x32x16 bf16) with a three-way split. Otherwise 4x4
+// register blocks of fp32 FMAs. The output row is assembled in LDS and written
+// with contiguous stores.
 constexpr int kRowThreads = 512;
 constexpr int kRowWaves = kRowThreads / kWave;
 constexpr int kStageCap = 2048;  // staged indices per sample; longer streams read indices from HBM
