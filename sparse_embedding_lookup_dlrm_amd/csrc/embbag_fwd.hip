@@ -567,13 +567,17 @@ struct RowShape {
   // (16-bit rows of 512 and 1024 bytes and table-wise 8-bit rows keep a few
   // rows fewer in flight, which keeps them within 80 VGPRs without spills;
   // bf16 rows of 256 bytes keep 12: on the 64-table capacity batch 12, 16 and
-  // 20 rows per window measured 780.5, 784.8 and 793.3 us, bit-identical)
+  // 20 rows per window measured 780.5, 784.8 and 793.3 us, bit-identical;
+  // fp32 rows of 512 bytes keep 7, so that a 26-row sample split over two
+  // waves is gathered in one round trip per wave: 17.1 us against 17.6 us
+  // with 6 on the 26-table batch; 128-byte 16-bit rows keep 16: 12 measured
+  // 27.7 us against 27.3 us on the multi-hot batch)
   static constexpr int WIN = DT == DLRM_Q4                   ? (LB >= 4 ? 6 : 12)
                              : DT == DLRM_Q8T                ? (LB >= 8 ? 4 : 12)
                              : (DT != DLRM_F32 && LB == 16) ? 3
                              : (DT != DLRM_F32 && LB == 8)  ? 6
                              : (DT == DLRM_BF16 && LB == 4) ? 12
-                             : (DT == DLRM_F32 && LB == 8)  ? 6
+                             : (DT == DLRM_F32 && LB == 8)  ? 7
                                                              : (LB >= 4 ? 64 / LB : 16);
 };
 
