@@ -104,7 +104,7 @@ __device__ __forceinline__ void interact_bwd_sample(const IbwdShare& ia, int b, 
   for (int u = 0; u < kBatch; ++u) s_first[u] = s_value(threadIdx.x + u * kBwdThreads);
   // the upstream gradient of e0 (row 0 is item threadIdx.x < D/4 of the dZ loop)
   float4 go = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (d_e0 && threadIdx.x < D4) {
+  if (d_e0 && static_cast<int>(threadIdx.x) < D4) {
     const float* p = d_out + static_cast<size_t>(b) * W + 4 * threadIdx.x;
     go = make_float4(p[0], p[1], p[2], p[3]);
   }
