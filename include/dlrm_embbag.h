@@ -354,13 +354,17 @@ int dlrm_embbag_bwd_update_adagrad(int32_t T, int32_t B, int32_t D, int32_t dtyp
 
 /*
  * How dlrm_embbag_bwd_update / _adagrad will run for these sizes. Host only:
- * no GPU call, nothing enqueued. plan is host int32 [4]:
+ * no GPU call, nothing enqueued. plan is host int32 [5]:
  *   plan[0]  digit width of the radix sort of the occurrences (8 or 9 bits)
- *   plan[1]  sort passes (0 when nnz = 0)
+ *   plan[1]  sort passes (0 when nnz = 0; with plan[4] set, the passes of the
+ *            table with the most rows)
  *   plan[2]  1 when the interaction backward's samples run as extra workgroups
  *            of the sort's launches, 0 when it is a launch of its own (one
  *            sample's LDS does not fit beside the sort kernel's within 160 KiB)
  *   plan[3]  largest LDS of any workgroup of the call, in bytes
+ *   plan[4]  1 when the occurrences are sorted per table (nnz <= 2048 * T and
+ *            B <= 65536: one workgroup sorts each table's occurrences by row,
+ *            a second launch places them), 0 for the radix sort over all keys
  *   want_segments  nonzero when the call will ask for unique_keys, seg_offsets or num_unique
  * Returns DLRM_E_UNSUPPORTED when one sample's interaction backward alone exceeds 160 KiB.
  */

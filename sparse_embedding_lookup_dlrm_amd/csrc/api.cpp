@@ -1,6 +1,7 @@
 // C ABI of libdlrm_embbag: argument validation on the host, then kernel
 // launches on the caller's stream. Every check here runs before the first HIP
 // call, so a rejected call touches neither the device nor any output.
+#include <algorithm>
 #include <stdint.h>
 #include <string.h>
 
@@ -303,17 +304,19 @@ int dlrm_embbag_bwd_plan(int32_t T, int32_t B, int32_t D, int64_t nnz, const int
                          int32_t* plan) {
   if (T < 1 || B < 1 || D < 1 || nnz < 0 || nnz >= kI32Max || !rows || !plan) return DLRM_E_INVAL;
   if (T > DLRM_MAX_TABLES) return DLRM_E_UNSUPPORTED;
-  int64_t total = 0;
+  int64_t total = 0, max_rows = 0;
   for (int t = 0; t < T; ++t) {
     if (rows[t] < 1 || rows[t] >= kI32Max) return DLRM_E_INVAL;
     total += rows[t];
+    max_rows = std::max(max_rows, rows[t]);
   }
   if (total >= kI32Max) return DLRM_E_UNSUPPORTED;
-  const BwdPlanInfo p = bwd_plan(T, B, D, nnz, total, want_segments != 0);
+  const BwdPlanInfo p = bwd_plan(T, B, D, nnz, total, max_rows, want_segments != 0);
   plan[0] = p.radix_bits;
   plan[1] = p.passes;
   plan[2] = p.ibwd_shared ? 1 : 0;
   plan[3] = static_cast<int32_t>(p.max_lds);
+  plan[4] = p.table_sort ? 1 : 0;
   return p.ibwd_lds > kLds ? DLRM_E_UNSUPPORTED : DLRM_OK;
 }
 

@@ -7,8 +7,8 @@
 //    upstream gradient of pair (i, j) at (i, j) and (j, i), zero diagonal;
 //    dL/dpooled[b][t] = dZ[b][1 + t], dL/de0[b] = d_out[b][:D] + dZ[b][0].
 //    One workgroup per sample; in the sparse backward these workgroups ride as
-//    extras on the sort's scatter launches and the segment build, since
-//    nothing before the reduce reads dZ.
+//    extras on the sort's scatter launches and the segment build (or on the
+//    per-table sort's first launch), since nothing before the reduce reads dZ.
 // 2. keys: occurrence p of bag (t, b) gets key base_t + index (its global row)
 //    and value p; an out-of-range index, or a position no bag covers (invalid
 //    offsets), gets the sentinel key sum(rows).
@@ -18,6 +18,11 @@
 //    tiles, else scanned per digit by one kernel), a stable scatter that ranks
 //    equal digits inside a wave with ballots. The last pass also writes each
 //    sorted position's bag.
+//    Small batches (at most one tile of occurrences per table on average) sort
+//    per table instead: a table's occurrences form one range of positions and
+//    one range of keys, so one workgroup per table sorts its range by row
+//    index and a second launch places the ranges (table_sort, table_place):
+//    two launches in place of the key build and two or three per radix pass.
 // 4. segments (API outputs only): head flags (key differs from its
 //    predecessor), scanned into the position of each distinct key. With few
 //    reduce chunks the reduce counts each chunk's heads and the combine step
@@ -472,6 +477,416 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
     keys_out[dst] = key[r];
     vals_out[dst] = val[r];
     if (src_out) src_out[dst] = src[r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3b. per-table sort (small batches)
+// ---------------------------------------------------------------------------
+// Bags are in table-major order, so the occurrences of table t fill one range of
+// positions [c_t, c_t+1), and every key of table t lies below every key of table
+// t + 1. The stable order by key is therefore each table's stable order by row
+// index, one table after another, followed by the occurrences with an
+// out-of-range index and the positions outside every bag, in position order.
+//  - table_sort: one workgroup per table sorts its range by row index (LSD, 8-bit
+//    digits, as many passes as the table's row count needs; an out-of-range index
+//    takes the key rows_t, so it sorts after the table's valid ones) and writes
+//    it in that order to temporaries over the same range, with the table's count
+//    of valid occurrences. A range of at most one tile (2048) stays in registers,
+//    exchanged through LDS between passes; a longer one goes tile by tile through
+//    the workspace.
+//  - table_place: one workgroup per table moves its sorted range to the final
+//    slots: its valid occurrences after those of the earlier tables, its invalid
+//    ones after every valid occurrence, the gap positions and the invalid ones of
+//    earlier tables.
+// table_sort also carries the interaction-backward samples as extra workgroups. The
+// table ranges are the offsets at the table boundaries, clamped into [0, nnz] and
+// made non-decreasing (a running maximum), which changes nothing for a valid CSR.
+constexpr int kTableTile = kRadixTile;  // occurrences a table sorts in registers: 8 per thread
+constexpr int kTableBins = 1 << 8;
+
+// table_sort's LDS, carved from the dynamic segment (which the interaction
+// backward's extra workgroups of the same launch use for their own tile)
+struct TableSortLds {
+  int wcount[kRadixWaves][kTableBins];  // per-wave digit counts, then their prefix over the waves
+  int dbase[kTableBins];                // first slot of each digit
+  int hist[kTableBins];                 // digit totals (tiles through the workspace)
+  int cum[kTableBins];                  // keys of each digit in the tiles done so far
+  long long scan[kRadixWaves];          // block scan across the waves
+  int misc[4];                          // [0] invalid occurrences, [1..2] table bounds
+  int xk[kTableTile];                   // one tile's keys and values between passes
+  int xv[kTableTile];
+  int lbag[kTableTile];                 // each position's bag (one-tile ranges)
+};
+
+struct TableSortArgs {
+  int T, B;
+  const int32_t* offsets;
+  const int32_t* indices;
+  long long nnz;
+  int32_t* tkey;    // out [nnz]: each table's range sorted, its row index (rows_t for invalid)
+  int32_t* tval;    // out [nnz]: ... and the occurrence's position
+  int32_t* tbag;    // out [nnz]: ... and its bag's row of the pooled gradients (b * T + t)
+  int32_t* tvalid;  // out [T]: valid occurrences per table
+  int32_t* tbound;  // out [T + 1]: c_0 .. c_T
+  // ranges longer than a tile: keys and values ping-pong between (k0, v0) and
+  // (k1, v1); bag_of holds each position's bag
+  int32_t* k0;
+  int32_t* v0;
+  int32_t* k1;
+  int32_t* v1;
+  int32_t* bag_of;  // as tbag, by position
+  int32_t* status;
+};
+
+// c_t and c_t+1: the running maximum of the clamped table-boundary offsets,
+// worked out by each wave on its own (a butterfly, no LDS, no barrier).
+__device__ __forceinline__ void table_bounds(const int32_t* __restrict__ offsets, int B, long long nnz, int t,
+                                             int& c0, int& c1) {
+  const int lane = threadIdx.x & (kWave - 1);
+  long long m0 = 0, m1 = 0;
+  for (int s = lane; s <= t + 1; s += kWave) {
+    long long o = offsets[static_cast<long long>(s) * B];
+    o = o < 0 ? 0 : (o > nnz ? nnz : o);
+    if (s <= t) m0 = o > m0 ? o : m0;
+    m1 = o > m1 ? o : m1;
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const long long y0 = __shfl_xor(m0, o, kWave), y1 = __shfl_xor(m1, o, kWave);
+    m0 = y0 > m0 ? y0 : m0;
+    m1 = y1 > m1 ? y1 : m1;
+  }
+  c0 = static_cast<int>(m0);
+  c1 = static_cast<int>(m1);
+}
+
+// Stable ranking of one round of 64 keys of a wave by their digit d (ok false:
+// no key): the number of equal digits at lower lanes, plus the wave's running
+// count of that digit, which the round then advances.
+__device__ __forceinline__ int rank_in_wave(int d, bool ok, int* wcnt, unsigned long long lt) {
+  unsigned long long peers = __ballot(ok);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const unsigned long long m = __ballot((d >> bit) & 1);
+    peers &= ((d >> bit) & 1) ? m : ~m;
+  }
+  const int before = __popcll(peers & lt);
+  const int cnt = __popcll(peers);
+  int running = 0;
+  if (ok) running = wcnt[d];
+  __builtin_amdgcn_wave_barrier();
+  if (ok && before == 0) wcnt[d] = running + cnt;
+  __builtin_amdgcn_wave_barrier();
+  return running + before;
+}
+
+// Thread d: turns the waves' counts of digit d into their exclusive prefix over
+// the waves and returns the digit's total.
+__device__ __forceinline__ int wave_prefix(TableSortLds& sm) {
+  const int d = threadIdx.x;
+  int tot = 0;
+#pragma unroll
+  for (int w = 0; w < kRadixWaves; ++w) {
+    const int c = sm.wcount[w][d];
+    sm.wcount[w][d] = tot;
+    tot += c;
+  }
+  return tot;
+}
+
+__global__ __launch_bounds__(kBwdThreads) void table_sort(TableSortArgs a, MutTableArgs tabs, IbwdShare ia) {
+  if (ibwd_extra(ia, a.T)) return;
+  extern __shared__ __align__(16) float smem[];
+  TableSortLds& sm = *reinterpret_cast<TableSortLds*>(smem);
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int rows = tabs.rows[t];
+  const long long bag0 = static_cast<long long>(t) * a.B;
+  const long long nbags = static_cast<long long>(a.T) * a.B;
+  // Bag j = (t, b) holds [o_j, max(o_j, o_j+1)) once clamped into [0, nnz] (the
+  // CSR checks as in build_keys) and is recorded as b * T + t, its row of the
+  // pooled gradients. A position of the range that no bag of this table holds
+  // (invalid offsets only) keeps the table's first bag, t.
+  // The offsets of a thread's first kRadixRounds bags are loaded with the
+  // table bounds, the indices right after: two memory round trips in all.
+  constexpr int kBagBatch = kRadixRounds * kBwdThreads;
+  long long o0[kRadixRounds], o1[kRadixRounds];
+#pragma unroll
+  for (int u = 0; u < kRadixRounds; ++u) {
+    const int j = threadIdx.x + u * kBwdThreads;
+    const long long g = bag0 + (j < a.B ? j : 0);
+    o0[u] = a.offsets[g];
+    o1[u] = a.offsets[g + 1];
+  }
+  for (int q = threadIdx.x; q < kTableTile; q += kBwdThreads) sm.lbag[q] = t;
+  if (threadIdx.x == 0) sm.misc[0] = 0;
+  int c0, c1;
+  table_bounds(a.offsets, a.B, a.nnz, t, c0, c1);
+  const int N = c1 - c0;
+  const bool one_tile = N <= kTableTile;
+  if (threadIdx.x == 0) {
+    a.tbound[t] = c0;
+    if (t == a.T - 1) a.tbound[a.T] = c1;
+  }
+  int idx[kRadixRounds];  // one-tile ranges: slot q = wave * 512 + r * 64 + lane holds position c0 + q
+  if (one_tile) {
+#pragma unroll
+    for (int r = 0; r < kRadixRounds; ++r) {
+      const int q = wave * kRadixRounds * kWave + r * kWave + lane;
+      idx[r] = a.indices[q < N ? c0 + q : 0];
+    }
+  } else {
+    for (int q = threadIdx.x; q < N; q += kBwdThreads) a.bag_of[c0 + q] = t;
+  }
+  __syncthreads();  // the default bags are written
+  bool bad_off = false;
+  auto put_bag = [&](int j, long long s0, long long s1) {
+    const long long g = bag0 + j;
+    if (g == 0 && s0 != 0) bad_off = true;
+    if (g == nbags - 1 && s1 != a.nnz) bad_off = true;
+    if (s0 < 0) { s0 = 0; bad_off = true; }
+    if (s0 > a.nnz) { s0 = a.nnz; bad_off = true; }
+    if (s1 < 0) { s1 = 0; bad_off = true; }
+    if (s1 > a.nnz) { s1 = a.nnz; bad_off = true; }
+    if (s1 < s0) { s1 = s0; bad_off = true; }
+    const long long p0 = s0 > c0 ? s0 : c0, p1 = s1 < c1 ? s1 : c1;
+    const int row = j * a.T + t;
+    for (long long p = p0; p < p1; ++p) {
+      if (one_tile) sm.lbag[p - c0] = row;
+      else a.bag_of[p] = row;
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kRadixRounds; ++u) {
+    const int j = threadIdx.x + u * kBwdThreads;
+    if (j < a.B) put_bag(j, o0[u], o1[u]);
+  }
+  for (int j = threadIdx.x + kBagBatch; j < a.B; j += kBwdThreads) put_bag(j, a.offsets[bag0 + j], a.offsets[bag0 + j + 1]);
+  if (bad_off) flag(a.status, DLRM_STATUS_BAD_OFFSETS);
+  // keys are in [0, rows]: as many 8-bit passes as rows needs bits
+  const int passes = (32 - __clz(rows) + 7) / 8;
+  int nbad = 0;
+  if (one_tile) {
+    // keys in registers
+    int key[kRadixRounds], val[kRadixRounds], rank[kRadixRounds];
+#pragma unroll
+    for (int r = 0; r < kRadixRounds; ++r) {
+      const int q = wave * kRadixRounds * kWave + r * kWave + lane;
+      const bool ok = q < N;
+      const bool valid = idx[r] >= 0 && idx[r] < rows;
+      key[r] = valid ? idx[r] : rows;
+      val[r] = c0 + q;
+      nbad += (ok && !valid) ? 1 : 0;
+    }
+    __syncthreads();  // the bags are in LDS
+    // the passes: rank in each wave, prefix over the waves and digits, exchange
+    for (int ps = 0; ps < passes; ++ps) {
+      const int shift = 8 * ps;
+#pragma unroll
+      for (int w = 0; w < kRadixWaves; ++w) sm.wcount[w][threadIdx.x] = 0;
+      __syncthreads();
+      int dig[kRadixRounds];
+#pragma unroll
+      for (int r = 0; r < kRadixRounds; ++r) {
+        const int q = wave * kRadixRounds * kWave + r * kWave + lane;
+        const bool ok = q < N;
+        const int d = (key[r] >> shift) & (kTableBins - 1);
+        dig[r] = ok ? d : -1;
+        rank[r] = rank_in_wave(d, ok, sm.wcount[wave], lt);
+      }
+      __syncthreads();
+      long long total;
+      const int tot = wave_prefix(sm);
+      sm.dbase[threadIdx.x] = static_cast<int>(block_exclusive_scan(tot, &total, sm.scan));
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < kRadixRounds; ++r) {
+        if (dig[r] < 0) continue;
+        const int dst = sm.dbase[dig[r]] + sm.wcount[wave][dig[r]] + rank[r];
+        sm.xk[dst] = key[r];
+        sm.xv[dst] = val[r];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < kRadixRounds; ++r) {
+        const int q = wave * kRadixRounds * kWave + r * kWave + lane;
+        if (q < N) {
+          key[r] = sm.xk[q];
+          val[r] = sm.xv[q];
+        }
+      }
+    }
+    // the sorted range, with each occurrence's bag
+#pragma unroll
+    for (int r = 0; r < kRadixRounds; ++r) {
+      const int q = wave * kRadixRounds * kWave + r * kWave + lane;
+      if (q < N) {
+        a.tkey[c0 + q] = key[r];
+        a.tval[c0 + q] = val[r];
+        a.tbag[c0 + q] = sm.lbag[val[r] - c0];
+      }
+    }
+  } else {
+    __syncthreads();  // the bags are in the workspace
+    // keys through the workspace
+    for (int q = threadIdx.x; q < N; q += kBwdThreads) {
+      const int ix = a.indices[c0 + q];
+      const bool valid = ix >= 0 && ix < rows;
+      a.k0[c0 + q] = valid ? ix : rows;
+      a.v0[c0 + q] = c0 + q;
+      nbad += valid ? 0 : 1;
+    }
+    __syncthreads();
+    const int32_t* sk = a.k0;
+    const int32_t* sv = a.v0;
+    if (passes == 0) {  // a single row: the order stays the positions'
+      for (int q = threadIdx.x; q < N; q += kBwdThreads) {
+        a.tkey[c0 + q] = sk[c0 + q];
+        a.tval[c0 + q] = sv[c0 + q];
+        a.tbag[c0 + q] = a.bag_of[sv[c0 + q]];
+      }
+    }
+    for (int ps = 0; ps < passes; ++ps) {
+      const int shift = 8 * ps;
+      const bool last = ps + 1 == passes;
+      int32_t* dk = last ? a.tkey : ((ps & 1) ? a.k0 : a.k1);
+      int32_t* dv = last ? a.tval : ((ps & 1) ? a.v0 : a.v1);
+      // digit totals over the whole range, then their exclusive scan
+      sm.hist[threadIdx.x] = 0;
+      __syncthreads();
+      for (int q = threadIdx.x; q < N; q += kBwdThreads) atomicAdd(&sm.hist[(sk[c0 + q] >> shift) & (kTableBins - 1)], 1);
+      __syncthreads();
+      long long total;
+      sm.dbase[threadIdx.x] = static_cast<int>(block_exclusive_scan(sm.hist[threadIdx.x], &total, sm.scan));
+      sm.cum[threadIdx.x] = 0;
+      // tiles in position order, each ranked like a one-tile range
+      for (int q0 = 0; q0 < N; q0 += kTableTile) {
+#pragma unroll
+        for (int w = 0; w < kRadixWaves; ++w) sm.wcount[w][threadIdx.x] = 0;
+        __syncthreads();
+        int key[kRadixRounds], val[kRadixRounds], dig[kRadixRounds], rank[kRadixRounds];
+#pragma unroll
+        for (int r = 0; r < kRadixRounds; ++r) {
+          const int q = q0 + wave * kRadixRounds * kWave + r * kWave + lane;
+          const bool ok = q < N;
+          key[r] = ok ? sk[c0 + q] : 0;
+          val[r] = ok ? sv[c0 + q] : 0;
+          const int d = (key[r] >> shift) & (kTableBins - 1);
+          dig[r] = ok ? d : -1;
+          rank[r] = rank_in_wave(d, ok, sm.wcount[wave], lt);
+        }
+        __syncthreads();
+        sm.hist[threadIdx.x] = wave_prefix(sm);  // this tile's digit totals
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kRadixRounds; ++r) {
+          if (dig[r] < 0) continue;
+          const int dst = c0 + sm.dbase[dig[r]] + sm.cum[dig[r]] + sm.wcount[wave][dig[r]] + rank[r];
+          dk[dst] = key[r];
+          dv[dst] = val[r];
+          if (last) a.tbag[dst] = a.bag_of[val[r]];
+        }
+        __syncthreads();
+        sm.cum[threadIdx.x] += sm.hist[threadIdx.x];
+      }
+      __syncthreads();  // this pass's output is the next one's input
+      sk = dk;
+      sv = dv;
+    }
+  }
+  // valid occurrences of the table
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) nbad += __shfl_xor(nbad, o, kWave);
+  if (lane == 0 && nbad) atomicAdd(&sm.misc[0], nbad);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    a.tvalid[t] = N - sm.misc[0];
+    if (sm.misc[0]) flag(a.status, DLRM_STATUS_BAD_INDEX);
+  }
+}
+
+// The final order (see table_sort): sorted keys, the permutation (if wanted) and
+// each sorted position's bag.
+__global__ __launch_bounds__(kBwdThreads) void table_place(const int32_t* __restrict__ tkey,
+                                                           const int32_t* __restrict__ tval,
+                                                           const int32_t* __restrict__ tbag,
+                                                           const int32_t* __restrict__ tvalid,
+                                                           const int32_t* __restrict__ tbound, MutTableArgs tabs,
+                                                           int T, long long nnz, int32_t sentinel,
+                                                           int32_t* __restrict__ skeys, int32_t* __restrict__ perm,
+                                                           int32_t* __restrict__ src_bag) {
+  __shared__ int red[2][kRadixWaves];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int c0 = tbound[t], c1 = tbound[t + 1], nvalid = tvalid[t];
+  // valid occurrences of the tables before t (before) and of all tables (all)
+  int before = 0, all = 0;
+  for (int s = threadIdx.x; s < T; s += kBwdThreads) {
+    const int v = tvalid[s];
+    all += v;
+    before += s < t ? v : 0;
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    before += __shfl_xor(before, o, kWave);
+    all += __shfl_xor(all, o, kWave);
+  }
+  if (lane == 0) {
+    red[0][wave] = before;
+    red[1][wave] = all;
+  }
+  __syncthreads();
+  before = 0;
+  all = 0;
+#pragma unroll
+  for (int w = 0; w < kRadixWaves; ++w) {
+    before += red[0][w];
+    all += red[1][w];
+  }
+  const int base = tabs.base[t];
+  // the invalid occurrences before this table's: the gap in front (c_0 positions)
+  // and those of the earlier tables (c_t - c_0 - before)
+  const int bad_first = all + c0 - before;
+  // kRadixRounds entries per thread in flight: all loads of a batch before its stores
+  for (int s0 = 0; s0 < c1 - c0; s0 += kRadixRounds * kBwdThreads) {
+    int k[kRadixRounds], v[kRadixRounds], g[kRadixRounds];
+#pragma unroll
+    for (int u = 0; u < kRadixRounds; ++u) {
+      const int s = s0 + u * kBwdThreads + threadIdx.x;
+      const int q = s < c1 - c0 ? c0 + s : c0;
+      k[u] = tkey[q];
+      v[u] = tval[q];
+      g[u] = tbag[q];
+    }
+#pragma unroll
+    for (int u = 0; u < kRadixRounds; ++u) {
+      const int s = s0 + u * kBwdThreads + threadIdx.x;
+      if (s < c1 - c0) {
+        const bool ok = s < nvalid;
+        const int out = ok ? before + s : bad_first + (s - nvalid);
+        skeys[out] = ok ? base + k[u] : sentinel;
+        if (perm) perm[out] = v[u];
+        src_bag[out] = g[u];
+      }
+    }
+  }
+  // positions outside every table's range (invalid offsets only): in front of c_0,
+  // and from c_T on (which stay where they are)
+  if (t == 0) {
+    for (int p = threadIdx.x; p < tbound[0]; p += kBwdThreads) {
+      skeys[all + p] = sentinel;
+      if (perm) perm[all + p] = p;
+      src_bag[all + p] = 0;
+    }
+  }
+  if (t == T - 1) {
+    for (long long p = tbound[T] + threadIdx.x; p < nnz; p += kBwdThreads) {
+      skeys[p] = sentinel;
+      if (perm) perm[p] = static_cast<int32_t>(p);
+      src_bag[p] = 0;
+    }
   }
 }
 
@@ -1202,7 +1617,13 @@ size_t bwd_workspace_bytes(int T, int B, int D, int64_t nnz, int64_t /*total_row
 }
 
 // How a backward call runs, decided on the host from the sizes alone.
-BwdPlanInfo bwd_plan(int T, int B, int D, int64_t nnz, int64_t total_rows, bool want_segments) {
+// The per-table sort takes batches of at most one tile of occurrences per table
+// on average (a longer table range still sorts, tile by tile through the
+// workspace) and batches whose bags per table its bag loop walks quickly.
+constexpr int kTableMaxBatch = 65536;
+
+
+BwdPlanInfo bwd_plan(int T, int B, int D, int64_t nnz, int64_t total_rows, int64_t max_rows, bool want_segments) {
   BwdPlanInfo p{};
   const RadixPlan rp = radix_plan(total_rows);
   p.radix_bits = rp.bits;
@@ -1211,6 +1632,20 @@ BwdPlanInfo bwd_plan(int T, int B, int D, int64_t nnz, int64_t total_rows, bool 
   p.fused_seg = nnz > 0 && want_segments && red_chunks <= kFusedSegChunks;
   p.seg_one_pass = nnz > 0 && want_segments && !p.fused_seg && scan_chunks(nnz) <= kScanThreads;
   const size_t ilds = ibwd_lds(T, D);
+  p.table_sort = nnz > 0 && nnz <= static_cast<int64_t>(T) * kTableTile && B <= kTableMaxBatch;
+  if (p.table_sort) {
+    // row indices in [0, rows_t], an out-of-range index taking rows_t
+    int bits = 0;
+    while ((1ll << bits) <= max_rows) ++bits;
+    p.radix_bits = 8;
+    p.passes = (bits + 7) / 8;
+    // the interaction backward's samples ride on table_sort, whose own
+    // workgroups use the same dynamic LDS segment
+    p.ibwd_shared = ilds <= kLdsPerWorkgroup;
+    p.ibwd_lds = ilds;
+    p.max_lds = std::max(sizeof(TableSortLds), ilds);
+    return p;
+  }
   // the interaction backward's samples ride on the scatter launches (and the
   // one-pass segment build) as extra workgroups when one sample's LDS fits
   // beside those kernels' own static LDS; otherwise it is a launch of its own
@@ -1241,7 +1676,9 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
 
   const long long n = a.nnz;
   const bool want_segments = a.unique_keys || a.seg_offsets || a.num_unique;
-  const BwdPlanInfo plan = bwd_plan(a.T, a.B, a.D, n, a.total_rows, want_segments);
+  int max_rows = 0;
+  for (int t = 0; t < a.T; ++t) max_rows = std::max(max_rows, static_cast<int>(a.tabs.rows[t]));
+  const BwdPlanInfo plan = bwd_plan(a.T, a.B, a.D, n, a.total_rows, max_rows, want_segments);
   const size_t ilds = plan.ibwd_lds;
   if (ilds > kLdsPerWorkgroup) return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
@@ -1264,13 +1701,13 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   // 1. otherwise the interaction backward's samples are shared out as extra
   // workgroups over the sort passes' scatter launches (the longest of the
   // sort; a share takes about as long as a scatter, and much longer than a
-  // count) and the one-pass segment build when that runs; nothing before the
-  // reduce reads its outputs
+  // count) and the one-pass segment build when that runs, or over the two
+  // launches of the per-table sort; nothing before the reduce reads its outputs
   const int passes = plan.passes;
   const bool fused_seg = plan.fused_seg;
   const long long nscan = scan_chunks(n);
   const bool seg_one_pass = plan.seg_one_pass;
-  const int nshare = plan.ibwd_shared ? passes + (seg_one_pass ? 1 : 0) : 0;
+  const int nshare = !plan.ibwd_shared || plan.table_sort ? 0 : passes + (seg_one_pass ? 1 : 0);
   int ishare = 0;
   const IbwdShare none{a.T, a.D, false, false, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
   auto share = [&]() {
@@ -1285,6 +1722,28 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
   // dynamic LDS only for a launch that carries interaction-backward workgroups
   auto share_lds = [&](const IbwdShare& ia) -> size_t { return ia.count > 0 ? ilds : 0; };
   const int32_t sentinel = static_cast<int32_t>(a.total_rows);
+  const int32_t* skeys = nullptr;
+  if (plan.table_sort) {  // 2-3. per table
+    int32_t* tvalid = counts;
+    int32_t* tbound = counts + a.T;
+    int32_t* ws_uniq = reinterpret_cast<int32_t*>(ws + L.uniq);
+    const TableSortArgs ts{a.T,    a.B,    a.offsets, a.indices, n,       keys[1], vals[1],  pos,      tvalid,
+                           tbound, keys[0], vals[0],  src_bag,   ws_uniq, bag_of,  a.status};
+    // every interaction-backward sample rides on table_sort: its table
+    // workgroups run about as long as the samples (splitting the samples with
+    // table_place measured 1-2 us slower per step on the 26-table batch)
+    const IbwdShare ia_sort =
+        plan.ibwd_shared ? IbwdShare{a.T, a.D, (a.layout & DLRM_PAIRS_SELF) != 0, (a.layout & DLRM_WITH_EMBEDDINGS) != 0,
+                                     a.e0, a.pooled, a.d_out, d_pooled, a.d_e0, 0, a.B}
+                         : none;
+    const size_t sort_lds = std::max(sizeof(TableSortLds), share_lds(ia_sort));
+    hipLaunchKernelGGL(table_sort, dim3(a.T + ia_sort.count), dim3(kBwdThreads), sort_lds, st, ts, a.tabs, ia_sort);
+    DLRM_CHECK_LAUNCH();
+    hipLaunchKernelGGL(table_place, dim3(a.T), dim3(kBwdThreads), 0, st, keys[1], vals[1], pos, tvalid, tbound, a.tabs,
+                       a.T, n, sentinel, keys[0], a.perm, src_bag);
+    DLRM_CHECK_LAUNCH();
+    skeys = keys[0];
+  } else {
   // 2. keys
   {
     const long long nb = static_cast<long long>(a.T) * a.B;
@@ -1338,8 +1797,9 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
 #undef DLRM_SORT_PASS
     cur ^= 1;
   }
-  const int32_t* skeys = keys[cur];
+  skeys = keys[cur];
   // plan.passes >= 1, so the last pass wrote a.perm (if given) and src_bag
+  }
   // 4. segments: outputs only (the reduce reads the sorted keys), so built only
   // when the caller asks for any of them
   if (want_segments && !fused_seg) {
@@ -1348,7 +1808,7 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((scan_chunk_totals<HeadIn>), dim3(static_cast<unsigned>(m)), dim3(kScanThreads), 0, st,
                          HeadIn{skeys, sentinel}, n, partial);
       DLRM_CHECK_LAUNCH();
-      const IbwdShare ia_seg = share();
+      const IbwdShare ia_seg = plan.table_sort ? none : share();
       hipLaunchKernelGGL(build_segments_chunked, dim3(static_cast<unsigned>(m) + ia_seg.count), dim3(kScanThreads),
                          share_lds(ia_seg), st, skeys, n, sentinel, partial, pos, uniq, seg, nuniq,
                          static_cast<int>(m), ia_seg);

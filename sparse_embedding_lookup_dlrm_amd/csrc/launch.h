@@ -87,14 +87,15 @@ hipError_t noalloc_scratch(void** ptr);
 // How the sparse backward runs for given sizes (host only).
 struct BwdPlanInfo {
   int radix_bits;    // digit width of the sort (8 or 9)
-  int passes;        // sort passes
+  int passes;        // sort passes (per-table sort: those of the table with the most rows)
+  bool table_sort;   // occurrences sorted per table (two launches) instead of by radix passes
   bool fused_seg;    // segment outputs written by the reduce's combine step
   bool seg_one_pass; // segment outputs from chunk totals + one scan-and-write launch
   bool ibwd_shared;  // interaction backward rides on the sort launches (else its own launch)
   size_t ibwd_lds;   // LDS of one interaction-backward sample
   size_t max_lds;    // largest LDS of any workgroup of the call
 };
-BwdPlanInfo bwd_plan(int T, int B, int D, int64_t nnz, int64_t total_rows, bool want_segments);
+BwdPlanInfo bwd_plan(int T, int B, int D, int64_t nnz, int64_t total_rows, int64_t max_rows, bool want_segments);
 hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t s);
 
 // shared by forward and backward: fused/standalone interaction tile sizes

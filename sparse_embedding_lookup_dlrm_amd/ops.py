@@ -358,10 +358,11 @@ def _check_bwd_buffers(T, B, D, offsets, indices, e0, pooled, d_out, d_e0, statu
 
 def bwd_plan(T: int, B: int, D: int, nnz: int, rows: Sequence[int], want_segments: bool = True) -> dict:
     """How the sparse backward will run for these sizes (dlrm_embbag_bwd_plan; host only)."""
-    plan = (_i32 * 4)()
+    plan = (_i32 * 5)()
     _check(lib().dlrm_embbag_bwd_plan(T, B, D, nnz, (_i64 * T)(*rows), 1 if want_segments else 0, plan),
            "dlrm_embbag_bwd_plan")
-    return {"radix_bits": plan[0], "passes": plan[1], "interact_bwd_shared": bool(plan[2]), "max_lds": plan[3]}
+    return {"radix_bits": plan[0], "passes": plan[1], "interact_bwd_shared": bool(plan[2]), "max_lds": plan[3],
+            "table_sort": bool(plan[4])}
 
 
 def embbag_bwd_update(tables: Sequence[torch.Tensor], offsets: torch.Tensor, indices: torch.Tensor, B: int,

@@ -129,29 +129,42 @@ def _ibwd_lds(T, D):
 
 
 def test_bwd_plan_interaction_backward_placement(lib):
-    """The interaction backward rides on the sort's launches only where one sample's LDS fits
-    beside the sort kernel's own within 160 KiB; otherwise it is a launch of its own."""
-    # 26 fp32 tables, D = 128, 22-bit keys: three 8-bit passes, shared
+    """Batches of at most 2048 occurrences per table on average sort per table (two
+    launches, the interaction backward riding on both); larger ones take the radix passes
+    over all keys, on whose launches the interaction backward rides only where one
+    sample's LDS fits beside the sort kernel's own within 160 KiB."""
+    # 26 fp32 tables, D = 128, one index per bag: per table, rows of 16 bits: two passes
     p = ops.bwd_plan(26, 2048, 128, 53248, [40_000] * 26)
-    assert (p["radix_bits"], p["passes"], p["interact_bwd_shared"]) == (8, 3, True)
+    assert (p["table_sort"], p["radix_bits"], p["passes"], p["interact_bwd_shared"]) == (True, 8, 2, True)
     assert p["max_lds"] <= 160 * 1024
-    # 68 tables, D = 512: one sample's tile (152 KiB) plus the scatter's static LDS exceeds 160 KiB
+    # one occurrence more: radix passes over the 22-bit keys, three 8-bit passes, shared
+    p = ops.bwd_plan(26, 2048, 128, 53249, [40_000] * 26)
+    assert (p["table_sort"], p["radix_bits"], p["passes"], p["interact_bwd_shared"]) == (False, 8, 3, True)
+    # per table, the passes follow the largest table (1000 and 70000 rows: 17 bits)
+    p = ops.bwd_plan(2, 100, 16, 300, [1000, 70_000])
+    assert (p["table_sort"], p["passes"]) == (True, 3)
+    # a batch past 65536 samples takes the radix passes
+    assert not ops.bwd_plan(2, 65537, 16, 300, [1000, 1000])["table_sort"]
+    # 68 tables, D = 512: one sample's tile (152 KiB) fits beside table_place's few bytes...
     assert _ibwd_lds(68, 512) <= 160 * 1024
     p = ops.bwd_plan(68, 16, 512, 1000, [2000] * 68)
-    assert p["interact_bwd_shared"] is False
+    assert p["table_sort"] and p["interact_bwd_shared"] is True
+    # ... but not beside the radix scatter's static LDS
+    p = ops.bwd_plan(68, 16, 512, 140_000, [2000] * 68)
+    assert not p["table_sort"] and p["interact_bwd_shared"] is False
     assert p["max_lds"] <= 160 * 1024
     # 65 tables, D = 512, 17-bit keys: two 9-bit passes (their scatter keeps 10 KiB of LDS): own launch
-    p = ops.bwd_plan(65, 24, 512, 800, [2000] * 65)
-    assert (p["radix_bits"], p["passes"], p["interact_bwd_shared"]) == (9, 2, False)
+    p = ops.bwd_plan(65, 24, 512, 140_000, [2000] * 65)
+    assert (p["table_sort"], p["radix_bits"], p["passes"], p["interact_bwd_shared"]) == (False, 9, 2, False)
     # the same with 24-bit keys (three 8-bit passes, a 5 KiB scatter): still too large together
-    p = ops.bwd_plan(65, 24, 512, 800, [200_000] * 65)
+    p = ops.bwd_plan(65, 24, 512, 140_000, [200_000] * 65)
     assert (p["radix_bits"], p["passes"]) == (8, 3)
     assert p["interact_bwd_shared"] is (_ibwd_lds(65, 512) + 5136 + 256 <= 160 * 1024)
     # no occurrences: no sort passes, the interaction backward runs alone
     p = ops.bwd_plan(4, 8, 16, 0, [10] * 4)
-    assert p["passes"] == 0 and p["interact_bwd_shared"] is False
+    assert p["passes"] == 0 and p["interact_bwd_shared"] is False and p["table_sort"] is False
     # one sample's tile alone beyond 160 KiB
-    plan = (ctypes.c_int32 * 4)()
+    plan = (ctypes.c_int32 * 5)()
     rows = (ctypes.c_int64 * 128)(*([10] * 128))
     assert lib.dlrm_embbag_bwd_plan(128, 4, 512, 8, rows, 1, plan) == E_UNSUPPORTED
     assert lib.dlrm_embbag_bwd_plan(0, 4, 512, 8, rows, 1, plan) == E_INVAL

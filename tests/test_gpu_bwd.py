@@ -25,8 +25,25 @@ def _round_storage(x64, dtype):
     return x32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def run_bwd(w: synth.Workload, lr=0.01, exact=False, twice=False, fused_fwd=True, layout=0):
+def set_lengths(b: synth.Batch, lengths) -> None:
+    """Give the batch other bag lengths (table-major), with fresh indices for them."""
+    b.lengths = np.asarray(lengths, dtype=np.int32)
+    b.indices = synth.gen_indices(b.w, b.rows, b.lengths)
+
+
+def sort_plan(w: synth.Workload, nnz: int) -> dict:
+    return ops.bwd_plan(w.T, w.B, w.D, nnz, synth.table_rows(w))
+
+
+def run_bwd(w: synth.Workload, lr=0.01, exact=False, twice=False, fused_fwd=True, layout=0, lengths=None,
+            table_sort=None):
+    """Backward + SGD against the oracle. lengths replaces the bag lengths; table_sort, if
+    given, is whether the call must sort per table (else by radix passes over all keys)."""
     b = synth.make_batch(w, with_dout=True)
+    if lengths is not None:
+        set_lengths(b, lengths)
+    if table_sort is not None:
+        assert sort_plan(w, len(b.indices))["table_sort"] is table_sort
     self_pairs = bool(layout & ops.PAIRS_SELF)
     with_emb = bool(layout & ops.WITH_EMBEDDINGS)
     if layout:
@@ -111,8 +128,9 @@ def run_bwd(w: synth.Workload, lr=0.01, exact=False, twice=False, fused_fwd=True
 
 
 def test_backward_zipf_26_tables_full():
-    """Backward + SGD (lr = 0.01) on the 26-table Zipf(1.05) workload, full size."""
-    run_bwd(synth.WORKLOADS["bwd-zipf-26t-d128-b2048"], lr=0.01, twice=True)
+    """Backward + SGD (lr = 0.01) on the 26-table Zipf(1.05) workload, full size (one
+    index per bag: 2048 occurrences per table, sorted per table)."""
+    run_bwd(synth.WORKLOADS["bwd-zipf-26t-d128-b2048"], lr=0.01, twice=True, table_sort=True)
 
 
 @pytest.mark.parametrize("name", ["tiny-4t1k-d16-b128", "bwd-zipf-26t-d128-b2048"])
@@ -141,16 +159,17 @@ def test_backward_interaction_layouts_exact(layout):
 def test_backward_interaction_layout_own_launch():
     """Self-pairs and the embeddings at T = 65, D = 512 bf16: the interaction backward in
     its own launch, in the layout."""
-    w = synth.Workload("ibwd-own-layout", T=65, rows=2000, D=512, dtype="bf16", B=24, bag=("uniform", 0, 4),
+    w = synth.Workload("ibwd-own-layout", T=65, rows=2000, D=512, dtype="bf16", B=24, bag=("uniform", 85, 95),
                        dist=("zipf", 1.1), seed=653)
     nnz = int(synth.make_batch(w).indices.size)
-    assert not ops.bwd_plan(w.T, w.B, w.D, nnz, [2000] * w.T)["interact_bwd_shared"]
+    p = ops.bwd_plan(w.T, w.B, w.D, nnz, [2000] * w.T)
+    assert not p["interact_bwd_shared"] and not p["table_sort"]
     run_bwd(w, lr=0.01, fused_fwd=False, layout=3)
 
 
 def test_backward_multihot_fp16():
     w = synth.WORKLOADS["multihot-8t4m-d64-fp16-b4096"].replace(B=512, rows=200_000)
-    run_bwd(w, lr=0.01)
+    run_bwd(w, lr=0.01, table_sort=False)
 
 
 def test_backward_capacity_shape_bf16():
@@ -170,7 +189,7 @@ def test_backward_many_keys_9bit_digits():
     need four)."""
     w = synth.Workload("bigkeys", T=3, rows=6_000_000, D=8, dtype="bf16", B=700, bag=("uniform", 0, 9),
                        dist=("zipf", 1.05), seed=77)
-    run_bwd(w, lr=0.01)
+    run_bwd(w, lr=0.01, table_sort=False)
 
 
 def test_backward_9bit_digits_row_scan():
@@ -178,13 +197,13 @@ def test_backward_9bit_digits_row_scan():
     so each digit's offsets come from the row-scan launch, over 512 digit rows."""
     w = synth.Workload("bigkeys-rs", T=3, rows=6_000_000, D=8, dtype="bf16", B=2100, bag=("uniform", 60, 70),
                        dist=("zipf", 1.05), seed=78)
-    run_bwd(w, lr=0.01)
+    run_bwd(w, lr=0.01, table_sort=False)
 
 
 @pytest.mark.parametrize("T,rows,B,bag", [
-    (1, 200, 300, ("uniform", 0, 12)),  # 8-bit keys: one 8-bit pass
-    (1, 400, 300, ("uniform", 0, 12)),  # 9 bits: one 9-bit pass
-    (3, 500, 300, ("uniform", 0, 12)),  # 11 bits: two 8-bit passes
+    (1, 200, 600, ("uniform", 0, 12)),  # 8-bit keys: one 8-bit pass
+    (1, 400, 600, ("uniform", 0, 12)),  # 9 bits: one 9-bit pass
+    (3, 500, 1200, ("uniform", 0, 12)),  # 11 bits: two 8-bit passes
     (2, 50_000, 900, ("uniform", 0, 12)),  # 17 bits: two 9-bit passes
     (3, 1_000_000, 2000, ("uniform", 10, 14)),  # 22 bits: three 8-bit passes, 36 tiles
     (2, 5_000_000, 500, ("uniform", 0, 12)),  # 24 bits: three 8-bit passes, the last digit full
@@ -195,7 +214,7 @@ def test_backward_sort_pass_counts(T, rows, B, bag):
     9-bit passes of 25-bit keys in the test above."""
     w = synth.Workload("passes", T=T, rows=rows, D=8, dtype="f32", B=B, bag=bag, dist=("zipf", 1.05),
                        seed=rows % 997 + B)
-    run_bwd(w, lr=0.01)
+    run_bwd(w, lr=0.01, table_sort=False)
 
 
 @pytest.mark.parametrize("B,bag", [(2100, ("uniform", 60, 70)), (8200, ("uniform", 62, 68))])
@@ -204,7 +223,7 @@ def test_backward_sort_and_segment_paths(B, bag):
     device-wide scan rather than inside each tile) and about 1.07M (more than 256 scan
     chunks of 4096: the segment scan also takes the device-wide path)."""
     w = synth.Workload("paths", T=2, rows=3000, D=8, dtype="f32", B=B, bag=bag, dist=("zipf", 1.05), seed=B)
-    run_bwd(w, lr=0.01)
+    run_bwd(w, lr=0.01, table_sort=False)
 
 
 @pytest.mark.parametrize("B,twice", [(2048, True), (2040, False), (2064, False)])
@@ -214,8 +233,38 @@ def test_backward_sort_tile_count_boundary(B, twice):
     (the offsets come from a per-digit scan launch). The run twice matches bit for bit."""
     w = synth.Workload("tiles", T=2, rows=3000, D=8, dtype="f32", B=B, bag=("fixed", 64),
                        dist=("zipf", 1.05), seed=B + 5)
-    res, r = run_bwd(w, lr=0.01, twice=twice)
+    res, r = run_bwd(w, lr=0.01, twice=twice, table_sort=False)
     assert len(r["perm"]) == 2 * 64 * B
+
+
+@pytest.mark.parametrize("name,T,rows,B,spec", [
+    # about 4096 occurrences in table 0 (two tiles, sorted through the workspace), 13-bit rows
+    ("long-table", 4, 5000, 512, [(4, 12), (0, 2), (0, 2), (0, 2)]),
+    # about 4800 occurrences in table 1 (three tiles) with 17-bit rows: three passes
+    ("long-table-3p", 3, 100_000, 600, [(0, 1), (6, 10), (0, 1)]),
+    # 2049 occurrences in table 0 (one more than a tile) and 2047 in table 1
+    ("tile-plus-one", 2, 3000, 2049, None),
+    # an empty table between two others
+    ("empty-table", 3, 700, 400, [(1, 5), (0, 0), (1, 5)]),
+    # 256 rows: the out-of-range key 256 needs a ninth bit, so two passes
+    ("pow2-rows", 3, 256, 300, [(0, 6)] * 3),
+    # a single row per table: keys 0 or 1, one pass
+    ("one-row", 2, 1, 100, [(0, 3)] * 2),
+])
+def test_backward_per_table_sort(name, T, rows, B, spec):
+    """Batches of at most 2048 occurrences per table on average sort per table: table
+    ranges longer than one tile, a tile plus one, an empty table, rows at a power of two
+    and a single row; perm, segments and U bit-exact, the update within tolerance, and a
+    second run bit-identical."""
+    w = synth.Workload(name, T=T, rows=rows, D=16, dtype="f32", B=B, bag=("uniform", 0, 1),
+                       dist=("zipf", 1.1), seed=len(name) * 31 + B)
+    rng = np.random.default_rng(w.seed)
+    if spec is None:
+        lengths = np.ones(T * B, np.int32)
+        lengths[B + rng.choice(B, 2, replace=False)] = 0
+    else:
+        lengths = np.concatenate([rng.integers(lo, hi + 1, B) for lo, hi in spec]).astype(np.int32)
+    run_bwd(w, lr=0.01, twice=True, lengths=lengths, table_sort=True)
 
 
 @pytest.mark.parametrize("B", [8192, 8193])
@@ -237,12 +286,15 @@ def test_backward_segment_outputs_one_pass_scan():
     run_bwd(w, lr=0.01, twice=True)
 
 
-def test_backward_positions_outside_every_bag_are_skipped():
+@pytest.mark.parametrize("B,table_sort", [(50, True), (2000, False)])
+def test_backward_positions_outside_every_bag_are_skipped(B, table_sort):
     """Offsets that start at 3 and end 5 short of nnz (invalid, flagged): the positions
-    before the first offset and from the last one on belong to no bag and add nothing."""
-    w = synth.Workload("gaps", T=3, rows=200, D=32, dtype="f32", B=50, bag=("uniform", 0, 8),
+    before the first offset and from the last one on belong to no bag and add nothing
+    (sorted per table, and by radix passes over all keys)."""
+    w = synth.Workload("gaps", T=3, rows=200, D=32, dtype="f32", B=B, bag=("uniform", 0, 8),
                        dist=("zipf", 1.1), seed=91)
     b = synth.make_batch(w, with_dout=True)
+    assert sort_plan(w, len(b.indices) + 8)["table_sort"] is table_sort
     db = DeviceBatch(b)
     pooled, _ = db.fwd(want_pooled=True)
     d_out = torch.from_numpy(b.dout).cuda()
@@ -269,7 +321,7 @@ def test_backward_positions_outside_every_bag_are_skipped():
     assert nnz + 8 == len(idx)
 
 
-@pytest.mark.parametrize("T,rows,B", [(3, 200, 50), (26, 40_000, 300)])
+@pytest.mark.parametrize("T,rows,B", [(3, 200, 50), (26, 40_000, 300), (2, 3000, 1500)])
 def test_backward_overlapping_bags_stay_in_bounds(T, rows, B):
     """Offsets that decrease (invalid, flagged) make later bags cover positions that an
     earlier bag already covers. The call still finishes in bounds: the status carries
@@ -465,24 +517,35 @@ def test_backward_interaction_backward_own_launch():
     """65 bf16 tables with D = 512 and 17-bit keys (two 9-bit sort passes): one sample's
     interaction-backward LDS does not fit beside the 9-bit scatter's own within 160 KiB, so
     the interaction backward runs as a launch of its own instead of riding on the sort's."""
-    w = synth.Workload("ibwd-own-65t-d512-bf16", T=65, rows=2000, D=512, dtype="bf16", B=24, bag=("uniform", 0, 4),
-                       dist=("zipf", 1.1), seed=655)
+    w = synth.Workload("ibwd-own-65t-d512-bf16", T=65, rows=2000, D=512, dtype="bf16", B=24,
+                       bag=("uniform", 85, 95), dist=("zipf", 1.1), seed=655)
     nnz = int(synth.make_batch(w).indices.size)
     p = ops.bwd_plan(w.T, w.B, w.D, nnz, [2000] * w.T)
-    assert (p["radix_bits"], p["passes"], p["interact_bwd_shared"]) == (9, 2, False)
+    assert (p["radix_bits"], p["passes"], p["interact_bwd_shared"], p["table_sort"]) == (9, 2, False, False)
     run_bwd(w, lr=0.01, twice=True, fused_fwd=False)
 
 
-@pytest.mark.parametrize("dtype,T,D", [("f32", 5, 32), ("bf16", 26, 128)])
-def test_backward_out_of_range_indices_dropped(dtype, T, D):
+@pytest.mark.parametrize("dtype,T,D,B,long0,table_sort", [
+    ("f32", 5, 32, 64, False, True),
+    ("bf16", 26, 128, 64, False, True),
+    ("f32", 5, 32, 300, True, True),  # table 0 holds about 3000 occurrences: sorted tile by tile
+    ("f32", 2, 32, 1500, False, False),  # radix passes over all keys
+])
+def test_backward_out_of_range_indices_dropped(dtype, T, D, B, long0, table_sort):
     """One out-of-range index per table (one of them negative): the status carries the
     bad-index bit, and perm, the distinct rows, the segment bounds and U equal the oracle's
     on the batch without those occurrences (positions mapped back; the dropped ones sort
     last, in CSR order, and seg_offsets[U] counts the valid occurrences only); d_e0 and the
     updated rows match within tolerance; rows nothing references stay bit-identical."""
-    w = synth.Workload("badidx", T=T, rows=300, D=D, dtype=dtype, B=64, bag=("uniform", 1, 6),
+    w = synth.Workload("badidx", T=T, rows=300, D=D, dtype=dtype, B=B, bag=("uniform", 1, 6),
                        dist=("zipf", 1.1), seed=T * 7 + D)
     b = synth.make_batch(w, with_dout=True)
+    if long0:
+        lengths = b.lengths.copy()
+        lengths[:B] = np.random.default_rng(w.seed).integers(8, 13, B)
+        set_lengths(b, lengths)
+        assert b.lengths[:B].sum() > 2048
+    assert sort_plan(w, len(b.indices))["table_sort"] is table_sort
     off = orc.lengths_to_offsets(b.lengths)
     idx = b.indices.copy()
     rng = np.random.default_rng(w.seed)
