@@ -140,8 +140,8 @@ def summarize_profile(d: str, out: str, command: str, timed: int = 0) -> None:
 def summarize_backward(d: str, out: str, command: str, warmup: int, steps: int) -> None:
     """Per-kernel durations of one backward step, averaged over the timed steps, for the
     three backward timings of a default run (26-table SGD, 26-table row-wise AdaGrad,
-    multi-hot SGD; each step starts with the key build, whose launch also carries a share
-    of the interaction backward)."""
+    multi-hot SGD; each step starts with its first sort launch, the per-table sort or the
+    key build)."""
     import csv
 
     rows = []
@@ -149,7 +149,7 @@ def summarize_backward(d: str, out: str, command: str, warmup: int, steps: int) 
         with open(p) as f:
             rows += list(csv.DictReader(f))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    starts = [i for i, r in enumerate(rows) if "build_keys" in r["Kernel_Name"]]
+    starts = [i for i, r in enumerate(rows) if "build_keys" in r["Kernel_Name"] or "table_sort" in r["Kernel_Name"]]
     steps_bwd = max(steps, 20)
     # each timing: its warm-up steps, the timed steps (one event pair), then as many
     # steps again with an event pair each (for the median and min)

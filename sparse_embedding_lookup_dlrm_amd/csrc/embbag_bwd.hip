@@ -507,16 +507,23 @@ constexpr int kTableBins = 1 << 8;
 
 // table_sort's LDS, carved from the dynamic segment (which the interaction
 // backward's extra workgroups of the same launch use for their own tile)
+// About the size of one interaction-backward sample's LDS at D = 128 (the
+// launch's dynamic LDS is the larger of the two).
 struct TableSortLds {
-  int wcount[kRadixWaves][kTableBins];  // per-wave digit counts, then their prefix over the waves
-  int dbase[kTableBins];                // first slot of each digit
-  int hist[kTableBins];                 // digit totals (tiles through the workspace)
-  int cum[kTableBins];                  // keys of each digit in the tiles done so far
-  long long scan[kRadixWaves];          // block scan across the waves
-  int misc[4];                          // [0] invalid occurrences, [1..2] table bounds
-  int xk[kTableTile];                   // one tile's keys and values between passes
-  int xv[kTableTile];
-  int lbag[kTableTile];                 // each position's bag (one-tile ranges)
+  unsigned short wcount[kRadixWaves][kTableBins];  // per-wave digit counts, then their prefix over the waves
+  int dbase[kTableBins];                           // first slot of each digit
+  long long scan[kRadixWaves];                     // block scan across the waves
+  int misc[4];                                     // [0] invalid occurrences
+  union {
+    struct {
+      int xk[kTableTile];  // one-tile ranges: the keys and values between passes
+      int xv[kTableTile];
+    } x;
+    struct {
+      int hist[kTableBins];  // longer ranges: digit totals
+      int cum[kTableBins];   // keys of each digit in the tiles done so far
+    } m;
+  };
 };
 
 struct TableSortArgs {
@@ -544,39 +551,42 @@ struct TableSortArgs {
 __device__ __forceinline__ void table_bounds(const int32_t* __restrict__ offsets, int B, long long nnz, int t,
                                              int& c0, int& c1) {
   const int lane = threadIdx.x & (kWave - 1);
-  long long m0 = 0, m1 = 0;
+  const int n = static_cast<int>(nnz);  // nnz < 2^31
+  int m0 = 0, m1 = 0;
   for (int s = lane; s <= t + 1; s += kWave) {
-    long long o = offsets[static_cast<long long>(s) * B];
-    o = o < 0 ? 0 : (o > nnz ? nnz : o);
+    int o = offsets[static_cast<long long>(s) * B];
+    o = o < 0 ? 0 : (o > n ? n : o);
     if (s <= t) m0 = o > m0 ? o : m0;
     m1 = o > m1 ? o : m1;
   }
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) {
-    const long long y0 = __shfl_xor(m0, o, kWave), y1 = __shfl_xor(m1, o, kWave);
+    const int y0 = __shfl_xor(m0, o, kWave), y1 = __shfl_xor(m1, o, kWave);
     m0 = y0 > m0 ? y0 : m0;
     m1 = y1 > m1 ? y1 : m1;
   }
-  c0 = static_cast<int>(m0);
-  c1 = static_cast<int>(m1);
+  c0 = m0;
+  c1 = m1;
 }
 
 // Stable ranking of one round of 64 keys of a wave by their digit d (ok false:
 // no key): the number of equal digits at lower lanes, plus the wave's running
 // count of that digit, which the round then advances.
-__device__ __forceinline__ int rank_in_wave(int d, bool ok, int* wcnt, unsigned long long lt) {
+__device__ __forceinline__ int rank_in_wave(int d, bool ok, unsigned short* wcnt) {
   unsigned long long peers = __ballot(ok);
 #pragma unroll
   for (int bit = 0; bit < 8; ++bit) {
     const unsigned long long m = __ballot((d >> bit) & 1);
     peers &= ((d >> bit) & 1) ? m : ~m;
   }
-  const int before = __popcll(peers & lt);
+  // set bits of peers at lower lanes
+  const int before = static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(peers >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(peers), 0u)));
   const int cnt = __popcll(peers);
   int running = 0;
   if (ok) running = wcnt[d];
   __builtin_amdgcn_wave_barrier();
-  if (ok && before == 0) wcnt[d] = running + cnt;
+  if (ok && before == 0) wcnt[d] = static_cast<unsigned short>(running + cnt);
   __builtin_amdgcn_wave_barrier();
   return running + before;
 }
@@ -589,7 +599,7 @@ __device__ __forceinline__ int wave_prefix(TableSortLds& sm) {
 #pragma unroll
   for (int w = 0; w < kRadixWaves; ++w) {
     const int c = sm.wcount[w][d];
-    sm.wcount[w][d] = tot;
+    sm.wcount[w][d] = static_cast<unsigned short>(tot);
     tot += c;
   }
   return tot;
@@ -601,18 +611,17 @@ __global__ __launch_bounds__(kBwdThreads) void table_sort(TableSortArgs a, MutTa
   TableSortLds& sm = *reinterpret_cast<TableSortLds*>(smem);
   const int t = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const unsigned long long lt = (1ull << lane) - 1ull;
   const int rows = tabs.rows[t];
   const long long bag0 = static_cast<long long>(t) * a.B;
   const long long nbags = static_cast<long long>(a.T) * a.B;
   // Bag j = (t, b) holds [o_j, max(o_j, o_j+1)) once clamped into [0, nnz] (the
-  // CSR checks as in build_keys) and is recorded as b * T + t, its row of the
-  // pooled gradients. A position of the range that no bag of this table holds
-  // (invalid offsets only) keeps the table's first bag, t.
+  // CSR checks as in build_keys) and is recorded in bag_of, by position, as
+  // b * T + t, its row of the pooled gradients. A position of the range that no
+  // bag of this table holds (invalid offsets only) keeps the table's first bag, t.
   // The offsets of a thread's first kRadixRounds bags are loaded with the
   // table bounds, the indices right after: two memory round trips in all.
   constexpr int kBagBatch = kRadixRounds * kBwdThreads;
-  long long o0[kRadixRounds], o1[kRadixRounds];
+  int o0[kRadixRounds], o1[kRadixRounds];
 #pragma unroll
   for (int u = 0; u < kRadixRounds; ++u) {
     const int j = threadIdx.x + u * kBwdThreads;
@@ -620,7 +629,6 @@ __global__ __launch_bounds__(kBwdThreads) void table_sort(TableSortArgs a, MutTa
     o0[u] = a.offsets[g];
     o1[u] = a.offsets[g + 1];
   }
-  for (int q = threadIdx.x; q < kTableTile; q += kBwdThreads) sm.lbag[q] = t;
   if (threadIdx.x == 0) sm.misc[0] = 0;
   int c0, c1;
   table_bounds(a.offsets, a.B, a.nnz, t, c0, c1);
@@ -637,26 +645,23 @@ __global__ __launch_bounds__(kBwdThreads) void table_sort(TableSortArgs a, MutTa
       const int q = wave * kRadixRounds * kWave + r * kWave + lane;
       idx[r] = a.indices[q < N ? c0 + q : 0];
     }
-  } else {
-    for (int q = threadIdx.x; q < N; q += kBwdThreads) a.bag_of[c0 + q] = t;
   }
+  for (int q = threadIdx.x; q < N; q += kBwdThreads) a.bag_of[c0 + q] = t;
   __syncthreads();  // the default bags are written
   bool bad_off = false;
-  auto put_bag = [&](int j, long long s0, long long s1) {
+  const int n = static_cast<int>(a.nnz);  // nnz < 2^31
+  auto put_bag = [&](int j, int s0, int s1) {  // s0, s1: o_j, o_j+1
     const long long g = bag0 + j;
     if (g == 0 && s0 != 0) bad_off = true;
-    if (g == nbags - 1 && s1 != a.nnz) bad_off = true;
+    if (g == nbags - 1 && s1 != n) bad_off = true;
     if (s0 < 0) { s0 = 0; bad_off = true; }
-    if (s0 > a.nnz) { s0 = a.nnz; bad_off = true; }
+    if (s0 > n) { s0 = n; bad_off = true; }
     if (s1 < 0) { s1 = 0; bad_off = true; }
-    if (s1 > a.nnz) { s1 = a.nnz; bad_off = true; }
+    if (s1 > n) { s1 = n; bad_off = true; }
     if (s1 < s0) { s1 = s0; bad_off = true; }
-    const long long p0 = s0 > c0 ? s0 : c0, p1 = s1 < c1 ? s1 : c1;
+    const int p0 = s0 > c0 ? s0 : c0, p1 = s1 < c1 ? s1 : c1;
     const int row = j * a.T + t;
-    for (long long p = p0; p < p1; ++p) {
-      if (one_tile) sm.lbag[p - c0] = row;
-      else a.bag_of[p] = row;
-    }
+    for (int p = p0; p < p1; ++p) a.bag_of[p] = row;
   };
 #pragma unroll
   for (int u = 0; u < kRadixRounds; ++u) {
@@ -670,31 +675,28 @@ __global__ __launch_bounds__(kBwdThreads) void table_sort(TableSortArgs a, MutTa
   int nbad = 0;
   if (one_tile) {
     // keys in registers
-    int key[kRadixRounds], val[kRadixRounds], rank[kRadixRounds];
+    int key[kRadixRounds], val[kRadixRounds];
 #pragma unroll
     for (int r = 0; r < kRadixRounds; ++r) {
       const int q = wave * kRadixRounds * kWave + r * kWave + lane;
       const bool ok = q < N;
       const bool valid = idx[r] >= 0 && idx[r] < rows;
       key[r] = valid ? idx[r] : rows;
-      val[r] = c0 + q;
+      val[r] = q;  // the occurrence's slot (its position less c0)
       nbad += (ok && !valid) ? 1 : 0;
     }
-    __syncthreads();  // the bags are in LDS
-    // the passes: rank in each wave, prefix over the waves and digits, exchange
+    // the passes: rank in each wave, prefix over the waves and digits, exchange;
+    // a slot and its rank (both below 2^16) share a register until the exchange
     for (int ps = 0; ps < passes; ++ps) {
       const int shift = 8 * ps;
 #pragma unroll
       for (int w = 0; w < kRadixWaves; ++w) sm.wcount[w][threadIdx.x] = 0;
       __syncthreads();
-      int dig[kRadixRounds];
 #pragma unroll
       for (int r = 0; r < kRadixRounds; ++r) {
         const int q = wave * kRadixRounds * kWave + r * kWave + lane;
-        const bool ok = q < N;
         const int d = (key[r] >> shift) & (kTableBins - 1);
-        dig[r] = ok ? d : -1;
-        rank[r] = rank_in_wave(d, ok, sm.wcount[wave], lt);
+        val[r] = (val[r] << 16) | rank_in_wave(d, q < N, sm.wcount[wave]);
       }
       __syncthreads();
       long long total;
@@ -703,29 +705,33 @@ __global__ __launch_bounds__(kBwdThreads) void table_sort(TableSortArgs a, MutTa
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < kRadixRounds; ++r) {
-        if (dig[r] < 0) continue;
-        const int dst = sm.dbase[dig[r]] + sm.wcount[wave][dig[r]] + rank[r];
-        sm.xk[dst] = key[r];
-        sm.xv[dst] = val[r];
+        const int q = wave * kRadixRounds * kWave + r * kWave + lane;
+        if (q >= N) continue;
+        const int d = (key[r] >> shift) & (kTableBins - 1);
+        const int dst = sm.dbase[d] + sm.wcount[wave][d] + (val[r] & 0xffff);
+        sm.x.xk[dst] = key[r];
+        sm.x.xv[dst] = val[r] >> 16;
       }
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < kRadixRounds; ++r) {
         const int q = wave * kRadixRounds * kWave + r * kWave + lane;
         if (q < N) {
-          key[r] = sm.xk[q];
-          val[r] = sm.xv[q];
+          key[r] = sm.x.xk[q];
+          val[r] = sm.x.xv[q];
         }
       }
     }
-    // the sorted range, with each occurrence's bag
+    // the sorted range, with each occurrence's bag (the bags were stored before
+    // at least one barrier: every pass, and the one below with no pass, has one)
+    if (passes == 0) __syncthreads();
 #pragma unroll
     for (int r = 0; r < kRadixRounds; ++r) {
       const int q = wave * kRadixRounds * kWave + r * kWave + lane;
       if (q < N) {
         a.tkey[c0 + q] = key[r];
-        a.tval[c0 + q] = val[r];
-        a.tbag[c0 + q] = sm.lbag[val[r] - c0];
+        a.tval[c0 + q] = c0 + val[r];
+        a.tbag[c0 + q] = a.bag_of[c0 + val[r]];
       }
     }
   } else {
@@ -754,42 +760,41 @@ __global__ __launch_bounds__(kBwdThreads) void table_sort(TableSortArgs a, MutTa
       int32_t* dk = last ? a.tkey : ((ps & 1) ? a.k0 : a.k1);
       int32_t* dv = last ? a.tval : ((ps & 1) ? a.v0 : a.v1);
       // digit totals over the whole range, then their exclusive scan
-      sm.hist[threadIdx.x] = 0;
+      sm.m.hist[threadIdx.x] = 0;
       __syncthreads();
-      for (int q = threadIdx.x; q < N; q += kBwdThreads) atomicAdd(&sm.hist[(sk[c0 + q] >> shift) & (kTableBins - 1)], 1);
+      for (int q = threadIdx.x; q < N; q += kBwdThreads) atomicAdd(&sm.m.hist[(sk[c0 + q] >> shift) & (kTableBins - 1)], 1);
       __syncthreads();
       long long total;
-      sm.dbase[threadIdx.x] = static_cast<int>(block_exclusive_scan(sm.hist[threadIdx.x], &total, sm.scan));
-      sm.cum[threadIdx.x] = 0;
+      sm.dbase[threadIdx.x] = static_cast<int>(block_exclusive_scan(sm.m.hist[threadIdx.x], &total, sm.scan));
+      sm.m.cum[threadIdx.x] = 0;
       // tiles in position order, each ranked like a one-tile range
       for (int q0 = 0; q0 < N; q0 += kTableTile) {
 #pragma unroll
         for (int w = 0; w < kRadixWaves; ++w) sm.wcount[w][threadIdx.x] = 0;
         __syncthreads();
-        int key[kRadixRounds], val[kRadixRounds], dig[kRadixRounds], rank[kRadixRounds];
+        int key[kRadixRounds], val[kRadixRounds], rank[kRadixRounds];
 #pragma unroll
         for (int r = 0; r < kRadixRounds; ++r) {
           const int q = q0 + wave * kRadixRounds * kWave + r * kWave + lane;
           const bool ok = q < N;
           key[r] = ok ? sk[c0 + q] : 0;
           val[r] = ok ? sv[c0 + q] : 0;
-          const int d = (key[r] >> shift) & (kTableBins - 1);
-          dig[r] = ok ? d : -1;
-          rank[r] = rank_in_wave(d, ok, sm.wcount[wave], lt);
+          rank[r] = rank_in_wave((key[r] >> shift) & (kTableBins - 1), ok, sm.wcount[wave]);
         }
         __syncthreads();
-        sm.hist[threadIdx.x] = wave_prefix(sm);  // this tile's digit totals
+        sm.m.hist[threadIdx.x] = wave_prefix(sm);  // this tile's digit totals
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < kRadixRounds; ++r) {
-          if (dig[r] < 0) continue;
-          const int dst = c0 + sm.dbase[dig[r]] + sm.cum[dig[r]] + sm.wcount[wave][dig[r]] + rank[r];
+          if (q0 + wave * kRadixRounds * kWave + r * kWave + lane >= N) continue;
+          const int d = (key[r] >> shift) & (kTableBins - 1);
+          const int dst = c0 + sm.dbase[d] + sm.m.cum[d] + sm.wcount[wave][d] + rank[r];
           dk[dst] = key[r];
           dv[dst] = val[r];
           if (last) a.tbag[dst] = a.bag_of[val[r]];
         }
         __syncthreads();
-        sm.cum[threadIdx.x] += sm.hist[threadIdx.x];
+        sm.m.cum[threadIdx.x] += sm.m.hist[threadIdx.x];
       }
       __syncthreads();  // this pass's output is the next one's input
       sk = dk;
