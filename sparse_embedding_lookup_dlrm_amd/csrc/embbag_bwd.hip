@@ -1226,18 +1226,21 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
 
   // all gradient rows and the table rows of the segments completed here are
   // loaded up front (slots without a completed segment re-read its first row)
+  // A slot's table row is named by its lane's (tk, rk), read into scalars where
+  // the row is loaded and again where it is stored, rather than kept in 32
+  // scalar registers per slot in between (which spilled).
+  auto ref_of = [&](int j) {
+    return RowRef{__builtin_amdgcn_readlane(tk, j),
+                  static_cast<size_t>(__builtin_amdgcn_readlane(rk, j)) * static_cast<size_t>(D)};
+  };
   RowVec<EL> rows[C];
   TabVec<DT, EL> trow[C];
-  RowRef refs[C];
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int r = __shfl(src, j, kWave);
     rows[j].load(d_pooled + static_cast<size_t>(r) * D + col);
     const int jj = ((complete_mask >> j) & 1ull) ? j : 0;
-    refs[j].t = __builtin_amdgcn_readfirstlane(__shfl(tk, jj, kWave));
-    const int rj = __builtin_amdgcn_readfirstlane(__shfl(rk, jj, kWave));
-    refs[j].off = static_cast<size_t>(rj) * D;
-    trow[j].load(tabs, refs[j], col);
+    trow[j].load(tabs, ref_of(jj), col);
   }
   RowVec<EL> acc;
 #pragma unroll
@@ -1250,13 +1253,14 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
       for (int e = 0; e < EL; ++e) acc.v[e] += rows[j].v[e];
       if ((close_mask >> j) & 1ull) {
         if ((complete_mask >> j) & 1ull) {
+          const RowRef ref = ref_of(j);
           if constexpr (OPT == kRowwiseAdagrad) {
             // a complete segment closes at j, so lane j holds its row and that row's state
             const int rj = __builtin_amdgcn_readlane(rk, j);
             const float s_old = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane), j));
-            trow[j].sgd_store(tabs, refs[j], col, acc, adagrad_step<EL>(acc, s_old, sstate[refs[j].t] + rj, D, lr, eps));
+            trow[j].sgd_store(tabs, ref, col, acc, adagrad_step<EL>(acc, s_old, sstate[ref.t] + rj, D, lr, eps));
           } else {
-            trow[j].sgd_store(tabs, refs[j], col, acc, lr);
+            trow[j].sgd_store(tabs, ref, col, acc, lr);
           }
         } else if ((carry_mask >> j) & 1ull) {
           // the chunk's first segment, begun in an earlier chunk, ends or runs through here
