@@ -1130,12 +1130,15 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
                                                                  const int32_t* __restrict__ src_bag,
                                                                  const float* __restrict__ d_pooled, float lr,
                                                                  float* __restrict__ carry, float* __restrict__ head,
+                                                                 float* __restrict__ wgcarry,
                                                                  int32_t* __restrict__ chunk_flags, long long nchunks,
                                                                  int32_t* __restrict__ hcount, int32_t* __restrict__ hwg) {
   static_assert(C <= kWave, "one lane per chunk position");
+  constexpr int kWaves = kBwdThreads / kWave;
   __shared__ int sbase[DLRM_MAX_TABLES];  // first global key of each table
   __shared__ float* sstate[OPT == kRowwiseAdagrad ? DLRM_MAX_TABLES : 1];  // each table's row states
-  __shared__ int wg_heads, wg_done;  // the workgroup's heads so far, and its waves done
+  __shared__ int wg_heads, wg_done, wg_pure;  // the workgroup's heads so far, its waves done, its pure chunks
+  __shared__ float wcarry[kWaves][kWave * EL];  // the carries of pure chunks
   for (int t = threadIdx.x; t < T; t += kBwdThreads) {
     sbase[t] = tabs.base[t];
     if constexpr (OPT == kRowwiseAdagrad) sstate[t] = state.ptr[t];
@@ -1143,25 +1146,42 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
   if (threadIdx.x == 0) {
     wg_heads = 0;
     wg_done = 0;
+    wg_pure = 0;
   }
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int lpr = D < kWave ? D : kWave;
+  const int col = (lane % lpr) * EL;
   // Every wave ends here with its chunk's number of segment starts (heads):
   // it adds them to the workgroup's sum, then counts itself done; the last of
   // the four stores the sum for the combine step's prefix sums (no barrier, so
-  // waves may leave early).
+  // waves may leave early). When all four chunks are pure (wholly inside one
+  // segment that began before them and goes on after them), the last wave also
+  // stores the sum of their four carries, in wave order, as the workgroup's
+  // carry: the combine step then adds a long segment's carries four chunks at
+  // a time.
   auto finish = [&](int heads) {
-    if (hwg && lane == 0) {
-      atomicAdd(&wg_heads, heads);
+    int last = 0;
+    if (lane == 0) {
+      if (hwg) atomicAdd(&wg_heads, heads);
       __threadfence_block();
-      if (atomicAdd(&wg_done, 1) == kBwdThreads / kWave - 1) {
-        __threadfence_block();
-        hwg[blockIdx.x] = atomicAdd(&wg_heads, 0);
+      last = atomicAdd(&wg_done, 1) == kWaves - 1;
+    }
+    if (__builtin_amdgcn_readfirstlane(last)) {
+      __threadfence_block();
+      if (hwg && lane == 0) hwg[blockIdx.x] = atomicAdd(&wg_heads, 0);
+      if (atomicAdd(&wg_pure, 0) == kWaves) {
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          float v = wcarry[0][col + e];
+#pragma unroll
+          for (int w = 1; w < kWaves; ++w) v += wcarry[w][col + e];
+          wgcarry[static_cast<size_t>(blockIdx.x) * D + col + e] = v;
+        }
       }
     }
   };
-  const int lpr = D < kWave ? D : kWave;
-  const int col = (lane % lpr) * EL;
   const long long k = static_cast<long long>(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6);
   if (k >= nchunks) {
     finish(0);
@@ -1223,6 +1243,7 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
   int flags = first_cont ? kChunkFirstCont : 0;
   if (!next_starts) flags |= kChunkLastCont;
   if (__popcll(start_mask) + (first_cont ? 1 : 0) == 1) flags |= kChunkSingle;
+  const bool pure = flags == (kChunkFirstCont | kChunkLastCont | kChunkSingle);
 
   // all gradient rows and the table rows of the segments completed here are
   // loaded up front (slots without a completed segment re-read its first row)
@@ -1265,6 +1286,10 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
         } else if ((carry_mask >> j) & 1ull) {
           // the chunk's first segment, begun in an earlier chunk, ends or runs through here
           acc.store(carry + static_cast<size_t>(k) * D + col);
+          if (pure) {
+#pragma unroll
+            for (int e = 0; e < EL; ++e) wcarry[wave][col + e] = acc.v[e];
+          }
         } else {
           // a segment begun here that goes on into the next chunk
           acc.store(head + static_cast<size_t>(k) * D + col);
@@ -1277,6 +1302,10 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
   if (lane == 0) {
     chunk_flags[k] = flags;
     if (hcount) hcount[k] = __popcll(start_mask);  // the chunk's segment starts (heads)
+    if (pure) {
+      __threadfence_block();  // the wave's carry is in LDS
+      atomicAdd(&wg_pure, 1);
+    }
   }
   finish(__popcll(start_mask));
 }
@@ -1389,6 +1418,7 @@ __global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, St
                                                            const int32_t* __restrict__ skeys,
                                                            const float* __restrict__ carry,
                                                            const float* __restrict__ head,
+                                                           const float* __restrict__ wgcarry,
                                                            const int32_t* __restrict__ chunk_flags, long long nchunks,
                                                            float lr, SegOut so) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -1415,24 +1445,61 @@ __global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, St
   // at the chunk's last position) is that segment's
   // Chunk j's first part is this segment's; the segment goes on past chunk j
   // only if chunk j holds nothing else and its last segment continues. The
-  // last chunk it reaches is found 64 flags at a time (one per lane), so a
-  // segment spanning hundreds of chunks costs a few dependent loads, not one
-  // per chunk.
+  // last chunk it reaches is found 64 flags at a time (one per lane), then,
+  // past those, 256 at a time (four per lane, loaded together), so a segment
+  // spanning hundreds of chunks costs a few dependent loads, not one per chunk.
   long long last = nchunks - 1;
-  for (long long j = k + 1; j < nchunks; j += kWave) {
-    const long long jj = j + lane;
+  bool found = false;
+  {
+    const long long jj = k + 1 + lane;
     const int fj = jj < nchunks ? chunk_flags[jj] : 0;
     const unsigned long long ends = __ballot(!((fj & kChunkSingle) && (fj & kChunkLastCont)));
     if (ends) {
-      const long long e = j + __ffsll(static_cast<long long>(ends)) - 1;
+      const long long e = k + __ffsll(static_cast<long long>(ends));
       last = e < last ? e : last;
-      break;
+      found = true;
     }
   }
+  constexpr int kFlagLoads = 4;
+  for (long long j = k + 1 + kWave; !found && j < nchunks; j += kFlagLoads * kWave) {
+    int fj[kFlagLoads];
+#pragma unroll
+    for (int u = 0; u < kFlagLoads; ++u) {
+      const long long jj = j + u * kWave + lane;
+      fj[u] = jj < nchunks ? chunk_flags[jj] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kFlagLoads; ++u) {
+      const unsigned long long ends = __ballot(!((fj[u] & kChunkSingle) && (fj[u] & kChunkLastCont)));
+      if (!found && ends) {
+        const long long e = j + u * kWave + __ffsll(static_cast<long long>(ends)) - 1;
+        last = e < last ? e : last;
+        found = true;
+      }
+    }
+  }
+  // The carries to add: chunks k+1..last. Every chunk strictly between k and
+  // last lies wholly inside the segment, so each reduce workgroup whose four
+  // chunks all do (w with k < 4w and 4w + 3 < last) left their sum in
+  // wgcarry[w]; the others' carries are added one by one. Item i of the
+  // sequence [chunks k+1 .. 4wa) [workgroups wa .. wb) [chunks 4wb .. last]
+  // (or just chunks k+1 .. last) is at item_row(i).
+  constexpr int kWaves = kBwdThreads / kWave;  // chunks per reduce workgroup
+  const long long a0 = k + 1;
+  long long wa = (a0 + kWaves - 1) / kWaves, wb = last / kWaves;
+  if (wb <= wa) wa = wb = 0;
+  const long long nh = wb > wa ? kWaves * wa - a0 : 0;
+  const long long nw = wb - wa;
+  const long long t0 = wb > wa ? kWaves * wb : a0;
+  const long long nitems = nh + nw + (last - t0 + 1);
+  auto item_row = [&](long long i) -> const float* {
+    if (i < nh) return carry + static_cast<size_t>(a0 + i) * D;
+    if (i < nh + nw) return wgcarry + static_cast<size_t>(wa + i - nh) * D;
+    return carry + static_cast<size_t>(t0 + i - nh - nw) * D;
+  };
   if constexpr (EL <= 4) {
-    // D <= 256: the carries of chunks k+1..last summed R = 256 / D at a time,
-    // 4 columns per lane (slot q of a load holds chunk k+1+q, k+1+q+R, ...),
-    // with 8 loads in flight; then the R slot sums are added in a fixed
+    // D <= 256: the items summed R = 256 / D at a time, 4 columns per lane
+    // (slot q of a load holds items q, q+R, ...), with 8 loads in flight; then the R slot sums are added in a fixed
     // butterfly order and each lane takes its own columns. A Zipf-hot row
     // whose carries span hundreds of chunks thus costs R times fewer round
     // trips than one carry per load (multi-hot backward 152.8 -> 148.0 us;
@@ -1443,16 +1510,16 @@ __global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, St
     const int c4 = (lane - q * lr) * 4;
     constexpr int G = 8;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (long long j = k + 1; j <= last; j += static_cast<long long>(R) * G) {
+    for (long long j = 0; j < nitems; j += static_cast<long long>(R) * G) {
       float4 x[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const long long jj = j + static_cast<long long>(g) * R + q;
-        x[g] = *reinterpret_cast<const float4*>(carry + static_cast<size_t>(jj <= last ? jj : last) * D + c4);
+        x[g] = *reinterpret_cast<const float4*>(item_row(jj < nitems ? jj : nitems - 1) + c4);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        if (j + static_cast<long long>(g) * R + q <= last) {
+        if (j + static_cast<long long>(g) * R + q < nitems) {
           s.x += x[g].x;
           s.y += x[g].y;
           s.z += x[g].z;
@@ -1476,18 +1543,18 @@ __global__ __launch_bounds__(kBwdThreads) void seg_combine(MutTableArgs tabs, St
       acc.v[e] += comp == 0 ? vx : comp == 1 ? vy : comp == 2 ? vz : vw;
     }
   } else {
-    // the carries of chunks k+1..last, added in chunk order; 4 loads in flight
+    // the items added in order; 4 loads in flight
     constexpr int G = 4;
-    for (long long j = k + 1; j <= last; j += G) {
+    for (long long j = 0; j < nitems; j += G) {
       RowVec<EL> x[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const long long jj = j + g <= last ? j + g : last;
-        x[g].load(carry + static_cast<size_t>(jj) * D + col);
+        const long long jj = j + g < nitems ? j + g : nitems - 1;
+        x[g].load(item_row(jj) + col);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        if (j + g <= last) {
+        if (j + g < nitems) {
 #pragma unroll
           for (int e = 0; e < EL; ++e) acc.v[e] += x[g].v[e];
         }
@@ -1508,7 +1575,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct WsLayout {
   size_t d_pooled, keys_a, keys_b, vals_a, vals_b, bag_of, src_bag, counts, digit_off, row_total, partial, pos, uniq, seg,
       nuniq;
-  size_t carry, head, chunk_flags, hcount, hwg, total;
+  size_t carry, head, wgcarry, chunk_flags, hcount, hwg, total;
 };
 
 // Gradient columns per lane for a row of D fp32 values, and the chunk of sorted
@@ -1556,6 +1623,7 @@ WsLayout layout(int T, int B, int D, int64_t nnz) {
   const size_t nchunks = (n + C - 1) / C;
   L.carry = o; o = align_up(o + nchunks * D * 4);
   L.head = o; o = align_up(o + nchunks * D * 4);
+  L.wgcarry = o; o = align_up(o + (nchunks + 3) / 4 * D * 4);
   L.chunk_flags = o; o = align_up(o + nchunks * 4);
   L.hcount = o; o = align_up(o + nchunks * 4);
   L.hwg = o; o = align_up(o + (nchunks + 3) / 4 * 4);
@@ -1570,19 +1638,23 @@ hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, cons
   const long long nchunks = (a.nnz + C - 1) / C;
   float* carry = reinterpret_cast<float*>(ws + L.carry);
   float* head = reinterpret_cast<float*>(ws + L.head);
+  float* wgcarry = reinterpret_cast<float*>(ws + L.wgcarry);
   int32_t* flags = reinterpret_cast<int32_t*>(ws + L.chunk_flags);
   constexpr int kWavesPerBlock = kBwdThreads / kWave;
   const dim3 g(static_cast<unsigned>((nchunks + kWavesPerBlock - 1) / kWavesPerBlock)), blk(kBwdThreads);
   if (a.opt == kRowwiseAdagrad) {
     hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D,
-                       skeys, a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, so.hcount, so.hwg);
+                       skeys, a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, wgcarry, flags, nchunks, so.hcount,
+                       so.hwg);
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((seg_combine<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
-                       carry, head, flags, nchunks, a.lr, so);
+                       carry, head, wgcarry, flags, nchunks, a.lr, so);
   } else {
     hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
-                       a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, flags, nchunks, so.hcount, so.hwg);
+                       a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, wgcarry, flags, nchunks, so.hcount, so.hwg);
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((seg_combine<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys, carry, head,
-                       flags, nchunks, a.lr, so);
+                       wgcarry, flags, nchunks, a.lr, so);
   }
   return hipGetLastError();
 }
