@@ -378,6 +378,17 @@ def test_backward_single_row_whole_batch(B):
     run_bwd(w, lr=0.01, twice=True)
 
 
+@pytest.mark.parametrize("D,B,dtype", [(16, 5000, "f32"), (256, 1000, "bf16"), (512, 3000, "bf16")])
+def test_backward_single_row_long_segment_widths(D, B, dtype):
+    """One row takes every occurrence at 1, 4 and 8 gradient columns per lane (16 of 64 lanes
+    holding a row at D = 16): its partial sums span hundreds of chunks, most of them summed
+    per reduce workgroup before the combine step adds them; sorted per table (B = 1000) and
+    by radix passes (B = 3000, 5000)."""
+    w = synth.Workload("onerow-w", T=1, rows=1, D=D, dtype=dtype, B=B, bag=("fixed", 1),
+                       dist=("uniform",), seed=B + D)
+    run_bwd(w, lr=0.01, twice=True, table_sort=(B <= 2048))
+
+
 def test_backward_wide_rows_bf16():
     """D = 512 bf16 (eight fp32 gradient columns per lane)."""
     w = synth.Workload("wide", T=2, rows=50, D=512, dtype="bf16", B=40, bag=("uniform", 0, 20),
@@ -453,6 +464,14 @@ def run_bwd_adagrad(w: synth.Workload, lr=0.05, eps=1e-6, steps=2, layout=0):
 
 def test_backward_rowwise_adagrad_zipf_26_tables():
     run_bwd_adagrad(synth.WORKLOADS["bwd-zipf-26t-d128-b2048"], lr=0.01)
+
+
+def test_backward_rowwise_adagrad_single_row_long_segment():
+    """Row-wise AdaGrad where one row takes all 4000 occurrences (D = 64): the state step of a
+    segment summed through hundreds of chunks and their workgroup sums."""
+    w = synth.Workload("onerow-ada", T=1, rows=1, D=64, dtype="f32", B=4000, bag=("fixed", 1),
+                       dist=("uniform",), seed=4064)
+    run_bwd_adagrad(w, lr=0.01)
 
 
 def test_backward_rowwise_adagrad_hot_rows_fp16():
