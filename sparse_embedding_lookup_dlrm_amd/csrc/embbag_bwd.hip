@@ -1153,6 +1153,11 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
   const int wave = threadIdx.x >> 6;
   const int lpr = D < kWave ? D : kWave;
   const int col = (lane % lpr) * EL;
+  // Each XCD takes a contiguous run of chunks (the workgroups it is dealt are
+  // renumbered): the sorted occurrences of a run belong to one or a few
+  // tables, so the pooled-gradient rows its chunks gather (one bag row is read
+  // once per occurrence in the bag) come from a slice that fits its L2.
+  const int wg = xcd_block(blockIdx.x, gridDim.x);
   // Every wave ends here with its chunk's number of segment starts (heads):
   // it adds them to the workgroup's sum, then counts itself done; the last of
   // the four stores the sum for the combine step's prefix sums (no barrier, so
@@ -1170,19 +1175,19 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
     }
     if (__builtin_amdgcn_readfirstlane(last)) {
       __threadfence_block();
-      if (hwg && lane == 0) hwg[blockIdx.x] = atomicAdd(&wg_heads, 0);
+      if (hwg && lane == 0) hwg[wg] = atomicAdd(&wg_heads, 0);
       if (atomicAdd(&wg_pure, 0) == kWaves) {
 #pragma unroll
         for (int e = 0; e < EL; ++e) {
           float v = wcarry[0][col + e];
 #pragma unroll
           for (int w = 1; w < kWaves; ++w) v += wcarry[w][col + e];
-          wgcarry[static_cast<size_t>(blockIdx.x) * D + col + e] = v;
+          wgcarry[static_cast<size_t>(wg) * D + col + e] = v;
         }
       }
     }
   };
-  const long long k = static_cast<long long>(blockIdx.x) * (kBwdThreads / kWave) + (threadIdx.x >> 6);
+  const long long k = static_cast<long long>(wg) * (kBwdThreads / kWave) + (threadIdx.x >> 6);
   if (k >= nchunks) {
     finish(0);
     return;
