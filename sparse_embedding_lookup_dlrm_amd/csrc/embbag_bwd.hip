@@ -499,16 +499,16 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
 //    slots: its valid occurrences after those of the earlier tables, its invalid
 //    ones after every valid occurrence, the gap positions and the invalid ones of
 //    earlier tables.
-// table_sort also carries the interaction-backward samples as extra workgroups. The
-// table ranges are the offsets at the table boundaries, clamped into [0, nnz] and
-// made non-decreasing (a running maximum), which changes nothing for a valid CSR.
+// table_sort also carries the interaction-backward samples as extra workgroups.
+// The table ranges are the offsets at the table boundaries, clamped into
+// [0, nnz] and made non-decreasing (a running maximum), which changes nothing
+// for a valid CSR.
 constexpr int kTableTile = kRadixTile;  // occurrences a table sorts in registers: 8 per thread
 constexpr int kTableBins = 1 << 8;
 
-// table_sort's LDS, carved from the dynamic segment (which the interaction
-// backward's extra workgroups of the same launch use for their own tile)
-// About the size of one interaction-backward sample's LDS at D = 128 (the
-// launch's dynamic LDS is the larger of the two).
+// table_sort's LDS (19 KiB), carved from the dynamic segment, which the
+// interaction backward's extra workgroups of the same launch use for their own
+// tile; the launch's dynamic LDS is the larger of the two.
 struct TableSortLds {
   unsigned short wcount[kRadixWaves][kTableBins];  // per-wave digit counts, then their prefix over the waves
   int dbase[kTableBins];                           // first slot of each digit
