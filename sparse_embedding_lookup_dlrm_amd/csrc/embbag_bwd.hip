@@ -498,7 +498,10 @@ __global__ __launch_bounds__(kBwdThreads) void radix_scatter(const int32_t* __re
 //  - table_place: one workgroup per table moves its sorted range to the final
 //    slots: its valid occurrences after those of the earlier tables, its invalid
 //    ones after every valid occurrence, the gap positions and the invalid ones of
-//    earlier tables.
+//    earlier tables. When every occurrence is valid, no position lies outside
+//    the ranges and every range was sorted in registers, the final order is
+//    each range in place, which table_sort has already written: table_place
+//    then only checks that and returns.
 // table_sort also carries the interaction-backward samples as extra workgroups.
 // The table ranges are the offsets at the table boundaries, clamped into
 // [0, nnz] and made non-decreasing (a running maximum), which changes nothing
@@ -543,6 +546,13 @@ struct TableSortArgs {
   int32_t* k1;
   int32_t* v1;
   int32_t* bag_of;  // as tbag, by position
+  // a range of at most one tile also goes straight to the final arrays at its
+  // own positions: the final order whenever every occurrence is valid and
+  // every position lies in a range (table_place then leaves them as they are)
+  int32_t* skeys;   // out [nnz]: global key, or the sentinel
+  int32_t* src_bag; // out [nnz]: as tbag
+  int32_t* perm;    // out [nnz] or null: the position
+  int32_t sentinel;
   int32_t* status;
 };
 
@@ -729,9 +739,13 @@ __global__ __launch_bounds__(kBwdThreads) void table_sort(TableSortArgs a, MutTa
     for (int r = 0; r < kRadixRounds; ++r) {
       const int q = wave * kRadixRounds * kWave + r * kWave + lane;
       if (q < N) {
+        const int bag = a.bag_of[c0 + val[r]];
         a.tkey[c0 + q] = key[r];
         a.tval[c0 + q] = c0 + val[r];
-        a.tbag[c0 + q] = a.bag_of[c0 + val[r]];
+        a.tbag[c0 + q] = bag;
+        a.skeys[c0 + q] = key[r] < rows ? tabs.base[t] + key[r] : a.sentinel;
+        a.src_bag[c0 + q] = bag;
+        if (a.perm) a.perm[c0 + q] = c0 + val[r];
       }
     }
   } else {
@@ -850,6 +864,18 @@ __global__ __launch_bounds__(kBwdThreads) void table_place(const int32_t* __rest
     before += red[0][w];
     all += red[1][w];
   }
+  // every position valid and in a range (all = nnz), and every range sorted in
+  // registers: table_sort has already written the final order
+  bool longer = false;
+  for (int s = threadIdx.x; s < T; s += kBwdThreads) longer |= tbound[s + 1] - tbound[s] > kTableTile;
+  __syncthreads();  // red is read by every thread above before it is reused
+  const unsigned long long any_longer = __ballot(longer);  // every lane votes (not in lane 0's branch)
+  if (lane == 0) red[0][wave] = any_longer != 0ull;
+  __syncthreads();
+  longer = false;
+#pragma unroll
+  for (int w = 0; w < kRadixWaves; ++w) longer |= red[0][w] != 0;
+  if (all == nnz && !longer) return;
   const int base = tabs.base[t];
   // the invalid occurrences before this table's: the gap in front (c_0 positions)
   // and those of the earlier tables (c_t - c_0 - before)
@@ -1813,8 +1839,9 @@ hipError_t launch_embbag_bwd_update(const BwdArgs& a, hipStream_t st) {
     int32_t* tvalid = counts;
     int32_t* tbound = counts + a.T;
     int32_t* ws_uniq = reinterpret_cast<int32_t*>(ws + L.uniq);
-    const TableSortArgs ts{a.T,    a.B,    a.offsets, a.indices, n,       keys[1], vals[1],  pos,      tvalid,
-                           tbound, keys[0], vals[0],  src_bag,   ws_uniq, bag_of,  a.status};
+    const TableSortArgs ts{a.T,    a.B,     a.offsets, a.indices, n,      keys[1], vals[1], pos,      tvalid,
+                           tbound, keys[0], vals[0],   src_bag,   ws_uniq, bag_of, keys[0], src_bag, a.perm,
+                           sentinel, a.status};
     // every interaction-backward sample rides on table_sort: its table
     // workgroups run about as long as the samples (splitting the samples with
     // table_place measured 1-2 us slower per step on the 26-table batch)

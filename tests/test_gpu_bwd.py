@@ -242,6 +242,8 @@ def test_backward_sort_tile_count_boundary(B, twice):
     ("long-table", 4, 5000, 512, [(4, 12), (0, 2), (0, 2), (0, 2)]),
     # about 4800 occurrences in table 1 (three tiles) with 17-bit rows: three passes
     ("long-table-3p", 3, 100_000, 600, [(0, 1), (6, 10), (0, 1)]),
+    # the last of five tables holds about 4000 occurrences (two tiles); the others one tile each
+    ("long-last", 5, 5000, 400, [(0, 2)] * 4 + [(8, 12)]),
     # 2049 occurrences in table 0 (one more than a tile) and 2047 in table 1
     ("tile-plus-one", 2, 3000, 2049, None),
     # an empty table between two others
@@ -253,9 +255,10 @@ def test_backward_sort_tile_count_boundary(B, twice):
 ])
 def test_backward_per_table_sort(name, T, rows, B, spec):
     """Batches of at most 2048 occurrences per table on average sort per table: table
-    ranges longer than one tile, a tile plus one, an empty table, rows at a power of two
-    and a single row; perm, segments and U bit-exact, the update within tolerance, and a
-    second run bit-identical."""
+    ranges longer than one tile (first, middle or last table; the final order then comes
+    from the placement launch, not from the ranges written in place), a tile plus one, an
+    empty table, rows at a power of two and a single row; perm, segments and U bit-exact,
+    the update within tolerance, and a second run bit-identical."""
     w = synth.Workload(name, T=T, rows=rows, D=16, dtype="f32", B=B, bag=("uniform", 0, 1),
                        dist=("zipf", 1.1), seed=len(name) * 31 + B)
     rng = np.random.default_rng(w.seed)
