@@ -1154,7 +1154,7 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
                                                                  const int32_t* __restrict__ skeys, long long n,
                                                                  int32_t sentinel,
                                                                  const int32_t* __restrict__ src_bag,
-                                                                 const float* __restrict__ d_pooled, float lr,
+                                                                 const float* __restrict__ d_pooled, int nbags, float lr,
                                                                  float* __restrict__ carry, float* __restrict__ head,
                                                                  float* __restrict__ wgcarry,
                                                                  int32_t* __restrict__ chunk_flags, long long nchunks,
@@ -1242,7 +1242,10 @@ __global__ __launch_bounds__(kBwdThreads) void seg_reduce_chunks(MutTableArgs ta
   }
   const bool mine = lane < nq;
   const int key = mine ? key_raw : __shfl(key_raw, 0, kWave);
-  const int src = mine ? src_raw : __shfl(src_raw, 0, kWave);
+  // a bag row outside [0, B*T) would be an error of an earlier step; it is
+  // clamped so that the gradient reads stay inside d_pooled whatever happens
+  int src = mine ? src_raw : __shfl(src_raw, 0, kWave);
+  src = src < 0 ? 0 : (src >= nbags ? nbags - 1 : src);
   // the position after the chunk's last valid one starts a new segment, or is
   // the end of the valid keys
   const int last_next = __shfl(key_next, nq - 1, kWave);
@@ -1675,14 +1678,15 @@ hipError_t launch_seg_reduce(const BwdArgs& a, const WsLayout& L, char* ws, cons
   const dim3 g(static_cast<unsigned>((nchunks + kWavesPerBlock - 1) / kWavesPerBlock)), blk(kBwdThreads);
   if (a.opt == kRowwiseAdagrad) {
     hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D,
-                       skeys, a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, wgcarry, flags, nchunks, so.hcount,
-                       so.hwg);
+                       skeys, a.nnz, sentinel, src_bag, d_pooled, a.T * a.B, a.lr, carry, head, wgcarry, flags, nchunks,
+                       so.hcount, so.hwg);
     if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((seg_combine<DT, EL, C, kRowwiseAdagrad>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
                        carry, head, wgcarry, flags, nchunks, a.lr, so);
   } else {
     hipLaunchKernelGGL((seg_reduce_chunks<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys,
-                       a.nnz, sentinel, src_bag, d_pooled, a.lr, carry, head, wgcarry, flags, nchunks, so.hcount, so.hwg);
+                       a.nnz, sentinel, src_bag, d_pooled, a.T * a.B, a.lr, carry, head, wgcarry, flags, nchunks, so.hcount,
+                       so.hwg);
     if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     hipLaunchKernelGGL((seg_combine<DT, EL, C, kSgd>), g, blk, 0, st, a.tabs, a.state, a.eps, a.T, a.D, skeys, carry, head,
                        wgcarry, flags, nchunks, a.lr, so);
