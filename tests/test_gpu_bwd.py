@@ -392,6 +392,28 @@ def test_backward_single_row_long_segment_widths(D, B, dtype):
     run_bwd(w, lr=0.01, twice=True, table_sort=(B <= 2048))
 
 
+def _random_case(i):
+    """Seeded shapes across both sorts, the four gradient widths and the three storage
+    types (bags uniform in [0, hi], rows per table a few hundred to a few hundred thousand)."""
+    rng = np.random.default_rng(9000 + i)
+    T = int(rng.integers(1, 40))
+    D = int(rng.choice([16, 32, 64, 128, 256, 512]))
+    dtype = str(rng.choice(["f32", "f16", "bf16"]))
+    B = int(rng.integers(1, 700))
+    hi = int(rng.choice([1, 3, 8, 40]))
+    rows = int(rng.choice([100, 3000, 70_000, 300_000]))
+    rows = min(rows, 20_000_000 // (T * D))  # at most 20M table elements
+    return synth.Workload(f"rand{i}", T=T, rows=rows, D=D, dtype=dtype, B=B, bag=("uniform", 0, hi),
+                          dist=("zipf", float(rng.choice([1.05, 1.2]))), seed=9000 + i)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_backward_random_shapes(i):
+    """Backward + SGD on seeded random shapes against the oracle (perm, segments and U
+    bit-exact, the update within tolerance, a second run bit-identical)."""
+    run_bwd(_random_case(i), lr=0.01, twice=True)
+
+
 def test_backward_wide_rows_bf16():
     """D = 512 bf16 (eight fp32 gradient columns per lane)."""
     w = synth.Workload("wide", T=2, rows=50, D=512, dtype="bf16", B=40, bag=("uniform", 0, 20),
