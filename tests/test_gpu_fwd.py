@@ -187,6 +187,40 @@ def test_status_bits_and_no_out_of_bounds_reads():
     assert db.status.item() & ops.STATUS_BAD_OFFSETS
 
 
+def _random_fwd_case(i):
+    """Seeded shapes across the forward's launch shapes: 1-70 tables, D from 16 to 512, the
+    three storage types, bags of 0-1 up to 0-60 indices (short samples in groups, long
+    ones one per workgroup), batches of 1 to 3000 samples."""
+    rng = np.random.default_rng(7000 + i)
+    T = int(rng.integers(1, 71))
+    D = int(rng.choice([16, 32, 64, 128, 256, 512]))
+    dtype = str(rng.choice(["f32", "f16", "bf16"]))
+    B = int(rng.integers(1, 3000))
+    hi = int(rng.choice([1, 4, 20, 60]))
+    B = max(1, min(B, 400_000 // (T * (hi + 1) // 2 + 1)))  # at most about 400K lookups
+    rows = min(int(rng.choice([100, 5000, 200_000])), 20_000_000 // (T * D))
+    return synth.Workload(f"rfwd{i}", T=T, rows=rows, D=D, dtype=dtype, B=B, bag=("uniform", 0, hi),
+                          dist=("zipf", 1.1), seed=7000 + i)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shapes_fused_forward(i):
+    """The fused forward ([e0 | dots] and the pooled vectors) on seeded random shapes,
+    against the oracle within R14. A shape whose interaction tile exceeds one workgroup's
+    LDS (many tables of wide rows) is rejected before any launch (-2); its pooled vectors
+    are then checked alone."""
+    b = synth.make_batch(_random_fwd_case(i))
+    db = DeviceBatch(b)
+    try:
+        pooled, inter = db.fwd(want_pooled=True)
+    except ops.DlrmError as e:
+        assert e.code == -2 and b.w.T * b.w.D >= 16384, (e.code, b.w.T, b.w.D)
+        pooled, inter = db.fwd(want_pooled=True, want_inter=False)
+    torch.cuda.synchronize()
+    assert db.status.item() == 0
+    check_fwd(db, pooled, inter)
+
+
 def test_run_twice_bit_identical():
     b = synth.make_batch(_capacity_like(B=64))
     db = DeviceBatch(b)
