@@ -1035,7 +1035,7 @@ __device__ __forceinline__ void touch(uint4 x) { asm volatile("" ::"v"(x.x), "v"
 // there; window k+1's loads are issued before window k is summed. Slots past
 // the range issue a load that reads nothing and returns zeros, so every window
 // issues the same number of loads (and the compiler's wait counts stay exact).
-template <int DT, int LB, bool BEYOND, int CAP>
+template <int DT, int LB, bool BEYOND, int CAP, int WIN>
 __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, const int* pos, const int* stage,
                                              const uint8_t* sbag, const char* const* tbase, const int* trows, int T,
                                              int p0, int p1, float* Z, int LD, float* carry_w, int* carry_t_w,
@@ -1044,7 +1044,6 @@ __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, c
   using C = LaneChunk<LB>;
   using RS = RowShape<DT, LB>;
   constexpr int EL = RS::EL;
-  constexpr int WIN = RS::WIN;
   constexpr int RB = LB * kWave;  // row bytes
   // the bag holding p0 (a search of fixed length: a wave late in the sample
   // would otherwise walk past dozens of bags before its first load)
@@ -1226,12 +1225,17 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
       if (p0 < p1) {
         float* cw = carry + wave * D;
         int* ctw = carry_t + wave;
+        // fp16 rows of 512 bytes in sample groups keep 4 rows per window: 6 made
+        // the compiler spill (52-56 bytes per lane), and 4 measured 35.1 against
+        // 40.0 us on 26 tables of D = 256 with one index per bag (one sample per
+        // workgroup keeps 6: 86.9 against 88.2 us with 20 rows per bag)
+        constexpr int WIN = (DT == DLRM_F16 && LB == 8 && G > 1) ? 4 : RowShape<DT, LB>::WIN;
         if (p1 <= CAP)
-          gather_range<DT, LB, false, CAP>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid,
-                                           qsb);
+          gather_range<DT, LB, false, CAP, WIN>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw,
+                                                tid, qsb);
         else
-          gather_range<DT, LB, true, CAP>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw, tid,
-                                          qsb);
+          gather_range<DT, LB, true, CAP, WIN>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw,
+                                               tid, qsb);
       }
     }
     // the prefetched values are first used here (the barrier keeps every use,
