@@ -1085,6 +1085,166 @@ __device__ __forceinline__ void gather_range(const FwdArgs& a, const int* beg, c
   }
 }
 
+// One sample's gather by one wave for 128-byte rows of 16-bit values (D = 64),
+// four rows per load instruction: an instruction takes four consecutive rows
+// of one bag, one per quarter of the wave (16 lanes, 8 bytes = four columns
+// each). The table is then the same for the whole instruction, so the load
+// goes through one buffer resource over the table with a row offset per lane;
+// a slot past the bag's end or holding an index outside the table reads past
+// the buffer (zeros, no memory request). Quarter k sums rows 4m + k of the bag
+// in order; at the bag's end each column's four partial sums are added as
+// (q0 + q1) + (q2 + q3) and written to the bag's Z row. Lane (k, i) of a
+// window of WIN instructions works out instruction q + i's bag and the row
+// quarter k loads in it, so an instruction takes its table base with lane
+// reads and each quarter's row offset with a row broadcast (no LDS access
+// between two loads). Needs T <= 64, the sample staged in LDS and tables of
+// fewer than 2^24 rows (under 2^31 bytes). Multi-hot batch (8 fp16 tables of
+// 4M rows, 20 rows per bag): 22.0 us against 27.2 us with one row per load.
+struct QuadWindow {
+  int t;                       // lane i: instruction q + i's bag
+  uint32_t roff;               // lane (k, i): byte offset of the row quarter k loads in instruction q + i
+  uint32_t blo, bhi;           // lane i: the bag's table base
+  unsigned long long fmask;    // bit i: instruction q + i ends its bag
+};
+
+constexpr int kQuadWin = 7;  // load instructions (28 rows) per window: 6, 7 and 8 measured 22.2, 22.0 and
+                             // 21.9 us on the multi-hot batch, and 8 spills 8 bytes per lane
+// Bytes every buffer resource of the gather covers: more than any table it
+// takes (under 2^24 rows of 128 bytes) and less than the offset of a slot that
+// reads nothing, so that slot is out of range and every other is a row of the
+// table.
+constexpr int kQuadRange = 0x7FFFFFFF;
+
+// Lane (k, i) works out instruction q + i (the same for all four quarters) and
+// the row of it that quarter k loads.
+template <int WIN>
+__device__ __forceinline__ void quad_prepare(QuadWindow& w, const int* pos, const int* stage,
+                                             const char* const* tbase, int incl, int T, int I, int q, int lane) {
+  const int k = lane >> 4, i = lane & 15;
+  const int x = q + i;
+  const bool valid = i < WIN && x < I;
+  // x's bag: the number of bags whose instructions all come before x
+  int t = 0;
+#pragma unroll
+  for (int step = 32; step > 0; step >>= 1) {
+    const int c = t + step;
+    const int e = __shfl(incl, c - 1 < kWave ? c - 1 : kWave - 1, kWave);
+    if (c <= T && e <= x) t = c;
+  }
+  const int ex_raw = __shfl(incl, t > 0 ? t - 1 : 0, kWave);
+  bool flush = false;
+  uint32_t roff = 0xFFFFFF00u;  // past kQuadRange: the load returns zeros
+  if (valid) {
+    const int ex = t > 0 ? ex_raw : 0;
+    const int end = pos[t + 1];
+    const int p = pos[t] + 4 * (x - ex);
+    const int c = min(4, end - p);
+    flush = k == 0 && p + c == end;
+    if (k < c) {
+      const int r = stage[p + k];
+      if (r >= 0) roff = static_cast<uint32_t>(r) * 128u;
+    }
+  } else {
+    t = 0;
+  }
+  const uint64_t base = reinterpret_cast<uint64_t>(tbase[t]);
+  w.t = t;
+  w.roff = roff;
+  w.blo = static_cast<uint32_t>(base);
+  w.bhi = static_cast<uint32_t>(base >> 32);
+  w.fmask = __ballot(flush);
+}
+
+// Lane I of each 16-lane row of the wave, to the whole row (DPP row_newbcast).
+template <int I>
+__device__ __forceinline__ uint32_t quarter_bcast(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x150 + I, 0xF, 0xF, false));
+}
+
+// Instructions I.. of a window: instruction I's table base from lane I, each
+// quarter's row offset from lane I of the quarter.
+template <int I, int WIN>
+__device__ __forceinline__ void quad_issue(const QuadWindow& w, uint2 (&v)[WIN], uint32_t sub8) {
+  if constexpr (I < WIN) {
+    const uint64_t base = bcast64(w.blo, w.bhi, I);
+    const uint32_t off = quarter_bcast<I>(w.roff) + sub8;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, kQuadRange, 0x00020000);
+    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kNonTemporal);
+    v[I] = make_uint2(x.x, x.y);
+    quad_issue<I + 1, WIN>(w, v, sub8);
+  }
+}
+
+template <int DT, int WIN>
+__device__ __forceinline__ void quad_consume(const QuadWindow& w, uint2 (&v)[WIN], float4& acc, float* Z, int LD,
+                                             int lane) {
+#pragma unroll
+  for (int i = 0; i < WIN; ++i) {
+    acc.x += decode_lo<DT>(v[i].x);
+    acc.y += decode_hi<DT>(v[i].x);
+    acc.z += decode_lo<DT>(v[i].y);
+    acc.w += decode_hi<DT>(v[i].y);
+    if ((w.fmask >> i) & 1ull) {  // uniform: every lane takes part in the exchanges
+      float4 s = acc;
+      s.x += __shfl_xor(s.x, 16, kWave);
+      s.y += __shfl_xor(s.y, 16, kWave);
+      s.z += __shfl_xor(s.z, 16, kWave);
+      s.w += __shfl_xor(s.w, 16, kWave);
+      s.x += __shfl_xor(s.x, 32, kWave);
+      s.y += __shfl_xor(s.y, 32, kWave);
+      s.z += __shfl_xor(s.z, 32, kWave);
+      s.w += __shfl_xor(s.w, 32, kWave);
+      const int t = __builtin_amdgcn_readlane(w.t, i);
+      if (lane < 16) *reinterpret_cast<float4*>(Z + (1 + t) * LD + lane * 4) = s;
+      acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
+// True when a sample of this launch may take gather_quads (uniform).
+__device__ __forceinline__ bool quads_fit(const int* trows, int T, int lane) {
+  const bool small = lane >= T || static_cast<uint32_t>(trows[lane < T ? lane : 0]) < (1u << 24);
+  return T <= kWave && __ballot(!small) == 0ull;
+}
+
+template <int DT, int WIN>
+__device__ __forceinline__ void gather_quads(const int* pos, const int* stage, const char* const* tbase, int T,
+                                             float* Z, int LD, int tid) {
+  const int lane = tid & (kWave - 1);
+  // instructions per bag (a bag of n rows takes ceil(n / 4)), scanned over the bags
+  int incl = lane < T ? (pos[lane + 1] - pos[lane] + 3) >> 2 : 0;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  const int I = rfl(__shfl(incl, T - 1, kWave));
+  const uint32_t sub8 = static_cast<uint32_t>(lane & 15) * 8u;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  QuadWindow wa, wb;
+  uint2 va[WIN], vb[WIN];
+  quad_prepare<WIN>(wa, pos, stage, tbase, incl, T, I, 0, lane);
+  quad_issue<0, WIN>(wa, va, sub8);
+  for (int q = 0;;) {
+    quad_prepare<WIN>(wb, pos, stage, tbase, incl, T, I, q + WIN, lane);
+    quad_issue<0, WIN>(wb, vb, sub8);
+    quad_consume<DT, WIN>(wa, va, acc, Z, LD, lane);
+    q += WIN;
+    if (q >= I) break;
+    quad_prepare<WIN>(wa, pos, stage, tbase, incl, T, I, q + WIN, lane);
+    quad_issue<0, WIN>(wa, va, sub8);
+    quad_consume<DT, WIN>(wb, vb, acc, Z, LD, lane);
+    q += WIN;
+    if (q >= I) break;
+  }
+#pragma unroll
+  for (int j = 0; j < WIN; ++j) {
+    touch(va[j]);
+    touch(vb[j]);
+  }
+}
+
 // Logical block of workgroup bid in the row-streaming kernel. The dispatcher
 // deals workgroups out round-robin over the 8 XCDs; here each XCD takes runs
 // of 16 consecutive logical blocks, interleaved with the other XCDs' runs. The
@@ -1230,12 +1390,23 @@ __global__ __launch_bounds__(kRowThreads, 6) void fused_rows_kernel(FwdArgs a, R
         // 40.0 us on 26 tables of D = 256 with one index per bag (one sample per
         // workgroup keeps 6: 86.9 against 88.2 us with 20 rows per bag)
         constexpr int WIN = (DT == DLRM_F16 && LB == 8 && G > 1) ? 4 : RowShape<DT, LB>::WIN;
-        if (p1 <= CAP)
-          gather_range<DT, LB, false, CAP, WIN>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw,
-                                                tid, qsb);
-        else
-          gather_range<DT, LB, true, CAP, WIN>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw,
-                                               tid, qsb);
+        // 128-byte 16-bit rows with one wave per sample: four rows per load
+        constexpr bool kQuads = (DT == DLRM_F16 || DT == DLRM_BF16) && LB == 2 && GW == 1;
+        bool done = false;
+        if constexpr (kQuads) {
+          if (p1 <= CAP && quads_fit(trows, T, tid & (kWave - 1))) {
+            gather_quads<DT, kQuadWin>(pos, stage, tbase, T, Z, LD, tid);
+            done = true;
+          }
+        }
+        if (!done) {
+          if (p1 <= CAP)
+            gather_range<DT, LB, false, CAP, WIN>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw,
+                                                  tid, qsb);
+          else
+            gather_range<DT, LB, true, CAP, WIN>(a, beg, pos, stage, sbag, tbase, trows, T, p0, p1, Z, LD, cw, ctw,
+                                                 tid, qsb);
+        }
       }
     }
     // the prefetched values are first used here (the barrier keeps every use,

@@ -102,3 +102,42 @@ def test_grouped_bad_indices_are_flagged_and_skipped():
     off2 = np.array([int(keep[:o].sum()) for o in orc.lengths_to_offsets(b.lengths)])
     r = orc.embbag_fwd(b.tables, "f16", w.B, off2, idx[keep], b.e0)
     np.testing.assert_allclose(pooled.cpu().numpy(), r["pooled"], rtol=2e-3, atol=1e-5)
+
+
+# 16-bit rows of 128 bytes (D = 64) with one wave per sample (G = 8) are gathered four
+# rows per load instruction, four consecutive rows of one bag per instruction
+QUAD_CASES = [
+    # the most tables a group of 64 threads takes, bags of 0 to 4 rows
+    ("q-64t", dict(T=64, rows=300, D=64, dtype="bf16", B=600, bag=("uniform", 0, 5), dist=("uniform",), seed=41)),
+    # one table, long bags (up to 100 rows: 25 instructions)
+    ("q-1t", dict(T=1, rows=5000, D=64, dtype="f16", B=900, bag=("poisson", 20, 100), dist=("zipf", 1.1), seed=42)),
+    # bags of exactly four rows: every instruction full, one per bag
+    ("q-fixed4", dict(T=13, rows=2000, D=64, dtype="f16", B=700, bag=("fixed", 4), dist=("uniform",), seed=43)),
+    # bags of five rows: a full instruction, then one holding a single row
+    ("q-fixed5", dict(T=7, rows=2000, D=64, dtype="bf16", B=700, bag=("fixed", 5), dist=("zipf", 1.05), seed=44)),
+    # mostly empty bags
+    ("q-sparse", dict(T=9, rows=2000, D=64, dtype="f16", B=800, bag=("uniform", 0, 2), dist=("uniform",), seed=45)),
+]
+
+
+@pytest.mark.parametrize("name,kw", QUAD_CASES, ids=[c[0] for c in QUAD_CASES])
+def test_grouped_four_rows_per_load(name, kw):
+    """Parity (and exact integer sums) of the four-rows-per-load gather, run to run bit for
+    bit; the plan of each case is G = 8."""
+    w = synth.Workload(name, **kw)
+    b = synth.make_batch(w)
+    avg = b.indices.size // w.B
+    assert 8 * max(w.T, w.D) <= 512 and avg * 3 // 2 <= 256 and w.B >= 512  # G = 8
+    db = DeviceBatch(b)
+    pooled, inter = db.fwd(want_pooled=True)
+    torch.cuda.synchronize()
+    assert db.status.item() == 0
+    check_fwd(db, pooled, inter)
+    _, inter2 = db.fwd()
+    torch.cuda.synchronize()
+    assert torch.equal(inter, inter2)
+    wi = synth.Workload(name + "-int", values="int", **{**kw, "seed": kw["seed"] + 100})
+    dbi = DeviceBatch(synth.make_batch(wi))
+    pi, ii = dbi.fwd(want_pooled=True)
+    torch.cuda.synchronize()
+    check_fwd(dbi, pi, ii, exact=True)
