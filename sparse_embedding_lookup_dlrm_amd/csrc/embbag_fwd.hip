@@ -1109,11 +1109,11 @@ struct QuadWindow {
 
 constexpr int kQuadWin = 7;  // load instructions (28 rows) per window: 6, 7 and 8 measured 22.2, 22.0 and
                              // 21.9 us on the multi-hot batch, and 8 spills 8 bytes per lane
-// Bytes every buffer resource of the gather covers: more than any table it
-// takes (under 2^24 rows of 128 bytes) and less than the offset of a slot that
-// reads nothing, so that slot is out of range and every other is a row of the
-// table.
-constexpr int kQuadRange = 0x7FFFFFFF;
+// Bytes every buffer resource of the gather covers, 2^31: at least any table it
+// takes (under 2^24 rows of 128 bytes, so a last row ends by 2^31) and less
+// than the offset of a slot that reads nothing, so that slot is out of range
+// and every other is a row of the table.
+constexpr int kQuadRange = static_cast<int>(0x80000000u);
 
 // Lane (k, i) works out instruction q + i (the same for all four quarters) and
 // the row of it that quarter k loads.

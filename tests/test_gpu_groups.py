@@ -11,7 +11,7 @@ import torch
 from oracle import dlrm_oracle as orc
 from sparse_embedding_lookup_dlrm_amd import ops, synth
 
-from gpu_util import DeviceBatch, check_fwd, need_gpu
+from gpu_util import RTOL, DeviceBatch, abs_tables, assert_mag_close, check_fwd, need_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -141,3 +141,50 @@ def test_grouped_four_rows_per_load(name, kw):
     pi, ii = dbi.fwd(want_pooled=True)
     torch.cuda.synchronize()
     check_fwd(dbi, pi, ii, exact=True)
+
+
+@pytest.mark.parametrize("rows", [[(1 << 24) - 1, 1000], [(1 << 24) - 1, 1 << 24]], ids=["2^24-1", "2^24"])
+def test_grouped_four_rows_per_load_largest_tables(rows):
+    """The four-rows-per-load gather takes tables of fewer than 2^24 rows (its buffer range
+    is 2^31 bytes): a table of 2^24 - 1 rows goes through it, with indices on its last row,
+    and a launch holding a table of 2^24 rows takes the one-row-per-load gather instead.
+    The tables (2 and 4 GiB) are zeros except the rows the batch touches; the oracle runs on
+    those rows alone, the indices remapped in order."""
+    dev = torch.device("cuda:0")
+    T, D, B = len(rows), 64, 600
+    rng = np.random.default_rng(sum(rows) % 1000)
+    lengths = rng.integers(1, 9, size=T * B).astype(np.int32)
+    off = orc.lengths_to_offsets(lengths)
+    idx = np.concatenate([rng.integers(0, rows[t], size=int(lengths[t * B:(t + 1) * B].sum())) for t in range(T)])
+    for t in range(T):  # the last row of each table, at a bag's start and at a bag's end
+        idx[off[t * B]] = rows[t] - 1
+        idx[off[t * B + 7] - 1] = rows[t] - 1
+    idx = idx.astype(np.int32)
+    e0 = rng.standard_normal((B, D)).astype(np.float32)
+    tables, sub_tables, sub_idx = [], [], np.empty_like(idx)
+    try:
+        for t in range(T):
+            seg = idx[off[t * B]:off[(t + 1) * B]]
+            u = np.unique(seg)
+            vals = rng.standard_normal((len(u), D)).astype(np.float16)
+            tab = torch.zeros((rows[t], D), dtype=torch.float16, device=dev)
+            tab[torch.from_numpy(u.astype(np.int64)).to(dev)] = torch.from_numpy(vals).to(dev)
+            tables.append(tab)
+            sub_tables.append(vals)
+            sub_idx[off[t * B]:off[(t + 1) * B]] = np.searchsorted(u, seg)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        pooled, inter = ops.embbag_fwd(tables, torch.from_numpy(off.astype(np.int32)).to(dev),
+                                       torch.from_numpy(idx).to(dev), B, torch.from_numpy(e0).to(dev),
+                                       want_pooled=True, status=status)
+        torch.cuda.synchronize()
+        assert status.item() == 0
+        got_p, got_i = pooled.cpu().numpy(), inter.cpu().numpy()
+    finally:
+        del tables
+        torch.cuda.empty_cache()
+    ref = orc.embbag_fwd(sub_tables, "f16", B, off, sub_idx, e0)
+    pm = orc.embbag_pool(abs_tables(sub_tables, "f16"), "f16", B, off, sub_idx)
+    assert_mag_close(got_p, ref["pooled"], pm, RTOL["f16"], "pooled")
+    mag = orc.interact(np.abs(e0), pm)
+    assert_mag_close(got_i[:, D:], ref["out"][:, D:], mag[:, D:], RTOL["f16"], "dots")
+    np.testing.assert_array_equal(got_i[:, :D], e0)
